@@ -1,0 +1,6 @@
+"""CPU oracle for the speculative-sampling verify step (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  See ``oracle.verify`` for the definitions it follows."""
+from .verify import (decode_row, process, inverse_cdf, verify_sequence,  # noqa: F401
+                     verify_sequence_vectorised, verify_batch, BatchResult, SeqResult)

@@ -488,3 +488,28 @@ def test_neg_inf_logits_allowed():
     r = verify_sequence(zp, zq, np.array([0], np.int32), np.array([0.99, 0.3]), 1.0, 0, 1.0, 1)
     assert r.n in (0, 1) and r.tokens[r.n] in (0, 2) if r.n == 0 else True
     assert r.pq[0, 0] > 0 and r.pq[0, 1] > 0
+
+
+def test_inverse_cdf_never_picks_zero_mass():
+    # Leading zero-mass entries and u = 0: the draw must land on the first
+    # token that carries mass (a token of zero probability is never sampled).
+    w = np.array([0.0, 0.0, 0.3, 0.0, 0.7])
+    assert inverse_cdf(w, 0.0)[0] == 2
+    zp = np.stack([logits_of([0.0, 0.0, 0.3, 0.0, 0.7])] * 2)
+    zq = np.stack([logits_of([0.0, 0.0, 0.3, 0.0, 0.7])])
+    r = verify_sequence(zp, zq, np.array([2], np.int32), np.array([0.0, 0.0]), 1.0, 0, 1.0, 1)
+    assert r.n == 1 and r.tokens[1] == 2
+
+
+@pytest.mark.parametrize("cut", [0, 1, 2, 4])
+def test_topp_mass_exactly_at_threshold(cut):
+    # When the mass of the top (cut+1) values equals top_p exactly, those
+    # values already reach top_p and form the nucleus.
+    rng = np.random.default_rng(800 + cut)
+    z = rng.normal(size=10) * 2
+    base = process(z, 1.0, 0, 1.0).prob
+    order = np.argsort(-z, kind="stable")
+    cum = np.cumsum(base[order])
+    pr = process(z, 1.0, 0, float(cum[cut]))
+    assert pr.kept.sum() == cut + 1
+    assert set(np.nonzero(pr.kept)[0]) == set(order[: cut + 1].tolist())

@@ -1,0 +1,133 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) batched speculative-sampling
+ * verify step.
+ *
+ * What one call computes, per sequence b (definitions as on the pages):
+ *   - p_j = processed target distribution at position j (0 <= j <= gamma_b),
+ *     q_i = processed draft distribution at position i (0 <= i < gamma_b).
+ *     "Processed" = temperature, then top-k, then top-p, then normalise: the
+ *     sampling adjustments are applied to both models before the test
+ *     ("Fast Inference from Transformers via Speculative Decoding", mtandhj.com
+ *     summary, "Speculative Sampling: theoretical basis"; the Leviathan review,
+ *     "Method / Overview": argmax, top-k, nucleus and temperature are all
+ *     standard sampling from an adjusted distribution).  Temperature 0 is
+ *     argmax (all mass on the largest logit, lowest id on ties).
+ *   - Draft x_i is accepted while u_i < min(1, p_i(x_i)/q_i(x_i)), evaluated
+ *     division-free as u_i * q_i(x_i) < p_i(x_i); n = number accepted before
+ *     the first rejection (Leviathan review, Algorithm 1, step 3; llm-compass,
+ *     section 4, speculative_step).
+ *   - If n < gamma_b the extra token is drawn from norm(max(0, p_n - q_n)),
+ *     else from p_{gamma_b} (the bonus token) (Algorithm 1, steps 4-5; "the
+ *     art of guessing well", section "Speculative sampling", where the draft
+ *     distribution after the last draft is taken as zero).  The draw is an
+ *     inverse CDF over ascending vocabulary id with the residual/bonus uniform
+ *     ("the art of guessing well", section "Sampling with shared noise",
+ *     textbook method): token = min{v : C(v) > u * Z}.
+ *   - alpha_i = sum_v min(p_i(v), q_i(v)) for every draft position
+ *     (mtandhj summary, "How to choose gamma"; "the art of guessing well",
+ *     "Speculative sampling").
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device allocations owned by the caller; the
+ *     library keeps no reference after the call returns and allocates no
+ *     device memory.  All arrays are dense and row-major.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and runs asynchronously: there is no host synchronisation and no
+ *     device-to-host copy.  Outputs are valid once the stream reaches them.
+ *   - Argument errors are reported synchronously by a negative return code
+ *     before anything is enqueued.  Bad *data* (NaN or +inf logits, a row of
+ *     only -inf, a draft token outside [0, V), gamma_len outside
+ *     [1, gamma_max], a negative or NaN temperature, a NaN top_p, a uniform
+ *     outside [0, 1)) is reported per sequence: n_accepted = -1, every token
+ *     -1, alpha and pq NaN.
+ *   - Calls that share one workspace must be ordered (same stream or
+ *     synchronised); distinct workspaces make calls independent.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Logit storage types. */
+enum { SV_BF16 = 0, SV_FP32 = 1 };
+
+/* Return codes. */
+enum {
+  SV_OK = 0,
+  SV_ERR_ARG = -1,          /* null pointer, bad size, misaligned base      */
+  SV_ERR_UNSUPPORTED = -2,  /* unknown dtype, V or gamma_max beyond limits  */
+  SV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required  */
+  SV_ERR_HIP = -4           /* a HIP call failed (see spec_verify_strerror) */
+};
+
+/* Limits (checked synchronously). */
+#define SV_MAX_GAMMA 64      /* gamma_max <= 64: one wavefront ballot spans all drafts */
+#define SV_MAX_VOCAB 1048576 /* V <= 2^20                                            */
+
+/*
+ * Bytes of device workspace that spec_verify needs for these sizes
+ * (0 for invalid sizes).  The workspace holds per-row candidate lists,
+ * per-row statistics and completion counters.
+ */
+size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype);
+
+/*
+ * Prepare a workspace for its first use: clears the completion counters
+ * (enqueued on `stream`).  Every successful spec_verify call leaves the
+ * counters cleared again, so this is needed once per allocation.
+ * Returns SV_OK or a negative code.
+ */
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
+                               int dtype, void* stream);
+
+/*
+ * The batched verify step.
+ *
+ *  p_logits     [B][gamma_max+1][V] target logits (bf16 bit patterns or fp32), 16-byte aligned.
+ *  q_logits     [B][gamma_max][V]   draft logits, same dtype, 16-byte aligned.
+ *  dtype        SV_BF16 or SV_FP32.
+ *  draft_tokens [B][gamma_max] int32: x_1..x_gamma_b; slots beyond gamma_b are ignored.
+ *  gamma_len    [B] int32 per-sequence gamma_b in [1, gamma_max], or NULL (all gamma_max).
+ *               Target rows beyond gamma_b and draft rows at or beyond gamma_b are never read.
+ *  uniforms     [B][gamma_max+1] float in [0, 1): u[b][i] (i < gamma_b) tests draft i;
+ *               u[b][gamma_max] drives the residual or bonus draw.
+ *  temperature  [B] float, >= 0; 0 selects exact argmax matching (uniforms and filters unused).
+ *  top_k        [B] int32 or NULL; k <= 0 or k >= V means no top-k.  Keeps every logit
+ *               >= the k-th largest (ties kept).
+ *  top_p        [B] float or NULL; top_p >= 1 means no top-p.  Applied after top-k: keeps every
+ *               value >= t*, the largest value whose mass at-or-above reaches top_p (ties kept).
+ *  B, gamma_max, V  sizes; B >= 0 (B == 0 is a no-op), 1 <= gamma_max <= SV_MAX_GAMMA,
+ *               1 <= V <= SV_MAX_VOCAB.
+ *  out_tokens   [B][gamma_max+1] int32: x_1..x_n, then the drawn token, then -1 padding.
+ *  out_n_accepted [B] int32: n, or -1 for an invalid sequence.
+ *  out_alpha    [B][gamma_max] float: alpha_i for i < gamma_b, 0 in padded slots.
+ *  out_pq       [B][gamma_max][2] float or NULL: (p_i(x_i), q_i(x_i)) for i < gamma_b, 0 beyond.
+ *  workspace    device buffer of at least spec_verify_workspace_bytes(...) bytes, 256-byte
+ *               aligned, prepared once with spec_verify_workspace_init.
+ *  stream       hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Returns SV_OK, or a negative code (nothing enqueued).
+ */
+int spec_verify(const void* p_logits, const void* q_logits, int dtype,
+                const int32_t* draft_tokens, const int32_t* gamma_len, const float* uniforms,
+                const float* temperature, const int32_t* top_k, const float* top_p,
+                int B, int gamma_max, int V,
+                int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
+const char* spec_verify_strerror(int code);
+
+/* ABI version: 1. */
+int spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

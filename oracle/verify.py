@@ -96,7 +96,7 @@ def process(z: np.ndarray, T: float, top_k: int, top_p: float) -> Processed:
     s = z / T
     kept = np.ones(V, dtype=bool)
     if 0 < top_k < V:
-        kth = np.sort(s)[V - top_k]
+        kth = np.partition(s, V - top_k)[V - top_k]     # the k-th largest value
         kept = s >= kth
     m = s[kept].max()
     e = np.where(kept, np.exp(s - m), 0.0)

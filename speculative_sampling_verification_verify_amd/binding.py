@@ -1,0 +1,164 @@
+"""ctypes binding of libspecverify.so (the C ABI in include/spec_verify.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the verify computation runs in the HIP
+kernels.  The functions keep the C names; ``Verifier`` owns a workspace and
+output tensors for repeated calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_BF16, SV_FP32 = 0, 1
+SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
+SV_MAX_GAMMA = 64
+SV_MAX_VOCAB = 1 << 20
+
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify",
+            "spec_verify_strerror", "spec_verify_version")
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where} failed with {code}: {spec_verify_strerror(code)}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.spec_verify_workspace_bytes.argtypes = [i, i, i, i]
+        L.spec_verify_workspace_bytes.restype = sz
+        L.spec_verify_workspace_init.argtypes = [vp, sz, i, i, i, i, vp]
+        L.spec_verify_workspace_init.restype = i
+        L.spec_verify.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_verify.restype = i
+        L.spec_verify_strerror.argtypes = [i]
+        L.spec_verify_strerror.restype = ctypes.c_char_p
+        L.spec_verify_version.argtypes = []
+        L.spec_verify_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return h or None
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_FP32
+    raise TypeError(f"logits must be bfloat16 (or int16 bf16 bit patterns) or float32, got {t.dtype}")
+
+
+def spec_verify_workspace_bytes(B: int, gamma_max: int, V: int, dtype: int) -> int:
+    return int(lib().spec_verify_workspace_bytes(B, gamma_max, V, dtype))
+
+
+def spec_verify_strerror(code: int) -> str:
+    return lib().spec_verify_strerror(code).decode()
+
+
+def spec_verify_version() -> int:
+    return int(lib().spec_verify_version())
+
+
+def spec_verify_workspace_init(workspace: torch.Tensor, B: int, gamma_max: int, V: int, dtype: int,
+                               stream=None) -> None:
+    rc = lib().spec_verify_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          B, gamma_max, V, dtype, _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_workspace_init")
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, shape, device):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                gamma_len: Optional[torch.Tensor], uniforms: torch.Tensor, temperature: torch.Tensor,
+                top_k: Optional[torch.Tensor], top_p: Optional[torch.Tensor],
+                out_tokens: torch.Tensor, out_n_accepted: torch.Tensor, out_alpha: torch.Tensor,
+                out_pq: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    """Enqueue one verify call (see include/spec_verify.h for the contract)."""
+    if p_logits.dim() != 3 or q_logits.dim() != 3:
+        raise ValueError("p_logits must be [B, gamma_max+1, V] and q_logits [B, gamma_max, V]")
+    B, G1, V = p_logits.shape
+    G = G1 - 1
+    dev = p_logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must live in GPU memory")
+    dt = _dtype_code(p_logits)
+    _check(q_logits, "q_logits", p_logits.dtype, (B, G, V), dev)
+    _check(p_logits, "p_logits", p_logits.dtype, (B, G + 1, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, G), dev)
+    _check(gamma_len, "gamma_len", torch.int32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, G + 1), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(top_k, "top_k", torch.int32, (B,), dev)
+    _check(top_p, "top_p", torch.float32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, G + 1), dev)
+    _check(out_n_accepted, "out_n_accepted", torch.int32, (B,), dev)
+    _check(out_alpha, "out_alpha", torch.float32, (B, G), dev)
+    _check(out_pq, "out_pq", torch.float32, (B, G, 2), dev)
+    rc = lib().spec_verify(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
+                           _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V,
+                           _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify")
+
+
+class Verifier:
+    """Owns a workspace and output buffers for calls of one shape."""
+
+    def __init__(self, B: int, gamma_max: int, V: int, dtype: int = SV_BF16, device="cuda", with_pq=True):
+        self.B, self.G, self.V, self.dtype = B, gamma_max, V, dtype
+        dev = torch.device(device)
+        nbytes = spec_verify_workspace_bytes(B, gamma_max, V, dtype)
+        if nbytes == 0:
+            raise ValueError("unsupported sizes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        spec_verify_workspace_init(self.workspace, B, gamma_max, V, dtype)
+        self.tokens = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
+        self.n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.alpha = torch.empty((B, gamma_max), dtype=torch.float32, device=dev)
+        self.pq = torch.empty((B, gamma_max, 2), dtype=torch.float32, device=dev) if with_pq else None
+
+    def __call__(self, p_logits, q_logits, draft_tokens, uniforms, temperature, top_k=None, top_p=None,
+                 gamma_len=None, stream=None):
+        spec_verify(p_logits, q_logits, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p,
+                    self.tokens, self.n_accepted, self.alpha, self.pq, self.workspace, stream)
+        return self.tokens, self.n_accepted, self.alpha, self.pq

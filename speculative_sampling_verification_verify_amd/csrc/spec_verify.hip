@@ -1,0 +1,186 @@
+// Batched speculative-sampling verify step for MI355X (gfx950): kernels and
+// the C ABI.
+//
+// A call is two launches on the caller's stream:
+//   1. select_kernel -- one workgroup per (logit row, row part) of every
+//      top-k / argmax sequence: streams the row once from HBM with 16-byte
+//      non-temporal loads and leaves the exact kept set (top-k survivors,
+//      ties included) in the workspace.  See sv_select.h.
+//   2. finish_kernel -- one workgroup per sequence: normalisers, top-p,
+//      p(x) and q(x), the overlap, the acceptance test with the first
+//      rejection found by one wavefront ballot, and the residual / bonus
+//      draw; unfiltered and top-p sequences are computed here from the
+//      logits by a multi-pass procedure.  See sv_finish.h.
+//
+// Definitions followed (page titles and sections): the acceptance rule and
+// the residual, "Fast Inference from Transformers via Speculative Decoding"
+// (mtandhj.com summary), "Speculative Sampling: theoretical basis"; the
+// first-rejection count, the Leviathan review (dongryeollee1), Algorithm 1;
+// the bonus token via a zero draft distribution after the last draft,
+// "Speculative Decoding: the art of guessing well", "Speculative sampling";
+// the inverse-CDF draw, same page, "Sampling with shared noise"; the overlap
+// alpha = sum min(p, q), mtandhj summary, "How to choose gamma".
+
+#include "sv_select.h"
+#include "sv_finish.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace sv {
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t rows_off, cand_off, total, counters_bytes;
+};
+
+static bool sizes_ok(int B, int G, int V) {
+  return B >= 0 && G >= 1 && G <= SV_MAX_GAMMA && V >= 1 && V <= SV_MAX_VOCAB;
+}
+
+static Layout layout(int B, int G) {
+  Layout L;
+  const size_t R = (size_t)B * (2 * G + 1);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L.rows_off = 0;
+  L.cand_off = up(R * sizeof(RowInfo));
+  L.counters_bytes = L.cand_off;
+  L.total = L.cand_off + R * RCAP * sizeof(uint2);
+  return L;
+}
+
+static thread_local char g_errbuf[256];
+
+template <typename ET, bool VECTOR>
+static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_kernel<ET, VECTOR>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((finish_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), fin_lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype) {
+  if (!sizes_ok(B, gamma_max, V) || (dtype != SV_BF16 && dtype != SV_FP32)) return 0;
+  if (B == 0) return 256;
+  return layout(B, gamma_max).total;
+}
+
+extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
+                                          int dtype, void* stream) {
+  const size_t need = spec_verify_workspace_bytes(B, gamma_max, V, dtype);
+  if (need == 0) return SV_ERR_ARG;
+  if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
+  if (B == 0) return SV_OK;
+  const Layout L = layout(B, gamma_max);
+  const size_t n = L.counters_bytes / 4;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
+                     (hipStream_t)stream, (uint32_t*)workspace, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(e));
+    return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
+extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
+                           const int32_t* gamma_len, const float* uniforms, const float* temperature,
+                           const int32_t* top_k, const float* top_p, int B, int gamma_max, int V,
+                           int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  if (!p_logits || !q_logits || !draft_tokens || !uniforms || !temperature || !out_tokens || !out_n_accepted ||
+      !out_alpha)
+    return SV_ERR_ARG;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)p_logits % es) || ((uintptr_t)q_logits % es)) return SV_ERR_ARG;
+  const size_t need = spec_verify_workspace_bytes(B, gamma_max, V, dtype);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256)) return SV_ERR_WORKSPACE;
+  const long long rows = (long long)B * (2 * gamma_max + 1);
+  const int vec = dtype == SV_BF16 ? 8 : 4;
+  const int chunk_max = NT * VPL * vec;
+  const int NC = (V + chunk_max - 1) / chunk_max;
+  int L = (V + NC - 1) / NC;
+  L = (L + vec - 1) / vec * vec;
+  // Rows longer than a few chunks are split into parts of about five chunks
+  // so that the grid has enough workgroups to balance across compute units.
+  const int NP = (NC + 4) / 5;
+  const int CPP = (NC + NP - 1) / NP;
+  const long long grid = rows * NP;
+  if (grid > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
+  const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)q_logits % 16 == 0);
+  int vb = 0;
+  while ((1LL << vb) < (long long)V + 1) ++vb;
+  const Layout Lw = layout(B, gamma_max);
+  Args a;
+  a.p = p_logits;
+  a.q = q_logits;
+  a.draft = draft_tokens;
+  a.gamma_len = gamma_len;
+  a.u = uniforms;
+  a.temp = temperature;
+  a.topk = top_k;
+  a.topp = top_p;
+  a.B = B;
+  a.G = gamma_max;
+  a.V = V;
+  a.NC = NC;
+  a.L = L;
+  a.NP = NP;
+  a.CPP = CPP;
+  a.fixbits = 62 - vb;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n_accepted;
+  a.out_alpha = out_alpha;
+  a.out_pq = out_pq;
+  a.rows = reinterpret_cast<RowInfo*>((char*)workspace + Lw.rows_off);
+  a.cand = reinterpret_cast<uint2*>((char*)workspace + Lw.cand_off);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t fin_lds = sizeof(FinSmem);
+  hipError_t e = hipSuccess;
+  if (dtype == SV_BF16) {
+    e = vector_ok ? launch_pair<uint16_t, true>(a, grid, fin_lds, st) : launch_pair<uint16_t, false>(a, grid, fin_lds, st);
+  } else {
+    e = vector_ok ? launch_pair<float, true>(a, grid, fin_lds, st) : launch_pair<float, false>(a, grid, fin_lds, st);
+  }
+  if (e != hipSuccess) {
+    snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(e));
+    return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
+extern "C" const char* spec_verify_strerror(int code) {
+  switch (code) {
+    case SV_OK: return "ok";
+    case SV_ERR_ARG: return "invalid argument (null pointer, size out of range or misaligned pointer)";
+    case SV_ERR_UNSUPPORTED: return "unsupported dtype or size";
+    case SV_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case SV_ERR_HIP: return g_errbuf[0] ? g_errbuf : "HIP error";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int spec_verify_version(void) { return 1; }

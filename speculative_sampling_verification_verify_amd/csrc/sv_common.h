@@ -1,0 +1,116 @@
+// Shared definitions of the verify kernels: workspace records, call
+// arguments, per-sequence mode, row addressing, completion tickets.
+#pragma once
+
+#include "sv_device.h"
+#include "spec_verify.h"
+
+namespace sv {
+
+enum { MODE_INVALID = 0, MODE_GREEDY = 1, MODE_SPARSE = 2, MODE_DENSE = 3 };
+
+struct RowInfo {      // 32 bytes per logit row (workspace)
+  uint32_t done;      // completion ticket over the row's parts
+  uint32_t cnt;       // candidates appended by the parts
+  uint32_t thr;       // certified lower bound on the row's k-th largest key (0 = none)
+  uint32_t flags;     // F_BAD | F_DEMOTE
+  int32_t nsurv;      // survivors after the row's exact selection
+  uint32_t pad[3];
+};
+
+struct Args {
+  const void* p;
+  const void* q;
+  const int32_t* draft;
+  const int32_t* gamma_len;
+  const float* u;
+  const float* temp;
+  const int32_t* topk;
+  const float* topp;
+  int B, G, V;
+  int NC, L;          // chunks per row, chunk length in elements
+  int NP, CPP;        // parts per row, chunks per part
+  int fixbits;        // fixed-point fraction bits for mass sums
+  int32_t* out_tokens;
+  int32_t* out_n;
+  float* out_alpha;
+  float* out_pq;
+  RowInfo* rows;
+  uint2* cand;        // [rows][RCAP] (key, vocabulary id)
+};
+
+struct Mode {
+  int g;        // rows used by this sequence: clamp(gamma_b, 1, G) drafts
+  int mode;
+  uint32_t k;   // effective top-k of the streaming select (1 for argmax)
+  float T;
+  float tp;
+};
+
+// The processing mode is a pure function of the sequence's own parameters,
+// so every kernel derives the same answer.
+__device__ __forceinline__ Mode seq_mode(const Args& a, int b) {
+  Mode m;
+  const int gl = a.gamma_len ? a.gamma_len[b] : a.G;
+  m.g = min(max(gl, 1), a.G);
+  m.T = a.temp[b];
+  const int k = a.topk ? a.topk[b] : 0;
+  m.tp = a.topp ? a.topp[b] : 1.0f;
+  m.k = 0;
+  if (!(m.T >= 0.0f)) {
+    m.mode = MODE_INVALID;
+  } else if (m.T == 0.0f) {
+    m.mode = MODE_GREEDY;
+    m.k = 1;
+  } else if (k > 0 && k < a.V && k <= KMAX_SPARSE) {
+    m.mode = MODE_SPARSE;
+    m.k = (uint32_t)k;
+  } else {
+    m.mode = MODE_DENSE;
+  }
+  return m;
+}
+
+template <typename ET>
+__device__ __forceinline__ const ET* row_ptr(const Args& a, int b, bool isP, int pos) {
+  if (isP) return reinterpret_cast<const ET*>(a.p) + ((size_t)b * (a.G + 1) + pos) * (size_t)a.V;
+  return reinterpret_cast<const ET*>(a.q) + ((size_t)b * a.G + pos) * (size_t)a.V;
+}
+
+// Row slots of sequence b: slot s in [0, G] is target position s, slot
+// G+1+i is draft position i.  `r` enumerates the used rows: 0..g are the
+// target positions, g+1..2g the draft positions.
+__device__ __forceinline__ int used_slot(int G, int g, int r) { return r <= g ? r : G + 1 + (r - g - 1); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t atomic_load_u32(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the block calls this.  Returns true in the one workgroup
+// that makes the total-th arrival, after resetting the counter for the next
+// call; its global writes made before the call are visible to that
+// workgroup (release/acquire at device scope).
+__device__ __forceinline__ bool block_ticket(uint32_t* counter, uint32_t total, uint32_t* s_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t last = (t == total - 1) ? 1u : 0u;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  __syncthreads();
+  if (last) __threadfence();
+  return last;
+}
+
+}  // namespace sv

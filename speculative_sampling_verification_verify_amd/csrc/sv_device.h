@@ -1,0 +1,230 @@
+// Device-side building blocks for the verify kernels (gfx950, wave64).
+//
+// Logit values are compared as integer keys: a bf16 (or fp32) bit pattern in
+// sign-magnitude form is turned into a two's-complement integer and biased to
+// an unsigned key, so integer order equals float order, -0 and +0 share one
+// key, -inf is the smallest valid key, and NaN / +inf land outside the valid
+// range.  Key 0 never occurs and means "no element".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int NT = 512;          // threads per workgroup (8 wavefronts)
+constexpr int NWAVE = NT / 64;
+constexpr int VPL = 4;           // 16-byte vectors held per lane per chunk
+constexpr int CCAP = 2048;       // candidate slots per chunk (LDS)
+constexpr int RCAP = 2048;       // candidate slots per logit row (workspace)
+constexpr int KMAX_SPARSE = 512; // largest top-k handled by the streaming select
+constexpr uint32_t NONE = 0xFFFFFFFFu;
+
+// Row flags (workspace).
+constexpr uint32_t F_BAD = 1u;      // NaN or +inf seen
+constexpr uint32_t F_DEMOTE = 2u;   // candidate overflow: sequence goes to the multi-pass path
+
+template <typename ET> struct Key;
+
+// bf16 stored as its 16-bit pattern.
+template <> struct Key<uint16_t> {
+  static constexpr int VEC = 8;             // elements per 16-byte vector
+  static constexpr int LEVELS = 2;          // 8-bit radix digits in a key
+  static constexpr uint32_t NEG_INF = 0x8000u - 0x7F80u;
+  static constexpr uint32_t POS_INF = 0x8000u + 0x7F80u;
+  __device__ __forceinline__ static uint32_t of_bits(uint32_t h) {
+    uint32_t mag = h & 0x7FFFu;
+    return (h & 0x8000u) ? (0x8000u - mag) : (0x8000u + mag);
+  }
+  __device__ __forceinline__ static float value(uint32_t uk) {
+    uint32_t bits = uk >= 0x8000u ? (uk - 0x8000u) : (0x8000u | (0x8000u - uk));
+    return __uint_as_float(bits << 16);
+  }
+  __device__ __forceinline__ static uint32_t load_key(const uint16_t* row, int i) {
+    return of_bits(row[i]);
+  }
+};
+
+// fp32.
+template <> struct Key<float> {
+  static constexpr int VEC = 4;
+  static constexpr int LEVELS = 4;
+  static constexpr uint32_t NEG_INF = 0x80000000u - 0x7F800000u;
+  static constexpr uint32_t POS_INF = 0x80000000u + 0x7F800000u;
+  __device__ __forceinline__ static uint32_t of_bits(uint32_t b) {
+    uint32_t mag = b & 0x7FFFFFFFu;
+    return (b & 0x80000000u) ? (0x80000000u - mag) : (0x80000000u + mag);
+  }
+  __device__ __forceinline__ static float value(uint32_t uk) {
+    uint32_t bits = uk >= 0x80000000u ? (uk - 0x80000000u) : (0x80000000u | (0x80000000u - uk));
+    return __uint_as_float(bits);
+  }
+  __device__ __forceinline__ static uint32_t load_key(const float* row, int i) {
+    return of_bits(__float_as_uint(row[i]));
+  }
+};
+
+template <typename ET>
+__device__ __forceinline__ bool key_valid(uint32_t uk) {
+  return uk >= Key<ET>::NEG_INF && uk < Key<ET>::POS_INF;
+}
+
+// ---------------------------------------------------------------------------
+// Wave / block reductions (wave64).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+// Inclusive prefix sum across the wave (lane order).
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Block-wide reductions through a small LDS scratch of NWAVE entries.
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T r = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) r += scratch[i];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* scratch) {
+  v = wave_max_u32(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) r = max(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* scratch) {
+  v = wave_min_u32(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  uint32_t r = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) r = min(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* scratch) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, 64);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) r |= scratch[i];
+  __syncthreads();
+  return r;
+}
+
+// Block exclusive scan of one value per thread (thread order); returns the
+// exclusive prefix and writes the block total to *total.
+template <typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T* scratch, T* total) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  T incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == 63) scratch[w] = incl;
+  __syncthreads();
+  T base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    T s = scratch[i];
+    if (i < w) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Block radix select: the k-th largest key (1-based) of a multiset spread
+// over the block's threads.  `feed(fn)` must call fn(key) for every key the
+// calling thread holds (keys of 0 are ignored).  Every thread of the block
+// calls this with the same k.  Returns the exact k-th largest key, or 0 when
+// fewer than k keys exist.  hist: 256 words of LDS; bc: 2 words of LDS.
+// ---------------------------------------------------------------------------
+template <int LEVELS, class Feed>
+__device__ __forceinline__ uint32_t block_kth_largest(Feed feed, uint32_t k, uint32_t* hist, uint32_t* bc) {
+  uint32_t prefix = 0, pmask = 0, krem = k;
+  for (int lvl = 0; lvl < LEVELS; ++lvl) {
+    const int shift = 8 * (LEVELS - 1 - lvl);
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    feed([&](uint32_t key) {
+      if (key != 0 && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int top = 255 - 4 * lane;
+      uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+      uint32_t s = c0 + c1 + c2 + c3;
+      uint32_t incl = wave_incl_scan(s);
+      uint32_t excl = incl - s;
+      bool hit = excl < krem && incl >= krem;
+      unsigned long long any = __ballot(hit);
+      if (hit) {
+        uint32_t r = krem - excl, d;
+        if (c0 >= r) {
+          d = top;
+        } else if (c0 + c1 >= r) {
+          d = top - 1; r -= c0;
+        } else if (c0 + c1 + c2 >= r) {
+          d = top - 2; r -= c0 + c1;
+        } else {
+          d = top - 3; r -= c0 + c1 + c2;
+        }
+        bc[0] = d;
+        bc[1] = r;
+      }
+      if (lane == 0 && any == 0ull) bc[0] = NONE;
+    }
+    __syncthreads();
+    const uint32_t d = bc[0], r = bc[1];
+    __syncthreads();
+    if (d == NONE) return 0;
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+    krem = r;
+  }
+  return prefix;
+}
+
+}  // namespace sv

@@ -1,0 +1,634 @@
+// Per-sequence finisher: acceptance, first rejection, overlap, residual or
+// bonus draw.
+//
+// Sparse sequences (top-k / argmax) work from the survivor lists written by
+// the streaming select: all lists of the sequence are brought into LDS in one
+// round trip, then each wavefront takes whole rows (normalisers, top-p cut)
+// and whole positions (p(x), q(x), overlap) without block-wide barriers.
+// Probabilities over survivors are evaluated in double precision.
+//
+// Dense sequences (no top-k, top-p, or lists that overflowed) run a
+// multi-pass procedure over the logits in one workgroup: maximum, count-based
+// radix select for top-k, mass-weighted radix select for top-p (fixed-point
+// 64-bit masses, so the result does not depend on summation order),
+// normalisers, overlap, and a tiled inverse-CDF scan in ascending id order.
+#pragma once
+
+#include "sv_common.h"
+
+namespace sv {
+
+constexpr int POOL = 8192;                      // survivor entries of one sequence held in LDS
+constexpr int MAXROWS = 2 * SV_MAX_GAMMA + 1;
+
+struct FinSmem {
+  uint2 pool[POOL];                             // (key, id) of every survivor of the sequence
+  double pe[POOL];                              // exp((z - zmax) / T) per survivor
+  uint32_t off[MAXROWS + 1];                    // pool offset of each used row
+  uint32_t st_thr[MAXROWS];                     // kept keys are >= st_thr
+  uint32_t st_arg[MAXROWS];                     // argmax (T == 0)
+  float st_zmax[MAXROWS];
+  double st_S[MAXROWS];                         // normaliser over the kept keys
+  double pos_p[SV_MAX_GAMMA];
+  double pos_q[SV_MAX_GAMMA];
+  double pos_alpha[SV_MAX_GAMMA];
+  union {
+    uint32_t h32[256];
+    unsigned long long h64[256];
+  } hist;
+  double red_d[NWAVE];
+  unsigned long long red_u64[NWAVE];
+  uint32_t red_u[NWAVE];
+  uint32_t bc[8];
+  uint32_t flag;
+};
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ===========================================================================
+// Sparse path.
+// ===========================================================================
+
+// Statistics of one row from its pool range [o, o+n), by one wavefront.
+template <typename ET>
+__device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, const Mode& m) {
+  const int lane = threadIdx.x & 63;
+  if (m.mode == MODE_GREEDY) {
+    uint32_t best = 0xFFFFFFFFu;
+    for (int i = lane; i < n; i += 64) best = min(best, s.pool[o + i].y);
+    best = wave_min_u32(best);
+    if (lane == 0) s.st_arg[r] = best;
+    return;
+  }
+  const double T = (double)m.T;
+  uint32_t kmax = 0;
+  for (int i = lane; i < n; i += 64) kmax = max(kmax, s.pool[o + i].x);
+  kmax = wave_max_u32(kmax);
+  const float zmax = Key<ET>::value(kmax);
+  double S = 0.0;
+  for (int i = lane; i < n; i += 64) {
+    const double e = exp(((double)Key<ET>::value(s.pool[o + i].x) - (double)zmax) / T);
+    s.pe[o + i] = e;
+    S += e;
+  }
+  S = wave_sum_d(S);
+  uint32_t thr = 1;
+  if (m.tp < 1.0f) {
+    // The nucleus: order survivors by (value desc, id asc); the cut is the
+    // first position whose running mass reaches top_p; every value >= the
+    // value there is kept.  Running mass of entry i = mass of all entries
+    // ordered at or before it.
+    const double target = (double)m.tp * S;
+    uint32_t cut_rank = 0xFFFFFFFFu, cut_key = 0;
+    for (int i = lane; i < n; i += 64) {
+      const uint2 e = s.pool[o + i];
+      uint32_t rank = 0;
+      double run = 0.0;
+      for (int j = 0; j < n; ++j) {
+        const uint2 f = s.pool[o + j];
+        const bool before = (f.x > e.x) || (f.x == e.x && f.y <= e.y);
+        rank += before && f.y != e.y ? 1u : 0u;
+        if (before) run += s.pe[o + j];
+      }
+      const bool reach = m.tp <= 0.0f ? rank == 0 : run >= target;
+      if (reach && rank < cut_rank) {
+        cut_rank = rank;
+        cut_key = e.x;
+      }
+    }
+    const uint32_t best = wave_min_u32(cut_rank);
+    const unsigned long long who = __ballot(cut_rank == best && best != 0xFFFFFFFFu);
+    if (best != 0xFFFFFFFFu) {
+      const int src = __ffsll((long long)who) - 1;
+      thr = (uint32_t)__shfl((int)cut_key, src, 64);
+      double S2 = 0.0;
+      for (int i = lane; i < n; i += 64)
+        if (s.pool[o + i].x >= thr) S2 += s.pe[o + i];
+      S = wave_sum_d(S2);
+    }
+  }
+  if (lane == 0) {
+    s.st_thr[r] = thr;
+    s.st_zmax[r] = zmax;
+    s.st_S[r] = S;
+  }
+}
+
+// Probability of pool entry i of row r (0 when cut by top-p).
+__device__ __forceinline__ double pool_prob(const FinSmem& s, int r, int i) {
+  return s.pool[i].x >= s.st_thr[r] ? s.pe[i] / s.st_S[r] : 0.0;
+}
+
+// Probability of vocabulary id v in row r (linear search of its pool range).
+__device__ __forceinline__ double pool_lookup(const FinSmem& s, int r, uint32_t v) {
+  const int o = (int)s.off[r], e = (int)s.off[r + 1];
+  for (int j = o; j < e; ++j)
+    if (s.pool[j].y == v) return pool_prob(s, r, j);
+  return 0.0;
+}
+
+// p_i(x_i), q_i(x_i) and alpha_i for one position, by one wavefront.
+__device__ __forceinline__ void wave_position(FinSmem& s, int i, int x, const Mode& m) {
+  const int lane = threadIdx.x & 63;
+  const int rp = i, rq = m.g + 1 + i;
+  if (m.mode == MODE_GREEDY) {
+    if (lane == 0) {
+      s.pos_p[i] = (uint32_t)x == s.st_arg[rp] ? 1.0 : 0.0;
+      s.pos_q[i] = (uint32_t)x == s.st_arg[rq] ? 1.0 : 0.0;
+      s.pos_alpha[i] = s.st_arg[rp] == s.st_arg[rq] ? 1.0 : 0.0;
+    }
+    return;
+  }
+  const int o = (int)s.off[rp], e = (int)s.off[rp + 1];
+  double al = 0.0, px = 0.0;
+  for (int j = o + lane; j < e; j += 64) {
+    const double pv = pool_prob(s, rp, j);
+    const uint32_t v = s.pool[j].y;
+    if (v == (uint32_t)x) px = pv;
+    if (pv > 0.0) al += fmin(pv, pool_lookup(s, rq, v));
+  }
+  al = wave_sum_d(al);
+  px = wave_sum_d(px);
+  double qx = 0.0;
+  const int oq = (int)s.off[rq], eq = (int)s.off[rq + 1];
+  for (int j = oq + lane; j < eq; j += 64)
+    if (s.pool[j].y == (uint32_t)x) qx = pool_prob(s, rq, j);
+  qx = wave_sum_d(qx);
+  if (lane == 0) {
+    s.pos_p[i] = px;
+    s.pos_q[i] = qx;
+    s.pos_alpha[i] = al;
+  }
+}
+
+// Residual (n < g) or bonus (n == g) draw from the pool, whole block.
+// weight(v) = max(0, p_n(v) - q_n(v)) (or p_g(v)); token = the smallest id
+// whose running weight in ascending id order exceeds u * Z.
+__device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float ures) {
+  if (m.mode == MODE_GREEDY) return (int)s.st_arg[n];
+  const bool resid = n < m.g;
+  const int rp = n, rq = m.g + 1 + n;
+  const int o = (int)s.off[rp], e = (int)s.off[rp + 1];
+  // Residual weights, kept in pe[] of a scratch range after the pool's used part.
+  const int w0 = (int)s.off[2 * m.g + 1];
+  const int cnt = e - o;
+  bool fallback = false;
+  double zl = 0.0;
+  for (int j = threadIdx.x; j < cnt; j += NT) {
+    const double p = pool_prob(s, rp, o + j);
+    double w = p;
+    if (resid && p > 0.0) w = fmax(p - pool_lookup(s, rq, s.pool[o + j].y), 0.0);
+    s.pe[w0 + j] = w;
+    zl += w;
+  }
+  double Z = block_sum(zl, s.red_d);
+  if (!(Z > 0.0)) {   // zero residual mass: draw from the target itself
+    fallback = true;
+    zl = 0.0;
+    for (int j = threadIdx.x; j < cnt; j += NT) {
+      const double p = pool_prob(s, rp, o + j);
+      s.pe[w0 + j] = p;
+      zl += p;
+    }
+    Z = block_sum(zl, s.red_d);
+  }
+  (void)fallback;
+  const double target = (double)ures * Z;
+  uint32_t best = 0xFFFFFFFFu, lastpos = 0;
+  for (int j = threadIdx.x; j < cnt; j += NT) {
+    const uint32_t v = s.pool[o + j].y;
+    const double wj = s.pe[w0 + j];
+    if (wj > 0.0) lastpos = max(lastpos, v + 1u);
+    double run = 0.0;
+    for (int l = 0; l < cnt; ++l)
+      if (s.pool[o + l].y <= v) run += s.pe[w0 + l];
+    if (run > target) best = min(best, v);
+  }
+  best = block_min_u32(best, s.red_u);
+  if (best != 0xFFFFFFFFu) return (int)best;
+  return (int)block_max_u32(lastpos, s.red_u) - 1;   // rounding left no crossing
+}
+
+// ===========================================================================
+// Multi-pass procedure for a whole sequence (unfiltered / top-p / overflow).
+// ===========================================================================
+
+// Calls fn(key, index) for every element of a logit row, this thread's share.
+template <typename ET, bool VECTOR, class F>
+__device__ __forceinline__ void row_for_each(const ET* rp, int V, F fn) {
+  constexpr int VEC = Key<ET>::VEC;
+  if constexpr (VECTOR) {
+    const uint4* vp = reinterpret_cast<const uint4*>(rp);
+    const int nv = V / VEC;
+    for (int vi = threadIdx.x; vi < nv; vi += NT) {
+      const uint4 d = vp[vi];
+      const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+      if constexpr (sizeof(ET) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          fn(Key<ET>::of_bits(w[e] & 0xFFFFu), vi * VEC + 2 * e);
+          fn(Key<ET>::of_bits(w[e] >> 16), vi * VEC + 2 * e + 1);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fn(Key<ET>::of_bits(w[e]), vi * VEC + e);
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += NT) fn(Key<ET>::load_key(rp, i), i);
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int o) {
+  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, o, 64);
+  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), o, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Mass-weighted radix select: the largest key t with mass(key >= t) >= tau,
+// over keys >= lo.  Returns (t, mass(key >= t)) in fixed point.
+template <typename ET, bool VECTOR>
+__device__ __forceinline__ uint32_t dense_topp_select(FinSmem& s, const ET* rp, int V, uint32_t lo, float zmax, float invT,
+                                      double fscale, double tau, unsigned long long* mass_out) {
+  constexpr int LEVELS = Key<ET>::LEVELS;
+  uint32_t prefix = 0, pmask = 0;
+  unsigned long long above = 0;
+  for (int lvl = 0; lvl < LEVELS; ++lvl) {
+    const int shift = 8 * (LEVELS - 1 - lvl);
+    for (int i = threadIdx.x; i < 256; i += NT) s.hist.h64[i] = 0ull;
+    __syncthreads();
+    row_for_each<ET, VECTOR>(rp, V, [&](uint32_t uk, int) {
+      if (uk >= lo && (uk & pmask) == prefix) {
+        const float e = __expf((Key<ET>::value(uk) - zmax) * invT);
+        const unsigned long long f = (unsigned long long)((double)e * fscale);
+        if (f) atomicAdd(&s.hist.h64[(uk >> shift) & 255u], f);
+      }
+    });
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int top = 255 - 4 * lane;
+      const unsigned long long c0 = s.hist.h64[top], c1 = s.hist.h64[top - 1], c2 = s.hist.h64[top - 2],
+                               c3 = s.hist.h64[top - 3];
+      const unsigned long long sum = c0 + c1 + c2 + c3;
+      unsigned long long incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long u = shfl_up_u64(incl, o);
+        if (lane >= o) incl += u;
+      }
+      const unsigned long long excl = incl - sum;
+      const double cum0 = (double)(above + excl + c0), cum1 = (double)(above + excl + c0 + c1),
+                   cum2 = (double)(above + excl + c0 + c1 + c2), cum3 = (double)(above + incl);
+      // Cumulative mass grows bin by bin from the top: the first lane whose
+      // last bin reaches tau holds the crossing bin.
+      const unsigned long long any = __ballot(cum3 >= tau);
+      const int firstlane = any ? __ffsll((long long)any) - 1 : -1;
+      if (lane == firstlane) {
+        uint32_t d;
+        unsigned long long ab;
+        if (cum0 >= tau) {
+          d = top; ab = above + excl;
+        } else if (cum1 >= tau) {
+          d = top - 1; ab = above + excl + c0;
+        } else if (cum2 >= tau) {
+          d = top - 2; ab = above + excl + c0 + c1;
+        } else {
+          d = top - 3; ab = above + excl + c0 + c1 + c2;
+        }
+        s.bc[0] = d;
+        s.bc[1] = (uint32_t)ab;
+        s.bc[2] = (uint32_t)(ab >> 32);
+        const unsigned long long at = ab + s.hist.h64[d];
+        s.bc[5] = (uint32_t)at;
+        s.bc[6] = (uint32_t)(at >> 32);
+      }
+      if (lane == 0 && any == 0ull) s.bc[0] = NONE;
+    }
+    __syncthreads();
+    const uint32_t d = s.bc[0];
+    const unsigned long long ab = ((unsigned long long)s.bc[2] << 32) | s.bc[1];
+    const unsigned long long at = ((unsigned long long)s.bc[6] << 32) | s.bc[5];
+    __syncthreads();
+    if (d == NONE) {
+      *mass_out = 0;
+      return 0;   // rounding: caller keeps everything
+    }
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+    above = ab;
+    if (lvl == LEVELS - 1) *mass_out = at;
+  }
+  return prefix;
+}
+
+template <typename ET, bool VECTOR>
+__device__ __forceinline__ bool dense_row_stats(const Args& a, FinSmem& s, int b, const Mode& m) {
+  constexpr int LEVELS = Key<ET>::LEVELS;
+  const int RS = 2 * a.G + 1;
+  const double fscale = ldexp(1.0, a.fixbits);
+  const int k = a.topk ? a.topk[b] : 0;
+  for (int r = 0; r <= 2 * m.g; ++r) {
+    const int slot = used_slot(a.G, m.g, r);
+    const bool isP = slot <= a.G;
+    const ET* rp = row_ptr<ET>(a, b, isP, isP ? slot : slot - a.G - 1);
+    uint32_t kmax = 0, bad = 0;
+    row_for_each<ET, VECTOR>(rp, a.V, [&](uint32_t uk, int) {
+      kmax = max(kmax, uk);
+      bad |= key_valid<ET>(uk) ? 0u : 1u;
+    });
+    bad = block_or_u32(bad, s.red_u);
+    kmax = block_max_u32(kmax, s.red_u);
+    if (bad || kmax <= Key<ET>::NEG_INF) return false;
+    if (m.mode == MODE_GREEDY) {
+      uint32_t arg = 0xFFFFFFFFu;
+      row_for_each<ET, VECTOR>(rp, a.V, [&](uint32_t uk, int i) {
+        if (uk == kmax) arg = min(arg, (uint32_t)i);
+      });
+      arg = block_min_u32(arg, s.red_u);
+      if (threadIdx.x == 0) s.st_arg[r] = arg;
+      __syncthreads();
+      continue;
+    }
+    const float zmax = Key<ET>::value(kmax);
+    const float invT = 1.0f / m.T;
+    uint32_t thr = 1;
+    if (k > 0 && k < a.V) {
+      thr = block_kth_largest<LEVELS>(
+          [&](auto fn) { row_for_each<ET, VECTOR>(rp, a.V, [&](uint32_t uk, int) { fn(uk); }); }, (uint32_t)k,
+          s.hist.h32, s.bc);
+      if (thr == 0) thr = 1;
+    }
+    unsigned long long sl = 0;
+    row_for_each<ET, VECTOR>(rp, a.V, [&](uint32_t uk, int) {
+      if (uk >= thr) sl += (unsigned long long)((double)__expf((Key<ET>::value(uk) - zmax) * invT) * fscale);
+    });
+    unsigned long long S = block_sum(sl, s.red_u64);
+    if (m.tp < 1.0f) {
+      uint32_t tstar;
+      unsigned long long mass = 0;
+      if (m.tp <= 0.0f) {
+        tstar = kmax;
+        unsigned long long ml = 0;
+        row_for_each<ET, VECTOR>(rp, a.V, [&](uint32_t uk, int) {
+          if (uk >= tstar) ml += (unsigned long long)((double)__expf((Key<ET>::value(uk) - zmax) * invT) * fscale);
+        });
+        mass = block_sum(ml, s.red_u64);
+      } else {
+        tstar = dense_topp_select<ET, VECTOR>(s, rp, a.V, thr, zmax, invT, fscale, (double)m.tp * (double)S, &mass);
+      }
+      if (tstar != 0 && mass > 0) {
+        thr = max(thr, tstar);
+        S = mass;
+      }
+    }
+    if (threadIdx.x == 0) {
+      s.st_thr[r] = thr;
+      s.st_zmax[r] = zmax;
+      s.st_S[r] = (double)S / fscale;
+    }
+    __syncthreads();
+  }
+  return true;
+}
+
+template <typename ET>
+__device__ __forceinline__ double dense_prob(uint32_t uk, uint32_t thr, float zmax, float invT, double invS) {
+  if (uk < thr) return 0.0;
+  return (double)__expf((Key<ET>::value(uk) - zmax) * invT) * invS;
+}
+
+template <typename ET, bool VECTOR>
+__device__ __forceinline__ void dense_positions(const Args& a, FinSmem& s, int b, const Mode& m) {
+  const float invT = m.mode == MODE_GREEDY ? 0.f : 1.0f / m.T;
+  for (int i = 0; i < m.g; ++i) {
+    const int rp = i, rq = m.g + 1 + i;
+    const int x = a.draft[(size_t)b * a.G + i];
+    if (m.mode == MODE_GREEDY) {
+      if (threadIdx.x == 0) {
+        s.pos_p[i] = (uint32_t)x == s.st_arg[rp] ? 1.0 : 0.0;
+        s.pos_q[i] = (uint32_t)x == s.st_arg[rq] ? 1.0 : 0.0;
+        s.pos_alpha[i] = s.st_arg[rp] == s.st_arg[rq] ? 1.0 : 0.0;
+      }
+      continue;
+    }
+    const ET* pp = row_ptr<ET>(a, b, true, i);
+    const ET* qp = row_ptr<ET>(a, b, false, i);
+    const uint32_t thrA = s.st_thr[rp], thrB = s.st_thr[rq];
+    const float zA = s.st_zmax[rp], zB = s.st_zmax[rq];
+    const double iA = 1.0 / s.st_S[rp], iB = 1.0 / s.st_S[rq];
+    double al = 0.0;
+    row_for_each<ET, VECTOR>(pp, a.V, [&](uint32_t uk, int v) {
+      const double pv = dense_prob<ET>(uk, thrA, zA, invT, iA);
+      if (pv > 0.0) {
+        const double qv = dense_prob<ET>(Key<ET>::load_key(qp, v), thrB, zB, invT, iB);
+        al += fmin(pv, qv);
+      }
+    });
+    al = block_sum(al, s.red_d);
+    if (threadIdx.x == 0) {
+      s.pos_p[i] = dense_prob<ET>(Key<ET>::load_key(pp, x), thrA, zA, invT, iA);
+      s.pos_q[i] = dense_prob<ET>(Key<ET>::load_key(qp, x), thrB, zB, invT, iB);
+      s.pos_alpha[i] = al;
+    }
+    __syncthreads();
+  }
+  __syncthreads();
+}
+
+template <typename ET, bool VECTOR>
+__device__ __forceinline__ int dense_draw(const Args& a, FinSmem& s, int b, const Mode& m, int n, float ures) {
+  if (m.mode == MODE_GREEDY) return (int)s.st_arg[n];
+  const float invT = 1.0f / m.T;
+  const bool resid = n < m.g;
+  const int rp = n, rq = m.g + 1 + n;
+  const ET* pp = row_ptr<ET>(a, b, true, n);
+  const ET* qp = resid ? row_ptr<ET>(a, b, false, n) : nullptr;
+  const uint32_t thrA = s.st_thr[rp];
+  const float zA = s.st_zmax[rp];
+  const double iA = 1.0 / s.st_S[rp];
+  uint32_t thrB = 0;
+  float zB = 0.f;
+  double iB = 0.0;
+  if (resid) {
+    thrB = s.st_thr[rq];
+    zB = s.st_zmax[rq];
+    iB = 1.0 / s.st_S[rq];
+  }
+  const int V = a.V;
+  auto weight = [&](int v, bool fallback) -> double {
+    const double p = dense_prob<ET>(Key<ET>::load_key(pp, v), thrA, zA, invT, iA);
+    if (!resid || fallback) return p;
+    const double q = dense_prob<ET>(Key<ET>::load_key(qp, v), thrB, zB, invT, iB);
+    return fmax(p - q, 0.0);
+  };
+  bool fallback = false;
+  double zl = 0.0;
+  for (int v = threadIdx.x; v < V; v += NT) zl += weight(v, false);
+  double Z = block_sum(zl, s.red_d);
+  if (!(Z > 0.0)) {
+    fallback = true;
+    zl = 0.0;
+    for (int v = threadIdx.x; v < V; v += NT) zl += weight(v, true);
+    Z = block_sum(zl, s.red_d);
+  }
+  const double target = (double)ures * Z;
+  // Ascending vocabulary order: each thread takes 8 consecutive ids per tile.
+  constexpr int PER = 8;
+  double base = 0.0;
+  int lastpos = -1;
+  for (int t0 = 0; t0 < V; t0 += NT * PER) {
+    const int v0 = t0 + (int)threadIdx.x * PER;
+    double w[PER];
+    double loc = 0.0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      w[e] = (v0 + e < V) ? weight(v0 + e, fallback) : 0.0;
+      loc += w[e];
+      if (w[e] > 0.0) lastpos = v0 + e;
+    }
+    double tot;
+    const double ex = block_excl_scan(loc, s.red_d, &tot);
+    double c = base + ex;
+    uint32_t hit = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      c += w[e];
+      if (hit == 0xFFFFFFFFu && v0 + e < V && c > target) hit = (uint32_t)(v0 + e);
+    }
+    hit = block_min_u32(hit, s.red_u);
+    if (hit != 0xFFFFFFFFu) return (int)hit;
+    base += tot;
+  }
+  return (int)block_max_u32((uint32_t)(lastpos + 1), s.red_u) - 1;
+}
+
+
+// ===========================================================================
+// The finisher kernel: one workgroup per sequence.
+// ===========================================================================
+template <typename ET, bool VECTOR>
+__device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
+  const Mode m = seq_mode(a, b);
+  const int RS = 2 * a.G + 1;
+  const int G = a.G;
+  const int R = 2 * m.g + 1;
+  const int wave = threadIdx.x >> 6;
+  bool ok = m.mode != MODE_INVALID;
+  const int gl = a.gamma_len ? a.gamma_len[b] : G;
+  ok = ok && gl >= 1 && gl <= G;
+  ok = ok && !(m.tp != m.tp);
+  const float* ub = a.u + (size_t)b * (G + 1);
+  const int32_t* xb = a.draft + (size_t)b * G;
+  {
+    uint32_t badin = 0;
+    for (int i = threadIdx.x; i < m.g; i += NT) {
+      const int x = xb[i];
+      const float ui = ub[i];
+      badin |= (x < 0 || x >= a.V || !(ui >= 0.0f && ui < 1.0f)) ? 1u : 0u;
+    }
+    if (threadIdx.x == 0) badin |= !(ub[G] >= 0.0f && ub[G] < 1.0f) ? 1u : 0u;
+    ok = ok && block_or_u32(badin, s.red_u) == 0;
+  }
+  bool dense = m.mode == MODE_DENSE;
+  if (ok && !dense) {
+    uint32_t fl = 0, empty = 0;
+    for (int r = threadIdx.x; r < R; r += NT) {
+      const RowInfo& ri = a.rows[b * RS + used_slot(G, m.g, r)];
+      fl |= ri.flags;
+      const int ns = ri.nsurv;
+      empty |= ns <= 0 ? 1u : 0u;
+      s.off[r + 1] = (uint32_t)max(ns, 0);
+    }
+    fl = block_or_u32(fl, s.red_u);
+    empty = block_or_u32(empty, s.red_u);
+    if (fl & F_BAD) ok = false;
+    else if (fl & F_DEMOTE) dense = true;
+    else if (empty) ok = false;    // a row with no finite logit
+    if (ok && !dense) {
+      if (threadIdx.x == 0) {
+        s.off[0] = 0;
+        for (int r = 0; r < R; ++r) s.off[r + 1] += s.off[r];
+        // Room for the residual weights after the survivors.
+        s.flag = s.off[R] + (s.off[m.g + 1] - s.off[m.g]) > (uint32_t)POOL ? 1u : 0u;
+        uint32_t mx = 0;
+        for (int r = 0; r < R; ++r) mx = max(mx, s.off[r + 1] - s.off[r]);
+        if (s.off[R] + mx > (uint32_t)POOL) s.flag = 1u;
+      }
+      __syncthreads();
+      if (s.flag) dense = true;   // does not fit in LDS: multi-pass path
+      __syncthreads();
+    }
+  }
+  if (ok && !dense) {
+    // All survivor lists in one round trip.
+    const uint32_t total = s.off[R];
+    for (uint32_t e = threadIdx.x; e < total; e += NT) {
+      int lo = 0, hi = R;   // find r with off[r] <= e < off[r+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s.off[mid] <= e) lo = mid;
+        else hi = mid;
+      }
+      const int rowid = b * RS + used_slot(G, m.g, lo);
+      s.pool[e] = a.cand[(size_t)rowid * RCAP + (e - s.off[lo])];
+    }
+    __syncthreads();
+    for (int r = wave; r < R; r += NWAVE) wave_row_stats<ET>(s, r, (int)s.off[r], (int)(s.off[r + 1] - s.off[r]), m);
+    __syncthreads();
+    for (int i = wave; i < m.g; i += NWAVE) wave_position(s, i, xb[i], m);
+    __syncthreads();
+  } else if (ok && dense) {
+    ok = dense_row_stats<ET, VECTOR>(a, s, b, m);
+    if (ok) dense_positions<ET, VECTOR>(a, s, b, m);
+  }
+  int n = 0, tok = -1;
+  if (ok) {
+    // Acceptance of each draft, then the first rejection via one ballot.
+    if (threadIdx.x < 64) {
+      const int i = threadIdx.x;
+      bool rej = false;
+      if (i < m.g) rej = !((double)ub[i] * s.pos_q[i] < s.pos_p[i]);
+      const unsigned long long mask = __ballot(rej);
+      if (i == 0) s.bc[7] = mask ? (uint32_t)(__ffsll((long long)mask) - 1) : (uint32_t)m.g;
+    }
+    __syncthreads();
+    n = (int)s.bc[7];
+    __syncthreads();
+    tok = dense ? dense_draw<ET, VECTOR>(a, s, b, m, n, ub[G]) : pool_draw(s, m, n, ub[G]);
+  }
+  int32_t* ot = a.out_tokens + (size_t)b * (G + 1);
+  float* oa = a.out_alpha + (size_t)b * G;
+  for (int i = threadIdx.x; i <= G; i += NT) ot[i] = ok ? (i < n ? xb[i] : (i == n ? tok : -1)) : -1;
+  const float qnan = __int_as_float(0x7FC00000);
+  for (int i = threadIdx.x; i < G; i += NT) {
+    oa[i] = ok ? (i < m.g ? (float)s.pos_alpha[i] : 0.0f) : qnan;
+    if (a.out_pq) {
+      float* op = a.out_pq + ((size_t)b * G + i) * 2;
+      op[0] = ok ? (i < m.g ? (float)s.pos_p[i] : 0.0f) : qnan;
+      op[1] = ok ? (i < m.g ? (float)s.pos_q[i] : 0.0f) : qnan;
+    }
+  }
+  if (threadIdx.x == 0) a.out_n[b] = ok ? n : -1;
+  // Leave the rows' records cleared for the next call.
+  for (int r = threadIdx.x; r < R; r += NT) {
+    RowInfo& ri = a.rows[b * RS + used_slot(G, m.g, r)];
+    ri.cnt = 0;
+    ri.thr = 0;
+    ri.flags = 0;
+    ri.nsurv = 0;
+  }
+}
+
+template <typename ET, bool VECTOR>
+__global__ __launch_bounds__(NT) void finish_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char fin_smem_raw[];
+  FinSmem& s = *reinterpret_cast<FinSmem*>(fin_smem_raw);
+  finish_sequence<ET, VECTOR>(a, s, blockIdx.x);
+}
+
+}  // namespace sv

@@ -1,0 +1,96 @@
+"""The C ABI library: it loads, exports every entry point declared in
+include/spec_verify.h, and rejects bad arguments on the host before touching
+the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_sampling_verification_verify_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def _ensure_built():
+    if not os.path.exists(binding.LIB_PATH):
+        from speculative_sampling_verification_verify_amd import build
+        build.build_library()
+    return binding.lib()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(spec_verify\w*)\s*\(", txt, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _ensure_built()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert binding.spec_verify_version() == 1
+
+
+def test_workspace_bytes():
+    _ensure_built()
+    ws = binding.spec_verify_workspace_bytes
+    assert ws(256, 7, 152064, binding.SV_BF16) > 0
+    assert ws(256, 7, 152064, binding.SV_BF16) >= ws(128, 7, 152064, binding.SV_BF16)
+    assert ws(1, 1, 1, binding.SV_FP32) > 0
+    assert ws(0, 4, 100, binding.SV_BF16) > 0
+    for bad in [(-1, 4, 100, 0), (4, 0, 100, 0), (4, 65, 100, 0), (4, 4, 0, 0), (4, 4, (1 << 20) + 1, 0),
+                (4, 4, 100, 7)]:
+        assert ws(*bad) == 0, bad
+
+
+def test_host_argument_errors():
+    L = _ensure_built()
+    fake = ctypes.c_void_p(0x100000)   # never dereferenced: every case below fails on the host
+    nul = None
+    B, G, V = 2, 3, 64
+    need = binding.spec_verify_workspace_bytes(B, G, V, binding.SV_BF16)
+
+    def call(p=fake, q=fake, dt=binding.SV_BF16, draft=fake, u=fake, temp=fake, B=B, G=G, V=V, out=fake,
+             ws=fake, wsb=need):
+        return L.spec_verify(p, q, dt, draft, nul, u, temp, nul, nul, B, G, V, out, out, out, nul, ws, wsb, nul)
+
+    assert call(dt=5) == binding.SV_ERR_UNSUPPORTED
+    assert call(G=65) == binding.SV_ERR_UNSUPPORTED
+    assert call(V=(1 << 20) + 1) == binding.SV_ERR_UNSUPPORTED
+    assert call(G=0) == binding.SV_ERR_ARG
+    assert call(V=0) == binding.SV_ERR_ARG
+    assert call(B=-3) == binding.SV_ERR_ARG
+    assert call(p=nul) == binding.SV_ERR_ARG
+    assert call(draft=nul) == binding.SV_ERR_ARG
+    assert call(u=nul) == binding.SV_ERR_ARG
+    assert call(temp=nul) == binding.SV_ERR_ARG
+    assert call(out=nul) == binding.SV_ERR_ARG
+    assert call(p=ctypes.c_void_p(0x100001)) == binding.SV_ERR_ARG          # misaligned bf16
+    assert call(ws=nul) == binding.SV_ERR_WORKSPACE
+    assert call(wsb=need - 1) == binding.SV_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == binding.SV_ERR_WORKSPACE   # not 256-byte aligned
+    assert call(B=0) == binding.SV_OK                                         # empty batch: nothing to do
+    rc = L.spec_verify_workspace_init(nul, 0, B, G, V, binding.SV_BF16, nul)
+    assert rc == binding.SV_ERR_WORKSPACE
+    assert L.spec_verify_workspace_init(fake, need, B, 0, V, binding.SV_BF16, nul) == binding.SV_ERR_ARG
+
+
+def test_strerror():
+    _ensure_built()
+    for code in (0, -1, -2, -3, -4, 17):
+        assert isinstance(binding.spec_verify_strerror(code), str)
+    assert "workspace" in binding.spec_verify_strerror(binding.SV_ERR_WORKSPACE)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

@@ -1,0 +1,259 @@
+"""GPU path (through the C ABI) against the CPU oracle on the same seeded
+inputs.  n_accepted and every token must be identical except in rows whose
+oracle decision margin is below 1e-5; overlap and p(x), q(x) must agree
+within 1e-5 absolute."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from speculative_sampling_verification_verify_amd import synth
+from gpu_util import TOL, compare, log, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def batch_from(bt, **over):
+    d = {f.name: getattr(bt, f.name) for f in dataclasses.fields(bt)}
+    for k, v in over.items():
+        d[k] = v
+    return synth.Batch(**d)
+
+
+def check(bt, label):
+    log(f"[parity] {label}: B={bt.B} V={bt.V} gamma_max={bt.gamma_max} dtype={bt.p_logits.dtype}")
+    g = run_gpu(bt)
+    ref = run_oracle(bt)
+    rep = compare(bt, g, ref, label)
+    log(f"[parity] {label}: ok {rep}")
+    return g, ref, rep
+
+
+# --------------------------------------------------------------------------
+# The five workloads, small instances that still span several chunks and a
+# ragged tail, then the full sizes.
+# --------------------------------------------------------------------------
+SMALL = [
+    (0, 1000, None),     # all 1000 single-sequence rounds, fp32, V = 1000
+    (1, 8, None),        # unfiltered, T = 0.8, V = 32000
+    (2, 8, 40000),       # top-k 50 over 3 chunks
+    (3, 8, None),        # top-k 64, V = 152064: 10 chunks in 2 parts
+    (4, 24, 20000),      # mixed gamma / temperature, top-p 0.9
+    (3, 6, 50001),       # odd V: scalar load path
+    (0, 16, 1001),       # odd V, fp32
+    (2, 5, 16391),       # one chunk plus a 7-element tail... of a second chunk
+]
+
+
+@pytest.mark.parametrize("cid,B,V", SMALL)
+def test_workload_small(cid, B, V):
+    bt = synth.make_batch(cid, B=B, V=V)
+    check(bt, f"workload{cid}-B{B}-V{bt.V}")
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
+def test_workload_full_size(cid):
+    bt = synth.make_batch(cid)
+    _, ref, rep = check(bt, f"workload{cid}-full")
+    log(f"[parity] workload{cid}-full: mean alpha {np.nanmean(ref.alpha[ref.alpha > 0]):.3f}, "
+        f"mean tokens/round {np.mean(ref.n[ref.n >= 0] + 1):.3f}, near-margin rows {rep.near}, "
+        f"of which differ {rep.near_differ}")
+
+
+# --------------------------------------------------------------------------
+# Edge cases.
+# --------------------------------------------------------------------------
+def _bf(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_invalid_rows_get_sentinels():
+    bt = synth.make_batch(3, B=12, V=9000)
+    P, Q = bt.p_logits.copy(), bt.q_logits.copy()
+    d, u, T, gl, tp = bt.draft.copy(), bt.u.copy(), bt.temperature.copy(), bt.gamma_len.copy(), bt.top_p.copy()
+    P[0, 1, 17] = 0x7FC0                 # NaN
+    Q[1, 0, 5] = 0x7F80                  # +inf
+    d[2, 3] = bt.V                       # token out of range
+    T[3] = -1.0                          # negative temperature
+    gl[4] = 0                            # gamma_b out of range
+    u[5, 2] = 1.0                        # uniform not in [0, 1)
+    P[6, 0, :] = 0xFF80                  # a row of only -inf
+    tp[7] = np.nan                       # NaN top_p
+    Q[8, 6, 100] = 0xFFC1                # negative NaN
+    u[9, bt.gamma_max] = -0.25           # bad residual uniform
+    T[10] = np.nan
+    bt2 = batch_from(bt, p_logits=P, q_logits=Q, draft=d, u=u, temperature=T, gamma_len=gl, top_p=tp)
+    g, ref, _ = check(bt2, "invalid")
+    assert (ref.n[:11] == -1).all() and ref.n[11] >= 0
+    assert (g.n[:11] == -1).all() and g.n[11] >= 0
+
+
+def test_padding_rows_never_read():
+    bt = synth.make_batch(4, B=16, V=6000)
+    P, Q = bt.p_logits.copy(), bt.q_logits.copy()
+    d = bt.draft.copy()
+    for b in range(bt.B):
+        gb = int(bt.gamma_len[b])
+        P[b, gb + 1:] = 0x7FC0           # NaN beyond the used target rows
+        Q[b, gb:] = 0x7FC0
+        d[b, gb:] = -5
+    check(batch_from(bt, p_logits=P, q_logits=Q, draft=d), "padding")
+
+
+@pytest.mark.parametrize("mode", ["greedy", "topk", "topp", "dense"])
+def test_ties_and_neg_inf(mode):
+    rng = np.random.default_rng(77)
+    B, G, V = 10, 4, 3000
+    zp = rng.integers(-6, 7, size=(B, G + 1, V)).astype(np.float32)   # integers: heavy ties
+    zq = zp[:, :G] + rng.integers(-1, 2, size=(B, G, V)).astype(np.float32)
+    zp[:, :, : V // 3] = -np.inf                                       # masked vocabulary
+    zq[:, :, V // 2: V // 2 + 50] = -np.inf
+    T = {"greedy": 0.0, "topk": 0.9, "topp": 1.1, "dense": 0.7}[mode]
+    k = {"greedy": 0, "topk": 40, "topp": 0, "dense": 0}[mode]
+    tp = {"greedy": 1.0, "topk": 1.0, "topp": 0.8, "dense": 1.0}[mode]
+    bt = synth.make_batch(3, B=B, V=V)
+    draft = np.argmax(zq, axis=2).astype(np.int32)
+    draft[::2, 1] = rng.integers(V // 3, V, size=(B + 1) // 2)
+    bt2 = synth.Batch(bt.workload, _bf(zp), _bf(zq), draft, synth.uniforms(5, B, G), np.full(B, G, np.int32),
+                      np.full(B, T, np.float32), np.full(B, k, np.int32), np.full(B, tp, np.float32), 5)
+    check(bt2, f"ties-{mode}")
+
+
+def test_topk_boundaries_and_noop_filters():
+    bt = synth.make_batch(3, B=12, V=20000)
+    k = np.array([1, 2, 63, 64, 65, 511, 512, 513, 19999, 20000, 0, -3], np.int32)
+    T = np.full(12, 0.8, np.float32)
+    check(batch_from(bt, top_k=k, temperature=T), "topk-range")
+
+
+def test_topp_extremes():
+    bt = synth.make_batch(4, B=16, V=7000)
+    tp = np.array([0.0, -1.0, 1e-6, 0.5, 0.9, 0.99, 0.999999, 1.0, 2.0, 0.3, 0.95, 0.1, 0.7, 0.8, 0.6, 0.05],
+                  np.float32)
+    T = np.where(bt.temperature == 0, np.float32(1.0), bt.temperature)
+    k = np.where(np.arange(16) % 3 == 0, 30, 0).astype(np.int32)      # top-k then top-p on some rows
+    check(batch_from(bt, top_p=tp, temperature=T, top_k=k), "topp-range")
+
+
+def test_massive_ties_go_to_multipass():
+    bt = synth.make_batch(3, B=4, V=12000)
+    P, Q = bt.p_logits.copy(), bt.q_logits.copy()
+    P[0, :, :] = _bf(1.5)                # every logit equal: top-k keeps the whole row
+    Q[1, 2, :] = _bf(-0.5)
+    P[2, 3, 4000:9000] = _bf(20.0)       # 5000 tied maxima
+    check(batch_from(bt, p_logits=P, q_logits=Q), "massive-ties")
+
+
+def test_sorted_rows_overflow_recovery():
+    # Increasing logits along the vocabulary: every chunk beats the bound of
+    # the previous ones, so the candidate buffer overflows and recovers.
+    bt = synth.make_batch(3, B=4, V=152064)
+    P, Q = bt.p_logits.copy(), bt.q_logits.copy()
+    ramp = np.linspace(-20, 20, bt.V, dtype=np.float32)
+    P[0, :, :] = _bf(ramp)[None, :]
+    Q[0, :, :] = _bf(ramp + 0.01)[None, :]
+    P[1, :, :] = _bf(ramp[::-1].copy())[None, :]
+    k = bt.top_k.copy()
+    k[:] = 400
+    check(batch_from(bt, p_logits=P, q_logits=Q, top_k=k), "sorted-rows")
+
+
+def test_large_gamma():
+    bt = synth.make_batch(4, B=6, V=3000)
+    w = dataclasses.replace(bt.workload, gamma_max=64)
+    rng = np.random.default_rng(3)
+    B, G, V = 6, 64, 3000
+    zp = (3 * rng.normal(size=(B, G + 1, V))).astype(np.float32)
+    zq = zp[:, :G] + rng.normal(size=(B, G, V)).astype(np.float32) * 0.1
+    draft = np.argmax(zq, axis=2).astype(np.int32)
+    gl = np.array([64, 1, 33, 64, 17, 2], np.int32)
+    T = np.array([0.0, 0.7, 1.0, 0.5, 0.0, 1.2], np.float32)
+    k = np.array([0, 20, 0, 5, 0, 0], np.int32)
+    tp = np.array([1.0, 1.0, 0.9, 1.0, 1.0, 0.5], np.float32)
+    bt2 = synth.Batch(w, _bf(zp), _bf(zq), draft, synth.uniforms(11, B, G), gl, T, k, tp, 11)
+    check(bt2, "gamma64")
+
+
+def test_tiny_vocabulary():
+    for V in (1, 2, 7):
+        bt = synth.make_batch(0, B=40, V=V)
+        check(bt, f"tiny-V{V}")
+
+
+# --------------------------------------------------------------------------
+# Call-level properties.
+# --------------------------------------------------------------------------
+def test_deterministic_and_workspace_reuse():
+    from speculative_sampling_verification_verify_amd import binding
+    a = synth.make_batch(3, B=6, V=40000)
+    b = synth.make_batch(3, B=6, V=40000, seed=99)
+    ver = binding.Verifier(6, a.gamma_max, 40000, binding.SV_BF16)
+    ga1 = run_gpu(a, verifier=ver)
+    gb = run_gpu(b, verifier=ver)
+    ga2 = run_gpu(a, verifier=ver)
+    for f in ("tokens", "n", "alpha", "pq"):
+        assert np.array_equal(getattr(ga1, f), getattr(ga2, f), equal_nan=True), f
+    compare(b, gb, run_oracle(b), "reuse-b")
+    compare(a, ga1, run_oracle(a), "reuse-a")
+
+
+def test_null_gamma_and_filters():
+    bt = synth.make_batch(3, B=5, V=30000)
+    g = run_gpu(bt, pass_gamma=False)
+    compare(bt, g, run_oracle(bt), "null-gamma")
+    bt2 = batch_from(bt, top_k=np.zeros(5, np.int32), top_p=np.ones(5, np.float32))
+    g2 = run_gpu(bt2, with_params=False)
+    compare(bt2, g2, run_oracle(bt2), "null-filters")
+
+
+# --------------------------------------------------------------------------
+# Distributional checks on the GPU outputs themselves.
+# --------------------------------------------------------------------------
+def test_gpu_output_follows_target_chi_square():
+    from scipy import stats
+    rng = np.random.default_rng(2024)
+    N, G, V = 40000, 2, 8
+    zp = (1.5 * rng.normal(size=(G + 1, V))).astype(np.float32)
+    zq = (zp[:G] + 1.2 * rng.normal(size=(G, V))).astype(np.float32)
+    sm = lambda z: np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+    Pd = np.stack([sm(zp[j].astype(np.float64)) for j in range(G + 1)])
+    Qd = np.stack([sm(zq[i].astype(np.float64)) for i in range(G)])
+    draft = np.stack([np.searchsorted(np.cumsum(Qd[i]), rng.random(N), side="right") for i in range(G)], 1)
+    draft = np.minimum(draft, V - 1).astype(np.int32)
+    bt = synth.make_batch(0, B=2, V=V)
+    bt2 = synth.Batch(bt.workload, np.broadcast_to(zp, (N, G + 1, V)).copy(),
+                      np.broadcast_to(zq, (N, G, V)).copy(), draft, rng.random((N, G + 1)).astype(np.float32),
+                      np.full(N, G, np.int32), np.ones(N, np.float32), np.zeros(N, np.int32),
+                      np.ones(N, np.float32), 0)
+    g = run_gpu(bt2)
+    obs = np.bincount(g.tokens[:, 0], minlength=V)
+    p1 = stats.chisquare(obs, Pd[0] * N).pvalue
+    sel = g.n >= 1
+    obs2 = np.bincount(g.tokens[sel, 1], minlength=V)
+    p2 = stats.chisquare(obs2, Pd[1] * sel.sum()).pvalue
+    log(f"[stat] chi-square p-values: first token {p1:.3g}, second token {p2:.3g}")
+    assert p1 > 1e-4 and p2 > 1e-4
+    alpha_exact = np.minimum(Pd[:G], Qd).sum(axis=1)
+    assert np.abs(g.alpha.astype(np.float64) - alpha_exact[None, :]).max() < TOL
+
+
+def test_gpu_tokens_per_round_law():
+    rng = np.random.default_rng(5)
+    N, G, V = 40000, 5, 4
+    alpha = 0.8
+    p = np.array([alpha, 1 - alpha, 0, 0])
+    q = np.array([alpha, 0, 1 - alpha, 0])
+    with np.errstate(divide="ignore"):
+        zp = np.log(p).astype(np.float32)
+        zq = np.log(q).astype(np.float32)
+    draft = np.where(rng.random((N, G)) < alpha, 0, 2).astype(np.int32)
+    bt = synth.make_batch(0, B=2, V=V)
+    bt2 = synth.Batch(bt.workload, np.broadcast_to(zp, (N, G + 1, V)).copy(), np.broadcast_to(zq, (N, G, V)).copy(),
+                      draft, rng.random((N, G + 1)).astype(np.float32), np.full(N, G, np.int32),
+                      np.ones(N, np.float32), np.zeros(N, np.int32), np.ones(N, np.float32), 0)
+    g = run_gpu(bt2)
+    mean = (g.n + 1.0).mean()
+    expect = (1 - alpha ** (G + 1)) / (1 - alpha)     # 3.69 in the page's table
+    sem = (g.n + 1.0).std() / np.sqrt(N)
+    log(f"[stat] tokens per round {mean:.4f} vs {expect:.4f} (sem {sem:.4f})")
+    assert abs(mean - expect) < 4 * sem

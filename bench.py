@@ -1,0 +1,204 @@
+"""Benchmark of the batched speculative-sampling verify step on one MI355X.
+
+One step = one spec_verify call over one batch of synthetic inputs that are
+already resident in HBM.  The default workload is the headline one:
+B = 256 sequences, V = 152064, gamma = 7, bf16 logits, temperature 0.7,
+top-k 64 (1.17 GB of logits per call).
+
+Prints one JSON line with verify-rows/s (a row is one sequence), the select
+kernel's achieved HBM bandwidth against the 8 TB/s peak (timed with HIP
+events recorded around that kernel on the call's stream), and the CPU
+oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from speculative_sampling_verification_verify_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "spec-verify rows/sec + achieved HBM GB/s vs peak at B=256,V=152064,γ=7"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_B256_V152064_g7_pmc.txt")
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """Per-launch HBM bytes (read, write) of the select kernel from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(kv["hbm_read_bytes_per_launch"]) + float(kv["hbm_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(bt, seconds_target: float, cores: int):
+    """Time the CPU oracle (as it stands) on whole sequences of the same
+    workload, in worker processes (fork) on `cores` host cores."""
+    import oracle
+    # Estimate the per-sequence cost on a few sequences, then size the sample.
+    t0 = time.perf_counter()
+    oracle.verify_batch(bt.p_logits, bt.q_logits, bt.draft, bt.u, bt.temperature, bt.top_k, bt.top_p,
+                        bt.gamma_len, rows=range(2), processes=1)
+    per_seq = max((time.perf_counter() - t0) / 2, 1e-4)
+    n = int(min(bt.B, max(cores, seconds_target / per_seq)))
+    rows = list(range(n))
+    t0 = time.perf_counter()
+    oracle.verify_batch(bt.p_logits, bt.q_logits, bt.draft, bt.u, bt.temperature, bt.top_k, bt.top_p,
+                        bt.gamma_len, rows=rows, processes=cores)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} sequences of the same workload (float64 numpy oracle, {cores} worker processes, "
+                      f"{dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (3 = headline)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the verify step on one GPU; runs on more than one GPU are not supported "
+              "(sequences shard across GPUs with no exchange, so per-GPU throughput is the figure).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        import torch
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}))
+        return
+
+    t_gen = time.perf_counter()
+    bt = synth.make_batch(args.workload)
+    t_gen = time.perf_counter() - t_gen
+    alg_bytes = synth.algorithmic_bytes(bt)
+    logit_bytes = int((2 * bt.gamma_len.astype(np.int64) + 1).sum()) * bt.V * bt.p_logits.itemsize
+
+    # CPU baseline first: worker processes are forked before the GPU is touched.
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cores = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            cores = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(bt, args.cpu_seconds, cores)
+
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+
+    dev = torch.device("cuda:0")
+    if bt.p_logits.dtype == np.uint16:
+        P = torch.from_numpy(bt.p_logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        Q = torch.from_numpy(bt.q_logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        dt_code, dtype_name = binding.SV_BF16, "bf16"
+    else:
+        P = torch.from_numpy(bt.p_logits).to(dev)
+        Q = torch.from_numpy(bt.q_logits).to(dev)
+        dt_code, dtype_name = binding.SV_FP32, "fp32"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    draft, u, temp, topk, topp, gl = (t(bt.draft), t(bt.u), t(bt.temperature), t(bt.top_k), t(bt.top_p),
+                                      t(bt.gamma_len))
+    ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt_code, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        ver(P, Q, draft, u, temp, topk, topp, gl)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Events around the select kernel of every timed call (same stream).
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in evs:     # materialise the underlying hipEvent_t handles
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        binding.spec_verify_set_stage_events(a, b)
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    binding.spec_verify_set_stage_events(None, None)
+    sel_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / K
+
+    n_acc = ver.n_accepted.cpu().numpy()
+    alpha = ver.alpha.cpu().numpy()
+    sel_avg = float(sel_ms.mean())
+    achieved = logit_bytes / (sel_avg * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    w = bt.workload
+    out = {
+        "metric": METRIC,
+        "value": bt.B / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": bt.B, "V": bt.V, "gamma": bt.gamma_max,
+                   "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
+                   "logit_bytes_per_call": logit_bytes, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "select_kernel", "kernel_avg_us": sel_avg * 1e3,
+                     "kernel_p10_us": float(np.percentile(sel_ms, 10) * 1e3),
+                     "kernel_p90_us": float(np.percentile(sel_ms, 90) * 1e3)},
+        "cpu_baseline": cpu,
+        "extra": {"call_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+                  "logit_rows_per_s": int((2 * bt.gamma_len.astype(np.int64) + 1).sum()) / (ms_per_step * 1e-3),
+                  "mean_alpha": float(alpha[alpha > 0].mean()) if (alpha > 0).any() else None,
+                  "mean_tokens_per_round": float((n_acc[n_acc >= 0] + 1).mean()),
+                  "input_generation_s": t_gen},
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

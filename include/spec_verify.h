@@ -120,6 +120,16 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
                 int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement hook (for benchmarks and profilers, not needed for normal use).
+ * With non-NULL hipEvent_t handles `begin` and `end`, every later spec_verify
+ * call made from this host thread records `begin` on its stream just before
+ * the streaming select kernel and `end` just after it, so that
+ * hipEventElapsedTime(begin, end) is that kernel's duration.  The caller owns
+ * the events.  Passing NULL, NULL stops the recording.  Returns SV_OK.
+ */
+int spec_verify_set_stage_events(void* begin, void* end);
+
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 

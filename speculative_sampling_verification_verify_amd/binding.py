@@ -22,7 +22,7 @@ SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify",
-            "spec_verify_strerror", "spec_verify_version")
+            "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_strerror.restype = ctypes.c_char_p
         L.spec_verify_version.argtypes = []
         L.spec_verify_version.restype = i
+        L.spec_verify_set_stage_events.argtypes = [vp, vp]
+        L.spec_verify_set_stage_events.restype = i
         _lib = L
     return _lib
 
@@ -84,6 +86,14 @@ def spec_verify_strerror(code: int) -> str:
 
 def spec_verify_version() -> int:
     return int(lib().spec_verify_version())
+
+
+def spec_verify_set_stage_events(begin, end) -> None:
+    """Record hipEvent_t handles (ints, or torch.cuda.Event already recorded
+    once) around the streaming select kernel of the following calls; pass
+    None, None to stop."""
+    h = lambda e: None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    lib().spec_verify_set_stage_events(h(begin), h(end))
 
 
 def spec_verify_workspace_init(workspace: torch.Tensor, B: int, gamma_max: int, V: int, dtype: int,

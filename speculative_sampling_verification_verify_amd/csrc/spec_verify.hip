@@ -26,6 +26,7 @@
 
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 namespace sv {
@@ -57,6 +58,7 @@ static Layout layout(int B, int G) {
 }
 
 static thread_local char g_errbuf[256];
+static thread_local hipEvent_t g_stage_begin = nullptr, g_stage_end = nullptr;
 
 template <typename ET, bool VECTOR>
 static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
@@ -67,9 +69,17 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  if (g_stage_begin) {
+    hipError_t e = hipEventRecord(g_stage_begin, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (g_stage_end) {
+    e = hipEventRecord(g_stage_end, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((finish_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), fin_lds, st, a);
   return hipGetLastError();
 }
@@ -124,10 +134,15 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   const int NC = (V + chunk_max - 1) / chunk_max;
   int L = (V + NC - 1) / NC;
   L = (L + vec - 1) / vec * vec;
-  // Rows longer than a few chunks are split into parts of about five chunks
-  // so that the grid has enough workgroups to balance across compute units.
-  const int NP = (NC + 4) / 5;
+  // Rows can be split into NP parts (one workgroup each); the default is
+  // one part per row.  SPEC_VERIFY_PARTS / SPEC_VERIFY_CHECK_EVERY override
+  // the schedule for A/B measurements.
+  int NP = 1, check_every = 4;
+  if (const char* e = getenv("SPEC_VERIFY_PARTS")) NP = atoi(e) > 0 ? atoi(e) : NP;
+  if (const char* e = getenv("SPEC_VERIFY_CHECK_EVERY")) check_every = atoi(e) > 0 ? atoi(e) : check_every;
+  NP = NP > MAXNP ? MAXNP : (NP > NC ? NC : NP);
   const int CPP = (NC + NP - 1) / NP;
+  NP = (NC + CPP - 1) / CPP;
   const long long grid = rows * NP;
   if (grid > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
   const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)q_logits % 16 == 0);
@@ -150,6 +165,8 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   a.L = L;
   a.NP = NP;
   a.CPP = CPP;
+  a.seg = RCAP / NP;
+  a.sync = check_every;
   a.fixbits = 62 - vb;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
@@ -184,3 +201,9 @@ extern "C" const char* spec_verify_strerror(int code) {
 }
 
 extern "C" int spec_verify_version(void) { return 1; }
+
+extern "C" int spec_verify_set_stage_events(void* begin, void* end) {
+  g_stage_begin = (hipEvent_t)begin;
+  g_stage_end = (hipEvent_t)end;
+  return SV_OK;
+}

@@ -9,13 +9,11 @@ namespace sv {
 
 enum { MODE_INVALID = 0, MODE_GREEDY = 1, MODE_SPARSE = 2, MODE_DENSE = 3 };
 
-struct RowInfo {      // 32 bytes per logit row (workspace)
-  uint32_t done;      // completion ticket over the row's parts
-  uint32_t cnt;       // candidates appended by the parts
-  uint32_t thr;       // certified lower bound on the row's k-th largest key (0 = none)
-  uint32_t flags;     // F_BAD | F_DEMOTE
-  int32_t nsurv;      // survivors after the row's exact selection
-  uint32_t pad[3];
+constexpr int MAXNP = 7;   // parts per logit row
+
+struct RowInfo {              // 32 bytes per logit row (workspace)
+  uint32_t flags;             // F_BAD | F_DEMOTE, from any part
+  int32_t nsurv[MAXNP];       // candidates each part left in its segment of the row's list
 };
 
 struct Args {
@@ -28,8 +26,10 @@ struct Args {
   const int32_t* topk;
   const float* topp;
   int B, G, V;
-  int NC, L;          // chunks per row, chunk length in elements
+  int NC, L;          // chunks per row, chunk length in elements (a multiple of the vector width)
   int NP, CPP;        // parts per row, chunks per part
+  int seg;            // list entries per part (RCAP / NP)
+  int sync;           // chunks between candidate-buffer check points
   int fixbits;        // fixed-point fraction bits for mass sums
   int32_t* out_tokens;
   int32_t* out_n;
@@ -91,26 +91,6 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
 
 __device__ __forceinline__ uint32_t atomic_load_u32(uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Every thread of the block calls this.  Returns true in the one workgroup
-// that makes the total-th arrival, after resetting the counter for the next
-// call; its global writes made before the call are visible to that
-// workgroup (release/acquire at device scope).
-__device__ __forceinline__ bool block_ticket(uint32_t* counter, uint32_t total, uint32_t* s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t last = (t == total - 1) ? 1u : 0u;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last;
-  }
-  __syncthreads();
-  const bool last = *s_flag != 0;
-  __syncthreads();
-  if (last) __threadfence();
-  return last;
 }
 
 }  // namespace sv

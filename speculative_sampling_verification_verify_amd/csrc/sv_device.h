@@ -15,7 +15,7 @@ namespace sv {
 constexpr int NT = 512;          // threads per workgroup (8 wavefronts)
 constexpr int NWAVE = NT / 64;
 constexpr int VPL = 4;           // 16-byte vectors held per lane per chunk
-constexpr int CCAP = 2048;       // candidate slots per chunk (LDS)
+constexpr int CCAP = 2048;       // candidate slots per workgroup (LDS)
 constexpr int RCAP = 2048;       // candidate slots per logit row (workspace)
 constexpr int KMAX_SPARSE = 512; // largest top-k handled by the streaming select
 constexpr uint32_t NONE = 0xFFFFFFFFu;
@@ -220,6 +220,62 @@ __device__ __forceinline__ uint32_t block_kth_largest(Feed feed, uint32_t k, uin
     const uint32_t d = bc[0], r = bc[1];
     __syncthreads();
     if (d == NONE) return 0;
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+    krem = r;
+  }
+  return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront radix select: like block_kth_largest, for the keys the calling
+// wavefront's lanes feed; hist is the wavefront's private 256-word LDS
+// histogram.  No block barrier.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int LEVELS, class Feed>
+__device__ __forceinline__ uint32_t wave_kth(Feed feed, uint32_t k, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0, krem = k;
+  for (int lvl = 0; lvl < LEVELS; ++lvl) {
+    const int shift = 8 * (LEVELS - 1 - lvl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0;
+    wave_sync_lds();
+    feed([&](uint32_t key) {
+      if (key != 0 && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
+    wave_sync_lds();
+    const int top = 255 - 4 * lane;
+    const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+    const uint32_t sum = c0 + c1 + c2 + c3;
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t excl = incl - sum;
+    const bool hit = excl < krem && incl >= krem;
+    const unsigned long long any = __ballot(hit);
+    wave_sync_lds();
+    if (any == 0ull) return 0;
+    uint32_t d = 0, r = 0;
+    if (hit) {
+      r = krem - excl;
+      if (c0 >= r) {
+        d = top;
+      } else if (c0 + c1 >= r) {
+        d = top - 1; r -= c0;
+      } else if (c0 + c1 + c2 >= r) {
+        d = top - 2; r -= c0 + c1;
+      } else {
+        d = top - 3; r -= c0 + c1 + c2;
+      }
+    }
+    const int src = __ffsll((long long)any) - 1;
+    d = (uint32_t)__shfl((int)d, src, 64);
+    r = (uint32_t)__shfl((int)r, src, 64);
     prefix |= d << shift;
     pmask |= 255u << shift;
     krem = r;

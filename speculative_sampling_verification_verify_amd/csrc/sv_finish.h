@@ -25,10 +25,13 @@ struct FinSmem {
   uint2 pool[POOL];                             // (key, id) of every survivor of the sequence
   double pe[POOL];                              // exp((z - zmax) / T) per survivor
   uint32_t off[MAXROWS + 1];                    // pool offset of each used row
+  uint32_t soff[MAXROWS * MAXNP + 1];           // pool offset of each (row, part) segment
+  uint32_t whist[NWAVE][256];                   // per-wavefront radix histograms
   uint32_t st_thr[MAXROWS];                     // kept keys are >= st_thr
   uint32_t st_arg[MAXROWS];                     // argmax (T == 0)
   float st_zmax[MAXROWS];
   double st_S[MAXROWS];                         // normaliser over the kept keys
+  double st_invS[MAXROWS];
   double pos_p[SV_MAX_GAMMA];
   double pos_q[SV_MAX_GAMMA];
   double pos_alpha[SV_MAX_GAMMA];
@@ -53,13 +56,69 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // Sparse path.
 // ===========================================================================
 
+// The k-th largest key (1-based) of ents[0, n) by one wavefront, with a
+// wave-private 256-bin histogram; 0 when n < k.
+template <int LEVELS>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint2* ents, int n, uint32_t k, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0, krem = k;
+  for (int lvl = 0; lvl < LEVELS; ++lvl) {
+    const int shift = 8 * (LEVELS - 1 - lvl);
+    for (int i = lane; i < 256; i += 64) hist[i] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < n; i += 64) {
+      const uint32_t key = ents[i].x;
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int top = 255 - 4 * lane;
+    const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+    const uint32_t sum = c0 + c1 + c2 + c3;
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t excl = incl - sum;
+    const bool hit = excl < krem && incl >= krem;
+    const unsigned long long any = __ballot(hit);
+    if (any == 0ull) return 0;
+    uint32_t d = 0, r = 0;
+    if (hit) {
+      r = krem - excl;
+      if (c0 >= r) {
+        d = top;
+      } else if (c0 + c1 >= r) {
+        d = top - 1; r -= c0;
+      } else if (c0 + c1 + c2 >= r) {
+        d = top - 2; r -= c0 + c1;
+      } else {
+        d = top - 3; r -= c0 + c1 + c2;
+      }
+    }
+    const int src = __ffsll((long long)any) - 1;
+    d = (uint32_t)__shfl((int)d, src, 64);
+    r = (uint32_t)__shfl((int)r, src, 64);
+    prefix |= d << shift;
+    pmask |= 255u << shift;
+    krem = r;
+    __builtin_amdgcn_wave_barrier();
+  }
+  return prefix;
+}
+
 // Statistics of one row from its pool range [o, o+n), by one wavefront.
+// The range is the union of the row's part segments; the row's kept set is
+// every key >= the k-th largest of the union (ties kept).
 template <typename ET>
 __device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, const Mode& m) {
   const int lane = threadIdx.x & 63;
+  uint32_t* hist = s.whist[threadIdx.x >> 6];
+  const uint32_t kth = n > (int)m.k ? wave_kth_largest<Key<ET>::LEVELS>(s.pool + o, n, m.k, hist) : 1u;
   if (m.mode == MODE_GREEDY) {
     uint32_t best = 0xFFFFFFFFu;
-    for (int i = lane; i < n; i += 64) best = min(best, s.pool[o + i].y);
+    for (int i = lane; i < n; i += 64)
+      if (s.pool[o + i].x >= kth) best = min(best, s.pool[o + i].y);
     best = wave_min_u32(best);
     if (lane == 0) s.st_arg[r] = best;
     return;
@@ -71,12 +130,13 @@ __device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, 
   const float zmax = Key<ET>::value(kmax);
   double S = 0.0;
   for (int i = lane; i < n; i += 64) {
-    const double e = exp(((double)Key<ET>::value(s.pool[o + i].x) - (double)zmax) / T);
+    const uint32_t key = s.pool[o + i].x;
+    const double e = key >= kth ? exp(((double)Key<ET>::value(key) - (double)zmax) / T) : 0.0;
     s.pe[o + i] = e;
     S += e;
   }
   S = wave_sum_d(S);
-  uint32_t thr = 1;
+  uint32_t thr = kth;
   if (m.tp < 1.0f) {
     // The nucleus: order survivors by (value desc, id asc); the cut is the
     // first position whose running mass reaches top_p; every value >= the
@@ -86,11 +146,12 @@ __device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, 
     uint32_t cut_rank = 0xFFFFFFFFu, cut_key = 0;
     for (int i = lane; i < n; i += 64) {
       const uint2 e = s.pool[o + i];
+      if (e.x < kth) continue;
       uint32_t rank = 0;
       double run = 0.0;
       for (int j = 0; j < n; ++j) {
         const uint2 f = s.pool[o + j];
-        const bool before = (f.x > e.x) || (f.x == e.x && f.y <= e.y);
+        const bool before = f.x >= kth && ((f.x > e.x) || (f.x == e.x && f.y <= e.y));
         rank += before && f.y != e.y ? 1u : 0u;
         if (before) run += s.pe[o + j];
       }
@@ -104,7 +165,7 @@ __device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, 
     const unsigned long long who = __ballot(cut_rank == best && best != 0xFFFFFFFFu);
     if (best != 0xFFFFFFFFu) {
       const int src = __ffsll((long long)who) - 1;
-      thr = (uint32_t)__shfl((int)cut_key, src, 64);
+      thr = max(kth, (uint32_t)__shfl((int)cut_key, src, 64));
       double S2 = 0.0;
       for (int i = lane; i < n; i += 64)
         if (s.pool[o + i].x >= thr) S2 += s.pe[o + i];
@@ -115,20 +176,22 @@ __device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, 
     s.st_thr[r] = thr;
     s.st_zmax[r] = zmax;
     s.st_S[r] = S;
+    s.st_invS[r] = 1.0 / S;
   }
 }
 
-// Probability of pool entry i of row r (0 when cut by top-p).
+// Probability of pool entry i of row r (0 when cut by top-k / top-p).
 __device__ __forceinline__ double pool_prob(const FinSmem& s, int r, int i) {
-  return s.pool[i].x >= s.st_thr[r] ? s.pe[i] / s.st_S[r] : 0.0;
+  return s.pool[i].x >= s.st_thr[r] ? s.pe[i] * s.st_invS[r] : 0.0;
 }
 
-// Probability of vocabulary id v in row r (linear search of its pool range).
+// Probability of vocabulary id v in row r.  Every lane of the wave walks the
+// same entries (broadcast LDS reads, no early exit), so the loop pipelines.
 __device__ __forceinline__ double pool_lookup(const FinSmem& s, int r, uint32_t v) {
   const int o = (int)s.off[r], e = (int)s.off[r + 1];
-  for (int j = o; j < e; ++j)
-    if (s.pool[j].y == v) return pool_prob(s, r, j);
-  return 0.0;
+  int hit = -1;
+  for (int j = o; j < e; ++j) hit = s.pool[j].y == v ? j : hit;
+  return hit >= 0 ? pool_prob(s, r, hit) : 0.0;
 }
 
 // p_i(x_i), q_i(x_i) and alpha_i for one position, by one wavefront.
@@ -536,46 +599,52 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   }
   bool dense = m.mode == MODE_DENSE;
   if (ok && !dense) {
-    uint32_t fl = 0, empty = 0;
-    for (int r = threadIdx.x; r < R; r += NT) {
+    // Segment sizes: (row r, part p) -> soff[r * NP + p + 1].
+    const int NPp = a.NP;
+    uint32_t fl = 0;
+    for (int i = threadIdx.x; i < R * NPp; i += NT) {
+      const int r = i / NPp, p = i - r * NPp;
       const RowInfo& ri = a.rows[b * RS + used_slot(G, m.g, r)];
-      fl |= ri.flags;
-      const int ns = ri.nsurv;
-      empty |= ns <= 0 ? 1u : 0u;
-      s.off[r + 1] = (uint32_t)max(ns, 0);
+      if (p == 0) fl |= ri.flags;
+      s.soff[i + 1] = (uint32_t)max(ri.nsurv[p], 0);
     }
     fl = block_or_u32(fl, s.red_u);
-    empty = block_or_u32(empty, s.red_u);
     if (fl & F_BAD) ok = false;
     else if (fl & F_DEMOTE) dense = true;
-    else if (empty) ok = false;    // a row with no finite logit
     if (ok && !dense) {
       if (threadIdx.x == 0) {
-        s.off[0] = 0;
-        for (int r = 0; r < R; ++r) s.off[r + 1] += s.off[r];
-        // Room for the residual weights after the survivors.
-        s.flag = s.off[R] + (s.off[m.g + 1] - s.off[m.g]) > (uint32_t)POOL ? 1u : 0u;
-        uint32_t mx = 0;
-        for (int r = 0; r < R; ++r) mx = max(mx, s.off[r + 1] - s.off[r]);
-        if (s.off[R] + mx > (uint32_t)POOL) s.flag = 1u;
+        s.soff[0] = 0;
+        for (int i = 0; i < R * NPp; ++i) s.soff[i + 1] += s.soff[i];
+        uint32_t mx = 0, empty = 0;
+        for (int r = 0; r <= R; ++r) s.off[r] = s.soff[r * NPp];
+        for (int r = 0; r < R; ++r) {
+          mx = max(mx, s.off[r + 1] - s.off[r]);
+          empty |= s.off[r + 1] == s.off[r] ? 1u : 0u;
+        }
+        // The pool also holds one row's residual weights after the survivors.
+        s.flag = (s.off[R] + mx > (uint32_t)POOL ? 1u : 0u) | (empty ? 2u : 0u);
       }
       __syncthreads();
-      if (s.flag) dense = true;   // does not fit in LDS: multi-pass path
+      const uint32_t f = s.flag;
       __syncthreads();
+      if (f & 2u) ok = false;          // a row with no finite logit
+      else if (f & 1u) dense = true;   // does not fit in LDS: multi-pass path
     }
   }
   if (ok && !dense) {
-    // All survivor lists in one round trip.
-    const uint32_t total = s.off[R];
+    // All candidate segments in one round trip.
+    const int NS = R * a.NP;
+    const uint32_t total = s.soff[NS];
     for (uint32_t e = threadIdx.x; e < total; e += NT) {
-      int lo = 0, hi = R;   // find r with off[r] <= e < off[r+1]
+      int lo = 0, hi = NS;   // segment with soff[lo] <= e < soff[lo+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s.off[mid] <= e) lo = mid;
+        if (s.soff[mid] <= e) lo = mid;
         else hi = mid;
       }
-      const int rowid = b * RS + used_slot(G, m.g, lo);
-      s.pool[e] = a.cand[(size_t)rowid * RCAP + (e - s.off[lo])];
+      const int r = lo / a.NP, p = lo - r * a.NP;
+      const int rowid = b * RS + used_slot(G, m.g, r);
+      s.pool[e] = a.cand[(size_t)rowid * RCAP + (size_t)p * a.seg + (e - s.soff[lo])];
     }
     __syncthreads();
     for (int r = wave; r < R; r += NWAVE) wave_row_stats<ET>(s, r, (int)s.off[r], (int)(s.off[r + 1] - s.off[r]), m);
@@ -617,10 +686,9 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   // Leave the rows' records cleared for the next call.
   for (int r = threadIdx.x; r < R; r += NT) {
     RowInfo& ri = a.rows[b * RS + used_slot(G, m.g, r)];
-    ri.cnt = 0;
-    ri.thr = 0;
     ri.flags = 0;
-    ri.nsurv = 0;
+#pragma unroll
+    for (int p = 0; p < MAXNP; ++p) ri.nsurv[p] = 0;
   }
 }
 

@@ -2,15 +2,16 @@
 // the C ABI.
 //
 // A call is two launches on the caller's stream:
-//   1. select_kernel -- one workgroup per (logit row, row part) of every
-//      top-k / argmax sequence: streams the row once from HBM with 16-byte
-//      non-temporal loads and leaves the exact kept set (top-k survivors,
-//      ties included) in the workspace.  See sv_select.h.
-//   2. finish_kernel -- one workgroup per sequence: normalisers, top-p,
-//      p(x) and q(x), the overlap, the acceptance test with the first
-//      rejection found by one wavefront ballot, and the residual / bonus
-//      draw; unfiltered and top-p sequences are computed here from the
-//      logits by a multi-pass procedure.  See sv_finish.h.
+//   1. select_kernel -- one wavefront per (logit row, row part) of every
+//      top-k / argmax sequence: streams the part once from HBM with 16-byte
+//      non-temporal loads and writes its exact kept set (top-k survivors,
+//      ties included) to the workspace.  See sv_wave.h.
+//   2. finish_kernel -- one workgroup per sequence: for top-k / argmax
+//      sequences, merges the part lists of every row and computes the
+//      normalisers, top-p cut, p(x), q(x), overlap, the first rejection (one
+//      wavefront ballot) and the residual / bonus draw from the lists; for
+//      unfiltered and top-p sequences (and lists that overflowed), runs a
+//      multi-pass procedure over the logits.  See sv_finish.h.
 //
 // Definitions followed (page titles and sections): the acceptance rule and
 // the residual, "Fast Inference from Transformers via Speculative Decoding"
@@ -21,7 +22,7 @@
 // the inverse-CDF draw, same page, "Sampling with shared noise"; the overlap
 // alpha = sum min(p, q), mtandhj summary, "How to choose gamma".
 
-#include "sv_select.h"
+#include "sv_wave.h"
 #include "sv_finish.h"
 
 #include <math.h>
@@ -38,22 +39,47 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-struct Layout {
-  size_t rows_off, cand_off, total, counters_bytes;
-};
-
 static bool sizes_ok(int B, int G, int V) {
   return B >= 0 && G >= 1 && G <= SV_MAX_GAMMA && V >= 1 && V <= SV_MAX_VOCAB;
 }
 
-static Layout layout(int B, int G) {
+struct Plan {
+  int NP;     // parts per logit row
+  int PL;     // part length in elements
+};
+
+// Parts per row: enough units to give every SIMD of the chip about four
+// wavefronts (256 CUs x 4 SIMDs x 4), with at least two steps per part.
+static Plan plan(int B, int G, int V, int dtype) {
+  const int vec = dtype == SV_BF16 ? 8 : 4;
+  const int step = 64 * WVPL * vec;
+  const long long R = (long long)B * (2 * G + 1);
+  long long np = R > 0 ? 4096 / R : 1;
+  np = np < 1 ? 1 : np;
+  np = np > MAXNP ? MAXNP : np;
+  const long long by_len = V / (2 * step);
+  if (np > by_len) np = by_len < 1 ? 1 : by_len;
+  Plan p;
+  int pl = (int)((V + np - 1) / np);
+  pl = (pl + vec - 1) / vec * vec;
+  p.PL = pl;
+  p.NP = (V + pl - 1) / pl;
+  return p;
+}
+
+struct Layout {
+  size_t seq_flags_off, counters_bytes, counts_off, lists_off, total;
+};
+
+static Layout layout(int B, int G, const Plan& p) {
   Layout L;
   const size_t R = (size_t)B * (2 * G + 1);
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  L.rows_off = 0;
-  L.cand_off = up(R * sizeof(RowInfo));
-  L.counters_bytes = L.cand_off;
-  L.total = L.cand_off + R * RCAP * sizeof(uint2);
+  L.seq_flags_off = 0;
+  L.counters_bytes = up(L.seq_flags_off + (size_t)B * 4);
+  L.counts_off = L.counters_bytes;
+  L.lists_off = up(L.counts_off + R * p.NP * 4);
+  L.total = L.lists_off + R * p.NP * SEG * sizeof(uint2);
   return L;
 }
 
@@ -62,19 +88,24 @@ static thread_local hipEvent_t g_stage_begin = nullptr, g_stage_end = nullptr;
 
 template <typename ET, bool VECTOR>
 static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_kernel<ET, VECTOR>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
+  // The finisher's LDS exceeds the default dynamic limit; raise it once per
+  // device.
+  static int attr_dev[64];   // 1 + device ordinal once set
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && attr_dev[dev] != dev + 1) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_kernel<ET, VECTOR>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_dev[dev] = dev + 1;
   }
   if (g_stage_begin) {
-    hipError_t e = hipEventRecord(g_stage_begin, st);
+    e = hipEventRecord(g_stage_begin, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(NT), 0, st, a);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g_stage_end) {
     e = hipEventRecord(g_stage_end, st);
@@ -91,7 +122,7 @@ using namespace sv;
 extern "C" size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype) {
   if (!sizes_ok(B, gamma_max, V) || (dtype != SV_BF16 && dtype != SV_FP32)) return 0;
   if (B == 0) return 256;
-  return layout(B, gamma_max).total;
+  return layout(B, gamma_max, plan(B, gamma_max, V, dtype)).total;
 }
 
 extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
@@ -100,7 +131,7 @@ extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_byte
   if (need == 0) return SV_ERR_ARG;
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
   if (B == 0) return SV_OK;
-  const Layout L = layout(B, gamma_max);
+  const Layout L = layout(B, gamma_max, plan(B, gamma_max, V, dtype));
   const size_t n = L.counters_bytes / 4;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
                      (hipStream_t)stream, (uint32_t*)workspace, n);
@@ -128,27 +159,17 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   if (((uintptr_t)p_logits % es) || ((uintptr_t)q_logits % es)) return SV_ERR_ARG;
   const size_t need = spec_verify_workspace_bytes(B, gamma_max, V, dtype);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256)) return SV_ERR_WORKSPACE;
+  const Plan pl = plan(B, gamma_max, V, dtype);
   const long long rows = (long long)B * (2 * gamma_max + 1);
+  const long long units = rows * pl.NP;
+  const long long grid = (units + K1_WAVES - 1) / K1_WAVES;
+  if (grid > 0x7FFFFFFFLL || units > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
   const int vec = dtype == SV_BF16 ? 8 : 4;
-  const int chunk_max = NT * VPL * vec;
-  const int NC = (V + chunk_max - 1) / chunk_max;
-  int L = (V + NC - 1) / NC;
-  L = (L + vec - 1) / vec * vec;
-  // Rows can be split into NP parts (one workgroup each); the default is
-  // one part per row.  SPEC_VERIFY_PARTS / SPEC_VERIFY_CHECK_EVERY override
-  // the schedule for A/B measurements.
-  int NP = 1, check_every = 4;
-  if (const char* e = getenv("SPEC_VERIFY_PARTS")) NP = atoi(e) > 0 ? atoi(e) : NP;
-  if (const char* e = getenv("SPEC_VERIFY_CHECK_EVERY")) check_every = atoi(e) > 0 ? atoi(e) : check_every;
-  NP = NP > MAXNP ? MAXNP : (NP > NC ? NC : NP);
-  const int CPP = (NC + NP - 1) / NP;
-  NP = (NC + CPP - 1) / CPP;
-  const long long grid = rows * NP;
-  if (grid > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
   const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)q_logits % 16 == 0);
   int vb = 0;
   while ((1LL << vb) < (long long)V + 1) ++vb;
-  const Layout Lw = layout(B, gamma_max);
+  const Layout Lw = layout(B, gamma_max, pl);
+  char* ws = (char*)workspace;
   Args a;
   a.p = p_logits;
   a.q = q_logits;
@@ -161,19 +182,16 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   a.B = B;
   a.G = gamma_max;
   a.V = V;
-  a.NC = NC;
-  a.L = L;
-  a.NP = NP;
-  a.CPP = CPP;
-  a.seg = RCAP / NP;
-  a.sync = check_every;
+  a.NP = pl.NP;
+  a.PL = pl.PL;
   a.fixbits = 62 - vb;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
   a.out_alpha = out_alpha;
   a.out_pq = out_pq;
-  a.rows = reinterpret_cast<RowInfo*>((char*)workspace + Lw.rows_off);
-  a.cand = reinterpret_cast<uint2*>((char*)workspace + Lw.cand_off);
+  a.seq_flags = reinterpret_cast<uint32_t*>(ws + Lw.seq_flags_off);
+  a.counts = reinterpret_cast<int32_t*>(ws + Lw.counts_off);
+  a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);
   hipStream_t st = (hipStream_t)stream;
   const size_t fin_lds = sizeof(FinSmem);
   hipError_t e = hipSuccess;

@@ -1,5 +1,5 @@
-// Shared definitions of the verify kernels: workspace records, call
-// arguments, per-sequence mode, row addressing, completion tickets.
+// Shared definitions of the verify kernels: call arguments, per-sequence
+// mode, row addressing and workspace records.
 #pragma once
 
 #include "sv_device.h"
@@ -9,12 +9,12 @@ namespace sv {
 
 enum { MODE_INVALID = 0, MODE_GREEDY = 1, MODE_SPARSE = 2, MODE_DENSE = 3 };
 
-constexpr int MAXNP = 7;   // parts per logit row
+constexpr int SEG = 1024;          // survivor slots per (logit row, row part) in the workspace
+constexpr int MAXNP = 16;          // parts per logit row
 
-struct RowInfo {              // 32 bytes per logit row (workspace)
-  uint32_t flags;             // F_BAD | F_DEMOTE, from any part
-  int32_t nsurv[MAXNP];       // candidates each part left in its segment of the row's list
-};
+// Sequence flags (workspace, one word per sequence).
+constexpr uint32_t F_BAD = 1u;     // NaN or +inf among the logits
+constexpr uint32_t F_DEMOTE = 2u;  // survivor lists unusable: recompute from the logits
 
 struct Args {
   const void* p;
@@ -26,17 +26,16 @@ struct Args {
   const int32_t* topk;
   const float* topp;
   int B, G, V;
-  int NC, L;          // chunks per row, chunk length in elements (a multiple of the vector width)
-  int NP, CPP;        // parts per row, chunks per part
-  int seg;            // list entries per part (RCAP / NP)
-  int sync;           // chunks between candidate-buffer check points
+  int NP;             // parts per logit row (streaming select)
+  int PL;             // part length in elements (a multiple of the vector width)
   int fixbits;        // fixed-point fraction bits for mass sums
   int32_t* out_tokens;
   int32_t* out_n;
   float* out_alpha;
   float* out_pq;
-  RowInfo* rows;
-  uint2* cand;        // [rows][RCAP] (key, vocabulary id)
+  uint32_t* seq_flags;    // [B]     F_* bits, set by the select, cleared by the finisher
+  int32_t* counts;        // [R][NP] survivors per (row, part)
+  uint2* lists;           // [R][NP][SEG] (key, vocabulary id)
 };
 
 struct Mode {
@@ -82,15 +81,15 @@ __device__ __forceinline__ const ET* row_ptr(const Args& a, int b, bool isP, int
 // target positions, g+1..2g the draft positions.
 __device__ __forceinline__ int used_slot(int G, int g, int r) { return r <= g ? r : G + 1 + (r - g - 1); }
 
+__device__ __forceinline__ size_t list_index(const Args& a, int rowid, int part) {
+  return ((size_t)rowid * a.NP + part) * SEG;
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t atomic_load_u32(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sv

@@ -14,15 +14,8 @@ namespace sv {
 
 constexpr int NT = 512;          // threads per workgroup (8 wavefronts)
 constexpr int NWAVE = NT / 64;
-constexpr int VPL = 4;           // 16-byte vectors held per lane per chunk
-constexpr int CCAP = 2048;       // candidate slots per workgroup (LDS)
-constexpr int RCAP = 2048;       // candidate slots per logit row (workspace)
 constexpr int KMAX_SPARSE = 512; // largest top-k handled by the streaming select
 constexpr uint32_t NONE = 0xFFFFFFFFu;
-
-// Row flags (workspace).
-constexpr uint32_t F_BAD = 1u;      // NaN or +inf seen
-constexpr uint32_t F_DEMOTE = 2u;   // candidate overflow: sequence goes to the multi-pass path
 
 template <typename ET> struct Key;
 
@@ -274,8 +267,8 @@ __device__ __forceinline__ uint32_t wave_kth(Feed feed, uint32_t k, uint32_t* hi
       }
     }
     const int src = __ffsll((long long)any) - 1;
-    d = (uint32_t)__shfl((int)d, src, 64);
-    r = (uint32_t)__shfl((int)r, src, 64);
+    d = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
+    r = (uint32_t)__builtin_amdgcn_readlane((int)r, src);
     prefix |= d << shift;
     pmask |= 255u << shift;
     krem = r;

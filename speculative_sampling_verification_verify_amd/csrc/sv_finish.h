@@ -1,33 +1,39 @@
 // Per-sequence finisher: acceptance, first rejection, overlap, residual or
-// bonus draw.
+// bonus draw.  One workgroup (NT threads) per sequence.
 //
-// Sparse sequences (top-k / argmax) work from the survivor lists written by
-// the streaming select: all lists of the sequence are brought into LDS in one
-// round trip, then each wavefront takes whole rows (normalisers, top-p cut)
-// and whole positions (p(x), q(x), overlap) without block-wide barriers.
-// Probabilities over survivors are evaluated in double precision.
+// Top-k and argmax sequences work from the survivor lists left by the
+// streaming select: every (row, part) list of the sequence is brought into
+// LDS in one round trip; then each wavefront takes whole rows (the row's
+// exact kept set from the union of its part lists, normaliser, top-p cut)
+// and whole positions (p(x), q(x), overlap), and one wavefront takes the
+// acceptance test and the draw.  Entries are broadcast to the wavefront
+// through registers (readlane), so the all-pairs loops over a row's
+// survivors do not wait on LDS once per entry.
 //
-// Dense sequences (no top-k, top-p, or lists that overflowed) run a
-// multi-pass procedure over the logits in one workgroup: maximum, count-based
-// radix select for top-k, mass-weighted radix select for top-p (fixed-point
-// 64-bit masses, so the result does not depend on summation order),
-// normalisers, overlap, and a tiled inverse-CDF scan in ascending id order.
+// Sequences without top-k (or whose lists overflowed) run a multi-pass
+// procedure over the logits in one workgroup: maximum, count-based radix
+// select for top-k, mass-weighted radix select for top-p (fixed-point 64-bit
+// masses, so the result does not depend on summation order), normalisers,
+// overlap, and a tiled inverse-CDF scan in ascending id order.
 #pragma once
 
 #include "sv_common.h"
 
 namespace sv {
 
-constexpr int POOL = 8192;                      // survivor entries of one sequence held in LDS
+constexpr int POOL = 4096;                      // survivor entries of one sequence held in LDS
 constexpr int MAXROWS = 2 * SV_MAX_GAMMA + 1;
+constexpr int MAXSEG = 512;                     // (row, part) lists of one sequence on the list path
 
 struct FinSmem {
   uint2 pool[POOL];                             // (key, id) of every survivor of the sequence
-  double pe[POOL];                              // exp((z - zmax) / T) per survivor
+  float pv[POOL];                               // exp((z - zmax) / T) per kept survivor
+  float wts[POOL];                              // residual / bonus weights of the drawn row
+  uint32_t soff[MAXSEG + 1];                    // pool offset of each (row, part) list
   uint32_t off[MAXROWS + 1];                    // pool offset of each used row
-  uint32_t soff[MAXROWS * MAXNP + 1];           // pool offset of each (row, part) segment
   uint32_t whist[NWAVE][256];                   // per-wavefront radix histograms
-  uint32_t st_thr[MAXROWS];                     // kept keys are >= st_thr
+  uint32_t st_thr[MAXROWS];                     // kept keys are >= st_thr (multi-pass path)
+  uint32_t st_cnt[MAXROWS];                     // kept survivors of each row (list path)
   uint32_t st_arg[MAXROWS];                     // argmax (T == 0)
   float st_zmax[MAXROWS];
   double st_S[MAXROWS];                         // normaliser over the kept keys
@@ -53,110 +59,122 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 // ===========================================================================
-// Sparse path.
+// List path.
 // ===========================================================================
+
+// fn(key, id, val) for every entry of ents[o, o+n) in order, seen by every
+// lane of the wavefront through readlane (no LDS access per entry).  Must be
+// called with the whole wavefront active and wavefront-uniform o, n.
+template <class F>
+__device__ __forceinline__ void wave_broadcast(const uint2* ents, const float* vals, int o, int n, F fn) {
+  const int lane = threadIdx.x & 63;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + lane;
+    const uint2 e = i < n ? ents[o + i] : make_uint2(0u, 0u);
+    const float v = i < n ? vals[o + i] : 0.0f;
+    const int m = min(64, n - b);
+    for (int l = 0; l < m; ++l) {
+      const uint32_t key = (uint32_t)__builtin_amdgcn_readlane((int)e.x, l);
+      const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)e.y, l);
+      const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+      fn(key, id, val);
+    }
+  }
+}
 
 // The k-th largest key (1-based) of ents[0, n) by one wavefront, with a
 // wave-private 256-bin histogram; 0 when n < k.
 template <int LEVELS>
 __device__ __forceinline__ uint32_t wave_kth_largest(const uint2* ents, int n, uint32_t k, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0, pmask = 0, krem = k;
-  for (int lvl = 0; lvl < LEVELS; ++lvl) {
-    const int shift = 8 * (LEVELS - 1 - lvl);
-    for (int i = lane; i < 256; i += 64) hist[i] = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int i = lane; i < n; i += 64) {
-      const uint32_t key = ents[i].x;
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int top = 255 - 4 * lane;
-    const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
-    const uint32_t sum = c0 + c1 + c2 + c3;
-    const uint32_t incl = wave_incl_scan(sum);
-    const uint32_t excl = incl - sum;
-    const bool hit = excl < krem && incl >= krem;
-    const unsigned long long any = __ballot(hit);
-    if (any == 0ull) return 0;
-    uint32_t d = 0, r = 0;
-    if (hit) {
-      r = krem - excl;
-      if (c0 >= r) {
-        d = top;
-      } else if (c0 + c1 >= r) {
-        d = top - 1; r -= c0;
-      } else if (c0 + c1 + c2 >= r) {
-        d = top - 2; r -= c0 + c1;
-      } else {
-        d = top - 3; r -= c0 + c1 + c2;
-      }
-    }
-    const int src = __ffsll((long long)any) - 1;
-    d = (uint32_t)__shfl((int)d, src, 64);
-    r = (uint32_t)__shfl((int)r, src, 64);
-    prefix |= d << shift;
-    pmask |= 255u << shift;
-    krem = r;
-    __builtin_amdgcn_wave_barrier();
-  }
-  return prefix;
+  return wave_kth<LEVELS>(
+      [&](auto fn) {
+        for (int i = lane; i < n; i += 64) fn(ents[i].x);
+      },
+      k, hist);
 }
 
-// Statistics of one row from its pool range [o, o+n), by one wavefront.
-// The range is the union of the row's part segments; the row's kept set is
-// every key >= the k-th largest of the union (ties kept).
-template <typename ET>
-__device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, const Mode& m) {
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Keep the entries of [o, o+n) (pool and pv together) whose key is >= t, in
+// order, at the start of the range; returns their number.
+__device__ __forceinline__ int wave_keep(FinSmem& s, int o, int n, uint32_t t) {
   const int lane = threadIdx.x & 63;
+  int outn = 0;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + lane;
+    const uint2 e = i < n ? s.pool[o + i] : make_uint2(0u, 0u);
+    const float v = i < n ? s.pv[o + i] : 0.0f;
+    const bool keep = i < n && e.x >= t;
+    const unsigned long long bal = __ballot(keep);
+    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    if (keep) {
+      const int d = o + outn + __popcll(bal & below);
+      s.pool[d] = e;
+      s.pv[d] = v;
+    }
+    outn += __popcll(bal);
+  }
+  wave_lds_sync();
+  return outn;
+}
+
+// Statistics of row r, by one wavefront.  The row's kept set is every key >=
+// the k-th largest of the union of its part lists (ties kept), then cut by
+// top-p when asked for; it is left compacted at the start of the row's pool
+// range (cnt[r] entries, exp((z - zmax) / T) of each in pv) with its
+// normaliser.
+template <typename ET>
+__device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m) {
+  const int lane = threadIdx.x & 63;
+  const int o = (int)s.off[r];
+  int n = (int)(s.off[r + 1] - s.off[r]);
   uint32_t* hist = s.whist[threadIdx.x >> 6];
   const uint32_t kth = n > (int)m.k ? wave_kth_largest<Key<ET>::LEVELS>(s.pool + o, n, m.k, hist) : 1u;
+  uint32_t kmax = 0;
+  for (int i = lane; i < n; i += 64) kmax = max(kmax, s.pool[o + i].x);
+  kmax = wave_max_u32(kmax);
   if (m.mode == MODE_GREEDY) {
     uint32_t best = 0xFFFFFFFFu;
     for (int i = lane; i < n; i += 64)
-      if (s.pool[o + i].x >= kth) best = min(best, s.pool[o + i].y);
+      if (s.pool[o + i].x == kmax) best = min(best, s.pool[o + i].y);
     best = wave_min_u32(best);
     if (lane == 0) s.st_arg[r] = best;
     return;
   }
-  const double T = (double)m.T;
-  uint32_t kmax = 0;
-  for (int i = lane; i < n; i += 64) kmax = max(kmax, s.pool[o + i].x);
-  kmax = wave_max_u32(kmax);
+  const float invT = 1.0f / m.T;
   const float zmax = Key<ET>::value(kmax);
+  n = wave_keep(s, o, n, kth);
   double S = 0.0;
   for (int i = lane; i < n; i += 64) {
-    const uint32_t key = s.pool[o + i].x;
-    const double e = key >= kth ? exp(((double)Key<ET>::value(key) - (double)zmax) / T) : 0.0;
-    s.pe[o + i] = e;
-    S += e;
+    const float e = expf((Key<ET>::value(s.pool[o + i].x) - zmax) * invT);
+    s.pv[o + i] = e;
+    S += (double)e;
   }
   S = wave_sum_d(S);
-  uint32_t thr = kth;
+  wave_lds_sync();
   if (m.tp < 1.0f) {
-    // The nucleus: order survivors by (value desc, id asc); the cut is the
-    // first position whose running mass reaches top_p; every value >= the
-    // value there is kept.  Running mass of entry i = mass of all entries
-    // ordered at or before it.
+    // The nucleus: order the survivors by (value desc, id asc); the cut is
+    // the first entry whose running mass reaches top_p; every value >= the
+    // cut's value is kept.
     const double target = (double)m.tp * S;
     uint32_t cut_rank = 0xFFFFFFFFu, cut_key = 0;
-    for (int i = lane; i < n; i += 64) {
-      const uint2 e = s.pool[o + i];
-      if (e.x < kth) continue;
+    for (int b = 0; b < n; b += 64) {
+      const int i = b + lane;
+      const uint2 e = i < n ? s.pool[o + i] : make_uint2(0u, 0u);
       uint32_t rank = 0;
       double run = 0.0;
-      for (int j = 0; j < n; ++j) {
-        const uint2 f = s.pool[o + j];
-        const bool before = f.x >= kth && ((f.x > e.x) || (f.x == e.x && f.y <= e.y));
-        rank += before && f.y != e.y ? 1u : 0u;
-        if (before) run += s.pe[o + j];
-      }
+      wave_broadcast(s.pool, s.pv, o, n, [&](uint32_t key, uint32_t id, float val) {
+        const bool before = key > e.x || (key == e.x && id <= e.y);
+        rank += (before && id != e.y) ? 1u : 0u;
+        run += before ? (double)val : 0.0;
+      });
       const bool reach = m.tp <= 0.0f ? rank == 0 : run >= target;
-      if (reach && rank < cut_rank) {
+      if (i < n && reach && rank < cut_rank) {
         cut_rank = rank;
         cut_key = e.x;
       }
@@ -165,33 +183,19 @@ __device__ __forceinline__ void wave_row_stats(FinSmem& s, int r, int o, int n, 
     const unsigned long long who = __ballot(cut_rank == best && best != 0xFFFFFFFFu);
     if (best != 0xFFFFFFFFu) {
       const int src = __ffsll((long long)who) - 1;
-      thr = max(kth, (uint32_t)__shfl((int)cut_key, src, 64));
+      const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)cut_key, src);
+      n = wave_keep(s, o, n, thr);
       double S2 = 0.0;
-      for (int i = lane; i < n; i += 64)
-        if (s.pool[o + i].x >= thr) S2 += s.pe[o + i];
+      for (int i = lane; i < n; i += 64) S2 += (double)s.pv[o + i];
       S = wave_sum_d(S2);
     }
   }
   if (lane == 0) {
-    s.st_thr[r] = thr;
+    s.st_cnt[r] = (uint32_t)n;
     s.st_zmax[r] = zmax;
     s.st_S[r] = S;
     s.st_invS[r] = 1.0 / S;
   }
-}
-
-// Probability of pool entry i of row r (0 when cut by top-k / top-p).
-__device__ __forceinline__ double pool_prob(const FinSmem& s, int r, int i) {
-  return s.pool[i].x >= s.st_thr[r] ? s.pe[i] * s.st_invS[r] : 0.0;
-}
-
-// Probability of vocabulary id v in row r.  Every lane of the wave walks the
-// same entries (broadcast LDS reads, no early exit), so the loop pipelines.
-__device__ __forceinline__ double pool_lookup(const FinSmem& s, int r, uint32_t v) {
-  const int o = (int)s.off[r], e = (int)s.off[r + 1];
-  int hit = -1;
-  for (int j = o; j < e; ++j) hit = s.pool[j].y == v ? j : hit;
-  return hit >= 0 ? pool_prob(s, r, hit) : 0.0;
 }
 
 // p_i(x_i), q_i(x_i) and alpha_i for one position, by one wavefront.
@@ -206,20 +210,23 @@ __device__ __forceinline__ void wave_position(FinSmem& s, int i, int x, const Mo
     }
     return;
   }
-  const int o = (int)s.off[rp], e = (int)s.off[rp + 1];
-  double al = 0.0, px = 0.0;
-  for (int j = o + lane; j < e; j += 64) {
-    const double pv = pool_prob(s, rp, j);
-    const uint32_t v = s.pool[j].y;
-    if (v == (uint32_t)x) px = pv;
-    if (pv > 0.0) al += fmin(pv, pool_lookup(s, rq, v));
+  const int op = (int)s.off[rp], np = (int)s.st_cnt[rp];
+  const int oq = (int)s.off[rq], nq = (int)s.st_cnt[rq];
+  const double ip = s.st_invS[rp], iq = s.st_invS[rq];
+  double al = 0.0, px = 0.0, qx = 0.0;
+  for (int b = 0; b < np; b += 64) {
+    const int j = b + lane;
+    const uint32_t id = j < np ? s.pool[op + j].y : 0xFFFFFFFFu;
+    const double pv = j < np ? (double)s.pv[op + j] * ip : 0.0;
+    float qe = 0.0f;
+    wave_broadcast(s.pool, s.pv, oq, nq, [&](uint32_t, uint32_t qid, float val) { qe = qid == id ? val : qe; });
+    if (id == (uint32_t)x) px = pv;
+    al += fmin(pv, (double)qe * iq);
   }
+  for (int j = lane; j < nq; j += 64)
+    if (s.pool[oq + j].y == (uint32_t)x) qx = (double)s.pv[oq + j] * iq;
   al = wave_sum_d(al);
   px = wave_sum_d(px);
-  double qx = 0.0;
-  const int oq = (int)s.off[rq], eq = (int)s.off[rq + 1];
-  for (int j = oq + lane; j < eq; j += 64)
-    if (s.pool[j].y == (uint32_t)x) qx = pool_prob(s, rq, j);
   qx = wave_sum_d(qx);
   if (lane == 0) {
     s.pos_p[i] = px;
@@ -228,52 +235,50 @@ __device__ __forceinline__ void wave_position(FinSmem& s, int i, int x, const Mo
   }
 }
 
-// Residual (n < g) or bonus (n == g) draw from the pool, whole block.
+// Residual (n < g) or bonus (n == g) draw from the lists, by one wavefront.
 // weight(v) = max(0, p_n(v) - q_n(v)) (or p_g(v)); token = the smallest id
 // whose running weight in ascending id order exceeds u * Z.
 __device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float ures) {
+  const int lane = threadIdx.x & 63;
   if (m.mode == MODE_GREEDY) return (int)s.st_arg[n];
   const bool resid = n < m.g;
   const int rp = n, rq = m.g + 1 + n;
-  const int o = (int)s.off[rp], e = (int)s.off[rp + 1];
-  // Residual weights, kept in pe[] of a scratch range after the pool's used part.
-  const int w0 = (int)s.off[2 * m.g + 1];
-  const int cnt = e - o;
-  bool fallback = false;
-  double zl = 0.0;
-  for (int j = threadIdx.x; j < cnt; j += NT) {
-    const double p = pool_prob(s, rp, o + j);
-    double w = p;
-    if (resid && p > 0.0) w = fmax(p - pool_lookup(s, rq, s.pool[o + j].y), 0.0);
-    s.pe[w0 + j] = w;
+  const int op = (int)s.off[rp], np = (int)s.st_cnt[rp];
+  const int oq = resid ? (int)s.off[rq] : 0, nq = resid ? (int)s.st_cnt[rq] : 0;
+  const double ip = s.st_invS[rp], iq = resid ? s.st_invS[rq] : 0.0;
+  double zl = 0.0, zp = 0.0;
+  for (int b = 0; b < np; b += 64) {
+    const int j = b + lane;
+    const uint32_t id = j < np ? s.pool[op + j].y : 0xFFFFFFFFu;
+    const double p = j < np ? (double)s.pv[op + j] * ip : 0.0;
+    float qe = 0.0f;
+    wave_broadcast(s.pool, s.pv, oq, nq, [&](uint32_t, uint32_t qid, float val) { qe = qid == id ? val : qe; });
+    const double w = resid ? fmax(p - (double)qe * iq, 0.0) : p;
+    if (j < np) s.wts[op + j] = (float)w;
     zl += w;
+    zp += p;
   }
-  double Z = block_sum(zl, s.red_d);
+  double Z = wave_sum_d(zl);
   if (!(Z > 0.0)) {   // zero residual mass: draw from the target itself
-    fallback = true;
-    zl = 0.0;
-    for (int j = threadIdx.x; j < cnt; j += NT) {
-      const double p = pool_prob(s, rp, o + j);
-      s.pe[w0 + j] = p;
-      zl += p;
-    }
-    Z = block_sum(zl, s.red_d);
+    for (int j = lane; j < np; j += 64) s.wts[op + j] = (float)((double)s.pv[op + j] * ip);
+    Z = wave_sum_d(zp);
   }
-  (void)fallback;
+  wave_lds_sync();
   const double target = (double)ures * Z;
   uint32_t best = 0xFFFFFFFFu, lastpos = 0;
-  for (int j = threadIdx.x; j < cnt; j += NT) {
-    const uint32_t v = s.pool[o + j].y;
-    const double wj = s.pe[w0 + j];
-    if (wj > 0.0) lastpos = max(lastpos, v + 1u);
+  for (int b = 0; b < np; b += 64) {
+    const int j = b + lane;
+    const uint32_t v = j < np ? s.pool[op + j].y : 0xFFFFFFFFu;
     double run = 0.0;
-    for (int l = 0; l < cnt; ++l)
-      if (s.pool[o + l].y <= v) run += s.pe[w0 + l];
-    if (run > target) best = min(best, v);
+    wave_broadcast(s.pool, s.wts, op, np, [&](uint32_t, uint32_t id, float w) { run += id <= v ? (double)w : 0.0; });
+    if (j < np) {
+      if (s.wts[op + j] > 0.0f) lastpos = max(lastpos, v + 1u);
+      if (run > target) best = min(best, v);
+    }
   }
-  best = block_min_u32(best, s.red_u);
+  best = wave_min_u32(best);
   if (best != 0xFFFFFFFFu) return (int)best;
-  return (int)block_max_u32(lastpos, s.red_u) - 1;   // rounding left no crossing
+  return (int)wave_max_u32(lastpos) - 1;   // rounding left no crossing
 }
 
 // ===========================================================================
@@ -577,66 +582,48 @@ __device__ __forceinline__ int dense_draw(const Args& a, FinSmem& s, int b, cons
 template <typename ET, bool VECTOR>
 __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
   const Mode m = seq_mode(a, b);
+  const uint32_t fl = a.seq_flags[b];
   const int RS = 2 * a.G + 1;
   const int G = a.G;
   const int R = 2 * m.g + 1;
+  const int NS = R * a.NP;          // (row, part) lists of the sequence
   const int wave = threadIdx.x >> 6;
-  bool ok = m.mode != MODE_INVALID;
+  const int lane = threadIdx.x & 63;
+  bool ok = m.mode != MODE_INVALID && !(fl & F_BAD);
   const int gl = a.gamma_len ? a.gamma_len[b] : G;
   ok = ok && gl >= 1 && gl <= G;
   ok = ok && !(m.tp != m.tp);
   const float* ub = a.u + (size_t)b * (G + 1);
   const int32_t* xb = a.draft + (size_t)b * G;
-  {
-    uint32_t badin = 0;
-    for (int i = threadIdx.x; i < m.g; i += NT) {
-      const int x = xb[i];
-      const float ui = ub[i];
-      badin |= (x < 0 || x >= a.V || !(ui >= 0.0f && ui < 1.0f)) ? 1u : 0u;
-    }
-    if (threadIdx.x == 0) badin |= !(ub[G] >= 0.0f && ub[G] < 1.0f) ? 1u : 0u;
-    ok = ok && block_or_u32(badin, s.red_u) == 0;
+  bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG;
+  uint32_t badin = 0;
+  for (int i = threadIdx.x; i < m.g; i += NT) {
+    const int x = xb[i];
+    const float ui = ub[i];
+    badin |= (x < 0 || x >= a.V || !(ui >= 0.0f && ui < 1.0f)) ? 1u : 0u;
   }
-  bool dense = m.mode == MODE_DENSE;
-  if (ok && !dense) {
-    // Segment sizes: (row r, part p) -> soff[r * NP + p + 1].
-    const int NPp = a.NP;
-    uint32_t fl = 0;
-    for (int i = threadIdx.x; i < R * NPp; i += NT) {
-      const int r = i / NPp, p = i - r * NPp;
-      const RowInfo& ri = a.rows[b * RS + used_slot(G, m.g, r)];
-      if (p == 0) fl |= ri.flags;
-      s.soff[i + 1] = (uint32_t)max(ri.nsurv[p], 0);
-    }
-    fl = block_or_u32(fl, s.red_u);
-    if (fl & F_BAD) ok = false;
-    else if (fl & F_DEMOTE) dense = true;
-    if (ok && !dense) {
-      if (threadIdx.x == 0) {
-        s.soff[0] = 0;
-        for (int i = 0; i < R * NPp; ++i) s.soff[i + 1] += s.soff[i];
-        uint32_t mx = 0, empty = 0;
-        for (int r = 0; r <= R; ++r) s.off[r] = s.soff[r * NPp];
-        for (int r = 0; r < R; ++r) {
-          mx = max(mx, s.off[r + 1] - s.off[r]);
-          empty |= s.off[r + 1] == s.off[r] ? 1u : 0u;
-        }
-        // The pool also holds one row's residual weights after the survivors.
-        s.flag = (s.off[R] + mx > (uint32_t)POOL ? 1u : 0u) | (empty ? 2u : 0u);
-      }
-      __syncthreads();
-      const uint32_t f = s.flag;
-      __syncthreads();
-      if (f & 2u) ok = false;          // a row with no finite logit
-      else if (f & 1u) dense = true;   // does not fit in LDS: multi-pass path
-    }
+  if (threadIdx.x == 0) badin |= !(ub[G] >= 0.0f && ub[G] < 1.0f) ? 1u : 0u;
+  // List sizes: (row r, part p) -> soff[r * NP + p + 1]; the block scan
+  // runs for every sequence so that control flow stays block-uniform.
+  uint32_t c = 0;
+  if (ok && !dense && (int)threadIdx.x < NS) {
+    const int r = threadIdx.x / a.NP, p = threadIdx.x - r * a.NP;
+    c = (uint32_t)max(a.counts[(size_t)(b * RS + used_slot(G, m.g, r)) * a.NP + p], 0);
   }
+  uint32_t total = 0;
+  const uint32_t excl = block_excl_scan(c, s.red_u, &total);
+  ok = ok && block_or_u32(badin, s.red_u) == 0;
   if (ok && !dense) {
-    // All candidate segments in one round trip.
-    const int NS = R * a.NP;
-    const uint32_t total = s.soff[NS];
+    if ((int)threadIdx.x < NS) s.soff[threadIdx.x] = excl;
+    if (threadIdx.x == 0) s.soff[NS] = total;
+    if (total > (uint32_t)POOL) dense = true;   // does not fit in LDS: multi-pass path
+  }
+  __syncthreads();
+  if (ok && !dense) {
+    for (int r = threadIdx.x; r <= R; r += NT) s.off[r] = s.soff[r * a.NP];
+    // All survivor lists in one round trip.
     for (uint32_t e = threadIdx.x; e < total; e += NT) {
-      int lo = 0, hi = NS;   // segment with soff[lo] <= e < soff[lo+1]
+      int lo = 0, hi = NS;   // list with soff[lo] <= e < soff[lo+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (s.soff[mid] <= e) lo = mid;
@@ -644,13 +631,18 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       }
       const int r = lo / a.NP, p = lo - r * a.NP;
       const int rowid = b * RS + used_slot(G, m.g, r);
-      s.pool[e] = a.cand[(size_t)rowid * RCAP + (size_t)p * a.seg + (e - s.soff[lo])];
+      s.pool[e] = a.lists[list_index(a, rowid, p) + (e - s.soff[lo])];
     }
     __syncthreads();
-    for (int r = wave; r < R; r += NWAVE) wave_row_stats<ET>(s, r, (int)s.off[r], (int)(s.off[r + 1] - s.off[r]), m);
-    __syncthreads();
-    for (int i = wave; i < m.g; i += NWAVE) wave_position(s, i, xb[i], m);
-    __syncthreads();
+    uint32_t empty = 0;
+    if ((int)threadIdx.x < R) empty = s.off[threadIdx.x + 1] == s.off[threadIdx.x] ? 1u : 0u;
+    ok = block_or_u32(empty, s.red_u) == 0;   // a row without a finite logit
+    if (ok) {
+      for (int r = wave; r < R; r += NWAVE) pool_row_stats<ET>(s, r, m);
+      __syncthreads();
+      for (int i = wave; i < m.g; i += NWAVE) wave_position(s, i, xb[i], m);
+      __syncthreads();
+    }
   } else if (ok && dense) {
     ok = dense_row_stats<ET, VECTOR>(a, s, b, m);
     if (ok) dense_positions<ET, VECTOR>(a, s, b, m);
@@ -663,12 +655,18 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       bool rej = false;
       if (i < m.g) rej = !((double)ub[i] * s.pos_q[i] < s.pos_p[i]);
       const unsigned long long mask = __ballot(rej);
-      if (i == 0) s.bc[7] = mask ? (uint32_t)(__ffsll((long long)mask) - 1) : (uint32_t)m.g;
+      const int nn = mask ? __ffsll((long long)mask) - 1 : m.g;
+      if (!dense) {
+        const int t = pool_draw(s, m, nn, ub[G]);
+        if (i == 0) s.bc[6] = (uint32_t)t;
+      }
+      if (i == 0) s.bc[7] = (uint32_t)nn;
     }
     __syncthreads();
     n = (int)s.bc[7];
+    tok = (int)s.bc[6];
     __syncthreads();
-    tok = dense ? dense_draw<ET, VECTOR>(a, s, b, m, n, ub[G]) : pool_draw(s, m, n, ub[G]);
+    if (dense) tok = dense_draw<ET, VECTOR>(a, s, b, m, n, ub[G]);
   }
   int32_t* ot = a.out_tokens + (size_t)b * (G + 1);
   float* oa = a.out_alpha + (size_t)b * G;
@@ -682,14 +680,11 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       op[1] = ok ? (i < m.g ? (float)s.pos_q[i] : 0.0f) : qnan;
     }
   }
-  if (threadIdx.x == 0) a.out_n[b] = ok ? n : -1;
-  // Leave the rows' records cleared for the next call.
-  for (int r = threadIdx.x; r < R; r += NT) {
-    RowInfo& ri = a.rows[b * RS + used_slot(G, m.g, r)];
-    ri.flags = 0;
-#pragma unroll
-    for (int p = 0; p < MAXNP; ++p) ri.nsurv[p] = 0;
+  if (threadIdx.x == 0) {
+    a.out_n[b] = ok ? n : -1;
+    a.seq_flags[b] = 0;
   }
+  (void)lane;
 }
 
 template <typename ET, bool VECTOR>

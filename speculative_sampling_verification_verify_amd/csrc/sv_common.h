@@ -87,6 +87,11 @@ __device__ __forceinline__ size_t list_index(const Args& a, int rowid, int part)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource word 3 for untyped loads on gfx9-family GPUs, and the
+// cache-policy bits of a non-temporal (streaming) load.
+constexpr int BUF_WORD3 = 0x00020000;
+constexpr int BUF_NT = 2;
+
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);

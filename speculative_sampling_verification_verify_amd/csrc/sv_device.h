@@ -93,6 +93,21 @@ __device__ __forceinline__ T wave_incl_scan(T v) {
   return v;
 }
 
+// Inclusive prefix sum of a 32-bit value across the wave with DPP row shifts
+// and row broadcasts (no LDS round trip): within each 16-lane row by
+// shifts of 1, 2, 4, 8, then lane 15 of each row added to the next row and
+// lane 31 to the upper half.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)x;
+}
+
 // Block-wide reductions through a small LDS scratch of NWAVE entries.
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T* scratch) {

@@ -26,17 +26,22 @@
 
 #include "sv_common.h"
 
+#include <type_traits>
+
 namespace sv {
 
 constexpr int K1_WAVES = 4;              // wavefronts per workgroup
 constexpr int K1_NT = 64 * K1_WAVES;
 constexpr int WVPL = 8;                  // 16-byte vectors per lane per step (packed bf16 path)
 constexpr int WVPL_GENERIC = 4;          // the same for fp32 and unaligned rows
-constexpr int WCB = 1024;                // candidate slots per wavefront (LDS)
+constexpr int WCB = 768;                 // candidate slots per wavefront (LDS)
+constexpr int SCAP = 128;                // staged vectors per wavefront (LDS)
 static_assert(WCB <= SEG, "a part's kept set must fit one list segment");
 
 struct WaveSmem {
   uint2 cand[WCB];                       // (key, vocabulary id)
+  uint4 stage[SCAP];                     // flagged 16-byte vectors awaiting the drain
+  uint32_t sidx[SCAP];                   // their vector index in the row
   struct {
     uint32_t hist[256];                  // radix-select histogram
   } h;
@@ -53,7 +58,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // load instruction of the wavefront reads 1 KiB of consecutive bytes.
 // ---------------------------------------------------------------------------
 template <typename ET, bool VECTOR>
-struct WChunk {
+struct GChunk {
   static constexpr int VEC = Key<ET>::VEC;
   static constexpr int NV = WVPL_GENERIC;   // vectors per lane per step
   uint4 raw[NV];
@@ -131,7 +136,7 @@ struct WChunk {
 
   // fn(key, index) for every marked element.
   template <class F>
-  __device__ __forceinline__ void for_marked(uint64_t mask, F fn) const {
+  __device__ __forceinline__ void for_marked(uint64_t mask, bool, F fn) const {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       uint32_t mb = (uint32_t)(mask >> (j * VEC)) & ((1u << VEC) - 1u);
@@ -144,112 +149,112 @@ struct WChunk {
   }
 };
 
-// bf16 with 16-byte vectors: the hot path works on packed pairs.  Each dword
-// holds two bf16 values; x ^ ((x >> 15) & 0x7FFF) per 16-bit half turns
-// sign-magnitude into a two's-complement int16 s' that orders like the
-// values, except that every negative value lands one below its key:
-// s' = K for K >= 0 and s' = K - 1 for K < 0, where K = key - 0x8000.  A test
-// key >= t is then s' >= T' with T = t - 0x8000 and T' = T if T >= 1, else
-// T - 1.  Lane minima and maxima use packed min / max; per-element compares
-// run only in lanes whose packed maximum reaches T'.
+// bf16 with 16-byte vectors: the hot path compares raw 16-bit patterns of
+// packed pairs with one test, chosen by the sign of the bound.  With key(x)
+// the order-preserving key of x and t a bound key:
+//  * t > 0x8000 (the bound stands for a value > 0): key(x) >= t exactly when
+//    the pattern read as int16 is >= t - 0x8000 (positive values order like
+//    their patterns; every negative pattern reads as a negative int16);
+//  * t <= 0x8000 (a value <= 0): key(x) >= t exactly when the pattern read
+//    as uint16 is <= 0x10000 - t (all positive patterns lie below 0x8000,
+//    and a negative value of magnitude m has pattern 0x8000 + m).
+// So per 16-byte vector a packed max (int16) or min (uint16) tree decides
+// whether any element reaches t; a packed uint16 max tree over all patterns
+// finds negative NaNs (patterns >= 0xFF81).  Positive NaN and +inf always
+// reach t and are caught as candidates.
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t ordered_pair(uint32_t w) {
-  const s16x2 v = __builtin_bit_cast(s16x2, w);
-  const s16x2 m = (v >> (short)15) & (short)0x7FFF;
-  return __builtin_bit_cast(uint32_t, v ^ m);
-}
 __device__ __forceinline__ int lo16(uint32_t w) { return (int)(short)(w & 0xFFFFu); }
 __device__ __forceinline__ int hi16(uint32_t w) { return (int)(short)(w >> 16); }
-__device__ __forceinline__ uint32_t key_of_ordered(int sp) { return (uint32_t)(0x8000 + (sp >= 0 ? sp : sp + 1)); }
-__device__ __forceinline__ int ordered_threshold(uint32_t t) {
-  const int T = (int)t - 0x8000;
-  return T >= 1 ? T : T - 1;
-}
-constexpr int ORDERED_NEG_INF = -32641;   // s' of -inf; a negative NaN orders below it
+constexpr uint32_t RAW_NEG_NAN = 0xFF81u; // smallest negative NaN pattern (as unsigned 16 bits)
 
-template <>
-struct WChunk<uint16_t, true> {
+// The compare of one 16-bit pattern h with the bound in the form above:
+// pos: (int16)h >= T; else: (uint16)h <= T.
+__device__ __forceinline__ bool reaches(uint32_t h, bool pos, int T) {
+  return pos ? (int)(short)h >= T : (int)h <= T;
+}
+__device__ __forceinline__ int bound_of(uint32_t t, bool pos) { return pos ? (int)t - 0x8000 : 0x10000 - (int)t; }
+
+struct PChunk {
   static constexpr int VEC = 8;
   static constexpr int NV = WVPL;   // vectors per lane per step
-  uint4 raw[NV];   // ordered int16 pairs after prepare()
+  uint4 raw[NV];   // bf16 patterns
   int first, lim;
 
-  __device__ __forceinline__ void load(const uint16_t* rp, int v0, int lim_, int) {
+  // Buffer loads through the row's resource descriptor: one 32-bit offset
+  // per lane plus immediates, and vectors past the part (num_records) read
+  // as zero without touching memory (valid() excludes them).
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int v0, int lim_) {
     first = v0 + (int)(threadIdx.x & 63);
     lim = lim_;
-    const uint4* vp = reinterpret_cast<const uint4*>(rp);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) raw[j] = load_nt(vp + min(first + 64 * j, lim - 1));
-  }
-  __device__ __forceinline__ bool valid(int j) const { return first + 64 * j < lim; }
-  __device__ __forceinline__ int index_of(int j, int e) const { return (first + 64 * j) * VEC + e; }
-
-  // Convert in place; fold the valid pairs into the packed minimum / maximum.
-  __device__ __forceinline__ void prepare(s16x2& mn, s16x2& mx) {
+    const uint32_t off = (uint32_t)first * 16u;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[q] = ordered_pair(w[q]);
-        if (valid(j)) {
-          const s16x2 v = __builtin_bit_cast(s16x2, w[q]);
-          mn = __builtin_elementwise_min(mn, v);
-          mx = __builtin_elementwise_max(mx, v);
-        }
-      }
-      raw[j] = make_uint4(w[0], w[1], w[2], w[3]);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(off + 1024u * (uint32_t)j), 0, BUF_NT);
+      raw[j] = make_uint4(v.x, v.y, v.z, v.w);
     }
   }
+  __device__ __forceinline__ bool valid(int j) const { return first + 64 * j < lim; }
 
-  __device__ __forceinline__ s16x2 vec_max(int j) const {
+  __device__ __forceinline__ s16x2 smax(int j) const {
     const s16x2 a = __builtin_elementwise_max(__builtin_bit_cast(s16x2, raw[j].x), __builtin_bit_cast(s16x2, raw[j].y));
     const s16x2 b = __builtin_elementwise_max(__builtin_bit_cast(s16x2, raw[j].z), __builtin_bit_cast(s16x2, raw[j].w));
     return __builtin_elementwise_max(a, b);
   }
-
-  // Largest key of vector j (0 when the vector is past the part).
-  __device__ __forceinline__ uint32_t vec_max_key(int j) const {
-    const s16x2 v = vec_max(j);
-    return valid(j) ? key_of_ordered(max((int)v.x, (int)v.y)) : 0u;
+  __device__ __forceinline__ u16x2 umin(int j) const {
+    const u16x2 a = __builtin_elementwise_min(__builtin_bit_cast(u16x2, raw[j].x), __builtin_bit_cast(u16x2, raw[j].y));
+    const u16x2 b = __builtin_elementwise_min(__builtin_bit_cast(u16x2, raw[j].z), __builtin_bit_cast(u16x2, raw[j].w));
+    return __builtin_elementwise_min(a, b);
+  }
+  __device__ __forceinline__ u16x2 umax(int j) const {
+    const u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, raw[j].x), __builtin_bit_cast(u16x2, raw[j].y));
+    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, raw[j].z), __builtin_bit_cast(u16x2, raw[j].w));
+    return __builtin_elementwise_max(a, b);
   }
 
-  // Per-element compares run only in lanes whose maximum reaches the bound,
-  // and there only for the vectors whose own maximum does.
-  __device__ __forceinline__ uint64_t mask_ge(uint32_t t, s16x2 mx) const {
-    const int Tp = ordered_threshold(t);
-    if (max((int)mx.x, (int)mx.y) < Tp) return 0ull;
-    uint64_t m = 0;
+  // Key of the largest element of vector j (0 when past the part): the
+  // largest non-negative pattern if there is one, else the negative pattern
+  // of smallest magnitude.
+  __device__ __forceinline__ uint32_t vec_max_key(int j) const {
+    const s16x2 s = smax(j);
+    const int m = max((int)s.x, (int)s.y);
+    const u16x2 u = umin(j);
+    const uint32_t h = m >= 0 ? (uint32_t)m : (uint32_t)min((int)u.x, (int)u.y);
+    return valid(j) ? Key<uint16_t>::of_bits(h) : 0u;
+  }
+
+  // Bit j set when vector j holds an element reaching the bound; folds the
+  // unsigned maxima into um (negative NaN check).
+  __device__ __forceinline__ uint32_t scan(bool pos, int T, u16x2& um) const {
+    uint32_t vf = 0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       if (!valid(j)) continue;
-      const s16x2 v = vec_max(j);
-      if (max((int)v.x, (int)v.y) < Tp) continue;
-      const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-      uint32_t mb = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        mb |= lo16(w[q]) >= Tp ? (1u << (2 * q)) : 0u;
-        mb |= hi16(w[q]) >= Tp ? (1u << (2 * q + 1)) : 0u;
+      um = __builtin_elementwise_max(um, umax(j));
+      bool hit;
+      if (pos) {
+        const s16x2 s = smax(j);
+        hit = max((int)s.x, (int)s.y) >= T;
+      } else {
+        const u16x2 u = umin(j);
+        hit = min((int)u.x, (int)u.y) <= T;
       }
-      m |= (uint64_t)mb << (8 * j);
+      vf |= hit ? (1u << j) : 0u;
     }
-    return m;
+    return vf;
   }
 
-  template <class F>
-  __device__ __forceinline__ void for_marked(uint64_t mask, F fn) const {
+  // Copy the flagged vectors to staging slots rank, rank + 1, ... (in
+  // vector order) with their vector index in the row.
+  __device__ __forceinline__ void stage(uint32_t vf, uint32_t rank, uint4* dst, uint32_t* didx) const {
+    uint32_t rk = rank;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      uint32_t mb = (uint32_t)(mask >> (8 * j)) & 0xFFu;
-      const uint4 r = raw[j];
-      while (mb) {
-        const int e = __builtin_ctz(mb);
-        mb &= mb - 1u;
-        const int q = e >> 1;
-        const uint32_t w = q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w;
-        fn(key_of_ordered((e & 1) ? hi16(w) : lo16(w)), index_of(j, e));
+      if (vf & (1u << j)) {
+        dst[rk] = raw[j];
+        didx[rk] = (uint32_t)(first + 64 * j);
+        ++rk;
       }
     }
   }
@@ -273,132 +278,28 @@ __device__ __forceinline__ uint32_t wave_compact(uint2* cand, uint32_t fill, uin
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)outn);
 }
 
-// ---------------------------------------------------------------------------
-// One part [e0, e1) of one logit row.  Writes the part's survivors (keys >=
-// its exact k-th largest, finite only) to out[0, *out_count); flags F_BAD /
-// F_DEMOTE on the sequence when the logits hold NaN / +inf or the ties do
-// not fit.  Wavefront-uniform control flow throughout.
-// ---------------------------------------------------------------------------
-template <typename ET, bool VECTOR>
-__device__ __forceinline__ void unit_select(WaveSmem& w, const ET* rp, int e0, int e1, uint32_t k, uint2* out,
-                                            int32_t* out_count, uint32_t* flags) {
-  constexpr int LEVELS = Key<ET>::LEVELS;
-  constexpr int VEC = Key<ET>::VEC;
-  constexpr int SPAN = 64 * WChunk<ET, VECTOR>::NV;   // vectors per step
-  constexpr bool PACKED = VECTOR && sizeof(ET) == 2;
+// Raise t to the exact k-th largest key of the buffer and keep the entries
+// >= it.  Wavefront-uniform.
+template <int LEVELS>
+__device__ __forceinline__ void buffer_select(WaveSmem& w, uint32_t k, uint32_t& t, uint32_t& fill) {
   const int lane = threadIdx.x & 63;
-  const int v0 = e0 / VEC;
-  const int lim = (e1 + VEC - 1) / VEC;
-  const int nsteps = (lim - v0 + SPAN - 1) / SPAN;
-  uint32_t t = 1;                        // certified bound (wavefront-uniform; 1 = none yet)
-  uint32_t fill = 0;                     // buffer fill (wavefront-uniform)
-  uint32_t bad = 0;                      // lane: NaN / +inf among the marked keys
-  uint32_t lo = 0xFFFFFFFFu;             // lane minimum key (generic path)
-  bool demoted = false;
-  s16x2 pmin = {(short)32767, (short)32767};
+  const uint32_t fl = fill;
+  const uint32_t kth = wave_kth<LEVELS>(
+      [&](auto fn) {
+        for (uint32_t i = lane; i < fl; i += 64) fn(w.cand[i].x);
+      },
+      k, w.h.hist);
+  t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)kth));
+  fill = wave_compact(w.cand, fill, t);
+}
 
-  constexpr int NVC = WChunk<ET, VECTOR>::NV;
-  // Buffer fill at which t is raised again (keeps candidates rare).
-  const uint32_t refresh_at = min(k + max(64u, k / 2), (uint32_t)WCB - 64u);
-  auto examine = [&](WChunk<ET, VECTOR>& ch, bool first) {
-    if (demoted) return;
-    uint64_t mask;
-    s16x2 mx = {(short)-32768, (short)-32768};
-    if constexpr (PACKED) ch.prepare(pmin, mx);
-    if (first) {
-      // The k-th largest of the lane maxima (or of the vector maxima) is a
-      // certified bound: each maximum is a distinct element of the part.
-      uint32_t t0 = 0;
-      if (k <= 64) {
-        uint32_t lm = 0;
-#pragma unroll
-        for (int j = 0; j < NVC; ++j) lm = max(lm, ch.vec_max_key(j));
-        t0 = wave_kth<LEVELS>([&](auto fn) { fn(lm); }, k, w.h.hist);
-      } else if (k <= 64u * NVC) {
-        t0 = wave_kth<LEVELS>(
-            [&](auto fn) {
-#pragma unroll
-              for (int j = 0; j < NVC; ++j) fn(ch.vec_max_key(j));
-            },
-            k, w.h.hist);
-      }
-      t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)t0));
-    }
-    if constexpr (PACKED) {
-      mask = ch.mask_ge(t, mx);
-    } else {
-      mask = ch.mask_ge(t, lo);
-    }
-    if (__ballot(mask != 0ull) == 0ull) return;
-    uint32_t c = (uint32_t)__popcll(mask);
-    uint32_t incl = wave_incl_scan(c);
-    uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    if (fill + tot > (uint32_t)WCB) {
-      // Raise t to the exact k-th largest of buffer + marked keys first.
-      const uint32_t fl = fill;
-      const uint32_t kth = wave_kth<LEVELS>(
-          [&](auto fn) {
-            for (uint32_t i = lane; i < fl; i += 64) fn(w.cand[i].x);
-            ch.for_marked(mask, [&](uint32_t kk, int) { fn(kk); });
-          },
-          k, w.h.hist);
-      t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)kth));
-      fill = wave_compact(w.cand, fill, t);
-      if constexpr (PACKED) {
-        mask = ch.mask_ge(t, mx);
-      } else {
-        uint32_t dummy = 0;
-        mask = ch.mask_ge(t, dummy);
-      }
-      c = (uint32_t)__popcll(mask);
-      incl = wave_incl_scan(c);
-      tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-      if (fill + tot > (uint32_t)WCB) {   // more ties at the k-th largest than the buffer holds
-        demoted = true;
-        return;
-      }
-    }
-    if (tot) {
-      uint32_t slot = fill + incl - c;
-      ch.for_marked(mask, [&](uint32_t kk, int idx) {
-        bad |= kk >= Key<ET>::POS_INF ? 1u : 0u;
-        w.cand[slot++] = make_uint2(kk, (uint32_t)idx);
-      });
-      fill += tot;
-      wave_sync_lds();
-      if (fill >= refresh_at) {
-        // Raise t to the exact k-th largest of the buffer and drop the rest.
-        const uint32_t fl = fill;
-        const uint32_t kth = wave_kth<LEVELS>(
-            [&](auto fn) {
-              for (uint32_t i = lane; i < fl; i += 64) fn(w.cand[i].x);
-            },
-            k, w.h.hist);
-        t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)kth));
-        fill = wave_compact(w.cand, fill, t);
-      }
-    }
-  };
-
-  // The loop body is straight-line: both buffers are examined every
-  // iteration (a step past the part holds no valid element and marks
-  // nothing), every load is issued unconditionally (a step past the part
-  // re-reads its last vector) and demotion only turns examine() into a
-  // no-op.  An early exit or a load under a branch would make the compiler
-  // wait for both buffers before examining either.
-  WChunk<ET, VECTOR> A, B;
-  A.load(rp, v0, lim, e1);
-  __builtin_amdgcn_sched_barrier(0);   // keep A's loads ahead of B's
-  B.load(rp, v0 + SPAN, lim, e1);
-  for (int s = 0; s < nsteps; s += 2) {
-    examine(A, s == 0);
-    A.load(rp, v0 + (s + 2) * SPAN, lim, e1);
-    examine(B, false);
-    B.load(rp, v0 + (s + 3) * SPAN, lim, e1);
-  }
-  if constexpr (PACKED) lo = min((int)pmin.x, (int)pmin.y) < ORDERED_NEG_INF ? 0u : 0xFFFFFFFFu;
-
-  const bool isbad = __ballot(bad != 0 || lo < Key<ET>::NEG_INF) != 0ull;
+// The end of a part: flags, then the keys >= the part's exact k-th largest
+// (finite only) written to its survivor list.
+template <typename ET>
+__device__ __forceinline__ void unit_finish(WaveSmem& w, uint32_t k, uint32_t t, uint32_t fill, bool demoted,
+                                            bool isbad, uint2* out, int32_t* out_count, uint32_t* flags) {
+  constexpr int LEVELS = Key<ET>::LEVELS;
+  const int lane = threadIdx.x & 63;
   if (demoted || isbad) {
     if (lane == 0) {
       atomicOr(flags, isbad ? F_BAD : F_DEMOTE);
@@ -406,7 +307,6 @@ __device__ __forceinline__ void unit_select(WaveSmem& w, const ET* rp, int e0, i
     }
     return;
   }
-  // The part's exact kept set among its candidates.
   uint32_t tf = t;
   if (fill > k) {
     const uint32_t fl = fill;
@@ -430,6 +330,262 @@ __device__ __forceinline__ void unit_select(WaveSmem& w, const ET* rp, int e0, i
     *out_count = (int32_t)min(outn, (uint32_t)SEG);
     if (outn > (uint32_t)SEG) atomicOr(flags, F_DEMOTE);
   }
+}
+
+// ---------------------------------------------------------------------------
+// One part [e0, e1) of one logit row, general element-by-element form (fp32
+// rows and rows that are not 16-byte vectors).  Writes the part's survivors
+// to out[0, *out_count); flags F_BAD / F_DEMOTE on the sequence when the
+// logits hold NaN / +inf or the ties do not fit.  Wavefront-uniform control
+// flow throughout.
+// ---------------------------------------------------------------------------
+template <typename ET, bool VECTOR>
+__device__ __forceinline__ void unit_select(WaveSmem& w, const ET* rp, int e0, int e1, uint32_t k, uint2* out,
+                                            int32_t* out_count, uint32_t* flags) {
+  constexpr int LEVELS = Key<ET>::LEVELS;
+  constexpr int VEC = Key<ET>::VEC;
+  constexpr int NVC = GChunk<ET, VECTOR>::NV;
+  constexpr int SPAN = 64 * NVC;         // vectors per step
+  const int lane = threadIdx.x & 63;
+  const int v0 = e0 / VEC;
+  const int lim = (e1 + VEC - 1) / VEC;
+  const int nsteps = (lim - v0 + SPAN - 1) / SPAN;
+  uint32_t t = 1;                        // certified bound (wavefront-uniform; 1 = none yet)
+  uint32_t fill = 0;                     // buffer fill (wavefront-uniform)
+  uint32_t bad = 0;                      // lane: NaN / +inf among the marked keys
+  uint32_t lo = 0xFFFFFFFFu;             // lane minimum key
+  bool demoted = false;
+  const uint32_t refresh_at = min(k + max(32u, k / 4), (uint32_t)WCB - 64u);
+
+  auto examine = [&](GChunk<ET, VECTOR>& ch, bool first) {
+    if (demoted) return;
+    if (first) {
+      // The k-th largest of the vector maxima is a certified bound: each
+      // maximum is a distinct element of the part.
+      uint32_t t0 = 0;
+      if (k <= 64u * NVC)
+        t0 = wave_kth<LEVELS>(
+            [&](auto fn) {
+#pragma unroll
+              for (int j = 0; j < NVC; ++j) fn(ch.vec_max_key(j));
+            },
+            k, w.h.hist);
+      t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)t0));
+    }
+    uint64_t mask = ch.mask_ge(t, lo);
+    if (__ballot(mask != 0ull) == 0ull) return;
+    uint32_t c = (uint32_t)__popcll(mask);
+    uint32_t incl = wave_incl_scan_dpp(c);
+    uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (fill + tot > (uint32_t)WCB) {
+      // Raise t to the exact k-th largest of buffer + marked keys first.
+      const uint32_t fl = fill;
+      const uint32_t kth = wave_kth<LEVELS>(
+          [&](auto fn) {
+            for (uint32_t i = lane; i < fl; i += 64) fn(w.cand[i].x);
+            ch.for_marked(mask, false, [&](uint32_t kk, int) { fn(kk); });
+          },
+          k, w.h.hist);
+      t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)kth));
+      fill = wave_compact(w.cand, fill, t);
+      uint32_t dummy = 0;
+      mask = ch.mask_ge(t, dummy);
+      c = (uint32_t)__popcll(mask);
+      incl = wave_incl_scan_dpp(c);
+      tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      if (fill + tot > (uint32_t)WCB) {   // more ties at the k-th largest than the buffer holds
+        demoted = true;
+        return;
+      }
+    }
+    if (tot) {
+      uint32_t slot = fill + incl - c;
+      ch.for_marked(mask, false, [&](uint32_t kk, int idx) {
+        bad |= kk >= Key<ET>::POS_INF ? 1u : 0u;
+        w.cand[slot++] = make_uint2(kk, (uint32_t)idx);
+      });
+      fill += tot;
+      wave_sync_lds();
+      if (fill >= refresh_at) buffer_select<LEVELS>(w, k, t, fill);
+    }
+  };
+
+  // The loop body is straight-line: both buffers are examined every
+  // iteration (a step past the part holds no valid element and marks
+  // nothing), every load is issued unconditionally (a step past the part
+  // re-reads its last vector) and demotion only turns examine() into a
+  // no-op.  An early exit or a load under a branch would make the compiler
+  // wait for both buffers before examining either.
+  GChunk<ET, VECTOR> A, B;
+  A.load(rp, v0, lim, e1);
+  __builtin_amdgcn_sched_barrier(0);   // keep A's loads ahead of B's
+  B.load(rp, v0 + SPAN, lim, e1);
+  for (int s = 0; s < nsteps; s += 2) {
+    examine(A, s == 0);
+    A.load(rp, v0 + (s + 2) * SPAN, lim, e1);
+    examine(B, false);
+    B.load(rp, v0 + (s + 3) * SPAN, lim, e1);
+  }
+  const bool isbad = __ballot(bad != 0 || lo < Key<ET>::NEG_INF) != 0ull;
+  unit_finish<ET>(w, k, t, fill, demoted, isbad, out, out_count, flags);
+}
+
+// ---------------------------------------------------------------------------
+// The same for bf16 rows of 16-byte vectors, the hot path.  A step only
+// flags the vectors whose maximum reaches t (packed max trees on the raw
+// patterns once t is positive) and copies the flagged vectors to the
+// wavefront's LDS staging area; a drain pass later gives each lane one
+// staged vector, so element work runs once per flagged vector, and the
+// step's registers are free again at once.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* rp, int e0, int e1, uint32_t k,
+                                                   uint2* out, int32_t* out_count, uint32_t* flags) {
+  constexpr int LEVELS = Key<uint16_t>::LEVELS;
+  constexpr int NVC = WVPL;
+  constexpr int SPAN = 64 * NVC;          // vectors per step
+  constexpr uint32_t DRAIN = 32;          // staged vectors per drain round (<= 8 * DRAIN appends)
+  const int lane = threadIdx.x & 63;
+  const int v0 = e0 / 8;
+  const int lim = e1 / 8;
+  const int nsteps = (lim - v0 + SPAN - 1) / SPAN;
+  uint32_t t = 1;                         // certified bound (wavefront-uniform; 1 = none yet)
+  uint32_t fill = 0;                      // candidate buffer fill (wavefront-uniform)
+  uint32_t staged = 0;                    // staged vectors (wavefront-uniform)
+  bool demoted = false;
+  uint32_t bad = 0;                       // lane: NaN / +inf among the candidates
+  u16x2 um = {(unsigned short)0, (unsigned short)0};   // unsigned maxima of the patterns seen
+  const uint32_t refresh_at = min(k + max(32u, k / 4), (uint32_t)WCB - 8u * DRAIN);
+
+  // Turn the staged vectors into candidates (keys >= the current t).
+  auto drain = [&]() {
+    for (uint32_t r0 = 0; r0 < staged; r0 += DRAIN) {
+      if (fill + 8u * DRAIN > (uint32_t)WCB) {
+        buffer_select<LEVELS>(w, k, t, fill);
+        if (fill + 8u * DRAIN > (uint32_t)WCB) {   // more ties at the k-th largest than the buffer holds
+          demoted = true;
+          staged = 0;
+          return;
+        }
+      }
+      const bool pos = t > 0x8000u;
+      const int T = bound_of(t, pos);
+      const uint32_t si = r0 + lane;
+      const bool have = lane < (int)DRAIN && si < staged;
+      uint4 d = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t vi = 0;
+      if (have) {
+        d = w.stage[si];
+        vi = w.sidx[si];
+      }
+      const uint32_t wd[4] = {d.x, d.y, d.z, d.w};
+      uint32_t mb = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mb |= reaches(wd[q] & 0xFFFFu, pos, T) ? (1u << (2 * q)) : 0u;
+        mb |= reaches(wd[q] >> 16, pos, T) ? (1u << (2 * q + 1)) : 0u;
+      }
+      if (!have) mb = 0;
+      const uint32_t c = (uint32_t)__popc(mb);
+      const uint32_t incl = wave_incl_scan_dpp(c);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      uint32_t slot = fill + incl - c;
+      while (mb) {
+        const int e = __builtin_ctz(mb);
+        mb &= mb - 1u;
+        const int q = e >> 1;
+        const uint32_t wq = q == 0 ? wd[0] : q == 1 ? wd[1] : q == 2 ? wd[2] : wd[3];
+        const uint32_t kk = Key<uint16_t>::of_bits((e & 1) ? (wq >> 16) : (wq & 0xFFFFu));
+        bad |= kk >= Key<uint16_t>::POS_INF ? 1u : 0u;
+        w.cand[slot++] = make_uint2(kk, vi * 8u + (uint32_t)e);
+      }
+      fill += tot;
+      wave_sync_lds();
+    }
+    staged = 0;
+    if (fill >= refresh_at) buffer_select<LEVELS>(w, k, t, fill);
+  };
+
+  // Flag, then stage, the vectors of one step that reach t.
+  auto examine = [&](PChunk& ch) {
+    if (demoted) return;
+    const bool pos = t > 0x8000u;
+    uint32_t vf = ch.scan(pos, bound_of(t, pos), um);
+    if (__ballot(vf != 0u) == 0ull) return;
+    uint32_t nv = (uint32_t)__popc(vf);
+    uint32_t vincl = wave_incl_scan_dpp(nv);
+    uint32_t tv = (uint32_t)__builtin_amdgcn_readlane((int)vincl, 63);
+    if (staged + tv > (uint32_t)SCAP) {
+      if (staged) drain();
+      if (demoted) return;
+      if (tv > (uint32_t)SCAP) {
+        // Too many flagged vectors: the k-th largest of their maxima is a
+        // certified bound (each maximum is a distinct element); re-flag.
+        if (tv > k) {
+          const uint32_t kth = wave_kth<LEVELS>(
+              [&](auto fn) {
+#pragma unroll
+                for (int j = 0; j < NVC; ++j)
+                  if (vf & (1u << j)) fn(ch.vec_max_key(j));
+              },
+              k, w.h.hist);
+          t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)kth));
+          const bool p2 = t > 0x8000u;
+          u16x2 dummy = um;
+          vf &= ch.scan(p2, bound_of(t, p2), dummy);
+          nv = (uint32_t)__popc(vf);
+          vincl = wave_incl_scan_dpp(nv);
+          tv = (uint32_t)__builtin_amdgcn_readlane((int)vincl, 63);
+        }
+        if (tv > (uint32_t)SCAP) {   // more tied maxima than the staging area holds
+          demoted = true;
+          return;
+        }
+      }
+    }
+    ch.stage(vf, staged + vincl - nv, w.stage, w.sidx);
+    staged += tv;
+    wave_sync_lds();
+    if (staged >= DRAIN) drain();
+  };
+
+  // The descriptor covers the row up to the part's end.
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rp), (short)0, e1 * 2, BUF_WORD3);
+  PChunk A, B;
+  A.load(rsrc, v0, lim);
+  __builtin_amdgcn_sched_barrier(0);   // keep A's loads ahead of B's
+  B.load(rsrc, v0 + SPAN, lim);
+  {
+    // First step: the k-th largest of the vector maxima is a certified
+    // bound (each maximum is a distinct element of the part).
+    uint32_t t0 = 0;
+    if (k <= 64u * NVC)
+      t0 = wave_kth<LEVELS>(
+          [&](auto fn) {
+#pragma unroll
+            for (int j = 0; j < NVC; ++j) fn(A.vec_max_key(j));
+          },
+          k, w.h.hist);
+    t = max(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)t0));
+    examine(A);
+  }
+  A.load(rsrc, v0 + 2 * SPAN, lim);
+  // The loop body is straight-line: both buffers are examined every
+  // iteration (a step past the part holds no valid element and flags
+  // nothing), every load is issued unconditionally (a step past the part
+  // reads zeros through the descriptor) and demotion only turns the
+  // examination into a no-op.  An early exit or a load under a branch would
+  // make the compiler wait for both buffers before examining either.
+  for (int s = 1; s < nsteps; s += 2) {
+    examine(B);
+    B.load(rsrc, v0 + (s + 2) * SPAN, lim);
+    examine(A);
+    A.load(rsrc, v0 + (s + 3) * SPAN, lim);
+  }
+  if (!demoted && staged) drain();
+  const bool negnan = max((uint32_t)um.x, (uint32_t)um.y) >= RAW_NEG_NAN;
+  const bool isbad = __ballot(bad != 0 || negnan) != 0ull;
+  unit_finish<uint16_t>(w, k, t, fill, demoted, isbad, out, out_count, flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -460,8 +616,12 @@ __global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) v
   const int e1 = min(a.V, e0 + a.PL);
   int32_t* cnt = a.counts + (size_t)rowid * a.NP + part;
   if (e0 < e1) {
-    unit_select<ET, VECTOR>(w, row_ptr<ET>(a, b, isP, pos), e0, e1, m.k, a.lists + list_index(a, rowid, part), cnt,
-                            a.seq_flags + b);
+    if constexpr (VECTOR && sizeof(ET) == 2)
+      unit_select_packed(w, row_ptr<ET>(a, b, isP, pos), e0, e1, m.k, a.lists + list_index(a, rowid, part), cnt,
+                         a.seq_flags + b);
+    else
+      unit_select<ET, VECTOR>(w, row_ptr<ET>(a, b, isP, pos), e0, e1, m.k, a.lists + list_index(a, rowid, part),
+                              cnt, a.seq_flags + b);
   } else if (lane == 0) {
     *cnt = 0;
   }

@@ -12,7 +12,7 @@
 
 namespace sv {
 
-constexpr int NT = 512;          // threads per workgroup (8 wavefronts)
+constexpr int NT = 1024;         // threads per finisher workgroup (16 wavefronts)
 constexpr int NWAVE = NT / 64;
 constexpr int KMAX_SPARSE = 512; // largest top-k handled by the streaming select
 constexpr uint32_t NONE = 0xFFFFFFFFu;
@@ -106,6 +106,50 @@ __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
   x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return (uint32_t)x;
+}
+
+// Whole-wave reductions with the same DPP pattern (an inclusive scan whose
+// lane 63 holds the result, read back uniformly).  The neutral element fills
+// the lanes a shift or broadcast does not reach.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_dpp_u32(uint32_t v, uint32_t neutral, Op op) {
+  const int nu = (int)neutral;
+  int x = (int)v;
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(nu, x, 0x111, 0xF, 0xF, false));
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(nu, x, 0x112, 0xF, 0xF, false));
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(nu, x, 0x114, 0xF, 0xF, false));
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(nu, x, 0x118, 0xF, 0xF, false));
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(nu, x, 0x142, 0xA, 0xF, false));
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(nu, x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  return wave_reduce_dpp_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+  return wave_reduce_dpp_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+// One DPP step of a double: v + (v moved by CTRL within ROWMASK), the 64-bit
+// value moving as two halves; unreached lanes add +0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFFll), CTRL, ROWMASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWMASK, 0xF, false);
+  return v + __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+// Sum of a double over the wave.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v = dpp_add_f64<0x111, 0xF>(v);
+  v = dpp_add_f64<0x112, 0xF>(v);
+  v = dpp_add_f64<0x114, 0xF>(v);
+  v = dpp_add_f64<0x118, 0xF>(v);
+  v = dpp_add_f64<0x142, 0xA>(v);
+  v = dpp_add_f64<0x143, 0xC>(v);
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
 // Block-wide reductions through a small LDS scratch of NWAVE entries.

@@ -28,12 +28,13 @@ constexpr int MAXSEG = 512;                     // (row, part) lists of one sequ
 struct FinSmem {
   uint2 pool[POOL];                             // (key, id) of every survivor of the sequence
   float pv[POOL];                               // exp((z - zmax) / T) per kept survivor
-  float wts[POOL];                              // residual / bonus weights of the drawn row
+  double wts[POOL];                             // residual / bonus weights of a row (draws)
   uint32_t soff[MAXSEG + 1];                    // pool offset of each (row, part) list
   uint32_t off[MAXROWS + 1];                    // pool offset of each used row
   uint32_t whist[NWAVE][256];                   // per-wavefront radix histograms
   uint32_t st_thr[MAXROWS];                     // kept keys are >= st_thr (multi-pass path)
   uint32_t st_cnt[MAXROWS];                     // kept survivors of each row (list path)
+  uint32_t st_sorted[MAXROWS];                  // 1 when the row's kept survivors are in ascending id
   uint32_t st_arg[MAXROWS];                     // argmax (T == 0)
   float st_zmax[MAXROWS];
   double st_S[MAXROWS];                         // normaliser over the kept keys
@@ -41,6 +42,7 @@ struct FinSmem {
   double pos_p[SV_MAX_GAMMA];
   double pos_q[SV_MAX_GAMMA];
   double pos_alpha[SV_MAX_GAMMA];
+  int32_t cand_tok[SV_MAX_GAMMA + 1];           // drawn token if the first rejection is at i (i = g: bonus)
   union {
     uint32_t h32[256];
     unsigned long long h64[256];
@@ -65,18 +67,25 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // fn(key, id, val) for every entry of ents[o, o+n) in order, seen by every
 // lane of the wavefront through readlane (no LDS access per entry).  Must be
 // called with the whole wavefront active and wavefront-uniform o, n.
-template <class F>
-__device__ __forceinline__ void wave_broadcast(const uint2* ents, const float* vals, int o, int n, F fn) {
+template <typename VT, class F>
+__device__ __forceinline__ void wave_broadcast(const uint2* ents, const VT* vals, int o, int n, F fn) {
   const int lane = threadIdx.x & 63;
   for (int b = 0; b < n; b += 64) {
     const int i = b + lane;
     const uint2 e = i < n ? ents[o + i] : make_uint2(0u, 0u);
-    const float v = i < n ? vals[o + i] : 0.0f;
+    const VT v = i < n ? vals[o + i] : (VT)0;
     const int m = min(64, n - b);
     for (int l = 0; l < m; ++l) {
       const uint32_t key = (uint32_t)__builtin_amdgcn_readlane((int)e.x, l);
       const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)e.y, l);
-      const float val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+      VT val;
+      if constexpr (sizeof(VT) == 4) {
+        val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+      } else {
+        const long long bv = __double_as_longlong(v);
+        val = __longlong_as_double(((long long)__builtin_amdgcn_readlane((int)(bv >> 32), l) << 32) |
+                                   (unsigned int)__builtin_amdgcn_readlane((int)(bv & 0xFFFFFFFFll), l));
+      }
       fn(key, id, val);
     }
   }
@@ -137,12 +146,12 @@ __device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m)
   const uint32_t kth = n > (int)m.k ? wave_kth_largest<Key<ET>::LEVELS>(s.pool + o, n, m.k, hist) : 1u;
   uint32_t kmax = 0;
   for (int i = lane; i < n; i += 64) kmax = max(kmax, s.pool[o + i].x);
-  kmax = wave_max_u32(kmax);
+  kmax = wave_max_dpp(kmax);
   if (m.mode == MODE_GREEDY) {
     uint32_t best = 0xFFFFFFFFu;
     for (int i = lane; i < n; i += 64)
       if (s.pool[o + i].x == kmax) best = min(best, s.pool[o + i].y);
-    best = wave_min_u32(best);
+    best = wave_min_dpp(best);
     if (lane == 0) s.st_arg[r] = best;
     return;
   }
@@ -155,7 +164,7 @@ __device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m)
     s.pv[o + i] = e;
     S += (double)e;
   }
-  S = wave_sum_d(S);
+  S = wave_sum_dpp(S);
   wave_lds_sync();
   if (m.tp < 1.0f) {
     // The nucleus: order the survivors by (value desc, id asc); the cut is
@@ -179,7 +188,7 @@ __device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m)
         cut_key = e.x;
       }
     }
-    const uint32_t best = wave_min_u32(cut_rank);
+    const uint32_t best = wave_min_dpp(cut_rank);
     const unsigned long long who = __ballot(cut_rank == best && best != 0xFFFFFFFFu);
     if (best != 0xFFFFFFFFu) {
       const int src = __ffsll((long long)who) - 1;
@@ -187,15 +196,114 @@ __device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m)
       n = wave_keep(s, o, n, thr);
       double S2 = 0.0;
       for (int i = lane; i < n; i += 64) S2 += (double)s.pv[o + i];
-      S = wave_sum_d(S2);
+      S = wave_sum_dpp(S2);
     }
   }
+  // Are the kept survivors in ascending id (the streaming select leaves them
+  // so)?
+  bool unsorted = false;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + lane;
+    unsorted |= i > 0 && i < n && s.pool[o + i].y <= s.pool[o + i - 1].y;
+  }
+  unsorted = __ballot(unsorted) != 0ull;
   if (lane == 0) {
     s.st_cnt[r] = (uint32_t)n;
+    s.st_sorted[r] = unsorted ? 0u : 1u;
     s.st_zmax[r] = zmax;
     s.st_S[r] = S;
     s.st_invS[r] = 1.0 / S;
   }
+}
+
+// Position of vocabulary id v among the ascending ids pool[o, o+n), or -1.
+__device__ __forceinline__ int find_sorted(const FinSmem& s, int o, int n, uint32_t v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s.pool[o + mid].y < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < n && s.pool[o + lo].y == v) ? lo : -1;
+}
+
+// Inclusive prefix sum of a double over the wave (lane order).
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+  v = dpp_add_f64<0x111, 0xF>(v);
+  v = dpp_add_f64<0x112, 0xF>(v);
+  v = dpp_add_f64<0x114, 0xF>(v);
+  v = dpp_add_f64<0x118, 0xF>(v);
+  v = dpp_add_f64<0x142, 0xA>(v);
+  v = dpp_add_f64<0x143, 0xC>(v);
+  return v;
+}
+
+// Rows with survivors in ascending id, by one wavefront: for i < g, p_i(x_i),
+// q_i(x_i), alpha_i and the residual draw at i (weights max(0, p_i - q_i));
+// for i == g the bonus draw (weights p_g).  q(v) is found by binary search
+// in q's ascending ids, and the inverse CDF in ascending id is a prefix scan
+// of the weights in list order.  Returns the drawn token.
+__device__ __forceinline__ int wave_position_draw_sorted(FinSmem& s, int i, int x, const Mode& m, float ures) {
+  const int lane = threadIdx.x & 63;
+  const bool resid = i < m.g;
+  const int rp = i, rq = m.g + 1 + i;
+  const int op = (int)s.off[rp], np = (int)s.st_cnt[rp];
+  const int oq = resid ? (int)s.off[rq] : 0, nq = resid ? (int)s.st_cnt[rq] : 0;
+  const double ip = s.st_invS[rp], iq = resid ? s.st_invS[rq] : 0.0;
+  double al = 0.0, px = 0.0, qx = 0.0, zl = 0.0, zp = 0.0;
+  for (int b = 0; b < np; b += 64) {
+    const int j = b + lane;
+    if (j < np) {
+      const uint32_t id = s.pool[op + j].y;
+      const double p = (double)s.pv[op + j] * ip;
+      double q = 0.0;
+      if (resid) {
+        const int qi = find_sorted(s, oq, nq, id);
+        q = qi >= 0 ? (double)s.pv[oq + qi] * iq : 0.0;
+      }
+      al += fmin(p, q);
+      if (id == (uint32_t)x) px = p;
+      const double w = resid ? fmax(p - q, 0.0) : p;
+      s.wts[op + j] = w;
+      zl += w;
+      zp += p;
+    }
+  }
+  if (resid) {
+    for (int j = lane; j < nq; j += 64)
+      if (s.pool[oq + j].y == (uint32_t)x) qx = (double)s.pv[oq + j] * iq;
+    al = wave_sum_dpp(al);
+    px = wave_sum_dpp(px);
+    qx = wave_sum_dpp(qx);
+    if (lane == 0) {
+      s.pos_p[i] = px;
+      s.pos_q[i] = qx;
+      s.pos_alpha[i] = al;
+    }
+  }
+  double Z = wave_sum_dpp(zl);
+  const bool fallback = !(Z > 0.0);   // zero residual mass: draw from the target itself
+  if (fallback) Z = wave_sum_dpp(zp);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const double target = (double)ures * Z;
+  double base = 0.0;
+  int lastpos = -1;
+  for (int b = 0; b < np; b += 64) {
+    const int j = b + lane;
+    double w = 0.0;
+    if (j < np) w = fallback ? (double)s.pv[op + j] * ip : s.wts[op + j];
+    const double c = base + wave_incl_scan_f64(w);
+    const unsigned long long hit = __ballot(j < np && c > target);
+    if (hit) return (int)s.pool[op + b + __ffsll((long long)hit) - 1].y;
+    const unsigned long long posw = __ballot(w > 0.0);
+    if (posw) lastpos = b + 63 - __clzll((long long)posw);
+    const long long cb = __double_as_longlong(c);
+    base = __longlong_as_double(((long long)__builtin_amdgcn_readlane((int)(cb >> 32), 63) << 32) |
+                                (unsigned int)__builtin_amdgcn_readlane((int)(cb & 0xFFFFFFFFll), 63));
+  }
+  return lastpos >= 0 ? (int)s.pool[op + lastpos].y : (int)s.pool[op + np - 1].y;   // rounding left no crossing
 }
 
 // p_i(x_i), q_i(x_i) and alpha_i for one position, by one wavefront.
@@ -225,9 +333,9 @@ __device__ __forceinline__ void wave_position(FinSmem& s, int i, int x, const Mo
   }
   for (int j = lane; j < nq; j += 64)
     if (s.pool[oq + j].y == (uint32_t)x) qx = (double)s.pv[oq + j] * iq;
-  al = wave_sum_d(al);
-  px = wave_sum_d(px);
-  qx = wave_sum_d(qx);
+  al = wave_sum_dpp(al);
+  px = wave_sum_dpp(px);
+  qx = wave_sum_dpp(qx);
   if (lane == 0) {
     s.pos_p[i] = px;
     s.pos_q[i] = qx;
@@ -254,14 +362,14 @@ __device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float
     float qe = 0.0f;
     wave_broadcast(s.pool, s.pv, oq, nq, [&](uint32_t, uint32_t qid, float val) { qe = qid == id ? val : qe; });
     const double w = resid ? fmax(p - (double)qe * iq, 0.0) : p;
-    if (j < np) s.wts[op + j] = (float)w;
+    if (j < np) s.wts[op + j] = w;
     zl += w;
     zp += p;
   }
-  double Z = wave_sum_d(zl);
+  double Z = wave_sum_dpp(zl);
   if (!(Z > 0.0)) {   // zero residual mass: draw from the target itself
-    for (int j = lane; j < np; j += 64) s.wts[op + j] = (float)((double)s.pv[op + j] * ip);
-    Z = wave_sum_d(zp);
+    for (int j = lane; j < np; j += 64) s.wts[op + j] = (double)s.pv[op + j] * ip;
+    Z = wave_sum_dpp(zp);
   }
   wave_lds_sync();
   const double target = (double)ures * Z;
@@ -270,15 +378,15 @@ __device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float
     const int j = b + lane;
     const uint32_t v = j < np ? s.pool[op + j].y : 0xFFFFFFFFu;
     double run = 0.0;
-    wave_broadcast(s.pool, s.wts, op, np, [&](uint32_t, uint32_t id, float w) { run += id <= v ? (double)w : 0.0; });
+    wave_broadcast(s.pool, s.wts, op, np, [&](uint32_t, uint32_t id, double w) { run += id <= v ? w : 0.0; });
     if (j < np) {
-      if (s.wts[op + j] > 0.0f) lastpos = max(lastpos, v + 1u);
+      if (s.wts[op + j] > 0.0) lastpos = max(lastpos, v + 1u);
       if (run > target) best = min(best, v);
     }
   }
-  best = wave_min_u32(best);
+  best = wave_min_dpp(best);
   if (best != 0xFFFFFFFFu) return (int)best;
-  return (int)wave_max_u32(lastpos) - 1;   // rounding left no crossing
+  return (int)wave_max_dpp(lastpos) - 1;   // rounding left no crossing
 }
 
 // ===========================================================================
@@ -640,7 +748,19 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     if (ok) {
       for (int r = wave; r < R; r += NWAVE) pool_row_stats<ET>(s, r, m);
       __syncthreads();
-      for (int i = wave; i < m.g; i += NWAVE) wave_position(s, i, xb[i], m);
+      // Every position's p(x), q(x), overlap and residual draw (as if the
+      // first rejection were there), and the bonus draw, in parallel; the
+      // acceptance test then only picks one of the drawn tokens.
+      for (int i = wave; i <= m.g; i += NWAVE) {
+        int tk;
+        if (m.mode != MODE_GREEDY && s.st_sorted[i] && (i == m.g || s.st_sorted[m.g + 1 + i])) {
+          tk = wave_position_draw_sorted(s, i, i < m.g ? xb[i] : -1, m, ub[G]);
+        } else {
+          if (i < m.g) wave_position(s, i, xb[i], m);
+          tk = pool_draw(s, m, i, ub[G]);
+        }
+        if (lane == 0) s.cand_tok[i] = tk;
+      }
       __syncthreads();
     }
   } else if (ok && dense) {
@@ -656,11 +776,10 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       if (i < m.g) rej = !((double)ub[i] * s.pos_q[i] < s.pos_p[i]);
       const unsigned long long mask = __ballot(rej);
       const int nn = mask ? __ffsll((long long)mask) - 1 : m.g;
-      if (!dense) {
-        const int t = pool_draw(s, m, nn, ub[G]);
-        if (i == 0) s.bc[6] = (uint32_t)t;
+      if (i == 0) {
+        if (!dense) s.bc[6] = (uint32_t)s.cand_tok[nn];
+        s.bc[7] = (uint32_t)nn;
       }
-      if (i == 0) s.bc[7] = (uint32_t)nn;
     }
     __syncthreads();
     n = (int)s.bc[7];

@@ -245,18 +245,25 @@ struct PChunk {
     return vf;
   }
 
-  // Copy the flagged vectors to staging slots rank, rank + 1, ... (in
-  // vector order) with their vector index in the row.
-  __device__ __forceinline__ void stage(uint32_t vf, uint32_t rank, uint4* dst, uint32_t* didx) const {
-    uint32_t rk = rank;
+  // Copy the flagged vectors of the step to staging slots base, base + 1,
+  // ... in ascending vector index (vector slot j major, lane minor), with
+  // their vector index in the row, so the candidates drained from them come
+  // out in ascending vocabulary id.  Returns the number staged.
+  __device__ __forceinline__ uint32_t stage(uint32_t vf, uint32_t base, uint4* dst, uint32_t* didx) const {
+    const uint64_t below = lanemask_lt();
+    uint32_t n = base;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (vf & (1u << j)) {
-        dst[rk] = raw[j];
-        didx[rk] = (uint32_t)(first + 64 * j);
-        ++rk;
+      const bool f = (vf >> j) & 1u;
+      const uint64_t bal = __ballot(f);
+      if (f) {
+        const uint32_t slot = n + (uint32_t)__popcll(bal & below);
+        dst[slot] = raw[j];
+        didx[slot] = (uint32_t)(first + 64 * j);
       }
+      n += (uint32_t)__popcll(bal);
     }
+    return n - base;
   }
 };
 
@@ -542,8 +549,7 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
         }
       }
     }
-    ch.stage(vf, staged + vincl - nv, w.stage, w.sidx);
-    staged += tv;
+    staged += ch.stage(vf, staged, w.stage, w.sidx);
     wave_sync_lds();
     if (staged >= DRAIN) drain();
   };

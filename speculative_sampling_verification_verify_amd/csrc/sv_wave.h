@@ -450,7 +450,9 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
   constexpr int LEVELS = Key<uint16_t>::LEVELS;
   constexpr int NVC = WVPL;
   constexpr int SPAN = 64 * NVC;          // vectors per step
-  constexpr uint32_t DRAIN = 32;          // staged vectors per drain round (<= 8 * DRAIN appends)
+  // Staged vectors per drain round (<= 8 per vector appended): a full
+  // wavefront when the buffer has the room, half of one for large k.
+  const uint32_t db = k <= 160u ? 64u : 32u;
   const int lane = threadIdx.x & 63;
   const int v0 = e0 / 8;
   const int lim = e1 / 8;
@@ -461,14 +463,14 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
   bool demoted = false;
   uint32_t bad = 0;                       // lane: NaN / +inf among the candidates
   u16x2 um = {(unsigned short)0, (unsigned short)0};   // unsigned maxima of the patterns seen
-  const uint32_t refresh_at = min(k + max(32u, k / 4), (uint32_t)WCB - 8u * DRAIN);
+  const uint32_t refresh_at = min(k + max(32u, k / 4), (uint32_t)WCB - 8u * db);
 
   // Turn the staged vectors into candidates (keys >= the current t).
   auto drain = [&]() {
-    for (uint32_t r0 = 0; r0 < staged; r0 += DRAIN) {
-      if (fill + 8u * DRAIN > (uint32_t)WCB) {
+    for (uint32_t r0 = 0; r0 < staged; r0 += db) {
+      if (fill + 8u * db > (uint32_t)WCB) {
         buffer_select<LEVELS>(w, k, t, fill);
-        if (fill + 8u * DRAIN > (uint32_t)WCB) {   // more ties at the k-th largest than the buffer holds
+        if (fill + 8u * db > (uint32_t)WCB) {   // more ties at the k-th largest than the buffer holds
           demoted = true;
           staged = 0;
           return;
@@ -477,7 +479,7 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
       const bool pos = t > 0x8000u;
       const int T = bound_of(t, pos);
       const uint32_t si = r0 + lane;
-      const bool have = lane < (int)DRAIN && si < staged;
+      const bool have = (uint32_t)lane < db && si < staged;
       uint4 d = make_uint4(0u, 0u, 0u, 0u);
       uint32_t vi = 0;
       if (have) {
@@ -551,7 +553,7 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
     }
     staged += ch.stage(vf, staged, w.stage, w.sidx);
     wave_sync_lds();
-    if (staged >= DRAIN) drain();
+    if (staged >= (uint32_t)SCAP - 32u) drain();   // drain in large batches
   };
 
   // The descriptor covers the row up to the part's end.

@@ -23,6 +23,7 @@
 // alpha = sum min(p, q), mtandhj summary, "How to choose gamma".
 
 #include "sv_wave.h"
+#include "sv_pair.h"
 #include "sv_finish.h"
 
 #include <math.h>
@@ -67,8 +68,26 @@ static Plan plan(int B, int G, int V, int dtype) {
   return p;
 }
 
+// Dense (unfiltered / large top-k / top-p) sequences run the pair kernel:
+// rows of up to 4 / 16 / 64 KB are held in LDS by 64 / 256 / 1024-thread
+// workgroups; longer rows are streamed by 1024-thread workgroups as long as
+// the residual pass fits its tile table.  Returns the workgroup size (0: the
+// finisher's multi-pass procedure handles dense rows) and sets *lds_bytes to
+// the dynamic LDS of the launch.
+static int pair_variant(int V, int dtype, bool vector_ok, size_t* lds_bytes) {
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  const size_t row = ((size_t)V * es + 15) / 16 * 16;
+  *lds_bytes = 2 * row;
+  if (row <= 4096) return 64;
+  if (row <= 16384) return 256;
+  if (row <= (size_t)PAIR_LDS_ROW_MAX) return 1024;
+  *lds_bytes = 0;
+  const size_t units = vector_ok ? (size_t)V * es / 16 : (size_t)V;
+  return units <= (size_t)1024 * PAIR_MAXTILE ? -1024 : 0;   // negative: streamed rows
+}
+
 struct Layout {
-  size_t seq_flags_off, counters_bytes, counts_off, lists_off, total;
+  size_t seq_flags_off, counters_bytes, pos_off, counts_off, lists_off, total;
 };
 
 static Layout layout(int B, int G, const Plan& p) {
@@ -77,7 +96,8 @@ static Layout layout(int B, int G, const Plan& p) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L.seq_flags_off = 0;
   L.counters_bytes = up(L.seq_flags_off + (size_t)B * 4);
-  L.counts_off = L.counters_bytes;
+  L.pos_off = L.counters_bytes;
+  L.counts_off = up(L.pos_off + (size_t)B * (G + 1) * sizeof(PosRec));
   L.lists_off = up(L.counts_off + R * p.NP * 4);
   L.total = L.lists_off + R * p.NP * SEG * sizeof(uint2);
   return L;
@@ -109,6 +129,31 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
   if (e != hipSuccess) return e;
   if (g_stage_end) {
     e = hipEventRecord(g_stage_end, st);
+    if (e != hipSuccess) return e;
+  }
+  if (a.pair) {
+    size_t plds = 0;
+    const int pv = pair_variant(a.V, sizeof(ET) == 2 ? SV_BF16 : SV_FP32, VECTOR, &plds);
+    const void* kfn = nullptr;
+    switch (pv) {
+      case 64: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 64, VECTOR, true>); break;
+      case 256: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 256, VECTOR, true>); break;
+      case 1024: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 1024, VECTOR, true>); break;
+      case -1024: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 1024, VECTOR, false>); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (plds) {
+      e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+      if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)(a.B * (a.G + 1)));
+    switch (pv) {
+      case 64: hipLaunchKernelGGL((pair_kernel<ET, 64, VECTOR, true>), grid, dim3(64), plds, st, a); break;
+      case 256: hipLaunchKernelGGL((pair_kernel<ET, 256, VECTOR, true>), grid, dim3(256), plds, st, a); break;
+      case 1024: hipLaunchKernelGGL((pair_kernel<ET, 1024, VECTOR, true>), grid, dim3(1024), plds, st, a); break;
+      default: hipLaunchKernelGGL((pair_kernel<ET, 1024, VECTOR, false>), grid, dim3(1024), 0, st, a); break;
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((finish_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), fin_lds, st, a);
@@ -191,6 +236,9 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   a.out_pq = out_pq;
   a.seq_flags = reinterpret_cast<uint32_t*>(ws + Lw.seq_flags_off);
   a.counts = reinterpret_cast<int32_t*>(ws + Lw.counts_off);
+  a.pos = reinterpret_cast<PosRec*>(ws + Lw.pos_off);
+  size_t pair_lds = 0;
+  a.pair = pair_variant(V, dtype, vector_ok, &pair_lds) != 0 && (long long)B * (gamma_max + 1) <= 0x7FFFFFFFLL ? 1 : 0;
   a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);
   hipStream_t st = (hipStream_t)stream;
   const size_t fin_lds = sizeof(FinSmem);

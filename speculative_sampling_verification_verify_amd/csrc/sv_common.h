@@ -16,6 +16,13 @@ constexpr int MAXNP = 16;          // parts per logit row
 constexpr uint32_t F_BAD = 1u;     // NaN or +inf among the logits
 constexpr uint32_t F_DEMOTE = 2u;  // survivor lists unusable: recompute from the logits
 
+// Result of the pair-resident kernel for one (sequence, position) (workspace).
+struct PosRec {
+  double px, qx, alpha;   // p_i(x_i), q_i(x_i), overlap (position < gamma_b)
+  int32_t tok;            // draw if the first rejection is here (bonus draw at gamma_b)
+  uint32_t bad;           // a row of the pair has NaN / +inf or no finite logit
+};
+
 struct Args {
   const void* p;
   const void* q;
@@ -36,6 +43,8 @@ struct Args {
   uint32_t* seq_flags;    // [B]     F_* bits, set by the select, cleared by the finisher
   int32_t* counts;        // [R][NP] survivors per (row, part)
   uint2* lists;           // [R][NP][SEG] (key, vocabulary id)
+  PosRec* pos;            // [B][G+1] pair-resident results
+  int pair;               // 1 when the pair-resident kernel ran for the dense sequences
 };
 
 struct Mode {

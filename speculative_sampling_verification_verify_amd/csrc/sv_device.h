@@ -152,6 +152,24 @@ __device__ __forceinline__ double wave_sum_dpp(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// Inclusive prefix sum of a double over the wave (lane order).
+__device__ __forceinline__ double wave_incl_scan_f64(double v) {
+  v = dpp_add_f64<0x111, 0xF>(v);
+  v = dpp_add_f64<0x112, 0xF>(v);
+  v = dpp_add_f64<0x114, 0xF>(v);
+  v = dpp_add_f64<0x118, 0xF>(v);
+  v = dpp_add_f64<0x142, 0xA>(v);
+  v = dpp_add_f64<0x143, 0xC>(v);
+  return v;
+}
+// Lane l's double, read uniformly by the whole wave (l wave-uniform).
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 // Block-wide reductions through a small LDS scratch of NWAVE entries.
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T* scratch) {
@@ -232,12 +250,12 @@ __device__ __forceinline__ T block_excl_scan(T v, T* scratch, T* total) {
 // calls this with the same k.  Returns the exact k-th largest key, or 0 when
 // fewer than k keys exist.  hist: 256 words of LDS; bc: 2 words of LDS.
 // ---------------------------------------------------------------------------
-template <int LEVELS, class Feed>
+template <int LEVELS, int NTHR = NT, class Feed>
 __device__ __forceinline__ uint32_t block_kth_largest(Feed feed, uint32_t k, uint32_t* hist, uint32_t* bc) {
   uint32_t prefix = 0, pmask = 0, krem = k;
   for (int lvl = 0; lvl < LEVELS; ++lvl) {
     const int shift = 8 * (LEVELS - 1 - lvl);
-    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    for (int i = threadIdx.x; i < 256; i += NTHR) hist[i] = 0;
     __syncthreads();
     feed([&](uint32_t key) {
       if (key != 0 && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);

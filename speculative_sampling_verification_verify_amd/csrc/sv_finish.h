@@ -227,17 +227,6 @@ __device__ __forceinline__ int find_sorted(const FinSmem& s, int o, int n, uint3
   return (lo < n && s.pool[o + lo].y == v) ? lo : -1;
 }
 
-// Inclusive prefix sum of a double over the wave (lane order).
-__device__ __forceinline__ double wave_incl_scan_f64(double v) {
-  v = dpp_add_f64<0x111, 0xF>(v);
-  v = dpp_add_f64<0x112, 0xF>(v);
-  v = dpp_add_f64<0x114, 0xF>(v);
-  v = dpp_add_f64<0x118, 0xF>(v);
-  v = dpp_add_f64<0x142, 0xA>(v);
-  v = dpp_add_f64<0x143, 0xC>(v);
-  return v;
-}
-
 // Rows with survivors in ascending id, by one wavefront: for i < g, p_i(x_i),
 // q_i(x_i), alpha_i and the residual draw at i (weights max(0, p_i - q_i));
 // for i == g the bonus draw (weights p_g).  q(v) is found by binary search
@@ -704,6 +693,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   const float* ub = a.u + (size_t)b * (G + 1);
   const int32_t* xb = a.draft + (size_t)b * G;
   bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG;
+  const bool from_pairs = a.pair && m.mode == MODE_DENSE;
   uint32_t badin = 0;
   for (int i = threadIdx.x; i < m.g; i += NT) {
     const int x = xb[i];
@@ -763,6 +753,21 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       }
       __syncthreads();
     }
+  } else if (ok && dense && from_pairs) {
+    // Per-position results of the pair-resident kernel.
+    const PosRec* rec = a.pos + (size_t)b * (G + 1);
+    uint32_t badr = 0;
+    for (int i = threadIdx.x; i <= m.g; i += NT) {
+      const PosRec r = rec[i];
+      badr |= r.bad;
+      s.cand_tok[i] = r.tok;
+      if (i < m.g) {
+        s.pos_p[i] = r.px;
+        s.pos_q[i] = r.qx;
+        s.pos_alpha[i] = r.alpha;
+      }
+    }
+    ok = block_or_u32(badr, s.red_u) == 0;
   } else if (ok && dense) {
     ok = dense_row_stats<ET, VECTOR>(a, s, b, m);
     if (ok) dense_positions<ET, VECTOR>(a, s, b, m);
@@ -777,7 +782,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       const unsigned long long mask = __ballot(rej);
       const int nn = mask ? __ffsll((long long)mask) - 1 : m.g;
       if (i == 0) {
-        if (!dense) s.bc[6] = (uint32_t)s.cand_tok[nn];
+        if (!dense || from_pairs) s.bc[6] = (uint32_t)s.cand_tok[nn];
         s.bc[7] = (uint32_t)nn;
       }
     }
@@ -785,7 +790,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     n = (int)s.bc[7];
     tok = (int)s.bc[6];
     __syncthreads();
-    if (dense) tok = dense_draw<ET, VECTOR>(a, s, b, m, n, ub[G]);
+    if (dense && !from_pairs) tok = dense_draw<ET, VECTOR>(a, s, b, m, n, ub[G]);
   }
   int32_t* ot = a.out_tokens + (size_t)b * (G + 1);
   float* oa = a.out_alpha + (size_t)b * G;

@@ -172,13 +172,13 @@ struct PT {
 // and probabilities agree element by element.
 __device__ __forceinline__ float ew(float z, float zmax, float c) { return __builtin_amdgcn_exp2f((z - zmax) * c); }
 
-// e * 2^fb truncated to an integer (e in [0, 1]; 0 below 2^-fb).
-__device__ __forceinline__ unsigned long long fixq(float e, int fb) {
-  const uint32_t b = __float_as_uint(e);
-  const int sh = (int)(b >> 23) - 150 + fb;
-  const unsigned long long man = (unsigned long long)((b & 0x7FFFFFu) | 0x800000u);
-  if (sh >= 0) return man << sh;
-  return sh > -24 ? man >> (-sh) : 0ull;
+// floor(e * 2^fb) as a 64-bit integer (e in [0, 1], fb <= 62): e * 2^fb is
+// exact in fp32; its high and low 32-bit halves are split off exactly.
+__device__ __forceinline__ unsigned long long fixq(float e, float two_fb, float two_fb32) {
+  const float t = e * two_fb;
+  const float hi = floorf(e * two_fb32);
+  const float lo = fmaf(-hi, 4294967296.0f, t);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 // Value bin of a weight: 32 bins per binade, bin 0 holding e = 1.  Bins are
 // monotone (non-increasing) in the logit, so a bin is a run of adjacent keys.
@@ -255,43 +255,81 @@ __device__ __forceinline__ uint32_t mass_select(Feed feed, double tau, unsigned 
   return prefix;
 }
 
-// Processed distribution of one row: p(z) = (key(z) >= thr) ? e(z) * sp : 0.
+// Processed distribution of one row: p(z) = (z >= zthr) ? e(z) * sp : 0.
+// Keys and values order the same way (+0 and -0 share a key), so the value
+// test equals the key test key(z) >= thr.
 struct RowStat {
-  uint32_t thr;
-  float zmax, c, sp;
+  float zthr, zmax, c, sp;
 };
 
-// Row statistics.  src: the row (LDS or global), NU units; kmax: its largest key.
+template <typename ET>
+__device__ __forceinline__ uint32_t key_of_value(float z) {
+  if constexpr (sizeof(ET) == 2) return Key<ET>::of_bits(__float_as_uint(z) >> 16);
+  else return Key<ET>::of_bits(__float_as_uint(z));
+}
+
+template <typename ET>
+__device__ __forceinline__ float key_floor_value(uint32_t thr) {
+  return thr <= Key<ET>::NEG_INF ? -INFINITY : Key<ET>::value(thr);
+}
+
+// Calls fn(unit) for every unit of the calling thread; streamed rows keep
+// UNR loads in flight.
+template <typename ET, int NTP, bool VECTOR, bool LDSR, class F>
+__device__ __forceinline__ void row_units(const typename PT<ET, VECTOR>::U* src, int NU, F fn) {
+  using T = PT<ET, VECTOR>;
+  constexpr int UNR = LDSR ? 2 : 4;
+  int ui = threadIdx.x;
+  for (; ui + (UNR - 1) * NTP < NU; ui += UNR * NTP) {
+    typename T::U u[UNR];
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) u[r] = src[ui + r * NTP];
+#pragma unroll
+    for (int r = 0; r < UNR; ++r) fn(u[r]);
+  }
+  for (; ui < NU; ui += NTP) fn(src[ui]);
+}
+// Calls fn(raw) for every element of the calling thread's units.
+template <typename ET, int NTP, bool VECTOR, bool LDSR, class F>
+__device__ __forceinline__ void row_each(const typename PT<ET, VECTOR>::U* src, int NU, F fn) {
+  using T = PT<ET, VECTOR>;
+  row_units<ET, NTP, VECTOR, LDSR>(src, NU, [&](const typename T::U& u) {
+    T::each(u, [&](int, uint32_t raw) { fn(raw); });
+  });
+}
+
+// Row statistics.  src: the row (LDS or global), NU units; zmax: its largest
+// logit.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
-__device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* src, int NU, uint32_t kmax,
+__device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* src, int NU, float zmax,
                                              const Args& a, const Mode& m, int k, PairSmem<NTP>& s,
                                              PairExtra<LDSR>& ps) {
   using T = PT<ET, VECTOR>;
   constexpr int LEVELS = Key<ET>::LEVELS;
   RowStat st;
-  st.zmax = Key<ET>::value(kmax);
+  st.zmax = zmax;
   st.c = LOG2E_F / m.T;
-  st.thr = 1;
-  const float zmax = st.zmax, c = st.c;
+  st.zthr = -INFINITY;
+  const float c = st.c;
   const int fb = a.fixbits;
-  // fn(key, raw) over the calling thread's elements.
-  auto row_each = [&](auto fn) {
-    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
-      const typename T::U u = src[ui];
-      T::each(u, [&](int, uint32_t raw) { fn(T::key(raw), raw); });
-    }
-  };
+  const float two_fb = ldexpf(1.0f, fb), two_fb32 = ldexpf(1.0f, fb - 32);
+  auto each = [&](auto fn) { row_each<ET, NTP, VECTOR, LDSR>(src, NU, fn); };
   if (k > KMAX_SPARSE && k < a.V) {
     const uint32_t kth = block_kth_largest<LEVELS, NTP>(
-        [&](auto fn) { row_each([&](uint32_t uk, uint32_t) { fn(uk); }); }, (uint32_t)k, s.hist.h32, s.bc);
-    st.thr = kth ? kth : 1u;
+        [&](auto fn) { each([&](uint32_t raw) { fn(T::key(raw)); }); }, (uint32_t)k, s.hist.h32, s.bc);
+    st.zthr = key_floor_value<ET>(kth ? kth : 1u);
   }
-  const uint32_t thr0 = st.thr;
+  const float zthr = st.zthr;
   if (!(m.tp < 1.0f)) {
-    // No nucleus cut: S = sum of e over the kept keys.
+    // No nucleus cut: S = sum of e over the kept elements.
     double sl = 0.0;
-    row_each([&](uint32_t uk, uint32_t raw) {
-      if (uk >= thr0) sl += (double)ew(T::val(raw), zmax, c);
+    row_units<ET, NTP, VECTOR, LDSR>(src, NU, [&](const typename T::U& u) {
+      float us = 0.0f;
+      T::each(u, [&](int, uint32_t raw) {
+        const float z = T::val(raw);
+        us += z >= zthr ? ew(z, zmax, c) : 0.0f;
+      });
+      sl += (double)us;
     });
     st.sp = (float)(1.0 / pb_sum_f64<NTP>(sl, s.red_d));
     return st;
@@ -299,25 +337,27 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
   if (m.tp <= 0.0f) {
     // Only the maximal logit (with its ties) survives.
     unsigned long long cl = 0;
-    row_each([&](uint32_t uk, uint32_t) { cl += uk == kmax ? 1ull : 0ull; });
+    each([&](uint32_t raw) { cl += T::val(raw) == zmax ? 1ull : 0ull; });
     const unsigned long long cnt = pb_sum_u64<NTP>(cl, s.red_u64);
-    st.thr = kmax;
+    st.zthr = zmax;
     st.sp = (float)(1.0 / (double)cnt);
     return st;
   }
-  const double fscale = ldexp(1.0, fb);
+  auto fx = [&](float z) { return fixq(ew(z, zmax, c), two_fb, two_fb32); };
   unsigned long long S, mass = 0;
   uint32_t tstar = 0;
   if constexpr (LDSR) {
     unsigned long long sl = 0;
-    row_each([&](uint32_t uk, uint32_t raw) {
-      if (uk >= thr0) sl += fixq(ew(T::val(raw), zmax, c), fb);
+    each([&](uint32_t raw) {
+      const float z = T::val(raw);
+      if (z >= zthr) sl += fx(z);
     });
     S = pb_sum_u64<NTP>(sl, s.red_u64);
     tstar = mass_select<LEVELS, NTP>(
         [&](auto fn) {
-          row_each([&](uint32_t uk, uint32_t raw) {
-            if (uk >= thr0) fn(uk, fixq(ew(T::val(raw), zmax, c), fb));
+          each([&](uint32_t raw) {
+            const float z = T::val(raw);
+            if (z >= zthr) fn(T::key(raw), fx(z));
           });
         },
         (double)m.tp * (double)S, 0ull, s.hist.h64, s.bc, &mass);
@@ -328,10 +368,11 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
     if (threadIdx.x == 0) ps.ncol = 0;
     __syncthreads();
     unsigned long long sl = 0;
-    row_each([&](uint32_t uk, uint32_t raw) {
-      if (uk >= thr0) {
-        const float e = ew(T::val(raw), zmax, c);
-        const unsigned long long f = fixq(e, fb);
+    each([&](uint32_t raw) {
+      const float z = T::val(raw);
+      if (z >= zthr) {
+        const float e = ew(z, zmax, c);
+        const unsigned long long f = fixq(e, two_fb, two_fb32);
         if (f) {
           sl += f;
           atomicAdd(&ps.vh[vbin(e)], f);
@@ -366,58 +407,79 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
           }
           ab += h;
         }
-        s.bc[5] = (uint32_t)cb;
-        s.bc[6] = (uint32_t)ab;
-        s.bc[7] = (uint32_t)(ab >> 32);
+        // The bin's key range [klo, khi): klo = smallest key whose bin is
+        // <= cb, khi the same for cb - 1 (bins fall as keys rise).
+        auto first_key_at_most = [&](int bin) {
+          uint32_t lo = Key<ET>::NEG_INF, hi = key_of_value<ET>(zmax);   // bin(hi) == 0
+          while (lo < hi) {
+            const uint32_t mid = lo + (hi - lo) / 2;
+            if (vbin(ew(Key<ET>::value(mid), zmax, c)) <= bin) hi = mid;
+            else lo = mid + 1;
+          }
+          return lo;
+        };
+        const uint32_t klo = first_key_at_most(cb);
+        const uint32_t khi = cb > 0 ? first_key_at_most(cb - 1) : Key<ET>::POS_INF;
+        s.bc[5] = klo;
+        s.bc[6] = khi;
+        s.bd[0] = __longlong_as_double((long long)ab);
+        s.bd[1] = __longlong_as_double((long long)ps.vh[cb]);
       }
     }
     __syncthreads();
-    const int cbin = (int)s.bc[5];
-    const unsigned long long above = ((unsigned long long)s.bc[7] << 32) | s.bc[6];
-    // Gather the crossing bin's keys.
-    row_each([&](uint32_t uk, uint32_t raw) {
-      if (uk >= thr0 && vbin(ew(T::val(raw), zmax, c)) == cbin) {
-        const uint32_t slot = atomicAdd(&ps.ncol, 1u);
-        if (slot < (uint32_t)PAIR_NCAP) ps.keys[slot] = uk;
-      }
-    });
-    __syncthreads();
-    const uint32_t n = ps.ncol;
-    if (n <= (uint32_t)PAIR_NCAP) {
-      tstar = mass_select<LEVELS, NTP>(
-          [&](auto fn) {
-            for (uint32_t j = threadIdx.x; j < n; j += NTP) {
-              const uint32_t uk = ps.keys[j];
-              fn(uk, fixq(ew(Key<ET>::value(uk), zmax, c), fb));
-            }
-          },
-          tau, above, s.hist.h64, s.bc, &mass);
+    const uint32_t klo = s.bc[5], khi = s.bc[6];
+    const unsigned long long above = (unsigned long long)__double_as_longlong(s.bd[0]);
+    const unsigned long long hbin = (unsigned long long)__double_as_longlong(s.bd[1]);
+    const float zlo = Key<ET>::value(klo);
+    if (khi == klo + 1) {
+      // One key in the bin: the nucleus ends with all of its ties.
+      tstar = klo;
+      mass = above + hbin;
     } else {
-      tstar = mass_select<LEVELS, NTP>(
-          [&](auto fn) {
-            row_each([&](uint32_t uk, uint32_t raw) {
-              if (uk >= thr0) {
-                const float e = ew(T::val(raw), zmax, c);
-                if (vbin(e) == cbin) fn(uk, fixq(e, fb));
+      // Gather the crossing bin's keys (a key range: no weights needed).
+      const float zhi = khi >= Key<ET>::POS_INF ? INFINITY : Key<ET>::value(khi);
+      const float zl = fmaxf(zlo, zthr);
+      each([&](uint32_t raw) {
+        const float z = T::val(raw);
+        if (z >= zl && z < zhi) {
+          const uint32_t slot = atomicAdd(&ps.ncol, 1u);
+          if (slot < (uint32_t)PAIR_NCAP) ps.keys[slot] = T::key(raw);
+        }
+      });
+      __syncthreads();
+      const uint32_t n = ps.ncol;
+      if (n <= (uint32_t)PAIR_NCAP) {
+        tstar = mass_select<LEVELS, NTP>(
+            [&](auto fn) {
+              for (uint32_t j = threadIdx.x; j < n; j += NTP) {
+                const uint32_t uk = ps.keys[j];
+                fn(uk, fx(Key<ET>::value(uk)));
               }
-            });
-          },
-          tau, above, s.hist.h64, s.bc, &mass);
+            },
+            tau, above, s.hist.h64, s.bc, &mass);
+      } else {
+        tstar = mass_select<LEVELS, NTP>(
+            [&](auto fn) {
+              each([&](uint32_t raw) {
+                const float z = T::val(raw);
+                if (z >= zl && z < zhi) fn(T::key(raw), fx(z));
+              });
+            },
+            tau, above, s.hist.h64, s.bc, &mass);
+      }
     }
   }
   if (tstar != 0 && mass > 0) {
-    st.thr = max(st.thr, tstar);
+    st.zthr = fmaxf(zthr, Key<ET>::value(tstar));
     S = mass;
   }
-  st.sp = (float)(fscale / (double)S);
+  st.sp = (float)(ldexp(1.0, fb) / (double)S);
   return st;
 }
 
 // Probability of one element under a row's statistics.
-template <typename ET, bool VECTOR>
-__device__ __forceinline__ float pprob(const RowStat& st, uint32_t raw) {
-  using T = PT<ET, VECTOR>;
-  return T::key(raw) >= st.thr ? ew(T::val(raw), st.zmax, st.c) * st.sp : 0.0f;
+__device__ __forceinline__ float pprob(const RowStat& st, float z) {
+  return z >= st.zthr ? ew(z, st.zmax, st.c) * st.sp : 0.0f;
 }
 
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
@@ -441,15 +503,17 @@ __global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
   const U* gp = reinterpret_cast<const U*>(row_ptr<ET>(a, b, true, i));
   const U* gq = resid ? reinterpret_cast<const U*>(row_ptr<ET>(a, b, false, i)) : gp;
 
-  // Pass 1: maxima and validity (LDS variant: the rows are copied on chip).
+  // Pass 1: maxima and validity (NaN or +inf makes the pair invalid); the
+  // LDS variant copies the rows on chip as it goes.
   const U* P;
   const U* Q;
-  uint32_t kmp = 0, kmq = 0, bad = 0;
-  auto scan_unit = [&](const U& u, uint32_t& km) {
+  float zmp = -INFINITY, zmq = -INFINITY;
+  uint32_t bad = 0;
+  auto scan_unit = [&](const U& u, float& zm) {
     T::each(u, [&](int, uint32_t raw) {
-      const uint32_t uk = T::key(raw);
-      km = max(km, uk);
-      bad |= key_valid<ET>(uk) ? 0u : 1u;
+      const float z = T::val(raw);
+      zm = fmaxf(zm, z);
+      bad |= z < INFINITY ? 0u : 1u;
     });
   };
   if constexpr (LDSR) {
@@ -466,21 +530,42 @@ __global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
         if (resid) uq = gq[ui];
       }
       lp[ui] = up;
-      scan_unit(up, kmp);
+      scan_unit(up, zmp);
       if (resid) {
         lq[ui] = uq;
-        scan_unit(uq, kmq);
+        scan_unit(uq, zmq);
       }
     }
     P = lp;
     Q = lq;
   } else {
-    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
-      scan_unit(gp[ui], kmp);
-      if (resid) scan_unit(gq[ui], kmq);
+    int ui = threadIdx.x;
+    for (; ui + NTP < NU; ui += 2 * NTP) {
+      const U p0 = gp[ui], p1 = gp[ui + NTP];
+      U q0, q1;
+      if (resid) {
+        q0 = gq[ui];
+        q1 = gq[ui + NTP];
+      }
+      scan_unit(p0, zmp);
+      scan_unit(p1, zmp);
+      if (resid) {
+        scan_unit(q0, zmq);
+        scan_unit(q1, zmq);
+      }
+    }
+    if (ui < NU) {
+      scan_unit(gp[ui], zmp);
+      if (resid) scan_unit(gq[ui], zmq);
     }
     P = gp;
     Q = gq;
+  }
+  // Order-preserving keys of the maxima (a max key of 0 marks no finite logit).
+  uint32_t kmp = Key<ET>::of_bits(__float_as_uint(zmp)), kmq = Key<ET>::of_bits(__float_as_uint(zmq));
+  if constexpr (sizeof(ET) == 2) {
+    kmp = Key<ET>::of_bits(__float_as_uint(zmp) >> 16);
+    kmq = Key<ET>::of_bits(__float_as_uint(zmq) >> 16);
   }
   pb_max3<NTP>(kmp, kmq, bad, s.red_u);   // its barriers also publish the LDS rows
   PosRec* rec = a.pos + (size_t)b * G1 + i;
@@ -491,31 +576,40 @@ __global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
     }
     return;
   }
-  const RowStat sp = row_stats<ET, NTP, VECTOR, LDSR>(P, NU, kmp, a, m, k, s, ps);
+  const RowStat sp = row_stats<ET, NTP, VECTOR, LDSR>(P, NU, Key<ET>::value(kmp), a, m, k, s, ps);
   RowStat sq = sp;
-  if (resid) sq = row_stats<ET, NTP, VECTOR, LDSR>(Q, NU, kmq, a, m, k, s, ps);
+  if (resid) sq = row_stats<ET, NTP, VECTOR, LDSR>(Q, NU, Key<ET>::value(kmq), a, m, k, s, ps);
 
   // Overlap and per-(tile, wavefront) sums of the draw weights: the residual
   // max(0, p - q), or p at the bonus position and when the residual is zero.
+  // Streamed rows load the next tile while the current one is summed.
   const int ntile = (NU + NTP - 1) / NTP;
   double al = 0.0;
   auto weights_pass = [&](bool use_q) {
-    for (int t = 0; t < ntile; ++t) {
-      const int ui = t * NTP + (int)threadIdx.x;
+    int ui = threadIdx.x;
+    U np{}, nq{};
+    if (ui < NU) {
+      np = P[ui];
+      if (use_q) nq = Q[ui];
+    }
+    for (int t = 0; t < ntile; ++t, ui += NTP) {
+      const U up = np, uq = nq;
+      if (ui + NTP < NU) {
+        np = P[ui + NTP];
+        if (use_q) nq = Q[ui + NTP];
+      }
       float r = 0.0f, av = 0.0f;
       if (ui < NU) {
-        const U up = P[ui];
         if (use_q) {
-          const U uq = Q[ui];
           float pv[E];
-          T::each(up, [&](int j, uint32_t raw) { pv[j] = pprob<ET, VECTOR>(sp, raw); });
+          T::each(up, [&](int j, uint32_t raw) { pv[j] = pprob(sp, T::val(raw)); });
           T::each(uq, [&](int j, uint32_t raw) {
-            const float qv = pprob<ET, VECTOR>(sq, raw);
+            const float qv = pprob(sq, T::val(raw));
             av += fminf(pv[j], qv);
             r += fmaxf(pv[j] - qv, 0.0f);
           });
         } else {
-          T::each(up, [&](int, uint32_t raw) { r += pprob<ET, VECTOR>(sp, raw); });
+          T::each(up, [&](int, uint32_t raw) { r += pprob(sp, T::val(raw)); });
         }
       }
       al += (double)av;
@@ -571,15 +665,14 @@ __global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
       const U up = P[ui];
       if (use_q) {
         const U uq = Q[ui];
-        T::each(up, [&](int j, uint32_t raw) { w[j] = pprob<ET, VECTOR>(sp, raw); });
+        T::each(up, [&](int j, uint32_t raw) { w[j] = pprob(sp, T::val(raw)); });
         T::each(uq, [&](int j, uint32_t raw) {
-          const float qv = pprob<ET, VECTOR>(sq, raw);
-          w[j] = fmaxf(w[j] - qv, 0.0f);
+          w[j] = fmaxf(w[j] - pprob(sq, T::val(raw)), 0.0f);
           r += w[j];
         });
       } else {
         T::each(up, [&](int j, uint32_t raw) {
-          w[j] = pprob<ET, VECTOR>(sp, raw);
+          w[j] = pprob(sp, T::val(raw));
           r += w[j];
         });
       }
@@ -605,8 +698,8 @@ __global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
     const int x = resid ? a.draft[(size_t)b * a.G + i] : -1;
     double px = 0.0, qx = 0.0;
     if (x >= 0 && x < V) {
-      px = (double)pprob<ET, VECTOR>(sp, T::raw_at(P, x));
-      qx = (double)pprob<ET, VECTOR>(sq, T::raw_at(Q, x));
+      px = (double)pprob(sp, T::val(T::raw_at(P, x)));
+      qx = (double)pprob(sq, T::val(T::raw_at(Q, x)));
     }
     rec->px = px;
     rec->qx = qx;

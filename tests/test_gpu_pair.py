@@ -1,0 +1,119 @@
+"""Dense rows (temperature > 0, no top-k up to 512) through every launch shape
+of the pair kernel, against the oracle: rows held in LDS by 64-, 256- and
+1024-thread workgroups, rows streamed from global memory, vector and scalar
+element paths, bf16 and fp32, with unfiltered, large-top-k and nucleus rows,
+and the nucleus corner cases (tie groups at the cut, a crossing bin too
+large to gather, point masses)."""
+import numpy as np
+import pytest
+
+from speculative_sampling_verification_verify_amd import synth
+from gpu_util import compare, log, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def dense_batch(V, dtype, B=6, G=3, seed=0, T=None, k=None, tp=None, zp=None, zq=None):
+    """Zipf-shaped target logits (scale 3, slope 1.1 over a seeded
+    permutation), draft logits = target + noise, drafts by Gumbel-max from
+    the draft logits at the row temperature, Philox uniforms."""
+    rng = np.random.default_rng(1000 + seed)
+    if zp is None:
+        rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
+        zp = (3.0 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
+    if zq is None:
+        zq = (zp[:, :G] + 0.7 * rng.normal(size=(B, G, V))).astype(np.float32)
+    T = np.full(B, 1.0, np.float32) if T is None else np.asarray(T, np.float32)
+    k = np.zeros(B, np.int32) if k is None else np.asarray(k, np.int32)
+    tp = np.ones(B, np.float32) if tp is None else np.asarray(tp, np.float32)
+    gum = -np.log(-np.log(rng.random(size=zq.shape)))
+    draft = np.argmax(zq / np.maximum(T, 1e-3)[:, None, None] + gum, axis=2).astype(np.int32)
+    cast = _bf if dtype == "bf16" else (lambda x: np.asarray(x, np.float32))
+    w = synth.make_batch(0, B=1, V=8).workload
+    return synth.Batch(w, cast(zp), cast(zq), draft, synth.uniforms(seed, B, G), np.full(B, G, np.int32),
+                       T, k, tp, seed)
+
+
+# (dtype, V): one case per launch shape.
+SHAPES = [
+    ("fp32", 1000),      # 4000-byte rows: 64-thread workgroup, vector loads
+    ("fp32", 1001),      # 64 threads, scalar elements
+    ("bf16", 2048),      # 64 threads, exactly 4 KB
+    ("bf16", 6000),      # 256 threads
+    ("bf16", 32768),     # 1024 threads, exactly 64 KB in LDS
+    ("bf16", 32769),     # streamed, scalar elements
+    ("fp32", 20000),     # streamed, vector, fp32 keys
+    ("bf16", 96000),     # streamed, vector
+]
+
+
+@pytest.mark.parametrize("dtype,V", SHAPES)
+def test_dense_launch_shapes(dtype, V):
+    B = 8
+    T = np.array([1.0, 0.6, 1.3, 0.8, 1.0, 0.7, 1.1, 2.0], np.float32)
+    k = np.array([0, 0, 0, 600, 600, 0, V + 3, 0], np.int32)
+    k = np.where(k >= V, V + 3, k).astype(np.int32)
+    tp = np.array([1.0, 0.9, 0.9, 1.0, 0.85, 0.5, 0.95, 0.99], np.float32)
+    bt = dense_batch(V, dtype, B=B, G=3, seed=V % 97, T=T, k=k, tp=tp)
+    log(f"[pair] shape {dtype} V={V}")
+    check = compare(bt, run_gpu(bt), run_oracle(bt), f"pair-{dtype}-V{V}")
+    log(f"[pair] shape {dtype} V={V}: ok {check}")
+
+
+@pytest.mark.parametrize("V", [5000, 70000])
+def test_point_mass_rows_and_zero_residual(V):
+    # top_p <= 0 keeps only the maximum (and its ties); where p and q share
+    # it, the residual is empty and a rejected draft is replaced from p.
+    B, G = 6, 4
+    rng = np.random.default_rng(9)
+    zp = rng.normal(size=(B, G + 1, V)).astype(np.float32)
+    zq = zp[:, :G].copy()
+    zq[1] += 0.3 * rng.normal(size=(G, V)).astype(np.float32)   # a different maximum on some positions
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=4, zp=zp, zq=zq, T=np.full(B, 0.9),
+                     tp=np.array([0.0, 0.0, -1.0, 0.0, 1.0, 0.0], np.float32))
+    d = bt.draft.copy()
+    d[::2, 1] = (np.argmax(zq[::2, 1], axis=1) + 1) % V     # drafts off the maximum: q(x) = 0 -> rejected
+    bt = synth.Batch(bt.workload, bt.p_logits, bt.q_logits, d, bt.u, bt.gamma_len, bt.temperature, bt.top_k,
+                     bt.top_p, bt.seed)
+    compare(bt, run_gpu(bt), run_oracle(bt), f"point-mass-V{V}")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 40000), ("bf16", 8000), ("fp32", 30000)])
+def test_nucleus_cut_inside_tie_group(dtype, V):
+    # 3000 equal logits hold most of the mass; the cut falls inside them, so
+    # the whole tie group is kept.
+    B, G = 4, 2
+    rng = np.random.default_rng(21)
+    zp = (rng.normal(size=(B, G + 1, V)) - 4).astype(np.float32)
+    zp[:, :, 100:3100] = 2.0
+    zq = (zp[:, :G] + 0.5 * rng.normal(size=(B, G, V))).astype(np.float32)
+    bt = dense_batch(V, dtype, B=B, G=G, seed=8, zp=zp, zq=zq, T=np.full(B, 1.0),
+                     tp=np.array([0.5, 0.9, 0.2, 0.99], np.float32))
+    compare(bt, run_gpu(bt), run_oracle(bt), f"tie-group-{dtype}-V{V}")
+
+
+def test_nucleus_crossing_bin_too_large_to_gather():
+    # fp32 logits packed into a band far narrower than one value bin: more
+    # than 2048 distinct keys share the crossing bin, so the exact cut is
+    # found by radix passes over the row.
+    B, G, V = 3, 2, 30000
+    rng = np.random.default_rng(5)
+    zp = (rng.normal(size=(B, G + 1, V)) - 8).astype(np.float32)
+    zp[:, :, :6000] = (4.0 + 1e-4 * rng.random(size=(B, G + 1, 6000))).astype(np.float32)
+    zq = (zp[:, :G] + 0.3 * rng.normal(size=(B, G, V))).astype(np.float32)
+    bt = dense_batch(V, "fp32", B=B, G=G, seed=6, zp=zp, zq=zq, T=np.full(B, 1.0),
+                     tp=np.array([0.5, 0.3, 0.8], np.float32))
+    compare(bt, run_gpu(bt), run_oracle(bt), "crossing-bin-overflow")
+
+
+def test_rows_beyond_the_tile_table_use_multipass():
+    # Odd V above 65536 elements: scalar streamed rows exceed the residual
+    # tile table, so these dense rows take the finisher's multi-pass path.
+    V = 70001
+    bt = dense_batch(V, "bf16", B=3, G=2, seed=3, T=np.array([1.0, 0.7, 1.2]),
+                     tp=np.array([1.0, 0.9, 0.8], np.float32))
+    compare(bt, run_gpu(bt), run_oracle(bt), "multipass-V70001")

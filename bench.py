@@ -5,10 +5,12 @@ already resident in HBM.  The default workload is the headline one:
 B = 256 sequences, V = 152064, gamma = 7, bf16 logits, temperature 0.7,
 top-k 64 (1.17 GB of logits per call).
 
-Prints one JSON line with verify-rows/s (a row is one sequence), the select
-kernel's achieved HBM bandwidth against the 8 TB/s peak (timed with HIP
-events recorded around that kernel on the call's stream), and the CPU
-oracle timed on a bounded sample on the host cores.
+Prints one JSON line with verify-rows/s (a row is one sequence), the
+achieved HBM bandwidth of the kernel that reads most of the logits (the
+streaming select for top-k and argmax sequences, the pair kernel for dense
+ones) against the 8 TB/s peak, timed with HIP events recorded around that
+kernel on the call's stream, and the CPU oracle timed on a bounded sample
+on the host cores.
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "spec-verify rows/sec + achieved HBM GB/s vs peak at B=256,V=152064,γ=7"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_B256_V152064_g7_pmc.txt")
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
+ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
 
 
 def source_hash() -> str:
@@ -57,6 +60,17 @@ def traffic_from_profile():
         return float(kv["hbm_read_bytes_per_launch"]) + float(kv["hbm_write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def kernel_bytes(bt):
+    """Logit bytes read by the streaming select (argmax and top-k <= 512
+    sequences) and by the pair kernel (every other sequence with T > 0)."""
+    g = bt.gamma_len.astype(np.int64)
+    rows = (2 * g + 1) * bt.V * bt.p_logits.itemsize
+    T, k = bt.temperature, bt.top_k
+    sel = (T == 0) | ((T > 0) & (k > 0) & (k < bt.V) & (k <= 512))
+    dense = (T > 0) & ~sel
+    return int(rows[sel].sum()), int(rows[dense].sum())
 
 
 def cpu_baseline(bt, seconds_target: float, cores: int):
@@ -138,36 +152,59 @@ def main():
     draft, u, temp, topk, topp, gl = (t(bt.draft), t(bt.u), t(bt.temperature), t(bt.top_k), t(bt.top_p),
                                       t(bt.gamma_len))
     ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt_code, device=dev)
+    # Copies of the logits, rotated step by step, so that a workload smaller
+    # than the 256 MB last-level cache is still read from HBM.
+    nsets = int(min(32, max(1, -(-ROTATE_BYTES // max(logit_bytes, 1)))))
+    sets = [(P, Q)] + [(P.clone(), Q.clone()) for _ in range(nsets - 1)]
     torch.cuda.synchronize()
 
-    def step():
-        ver(P, Q, draft, u, temp, topk, topp, gl)
+    def step(j):
+        Pj, Qj = sets[j % nsets]
+        ver(Pj, Qj, draft, u, temp, topk, topp, gl)
 
-    for _ in range(args.warmup):
-        step()
+    # The kernel that reads most of the logit bytes: the streaming select for
+    # top-k / argmax sequences, the pair kernel for dense ones.
+    sel_bytes, pair_bytes = kernel_bytes(bt)
+    kernel = binding.SV_KERNEL_PAIR if pair_bytes > sel_bytes else binding.SV_KERNEL_SELECT
+    kname = {binding.SV_KERNEL_SELECT: "select_kernel", binding.SV_KERNEL_PAIR: "pair_kernel"}[kernel]
+    kbytes = max(sel_bytes, pair_bytes)
+
+    for j in range(args.warmup):
+        step(j)
     torch.cuda.synchronize()
-    # Events around the select kernel of every timed call (same stream).
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for a, b in evs:     # materialise the underlying hipEvent_t handles
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in evs:
-        binding.spec_verify_set_stage_events(a, b)
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    binding.spec_verify_set_stage_events(None, None)
-    sel_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    ms_per_step = wall * 1e3 / K
 
+    def timed(kern, n):
+        """n calls with events around kernel `kern` of every call (same
+        stream); returns (wall seconds, per-launch ms)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:     # materialise the underlying hipEvent_t handles
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j, (a, b) in enumerate(evs):
+            binding.spec_verify_set_stage_events(a, b, kern)
+            step(j)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        binding.spec_verify_set_stage_events(None, None)
+        return wall, np.array([a.elapsed_time(b) for a, b in evs])
+
+    wall, k_ms = timed(kernel, K)
+    ms_per_step = wall * 1e3 / K
     n_acc = ver.n_accepted.cpu().numpy()
     alpha = ver.alpha.cpu().numpy()
-    sel_avg = float(sel_ms.mean())
-    achieved = logit_bytes / (sel_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile()
+    # Outside the timed region: the other kernels' durations, for the record.
+    other_us = {}
+    for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, "pair_kernel"),
+                       (binding.SV_KERNEL_FINISH, "finish_kernel")):
+        if kern != kernel:
+            _, ms = timed(kern, min(K, 20))
+            other_us[name] = float(ms.mean() * 1e3) if (ms > 0).all() else None
+    k_avg = float(k_ms.mean())
+    achieved = kbytes / (k_avg * 1e-3) / 1e9
+    traffic = traffic_from_profile() if kernel == binding.SV_KERNEL_SELECT else None
     w = bt.workload
     out = {
         "metric": METRIC,
@@ -187,14 +224,16 @@ def main():
                    "logit_bytes_per_call": logit_bytes, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "select_kernel", "kernel_avg_us": sel_avg * 1e3,
-                     "kernel_p10_us": float(np.percentile(sel_ms, 10) * 1e3),
-                     "kernel_p90_us": float(np.percentile(sel_ms, 90) * 1e3)},
+                     "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,
+                     "kernel_p10_us": float(np.percentile(k_ms, 10) * 1e3),
+                     "kernel_p90_us": float(np.percentile(k_ms, 90) * 1e3)},
         "cpu_baseline": cpu,
         "extra": {"call_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
                   "logit_rows_per_s": int((2 * bt.gamma_len.astype(np.int64) + 1).sum()) / (ms_per_step * 1e-3),
                   "mean_alpha": float(alpha[alpha > 0].mean()) if (alpha > 0).any() else None,
                   "mean_tokens_per_round": float((n_acc[n_acc >= 0] + 1).mean()),
+                  "other_kernels_avg_us": other_us,
+                  "input_sets_rotated": nsets,
                   "input_generation_s": t_gen},
     }
     print(json.dumps(out))

@@ -120,20 +120,30 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
                 int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernels of one call, for spec_verify_set_stage_events. */
+enum {
+  SV_KERNEL_SELECT = 0,  /* streaming top-k / argmax select over the logit rows      */
+  SV_KERNEL_PAIR = 1,    /* per-(sequence, position) pass over dense (unfiltered,   */
+                         /* large top-k, top-p) sequences; launched when V allows   */
+  SV_KERNEL_FINISH = 2   /* per-sequence acceptance, first rejection and draw       */
+};
+
 /*
  * Measurement hook (for benchmarks and profilers, not needed for normal use).
  * With non-NULL hipEvent_t handles `begin` and `end`, every later spec_verify
  * call made from this host thread records `begin` on its stream just before
- * the streaming select kernel and `end` just after it, so that
- * hipEventElapsedTime(begin, end) is that kernel's duration.  The caller owns
- * the events.  Passing NULL, NULL stops the recording.  Returns SV_OK.
+ * the chosen kernel (SV_KERNEL_*) and `end` just after it, so that
+ * hipEventElapsedTime(begin, end) is that kernel's duration.  If a call does
+ * not launch that kernel, nothing is recorded.  The caller owns the events.
+ * Passing NULL, NULL stops the recording.  Returns SV_OK, or SV_ERR_ARG for
+ * an unknown kernel.
  */
-int spec_verify_set_stage_events(void* begin, void* end);
+int spec_verify_set_stage_events(int kernel, void* begin, void* end);
 
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 1. */
+/* ABI version: 2. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

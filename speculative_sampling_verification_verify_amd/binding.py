@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_BF16, SV_FP32 = 0, 1
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
+SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH = 0, 1, 2
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 
@@ -51,7 +52,7 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_strerror.restype = ctypes.c_char_p
         L.spec_verify_version.argtypes = []
         L.spec_verify_version.restype = i
-        L.spec_verify_set_stage_events.argtypes = [vp, vp]
+        L.spec_verify_set_stage_events.argtypes = [i, vp, vp]
         L.spec_verify_set_stage_events.restype = i
         _lib = L
     return _lib
@@ -88,12 +89,14 @@ def spec_verify_version() -> int:
     return int(lib().spec_verify_version())
 
 
-def spec_verify_set_stage_events(begin, end) -> None:
+def spec_verify_set_stage_events(begin, end, kernel: int = SV_KERNEL_SELECT) -> None:
     """Record hipEvent_t handles (ints, or torch.cuda.Event already recorded
-    once) around the streaming select kernel of the following calls; pass
+    once) around one kernel (SV_KERNEL_*) of the following calls; pass
     None, None to stop."""
     h = lambda e: None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else int(e))
-    lib().spec_verify_set_stage_events(h(begin), h(end))
+    rc = lib().spec_verify_set_stage_events(kernel, h(begin), h(end))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_set_stage_events")
 
 
 def spec_verify_workspace_init(workspace: torch.Tensor, B: int, gamma_max: int, V: int, dtype: int,

@@ -1,17 +1,23 @@
 // Batched speculative-sampling verify step for MI355X (gfx950): kernels and
 // the C ABI.
 //
-// A call is two launches on the caller's stream:
+// A call is three launches on the caller's stream:
 //   1. select_kernel -- one wavefront per (logit row, row part) of every
 //      top-k / argmax sequence: streams the part once from HBM with 16-byte
 //      non-temporal loads and writes its exact kept set (top-k survivors,
-//      ties included) to the workspace.  See sv_wave.h.
-//   2. finish_kernel -- one workgroup per sequence: for top-k / argmax
+//      ties included) to the workspace; a few extra workgroups list the
+//      (sequence, position) pairs of the dense sequences.  See sv_wave.h.
+//   2. pair_kernel -- one workgroup per listed dense pair (unfiltered, large
+//      top-k and top-p sequences): normalisers, nucleus cut, p(x), q(x),
+//      overlap and the draw as if the first rejection were at that position.
+//      See sv_pair.h.
+//   3. finish_kernel -- one workgroup per sequence: for top-k / argmax
 //      sequences, merges the part lists of every row and computes the
 //      normalisers, top-p cut, p(x), q(x), overlap, the first rejection (one
 //      wavefront ballot) and the residual / bonus draw from the lists; for
-//      unfiltered and top-p sequences (and lists that overflowed), runs a
-//      multi-pass procedure over the logits.  See sv_finish.h.
+//      dense sequences it takes the pair kernel's per-position results (or,
+//      for rows beyond the pair kernel's limits, runs a multi-pass procedure
+//      over the logits).  See sv_finish.h.
 //
 // Definitions followed (page titles and sections): the acceptance rule and
 // the residual, "Fast Inference from Transformers via Speculative Decoding"
@@ -86,8 +92,19 @@ static int pair_variant(int V, int dtype, bool vector_ok, size_t* lds_bytes) {
   return units <= (size_t)1024 * PAIR_MAXTILE ? -1024 : 0;   // negative: streamed rows
 }
 
+// Resident workgroups of each pair-kernel shape across the chip (256 CUs):
+// the pair kernel's grid, which walks the dense-pair list.
+static int pair_grid_cap(int variant) {
+  switch (variant) {
+    case 64: return 256 * 16;
+    case 256: return 256 * 4;
+    case 1024: return 256;        // 128 KB of rows in LDS: one per CU
+    default: return 256 * 2;      // streamed rows
+  }
+}
+
 struct Layout {
-  size_t seq_flags_off, counters_bytes, pos_off, counts_off, lists_off, total;
+  size_t seq_flags_off, dense_count_off, counters_bytes, pos_off, dense_list_off, counts_off, lists_off, total;
 };
 
 static Layout layout(int B, int G, const Plan& p) {
@@ -95,16 +112,26 @@ static Layout layout(int B, int G, const Plan& p) {
   const size_t R = (size_t)B * (2 * G + 1);
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L.seq_flags_off = 0;
-  L.counters_bytes = up(L.seq_flags_off + (size_t)B * 4);
+  L.dense_count_off = (size_t)B * 4;
+  L.counters_bytes = up(L.dense_count_off + 4);
   L.pos_off = L.counters_bytes;
-  L.counts_off = up(L.pos_off + (size_t)B * (G + 1) * sizeof(PosRec));
+  L.dense_list_off = up(L.pos_off + (size_t)B * (G + 1) * sizeof(PosRec));
+  L.counts_off = up(L.dense_list_off + (size_t)B * (G + 1) * 4);
   L.lists_off = up(L.counts_off + R * p.NP * 4);
   L.total = L.lists_off + R * p.NP * SEG * sizeof(uint2);
   return L;
 }
 
 static thread_local char g_errbuf[256];
+// Timing hook: events recorded around one kernel of every call.
 static thread_local hipEvent_t g_stage_begin = nullptr, g_stage_end = nullptr;
+static thread_local int g_stage_kernel = SV_KERNEL_SELECT;
+
+static hipError_t stage_mark(int kernel, bool begin, hipStream_t st) {
+  if (kernel != g_stage_kernel) return hipSuccess;
+  hipEvent_t ev = begin ? g_stage_begin : g_stage_end;
+  return ev ? hipEventRecord(ev, st) : hipSuccess;
+}
 
 template <typename ET, bool VECTOR>
 static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
@@ -120,17 +147,11 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     if (e != hipSuccess) return e;
     attr_dev[dev] = dev + 1;
   }
-  if (g_stage_begin) {
-    e = hipEventRecord(g_stage_begin, st);
-    if (e != hipSuccess) return e;
-  }
+  if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (g_stage_end) {
-    e = hipEventRecord(g_stage_end, st);
-    if (e != hipSuccess) return e;
-  }
+  if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   if (a.pair) {
     size_t plds = 0;
     const int pv = pair_variant(a.V, sizeof(ET) == 2 ? SV_BF16 : SV_FP32, VECTOR, &plds);
@@ -143,10 +164,18 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
       default: return hipErrorInvalidValue;
     }
     if (plds) {
-      e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
-      if (e != hipSuccess) return e;
+      // Raised once per (device, kernel, size); sizes only grow with V.
+      static int pair_lds_set[64][4];
+      const int slot = pv == 64 ? 0 : pv == 256 ? 1 : 2;
+      if (dev < 0 || dev >= 64 || pair_lds_set[dev][slot] < (int)plds) {
+        e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) pair_lds_set[dev][slot] = (int)plds;
+      }
     }
-    const dim3 grid((unsigned)(a.B * (a.G + 1)));
+    const long long npairs = (long long)a.B * (a.G + 1);
+    const dim3 grid((unsigned)(npairs < pair_grid_cap(pv) ? npairs : pair_grid_cap(pv)));
+    if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
     switch (pv) {
       case 64: hipLaunchKernelGGL((pair_kernel<ET, 64, VECTOR, true>), grid, dim3(64), plds, st, a); break;
       case 256: hipLaunchKernelGGL((pair_kernel<ET, 256, VECTOR, true>), grid, dim3(256), plds, st, a); break;
@@ -155,9 +184,13 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if ((e = stage_mark(SV_KERNEL_PAIR, false, st)) != hipSuccess) return e;
   }
+  if ((e = stage_mark(SV_KERNEL_FINISH, true, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((finish_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), fin_lds, st, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return stage_mark(SV_KERNEL_FINISH, false, st);
 }
 
 }  // namespace sv
@@ -207,7 +240,9 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   const Plan pl = plan(B, gamma_max, V, dtype);
   const long long rows = (long long)B * (2 * gamma_max + 1);
   const long long units = rows * pl.NP;
-  const long long grid = (units + K1_WAVES - 1) / K1_WAVES;
+  const long long sel_grid = (units + K1_WAVES - 1) / K1_WAVES;
+  const long long list_grid = ((long long)B + K1_NT - 1) / K1_NT;
+  const long long grid = sel_grid + list_grid;
   if (grid > 0x7FFFFFFFLL || units > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
   const int vec = dtype == SV_BF16 ? 8 : 4;
   const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)q_logits % 16 == 0);
@@ -237,8 +272,13 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   a.seq_flags = reinterpret_cast<uint32_t*>(ws + Lw.seq_flags_off);
   a.counts = reinterpret_cast<int32_t*>(ws + Lw.counts_off);
   a.pos = reinterpret_cast<PosRec*>(ws + Lw.pos_off);
+  a.dense_count = reinterpret_cast<uint32_t*>(ws + Lw.dense_count_off);
+  a.dense_list = reinterpret_cast<int32_t*>(ws + Lw.dense_list_off);
   size_t pair_lds = 0;
   a.pair = pair_variant(V, dtype, vector_ok, &pair_lds) != 0 && (long long)B * (gamma_max + 1) <= 0x7FFFFFFFLL ? 1 : 0;
+  // Without the pair kernel the dense sequences go to the finisher whole and
+  // nothing is listed.
+  a.sel_blocks = a.pair ? sel_grid : grid;
   a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);
   hipStream_t st = (hipStream_t)stream;
   const size_t fin_lds = sizeof(FinSmem);
@@ -266,9 +306,11 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 1; }
+extern "C" int spec_verify_version(void) { return 2; }
 
-extern "C" int spec_verify_set_stage_events(void* begin, void* end) {
+extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
+  if (kernel != SV_KERNEL_SELECT && kernel != SV_KERNEL_PAIR && kernel != SV_KERNEL_FINISH) return SV_ERR_ARG;
+  g_stage_kernel = kernel;
   g_stage_begin = (hipEvent_t)begin;
   g_stage_end = (hipEvent_t)end;
   return SV_OK;

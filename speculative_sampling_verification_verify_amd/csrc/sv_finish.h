@@ -807,6 +807,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   if (threadIdx.x == 0) {
     a.out_n[b] = ok ? n : -1;
     a.seq_flags[b] = 0;
+    if (b == 0) *a.dense_count = 0;   // the pair kernel has finished with the list
   }
   (void)lane;
 }

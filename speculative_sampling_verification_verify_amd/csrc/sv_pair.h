@@ -482,17 +482,15 @@ __device__ __forceinline__ float pprob(const RowStat& st, float z) {
   return z >= st.zthr ? ew(z, st.zmax, st.c) * st.sp : 0.0f;
 }
 
+// One (sequence b, position i) pair by the whole workgroup.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
-__global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
+__device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<NTP>& s, PairExtra<LDSR>& ps,
+                                         unsigned char* pair_rows) {
   using T = PT<ET, VECTOR>;
   using U = typename T::U;
   constexpr int E = T::E;
   constexpr int NW = NTP / 64;
-  extern __shared__ __align__(16) unsigned char pair_rows[];
-  __shared__ PairSmem<NTP> s;
-  __shared__ PairExtra<LDSR> ps;
   const int G1 = a.G + 1;
-  const int b = blockIdx.x / G1, i = blockIdx.x - (blockIdx.x / G1) * G1;
   const Mode m = seq_mode(a, b);
   if (m.mode != MODE_DENSE || i > m.g) return;
   const bool resid = i < m.g;
@@ -706,6 +704,26 @@ __global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
     rec->alpha = al;
     rec->tok = tok;
     rec->bad = 0u;
+  }
+}
+
+// The dense pairs listed by the select kernel's extra workgroups, taken in
+// turn by a grid sized to what the chip holds at once: when no sequence is
+// dense every workgroup reads the count once and leaves.
+template <typename ET, int NTP, bool VECTOR, bool LDSR>
+__global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char pair_rows[];
+  __shared__ PairSmem<NTP> s;
+  __shared__ PairExtra<LDSR> ps;
+  const int G1 = a.G + 1;
+  const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
+  const uint32_t nd = min(*a.dense_count, npairs);
+  for (uint32_t t = blockIdx.x; t < nd; t += gridDim.x) {
+    const int pid = a.dense_list[t];
+    if (pid < 0 || (uint32_t)pid >= npairs) continue;   // never written by this call's listing
+    const int b = pid / G1;
+    pair_one<ET, NTP, VECTOR, LDSR>(a, b, pid - b * G1, s, ps, pair_rows);
+    __syncthreads();   // the next pair reuses the LDS
   }
 }
 

@@ -601,9 +601,35 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
 // (logit row, row part) unit each; units of sequences that are neither
 // top-k nor argmax exit at once (the finisher takes them whole).
 // ---------------------------------------------------------------------------
+// Workgroups past the streaming ones list the dense sequences' (sequence,
+// position) pairs for the pair kernel, one sequence per thread: each
+// wavefront reserves its pairs' slots with one atomic, so the list order is
+// arbitrary (every pair writes its own result record).
+__device__ __forceinline__ void list_dense_pairs(const Args& a, long long blk) {
+  const int lane = threadIdx.x & 63;
+  const long long bl = blk * K1_NT + threadIdx.x;
+  uint32_t c = 0;
+  if (bl < a.B) {
+    const Mode m = seq_mode(a, (int)bl);
+    if (m.mode == MODE_DENSE) c = (uint32_t)m.g + 1u;
+  }
+  const uint32_t incl = wave_incl_scan_dpp(c);
+  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if (tot == 0) return;
+  uint32_t base = 0;
+  if (lane == 63) base = atomicAdd(a.dense_count, tot);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
+  const int b = (int)bl;
+  for (uint32_t j = 0; j < c; ++j) a.dense_list[base + incl - c + j] = b * (a.G + 1) + (int)j;
+}
+
 template <typename ET, bool VECTOR>
 __global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void select_kernel(Args a) {
   __shared__ WaveSmem smem[K1_WAVES];
+  if ((long long)blockIdx.x >= a.sel_blocks) {
+    list_dense_pairs(a, (long long)blockIdx.x - a.sel_blocks);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   WaveSmem& w = smem[wave];

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 1
+    assert binding.spec_verify_version() == 2
 
 
 def test_workspace_bytes():

@@ -30,7 +30,11 @@ from speculative_sampling_verification_verify_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "spec-verify rows/sec + achieved HBM GB/s vs peak at B=256,V=152064,γ=7"
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "select_kernel_B256_V152064_g7_pmc.txt")
+# rocprofv3 HBM-counter summaries, by (kernel, workload name).
+PMC_SUMMARIES = {
+    ("select_kernel", "B256-V152064-g7-T0.7-topk64"): "select_kernel_B256_V152064_g7_pmc.txt",
+    ("pair_kernel", "B128-V128256-mixed-g1..8-topp0.9"): "pair_kernel_B128_V128256_mixed_topp_pmc.txt",
+}
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
 ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
 
@@ -43,14 +47,16 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """Per-launch HBM bytes (read, write) of the select kernel from the
-    committed rocprofv3 counter summary, if it was taken on the current
-    kernel sources; else None."""
-    if not os.path.exists(PMC_SUMMARY):
+def traffic_from_profile(kernel: str, workload: str):
+    """Per-launch HBM bytes (read + write) of `kernel` on `workload` from the
+    committed rocprofv3 counter summary, if one exists and was taken on the
+    current kernel sources; else None."""
+    name = PMC_SUMMARIES.get((kernel, workload))
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
@@ -204,7 +210,7 @@ def main():
             other_us[name] = float(ms.mean() * 1e3) if (ms > 0).all() else None
     k_avg = float(k_ms.mean())
     achieved = kbytes / (k_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile() if kernel == binding.SV_KERNEL_SELECT else None
+    traffic = traffic_from_profile(kname, bt.workload.name)
     w = bt.workload
     out = {
         "metric": METRIC,

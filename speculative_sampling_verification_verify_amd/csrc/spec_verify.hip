@@ -94,12 +94,15 @@ static int pair_variant(int V, int dtype, bool vector_ok, size_t* lds_bytes) {
 
 // Resident workgroups of each pair-kernel shape across the chip (256 CUs):
 // the pair kernel's grid, which walks the dense-pair list.
+#ifndef SV_PAIR_STREAM_WGS
+#define SV_PAIR_STREAM_WGS 512
+#endif
 static int pair_grid_cap(int variant) {
   switch (variant) {
     case 64: return 256 * 16;
     case 256: return 256 * 4;
     case 1024: return 256;        // 128 KB of rows in LDS: one per CU
-    default: return 256 * 2;      // streamed rows
+    default: return SV_PAIR_STREAM_WGS;   // streamed rows
   }
 }
 

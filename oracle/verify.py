@@ -332,3 +332,134 @@ def verify_batch(p_logits, q_logits, draft, u, temperature, top_k, top_p, gamma_
         out.zero_residual[k] = r.zero_residual
     _SHARED.clear()
     return out
+
+
+# ----------------------------------------------------------------------------
+# Verify with shared Gumbel noise (Gumbel coupling).
+# ----------------------------------------------------------------------------
+# "Speculative Decoding: the art of guessing well", section "Sampling with
+# shared noise": the drafter and the target use the same noise vector g_k at
+# draft position k.  The drafter proposes argmax_i(log q_k(i) + g_k,i); the
+# target's own sample is argmax_i(log p_k(i) + g_k,i); the verify keeps the
+# longest prefix on which the two agree and appends the target's token at the
+# first disagreement (the target's token after the last draft when all
+# agree).  Gumbel-max sampling itself (argmax of logits plus independent
+# Gumbel noise follows the softmax) is the same section's first part.
+#
+# log p_k(i) = s_i - log S over the processed support (s = z / T), so the
+# argmax only needs the support and s_i + g_i; log S is common to every i.
+# Readings: the score is formed in float32 as fl(fl(z / T) + g), the
+# precision of the kernel, so that both sides take the argmax decision on the
+# same numbers; ties go to the lowest id; T = 0 is exact argmax matching (the
+# noise is unused, as in "Draft and verify").
+
+def gumbel_scores(z: np.ndarray, g: np.ndarray, T: float) -> np.ndarray:
+    """float32 scores fl(fl(z / T) + g) of one row (z decoded logits, g the
+    row's noise, T > 0)."""
+    z32 = np.asarray(z, dtype=np.float32)
+    s = z32 / np.float32(T)
+    return (s + np.asarray(g, dtype=np.float32)).astype(np.float32)
+
+
+def gumbel_target_token(z: np.ndarray, g: np.ndarray, T: float, top_k: int, top_p: float):
+    """The target's sample at one position: the lowest id maximising the
+    score over the processed support.  Returns (token, top-p margin)."""
+    pr = process(z, T, top_k, top_p)
+    if T == 0.0:
+        return int(np.argmax(z)), INF
+    sc = gumbel_scores(z, g, T)
+    sc = np.where(pr.kept, sc, np.float32(-np.inf))
+    return int(np.argmax(sc)), pr.topp_margin
+
+
+@dataclasses.dataclass
+class GumbelResult:
+    tokens: np.ndarray        # int32 [gamma_max+1]: x_1..x_n, then target[n], -1 padded
+    n: int                    # drafts kept, -1 for an invalid sequence
+    target: np.ndarray        # int32 [gamma_max+1]: the target's sample at each used position
+    margin_topp: float
+
+
+def gumbel_verify_sequence(zp: np.ndarray, g: np.ndarray, draft: np.ndarray, T: float, top_k: int,
+                           top_p: float, gamma_b: int) -> GumbelResult:
+    """One sequence.  zp: [gamma_max+1, V] target logits (float64), g:
+    [gamma_max+1, V] noise (float32), draft: [gamma_max] proposed tokens.
+    Rows beyond gamma_b are padding and are never read."""
+    gamma_max = zp.shape[0] - 1
+    V = zp.shape[1]
+    T = float(T)
+    top_p = float(top_p)
+    bad = GumbelResult(np.full(gamma_max + 1, -1, np.int32), -1, np.full(gamma_max + 1, -1, np.int32), INF)
+    if not (1 <= gamma_b <= gamma_max) or not (T >= 0.0) or math.isnan(top_p):
+        return bad
+    x = np.asarray(draft[:gamma_b])
+    if (x < 0).any() or (x >= V).any():
+        return bad
+    for j in range(gamma_b + 1):
+        if not row_is_valid(zp[j]):
+            return bad
+        if T > 0.0 and not np.isfinite(np.asarray(g[j], dtype=np.float32)).all():
+            return bad
+    target = np.full(gamma_max + 1, -1, np.int32)
+    margin = INF
+    for j in range(gamma_b + 1):
+        t, m = gumbel_target_token(zp[j], g[j], T, top_k, top_p)
+        target[j] = t
+        margin = min(margin, m)
+    n = gamma_b
+    for k in range(gamma_b):
+        if int(x[k]) != int(target[k]):
+            n = k
+            break
+    tokens = np.full(gamma_max + 1, -1, np.int32)
+    tokens[:n] = x[:n]
+    tokens[n] = target[n]
+    return GumbelResult(tokens, n, target, margin)
+
+
+def gumbel_verify_listing_form(zp, zq, g, T, gamma_b):
+    """Second formulation, following the structure of the JAX
+    `gumbel_verify` listing on the same page (unfiltered rows): the draft is
+    the drafter's argmax of log q + g on the first gamma_b noise rows, the
+    target's samples are the argmax of log p + g on all gamma_b + 1 rows, and
+    n is the first False of (draft == target[:-1]) || False.  log-softmax
+    values are formed in float64 here (a different rounding path from the
+    main formulation).  Returns (draft, n, token)."""
+    def logsoftmax(z):
+        s = np.asarray(z, dtype=np.float64) / T
+        m = s.max()
+        return s - (m + np.log(np.exp(s - m).sum()))
+    gb = np.asarray(g, dtype=np.float64)
+    lq = np.stack([logsoftmax(zq[i]) for i in range(gamma_b)])
+    lp = np.stack([logsoftmax(zp[j]) for j in range(gamma_b + 1)])
+    draft = np.argmax(lq + gb[:gamma_b], axis=-1)
+    target = np.argmax(lp + gb[:gamma_b + 1], axis=-1)
+    n = int(np.argmin(np.append(draft == target[:-1], False)))
+    return draft.astype(np.int32), n, int(target[n])
+
+
+@dataclasses.dataclass
+class GumbelBatchResult:
+    tokens: np.ndarray        # int32 [B, gamma_max+1]
+    n: np.ndarray             # int32 [B]
+    target: np.ndarray        # int32 [B, gamma_max+1]
+    margin_topp: np.ndarray   # float64 [B]
+
+
+def gumbel_verify_batch(p_logits, noise, draft, temperature, top_k, top_p, gamma_len,
+                        rows: Optional[Sequence[int]] = None) -> GumbelBatchResult:
+    """The Gumbel-coupling verify over the sequences in ``rows`` (serial)."""
+    B = p_logits.shape[0]
+    G1 = p_logits.shape[1]
+    rows = list(range(B)) if rows is None else list(rows)
+    R = len(rows)
+    out = GumbelBatchResult(np.full((R, G1), -1, np.int32), np.zeros(R, np.int32), np.full((R, G1), -1, np.int32),
+                            np.zeros(R))
+    for k, b in enumerate(rows):
+        r = gumbel_verify_sequence(decode_row(p_logits[b]), noise[b], np.asarray(draft[b]), float(temperature[b]),
+                                   int(top_k[b]), float(top_p[b]), int(gamma_len[b]))
+        out.tokens[k] = r.tokens
+        out.n[k] = r.n
+        out.target[k] = r.target
+        out.margin_topp[k] = r.margin_topp
+    return out

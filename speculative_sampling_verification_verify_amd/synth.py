@@ -39,7 +39,8 @@ import numpy as np
 BASE_SEED = 20261202
 
 # Counter-stream ids.
-STREAM_PERM, STREAM_TARGET, STREAM_DRAFT_NOISE, STREAM_DRAFT_SAMPLE, STREAM_UNIFORM, STREAM_ROWPARAM = range(6)
+(STREAM_PERM, STREAM_TARGET, STREAM_DRAFT_NOISE, STREAM_DRAFT_SAMPLE, STREAM_UNIFORM, STREAM_ROWPARAM,
+ STREAM_GUMBEL) = range(7)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -304,3 +305,92 @@ def algorithmic_bytes(batch: Batch) -> int:
     B, G = batch.B, batch.gamma_max
     small = B * G * 4 + B * (G + 1) * 4 + B * 4 * 3 + B * (G + 1) * 4 + B * 4 + B * G * 4
     return rows * batch.V * el + small
+
+
+# ----------------------------------------------------------------------------
+# Shared-noise (Gumbel coupling) inputs.
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class GumbelBatch:
+    """Host copy of one shared-noise verify call's inputs.
+
+    p_logits: [B, gamma_max+1, V] target logits (uint16 bf16 bits, or float32)
+    noise:    [B, gamma_max+1, V] float32 Gumbel noise, one vector per position,
+              shared by the drafter and the target
+    draft:    [B, gamma_max] int32 proposals of a drafter that used the same noise
+    gamma_len, temperature, top_k, top_p: [B] per-row parameters
+    q_logits: the simulated drafter's logits (inputs of the drafter only)
+    """
+    workload: Workload
+    p_logits: np.ndarray
+    noise: np.ndarray
+    draft: np.ndarray
+    gamma_len: np.ndarray
+    temperature: np.ndarray
+    top_k: np.ndarray
+    top_p: np.ndarray
+    seed: int
+    q_logits: Optional[np.ndarray] = None
+
+    @property
+    def B(self):
+        return self.p_logits.shape[0]
+
+    @property
+    def V(self):
+        return self.p_logits.shape[2]
+
+    @property
+    def gamma_max(self):
+        return self.p_logits.shape[1] - 1
+
+
+def gumbel_noise_rows(seed: int, b: int, rows: int, V: int) -> np.ndarray:
+    """[rows, V] float32 standard Gumbel noise -log(-log u) of sequence b,
+    u uniform in (0, 1) from the sequence's own counter stream."""
+    u = _rng(seed, STREAM_GUMBEL, b).random((rows, V))
+    u = np.clip(u, 2.0 ** -60, 1.0 - 2.0 ** -53)
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
+def _coupled_drafter(zq: np.ndarray, g: np.ndarray, T: float, k: int, top_p: float) -> int:
+    """The simulated drafter's proposal under shared noise: the highest
+    drafter score plus noise over the drafter's candidate set (T == 0: the
+    highest drafter logit)."""
+    if T == 0.0:
+        return int(np.argmax(zq))
+    V = zq.shape[0]
+    cand = np.ones(V, dtype=bool)
+    if 0 < k < V:
+        cand &= zq >= np.partition(zq, V - k)[V - k]
+    if top_p < 1.0:
+        order = np.argsort(-np.where(cand, zq, -np.inf), kind="stable")
+        s = zq[order] / T
+        w = np.where(np.isfinite(s), np.exp(s - s[0]), 0.0)
+        c = np.cumsum(w) / w.sum()
+        cut = int(np.searchsorted(c, top_p, side="left")) + 1
+        keep = np.zeros(V, dtype=bool)
+        keep[order[:cut]] = True
+        cand &= keep
+    score = (zq.astype(np.float32) / np.float32(T) + g).astype(np.float32)
+    return int(np.argmax(np.where(cand, score, np.float32(-np.inf))))
+
+
+def make_gumbel_batch(cid: int, B: Optional[int] = None, V: Optional[int] = None,
+                      seed: Optional[int] = None) -> GumbelBatch:
+    """Inputs of the shared-noise verify on workload ``cid``'s shapes and value
+    recipe: the same target logits, one noise vector per position, and the
+    proposals of a drafter that scored its own logits with the same noise."""
+    base = make_batch(cid, B=B, V=V, seed=seed)
+    Bn, G, Vv = base.B, base.gamma_max, base.V
+    noise = np.empty((Bn, G + 1, Vv), dtype=np.float32)
+    draft = np.zeros((Bn, G), dtype=np.int32)
+    for b in range(Bn):
+        noise[b] = gumbel_noise_rows(base.seed, b, G + 1, Vv)
+        zq = base.logits_f64("q", b)
+        for i in range(int(base.gamma_len[b])):
+            draft[b, i] = _coupled_drafter(zq[i], noise[b, i], float(base.temperature[b]), int(base.top_k[b]),
+                                           float(base.top_p[b]))
+    w = dataclasses.replace(base.workload, name=base.workload.name + "-gumbel")
+    return GumbelBatch(w, base.p_logits, noise, draft, base.gamma_len, base.temperature, base.top_k, base.top_p,
+                       base.seed, base.q_logits)

@@ -346,19 +346,20 @@ def verify_batch(p_logits, q_logits, draft, u, temperature, top_k, top_p, gamma_
 # agree).  Gumbel-max sampling itself (argmax of logits plus independent
 # Gumbel noise follows the softmax) is the same section's first part.
 #
-# log p_k(i) = s_i - log S over the processed support (s = z / T), so the
-# argmax only needs the support and s_i + g_i; log S is common to every i.
-# Readings: the score is formed in float32 as fl(fl(z / T) + g), the
-# precision of the kernel, so that both sides take the argmax decision on the
-# same numbers; ties go to the lowest id; T = 0 is exact argmax matching (the
-# noise is unused, as in "Draft and verify").
+# log p_k(i) = z_i / T - log S over the processed support, so the argmax only
+# needs the support and z_i / T + g_i (log S is common to every i), or, after
+# multiplying by T > 0, which keeps the argmax, z_i + T g_i.
+# Readings: the score is formed in float32 as fl(z + fl(T * g)) with no fused
+# multiply-add, the precision of the kernel, so that both sides take the
+# argmax decision on the same numbers; ties go to the lowest id; T = 0 is
+# exact argmax matching (the noise is unused, as in "Draft and verify").
 
 def gumbel_scores(z: np.ndarray, g: np.ndarray, T: float) -> np.ndarray:
-    """float32 scores fl(fl(z / T) + g) of one row (z decoded logits, g the
+    """float32 scores fl(z + fl(T * g)) of one row (z decoded logits, g the
     row's noise, T > 0)."""
     z32 = np.asarray(z, dtype=np.float32)
-    s = z32 / np.float32(T)
-    return (s + np.asarray(g, dtype=np.float32)).astype(np.float32)
+    tg = (np.float32(T) * np.asarray(g, dtype=np.float32)).astype(np.float32)
+    return (z32 + tg).astype(np.float32)
 
 
 def gumbel_target_token(z: np.ndarray, g: np.ndarray, T: float, top_k: int, top_p: float):

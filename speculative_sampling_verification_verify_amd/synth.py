@@ -372,7 +372,7 @@ def _coupled_drafter(zq: np.ndarray, g: np.ndarray, T: float, k: int, top_p: flo
         keep = np.zeros(V, dtype=bool)
         keep[order[:cut]] = True
         cand &= keep
-    score = (zq.astype(np.float32) / np.float32(T) + g).astype(np.float32)
+    score = (zq.astype(np.float32) + np.float32(T) * g).astype(np.float32)
     return int(np.argmax(np.where(cand, score, np.float32(-np.inf))))
 
 

@@ -99,6 +99,120 @@ def cpu_baseline(bt, seconds_target: float, cores: int):
                       f"{dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
 
 
+def _gumbel_rows(args):
+    import oracle
+    (p, noise, draft, T, k, tp, gl), rows = args
+    r = oracle.gumbel_verify_batch(p, noise, draft, T, k, tp, gl, rows=rows)
+    return len(rows), int((r.n >= 0).sum())
+
+
+def cpu_baseline_gumbel(gb, seconds_target: float, cores: int):
+    """Time the CPU oracle of the shared-noise verify on whole sequences of
+    the same workload, in worker processes (fork)."""
+    import multiprocessing as mp
+    import oracle
+    data = (gb.p_logits, gb.noise, gb.draft, gb.temperature, gb.top_k, gb.top_p, gb.gamma_len)
+    t0 = time.perf_counter()
+    oracle.gumbel_verify_batch(*data, rows=[0])
+    per_seq = max(time.perf_counter() - t0, 1e-4)
+    n = int(min(gb.B, max(cores, seconds_target / per_seq)))
+    chunks = [list(range(i, n, cores)) for i in range(cores) if i < n]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(chunks)) as pool:
+        pool.map(_gumbel_rows, [(data, c) for c in chunks])
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
+            "sample": f"{n} sequences of the same workload (shared-noise oracle, {len(chunks)} worker processes, "
+                      f"{dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
+
+
+def main_gumbel(args):
+    """The shared-noise verify on workload `args.workload`'s shapes."""
+    t_gen = time.perf_counter()
+    gb = synth.make_gumbel_batch(args.workload)
+    t_gen = time.perf_counter() - t_gen
+    es = gb.p_logits.itemsize
+    g1 = gb.gamma_len.astype(np.int64) + 1
+    noisy = gb.temperature > 0
+    kbytes = int((g1 * gb.V * es).sum() + (g1[noisy] * gb.V * 4).sum())
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cores = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            cores = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline_gumbel(gb, args.cpu_seconds, cores)
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+    dev = torch.device("cuda:0")
+    if gb.p_logits.dtype == np.uint16:
+        P = torch.from_numpy(gb.p_logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        dtype_name = "bf16"
+    else:
+        P = torch.from_numpy(gb.p_logits).to(dev)
+        dtype_name = "fp32"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    N = t(gb.noise)
+    draft, temp, topk, topp, gl = t(gb.draft), t(gb.temperature), t(gb.top_k), t(gb.top_p), t(gb.gamma_len)
+    ver = binding.GumbelVerifier(gb.B, gb.gamma_max, device=dev)
+    nsets = int(min(32, max(1, -(-ROTATE_BYTES // max(kbytes, 1)))))
+    sets = [(P, N)] + [(P.clone(), N.clone()) for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+
+    def step(j):
+        Pj, Nj = sets[j % nsets]
+        ver(Pj, Nj, draft, temp, topk, topp, gl)
+
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j, (a, b) in enumerate(evs):
+        binding.spec_verify_set_stage_events(a, b, binding.SV_KERNEL_GUMBEL)
+        step(j)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    binding.spec_verify_set_stage_events(None, None)
+    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / K
+    n_acc = ver.n_accepted.cpu().numpy()
+    k_avg = float(k_ms.mean())
+    achieved = kbytes / (k_avg * 1e-3) / 1e9
+    w = gb.workload
+    out = {
+        "metric": "shared-noise spec-verify rows/sec + achieved HBM GB/s vs peak",
+        "value": gb.B / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": gb.B, "V": gb.V, "gamma": gb.gamma_max,
+                   "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile("gumbel_kernel", w.name),
+                     "kernel": "gumbel_kernel", "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,
+                     "kernel_p10_us": float(np.percentile(k_ms, 10) * 1e3),
+                     "kernel_p90_us": float(np.percentile(k_ms, 90) * 1e3)},
+        "cpu_baseline": cpu,
+        "extra": {"mean_tokens_per_round": float((n_acc[n_acc >= 0] + 1).mean()),
+                  "input_sets_rotated": nsets, "input_generation_s": t_gen},
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +221,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (3 = headline)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--gumbel", action="store_true",
+                    help="the shared-noise (Gumbel coupling) verify on the workload's shapes instead")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -125,6 +241,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": args.steps}))
+        return
+
+    if args.gumbel:
+        main_gumbel(args)
         return
 
     t_gen = time.perf_counter()

@@ -120,12 +120,48 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
                 int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Verify with shared Gumbel noise (Gumbel coupling; "Speculative Decoding: the
+ * art of guessing well", section "Sampling with shared noise").  The drafter
+ * proposed x_k = argmax_i(log q_k(i) + g_k,i) with the same noise vectors g_k
+ * that the target uses here; the target's own sample at position k is
+ * t_k = argmax_i(log p_k(i) + g_k,i) over its processed distribution p_k
+ * (temperature, top-k, top-p as for spec_verify).  The verify keeps the longest
+ * prefix with x_k == t_k and appends t at the first disagreement (t after the
+ * last draft when all agree): exact matching, drafter-independent output.
+ * The score is formed in float32 as fl(z + fl(T * g)) with no fused
+ * multiply-add (the argmax of log p + g, multiplied by T > 0); ties go to the
+ * lowest id; T = 0 is argmax of z and the noise is not read.
+ *
+ *  p_logits     [B][gamma_max+1][V] target logits (bf16 bit patterns or fp32).
+ *  noise        [B][gamma_max+1][V] float Gumbel noise, one vector per position
+ *               (the same vectors the drafter used).  NaN or infinite noise in a
+ *               used row (T > 0) makes the sequence invalid.
+ *  draft_tokens [B][gamma_max] int32 proposals; slots beyond gamma_b ignored.
+ *  gamma_len, temperature, top_k, top_p: as for spec_verify (uniforms are not used).
+ *  out_tokens   [B][gamma_max+1] int32: x_1..x_n, then t_n, then -1 padding.
+ *  out_n_accepted [B] int32: n, or -1 for an invalid sequence.
+ *  out_target   [B][gamma_max+1] int32: t_k for k <= gamma_b, -1 beyond (and for an
+ *               invalid sequence).  Also the call's only scratch: no workspace.
+ *
+ * Invalid data (as for spec_verify, plus bad noise) is reported per sequence with
+ * n = -1 and tokens -1.  Base pointers must be aligned to their element size;
+ * 16-byte alignment and V a multiple of 8 (bf16) or 4 (fp32) take the vector
+ * path.  Asynchronous on `stream`; allocates nothing.  Returns SV_OK or a
+ * negative code (nothing enqueued).
+ */
+int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
+                       const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
+                       const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
+                       int32_t* out_n_accepted, int32_t* out_target, void* stream);
+
 /* Kernels of one call, for spec_verify_set_stage_events. */
 enum {
   SV_KERNEL_SELECT = 0,  /* streaming top-k / argmax select over the logit rows      */
   SV_KERNEL_PAIR = 1,    /* per-(sequence, position) pass over dense (unfiltered,   */
                          /* large top-k, top-p) sequences; launched when V allows   */
-  SV_KERNEL_FINISH = 2   /* per-sequence acceptance, first rejection and draw       */
+  SV_KERNEL_FINISH = 2,  /* per-sequence acceptance, first rejection and draw       */
+  SV_KERNEL_GUMBEL = 3   /* per-(sequence, position) pass of spec_verify_gumbel      */
 };
 
 /*
@@ -143,7 +179,7 @@ int spec_verify_set_stage_events(int kernel, void* begin, void* end);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 2. */
+/* ABI version: 3. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_BF16, SV_FP32 = 0, 1
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
-SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH = 0, 1, 2
+SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL = 0, 1, 2, 3
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify",
-            "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events")
+            "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events", "spec_verify_gumbel")
 
 _lib = None
 
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_version.argtypes = []
         L.spec_verify_version.restype = i
         L.spec_verify_set_stage_events.argtypes = [i, vp, vp]
+        L.spec_verify_gumbel.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp]
+        L.spec_verify_gumbel.restype = i
         L.spec_verify_set_stage_events.restype = i
         _lib = L
     return _lib
@@ -175,3 +177,49 @@ class Verifier:
         spec_verify(p_logits, q_logits, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p,
                     self.tokens, self.n_accepted, self.alpha, self.pq, self.workspace, stream)
         return self.tokens, self.n_accepted, self.alpha, self.pq
+
+
+def spec_verify_gumbel(p_logits: torch.Tensor, noise: torch.Tensor, draft_tokens: torch.Tensor,
+                       gamma_len: Optional[torch.Tensor], temperature: torch.Tensor, top_k: Optional[torch.Tensor],
+                       top_p: Optional[torch.Tensor], out_tokens: torch.Tensor, out_n_accepted: torch.Tensor,
+                       out_target: torch.Tensor, stream=None) -> None:
+    """Enqueue one shared-noise verify call (see include/spec_verify.h)."""
+    if p_logits.dim() != 3:
+        raise ValueError("p_logits must be [B, gamma_max+1, V]")
+    B, G1, V = p_logits.shape
+    G = G1 - 1
+    dev = p_logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must live in GPU memory")
+    dt = _dtype_code(p_logits)
+    _check(p_logits, "p_logits", p_logits.dtype, (B, G + 1, V), dev)
+    _check(noise, "noise", torch.float32, (B, G + 1, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, G), dev)
+    _check(gamma_len, "gamma_len", torch.int32, (B,), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(top_k, "top_k", torch.int32, (B,), dev)
+    _check(top_p, "top_p", torch.float32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, G + 1), dev)
+    _check(out_n_accepted, "out_n_accepted", torch.int32, (B,), dev)
+    _check(out_target, "out_target", torch.int32, (B, G + 1), dev)
+    rc = lib().spec_verify_gumbel(_ptr(p_logits), dt, _ptr(noise), _ptr(draft_tokens), _ptr(gamma_len),
+                                  _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V, _ptr(out_tokens),
+                                  _ptr(out_n_accepted), _ptr(out_target), _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_gumbel")
+
+
+class GumbelVerifier:
+    """Output buffers for shared-noise verify calls of one shape."""
+
+    def __init__(self, B: int, gamma_max: int, device="cuda"):
+        dev = torch.device(device)
+        self.tokens = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
+        self.n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.target = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
+
+    def __call__(self, p_logits, noise, draft_tokens, temperature, top_k=None, top_p=None, gamma_len=None,
+                 stream=None):
+        spec_verify_gumbel(p_logits, noise, draft_tokens, gamma_len, temperature, top_k, top_p, self.tokens,
+                           self.n_accepted, self.target, stream)
+        return self.tokens, self.n_accepted, self.target

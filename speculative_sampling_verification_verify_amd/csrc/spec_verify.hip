@@ -31,6 +31,7 @@
 #include "sv_wave.h"
 #include "sv_pair.h"
 #include "sv_finish.h"
+#include "sv_gumbel.h"
 
 #include <math.h>
 #include <stdio.h>
@@ -298,6 +299,63 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   return SV_OK;
 }
 
+template <typename ET, bool VECTOR>
+static hipError_t launch_gumbel(const Args& a, hipStream_t st) {
+  hipError_t e;
+  if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((gumbel_kernel<ET, GUMBEL_NT, VECTOR>), dim3((unsigned)((long long)a.B * (a.G + 1))),
+                     dim3(GUMBEL_NT), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = stage_mark(SV_KERNEL_GUMBEL, false, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(gumbel_finish_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
+                                  const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
+                                  const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
+                                  int32_t* out_n_accepted, int32_t* out_target, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  if (!p_logits || !noise || !draft_tokens || !temperature || !out_tokens || !out_n_accepted || !out_target)
+    return SV_ERR_ARG;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)p_logits % es) || ((uintptr_t)noise % 4)) return SV_ERR_ARG;
+  if ((long long)B * (gamma_max + 1) > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
+  const int vec = dtype == SV_BF16 ? 8 : 4;
+  const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)noise % 16 == 0);
+  int vb = 0;
+  while ((1LL << vb) < (long long)V + 1) ++vb;
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.p = p_logits;
+  a.draft = draft_tokens;
+  a.gamma_len = gamma_len;
+  a.temp = temperature;
+  a.topk = top_k;
+  a.topp = top_p;
+  a.B = B;
+  a.G = gamma_max;
+  a.V = V;
+  a.fixbits = 62 - vb;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n_accepted;
+  a.noise = noise;
+  a.out_target = out_target;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == SV_BF16) e = vector_ok ? launch_gumbel<uint16_t, true>(a, st) : launch_gumbel<uint16_t, false>(a, st);
+  else e = vector_ok ? launch_gumbel<float, true>(a, st) : launch_gumbel<float, false>(a, st);
+  if (e != hipSuccess) {
+    snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(e));
+    return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
 extern "C" const char* spec_verify_strerror(int code) {
   switch (code) {
     case SV_OK: return "ok";
@@ -309,10 +367,11 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 2; }
+extern "C" int spec_verify_version(void) { return 3; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
-  if (kernel != SV_KERNEL_SELECT && kernel != SV_KERNEL_PAIR && kernel != SV_KERNEL_FINISH) return SV_ERR_ARG;
+  if (kernel != SV_KERNEL_SELECT && kernel != SV_KERNEL_PAIR && kernel != SV_KERNEL_FINISH && kernel != SV_KERNEL_GUMBEL)
+    return SV_ERR_ARG;
   g_stage_kernel = kernel;
   g_stage_begin = (hipEvent_t)begin;
   g_stage_end = (hipEvent_t)end;

@@ -1,0 +1,182 @@
+// Verify with shared Gumbel noise ("Speculative Decoding: the art of guessing
+// well", section "Sampling with shared noise"): the drafter proposed
+// x_k = argmax_i(log q_k(i) + g_k,i) with the same noise vectors g_k that the
+// target uses here.  The target's own sample at position k is
+// t_k = argmax_i(log p_k(i) + g_k,i); the verify keeps the longest prefix with
+// x_k == t_k and appends t at the first disagreement (t after the last draft
+// when all agree).  Exact matching, like greedy decoding.
+//
+// log p_k(i) = z_i / T - log S on the processed support, so the argmax needs
+// only the support and z_i + T g_i (the factor T > 0 keeps the argmax); the
+// score is formed in float32 as fl(z + fl(T * g)) with no fused multiply-add,
+// and ties go to the lowest id.  T = 0 is argmax of z (noise unused).
+//
+// gumbel_kernel: one workgroup per (sequence, position).  Unfiltered rows
+// take one pass over the logits and the noise (validity, and the argmax of
+// the score); top-k rows first find the k-th largest key (block radix
+// select), top-p rows the nucleus threshold (the pair kernel's row
+// statistics), then the argmax pass runs over the support.
+// gumbel_finish_kernel: one wavefront per sequence: the first disagreement
+// by one ballot and find-first-set, and the outputs.
+#pragma once
+
+#include "sv_pair.h"
+
+namespace sv {
+
+constexpr int GUMBEL_NT = 512;
+constexpr int32_t GUMBEL_BAD_ROW = -2;
+
+// Order-preserving 32-bit key of a float score (larger float -> larger key;
+// every non-NaN float maps above 0, so 0 means "no candidate").
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+template <typename ET, int NTP, bool VECTOR>
+__global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
+  using T = PT<ET, VECTOR>;
+  using U = typename T::U;
+  constexpr int E = T::E;
+  constexpr int LEVELS = Key<ET>::LEVELS;
+  __shared__ PairSmem<NTP> s;
+  __shared__ PairStream ps;
+  const int G1 = a.G + 1;
+  const int b = blockIdx.x / G1, j = blockIdx.x - (blockIdx.x / G1) * G1;
+  const int gl = a.gamma_len ? a.gamma_len[b] : a.G;
+  const int g = min(max(gl, 1), a.G);
+  if (j > g) return;                          // padding: the finisher writes it
+  int32_t* outp = a.out_target + (size_t)b * G1 + j;
+  const float Tv = a.temp[b];
+  const int k = a.topk ? a.topk[b] : 0;
+  const float tp = a.topp ? a.topp[b] : 1.0f;
+  if (!(Tv >= 0.0f) || tp != tp) {            // the finisher rejects the sequence
+    if (threadIdx.x == 0) *outp = GUMBEL_BAD_ROW;
+    return;
+  }
+  const int V = a.V;
+  const int NU = VECTOR ? V / E : V;
+  const U* gp = reinterpret_cast<const U*>(row_ptr<ET>(a, b, true, j));
+  const float* gn = a.noise + ((size_t)b * G1 + j) * (size_t)V;
+  const bool use_noise = Tv > 0.0f;
+  const bool filtered = use_noise && ((k > 0 && k < V) || tp < 1.0f);
+
+  // Support threshold: keep z >= zthr.
+  float zthr = -INFINITY;
+  uint32_t bad = 0;
+  if (filtered) {
+    // Validity and the maximum (the threshold passes need it).
+    uint32_t km = 0;
+    row_each<ET, NTP, VECTOR, false>(gp, NU, [&](uint32_t raw) {
+      const float z = T::val(raw);
+      bad |= z < INFINITY ? 0u : 1u;
+      km = max(km, T::key(raw));
+    });
+    uint32_t dummy = 0;
+    pb_max3<NTP>(km, bad, dummy, s.red_u);
+    if (bad || km <= Key<ET>::NEG_INF) {
+      if (threadIdx.x == 0) *outp = GUMBEL_BAD_ROW;
+      return;
+    }
+    if (tp < 1.0f) {
+      Mode m;
+      m.g = g;
+      m.mode = MODE_DENSE;
+      m.k = 0;
+      m.T = Tv;
+      m.tp = tp;
+      PairExtra<false>& pe = ps;
+      zthr = row_stats<ET, NTP, VECTOR, false>(gp, NU, Key<ET>::value(km), a, m, k, s, pe).zthr;
+    } else {
+      const uint32_t kth = block_kth_largest<LEVELS, NTP>(
+          [&](auto fn) { row_each<ET, NTP, VECTOR, false>(gp, NU, [&](uint32_t raw) { fn(T::key(raw)); }); },
+          (uint32_t)k, s.hist.h32, s.bc);
+      zthr = key_floor_value<ET>(kth ? kth : 1u);
+    }
+  }
+
+  // The argmax pass: the lowest id with the largest score over the support.
+  uint32_t bkey = 0, bidx = NONE, kmax = 0;
+  auto consider = [&](uint32_t raw, float noise, uint32_t idx) {
+#pragma clang fp contract(off)
+    // Two roundings, as the score's definition says: no fused multiply-add.
+    const float z = T::val(raw);
+    bad |= z < INFINITY ? 0u : 1u;
+    kmax = max(kmax, T::key(raw));
+    if (use_noise) bad |= fabsf(noise) < INFINITY ? 0u : 1u;
+    if (z >= zthr) {
+      const float tg = Tv * noise;
+      const float sc = use_noise ? z + tg : z;
+      const uint32_t sk = score_key(sc);
+      if (sc == sc && sk > bkey) {        // strictly greater: the first of equals in id order stays
+        bkey = sk;
+        bidx = idx;
+      }
+    }
+  };
+  for (int ui = threadIdx.x; ui < NU; ui += NTP) {
+    const U u = gp[ui];
+    if constexpr (VECTOR) {
+      float nv[E];
+      if (use_noise) {
+        const float4* np4 = reinterpret_cast<const float4*>(gn + (size_t)ui * E);
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const float4 f = np4[q];
+          nv[4 * q] = f.x;
+          nv[4 * q + 1] = f.y;
+          nv[4 * q + 2] = f.z;
+          nv[4 * q + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < E; ++q) nv[q] = 0.0f;
+      }
+      T::each(u, [&](int e, uint32_t raw) { consider(raw, nv[e], (uint32_t)(ui * E + e)); });
+    } else {
+      const float nz = use_noise ? gn[ui] : 0.0f;
+      T::each(u, [&](int, uint32_t raw) { consider(raw, nz, (uint32_t)ui); });
+    }
+  }
+  const uint32_t mykey = bkey;
+  pb_max3<NTP>(bkey, bad, kmax, s.red_u);     // block-wide maxima
+  const uint32_t win = pb_min<NTP>(bkey != 0u && mykey == bkey ? bidx : NONE, s.red_u);
+  if (threadIdx.x == 0)
+    *outp = (bad || kmax <= Key<ET>::NEG_INF || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
+}
+
+// One wavefront per sequence: validity, the first disagreement between the
+// drafts and the target's samples (one ballot, find-first-set), outputs.
+__global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + wave;
+  if (b >= a.B) return;
+  const int G = a.G, G1 = G + 1;
+  const int gl = a.gamma_len ? a.gamma_len[b] : G;
+  const float Tv = a.temp[b];
+  const float tp = a.topp ? a.topp[b] : 1.0f;
+  const int g = min(max(gl, 1), G);
+  int32_t* tgt = a.out_target + (size_t)b * G1;
+  const int32_t* xb = a.draft + (size_t)b * G;
+  uint32_t badl = (gl >= 1 && gl <= G && Tv >= 0.0f && tp == tp) ? 0u : 1u;
+  for (int jj = lane; jj <= g; jj += 64) badl |= tgt[jj] < 0 ? 1u : 0u;
+  bool mism = false;
+  if (lane < g) {
+    const int x = xb[lane];
+    badl |= (x < 0 || x >= a.V) ? 1u : 0u;
+    mism = x != tgt[lane];
+  }
+  const bool ok = __ballot(badl != 0u) == 0ull;
+  const unsigned long long mask = __ballot(mism);
+  const int n = mask ? __ffsll((long long)mask) - 1 : g;
+  const int32_t tok = ok ? tgt[n] : -1;
+  int32_t* ot = a.out_tokens + (size_t)b * G1;
+  for (int jj = lane; jj <= G; jj += 64) {
+    ot[jj] = ok ? (jj < n ? xb[jj] : (jj == n ? tok : -1)) : -1;
+    if (!ok || jj > g) tgt[jj] = -1;
+  }
+  if (lane == 0) a.out_n[b] = ok ? n : -1;
+}
+
+}  // namespace sv

@@ -314,7 +314,7 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
   const int fb = a.fixbits;
   const float two_fb = ldexpf(1.0f, fb), two_fb32 = ldexpf(1.0f, fb - 32);
   auto each = [&](auto fn) { row_each<ET, NTP, VECTOR, LDSR>(src, NU, fn); };
-  if (k > KMAX_SPARSE && k < a.V) {
+  if (k > 0 && k < a.V) {   // dense sequences reach here only with k > KMAX_SPARSE
     const uint32_t kth = block_kth_largest<LEVELS, NTP>(
         [&](auto fn) { each([&](uint32_t raw) { fn(T::key(raw)); }); }, (uint32_t)k, s.hist.h32, s.bc);
     st.zthr = key_floor_value<ET>(kth ? kth : 1u);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 2
+    assert binding.spec_verify_version() == 3
 
 
 def test_workspace_bytes():
@@ -80,6 +80,39 @@ def test_host_argument_errors():
     rc = L.spec_verify_workspace_init(nul, 0, B, G, V, binding.SV_BF16, nul)
     assert rc == binding.SV_ERR_WORKSPACE
     assert L.spec_verify_workspace_init(fake, need, B, 0, V, binding.SV_BF16, nul) == binding.SV_ERR_ARG
+
+
+def test_gumbel_host_argument_errors():
+    L = _ensure_built()
+    fake = ctypes.c_void_p(0x100000)   # never dereferenced: every case below fails on the host
+    nul = None
+    B, G, V = 2, 3, 64
+
+    def call(p=fake, dt=binding.SV_BF16, noise=fake, draft=fake, temp=fake, B=B, G=G, V=V, out=fake, tgt=fake):
+        return L.spec_verify_gumbel(p, dt, noise, draft, nul, temp, nul, nul, B, G, V, out, out, tgt, nul)
+
+    assert call(dt=3) == binding.SV_ERR_UNSUPPORTED
+    assert call(G=65) == binding.SV_ERR_UNSUPPORTED
+    assert call(V=(1 << 20) + 1) == binding.SV_ERR_UNSUPPORTED
+    assert call(G=0) == binding.SV_ERR_ARG
+    assert call(B=-1) == binding.SV_ERR_ARG
+    assert call(p=nul) == binding.SV_ERR_ARG
+    assert call(noise=nul) == binding.SV_ERR_ARG
+    assert call(draft=nul) == binding.SV_ERR_ARG
+    assert call(temp=nul) == binding.SV_ERR_ARG
+    assert call(out=nul) == binding.SV_ERR_ARG
+    assert call(tgt=nul) == binding.SV_ERR_ARG
+    assert call(noise=ctypes.c_void_p(0x100002)) == binding.SV_ERR_ARG      # misaligned float noise
+    assert call(p=ctypes.c_void_p(0x100001)) == binding.SV_ERR_ARG          # misaligned bf16
+    assert call(B=0) == binding.SV_OK
+
+
+def test_stage_events_kernel_selector():
+    L = _ensure_built()
+    assert L.spec_verify_set_stage_events(7, None, None) == binding.SV_ERR_ARG
+    assert L.spec_verify_set_stage_events(-1, None, None) == binding.SV_ERR_ARG
+    for k in (binding.SV_KERNEL_SELECT, binding.SV_KERNEL_PAIR, binding.SV_KERNEL_FINISH, binding.SV_KERNEL_GUMBEL):
+        assert L.spec_verify_set_stage_events(k, None, None) == binding.SV_OK
 
 
 def test_strerror():

@@ -166,10 +166,12 @@ def invalid_result(gamma_max: int) -> SeqResult:
                      np.full((gamma_max, 2), np.nan), INF, INF, INF, False)
 
 
-def _inputs_valid(zp, zq, draft, u, T, top_p, gamma_b, V, gamma_max) -> bool:
+def _inputs_valid(zp, zq, draft, u, T, top_p, gamma_b, V, gamma_max, lenience=1.0) -> bool:
     if not (1 <= gamma_b <= gamma_max):
         return False
     if not (T >= 0.0) or math.isnan(top_p):
+        return False
+    if not (0.0 <= lenience <= 1.0):
         return False
     x = draft[:gamma_b]
     if (x < 0).any() or (x >= V).any():
@@ -187,19 +189,26 @@ def _inputs_valid(zp, zq, draft, u, T, top_p, gamma_b, V, gamma_max) -> bool:
 
 
 def verify_sequence(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, u: np.ndarray,
-                    T: float, top_k: int, top_p: float, gamma_b: int) -> SeqResult:
+                    T: float, top_k: int, top_p: float, gamma_b: int, lenience: float = 1.0) -> SeqResult:
     """Verify one sequence.
 
     zp: [gamma_max+1, V] target logits (float64), zq: [gamma_max, V] draft
     logits, draft: [gamma_max] tokens, u: [gamma_max+1] uniforms where
     u[i] (i < gamma_b) tests draft i and u[gamma_max] drives the residual or
     bonus draw.  Positions at and beyond gamma_b (drafts) and gamma_b+1
-    (targets) are padding and are never read."""
+    (targets) are padding and are never read.
+
+    lenience l in [0, 1] multiplies q(x) in the acceptance test (the
+    Leviathan review, "Lenience"): accept iff u * l * q(x) < p(x).  l = 1 is
+    the exact method.  Reading: the page changes only the acceptance
+    decision, so the residual stays max(0, p - q); with it no token's output
+    probability exceeds p(x) / l, the page's guarantee."""
     gamma_max = zq.shape[0]
     V = zp.shape[1]
     T = float(T)
     top_p = float(top_p)
-    if not _inputs_valid(zp, zq, draft, u, T, top_p, gamma_b, V, gamma_max):
+    lenience = float(lenience)
+    if not _inputs_valid(zp, zq, draft, u, T, top_p, gamma_b, V, gamma_max, lenience):
         return invalid_result(gamma_max)
     P = [process(zp[j], T, top_k, top_p) for j in range(gamma_b + 1)]
     Q = [process(zq[i], T, top_k, top_p) for i in range(gamma_b)]
@@ -216,9 +225,9 @@ def verify_sequence(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, u: np.nda
     for i in range(gamma_b):
         px, qx = pq[i]
         ui = float(u[i])
-        if T > 0.0 and qx > 0.0:
-            margin_acc = min(margin_acc, abs(ui - px / qx))
-        if not (ui * qx < px):
+        if T > 0.0 and lenience * qx > 0.0:
+            margin_acc = min(margin_acc, abs(ui - px / (lenience * qx)))
+        if not (ui * lenience * qx < px):
             n = i
             break
 
@@ -295,20 +304,24 @@ _SHARED = {}
 def _one(b: int) -> SeqResult:
     a = _SHARED
     return verify_sequence(decode_row(a["p"][b]), decode_row(a["q"][b]), a["draft"][b], a["u"][b],
-                           float(a["T"][b]), int(a["k"][b]), float(a["top_p"][b]), int(a["g"][b]))
+                           float(a["T"][b]), int(a["k"][b]), float(a["top_p"][b]), int(a["g"][b]),
+                           float(a["l"][b]))
 
 
 def verify_batch(p_logits, q_logits, draft, u, temperature, top_k, top_p, gamma_len,
-                 rows: Optional[Sequence[int]] = None, processes: Optional[int] = None) -> BatchResult:
+                 rows: Optional[Sequence[int]] = None, processes: Optional[int] = None,
+                 lenience=None) -> BatchResult:
     """Run the oracle over the sequences in ``rows`` (default: all).
 
-    processes: worker processes (fork); None -> all host cores, 1 -> serial."""
+    processes: worker processes (fork); None -> all host cores, 1 -> serial.
+    lenience: [B] per-sequence lenience, None -> 1 (the exact method)."""
     B = p_logits.shape[0]
     gamma_max = q_logits.shape[1]
     rows = list(range(B)) if rows is None else list(rows)
     _SHARED.update(p=p_logits, q=q_logits, draft=np.asarray(draft), u=np.asarray(u),
                    T=np.asarray(temperature), k=np.asarray(top_k), top_p=np.asarray(top_p),
-                   g=np.asarray(gamma_len))
+                   g=np.asarray(gamma_len),
+                   l=np.ones(B, np.float32) if lenience is None else np.asarray(lenience))
     nproc = os.cpu_count() if processes is None else processes
     nproc = max(1, min(nproc, len(rows)))
     if nproc == 1:

@@ -121,6 +121,68 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spec_verify with lenience (the Leviathan review, section "Lenience"): the
+ * acceptance test multiplies q(x) by l in [0, 1], accept iff u * l * q(x) < p(x).
+ * No token is then output with more than 1/l times its target probability;
+ * alpha (the acceptance rate) rises as l falls; l = 1 is spec_verify exactly.
+ * The residual stays max(0, p - q) (the page changes only the acceptance
+ * decision).  out_alpha still reports the overlap sum min(p, q).
+ *
+ *  lenience     [B] float in [0, 1], or NULL (all 1).  A value outside [0, 1] or NaN
+ *               makes that sequence invalid.
+ * Every other argument, the workspace and the error behaviour are those of
+ * spec_verify.
+ */
+int spec_verify_ex(const void* p_logits, const void* q_logits, int dtype,
+                   const int32_t* draft_tokens, const int32_t* gamma_len, const float* uniforms,
+                   const float* temperature, const int32_t* top_k, const float* top_p, const float* lenience,
+                   int B, int gamma_max, int V,
+                   int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sampling one token per row from its processed distribution (the drafter's
+ * step before a verify, x ~ q after temperature / top-k / top-p: "Fast
+ * Inference from Transformers via Speculative Decoding", mtandhj.com summary,
+ * "Speculative Sampling: theoretical basis"), by the inverse CDF over
+ * ascending vocabulary id at the row's uniform ("Speculative Decoding: the art
+ * of guessing well", "Sampling with shared noise", textbook method):
+ * token = min{v : C(v) > u * Z}.  T = 0 is argmax (lowest id on ties).
+ *
+ *  logits       [R][V] bf16 bit patterns or fp32.
+ *  uniforms     [R] float in [0, 1).
+ *  temperature, top_k, top_p: [R] as for spec_verify (top_k / top_p may be NULL).
+ *  out_tokens   [R] int32: the sampled token, or -1 for an invalid row (NaN / +inf
+ *               logits, no finite logit, bad temperature or top_p, bad uniform).
+ *  workspace    device buffer of spec_sample_workspace_bytes(R, V, dtype) bytes,
+ *               256-byte aligned, prepared once with spec_sample_workspace_init.
+ * Asynchronous on `stream`, allocates nothing.  Returns SV_OK or a negative code.
+ */
+size_t spec_sample_workspace_bytes(int R, int V, int dtype);
+int spec_sample_workspace_init(void* workspace, size_t workspace_bytes, int R, int V, int dtype, void* stream);
+int spec_sample(const void* logits, int dtype, const float* uniforms, const float* temperature,
+                const int32_t* top_k, const float* top_p, int R, int V, int32_t* out_tokens,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The shared-noise drafter's step ("Speculative Decoding: the art of guessing
+ * well", section "Sampling with shared noise"): per row, the Gumbel-max sample
+ * argmax_i(log q(i) + g_i) over the processed distribution, scored as
+ * fl(z + fl(T * g)) without fused multiply-add, lowest id on ties; T = 0 is
+ * argmax of z.  With the drafter's logits and the noise vectors later given to
+ * spec_verify_gumbel, these are the drafts that the verify compares against.
+ *
+ *  logits       [R][V] bf16 or fp32;  noise [R][V] float.
+ *  temperature, top_k, top_p: [R] as for spec_verify (top_k / top_p may be NULL).
+ *  out_tokens   [R] int32: the sample, or -1 for an invalid row (as for
+ *               spec_verify_gumbel).
+ * No workspace; asynchronous on `stream`.  Returns SV_OK or a negative code.
+ */
+int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const float* temperature,
+                       const int32_t* top_k, const float* top_p, int R, int V, int32_t* out_tokens,
+                       void* stream);
+
+/*
  * Verify with shared Gumbel noise (Gumbel coupling; "Speculative Decoding: the
  * art of guessing well", section "Sampling with shared noise").  The drafter
  * proposed x_k = argmax_i(log q_k(i) + g_k,i) with the same noise vectors g_k
@@ -176,10 +238,30 @@ enum {
  */
 int spec_verify_set_stage_events(int kernel, void* begin, void* end);
 
+/*
+ * Throughput analytics (host functions; no GPU, no stream).  From the Leviathan
+ * review ("Analysis": expected generated tokens, walltime, operations, optimal
+ * gamma) and "Speculative Decoding: the art of guessing well" ("How many tokens
+ * do we get?"):
+ *   expected tokens per round  (1 - alpha^(gamma+1)) / (1 - alpha)   (gamma+1 at alpha = 1)
+ *   speedup                    expected tokens / (gamma c + 1), c = drafter/target cost ratio
+ *   operations                 (gamma c_hat + gamma + 1) / expected tokens, relative to plain
+ *                              decoding, c_hat = drafter/target operations ratio
+ *   optimal gamma              the gamma in [1, gamma_max] with the largest speedup (smallest on ties)
+ *   acceptance length tau      1 + sum_{k<=gamma} prod_{i<=k} alpha_i, from per-position rates
+ *                              (host array alpha[gamma], e.g. a column mean of spec_verify's out_alpha)
+ * alpha must lie in [0, 1]; invalid arguments give NaN (or -1 for the optimal gamma).
+ */
+double spec_verify_expected_tokens(double alpha, int gamma);
+double spec_verify_speedup(double alpha, int gamma, double c);
+double spec_verify_operations(double alpha, int gamma, double c_hat);
+int spec_verify_optimal_gamma(double alpha, double c, int gamma_max);
+double spec_verify_acceptance_length(const double* alpha, int gamma);
+
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 3. */
+/* ABI version: 4. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

@@ -477,3 +477,41 @@ def gumbel_verify_batch(p_logits, noise, draft, temperature, top_k, top_p, gamma
         out.target[k] = r.target
         out.margin_topp[k] = r.margin_topp
     return out
+
+
+# ----------------------------------------------------------------------------
+# Sampling one token per row (the drafter's step before a verify).
+# ----------------------------------------------------------------------------
+# x ~ the processed distribution ("Fast Inference from Transformers via
+# Speculative Decoding", mtandhj.com summary, "Speculative Sampling:
+# theoretical basis": both models sample from their adjusted distributions),
+# drawn by the inverse CDF at one uniform ("Speculative Decoding: the art of
+# guessing well", "Sampling with shared noise", textbook method).
+
+@dataclasses.dataclass
+class SampleBatchResult:
+    tokens: np.ndarray        # int32 [R], -1 for an invalid row
+    margin: np.ndarray        # float64 [R]: min of the CDF and top-p margins
+
+
+def sample_row(z: np.ndarray, u: float, T: float, top_k: int, top_p: float):
+    """Returns (token, margin) for one row; (-1, inf) for invalid input."""
+    T = float(T)
+    top_p = float(top_p)
+    if not row_is_valid(z) or not (T >= 0.0) or math.isnan(top_p) or not (0.0 <= u < 1.0):
+        return -1, INF
+    pr = process(z, T, top_k, top_p)
+    t, m_cdf = inverse_cdf(pr.prob, float(u))
+    if T == 0.0:
+        m_cdf = INF
+    return t, min(m_cdf, pr.topp_margin)
+
+
+def sample_batch(logits, u, temperature, top_k, top_p) -> SampleBatchResult:
+    R = logits.shape[0]
+    out = SampleBatchResult(np.full(R, -1, np.int32), np.full(R, INF))
+    for r in range(R):
+        t, m = sample_row(decode_row(logits[r]), float(u[r]), float(temperature[r]), int(top_k[r]), float(top_p[r]))
+        out.tokens[r] = t
+        out.margin[r] = m
+    return out

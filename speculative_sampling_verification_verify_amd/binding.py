@@ -22,8 +22,11 @@ SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL = 0, 1, 2, 
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 
-EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify",
-            "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events", "spec_verify_gumbel")
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify", "spec_verify_ex",
+            "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events", "spec_verify_gumbel",
+            "spec_sample_workspace_bytes", "spec_sample_workspace_init", "spec_sample", "spec_sample_gumbel",
+            "spec_verify_expected_tokens", "spec_verify_speedup", "spec_verify_operations",
+            "spec_verify_optimal_gamma", "spec_verify_acceptance_length")
 
 _lib = None
 
@@ -55,6 +58,27 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_set_stage_events.argtypes = [i, vp, vp]
         L.spec_verify_gumbel.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp]
         L.spec_verify_gumbel.restype = i
+        L.spec_verify_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_ex.restype = i
+        L.spec_sample_workspace_bytes.argtypes = [i, i, i]
+        L.spec_sample_workspace_bytes.restype = sz
+        L.spec_sample_workspace_init.argtypes = [vp, sz, i, i, i, vp]
+        L.spec_sample_workspace_init.restype = i
+        L.spec_sample.argtypes = [vp, i, vp, vp, vp, vp, i, i, vp, vp, sz, vp]
+        L.spec_sample.restype = i
+        L.spec_sample_gumbel.argtypes = [vp, i, vp, vp, vp, vp, i, i, vp, vp]
+        L.spec_sample_gumbel.restype = i
+        d = ctypes.c_double
+        L.spec_verify_expected_tokens.argtypes = [d, i]
+        L.spec_verify_expected_tokens.restype = d
+        L.spec_verify_speedup.argtypes = [d, i, d]
+        L.spec_verify_speedup.restype = d
+        L.spec_verify_operations.argtypes = [d, i, d]
+        L.spec_verify_operations.restype = d
+        L.spec_verify_optimal_gamma.argtypes = [d, d, i]
+        L.spec_verify_optimal_gamma.restype = i
+        L.spec_verify_acceptance_length.argtypes = [ctypes.POINTER(d), i]
+        L.spec_verify_acceptance_length.restype = d
         L.spec_verify_set_stage_events.restype = i
         _lib = L
     return _lib
@@ -126,8 +150,10 @@ def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: to
                 gamma_len: Optional[torch.Tensor], uniforms: torch.Tensor, temperature: torch.Tensor,
                 top_k: Optional[torch.Tensor], top_p: Optional[torch.Tensor],
                 out_tokens: torch.Tensor, out_n_accepted: torch.Tensor, out_alpha: torch.Tensor,
-                out_pq: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
-    """Enqueue one verify call (see include/spec_verify.h for the contract)."""
+                out_pq: Optional[torch.Tensor], workspace: torch.Tensor, stream=None,
+                lenience: Optional[torch.Tensor] = None) -> None:
+    """Enqueue one verify call (see include/spec_verify.h for the contract);
+    with `lenience` ([B] float32) the call goes to spec_verify_ex."""
     if p_logits.dim() != 3 or q_logits.dim() != 3:
         raise ValueError("p_logits must be [B, gamma_max+1, V] and q_logits [B, gamma_max, V]")
     B, G1, V = p_logits.shape
@@ -148,10 +174,18 @@ def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: to
     _check(out_n_accepted, "out_n_accepted", torch.int32, (B,), dev)
     _check(out_alpha, "out_alpha", torch.float32, (B, G), dev)
     _check(out_pq, "out_pq", torch.float32, (B, G, 2), dev)
-    rc = lib().spec_verify(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
-                           _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V,
-                           _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
-                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(lenience, "lenience", torch.float32, (B,), dev)
+    wsb = workspace.numel() * workspace.element_size()
+    if lenience is None:
+        rc = lib().spec_verify(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
+                               _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V,
+                               _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
+                               _ptr(workspace), wsb, _stream_handle(stream))
+    else:
+        rc = lib().spec_verify_ex(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
+                                  _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(lenience), B, G,
+                                  V, _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
+                                  _ptr(workspace), wsb, _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify")
 
@@ -173,9 +207,9 @@ class Verifier:
         self.pq = torch.empty((B, gamma_max, 2), dtype=torch.float32, device=dev) if with_pq else None
 
     def __call__(self, p_logits, q_logits, draft_tokens, uniforms, temperature, top_k=None, top_p=None,
-                 gamma_len=None, stream=None):
+                 gamma_len=None, stream=None, lenience=None):
         spec_verify(p_logits, q_logits, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p,
-                    self.tokens, self.n_accepted, self.alpha, self.pq, self.workspace, stream)
+                    self.tokens, self.n_accepted, self.alpha, self.pq, self.workspace, stream, lenience)
         return self.tokens, self.n_accepted, self.alpha, self.pq
 
 
@@ -223,3 +257,88 @@ class GumbelVerifier:
         spec_verify_gumbel(p_logits, noise, draft_tokens, gamma_len, temperature, top_k, top_p, self.tokens,
                            self.n_accepted, self.target, stream)
         return self.tokens, self.n_accepted, self.target
+
+
+def spec_sample_workspace_bytes(R: int, V: int, dtype: int) -> int:
+    return int(lib().spec_sample_workspace_bytes(R, V, dtype))
+
+
+class Sampler:
+    """One token per row from the processed distribution, by inverse CDF at a
+    uniform (spec_sample); owns the workspace and the output for one shape."""
+
+    def __init__(self, R: int, V: int, dtype: int = SV_BF16, device="cuda"):
+        self.R, self.V, self.dtype = R, V, dtype
+        dev = torch.device(device)
+        nbytes = spec_sample_workspace_bytes(R, V, dtype)
+        if nbytes == 0:
+            raise ValueError("unsupported sizes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        rc = lib().spec_sample_workspace_init(_ptr(self.workspace), nbytes, R, V, dtype,
+                                              _stream_handle(None))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_sample_workspace_init")
+        self.tokens = torch.empty((R,), dtype=torch.int32, device=dev)
+
+    def __call__(self, logits, uniforms, temperature, top_k=None, top_p=None, stream=None):
+        if logits.dim() != 2:
+            raise ValueError("logits must be [R, V]")
+        R, V = logits.shape
+        dev = logits.device
+        dt = _dtype_code(logits)
+        _check(logits, "logits", logits.dtype, (self.R, self.V), dev)
+        _check(uniforms, "uniforms", torch.float32, (R,), dev)
+        _check(temperature, "temperature", torch.float32, (R,), dev)
+        _check(top_k, "top_k", torch.int32, (R,), dev)
+        _check(top_p, "top_p", torch.float32, (R,), dev)
+        rc = lib().spec_sample(_ptr(logits), dt, _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), R, V,
+                               _ptr(self.tokens), _ptr(self.workspace),
+                               self.workspace.numel() * self.workspace.element_size(), _stream_handle(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_sample")
+        return self.tokens
+
+
+def spec_sample_gumbel(logits: torch.Tensor, noise: torch.Tensor, temperature: torch.Tensor,
+                       top_k: Optional[torch.Tensor] = None, top_p: Optional[torch.Tensor] = None,
+                       out_tokens: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The shared-noise drafter's sample per row (spec_sample_gumbel)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = logits.shape
+    dev = logits.device
+    dt = _dtype_code(logits)
+    _check(noise, "noise", torch.float32, (R, V), dev)
+    _check(temperature, "temperature", torch.float32, (R,), dev)
+    _check(top_k, "top_k", torch.int32, (R,), dev)
+    _check(top_p, "top_p", torch.float32, (R,), dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((R,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", torch.int32, (R,), dev)
+    rc = lib().spec_sample_gumbel(_ptr(logits), dt, _ptr(noise), _ptr(temperature), _ptr(top_k), _ptr(top_p), R, V,
+                                  _ptr(out_tokens), _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_sample_gumbel")
+    return out_tokens
+
+
+# Throughput analytics (host functions of the library).
+def spec_verify_expected_tokens(alpha: float, gamma: int) -> float:
+    return float(lib().spec_verify_expected_tokens(alpha, gamma))
+
+
+def spec_verify_speedup(alpha: float, gamma: int, c: float) -> float:
+    return float(lib().spec_verify_speedup(alpha, gamma, c))
+
+
+def spec_verify_operations(alpha: float, gamma: int, c_hat: float) -> float:
+    return float(lib().spec_verify_operations(alpha, gamma, c_hat))
+
+
+def spec_verify_optimal_gamma(alpha: float, c: float, gamma_max: int) -> int:
+    return int(lib().spec_verify_optimal_gamma(alpha, c, gamma_max))
+
+
+def spec_verify_acceptance_length(alphas) -> float:
+    arr = (ctypes.c_double * len(alphas))(*[float(a) for a in alphas])
+    return float(lib().spec_verify_acceptance_length(arr, len(alphas)))

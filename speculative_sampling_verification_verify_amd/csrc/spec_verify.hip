@@ -197,23 +197,21 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
   return stage_mark(SV_KERNEL_FINISH, false, st);
 }
 
-}  // namespace sv
-
-using namespace sv;
-
-extern "C" size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype) {
-  if (!sizes_ok(B, gamma_max, V) || (dtype != SV_BF16 && dtype != SV_FP32)) return 0;
+// Workspace size and preparation for B sequences of G drafts (G == 0: rows
+// to sample).
+static size_t ws_bytes(int B, int G, int V, int dtype) {
+  if (B < 0 || G < 0 || G > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
+  if (dtype != SV_BF16 && dtype != SV_FP32) return 0;
   if (B == 0) return 256;
-  return layout(B, gamma_max, plan(B, gamma_max, V, dtype)).total;
+  return layout(B, G, plan(B, G, V, dtype)).total;
 }
 
-extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
-                                          int dtype, void* stream) {
-  const size_t need = spec_verify_workspace_bytes(B, gamma_max, V, dtype);
+static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V, int dtype, void* stream) {
+  const size_t need = ws_bytes(B, G, V, dtype);
   if (need == 0) return SV_ERR_ARG;
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
   if (B == 0) return SV_OK;
-  const Layout L = layout(B, gamma_max, plan(B, gamma_max, V, dtype));
+  const Layout L = layout(B, G, plan(B, G, V, dtype));
   const size_t n = L.counters_bytes / 4;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
                      (hipStream_t)stream, (uint32_t*)workspace, n);
@@ -225,21 +223,19 @@ extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_byte
   return SV_OK;
 }
 
-extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
-                           const int32_t* gamma_len, const float* uniforms, const float* temperature,
-                           const int32_t* top_k, const float* top_p, int B, int gamma_max, int V,
-                           int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
-  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
-  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
-  if (B == 0) return SV_OK;
-  if (!p_logits || !q_logits || !draft_tokens || !uniforms || !temperature || !out_tokens || !out_n_accepted ||
-      !out_alpha)
-    return SV_ERR_ARG;
+// The verify launch sequence.  sampler == 1: G == 0, every "sequence" is one
+// row drawn from its processed distribution at u[b] (the bonus draw), with no
+// drafts, no draft logits and no n output.
+static int run_verify(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
+                      const int32_t* gamma_len, const float* uniforms, const float* temperature,
+                      const int32_t* top_k, const float* top_p, const float* lenience, int B, int gamma_max, int V,
+                      int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                      void* workspace, size_t workspace_bytes, void* stream, int sampler) {
+  if (!p_logits || !uniforms || !temperature || !out_tokens) return SV_ERR_ARG;
+  if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
-  if (((uintptr_t)p_logits % es) || ((uintptr_t)q_logits % es)) return SV_ERR_ARG;
-  const size_t need = spec_verify_workspace_bytes(B, gamma_max, V, dtype);
+  if (((uintptr_t)p_logits % es) || (q_logits && ((uintptr_t)q_logits % es))) return SV_ERR_ARG;
+  const size_t need = ws_bytes(B, gamma_max, V, dtype);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256)) return SV_ERR_WORKSPACE;
   const Plan pl = plan(B, gamma_max, V, dtype);
   const long long rows = (long long)B * (2 * gamma_max + 1);
@@ -249,20 +245,24 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   const long long grid = sel_grid + list_grid;
   if (grid > 0x7FFFFFFFLL || units > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
   const int vec = dtype == SV_BF16 ? 8 : 4;
-  const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)q_logits % 16 == 0);
+  const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) &&
+                         (!q_logits || (uintptr_t)q_logits % 16 == 0);
   int vb = 0;
   while ((1LL << vb) < (long long)V + 1) ++vb;
   const Layout Lw = layout(B, gamma_max, pl);
   char* ws = (char*)workspace;
   Args a;
+  memset(&a, 0, sizeof a);
   a.p = p_logits;
   a.q = q_logits;
   a.draft = draft_tokens;
-  a.gamma_len = gamma_len;
+  a.gamma_len = sampler ? nullptr : gamma_len;
   a.u = uniforms;
   a.temp = temperature;
   a.topk = top_k;
   a.topp = top_p;
+  a.lenience = lenience;
+  a.sampler = sampler;
   a.B = B;
   a.G = gamma_max;
   a.V = V;
@@ -299,6 +299,65 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
   return SV_OK;
 }
 
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype) {
+  if (!sizes_ok(B, gamma_max, V)) return 0;
+  return ws_bytes(B, gamma_max, V, dtype);
+}
+
+extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
+                                          int dtype, void* stream) {
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  return ws_init(workspace, workspace_bytes, B, gamma_max, V, dtype, stream);
+}
+
+extern "C" int spec_verify_ex(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
+                              const int32_t* gamma_len, const float* uniforms, const float* temperature,
+                              const int32_t* top_k, const float* top_p, const float* lenience, int B, int gamma_max,
+                              int V, int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  return run_verify(p_logits, q_logits, dtype, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p, lenience,
+                    B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, workspace, workspace_bytes,
+                    stream, 0);
+}
+
+extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
+                           const int32_t* gamma_len, const float* uniforms, const float* temperature,
+                           const int32_t* top_k, const float* top_p, int B, int gamma_max, int V,
+                           int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return spec_verify_ex(p_logits, q_logits, dtype, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p,
+                        nullptr, B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, workspace,
+                        workspace_bytes, stream);
+}
+
+extern "C" size_t spec_sample_workspace_bytes(int R, int V, int dtype) { return ws_bytes(R, 0, V, dtype); }
+
+extern "C" int spec_sample_workspace_init(void* workspace, size_t workspace_bytes, int R, int V, int dtype,
+                                          void* stream) {
+  return ws_init(workspace, workspace_bytes, R, 0, V, dtype, stream);
+}
+
+extern "C" int spec_sample(const void* logits, int dtype, const float* uniforms, const float* temperature,
+                           const int32_t* top_k, const float* top_p, int R, int V, int32_t* out_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (R < 0 || V < 1) return SV_ERR_ARG;
+  if (R == 0) return SV_OK;
+  return run_verify(logits, nullptr, dtype, nullptr, nullptr, uniforms, temperature, top_k, top_p, nullptr, R, 0, V,
+                    out_tokens, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
+}
+
+namespace sv {
+
 template <typename ET, bool VECTOR>
 static hipError_t launch_gumbel(const Args& a, hipStream_t st) {
   hipError_t e;
@@ -312,16 +371,15 @@ static hipError_t launch_gumbel(const Args& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
-                                  const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
-                                  const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
-                                  int32_t* out_n_accepted, int32_t* out_target, void* stream) {
-  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
-  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
-  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
-  if (B == 0) return SV_OK;
-  if (!p_logits || !noise || !draft_tokens || !temperature || !out_tokens || !out_n_accepted || !out_target)
-    return SV_ERR_ARG;
+// The shared-noise launch sequence.  sampler == 1: G == 0, each "sequence"
+// is one row whose Gumbel-max sample is written to out_tokens (which is also
+// the per-row scratch), no drafts, no n output.
+static int run_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
+                      const int32_t* gamma_len, const float* temperature, const int32_t* top_k, const float* top_p,
+                      int B, int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_target,
+                      void* stream, int sampler) {
+  if (!p_logits || !noise || !temperature || !out_tokens || !out_target) return SV_ERR_ARG;
+  if (!sampler && (!draft_tokens || !out_n_accepted)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)p_logits % es) || ((uintptr_t)noise % 4)) return SV_ERR_ARG;
   if ((long long)B * (gamma_max + 1) > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
@@ -333,7 +391,8 @@ extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* 
   memset(&a, 0, sizeof a);
   a.p = p_logits;
   a.draft = draft_tokens;
-  a.gamma_len = gamma_len;
+  a.gamma_len = sampler ? nullptr : gamma_len;
+  a.sampler = sampler;
   a.temp = temperature;
   a.topk = top_k;
   a.topp = top_p;
@@ -356,6 +415,33 @@ extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* 
   return SV_OK;
 }
 
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
+                                  const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
+                                  const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
+                                  int32_t* out_n_accepted, int32_t* out_target, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  return run_gumbel(p_logits, dtype, noise, draft_tokens, gamma_len, temperature, top_k, top_p, B, gamma_max, V,
+                    out_tokens, out_n_accepted, out_target, stream, 0);
+}
+
+extern "C" int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const float* temperature,
+                                  const int32_t* top_k, const float* top_p, int R, int V, int32_t* out_tokens,
+                                  void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (R < 0 || V < 1) return SV_ERR_ARG;
+  if (R == 0) return SV_OK;
+  return run_gumbel(logits, dtype, noise, nullptr, nullptr, temperature, top_k, top_p, R, 0, V, out_tokens, nullptr,
+                    out_tokens, stream, 1);
+}
+
 extern "C" const char* spec_verify_strerror(int code) {
   switch (code) {
     case SV_OK: return "ok";
@@ -367,7 +453,7 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 3; }
+extern "C" int spec_verify_version(void) { return 4; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel != SV_KERNEL_SELECT && kernel != SV_KERNEL_PAIR && kernel != SV_KERNEL_FINISH && kernel != SV_KERNEL_GUMBEL)
@@ -376,4 +462,48 @@ extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) 
   g_stage_begin = (hipEvent_t)begin;
   g_stage_end = (hipEvent_t)end;
   return SV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Throughput analytics (host code; no GPU).
+// ---------------------------------------------------------------------------
+extern "C" double spec_verify_expected_tokens(double alpha, int gamma) {
+  if (!(alpha >= 0.0 && alpha <= 1.0) || gamma < 0) return NAN;
+  if (alpha == 1.0) return (double)(gamma + 1);
+  return (1.0 - pow(alpha, gamma + 1)) / (1.0 - alpha);
+}
+
+extern "C" double spec_verify_speedup(double alpha, int gamma, double c) {
+  if (!(c >= 0.0)) return NAN;
+  return spec_verify_expected_tokens(alpha, gamma) / ((double)gamma * c + 1.0);
+}
+
+extern "C" double spec_verify_operations(double alpha, int gamma, double c_hat) {
+  if (!(c_hat >= 0.0)) return NAN;
+  return ((double)gamma * c_hat + gamma + 1.0) / spec_verify_expected_tokens(alpha, gamma);
+}
+
+extern "C" int spec_verify_optimal_gamma(double alpha, double c, int gamma_max) {
+  if (!(alpha >= 0.0 && alpha <= 1.0) || !(c >= 0.0) || gamma_max < 1) return -1;
+  int best = 1;
+  double best_s = -1.0;
+  for (int g = 1; g <= gamma_max; ++g) {
+    const double sp = spec_verify_speedup(alpha, g, c);
+    if (sp > best_s) {
+      best_s = sp;
+      best = g;
+    }
+  }
+  return best;
+}
+
+extern "C" double spec_verify_acceptance_length(const double* alpha, int gamma) {
+  if (gamma < 0 || (gamma > 0 && !alpha)) return NAN;
+  double tau = 1.0, run = 1.0;
+  for (int k = 0; k < gamma; ++k) {
+    if (!(alpha[k] >= 0.0 && alpha[k] <= 1.0)) return NAN;
+    run *= alpha[k];
+    tau += run;
+  }
+  return tau;
 }

@@ -48,6 +48,8 @@ struct Args {
   int32_t* dense_list;    // [B * (G+1)] pair ids b * (G+1) + i of the dense sequences, in any order
   long long sel_blocks;   // workgroups of the select kernel that stream rows; the rest list dense pairs
   int pair;               // 1 when the pair-resident kernel runs for the dense sequences
+  const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test
+  int sampler;            // 1: G == 0 and each "sequence" is one row to sample (no drafts)
   const float* noise;     // shared-noise verify: [B][G+1][V] Gumbel noise
   int32_t* out_target;    // shared-noise verify: [B][G+1] the target's sample per position
 };

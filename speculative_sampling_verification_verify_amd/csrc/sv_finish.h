@@ -688,8 +688,10 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   const int lane = threadIdx.x & 63;
   bool ok = m.mode != MODE_INVALID && !(fl & F_BAD);
   const int gl = a.gamma_len ? a.gamma_len[b] : G;
-  ok = ok && gl >= 1 && gl <= G;
+  ok = ok && (a.sampler || (gl >= 1 && gl <= G));
   ok = ok && !(m.tp != m.tp);
+  const float lv = a.lenience ? a.lenience[b] : 1.0f;
+  ok = ok && lv >= 0.0f && lv <= 1.0f;
   const float* ub = a.u + (size_t)b * (G + 1);
   const int32_t* xb = a.draft + (size_t)b * G;
   bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG;
@@ -778,7 +780,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     if (threadIdx.x < 64) {
       const int i = threadIdx.x;
       bool rej = false;
-      if (i < m.g) rej = !((double)ub[i] * s.pos_q[i] < s.pos_p[i]);
+      if (i < m.g) rej = !((double)ub[i] * (double)lv * s.pos_q[i] < s.pos_p[i]);
       const unsigned long long mask = __ballot(rej);
       const int nn = mask ? __ffsll((long long)mask) - 1 : m.g;
       if (i == 0) {
@@ -805,7 +807,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     }
   }
   if (threadIdx.x == 0) {
-    a.out_n[b] = ok ? n : -1;
+    if (a.out_n) a.out_n[b] = ok ? n : -1;
     a.seq_flags[b] = 0;
     if (b == 0) *a.dense_count = 0;   // the pair kernel has finished with the list
   }

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
   const int g = min(max(gl, 1), G);
   int32_t* tgt = a.out_target + (size_t)b * G1;
   const int32_t* xb = a.draft + (size_t)b * G;
-  uint32_t badl = (gl >= 1 && gl <= G && Tv >= 0.0f && tp == tp) ? 0u : 1u;
+  uint32_t badl = ((a.sampler || (gl >= 1 && gl <= G)) && Tv >= 0.0f && tp == tp) ? 0u : 1u;
   for (int jj = lane; jj <= g; jj += 64) badl |= tgt[jj] < 0 ? 1u : 0u;
   bool mism = false;
   if (lane < g) {
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
     ot[jj] = ok ? (jj < n ? xb[jj] : (jj == n ? tok : -1)) : -1;
     if (!ok || jj > g) tgt[jj] = -1;
   }
-  if (lane == 0) a.out_n[b] = ok ? n : -1;
+  if (lane == 0 && a.out_n) a.out_n[b] = ok ? n : -1;
 }
 
 }  // namespace sv

@@ -23,7 +23,7 @@ def _ensure_built():
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(spec_verify\w*)\s*\(", txt, flags=re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(spec_\w*)\s*\(", txt, flags=re.M)))
 
 
 def test_header_declares_entry_points():
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 3
+    assert binding.spec_verify_version() == 4
 
 
 def test_workspace_bytes():
@@ -105,6 +105,48 @@ def test_gumbel_host_argument_errors():
     assert call(noise=ctypes.c_void_p(0x100002)) == binding.SV_ERR_ARG      # misaligned float noise
     assert call(p=ctypes.c_void_p(0x100001)) == binding.SV_ERR_ARG          # misaligned bf16
     assert call(B=0) == binding.SV_OK
+
+
+def test_sample_and_lenient_host_argument_errors():
+    L = _ensure_built()
+    fake = ctypes.c_void_p(0x100000)
+    nul = None
+    R, V = 4, 64
+    need = binding.spec_sample_workspace_bytes(R, V, binding.SV_BF16)
+    assert need > 0 and binding.spec_sample_workspace_bytes(R, 0, binding.SV_BF16) == 0
+    assert binding.spec_sample_workspace_bytes(-1, V, binding.SV_BF16) == 0
+
+    def sample(p=fake, dt=binding.SV_BF16, u=fake, temp=fake, R=R, V=V, out=fake, ws=fake, wsb=need):
+        return L.spec_sample(p, dt, u, temp, nul, nul, R, V, out, ws, wsb, nul)
+
+    assert sample(dt=9) == binding.SV_ERR_UNSUPPORTED
+    assert sample(V=(1 << 20) + 1) == binding.SV_ERR_UNSUPPORTED
+    assert sample(R=-1) == binding.SV_ERR_ARG
+    assert sample(V=0) == binding.SV_ERR_ARG
+    assert sample(p=nul) == binding.SV_ERR_ARG
+    assert sample(u=nul) == binding.SV_ERR_ARG
+    assert sample(temp=nul) == binding.SV_ERR_ARG
+    assert sample(out=nul) == binding.SV_ERR_ARG
+    assert sample(ws=nul) == binding.SV_ERR_WORKSPACE
+    assert sample(wsb=need - 1) == binding.SV_ERR_WORKSPACE
+    assert sample(R=0) == binding.SV_OK
+    assert L.spec_sample_workspace_init(nul, 0, R, V, binding.SV_BF16, nul) == binding.SV_ERR_WORKSPACE
+
+    def gsample(p=fake, noise=fake, temp=fake, R=R, V=V, out=fake):
+        return L.spec_sample_gumbel(p, binding.SV_BF16, noise, temp, nul, nul, R, V, out, nul)
+
+    assert gsample(noise=nul) == binding.SV_ERR_ARG
+    assert gsample(out=nul) == binding.SV_ERR_ARG
+    assert gsample(R=-2) == binding.SV_ERR_ARG
+    assert gsample(R=0) == binding.SV_OK
+
+    B, G = 2, 3
+    wneed = binding.spec_verify_workspace_bytes(B, G, V, binding.SV_BF16)
+    ex = lambda q=fake, draft=fake, G=G: L.spec_verify_ex(fake, q, binding.SV_BF16, draft, nul, fake, fake, nul, nul,
+                                                          nul, B, G, V, fake, fake, fake, nul, fake, wneed, nul)
+    assert ex(q=nul) == binding.SV_ERR_ARG
+    assert ex(draft=nul) == binding.SV_ERR_ARG
+    assert ex(G=0) == binding.SV_ERR_ARG
 
 
 def test_stage_events_kernel_selector():

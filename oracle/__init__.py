@@ -8,3 +8,4 @@ from .verify import (decode_row, process, inverse_cdf, verify_sequence,  # noqa:
                      gumbel_verify_batch, GumbelResult, GumbelBatchResult, sample_row, sample_batch,
                      SampleBatchResult)
 from . import analytics  # noqa: F401
+from . import kseq  # noqa: F401

@@ -213,6 +213,113 @@ def main_gumbel(args):
     print(json.dumps(out))
 
 
+def _spectr_rows(args):
+    import oracle
+    (p, q, cand, u, T, k, tp), rows = args
+    oracle.kseq.spectr_batch(p, q, cand, u, T, k, tp, rows=rows)
+    return len(rows)
+
+
+def main_spectr(args):
+    """Multi-candidate verify (K-SEQ / SpecTr) at K = 8 candidates of L = 8
+    tokens (the configuration the SpecTr page reports), B = 32 sequences,
+    V = 32000 bf16, T = 0.8."""
+    import multiprocessing as mp
+    t_gen = time.perf_counter()
+    sb = synth.make_spectr_batch(32, 8, 8, 32000, dtype="bf16", temperature=0.8)
+    t_gen = time.perf_counter() - t_gen
+    es = sb.p_logits.itemsize
+    # Algorithmic bytes: each distinct prefix node reads its target and draft rows once.
+    nodes = 0
+    for b in range(sb.B):
+        for j in range(sb.L + 1):
+            nodes += len({tuple(sb.cand[b, c, :j]) for c in range(sb.K)}) * (2 if j < sb.L else 1)
+    kbytes = nodes * sb.V * es
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        try:
+            cores = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            cores = min(16, os.cpu_count() or 1)
+        data = (sb.p_logits, sb.q_logits, sb.cand, sb.u, sb.temperature, sb.top_k, sb.top_p)
+        t0 = time.perf_counter()
+        oracle.kseq.spectr_batch(*data, rows=[0])
+        per_seq = max(time.perf_counter() - t0, 1e-4)
+        n = int(min(sb.B, max(cores, args.cpu_seconds / per_seq)))
+        chunks = [list(range(i, n, cores)) for i in range(cores) if i < n]
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(len(chunks)) as pool:
+            pool.map(_spectr_rows, [(data, c) for c in chunks])
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
+               "sample": f"{n} sequences of the same workload (K-SEQ / SpecTr oracle, {len(chunks)} worker "
+                         f"processes, {dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+    dev = torch.device("cuda:0")
+    P = torch.from_numpy(sb.p_logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    Q = torch.from_numpy(sb.q_logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    cand, u, temp, topk, topp = t(sb.cand), t(sb.u), t(sb.temperature), t(sb.top_k), t(sb.top_p)
+    ver = binding.SpectrVerifier(sb.B, sb.K, sb.L, device=dev)
+    logit_bytes = sb.p_logits.nbytes + sb.q_logits.nbytes
+    nsets = int(min(32, max(1, -(-ROTATE_BYTES // logit_bytes))))
+    sets = [(P, Q)] + [(P.clone(), Q.clone()) for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+
+    def step(j):
+        Pj, Qj = sets[j % nsets]
+        ver(Pj, Qj, cand, u, temp, topk, topp)
+
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j, (a, b) in enumerate(evs):
+        binding.spec_verify_set_stage_events(a, b, binding.SV_KERNEL_KSEQ)
+        step(j)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    binding.spec_verify_set_stage_events(None, None)
+    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / K
+    n_out = ver.n.cpu().numpy()
+    k_avg = float(k_ms.mean())
+    achieved = kbytes / (k_avg * 1e-3) / 1e9
+    out = {
+        "metric": "multi-candidate (K-SEQ / SpecTr) verify rows/sec + achieved HBM GB/s vs peak",
+        "value": sb.B / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": sb.name, "B": sb.B, "K": sb.K, "L": sb.L, "V": sb.V, "temperature": 0.8,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile("kseq_node_kernel", sb.name),
+                     "kernel": "kseq_node_kernel", "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,
+                     "kernel_p10_us": float(np.percentile(k_ms, 10) * 1e3),
+                     "kernel_p90_us": float(np.percentile(k_ms, 90) * 1e3)},
+        "cpu_baseline": cpu,
+        "extra": {"mean_tokens_per_round": float((n_out[n_out >= 0] + 1).mean()), "distinct_nodes_rows": nodes,
+                  "input_sets_rotated": nsets, "input_generation_s": t_gen},
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +330,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--gumbel", action="store_true",
                     help="the shared-noise (Gumbel coupling) verify on the workload's shapes instead")
+    ap.add_argument("--spectr", action="store_true",
+                    help="the multi-candidate (K-SEQ / SpecTr) verify at K = 8, L = 8 instead")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -245,6 +354,9 @@ def main():
 
     if args.gumbel:
         main_gumbel(args)
+        return
+    if args.spectr:
+        main_spectr(args)
         return
 
     t_gen = time.perf_counter()

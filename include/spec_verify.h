@@ -68,6 +68,7 @@ enum {
 /* Limits (checked synchronously). */
 #define SV_MAX_GAMMA 64      /* gamma_max <= 64: one wavefront ballot spans all drafts */
 #define SV_MAX_VOCAB 1048576 /* V <= 2^20                                            */
+#define SV_MAX_CANDIDATES 64 /* K <= 64 candidate sequences (multi-candidate verify)  */
 
 /*
  * Bytes of device workspace that spec_verify needs for these sizes
@@ -217,13 +218,56 @@ int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, cons
                        const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
                        int32_t* out_n_accepted, int32_t* out_target, void* stream);
 
+/*
+ * Multi-candidate verify: K-SEQ at each depth and the SpecTr walk ("SpecTr:
+ * Fast Speculative Decoding via Optimal Transport", mtandhj.com, sections
+ * "K-SEQ", "Residual distribution", "SpecTr"; that page calls the draft p and
+ * the target q, here p is the target and q the draft).  K candidate sequences
+ * of length L were drawn from the drafter (repeats allowed).  At depth j the
+ * candidates are the j-th tokens of the sequences that agree with the output
+ * so far, k of them; with a(x) = min(1, p(x) / (rho* q(x))), where rho* is the
+ * smallest rho in [1, k] with rho beta(rho) >= 1 - (1 - beta(rho))^k and
+ * beta(rho) = sum_x min(q(x), p(x) / rho), they are tested in order (accept
+ * iff u < a); if all are rejected the output is drawn from the residual
+ * max(0, p(x) - (P_A / beta) min(q(x), p(x) / rho*)), P_A = 1 - (1 - beta)^k, by
+ * the inverse CDF over ascending id (p itself when beta = 0).  The output
+ * follows the target exactly.  The round continues while the output is one of
+ * the candidates and ends with a draw from the target after depth L.
+ *
+ *  p_logits     [B][K][L+1][V] target logits: row j of candidate c is the target
+ *               after c's first j tokens (rows of candidates with a common prefix
+ *               are read from the lowest-numbered one).
+ *  q_logits     [B][K][L][V] draft logits, same layout.
+ *  candidates   [B][K][L] int32 candidate tokens.
+ *  uniforms     [B][L+1][K+1] float in [0, 1): at depth j < L, u[j][i] tests the
+ *               i-th candidate (i < k) and u[j][k] drives the residual draw; u[L][0]
+ *               drives the draw after depth L.
+ *  temperature, top_k, top_p: [B] as for spec_verify (top_k / top_p may be NULL).
+ *  out_tokens   [B][L+1] int32: the outputs, out_tokens[b][0..n] valid, -1 after.
+ *  out_n        [B] int32: depths whose output was a candidate (0..L); -1 invalid.
+ *  out_node_tokens [B][K][L+1] int32: the output at the node of candidate c's
+ *               prefix of length j, for each class's lowest-numbered candidate (-1
+ *               elsewhere).  Also the call's scratch: no workspace.
+ * 1 <= K <= SV_MAX_CANDIDATES, 1 <= L <= SV_MAX_GAMMA.  Rows above 64 KB are read
+ * from global memory on each pass and may hold at most 65536 16-byte units.
+ * Invalid data (NaN / +inf or no finite logit on a visited node, a candidate
+ * outside [0, V), a uniform outside [0, 1), bad temperature or top_p) gives
+ * n = -1 and tokens -1.  Asynchronous on `stream`, allocates nothing.  Returns
+ * SV_OK or a negative code (nothing enqueued).
+ */
+int spec_verify_spectr(const void* p_logits, const void* q_logits, int dtype, const int32_t* candidates,
+                       const float* uniforms, const float* temperature, const int32_t* top_k,
+                       const float* top_p, int B, int K, int L, int V, int32_t* out_tokens,
+                       int32_t* out_n, int32_t* out_node_tokens, void* stream);
+
 /* Kernels of one call, for spec_verify_set_stage_events. */
 enum {
   SV_KERNEL_SELECT = 0,  /* streaming top-k / argmax select over the logit rows      */
   SV_KERNEL_PAIR = 1,    /* per-(sequence, position) pass over dense (unfiltered,   */
                          /* large top-k, top-p) sequences; launched when V allows   */
   SV_KERNEL_FINISH = 2,  /* per-sequence acceptance, first rejection and draw       */
-  SV_KERNEL_GUMBEL = 3   /* per-(sequence, position) pass of spec_verify_gumbel      */
+  SV_KERNEL_GUMBEL = 3,  /* per-(sequence, position) pass of spec_verify_gumbel      */
+  SV_KERNEL_KSEQ = 4     /* per-(sequence, prefix node) K-SEQ of spec_verify_spectr */
 };
 
 /*
@@ -261,7 +305,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 4. */
+/* ABI version: 5. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_BF16, SV_FP32 = 0, 1
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
-SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL = 0, 1, 2, 3
+SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL, SV_KERNEL_KSEQ = 0, 1, 2, 3, 4
+SV_MAX_CANDIDATES = 64
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 
@@ -26,7 +27,7 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_v
             "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events", "spec_verify_gumbel",
             "spec_sample_workspace_bytes", "spec_sample_workspace_init", "spec_sample", "spec_sample_gumbel",
             "spec_verify_expected_tokens", "spec_verify_speedup", "spec_verify_operations",
-            "spec_verify_optimal_gamma", "spec_verify_acceptance_length")
+            "spec_verify_optimal_gamma", "spec_verify_acceptance_length", "spec_verify_spectr")
 
 _lib = None
 
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.spec_sample.restype = i
         L.spec_sample_gumbel.argtypes = [vp, i, vp, vp, vp, vp, i, i, vp, vp]
         L.spec_sample_gumbel.restype = i
+        L.spec_verify_spectr.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp]
+        L.spec_verify_spectr.restype = i
         d = ctypes.c_double
         L.spec_verify_expected_tokens.argtypes = [d, i]
         L.spec_verify_expected_tokens.restype = d
@@ -342,3 +345,36 @@ def spec_verify_optimal_gamma(alpha: float, c: float, gamma_max: int) -> int:
 def spec_verify_acceptance_length(alphas) -> float:
     arr = (ctypes.c_double * len(alphas))(*[float(a) for a in alphas])
     return float(lib().spec_verify_acceptance_length(arr, len(alphas)))
+
+
+class SpectrVerifier:
+    """Output buffers for multi-candidate (K-SEQ / SpecTr) verify calls of one
+    shape (spec_verify_spectr)."""
+
+    def __init__(self, B: int, K: int, L: int, device="cuda"):
+        dev = torch.device(device)
+        self.B, self.K, self.L = B, K, L
+        self.tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+        self.n = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.node_tokens = torch.empty((B, K, L + 1), dtype=torch.int32, device=dev)
+
+    def __call__(self, p_logits, q_logits, candidates, uniforms, temperature, top_k=None, top_p=None, stream=None):
+        if p_logits.dim() != 4 or q_logits.dim() != 4:
+            raise ValueError("p_logits must be [B, K, L+1, V] and q_logits [B, K, L, V]")
+        B, K, L1, V = p_logits.shape
+        L = L1 - 1
+        dev = p_logits.device
+        dt = _dtype_code(p_logits)
+        _check(p_logits, "p_logits", p_logits.dtype, (self.B, self.K, self.L + 1, V), dev)
+        _check(q_logits, "q_logits", p_logits.dtype, (B, K, L, V), dev)
+        _check(candidates, "candidates", torch.int32, (B, K, L), dev)
+        _check(uniforms, "uniforms", torch.float32, (B, L + 1, K + 1), dev)
+        _check(temperature, "temperature", torch.float32, (B,), dev)
+        _check(top_k, "top_k", torch.int32, (B,), dev)
+        _check(top_p, "top_p", torch.float32, (B,), dev)
+        rc = lib().spec_verify_spectr(_ptr(p_logits), _ptr(q_logits), dt, _ptr(candidates), _ptr(uniforms),
+                                      _ptr(temperature), _ptr(top_k), _ptr(top_p), B, K, L, V, _ptr(self.tokens),
+                                      _ptr(self.n), _ptr(self.node_tokens), _stream_handle(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_verify_spectr")
+        return self.tokens, self.n

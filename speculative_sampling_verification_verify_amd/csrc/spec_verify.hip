@@ -32,6 +32,7 @@
 #include "sv_pair.h"
 #include "sv_finish.h"
 #include "sv_gumbel.h"
+#include "sv_kseq.h"
 
 #include <math.h>
 #include <stdio.h>
@@ -442,6 +443,88 @@ extern "C" int spec_sample_gumbel(const void* logits, int dtype, const float* no
                     out_tokens, stream, 1);
 }
 
+namespace sv {
+
+template <typename ET, bool VECTOR>
+static hipError_t launch_spectr(const Args& a, bool ldsr, size_t lds, hipStream_t st) {
+  hipError_t e;
+  const dim3 grid((unsigned)((long long)a.B * a.K * (a.L + 1)));
+  if ((e = stage_mark(SV_KERNEL_KSEQ, true, st)) != hipSuccess) return e;
+  if (ldsr) {
+    static int lds_set[64];
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= 64 || lds_set[dev] < (int)lds) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      if (dev >= 0 && dev < 64) lds_set[dev] = (int)lds;
+    }
+    hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>), grid, dim3(KSEQ_NT), lds, st, a);
+  } else {
+    hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, false>), grid, dim3(KSEQ_NT), 0, st, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = stage_mark(SV_KERNEL_KSEQ, false, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(spectr_walk_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv
+
+extern "C" int spec_verify_spectr(const void* p_logits, const void* q_logits, int dtype, const int32_t* candidates,
+                                  const float* uniforms, const float* temperature, const int32_t* top_k,
+                                  const float* top_p, int B, int K, int L, int V, int32_t* out_tokens,
+                                  int32_t* out_n, int32_t* out_node_tokens, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (K > SV_MAX_CANDIDATES || L > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (B < 0 || K < 1 || L < 1 || V < 1) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  if (!p_logits || !q_logits || !candidates || !uniforms || !temperature || !out_tokens || !out_n || !out_node_tokens)
+    return SV_ERR_ARG;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)p_logits % es) || ((uintptr_t)q_logits % es)) return SV_ERR_ARG;
+  if ((long long)B * K * (L + 1) > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
+  const int vec = dtype == SV_BF16 ? 8 : 4;
+  const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)q_logits % 16 == 0);
+  const size_t row = ((size_t)V * es + 15) / 16 * 16;
+  const bool ldsr = row <= (size_t)PAIR_LDS_ROW_MAX;
+  const size_t units = vector_ok ? (size_t)V * es / 16 : (size_t)V;
+  if (!ldsr && units > (size_t)KSEQ_NT * PAIR_MAXTILE) return SV_ERR_UNSUPPORTED;
+  int vb = 0;
+  while ((1LL << vb) < (long long)V + 1) ++vb;
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.p = p_logits;
+  a.q = q_logits;
+  a.cand = candidates;
+  a.u = uniforms;
+  a.temp = temperature;
+  a.topk = top_k;
+  a.topp = top_p;
+  a.B = B;
+  a.K = K;
+  a.L = L;
+  a.V = V;
+  a.fixbits = 62 - vb;
+  a.out_tokens = out_tokens;
+  a.out_n = out_n;
+  a.node_tok = out_node_tokens;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t lds = ldsr ? 2 * row : 0;
+  hipError_t e;
+  if (dtype == SV_BF16)
+    e = vector_ok ? launch_spectr<uint16_t, true>(a, ldsr, lds, st) : launch_spectr<uint16_t, false>(a, ldsr, lds, st);
+  else
+    e = vector_ok ? launch_spectr<float, true>(a, ldsr, lds, st) : launch_spectr<float, false>(a, ldsr, lds, st);
+  if (e != hipSuccess) {
+    snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(e));
+    return SV_ERR_HIP;
+  }
+  return SV_OK;
+}
+
 extern "C" const char* spec_verify_strerror(int code) {
   switch (code) {
     case SV_OK: return "ok";
@@ -453,11 +536,10 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 4; }
+extern "C" int spec_verify_version(void) { return 5; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
-  if (kernel != SV_KERNEL_SELECT && kernel != SV_KERNEL_PAIR && kernel != SV_KERNEL_FINISH && kernel != SV_KERNEL_GUMBEL)
-    return SV_ERR_ARG;
+  if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;
   g_stage_kernel = kernel;
   g_stage_begin = (hipEvent_t)begin;
   g_stage_end = (hipEvent_t)end;

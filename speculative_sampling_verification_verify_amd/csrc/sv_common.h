@@ -50,6 +50,9 @@ struct Args {
   int pair;               // 1 when the pair-resident kernel runs for the dense sequences
   const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test
   int sampler;            // 1: G == 0 and each "sequence" is one row to sample (no drafts)
+  int K, L;               // multi-candidate verify: candidate sequences and their length
+  const int32_t* cand;    // multi-candidate verify: [B][K][L] candidate tokens
+  int32_t* node_tok;      // multi-candidate verify: [B][K][L+1] output at each prefix node
   const float* noise;     // shared-noise verify: [B][G+1][V] Gumbel noise
   int32_t* out_target;    // shared-noise verify: [B][G+1] the target's sample per position
 };

@@ -1,0 +1,370 @@
+// Multi-candidate verify: K-SEQ at every node of the candidate tree, then
+// the SpecTr walk ("SpecTr: Fast Speculative Decoding via Optimal Transport",
+// mtandhj.com, sections "K-SEQ", "Residual distribution", "SpecTr").  That
+// page names the draft p and the target q; here p is the target and q the
+// draft:
+//   a_rho(x) = min(1, p(x) / (rho q(x))),  m_rho(x) = min(q(x), p(x) / rho),
+//   beta(rho) = sum_x m_rho(x),  P_A = 1 - (1 - beta)^k,
+//   rho* = the smallest rho in [1, k] with rho beta(rho) >= 1 - (1 - beta(rho))^k,
+//   residual weights max(0, p(x) - (P_A / beta) m_rho*(x)) (p itself when beta = 0
+//   or when they sum to zero).
+// The k candidates of a node are tested in order with u[0..k-1] (accept iff
+// u_i < a); if all are rejected the output is the inverse-CDF draw over
+// ascending id from the residual at u[k].
+//
+// kseq_node_kernel: one workgroup per (sequence, candidate c, depth j).  The
+// node of depth j holds the candidates whose first j tokens equal candidate
+// c's; only the lowest-numbered member of that class (the representative)
+// computes it.  Its rows are P[b][c][j] (target after that prefix) and
+// Q[b][c][j] (draft); depth L is the bonus node, a draw from P[b][c][L] at
+// u[L][0].  Rows of up to 64 KB are held in LDS, longer rows are read from
+// global memory on each pass.  rho* is found by bisection on block
+// reductions of beta(rho) (g(rho) is non-decreasing in rho).
+// spectr_walk_kernel: one thread per sequence follows the output through the
+// nodes: at depth j the node of the current class gives Y; the class shrinks
+// to the candidates whose j-th token is Y; the round ends at the first depth
+// whose output is no candidate, or with the bonus node after depth L.
+#pragma once
+
+#include "sv_pair.h"
+
+namespace sv {
+
+constexpr int KSEQ_NT = 1024;
+constexpr int KSEQ_MAXK = 64;
+constexpr int KSEQ_BISECT = 64;
+constexpr int32_t KSEQ_BAD = -2;
+
+// Inverse-CDF draw over ascending id from per-element weights w(idx, rawp,
+// rawq) >= 0 (block-wide).  Tiles of NTP units: one pass leaves per-(tile,
+// wavefront) sums, wavefront 0 finds the crossing tile, and only that tile is
+// read again.  Returns the token, or -1 when the weights sum to zero.
+template <typename ET, int NTP, bool VECTOR, class W>
+__device__ __forceinline__ int block_draw(const typename PT<ET, VECTOR>::U* P, const typename PT<ET, VECTOR>::U* Q,
+                                          int NU, double u, W wfn, PairSmem<NTP>& s) {
+  using T = PT<ET, VECTOR>;
+  using U = typename T::U;
+  constexpr int E = T::E;
+  constexpr int NW = NTP / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ntile = (NU + NTP - 1) / NTP;
+  auto unit_weights = [&](int ui, float* w) {
+    const U up = P[ui], uq = Q[ui];
+    uint32_t rq[E];
+    T::each(uq, [&](int e, uint32_t raw) { rq[e] = raw; });
+    T::each(up, [&](int e, uint32_t raw) { w[e] = wfn(ui * E + e, raw, rq[e]); });
+  };
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int ui = t * NTP + (int)threadIdx.x;
+    float r = 0.0f;
+    if (ui < NU) {
+      float w[E];
+      unit_weights(ui, w);
+#pragma unroll
+      for (int e = 0; e < E; ++e) r += w[e];
+    }
+    const double ws = wave_sum_dpp((double)r);
+    if (lane == 0) s.part[t][wave] = ws;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    double tt = 0.0;
+    if (lane < ntile) {
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) tt += s.part[lane][w2];
+    }
+    const double incl = wave_incl_scan_f64(tt);
+    const double Z = readlane_f64(incl, 63);
+    const double target = u * Z;
+    const unsigned long long hit = __ballot(lane < ntile && incl > target);
+    const int jt = hit ? __ffsll((long long)hit) - 1 : ntile - 1;
+    if (lane == jt) {
+      s.bc[0] = (uint32_t)jt;
+      s.bd[0] = incl - tt;
+    }
+    if (lane == 0) s.bd[1] = Z > 0.0 ? target : -1.0;
+  }
+  __syncthreads();
+  const int tj = (int)s.bc[0];
+  const double base = s.bd[0], target = s.bd[1];
+  __syncthreads();
+  if (!(target >= 0.0)) return -1;
+  uint32_t hitpos = 0xFFFFFFFFu, lastpos = 0;
+  {
+    const int ui = tj * NTP + (int)threadIdx.x;
+    float w[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[e] = 0.0f;
+    float r = 0.0f;
+    if (ui < NU) {
+      unit_weights(ui, w);
+#pragma unroll
+      for (int e = 0; e < E; ++e) r += w[e];
+    }
+    const double rd = (double)r;
+    const double incl = wave_incl_scan_f64(rd);
+    double cum = base;
+    for (int w2 = 0; w2 < wave; ++w2) cum += s.part[tj][w2];
+    cum += incl - rd;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      cum += (double)w[e];
+      const uint32_t idx = (uint32_t)(ui * E + e);
+      if (hitpos == 0xFFFFFFFFu && w[e] > 0.0f && cum > target) hitpos = idx;
+      if (w[e] > 0.0f) lastpos = idx + 1u;
+    }
+  }
+  hitpos = pb_min<NTP>(hitpos, s.red_u);
+  if (hitpos != 0xFFFFFFFFu) return (int)hitpos;
+  return (int)pb_max<NTP>(lastpos, s.red_u) - 1;   // rounding left no crossing
+}
+
+template <typename ET, int NTP, bool VECTOR, bool LDSR>
+__global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
+  using T = PT<ET, VECTOR>;
+  using U = typename T::U;
+  constexpr int E = T::E;
+  extern __shared__ __align__(16) unsigned char kseq_rows[];
+  __shared__ PairSmem<NTP> s;
+  __shared__ PairExtra<LDSR> ps;
+  __shared__ int32_t cands[KSEQ_MAXK];
+  __shared__ uint32_t kcount;
+  __shared__ int32_t result;
+  const int K = a.K, L = a.L, L1 = L + 1;
+  const int b = blockIdx.x / (K * L1);
+  const int rem = blockIdx.x - b * K * L1;
+  const int c = rem / L1, j = rem - (rem / L1) * L1;
+  int32_t* outp = a.node_tok + ((size_t)b * K + c) * L1 + j;
+  const int32_t* cb = a.cand + (size_t)b * K * L;
+  // The node's class: candidates whose first j tokens equal candidate c's.
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    bool same = false;
+    if (t < K) {
+      same = true;
+      for (int jj = 0; jj < j; ++jj) same = same && cb[t * L + jj] == cb[c * L + jj];
+    }
+    const unsigned long long m = __ballot(same);
+    const int rep = __ffsll((long long)m) - 1;
+    if (t == 0) kcount = rep == c ? (uint32_t)__popcll(m) : 0u;
+    if (same && j < L) cands[__popcll(m & ((1ull << t) - 1ull))] = cb[t * L + j];
+  }
+  __syncthreads();
+  const int k = (int)kcount;
+  if (k == 0) {   // another member of the class computes this node
+    if (threadIdx.x == 0) *outp = -1;
+    return;
+  }
+  const float Tv = a.temp[b];
+  const int kk = a.topk ? a.topk[b] : 0;
+  const float tp = a.topp ? a.topp[b] : 1.0f;
+  if (!(Tv >= 0.0f) || tp != tp) {
+    if (threadIdx.x == 0) *outp = KSEQ_BAD;
+    return;
+  }
+  const bool bonus = j == L;
+  const int V = a.V;
+  const int NU = VECTOR ? V / E : V;
+  const U* gp = reinterpret_cast<const U*>(reinterpret_cast<const ET*>(a.p) + (((size_t)b * K + c) * L1 + j) * (size_t)V);
+  const U* gq = bonus ? gp : reinterpret_cast<const U*>(reinterpret_cast<const ET*>(a.q) + (((size_t)b * K + c) * L + j) * (size_t)V);
+  const float* uj = a.u + ((size_t)b * L1 + j) * (K + 1);
+
+  // Pass 1: validity, maxima and (for T = 0) the lowest-id argmax of each
+  // row; rows of up to 64 KB are copied to LDS on the way.
+  const U* P;
+  const U* Q;
+  uint32_t bad = 0, kmp = 0, kmq = 0, ip = NONE, iq = NONE;
+  auto scan = [&](const U& u, int ui, uint32_t& km, uint32_t& im) {
+    T::each(u, [&](int e, uint32_t raw) {
+      const float z = T::val(raw);
+      bad |= z < INFINITY ? 0u : 1u;
+      const uint32_t kz = T::key(raw);
+      if (kz > km) {
+        km = kz;
+        im = (uint32_t)(ui * E + e);
+      }
+    });
+  };
+  if constexpr (LDSR) {
+    const int nup = (NU * (int)sizeof(U) + 15) / 16 * 16 / (int)sizeof(U);
+    U* lp = reinterpret_cast<U*>(kseq_rows);
+    U* lq = lp + nup;
+    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
+      const U up = gp[ui];
+      lp[ui] = up;
+      scan(up, ui, kmp, ip);
+      if (!bonus) {
+        const U uq = gq[ui];
+        lq[ui] = uq;
+        scan(uq, ui, kmq, iq);
+      }
+    }
+    P = lp;
+    Q = bonus ? lp : lq;
+  } else {
+    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
+      scan(gp[ui], ui, kmp, ip);
+      if (!bonus) scan(gq[ui], ui, kmq, iq);
+    }
+    P = gp;
+    Q = gq;
+  }
+  const uint32_t my_kmp = kmp, my_kmq = kmq;
+  pb_max3<NTP>(kmp, kmq, bad, s.red_u);   // its barriers also publish the LDS rows
+  if (bad || kmp <= Key<ET>::NEG_INF || (!bonus && kmq <= Key<ET>::NEG_INF)) {
+    if (threadIdx.x == 0) *outp = KSEQ_BAD;
+    return;
+  }
+  const uint32_t argp = pb_min<NTP>(my_kmp == kmp ? ip : NONE, s.red_u);
+  const uint32_t argq = bonus ? 0u : pb_min<NTP>(my_kmq == kmq ? iq : NONE, s.red_u);
+  const bool greedy = Tv == 0.0f;
+  Mode m;
+  m.g = 1;
+  m.mode = MODE_DENSE;
+  m.k = 0;
+  m.T = greedy ? 1.0f : Tv;
+  m.tp = tp;
+  RowStat sp{}, sq{};
+  if (!greedy) {
+    sp = row_stats<ET, NTP, VECTOR, LDSR>(P, NU, Key<ET>::value(kmp), a, m, kk, s, ps);
+    if (!bonus) sq = row_stats<ET, NTP, VECTOR, LDSR>(Q, NU, Key<ET>::value(kmq), a, m, kk, s, ps);
+  }
+  auto prob_p = [&](uint32_t idx, uint32_t raw) -> float {
+    return greedy ? (idx == argp ? 1.0f : 0.0f) : pprob(sp, T::val(raw));
+  };
+  auto prob_q = [&](uint32_t idx, uint32_t raw) -> float {
+    return greedy ? (idx == argq ? 1.0f : 0.0f) : pprob(sq, T::val(raw));
+  };
+
+  if (bonus) {
+    const int tok = block_draw<ET, NTP, VECTOR>(
+        P, Q, NU, (double)uj[0], [&](uint32_t idx, uint32_t rp, uint32_t) { return prob_p(idx, rp); }, s);
+    if (threadIdx.x == 0) *outp = tok;
+    return;
+  }
+
+  // beta(rho) = sum_x min(q(x), p(x) / rho), block-wide.
+  auto beta_of = [&](double rho) -> double {
+    const float inv = (float)(1.0 / rho);
+    double acc = 0.0;
+    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
+      const U up = P[ui], uq = Q[ui];
+      uint32_t rq[E];
+      T::each(uq, [&](int e, uint32_t raw) { rq[e] = raw; });
+      float part = 0.0f;
+      T::each(up, [&](int e, uint32_t raw) {
+        const uint32_t idx = (uint32_t)(ui * E + e);
+        part += fminf(prob_q(idx, rq[e]), prob_p(idx, raw) * inv);
+      });
+      acc += (double)part;
+    }
+    return pb_sum_f64<NTP>(acc, s.red_d);
+  };
+  auto gfun = [&](double rho, double& beta) {
+    beta = beta_of(rho);
+    return rho * beta - (1.0 - pow(1.0 - beta, (double)k));
+  };
+  double rho = 1.0, beta = 0.0;
+  if (k > 1 && gfun(1.0, beta) < 0.0) {
+    double lo = 1.0, hi = (double)k;
+    for (int it = 0; it < KSEQ_BISECT; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      double bm;
+      if (gfun(mid, bm) >= 0.0) hi = mid;
+      else lo = mid;
+    }
+    rho = hi;
+  }
+  beta = beta_of(rho);
+  const double pacc = 1.0 - pow(1.0 - beta, (double)k);
+
+  // The candidates in order.
+  if (threadIdx.x == 0) {
+    int y = -1;
+    for (int i = 0; i < k; ++i) {
+      const int x = cands[i];
+      if (x < 0 || x >= V) {
+        y = KSEQ_BAD;
+        break;
+      }
+      const double px = (double)prob_p((uint32_t)x, T::raw_at(P, x));
+      const double qx = (double)prob_q((uint32_t)x, T::raw_at(Q, x));
+      double acc;
+      if (qx == 0.0) acc = px > 0.0 ? 1.0 : 0.0;
+      else acc = qx * rho <= px ? 1.0 : px / (rho * qx);
+      if ((double)uj[i] < acc) {
+        y = x;
+        break;
+      }
+    }
+    result = y;
+  }
+  __syncthreads();
+  int tok = result;
+  if (tok == -1) {
+    const float scale = beta > 0.0 ? (float)(pacc / beta) : 0.0f;
+    const float inv = (float)(1.0 / rho);
+    tok = block_draw<ET, NTP, VECTOR>(
+        P, Q, NU, (double)uj[k],
+        [&](uint32_t idx, uint32_t rp, uint32_t rq) {
+          const float pv = prob_p(idx, rp);
+          if (!(beta > 0.0)) return pv;
+          return fmaxf(pv - scale * fminf(prob_q(idx, rq), pv * inv), 0.0f);
+        },
+        s);
+    if (tok < 0)   // residual weights summed to zero: draw from the target
+      tok = block_draw<ET, NTP, VECTOR>(
+          P, Q, NU, (double)uj[k], [&](uint32_t idx, uint32_t rp, uint32_t) { return prob_p(idx, rp); }, s);
+  }
+  if (threadIdx.x == 0) *outp = tok;
+}
+
+// One thread per sequence: the walk through the nodes.
+__global__ __launch_bounds__(256) void spectr_walk_kernel(Args a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.B) return;
+  const int K = a.K, L = a.L, L1 = L + 1, V = a.V;
+  const float Tv = a.temp[b];
+  const float tp = a.topp ? a.topp[b] : 1.0f;
+  bool ok = Tv >= 0.0f && tp == tp;
+  const int32_t* cb = a.cand + (size_t)b * K * L;
+  for (int i = 0; i < K * L && ok; ++i) ok = cb[i] >= 0 && cb[i] < V;
+  const float* ub = a.u + (size_t)b * L1 * (K + 1);
+  for (int i = 0; i < L1 * (K + 1) && ok; ++i) ok = ub[i] >= 0.0f && ub[i] < 1.0f;
+  const int32_t* nt = a.node_tok + (size_t)b * K * L1;
+  int32_t* ot = a.out_tokens + (size_t)b * L1;
+  unsigned long long alive = K >= 64 ? ~0ull : ((1ull << K) - 1ull);
+  int n = L;
+  for (int j = 0; j < L1; ++j) ot[j] = -1;
+  for (int j = 0; j < L && ok; ++j) {
+    const int rep = __ffsll((long long)alive) - 1;
+    const int y = nt[rep * L1 + j];
+    if (y < 0) {
+      ok = false;
+      break;
+    }
+    ot[j] = y;
+    unsigned long long next = 0ull;
+    for (int c = 0; c < K; ++c)
+      if (((alive >> c) & 1ull) && cb[c * L + j] == y) next |= 1ull << c;
+    if (!next) {
+      n = j;
+      break;
+    }
+    alive = next;
+  }
+  if (ok && n == L) {
+    const int rep = __ffsll((long long)alive) - 1;
+    const int y = nt[rep * L1 + L];
+    if (y < 0) ok = false;
+    else ot[L] = y;
+  }
+  if (!ok) {
+    for (int j = 0; j < L1; ++j) ot[j] = -1;
+    n = -1;
+  }
+  a.out_n[b] = n;
+}
+
+}  // namespace sv

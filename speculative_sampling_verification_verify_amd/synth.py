@@ -394,3 +394,96 @@ def make_gumbel_batch(cid: int, B: Optional[int] = None, V: Optional[int] = None
     w = dataclasses.replace(base.workload, name=base.workload.name + "-gumbel")
     return GumbelBatch(w, base.p_logits, noise, draft, base.gamma_len, base.temperature, base.top_k, base.top_p,
                        base.seed, base.q_logits)
+
+
+# ----------------------------------------------------------------------------
+# Multi-candidate (K-SEQ / SpecTr) inputs.
+# ----------------------------------------------------------------------------
+STREAM_SPECTR = 7
+
+
+@dataclasses.dataclass
+class SpectrBatch:
+    """Host copy of one multi-candidate verify call's inputs.
+
+    p_logits: [B, K, L+1, V] target logits; row j of candidate c is the target
+              after c's first j tokens (equal prefixes give identical rows)
+    q_logits: [B, K, L, V] draft logits, same layout
+    cand:     [B, K, L] int32 candidate tokens (K independent drafter samples)
+    u:        [B, L+1, K+1] float32 uniforms
+    temperature, top_k, top_p: [B]
+    """
+    name: str
+    p_logits: np.ndarray
+    q_logits: np.ndarray
+    cand: np.ndarray
+    u: np.ndarray
+    temperature: np.ndarray
+    top_k: np.ndarray
+    top_p: np.ndarray
+    seed: int
+
+    @property
+    def B(self):
+        return self.p_logits.shape[0]
+
+    @property
+    def K(self):
+        return self.p_logits.shape[1]
+
+    @property
+    def L(self):
+        return self.q_logits.shape[2]
+
+    @property
+    def V(self):
+        return self.p_logits.shape[3]
+
+
+def _prefix_rng(seed: int, b: int, prefix) -> np.random.Generator:
+    h = 1469598103934665603
+    for t in (b,) + tuple(int(x) for x in prefix) + (len(prefix),):
+        h = ((h ^ (t & 0xFFFFFFFFFFFF)) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return np.random.Generator(np.random.Philox(key=[seed, STREAM_SPECTR], counter=[0, h, 0, 0]))
+
+
+def make_spectr_batch(B: int, K: int, L: int, V: int, dtype: str = "bf16", seed: int = BASE_SEED + 10,
+                      scale: float = 3.0, slope: float = 1.1, sigma: float = 0.5, temperature=0.8, top_k=0,
+                      top_p=1.0) -> SpectrBatch:
+    """K candidate sequences per sequence, each drawn token by token from the
+    drafter's processed distribution after its own prefix (Gumbel-max over the
+    drafter's candidate set); target and draft rows are functions of the
+    prefix, so candidates with a common prefix share them."""
+    dt = np.uint16 if dtype == "bf16" else np.float32
+    P = np.empty((B, K, L + 1, V), dtype=dt)
+    Q = np.empty((B, K, L, V), dtype=dt)
+    cand = np.zeros((B, K, L), dtype=np.int32)
+    T = np.broadcast_to(np.asarray(temperature, np.float32), (B,)).copy()
+    kk = np.broadcast_to(np.asarray(top_k, np.int32), (B,)).copy()
+    tp = np.broadcast_to(np.asarray(top_p, np.float32), (B,)).copy()
+    for b in range(B):
+        perm = _rng(seed, STREAM_PERM, b).permutation(V)
+        zipf = (slope * np.log1p(perm.astype(np.float64))).astype(np.float32)
+        cache = {}
+
+        def rows(prefix):
+            key = tuple(prefix)
+            if key not in cache:
+                g = _prefix_rng(seed, b, key)
+                zp = np.float32(scale) * g.standard_normal(V, dtype=np.float32) - zipf
+                zq = zp + np.float32(sigma) * g.standard_normal(V, dtype=np.float32)
+                if dtype == "bf16":
+                    zp, zq = f32_to_bf16_bits(zp), f32_to_bf16_bits(zq)
+                cache[key] = (zp, zq)
+            return cache[key]
+        drng = _rng(seed, STREAM_DRAFT_SAMPLE, b)
+        for c in range(K):
+            for j in range(L + 1):
+                zp, zq = rows(cand[b, c, :j])
+                P[b, c, j] = zp
+                if j < L:
+                    Q[b, c, j] = zq
+                    zqv = bf16_bits_to_f32(zq).astype(np.float64) if dtype == "bf16" else zq.astype(np.float64)
+                    cand[b, c, j] = _drafter_sample(zqv, float(T[b]), int(kk[b]), float(tp[b]), drng)
+    u = np.random.default_rng([seed, STREAM_UNIFORM]).random((B, L + 1, K + 1)).astype(np.float32)
+    return SpectrBatch(f"spectr-B{B}-K{K}-L{L}-V{V}-{dtype}", P, Q, cand, u, T, kk, tp, seed)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 4
+    assert binding.spec_verify_version() == 5
 
 
 def test_workspace_bytes():
@@ -149,11 +149,36 @@ def test_sample_and_lenient_host_argument_errors():
     assert ex(G=0) == binding.SV_ERR_ARG
 
 
+def test_spectr_host_argument_errors():
+    L = _ensure_built()
+    fake = ctypes.c_void_p(0x100000)
+    nul = None
+
+    def call(p=fake, q=fake, dt=binding.SV_BF16, cand=fake, u=fake, temp=fake, B=2, K=4, Ln=3, V=64, out=fake):
+        return L.spec_verify_spectr(p, q, dt, cand, u, temp, nul, nul, B, K, Ln, V, out, out, out, nul)
+
+    assert call(dt=4) == binding.SV_ERR_UNSUPPORTED
+    assert call(K=65) == binding.SV_ERR_UNSUPPORTED
+    assert call(Ln=65) == binding.SV_ERR_UNSUPPORTED
+    assert call(V=(1 << 20) + 1) == binding.SV_ERR_UNSUPPORTED
+    assert call(K=0) == binding.SV_ERR_ARG
+    assert call(Ln=0) == binding.SV_ERR_ARG
+    assert call(V=0) == binding.SV_ERR_ARG
+    assert call(B=-1) == binding.SV_ERR_ARG
+    for kw in ("p", "q", "cand", "u", "temp", "out"):
+        assert call(**{kw: nul}) == binding.SV_ERR_ARG, kw
+    assert call(p=ctypes.c_void_p(0x100001)) == binding.SV_ERR_ARG
+    assert call(V=600001) == binding.SV_ERR_UNSUPPORTED     # odd V above 64 KB rows: beyond the streamed limit
+    assert call(B=0) == binding.SV_OK
+
+
 def test_stage_events_kernel_selector():
     L = _ensure_built()
     assert L.spec_verify_set_stage_events(7, None, None) == binding.SV_ERR_ARG
+    assert L.spec_verify_set_stage_events(5, None, None) == binding.SV_ERR_ARG
     assert L.spec_verify_set_stage_events(-1, None, None) == binding.SV_ERR_ARG
-    for k in (binding.SV_KERNEL_SELECT, binding.SV_KERNEL_PAIR, binding.SV_KERNEL_FINISH, binding.SV_KERNEL_GUMBEL):
+    for k in (binding.SV_KERNEL_SELECT, binding.SV_KERNEL_PAIR, binding.SV_KERNEL_FINISH, binding.SV_KERNEL_GUMBEL,
+              binding.SV_KERNEL_KSEQ):
         assert L.spec_verify_set_stage_events(k, None, None) == binding.SV_OK
 
 

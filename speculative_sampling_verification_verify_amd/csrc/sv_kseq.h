@@ -18,8 +18,8 @@
 // computes it.  Its rows are P[b][c][j] (target after that prefix) and
 // Q[b][c][j] (draft); depth L is the bonus node, a draw from P[b][c][L] at
 // u[L][0].  Rows of up to 64 KB are held in LDS, longer rows are read from
-// global memory on each pass.  rho* is found by bisection on block
-// reductions of beta(rho) (g(rho) is non-decreasing in rho).
+// global memory on each pass.  rho* is found by a multi-point bracket
+// search on block reductions of beta(rho) (g(rho) is non-decreasing in rho).
 // spectr_walk_kernel: one thread per sequence follows the output through the
 // nodes: at depth j the node of the current class gives Y; the class shrinks
 // to the candidates whose j-th token is Y; the round ends at the first depth
@@ -32,7 +32,8 @@ namespace sv {
 
 constexpr int KSEQ_NT = 1024;
 constexpr int KSEQ_MAXK = 64;
-constexpr int KSEQ_BISECT = 64;
+constexpr int KSEQ_NPT = 8;       // points of the rho* bracket evaluated per pass
+constexpr int KSEQ_PASSES = 24;   // bracket passes (each shrinks it (KSEQ_NPT + 1)-fold)
 constexpr int32_t KSEQ_BAD = -2;
 
 // Inverse-CDF draw over ascending id from per-element weights w(idx, rawp,
@@ -131,6 +132,9 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   __shared__ int32_t cands[KSEQ_MAXK];
   __shared__ uint32_t kcount;
   __shared__ int32_t result;
+  __shared__ double gred[NTP / 64][KSEQ_NPT];
+  __shared__ double rr[KSEQ_NPT], gg[KSEQ_NPT], bb[KSEQ_NPT];
+  __shared__ double brk[3];   // lo, hi, beta(hi)
   const int K = a.K, L = a.L, L1 = L + 1;
   const int b = blockIdx.x / (K * L1);
   const int rem = blockIdx.x - b * K * L1;
@@ -244,39 +248,90 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
     return;
   }
 
-  // beta(rho) = sum_x min(q(x), p(x) / rho), block-wide.
-  auto beta_of = [&](double rho) -> double {
-    const float inv = (float)(1.0 / rho);
-    double acc = 0.0;
+  // beta(rho) = sum_x min(q(x), p(x) / rho) and g(rho) = rho beta(rho) -
+  // (1 - (1 - beta(rho))^k) at the KSEQ_NPT values rr[] in one pass over the
+  // rows (per-thread float sums, block sums in double); results in gg[], bb[].
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  auto g_multi = [&]() {
+    float inv[KSEQ_NPT], acc[KSEQ_NPT];
+#pragma unroll
+    for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
+      inv[m2] = (float)(1.0 / rr[m2]);
+      acc[m2] = 0.0f;
+    }
     for (int ui = threadIdx.x; ui < NU; ui += NTP) {
       const U up = P[ui], uq = Q[ui];
       uint32_t rq[E];
       T::each(uq, [&](int e, uint32_t raw) { rq[e] = raw; });
-      float part = 0.0f;
       T::each(up, [&](int e, uint32_t raw) {
         const uint32_t idx = (uint32_t)(ui * E + e);
-        part += fminf(prob_q(idx, rq[e]), prob_p(idx, raw) * inv);
+        const float pv = prob_p(idx, raw), qv = prob_q(idx, rq[e]);
+#pragma unroll
+        for (int m2 = 0; m2 < KSEQ_NPT; ++m2) acc[m2] += fminf(qv, pv * inv[m2]);
       });
-      acc += (double)part;
     }
-    return pb_sum_f64<NTP>(acc, s.red_d);
-  };
-  auto gfun = [&](double rho, double& beta) {
-    beta = beta_of(rho);
-    return rho * beta - (1.0 - pow(1.0 - beta, (double)k));
-  };
-  double rho = 1.0, beta = 0.0;
-  if (k > 1 && gfun(1.0, beta) < 0.0) {
-    double lo = 1.0, hi = (double)k;
-    for (int it = 0; it < KSEQ_BISECT; ++it) {
-      const double mid = 0.5 * (lo + hi);
-      double bm;
-      if (gfun(mid, bm) >= 0.0) hi = mid;
-      else lo = mid;
+#pragma unroll
+    for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
+      const double w = wave_sum_dpp((double)acc[m2]);
+      if (lane == 0) gred[wave][m2] = w;
     }
-    rho = hi;
+    __syncthreads();
+    if (threadIdx.x < KSEQ_NPT) {
+      const int m2 = threadIdx.x;
+      double bsum = 0.0;
+      for (int w2 = 0; w2 < NTP / 64; ++w2) bsum += gred[w2][m2];
+      bb[m2] = bsum;
+      gg[m2] = rr[m2] * bsum - (1.0 - pow(1.0 - bsum, (double)k));
+    }
+    __syncthreads();
+  };
+  // rho*: the smallest root of the non-decreasing g on [1, k].  The first
+  // pass tries rho = 1 and spreads the other points up to k; later passes
+  // split the bracket (lo: g < 0, hi: g >= 0) into KSEQ_NPT + 1 parts.
+  if (threadIdx.x < KSEQ_NPT) rr[threadIdx.x] = 1.0 + ((double)k - 1.0) * threadIdx.x / (KSEQ_NPT - 1);
+  __syncthreads();
+  g_multi();
+  double rho = 1.0, beta = bb[0];
+  if (k > 1 && gg[0] < 0.0) {
+    if (threadIdx.x == 0) {
+      double lo = 1.0, hi = (double)k, bhi = bb[KSEQ_NPT - 1];
+      for (int m2 = 1; m2 < KSEQ_NPT; ++m2) {
+        if (gg[m2] >= 0.0) {
+          hi = rr[m2];
+          bhi = bb[m2];
+          break;
+        }
+        lo = rr[m2];
+      }
+      brk[0] = lo;
+      brk[1] = hi;
+      brk[2] = bhi;
+    }
+    __syncthreads();
+    for (int pass = 0; pass < KSEQ_PASSES; ++pass) {
+      const double lo = brk[0], hi = brk[1];
+      if (!(hi - lo > 1e-15 * hi)) break;          // uniform: every thread reads the same brk
+      __syncthreads();
+      if (threadIdx.x < KSEQ_NPT) rr[threadIdx.x] = lo + (hi - lo) * (threadIdx.x + 1) / (KSEQ_NPT + 1);
+      __syncthreads();
+      g_multi();
+      if (threadIdx.x == 0) {
+        double nlo = lo;
+        for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
+          if (gg[m2] >= 0.0) {
+            brk[1] = rr[m2];
+            brk[2] = bb[m2];
+            break;
+          }
+          nlo = rr[m2];
+        }
+        brk[0] = nlo;
+      }
+      __syncthreads();
+    }
+    rho = brk[1];
+    beta = brk[2];
   }
-  beta = beta_of(rho);
   const double pacc = 1.0 - pow(1.0 - beta, (double)k);
 
   // The candidates in order.

@@ -389,7 +389,12 @@ def main():
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     draft, u, temp, topk, topp, gl = (t(bt.draft), t(bt.u), t(bt.temperature), t(bt.top_k), t(bt.top_p),
                                       t(bt.gamma_len))
-    ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt_code, device=dev)
+    # The sampling settings are known on the host: when no sequence is dense
+    # (every one argmax or top-k <= 512) the call says so and the empty
+    # dense-pair launch is skipped.
+    sel_bytes, pair_bytes = kernel_bytes(bt)
+    hints = binding.SV_HINT_NO_DENSE if pair_bytes == 0 else 0
+    ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt_code, device=dev, hints=hints)
     # Copies of the logits, rotated step by step, so that a workload smaller
     # than the 256 MB last-level cache is still read from HBM.
     nsets = int(min(32, max(1, -(-ROTATE_BYTES // max(logit_bytes, 1)))))
@@ -402,7 +407,6 @@ def main():
 
     # The kernel that reads most of the logit bytes: the streaming select for
     # top-k / argmax sequences, the pair kernel for dense ones.
-    sel_bytes, pair_bytes = kernel_bytes(bt)
     kernel = binding.SV_KERNEL_PAIR if pair_bytes > sel_bytes else binding.SV_KERNEL_SELECT
     kname = {binding.SV_KERNEL_SELECT: "select_kernel", binding.SV_KERNEL_PAIR: "pair_kernel"}[kernel]
     kbytes = max(sel_bytes, pair_bytes)
@@ -437,7 +441,9 @@ def main():
     other_us = {}
     for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, "pair_kernel"),
                        (binding.SV_KERNEL_FINISH, "finish_kernel")):
-        if kern != kernel:
+        if kern == binding.SV_KERNEL_PAIR and hints & binding.SV_HINT_NO_DENSE:
+            other_us[name] = None      # not launched
+        elif kern != kernel:
             _, ms = timed(kern, min(K, 20))
             other_us[name] = float(ms.mean() * 1e3) if (ms > 0).all() else None
     k_avg = float(k_ms.mean())
@@ -459,7 +465,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": bt.B, "V": bt.V, "gamma": bt.gamma_max,
                    "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
-                   "logit_bytes_per_call": logit_bytes, "parallelism": "single-gpu"},
+                   "logit_bytes_per_call": logit_bytes, "parallelism": "single-gpu",
+                   "hints": "no-dense" if hints else "none"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,

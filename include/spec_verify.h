@@ -121,6 +121,14 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
                 int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Hints for spec_verify_ex (bit flags). */
+enum {
+  SV_HINT_NO_DENSE = 1   /* the caller knows that every sequence has T == 0 or 0 < top_k <= 512:
+                            the per-(sequence, position) kernel for dense sequences is not
+                            launched.  A dense sequence in such a call still gets its exact
+                            result, from a slower one-workgroup-per-sequence path.            */
+};
+
 /*
  * spec_verify with lenience (the Leviathan review, section "Lenience"): the
  * acceptance test multiplies q(x) by l in [0, 1], accept iff u * l * q(x) < p(x).
@@ -131,13 +139,14 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
  *
  *  lenience     [B] float in [0, 1], or NULL (all 1).  A value outside [0, 1] or NaN
  *               makes that sequence invalid.
+ *  hints        0 or SV_HINT_* flags (unknown bits: SV_ERR_ARG).
  * Every other argument, the workspace and the error behaviour are those of
  * spec_verify.
  */
 int spec_verify_ex(const void* p_logits, const void* q_logits, int dtype,
                    const int32_t* draft_tokens, const int32_t* gamma_len, const float* uniforms,
                    const float* temperature, const int32_t* top_k, const float* top_p, const float* lenience,
-                   int B, int gamma_max, int V,
+                   int hints, int B, int gamma_max, int V,
                    int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                    void* workspace, size_t workspace_bytes, void* stream);
 
@@ -305,7 +314,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 5. */
+/* ABI version: 6. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

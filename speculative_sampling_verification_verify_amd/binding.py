@@ -20,6 +20,7 @@ SV_BF16, SV_FP32 = 0, 1
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
 SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL, SV_KERNEL_KSEQ = 0, 1, 2, 3, 4
 SV_MAX_CANDIDATES = 64
+SV_HINT_NO_DENSE = 1
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 
@@ -59,7 +60,7 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_set_stage_events.argtypes = [i, vp, vp]
         L.spec_verify_gumbel.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp]
         L.spec_verify_gumbel.restype = i
-        L.spec_verify_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_ex.restype = i
         L.spec_sample_workspace_bytes.argtypes = [i, i, i]
         L.spec_sample_workspace_bytes.restype = sz
@@ -154,9 +155,10 @@ def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: to
                 top_k: Optional[torch.Tensor], top_p: Optional[torch.Tensor],
                 out_tokens: torch.Tensor, out_n_accepted: torch.Tensor, out_alpha: torch.Tensor,
                 out_pq: Optional[torch.Tensor], workspace: torch.Tensor, stream=None,
-                lenience: Optional[torch.Tensor] = None) -> None:
+                lenience: Optional[torch.Tensor] = None, hints: int = 0) -> None:
     """Enqueue one verify call (see include/spec_verify.h for the contract);
-    with `lenience` ([B] float32) the call goes to spec_verify_ex."""
+    with `lenience` ([B] float32) or `hints` (SV_HINT_* flags) the call goes
+    to spec_verify_ex."""
     if p_logits.dim() != 3 or q_logits.dim() != 3:
         raise ValueError("p_logits must be [B, gamma_max+1, V] and q_logits [B, gamma_max, V]")
     B, G1, V = p_logits.shape
@@ -179,15 +181,15 @@ def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: to
     _check(out_pq, "out_pq", torch.float32, (B, G, 2), dev)
     _check(lenience, "lenience", torch.float32, (B,), dev)
     wsb = workspace.numel() * workspace.element_size()
-    if lenience is None:
+    if lenience is None and not hints:
         rc = lib().spec_verify(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
                                _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V,
                                _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
                                _ptr(workspace), wsb, _stream_handle(stream))
     else:
         rc = lib().spec_verify_ex(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
-                                  _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(lenience), B, G,
-                                  V, _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
+                                  _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(lenience),
+                                  int(hints), B, G, V, _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha), _ptr(out_pq),
                                   _ptr(workspace), wsb, _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify")
@@ -196,8 +198,9 @@ def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: to
 class Verifier:
     """Owns a workspace and output buffers for calls of one shape."""
 
-    def __init__(self, B: int, gamma_max: int, V: int, dtype: int = SV_BF16, device="cuda", with_pq=True):
-        self.B, self.G, self.V, self.dtype = B, gamma_max, V, dtype
+    def __init__(self, B: int, gamma_max: int, V: int, dtype: int = SV_BF16, device="cuda", with_pq=True,
+                 hints: int = 0):
+        self.B, self.G, self.V, self.dtype, self.hints = B, gamma_max, V, dtype, hints
         dev = torch.device(device)
         nbytes = spec_verify_workspace_bytes(B, gamma_max, V, dtype)
         if nbytes == 0:
@@ -212,7 +215,7 @@ class Verifier:
     def __call__(self, p_logits, q_logits, draft_tokens, uniforms, temperature, top_k=None, top_p=None,
                  gamma_len=None, stream=None, lenience=None):
         spec_verify(p_logits, q_logits, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p,
-                    self.tokens, self.n_accepted, self.alpha, self.pq, self.workspace, stream, lenience)
+                    self.tokens, self.n_accepted, self.alpha, self.pq, self.workspace, stream, lenience, self.hints)
         return self.tokens, self.n_accepted, self.alpha, self.pq
 
 

@@ -229,9 +229,10 @@ static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V,
 // drafts, no draft logits and no n output.
 static int run_verify(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
                       const int32_t* gamma_len, const float* uniforms, const float* temperature,
-                      const int32_t* top_k, const float* top_p, const float* lenience, int B, int gamma_max, int V,
-                      int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
-                      void* workspace, size_t workspace_bytes, void* stream, int sampler) {
+                      const int32_t* top_k, const float* top_p, const float* lenience, int hints, int B,
+                      int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha,
+                      float* out_pq, void* workspace, size_t workspace_bytes, void* stream, int sampler) {
+  if (hints & ~SV_HINT_NO_DENSE) return SV_ERR_ARG;
   if (!p_logits || !uniforms || !temperature || !out_tokens) return SV_ERR_ARG;
   if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
@@ -281,6 +282,10 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
   a.dense_list = reinterpret_cast<int32_t*>(ws + Lw.dense_list_off);
   size_t pair_lds = 0;
   a.pair = pair_variant(V, dtype, vector_ok, &pair_lds) != 0 && (long long)B * (gamma_max + 1) <= 0x7FFFFFFFLL ? 1 : 0;
+  // The caller's promise that no sequence is dense saves the pair launch; a
+  // dense sequence under that hint still gets its exact result from the
+  // finisher's multi-pass path.
+  if (hints & SV_HINT_NO_DENSE) a.pair = 0;
   // Without the pair kernel the dense sequences go to the finisher whole and
   // nothing is listed.
   a.sel_blocks = a.pair ? sel_grid : grid;
@@ -317,15 +322,15 @@ extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_byte
 
 extern "C" int spec_verify_ex(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
                               const int32_t* gamma_len, const float* uniforms, const float* temperature,
-                              const int32_t* top_k, const float* top_p, const float* lenience, int B, int gamma_max,
-                              int V, int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              const int32_t* top_k, const float* top_p, const float* lenience, int hints, int B,
+                              int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha,
+                              float* out_pq, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
   if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
   if (B == 0) return SV_OK;
   return run_verify(p_logits, q_logits, dtype, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p, lenience,
-                    B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, workspace, workspace_bytes,
+                    hints, B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, workspace, workspace_bytes,
                     stream, 0);
 }
 
@@ -335,7 +340,7 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
                            int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return spec_verify_ex(p_logits, q_logits, dtype, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p,
-                        nullptr, B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, workspace,
+                        nullptr, 0, B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, workspace,
                         workspace_bytes, stream);
 }
 
@@ -353,8 +358,8 @@ extern "C" int spec_sample(const void* logits, int dtype, const float* uniforms,
   if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (R < 0 || V < 1) return SV_ERR_ARG;
   if (R == 0) return SV_OK;
-  return run_verify(logits, nullptr, dtype, nullptr, nullptr, uniforms, temperature, top_k, top_p, nullptr, R, 0, V,
-                    out_tokens, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
+  return run_verify(logits, nullptr, dtype, nullptr, nullptr, uniforms, temperature, top_k, top_p, nullptr, 0, R, 0,
+                    V, out_tokens, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
 }
 
 namespace sv {
@@ -536,7 +541,7 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 5; }
+extern "C" int spec_verify_version(void) { return 6; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;

@@ -30,6 +30,7 @@ struct FinSmem {
   float pv[POOL];                               // exp((z - zmax) / T) per kept survivor
   double wts[POOL];                             // residual / bonus weights of a row (draws)
   uint32_t soff[MAXSEG + 1];                    // pool offset of each (row, part) list
+  uint32_t cslot[MAXSEG];                       // survivor count of every (slot, part) of the sequence
   uint32_t off[MAXROWS + 1];                    // pool offset of each used row
   uint32_t whist[NWAVE][256];                   // per-wavefront radix histograms
   uint32_t st_thr[MAXROWS];                     // kept keys are >= st_thr (multi-pass path)
@@ -138,12 +139,16 @@ __device__ __forceinline__ int wave_keep(FinSmem& s, int o, int n, uint32_t t) {
 // range (cnt[r] entries, exp((z - zmax) / T) of each in pv) with its
 // normaliser.
 template <typename ET>
-__device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m) {
+__device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m, int np) {
   const int lane = threadIdx.x & 63;
   const int o = (int)s.off[r];
   int n = (int)(s.off[r + 1] - s.off[r]);
   uint32_t* hist = s.whist[threadIdx.x >> 6];
-  const uint32_t kth = n > (int)m.k ? wave_kth_largest<Key<ET>::LEVELS>(s.pool + o, n, m.k, hist) : 1u;
+  // A row streamed as one part already holds exactly its kept set (the k-th
+  // largest and everything above, ties included); the union of several
+  // parts is cut to the k-th largest here.
+  const uint32_t kth =
+      (np > 1 && n > (int)m.k) ? wave_kth_largest<Key<ET>::LEVELS>(s.pool + o, n, m.k, hist) : 1u;
   uint32_t kmax = 0;
   for (int i = lane; i < n; i += 64) kmax = max(kmax, s.pool[o + i].x);
   kmax = wave_max_dpp(kmax);
@@ -678,10 +683,23 @@ __device__ __forceinline__ int dense_draw(const Args& a, FinSmem& s, int b, cons
 // ===========================================================================
 template <typename ET, bool VECTOR>
 __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
-  const Mode m = seq_mode(a, b);
-  const uint32_t fl = a.seq_flags[b];
   const int RS = 2 * a.G + 1;
   const int G = a.G;
+  const float* ub = a.u + (size_t)b * (G + 1);
+  const int32_t* xb = a.draft + (size_t)b * G;
+  // Every global load of the opening is issued before any is used: the
+  // survivor counts of all slots and the drafts and uniforms of all
+  // positions (padding included, masked below), with the parameters.
+  const int nslot = RS * a.NP;
+  int32_t craw = 0, xraw = 0;
+  float uraw = 0.5f;
+  if (nslot <= MAXSEG && (int)threadIdx.x < nslot) craw = a.counts[(size_t)b * nslot + threadIdx.x];
+  if ((int)threadIdx.x < G) {
+    xraw = xb[threadIdx.x];
+    uraw = ub[threadIdx.x];
+  }
+  const Mode m = seq_mode(a, b);
+  const uint32_t fl = a.seq_flags[b];
   const int R = 2 * m.g + 1;
   const int NS = R * a.NP;          // (row, part) lists of the sequence
   const int wave = threadIdx.x >> 6;
@@ -692,23 +710,21 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   ok = ok && !(m.tp != m.tp);
   const float lv = a.lenience ? a.lenience[b] : 1.0f;
   ok = ok && lv >= 0.0f && lv <= 1.0f;
-  const float* ub = a.u + (size_t)b * (G + 1);
-  const int32_t* xb = a.draft + (size_t)b * G;
   bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG;
   const bool from_pairs = a.pair && m.mode == MODE_DENSE;
   uint32_t badin = 0;
-  for (int i = threadIdx.x; i < m.g; i += NT) {
-    const int x = xb[i];
-    const float ui = ub[i];
-    badin |= (x < 0 || x >= a.V || !(ui >= 0.0f && ui < 1.0f)) ? 1u : 0u;
-  }
+  if ((int)threadIdx.x < m.g)
+    badin |= (xraw < 0 || xraw >= a.V || !(uraw >= 0.0f && uraw < 1.0f)) ? 1u : 0u;
   if (threadIdx.x == 0) badin |= !(ub[G] >= 0.0f && ub[G] < 1.0f) ? 1u : 0u;
+  if (nslot <= MAXSEG && (int)threadIdx.x < nslot) s.cslot[threadIdx.x] = (uint32_t)max(craw, 0);
+  __syncthreads();
   // List sizes: (row r, part p) -> soff[r * NP + p + 1]; the block scan
   // runs for every sequence so that control flow stays block-uniform.
   uint32_t c = 0;
   if (ok && !dense && (int)threadIdx.x < NS) {
     const int r = threadIdx.x / a.NP, p = threadIdx.x - r * a.NP;
-    c = (uint32_t)max(a.counts[(size_t)(b * RS + used_slot(G, m.g, r)) * a.NP + p], 0);
+    const int si = used_slot(G, m.g, r) * a.NP + p;
+    c = nslot <= MAXSEG ? s.cslot[si] : (uint32_t)max(a.counts[(size_t)b * RS * a.NP + si], 0);
   }
   uint32_t total = 0;
   const uint32_t excl = block_excl_scan(c, s.red_u, &total);
@@ -738,7 +754,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     if ((int)threadIdx.x < R) empty = s.off[threadIdx.x + 1] == s.off[threadIdx.x] ? 1u : 0u;
     ok = block_or_u32(empty, s.red_u) == 0;   // a row without a finite logit
     if (ok) {
-      for (int r = wave; r < R; r += NWAVE) pool_row_stats<ET>(s, r, m);
+      for (int r = wave; r < R; r += NWAVE) pool_row_stats<ET>(s, r, m, a.NP);
       __syncthreads();
       // Every position's p(x), q(x), overlap and residual draw (as if the
       // first rejection were there), and the bonus draw, in parallel; the

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 5
+    assert binding.spec_verify_version() == 6
 
 
 def test_workspace_bytes():
@@ -142,11 +142,13 @@ def test_sample_and_lenient_host_argument_errors():
 
     B, G = 2, 3
     wneed = binding.spec_verify_workspace_bytes(B, G, V, binding.SV_BF16)
-    ex = lambda q=fake, draft=fake, G=G: L.spec_verify_ex(fake, q, binding.SV_BF16, draft, nul, fake, fake, nul, nul,
-                                                          nul, B, G, V, fake, fake, fake, nul, fake, wneed, nul)
+    ex = lambda q=fake, draft=fake, G=G, hints=0: L.spec_verify_ex(fake, q, binding.SV_BF16, draft, nul, fake, fake,
+                                                                   nul, nul, nul, hints, B, G, V, fake, fake, fake,
+                                                                   nul, fake, wneed, nul)
     assert ex(q=nul) == binding.SV_ERR_ARG
     assert ex(draft=nul) == binding.SV_ERR_ARG
     assert ex(G=0) == binding.SV_ERR_ARG
+    assert ex(hints=6) == binding.SV_ERR_ARG
 
 
 def test_spectr_host_argument_errors():

@@ -144,3 +144,23 @@ def test_gumbel_sampler_and_coupled_round(dtype, V, R):
         gb = synth.GumbelBatch(base.workload, P, Nz, draft, np.full(Bq, G, np.int32), Tb, kb, tpb, 0)
         from test_gpu_gumbel import check_gumbel
         check_gumbel(gb, f"coupled-round-{dtype}-V{V}")
+
+
+def test_no_dense_hint_keeps_dense_rows_exact():
+    # The hint only skips the dense-pair launch; dense sequences in such a
+    # call take the one-workgroup-per-sequence path and still match.
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+    from gpu_util import GpuOut
+    bt = synth.make_batch(4, B=16, V=20000)          # mixed greedy and top-p rows: some dense
+    P, dt = logits_to_dev(bt.p_logits, "cuda:0")
+    Q, _ = logits_to_dev(bt.q_logits, "cuda:0")
+    ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt, device="cuda:0", hints=binding.SV_HINT_NO_DENSE)
+    tok, n, alpha, pq = ver(P, Q, to_dev(bt.draft, "cuda:0"), to_dev(bt.u, "cuda:0"),
+                            to_dev(bt.temperature, "cuda:0"), to_dev(bt.top_k, "cuda:0"), to_dev(bt.top_p, "cuda:0"),
+                            to_dev(bt.gamma_len, "cuda:0"))
+    torch.cuda.synchronize()
+    g = GpuOut(tok.cpu().numpy(), n.cpu().numpy(), alpha.cpu().numpy(), pq.cpu().numpy())
+    ref = oracle.verify_batch(bt.p_logits, bt.q_logits, bt.draft, bt.u, bt.temperature, bt.top_k, bt.top_p,
+                              bt.gamma_len, processes=1)
+    compare(bt, g, ref, "no-dense-hint")

@@ -31,6 +31,13 @@
 
 namespace sv {
 
+#ifndef SV_PAIR_UNR
+#define SV_PAIR_UNR 4      // units in flight per thread on a streamed pass over one row
+#endif
+#ifndef SV_PAIR_UNR1
+#define SV_PAIR_UNR1 2     // units of each row in flight per thread on the first streamed pass
+#endif
+
 constexpr int PAIR_LDS_ROW_MAX = 65536;   // bytes of one row held in LDS
 constexpr int PAIR_MAXTILE = 64;          // residual tiles (NTP units each) per row
 constexpr int PAIR_NBIN = 2048;           // value bins of the streamed nucleus histogram
@@ -278,7 +285,7 @@ __device__ __forceinline__ float key_floor_value(uint32_t thr) {
 template <typename ET, int NTP, bool VECTOR, bool LDSR, class F>
 __device__ __forceinline__ void row_units(const typename PT<ET, VECTOR>::U* src, int NU, F fn) {
   using T = PT<ET, VECTOR>;
-  constexpr int UNR = LDSR ? 2 : 4;
+  constexpr int UNR = LDSR ? 2 : SV_PAIR_UNR;
   int ui = threadIdx.x;
   for (; ui + (UNR - 1) * NTP < NU; ui += UNR * NTP) {
     typename T::U u[UNR];
@@ -537,22 +544,22 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
     P = lp;
     Q = lq;
   } else {
+    constexpr int U1 = SV_PAIR_UNR1;
     int ui = threadIdx.x;
-    for (; ui + NTP < NU; ui += 2 * NTP) {
-      const U p0 = gp[ui], p1 = gp[ui + NTP];
-      U q0, q1;
-      if (resid) {
-        q0 = gq[ui];
-        q1 = gq[ui + NTP];
+    for (; ui + (U1 - 1) * NTP < NU; ui += U1 * NTP) {
+      U pu[U1], qu[U1];
+#pragma unroll
+      for (int r = 0; r < U1; ++r) {
+        pu[r] = gp[ui + r * NTP];
+        if (resid) qu[r] = gq[ui + r * NTP];
       }
-      scan_unit(p0, zmp);
-      scan_unit(p1, zmp);
-      if (resid) {
-        scan_unit(q0, zmq);
-        scan_unit(q1, zmq);
+#pragma unroll
+      for (int r = 0; r < U1; ++r) {
+        scan_unit(pu[r], zmp);
+        if (resid) scan_unit(qu[r], zmq);
       }
     }
-    if (ui < NU) {
+    for (; ui < NU; ui += NTP) {
       scan_unit(gp[ui], zmp);
       if (resid) scan_unit(gq[ui], zmq);
     }

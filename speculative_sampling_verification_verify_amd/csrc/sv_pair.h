@@ -32,11 +32,15 @@
 namespace sv {
 
 #ifndef SV_PAIR_UNR
-#define SV_PAIR_UNR 4      // units in flight per thread on a streamed pass over one row
+#define SV_PAIR_UNR 2      // units in flight per thread on a streamed pass over one row
 #endif
 #ifndef SV_PAIR_UNR1
 #define SV_PAIR_UNR1 2     // units of each row in flight per thread on the first streamed pass
 #endif
+// Streamed-row workgroups are kept to 64 VGPRs so that two 1024-thread
+// workgroups share a CU (8 waves per SIMD): their passes are latency-bound,
+// and two resident workgroups beat one with more loads in flight.
+constexpr int PAIR_STREAM_WAVES_PER_EU = 8;
 
 constexpr int PAIR_LDS_ROW_MAX = 65536;   // bytes of one row held in LDS
 constexpr int PAIR_MAXTILE = 64;          // residual tiles (NTP units each) per row
@@ -718,7 +722,8 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
 // turn by a grid sized to what the chip holds at once: when no sequence is
 // dense every workgroup reads the count once and leaves.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
-__global__ __launch_bounds__(NTP) void pair_kernel(Args a) {
+__global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(LDSR ? 1 : PAIR_STREAM_WAVES_PER_EU)))
+void pair_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char pair_rows[];
   __shared__ PairSmem<NTP> s;
   __shared__ PairExtra<LDSR> ps;

@@ -412,11 +412,15 @@ def gumbel_verify_sequence(zp: np.ndarray, g: np.ndarray, draft: np.ndarray, T: 
     for j in range(gamma_b + 1):
         if not row_is_valid(zp[j]):
             return bad
-        if T > 0.0 and not np.isfinite(np.asarray(g[j], dtype=np.float32)).all():
-            return bad
     target = np.full(gamma_max + 1, -1, np.int32)
     margin = INF
     for j in range(gamma_b + 1):
+        # Noise off the processed support never takes part in the argmax;
+        # a NaN or infinite value on it makes the sequence invalid.
+        if T > 0.0:
+            kept = process(zp[j], T, top_k, top_p).kept
+            if not np.isfinite(np.asarray(g[j], dtype=np.float32)[kept]).all():
+                return bad
         t, m = gumbel_target_token(zp[j], g[j], T, top_k, top_p)
         target[j] = t
         margin = min(margin, m)

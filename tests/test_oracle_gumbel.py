@@ -213,6 +213,12 @@ def test_ties_go_to_the_lowest_id_and_bad_inputs_are_flagged():
     g2 = g.copy()
     g2[1, 3] = np.nan
     assert gumbel_verify_sequence(z, g2, np.array([2], np.int32), 1.0, 0, 1.0, 1).n == -1
+    # Off the support (top-k 1 keeps only id 0 of a strictly decreasing row) the noise is never used.
+    zd = np.tile(-np.arange(6.0), (2, 1))
+    g3 = np.zeros((2, 6), np.float32)
+    g3[:, 3] = np.nan
+    assert gumbel_verify_sequence(zd, g3, np.array([0], np.int32), 1.0, 1, 1.0, 1).n == 1
+    assert gumbel_verify_sequence(zd, g3, np.array([0], np.int32), 1.0, 4, 1.0, 1).n == -1
     assert gumbel_verify_sequence(z, g2, np.array([0], np.int32), 0.0, 0, 1.0, 1).n == 1   # noise unused at T = 0
     assert gumbel_verify_sequence(z, g, np.array([6], np.int32), 1.0, 0, 1.0, 1).n == -1
     z2 = z.copy()

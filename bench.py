@@ -133,8 +133,13 @@ def main_gumbel(args):
     t_gen = time.perf_counter() - t_gen
     es = gb.p_logits.itemsize
     g1 = gb.gamma_len.astype(np.int64) + 1
-    noisy = gb.temperature > 0
-    kbytes = int((g1 * gb.V * es).sum() + (g1[noisy] * gb.V * 4).sum())
+    T, k = gb.temperature, gb.top_k
+    listed = (T == 0) | ((T > 0) & (k > 0) & (k < gb.V) & (k <= 512))
+    # The streaming select reads the listed sequences' logits once (noise only
+    # at their few kept ids); the dense kernel reads logits and noise.
+    sel_bytes = int((g1[listed] * gb.V * es).sum())
+    dense_bytes = int((g1[~listed] * gb.V * (es + 4)).sum())
+    kbytes = max(sel_bytes, dense_bytes)
     cpu = None
     if not args.no_cpu:
         try:
@@ -154,7 +159,8 @@ def main_gumbel(args):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     N = t(gb.noise)
     draft, temp, topk, topp, gl = t(gb.draft), t(gb.temperature), t(gb.top_k), t(gb.top_p), t(gb.gamma_len)
-    ver = binding.GumbelVerifier(gb.B, gb.gamma_max, device=dev)
+    ver = binding.GumbelVerifier(gb.B, gb.gamma_max, gb.V,
+                                 binding.SV_BF16 if dtype_name == "bf16" else binding.SV_FP32, device=dev)
     nsets = int(min(32, max(1, -(-ROTATE_BYTES // max(kbytes, 1)))))
     sets = [(P, N)] + [(P.clone(), N.clone()) for _ in range(nsets - 1)]
     torch.cuda.synchronize()
@@ -173,8 +179,10 @@ def main_gumbel(args):
         b.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    kern = binding.SV_KERNEL_SELECT if sel_bytes >= dense_bytes else binding.SV_KERNEL_GUMBEL
+    kname = "select_kernel" if kern == binding.SV_KERNEL_SELECT else "gumbel_kernel"
     for j, (a, b) in enumerate(evs):
-        binding.spec_verify_set_stage_events(a, b, binding.SV_KERNEL_GUMBEL)
+        binding.spec_verify_set_stage_events(a, b, kern)
         step(j)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -202,8 +210,8 @@ def main_gumbel(args):
                    "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile("gumbel_kernel", w.name),
-                     "kernel": "gumbel_kernel", "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(kname, w.name),
+                     "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,
                      "kernel_p10_us": float(np.percentile(k_ms, 10) * 1e3),
                      "kernel_p90_us": float(np.percentile(k_ms, 90) * 1e3)},
         "cpu_baseline": cpu,

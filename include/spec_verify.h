@@ -186,11 +186,13 @@ int spec_sample(const void* logits, int dtype, const float* uniforms, const floa
  *  temperature, top_k, top_p: [R] as for spec_verify (top_k / top_p may be NULL).
  *  out_tokens   [R] int32: the sample, or -1 for an invalid row (as for
  *               spec_verify_gumbel).
- * No workspace; asynchronous on `stream`.  Returns SV_OK or a negative code.
+ *  workspace    spec_verify_gumbel_workspace_bytes(R, 0, V, dtype) bytes, 256-byte
+ *               aligned, prepared once with spec_verify_gumbel_workspace_init(.., R, 0, ..).
+ * Asynchronous on `stream`.  Returns SV_OK or a negative code.
  */
 int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const float* temperature,
                        const int32_t* top_k, const float* top_p, int R, int V, int32_t* out_tokens,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Verify with shared Gumbel noise (Gumbel coupling; "Speculative Decoding: the
@@ -207,14 +209,21 @@ int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const 
  *
  *  p_logits     [B][gamma_max+1][V] target logits (bf16 bit patterns or fp32).
  *  noise        [B][gamma_max+1][V] float Gumbel noise, one vector per position
- *               (the same vectors the drafter used).  NaN or infinite noise in a
- *               used row (T > 0) makes the sequence invalid.
+ *               (the same vectors the drafter used).  NaN or infinite noise on the
+ *               processed support of a used row (T > 0) makes the sequence invalid.
  *  draft_tokens [B][gamma_max] int32 proposals; slots beyond gamma_b ignored.
  *  gamma_len, temperature, top_k, top_p: as for spec_verify (uniforms are not used).
  *  out_tokens   [B][gamma_max+1] int32: x_1..x_n, then t_n, then -1 padding.
  *  out_n_accepted [B] int32: n, or -1 for an invalid sequence.
  *  out_target   [B][gamma_max+1] int32: t_k for k <= gamma_b, -1 beyond (and for an
- *               invalid sequence).  Also the call's only scratch: no workspace.
+ *               invalid sequence).
+ *  workspace    spec_verify_gumbel_workspace_bytes(B, gamma_max, V, dtype) bytes,
+ *               256-byte aligned, prepared once with spec_verify_gumbel_workspace_init
+ *               (every successful call leaves it prepared again).
+ * Argmax and top-k (<= 512) sequences are streamed once by the select kernel and
+ * the noise is read only at their kept ids; other sequences stream logits and
+ * noise.  Only noise on the processed support is used, and only there does a NaN
+ * or infinite value make the sequence invalid.
  *
  * Invalid data (as for spec_verify, plus bad noise) is reported per sequence with
  * n = -1 and tokens -1.  Base pointers must be aligned to their element size;
@@ -225,7 +234,15 @@ int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const 
 int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
                        const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
                        const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
-                       int32_t* out_n_accepted, int32_t* out_target, void* stream);
+                       int32_t* out_n_accepted, int32_t* out_target, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Workspace of spec_verify_gumbel (and, with gamma_max = 0 and B = R rows, of
+ * spec_sample_gumbel): its size (0 for invalid sizes) and its one-time
+ * preparation on `stream`.  Returns SV_OK or a negative code. */
+size_t spec_verify_gumbel_workspace_bytes(int B, int gamma_max, int V, int dtype);
+int spec_verify_gumbel_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
+                                      int dtype, void* stream);
 
 /*
  * Multi-candidate verify: K-SEQ at each depth and the SpecTr walk ("SpecTr:
@@ -314,7 +331,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 6. */
+/* ABI version: 7. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,8 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_v
             "spec_verify_strerror", "spec_verify_version", "spec_verify_set_stage_events", "spec_verify_gumbel",
             "spec_sample_workspace_bytes", "spec_sample_workspace_init", "spec_sample", "spec_sample_gumbel",
             "spec_verify_expected_tokens", "spec_verify_speedup", "spec_verify_operations",
-            "spec_verify_optimal_gamma", "spec_verify_acceptance_length", "spec_verify_spectr")
+            "spec_verify_optimal_gamma", "spec_verify_acceptance_length", "spec_verify_spectr",
+            "spec_verify_gumbel_workspace_bytes", "spec_verify_gumbel_workspace_init")
 
 _lib = None
 
@@ -58,7 +59,11 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_version.argtypes = []
         L.spec_verify_version.restype = i
         L.spec_verify_set_stage_events.argtypes = [i, vp, vp]
-        L.spec_verify_gumbel.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp]
+        L.spec_verify_gumbel.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_gumbel_workspace_bytes.argtypes = [i, i, i, i]
+        L.spec_verify_gumbel_workspace_bytes.restype = sz
+        L.spec_verify_gumbel_workspace_init.argtypes = [vp, sz, i, i, i, i, vp]
+        L.spec_verify_gumbel_workspace_init.restype = i
         L.spec_verify_gumbel.restype = i
         L.spec_verify_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_ex.restype = i
@@ -68,7 +73,7 @@ def lib() -> ctypes.CDLL:
         L.spec_sample_workspace_init.restype = i
         L.spec_sample.argtypes = [vp, i, vp, vp, vp, vp, i, i, vp, vp, sz, vp]
         L.spec_sample.restype = i
-        L.spec_sample_gumbel.argtypes = [vp, i, vp, vp, vp, vp, i, i, vp, vp]
+        L.spec_sample_gumbel.argtypes = [vp, i, vp, vp, vp, vp, i, i, vp, vp, sz, vp]
         L.spec_sample_gumbel.restype = i
         L.spec_verify_spectr.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp]
         L.spec_verify_spectr.restype = i
@@ -219,10 +224,22 @@ class Verifier:
         return self.tokens, self.n_accepted, self.alpha, self.pq
 
 
+def gumbel_workspace(B: int, gamma_max: int, V: int, dtype: int, device) -> torch.Tensor:
+    """A prepared workspace for spec_verify_gumbel (gamma_max = 0: spec_sample_gumbel)."""
+    nbytes = int(lib().spec_verify_gumbel_workspace_bytes(B, gamma_max, V, dtype))
+    if nbytes == 0:
+        raise ValueError("unsupported sizes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    rc = lib().spec_verify_gumbel_workspace_init(_ptr(ws), nbytes, B, gamma_max, V, dtype, _stream_handle(None))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_gumbel_workspace_init")
+    return ws
+
+
 def spec_verify_gumbel(p_logits: torch.Tensor, noise: torch.Tensor, draft_tokens: torch.Tensor,
                        gamma_len: Optional[torch.Tensor], temperature: torch.Tensor, top_k: Optional[torch.Tensor],
                        top_p: Optional[torch.Tensor], out_tokens: torch.Tensor, out_n_accepted: torch.Tensor,
-                       out_target: torch.Tensor, stream=None) -> None:
+                       out_target: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     """Enqueue one shared-noise verify call (see include/spec_verify.h)."""
     if p_logits.dim() != 3:
         raise ValueError("p_logits must be [B, gamma_max+1, V]")
@@ -244,16 +261,18 @@ def spec_verify_gumbel(p_logits: torch.Tensor, noise: torch.Tensor, draft_tokens
     _check(out_target, "out_target", torch.int32, (B, G + 1), dev)
     rc = lib().spec_verify_gumbel(_ptr(p_logits), dt, _ptr(noise), _ptr(draft_tokens), _ptr(gamma_len),
                                   _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V, _ptr(out_tokens),
-                                  _ptr(out_n_accepted), _ptr(out_target), _stream_handle(stream))
+                                  _ptr(out_n_accepted), _ptr(out_target), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_gumbel")
 
 
 class GumbelVerifier:
-    """Output buffers for shared-noise verify calls of one shape."""
+    """Workspace and output buffers for shared-noise verify calls of one shape."""
 
-    def __init__(self, B: int, gamma_max: int, device="cuda"):
+    def __init__(self, B: int, gamma_max: int, V: int, dtype: int = SV_BF16, device="cuda"):
         dev = torch.device(device)
+        self.workspace = gumbel_workspace(B, gamma_max, V, dtype, dev)
         self.tokens = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
         self.n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
         self.target = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
@@ -261,7 +280,7 @@ class GumbelVerifier:
     def __call__(self, p_logits, noise, draft_tokens, temperature, top_k=None, top_p=None, gamma_len=None,
                  stream=None):
         spec_verify_gumbel(p_logits, noise, draft_tokens, gamma_len, temperature, top_k, top_p, self.tokens,
-                           self.n_accepted, self.target, stream)
+                           self.n_accepted, self.target, self.workspace, stream)
         return self.tokens, self.n_accepted, self.target
 
 
@@ -307,8 +326,10 @@ class Sampler:
 
 def spec_sample_gumbel(logits: torch.Tensor, noise: torch.Tensor, temperature: torch.Tensor,
                        top_k: Optional[torch.Tensor] = None, top_p: Optional[torch.Tensor] = None,
-                       out_tokens: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """The shared-noise drafter's sample per row (spec_sample_gumbel)."""
+                       out_tokens: Optional[torch.Tensor] = None, stream=None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The shared-noise drafter's sample per row (spec_sample_gumbel); a
+    workspace is made for the call when none is given."""
     if logits.dim() != 2:
         raise ValueError("logits must be [R, V]")
     R, V = logits.shape
@@ -321,8 +342,11 @@ def spec_sample_gumbel(logits: torch.Tensor, noise: torch.Tensor, temperature: t
     if out_tokens is None:
         out_tokens = torch.empty((R,), dtype=torch.int32, device=dev)
     _check(out_tokens, "out_tokens", torch.int32, (R,), dev)
+    if workspace is None:
+        workspace = gumbel_workspace(R, 0, V, dt, dev)
     rc = lib().spec_sample_gumbel(_ptr(logits), dt, _ptr(noise), _ptr(temperature), _ptr(top_k), _ptr(top_p), R, V,
-                                  _ptr(out_tokens), _stream_handle(stream))
+                                  _ptr(out_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_sample_gumbel")
     return out_tokens

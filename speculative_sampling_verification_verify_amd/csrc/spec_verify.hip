@@ -59,10 +59,12 @@ struct Plan {
 
 // Parts per row: enough units to give every SIMD of the chip about four
 // wavefronts (256 CUs x 4 SIMDs x 4), with at least two steps per part.
-static Plan plan(int B, int G, int V, int dtype) {
+// RS: logit rows per sequence in the list layout (2G+1 for the verify, G+1
+// for the shared-noise verify, whose draft rows are not inputs).
+static Plan plan(int B, int RS, int V, int dtype) {
   const int vec = dtype == SV_BF16 ? 8 : 4;
   const int step = 64 * WVPL * vec;
-  const long long R = (long long)B * (2 * G + 1);
+  const long long R = (long long)B * RS;
   long long np = R > 0 ? 4096 / R : 1;
   np = np < 1 ? 1 : np;
   np = np > MAXNP ? MAXNP : np;
@@ -112,9 +114,9 @@ struct Layout {
   size_t seq_flags_off, dense_count_off, counters_bytes, pos_off, dense_list_off, counts_off, lists_off, total;
 };
 
-static Layout layout(int B, int G, const Plan& p) {
+static Layout layout(int B, int G, int RS, const Plan& p) {
   Layout L;
-  const size_t R = (size_t)B * (2 * G + 1);
+  const size_t R = (size_t)B * RS;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L.seq_flags_off = 0;
   L.dense_count_off = (size_t)B * 4;
@@ -200,19 +202,19 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
 
 // Workspace size and preparation for B sequences of G drafts (G == 0: rows
 // to sample).
-static size_t ws_bytes(int B, int G, int V, int dtype) {
+static size_t ws_bytes(int B, int G, int V, int dtype, int RS) {
   if (B < 0 || G < 0 || G > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
   if (dtype != SV_BF16 && dtype != SV_FP32) return 0;
   if (B == 0) return 256;
-  return layout(B, G, plan(B, G, V, dtype)).total;
+  return layout(B, G, RS, plan(B, RS, V, dtype)).total;
 }
 
-static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V, int dtype, void* stream) {
-  const size_t need = ws_bytes(B, G, V, dtype);
+static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V, int dtype, int RS, void* stream) {
+  const size_t need = ws_bytes(B, G, V, dtype, RS);
   if (need == 0) return SV_ERR_ARG;
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
   if (B == 0) return SV_OK;
-  const Layout L = layout(B, G, plan(B, G, V, dtype));
+  const Layout L = layout(B, G, RS, plan(B, RS, V, dtype));
   const size_t n = L.counters_bytes / 4;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
                      (hipStream_t)stream, (uint32_t*)workspace, n);
@@ -237,10 +239,11 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
   if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)p_logits % es) || (q_logits && ((uintptr_t)q_logits % es))) return SV_ERR_ARG;
-  const size_t need = ws_bytes(B, gamma_max, V, dtype);
+  const int RS = 2 * gamma_max + 1;
+  const size_t need = ws_bytes(B, gamma_max, V, dtype, RS);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256)) return SV_ERR_WORKSPACE;
-  const Plan pl = plan(B, gamma_max, V, dtype);
-  const long long rows = (long long)B * (2 * gamma_max + 1);
+  const Plan pl = plan(B, RS, V, dtype);
+  const long long rows = (long long)B * RS;
   const long long units = rows * pl.NP;
   const long long sel_grid = (units + K1_WAVES - 1) / K1_WAVES;
   const long long list_grid = ((long long)B + K1_NT - 1) / K1_NT;
@@ -251,10 +254,11 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
                          (!q_logits || (uintptr_t)q_logits % 16 == 0);
   int vb = 0;
   while ((1LL << vb) < (long long)V + 1) ++vb;
-  const Layout Lw = layout(B, gamma_max, pl);
+  const Layout Lw = layout(B, gamma_max, RS, pl);
   char* ws = (char*)workspace;
   Args a;
   memset(&a, 0, sizeof a);
+  a.RS = RS;
   a.p = p_logits;
   a.q = q_logits;
   a.draft = draft_tokens;
@@ -311,13 +315,13 @@ using namespace sv;
 
 extern "C" size_t spec_verify_workspace_bytes(int B, int gamma_max, int V, int dtype) {
   if (!sizes_ok(B, gamma_max, V)) return 0;
-  return ws_bytes(B, gamma_max, V, dtype);
+  return ws_bytes(B, gamma_max, V, dtype, 2 * gamma_max + 1);
 }
 
 extern "C" int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
                                           int dtype, void* stream) {
   if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
-  return ws_init(workspace, workspace_bytes, B, gamma_max, V, dtype, stream);
+  return ws_init(workspace, workspace_bytes, B, gamma_max, V, dtype, 2 * gamma_max + 1, stream);
 }
 
 extern "C" int spec_verify_ex(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
@@ -344,11 +348,22 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
                         workspace_bytes, stream);
 }
 
-extern "C" size_t spec_sample_workspace_bytes(int R, int V, int dtype) { return ws_bytes(R, 0, V, dtype); }
+extern "C" size_t spec_sample_workspace_bytes(int R, int V, int dtype) { return ws_bytes(R, 0, V, dtype, 1); }
 
 extern "C" int spec_sample_workspace_init(void* workspace, size_t workspace_bytes, int R, int V, int dtype,
                                           void* stream) {
-  return ws_init(workspace, workspace_bytes, R, 0, V, dtype, stream);
+  return ws_init(workspace, workspace_bytes, R, 0, V, dtype, 1, stream);
+}
+
+extern "C" size_t spec_verify_gumbel_workspace_bytes(int B, int gamma_max, int V, int dtype) {
+  if (B < 0 || gamma_max < 0) return 0;
+  return ws_bytes(B, gamma_max, V, dtype, gamma_max + 1);
+}
+
+extern "C" int spec_verify_gumbel_workspace_init(void* workspace, size_t workspace_bytes, int B, int gamma_max, int V,
+                                                 int dtype, void* stream) {
+  if (B < 0 || gamma_max < 0) return SV_ERR_ARG;
+  return ws_init(workspace, workspace_bytes, B, gamma_max, V, dtype, gamma_max + 1, stream);
 }
 
 extern "C" int spec_sample(const void* logits, int dtype, const float* uniforms, const float* temperature,
@@ -365,14 +380,33 @@ extern "C" int spec_sample(const void* logits, int dtype, const float* uniforms,
 namespace sv {
 
 template <typename ET, bool VECTOR>
-static hipError_t launch_gumbel(const Args& a, hipStream_t st) {
+static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t st) {
   hipError_t e;
+  static int attr_dev[64];   // 1 + device ordinal once the list kernel's LDS limit is raised
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && attr_dev[dev] != dev + 1) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<ET>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
+    if (e != hipSuccess) return e;
+    attr_dev[dev] = dev + 1;
+  }
+  // 1. Streaming select over the target rows of argmax / top-k sequences.
+  if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)sel_grid), dim3(K1_NT), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
+  // 2. Their per-position argmax from the survivor lists.
+  hipLaunchKernelGGL((gumbel_list_kernel<ET>), dim3((unsigned)a.B), dim3(NT), sizeof(FinSmem), st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 3. Dense and demoted sequences, one workgroup per (sequence, position).
   if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((gumbel_kernel<ET, GUMBEL_NT, VECTOR>), dim3((unsigned)((long long)a.B * (a.G + 1))),
                      dim3(GUMBEL_NT), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = stage_mark(SV_KERNEL_GUMBEL, false, st)) != hipSuccess) return e;
+  // 4. The first disagreement and the outputs.
   hipLaunchKernelGGL(gumbel_finish_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -383,18 +417,28 @@ static hipError_t launch_gumbel(const Args& a, hipStream_t st) {
 static int run_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
                       const int32_t* gamma_len, const float* temperature, const int32_t* top_k, const float* top_p,
                       int B, int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_target,
-                      void* stream, int sampler) {
+                      void* workspace, size_t workspace_bytes, void* stream, int sampler) {
   if (!p_logits || !noise || !temperature || !out_tokens || !out_target) return SV_ERR_ARG;
   if (!sampler && (!draft_tokens || !out_n_accepted)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
   if (((uintptr_t)p_logits % es) || ((uintptr_t)noise % 4)) return SV_ERR_ARG;
-  if ((long long)B * (gamma_max + 1) > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
+  const int RS = gamma_max + 1;
+  const size_t need = ws_bytes(B, gamma_max, V, dtype, RS);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256)) return SV_ERR_WORKSPACE;
+  if ((long long)B * RS > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
+  const Plan pl = plan(B, RS, V, dtype);
+  const long long units = (long long)B * RS * pl.NP;
+  const long long sel_grid = (units + K1_WAVES - 1) / K1_WAVES;
+  if (sel_grid > 0x7FFFFFFFLL) return SV_ERR_UNSUPPORTED;
   const int vec = dtype == SV_BF16 ? 8 : 4;
   const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)noise % 16 == 0);
   int vb = 0;
   while ((1LL << vb) < (long long)V + 1) ++vb;
+  const Layout Lw = layout(B, gamma_max, RS, pl);
+  char* ws = (char*)workspace;
   Args a;
   memset(&a, 0, sizeof a);
+  a.RS = RS;
   a.p = p_logits;
   a.draft = draft_tokens;
   a.gamma_len = sampler ? nullptr : gamma_len;
@@ -405,15 +449,23 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   a.B = B;
   a.G = gamma_max;
   a.V = V;
+  a.NP = pl.NP;
+  a.PL = pl.PL;
   a.fixbits = 62 - vb;
   a.out_tokens = out_tokens;
   a.out_n = out_n_accepted;
   a.noise = noise;
   a.out_target = out_target;
+  a.seq_flags = reinterpret_cast<uint32_t*>(ws + Lw.seq_flags_off);
+  a.counts = reinterpret_cast<int32_t*>(ws + Lw.counts_off);
+  a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);
+  a.sel_blocks = sel_grid;   // no dense-pair listing here
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (dtype == SV_BF16) e = vector_ok ? launch_gumbel<uint16_t, true>(a, st) : launch_gumbel<uint16_t, false>(a, st);
-  else e = vector_ok ? launch_gumbel<float, true>(a, st) : launch_gumbel<float, false>(a, st);
+  if (dtype == SV_BF16)
+    e = vector_ok ? launch_gumbel<uint16_t, true>(a, sel_grid, st) : launch_gumbel<uint16_t, false>(a, sel_grid, st);
+  else
+    e = vector_ok ? launch_gumbel<float, true>(a, sel_grid, st) : launch_gumbel<float, false>(a, sel_grid, st);
   if (e != hipSuccess) {
     snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(e));
     return SV_ERR_HIP;
@@ -428,24 +480,25 @@ using namespace sv;
 extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
                                   const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
                                   const float* top_p, int B, int gamma_max, int V, int32_t* out_tokens,
-                                  int32_t* out_n_accepted, int32_t* out_target, void* stream) {
+                                  int32_t* out_n_accepted, int32_t* out_target, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
   if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
   if (B == 0) return SV_OK;
   return run_gumbel(p_logits, dtype, noise, draft_tokens, gamma_len, temperature, top_k, top_p, B, gamma_max, V,
-                    out_tokens, out_n_accepted, out_target, stream, 0);
+                    out_tokens, out_n_accepted, out_target, workspace, workspace_bytes, stream, 0);
 }
 
 extern "C" int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const float* temperature,
                                   const int32_t* top_k, const float* top_p, int R, int V, int32_t* out_tokens,
-                                  void* stream) {
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
   if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (R < 0 || V < 1) return SV_ERR_ARG;
   if (R == 0) return SV_OK;
   return run_gumbel(logits, dtype, noise, nullptr, nullptr, temperature, top_k, top_p, R, 0, V, out_tokens, nullptr,
-                    out_tokens, stream, 1);
+                    out_tokens, workspace, workspace_bytes, stream, 1);
 }
 
 namespace sv {
@@ -541,7 +594,7 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 6; }
+extern "C" int spec_verify_version(void) { return 7; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;

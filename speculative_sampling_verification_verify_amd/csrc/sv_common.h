@@ -33,6 +33,7 @@ struct Args {
   const int32_t* topk;
   const float* topp;
   int B, G, V;
+  int RS;             // logit rows per sequence in the list layout: 2G+1 (verify), G+1 (shared noise)
   int NP;             // parts per logit row (streaming select)
   int PL;             // part length in elements (a multiple of the vector width)
   int fixbits;        // fixed-point fraction bits for mass sums

@@ -683,7 +683,7 @@ __device__ __forceinline__ int dense_draw(const Args& a, FinSmem& s, int b, cons
 // ===========================================================================
 template <typename ET, bool VECTOR>
 __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
-  const int RS = 2 * a.G + 1;
+  const int RS = a.RS;
   const int G = a.G;
   const float* ub = a.u + (size_t)b * (G + 1);
   const int32_t* xb = a.draft + (size_t)b * G;

@@ -21,6 +21,7 @@
 #pragma once
 
 #include "sv_pair.h"
+#include "sv_finish.h"
 
 namespace sv {
 
@@ -47,6 +48,12 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
   const int gl = a.gamma_len ? a.gamma_len[b] : a.G;
   const int g = min(max(gl, 1), a.G);
   if (j > g) return;                          // padding: the finisher writes it
+  {
+    // Argmax and top-k sequences belong to the list path unless their lists
+    // were demoted (overflow) by the select or the list kernel.
+    const Mode sm = seq_mode(a, b);
+    if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE)) return;
+  }
   int32_t* outp = a.out_target + (size_t)b * G1 + j;
   const float Tv = a.temp[b];
   const int k = a.topk ? a.topk[b] : 0;
@@ -104,8 +111,8 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
     const float z = T::val(raw);
     bad |= z < INFINITY ? 0u : 1u;
     kmax = max(kmax, T::key(raw));
-    if (use_noise) bad |= fabsf(noise) < INFINITY ? 0u : 1u;
     if (z >= zthr) {
+      if (use_noise) bad |= fabsf(noise) < INFINITY ? 0u : 1u;   // noise on the support only
       const float tg = Tv * noise;
       const float sc = use_noise ? z + tg : z;
       const uint32_t sk = score_key(sc);
@@ -146,6 +153,94 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
     *outp = (bad || kmax <= Key<ET>::NEG_INF || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
 }
 
+// Argmax and top-k (<= KMAX_SPARSE) sequences from the streaming select's
+// survivor lists: one workgroup per sequence.  Every row's kept set (the
+// union of its part lists cut to the k-th largest, then to the nucleus when
+// top_p < 1) is built in LDS as by the verify's finisher; one wavefront per
+// row then takes the lowest-id argmax of fl(z + fl(T * g)) over it, reading
+// the noise only at the kept ids.  Sequences whose lists do not fit are
+// marked demoted and left to gumbel_kernel, which runs next.
+template <typename ET>
+__global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char gl_smem[];
+  FinSmem& s = *reinterpret_cast<FinSmem*>(gl_smem);
+  const int b = blockIdx.x;
+  const Mode m = seq_mode(a, b);
+  if (m.mode != MODE_GREEDY && m.mode != MODE_SPARSE) return;
+  const uint32_t fl = a.seq_flags[b];
+  if (fl & F_DEMOTE) return;
+  const int G = a.G, RS = a.RS, V = a.V;
+  const int R = m.g + 1;
+  const int NS = R * a.NP;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int32_t* tgt = a.out_target + (size_t)b * (G + 1);
+  if (fl & F_BAD) {
+    for (int j = threadIdx.x; j < R; j += NT) tgt[j] = GUMBEL_BAD_ROW;
+    return;
+  }
+  if (NS > MAXSEG) {
+    if (threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
+    return;
+  }
+  uint32_t c = 0;
+  if ((int)threadIdx.x < NS) c = (uint32_t)max(a.counts[(size_t)b * RS * a.NP + threadIdx.x], 0);
+  uint32_t total = 0;
+  const uint32_t excl = block_excl_scan(c, s.red_u, &total);
+  if (total > (uint32_t)POOL) {
+    if (threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
+    return;
+  }
+  if ((int)threadIdx.x < NS) s.soff[threadIdx.x] = excl;
+  if (threadIdx.x == 0) s.soff[NS] = total;
+  __syncthreads();
+  for (int r = threadIdx.x; r <= R; r += NT) s.off[r] = s.soff[r * a.NP];
+  for (uint32_t e = threadIdx.x; e < total; e += NT) {
+    int lo = 0, hi = NS;   // list with soff[lo] <= e < soff[lo+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s.soff[mid] <= e) lo = mid;
+      else hi = mid;
+    }
+    const int r = lo / a.NP, p = lo - r * a.NP;
+    s.pool[e] = a.lists[list_index(a, b * RS + r, p) + (e - s.soff[lo])];
+  }
+  __syncthreads();
+  for (int r = wave; r < R; r += NWAVE) {
+    if (s.off[r + 1] > s.off[r]) pool_row_stats<ET>(s, r, m, a.NP);
+  }
+  __syncthreads();
+  for (int r = wave; r < R; r += NWAVE) {
+    int32_t tok;
+    if (s.off[r + 1] == s.off[r]) {
+      tok = GUMBEL_BAD_ROW;   // no finite logit
+    } else if (m.mode == MODE_GREEDY) {
+      tok = (int32_t)s.st_arg[r];
+    } else {
+      const int o = (int)s.off[r], n = (int)s.st_cnt[r];
+      const float* gn = a.noise + ((size_t)b * (G + 1) + r) * (size_t)V;
+      uint32_t bkey = 0, bid = NONE, bad = 0;
+      for (int j = lane; j < n; j += 64) {
+#pragma clang fp contract(off)
+        const uint2 e = s.pool[o + j];
+        const float nz = gn[e.y];
+        bad |= fabsf(nz) < INFINITY ? 0u : 1u;
+        const float tg = m.T * nz;
+        const float sc = Key<ET>::value(e.x) + tg;
+        const uint32_t sk = score_key(sc);
+        if (sc == sc && (sk > bkey || (sk == bkey && e.y < bid))) {
+          bkey = sk;
+          bid = e.y;
+        }
+      }
+      const uint32_t best = wave_max_dpp(bkey);
+      const uint32_t id = wave_min_dpp(bkey == best && best != 0u ? bid : NONE);
+      bad = __ballot(bad != 0u) ? 1u : 0u;
+      tok = (bad || id == NONE) ? GUMBEL_BAD_ROW : (int32_t)id;
+    }
+    if (lane == 0) tgt[r] = tok;
+  }
+}
+
 // One wavefront per sequence: validity, the first disagreement between the
 // drafts and the target's samples (one ballot, find-first-set), outputs.
 __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
@@ -176,7 +271,10 @@ __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
     ot[jj] = ok ? (jj < n ? xb[jj] : (jj == n ? tok : -1)) : -1;
     if (!ok || jj > g) tgt[jj] = -1;
   }
-  if (lane == 0 && a.out_n) a.out_n[b] = ok ? n : -1;
+  if (lane == 0) {
+    if (a.out_n) a.out_n[b] = ok ? n : -1;
+    a.seq_flags[b] = 0;
+  }
 }
 
 }  // namespace sv

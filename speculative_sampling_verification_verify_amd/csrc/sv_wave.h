@@ -633,7 +633,7 @@ __global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) v
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   WaveSmem& w = smem[wave];
-  const int RS = 2 * a.G + 1;
+  const int RS = a.RS;
   const long long unit = (long long)blockIdx.x * K1_WAVES + wave;
   const long long rowid_ll = unit / a.NP;
   if (rowid_ll >= (long long)a.B * RS) return;

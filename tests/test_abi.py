@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 6
+    assert binding.spec_verify_version() == 7
 
 
 def test_workspace_bytes():
@@ -88,8 +88,15 @@ def test_gumbel_host_argument_errors():
     nul = None
     B, G, V = 2, 3, 64
 
-    def call(p=fake, dt=binding.SV_BF16, noise=fake, draft=fake, temp=fake, B=B, G=G, V=V, out=fake, tgt=fake):
-        return L.spec_verify_gumbel(p, dt, noise, draft, nul, temp, nul, nul, B, G, V, out, out, tgt, nul)
+    need = binding.lib().spec_verify_gumbel_workspace_bytes(B, G, V, binding.SV_BF16)
+    assert need > 0
+
+    def call(p=fake, dt=binding.SV_BF16, noise=fake, draft=fake, temp=fake, B=B, G=G, V=V, out=fake, tgt=fake,
+             ws=fake, wsb=need):
+        return L.spec_verify_gumbel(p, dt, noise, draft, nul, temp, nul, nul, B, G, V, out, out, tgt, ws, wsb, nul)
+
+    assert call(ws=nul) == binding.SV_ERR_WORKSPACE
+    assert call(wsb=need - 1) == binding.SV_ERR_WORKSPACE
 
     assert call(dt=3) == binding.SV_ERR_UNSUPPORTED
     assert call(G=65) == binding.SV_ERR_UNSUPPORTED
@@ -132,8 +139,10 @@ def test_sample_and_lenient_host_argument_errors():
     assert sample(R=0) == binding.SV_OK
     assert L.spec_sample_workspace_init(nul, 0, R, V, binding.SV_BF16, nul) == binding.SV_ERR_WORKSPACE
 
+    gneed = binding.lib().spec_verify_gumbel_workspace_bytes(R, 0, V, binding.SV_BF16)
+
     def gsample(p=fake, noise=fake, temp=fake, R=R, V=V, out=fake):
-        return L.spec_sample_gumbel(p, binding.SV_BF16, noise, temp, nul, nul, R, V, out, nul)
+        return L.spec_sample_gumbel(p, binding.SV_BF16, noise, temp, nul, nul, R, V, out, fake, gneed, nul)
 
     assert gsample(noise=nul) == binding.SV_ERR_ARG
     assert gsample(out=nul) == binding.SV_ERR_ARG

@@ -20,7 +20,8 @@ def run_gpu_gumbel(gb, dev="cuda:0", pass_gamma=True, with_params=True):
     from speculative_sampling_verification_verify_amd import binding
     P, _ = logits_to_dev(gb.p_logits, dev)
     N = to_dev(np.ascontiguousarray(gb.noise, dtype=np.float32), dev)
-    ver = binding.GumbelVerifier(gb.B, gb.gamma_max, device=dev)
+    ver = binding.GumbelVerifier(gb.B, gb.gamma_max, gb.V, binding.SV_BF16 if gb.p_logits.dtype == np.uint16
+                                 else binding.SV_FP32, device=dev)
     tok, n, tgt = ver(P, N, to_dev(gb.draft, dev), to_dev(gb.temperature, dev),
                       to_dev(gb.top_k, dev) if with_params else None, to_dev(gb.top_p, dev) if with_params else None,
                       to_dev(gb.gamma_len, dev) if pass_gamma else None)
@@ -88,8 +89,9 @@ def test_gumbel_invalid_rows_and_padding():
     T[:] = np.where(T == 0, 1.0, T)
     gl[:] = np.maximum(gl, 2)
     P[0, 1, 17] = 0x7FC0                 # NaN logit
-    N[1, 0, 5] = np.nan                  # NaN noise
-    N[2, 1, 9] = np.inf                  # infinite noise
+    # Bad noise at each row's largest logit, which every processed support holds.
+    N[1, 0, int(np.argmax(oracle.decode_row(P[1, 0])))] = np.nan
+    N[2, 1, int(np.argmax(oracle.decode_row(P[2, 1])))] = np.inf
     d[3, 0] = gb.V                       # token out of range
     T[4] = -1.0                          # negative temperature
     gl[5] = 0                            # gamma_b out of range

@@ -39,9 +39,19 @@ CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc"
 ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
 
 
-def source_hash() -> str:
+# The sources that determine a kernel's code and launch: its own header, the
+# shared device headers and the host file.  A counter summary stays valid
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "select_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_wave.h"),
+    "pair_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h"),
+}
+
+
+def source_hash(kernel: str | None = None) -> str:
+    names = KERNEL_SOURCES.get(kernel) or sorted(os.listdir(CSRC))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(names):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -60,7 +70,7 @@ def traffic_from_profile(kernel: str, workload: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != source_hash():
+    if kv.get("source_hash") != source_hash(kernel):
         return None
     try:
         return float(kv["hbm_read_bytes_per_launch"]) + float(kv["hbm_write_bytes_per_launch"])

@@ -120,7 +120,7 @@ static Layout layout(int B, int G, int RS, const Plan& p) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L.seq_flags_off = 0;
   L.dense_count_off = (size_t)B * 4;
-  L.counters_bytes = up(L.dense_count_off + 4);
+  L.counters_bytes = up(L.dense_count_off + 3 * 4);
   L.pos_off = L.counters_bytes;
   L.dense_list_off = up(L.pos_off + (size_t)B * (G + 1) * sizeof(PosRec));
   L.counts_off = up(L.dense_list_off + (size_t)B * (G + 1) * 4);

@@ -825,7 +825,11 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   if (threadIdx.x == 0) {
     if (a.out_n) a.out_n[b] = ok ? n : -1;
     a.seq_flags[b] = 0;
-    if (b == 0) *a.dense_count = 0;   // the pair kernel has finished with the list
+    if (b == 0) {   // the pair kernel has finished with the list
+      a.dense_count[0] = 0;
+      a.dense_count[1] = 0;
+      a.dense_count[2] = 0;
+    }
   }
   (void)lane;
 }

@@ -718,24 +718,42 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   }
 }
 
-// The dense pairs listed by the select kernel's extra workgroups, taken in
-// turn by a grid sized to what the chip holds at once: when no sequence is
-// dense every workgroup reads the count once and leaves.
+// The dense pairs listed by the select kernel's extra workgroups, run by a
+// grid sized to what the chip holds at once; workgroup w starts with pair w.
+// Streamed pairs are long and few: a workgroup that has finished one takes
+// the next unstarted pair from a shared counter, so the pairs left over after
+// the first round go to the workgroups that finished first (the list puts the
+// cheaper bonus positions last).  Pairs held in LDS are short and many, and a
+// counter taken after each would serialise thousands of atomics on one
+// address: those workgroups step through the list by the grid size.  When no
+// sequence is dense every workgroup reads the counts once and leaves.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
 __global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(LDSR ? 1 : PAIR_STREAM_WAVES_PER_EU)))
 void pair_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char pair_rows[];
   __shared__ PairSmem<NTP> s;
   __shared__ PairExtra<LDSR> ps;
+  __shared__ uint32_t next_pair;
   const int G1 = a.G + 1;
   const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
-  const uint32_t nd = min(*a.dense_count, npairs);
-  for (uint32_t t = blockIdx.x; t < nd; t += gridDim.x) {
-    const int pid = a.dense_list[t];
-    if (pid < 0 || (uint32_t)pid >= npairs) continue;   // never written by this call's listing
-    const int b = pid / G1;
-    pair_one<ET, NTP, VECTOR, LDSR>(a, b, pid - b * G1, s, ps, pair_rows);
+  const uint32_t nf = min(a.dense_count[0], npairs);
+  const uint32_t nd = min(nf + a.dense_count[1], npairs);
+  uint32_t t = blockIdx.x;
+  while (t < nd) {
+    const uint32_t idx = t < nf ? t : npairs - 1u - (t - nf);
+    const int pid = a.dense_list[idx];
+    if (pid >= 0 && (uint32_t)pid < npairs) {   // else never written by this call's listing
+      const int b = pid / G1;
+      pair_one<ET, NTP, VECTOR, LDSR>(a, b, pid - b * G1, s, ps, pair_rows);
+    }
     __syncthreads();   // the next pair reuses the LDS
+    if constexpr (LDSR) {
+      t += gridDim.x;
+    } else {
+      if (threadIdx.x == 0) next_pair = gridDim.x + atomicAdd(&a.dense_count[2], 1u);
+      __syncthreads();
+      t = next_pair;
+    }
   }
 }
 

@@ -602,25 +602,42 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
 // top-k nor argmax exit at once (the finisher takes them whole).
 // ---------------------------------------------------------------------------
 // Workgroups past the streaming ones list the dense sequences' (sequence,
-// position) pairs for the pair kernel, one sequence per thread: each
-// wavefront reserves its pairs' slots with one atomic, so the list order is
-// arbitrary (every pair writes its own result record).
+// position) pairs for the pair kernel, one sequence per thread.  Draft
+// positions (a target and a draft row) fill the list from the front, bonus
+// positions (a target row only, about half the work) from the back, so the
+// pair kernel takes the cheap ones last.  Each wavefront reserves its slots
+// with one atomic per end; the order within an end is arbitrary (every pair
+// writes its own result record).
 __device__ __forceinline__ void list_dense_pairs(const Args& a, long long blk) {
   const int lane = threadIdx.x & 63;
   const long long bl = blk * K1_NT + threadIdx.x;
-  uint32_t c = 0;
+  uint32_t cf = 0, cb = 0;
+  int g = 0;
   if (bl < a.B) {
     const Mode m = seq_mode(a, (int)bl);
-    if (m.mode == MODE_DENSE) c = (uint32_t)m.g + 1u;
+    if (m.mode == MODE_DENSE) {
+      g = m.g;
+      cf = (uint32_t)m.g;
+      cb = 1u;
+    }
   }
-  const uint32_t incl = wave_incl_scan_dpp(c);
-  const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  if (tot == 0) return;
-  uint32_t base = 0;
-  if (lane == 63) base = atomicAdd(a.dense_count, tot);
-  base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
+  const uint32_t inf = wave_incl_scan_dpp(cf);
+  const uint32_t inb = wave_incl_scan_dpp(cb);
+  const uint32_t totf = (uint32_t)__builtin_amdgcn_readlane((int)inf, 63);
+  const uint32_t totb = (uint32_t)__builtin_amdgcn_readlane((int)inb, 63);
+  if (totb == 0) return;   // no dense sequence in this wavefront
+  uint32_t basef = 0, baseb = 0;
+  if (lane == 63) {
+    basef = atomicAdd(&a.dense_count[0], totf);
+    baseb = atomicAdd(&a.dense_count[1], totb);
+  }
+  basef = (uint32_t)__builtin_amdgcn_readlane((int)basef, 63);
+  baseb = (uint32_t)__builtin_amdgcn_readlane((int)baseb, 63);
   const int b = (int)bl;
-  for (uint32_t j = 0; j < c; ++j) a.dense_list[base + incl - c + j] = b * (a.G + 1) + (int)j;
+  const int G1 = a.G + 1;
+  const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
+  for (uint32_t j = 0; j < cf; ++j) a.dense_list[basef + inf - cf + j] = b * G1 + (int)j;
+  if (cb) a.dense_list[npairs - 1u - (baseb + inb - 1u)] = b * G1 + g;
 }
 
 template <typename ET, bool VECTOR>

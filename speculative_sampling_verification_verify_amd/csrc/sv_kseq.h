@@ -12,14 +12,16 @@
 // u_i < a); if all are rejected the output is the inverse-CDF draw over
 // ascending id from the residual at u[k].
 //
-// kseq_node_kernel: one workgroup per (sequence, candidate c, depth j).  The
+// kseq_node_kernel: one workgroup per (depth j, candidate c, sequence).  The
 // node of depth j holds the candidates whose first j tokens equal candidate
 // c's; only the lowest-numbered member of that class (the representative)
 // computes it.  Its rows are P[b][c][j] (target after that prefix) and
 // Q[b][c][j] (draft); depth L is the bonus node, a draw from P[b][c][L] at
 // u[L][0].  Rows of up to 64 KB are held in LDS, longer rows are read from
 // global memory on each pass.  rho* is found by a multi-point bracket
-// search on block reductions of beta(rho) (g(rho) is non-decreasing in rho).
+// search on block reductions of beta(rho) (g(rho) is non-decreasing in rho);
+// once the elements whose ratio p / q lies inside the bracket fit a list in
+// LDS, the search continues on that list alone.
 // spectr_walk_kernel: one thread per sequence follows the output through the
 // nodes: at depth j the node of the current class gives Y; the class shrinks
 // to the candidates whose j-th token is Y; the round ends at the first depth
@@ -33,8 +35,22 @@ namespace sv {
 constexpr int KSEQ_NT = 1024;
 constexpr int KSEQ_MAXK = 64;
 constexpr int KSEQ_NPT = 8;       // points of the rho* bracket evaluated per pass
-constexpr int KSEQ_PASSES = 24;   // bracket passes (each shrinks it (KSEQ_NPT + 1)-fold)
+constexpr int KSEQ_PASSES = 24;   // bracket steps (over the rows: (KSEQ_NPT + 1)-fold, on the list: 65-fold)
+constexpr int KSEQ_NG = 1536;     // listed elements of the bracket (LDS)
+constexpr int KSEQ_UR = 4;        // units per row whose loads a thread issues together on the first pass
 constexpr int32_t KSEQ_BAD = -2;
+
+// x^n for 0 <= n <= 64 by repeated squaring (a few dependent multiplies
+// instead of a general power's logarithm and exponential).
+__device__ __forceinline__ double ipow(double x, int n) {
+  double r = 1.0;
+  while (n) {
+    if (n & 1) r *= x;
+    x *= x;
+    n >>= 1;
+  }
+  return r;
+}
 
 // Inverse-CDF draw over ascending id from per-element weights w(idx, rawp,
 // rawq) >= 0 (block-wide).  Tiles of NTP units: one pass leaves per-(tile,
@@ -135,10 +151,20 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   __shared__ double gred[NTP / 64][KSEQ_NPT];
   __shared__ double rr[KSEQ_NPT], gg[KSEQ_NPT], bb[KSEQ_NPT];
   __shared__ double brk[3];   // lo, hi, beta(hi)
+  __shared__ float glp[KSEQ_NG], glq[KSEQ_NG];   // listed (p, q) of the bracket's elements
+  __shared__ uint32_t gcount;
+  __shared__ double gout[2];  // q mass above the listing bracket, p mass below it
   const int K = a.K, L = a.L, L1 = L + 1;
-  const int b = blockIdx.x / (K * L1);
-  const int rem = blockIdx.x - b * K * L1;
-  const int c = rem / L1, j = rem - (rem / L1) * L1;
+  // Grid order (depth, candidate, sequence): the shallow nodes, where
+  // candidates still share prefixes and the rho* search runs, start first
+  // and the cheap deep and bonus nodes fill in behind them.  The sequence
+  // varies fastest, so the workgroups dealt round-robin to the chip's
+  // partitions mix sequences rather than candidate numbers (the lowest
+  // candidate of a class is its representative, so a candidate-major deal
+  // would pile the work on one partition).
+  const int j = blockIdx.x / (a.B * K);
+  const int rem = blockIdx.x - j * a.B * K;
+  const int c = rem / a.B, b = rem - (rem / a.B) * a.B;
   int32_t* outp = a.node_tok + ((size_t)b * K + c) * L1 + j;
   const int32_t* cb = a.cand + (size_t)b * K * L;
   // The node's class: candidates whose first j tokens equal candidate c's.
@@ -169,50 +195,87 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   }
   const bool bonus = j == L;
   const int V = a.V;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int NU = VECTOR ? V / E : V;
   const U* gp = reinterpret_cast<const U*>(reinterpret_cast<const ET*>(a.p) + (((size_t)b * K + c) * L1 + j) * (size_t)V);
   const U* gq = bonus ? gp : reinterpret_cast<const U*>(reinterpret_cast<const ET*>(a.q) + (((size_t)b * K + c) * L + j) * (size_t)V);
   const float* uj = a.u + ((size_t)b * L1 + j) * (K + 1);
 
   // Pass 1: validity, maxima and (for T = 0) the lowest-id argmax of each
-  // row; rows of up to 64 KB are copied to LDS on the way.
+  // row; rows of up to 64 KB are copied to LDS on the way.  Unfiltered rows
+  // at T > 0 also get their normaliser in this pass: each thread keeps a
+  // running maximum m and the sum of 2^((z - m) c) over its elements,
+  // rescaled when m grows (one exponential per element: 2^(-|z - m| c) is the
+  // new term or the rescale factor), and the block combines the sums at the
+  // row maximum.  Each thread issues the loads of up to KSEQ_UR units per row
+  // before it examines any of them.
   const U* P;
   const U* Q;
+  const bool greedy = Tv == 0.0f;
+  const bool online = !greedy && !(kk > 0 && kk < V) && !(tp < 1.0f);
+  const float cT = greedy ? 1.0f : LOG2E_F / Tv;
   uint32_t bad = 0, kmp = 0, kmq = 0, ip = NONE, iq = NONE;
-  auto scan = [&](const U& u, int ui, uint32_t& km, uint32_t& im) {
+  float mp = -INFINITY, smp = 0.0f, mq = -INFINITY, smq = 0.0f;
+  // The lowest-id argmax is tracked on keys at T = 0 only; otherwise the
+  // running maximum is a float and its key is taken once per thread.
+  auto scan = [&](const U& u, int ui, uint32_t& km, uint32_t& im, float& mo, float& so) {
     T::each(u, [&](int e, uint32_t raw) {
       const float z = T::val(raw);
       bad |= z < INFINITY ? 0u : 1u;
-      const uint32_t kz = T::key(raw);
-      if (kz > km) {
-        km = kz;
-        im = (uint32_t)(ui * E + e);
+      if (greedy) {
+        const uint32_t kz = T::key(raw);
+        if (kz > km) {
+          km = kz;
+          im = (uint32_t)(ui * E + e);
+        }
+      } else if (online) {
+        const float d = (z - mo) * cT;
+        const float ex = z > -INFINITY ? __builtin_amdgcn_exp2f(-fabsf(d)) : 0.0f;
+        so = d > 0.0f ? fmaf(so, ex, 1.0f) : so + ex;
+        mo = fmaxf(mo, z);
+      } else {
+        mo = fmaxf(mo, z);
       }
     });
   };
-  if constexpr (LDSR) {
-    const int nup = (NU * (int)sizeof(U) + 15) / 16 * 16 / (int)sizeof(U);
+  {
     U* lp = reinterpret_cast<U*>(kseq_rows);
-    U* lq = lp + nup;
-    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
-      const U up = gp[ui];
-      lp[ui] = up;
-      scan(up, ui, kmp, ip);
-      if (!bonus) {
-        const U uq = gq[ui];
-        lq[ui] = uq;
-        scan(uq, ui, kmq, iq);
+    U* lq = lp;
+    if constexpr (LDSR) lq = lp + (NU * (int)sizeof(U) + 15) / 16 * 16 / (int)sizeof(U);
+    for (int u0 = 0; u0 < NU; u0 += KSEQ_UR * NTP) {
+      U pu[KSEQ_UR], qu[KSEQ_UR];
+      // Unconditional loads (an index past the row reads its last unit, which
+      // is then skipped) keep all of them in flight together.
+#pragma unroll
+      for (int r = 0; r < KSEQ_UR; ++r) {
+        const int ui = min(u0 + r * NTP + (int)threadIdx.x, NU - 1);
+        pu[r] = gp[ui];
+        qu[r] = gq[ui];
+      }
+#pragma unroll
+      for (int r = 0; r < KSEQ_UR; ++r) {
+        const int ui = u0 + r * NTP + (int)threadIdx.x;
+        if (ui < NU) {
+          if constexpr (LDSR) lp[ui] = pu[r];
+          scan(pu[r], ui, kmp, ip, mp, smp);
+          if (!bonus) {
+            if constexpr (LDSR) lq[ui] = qu[r];
+            scan(qu[r], ui, kmq, iq, mq, smq);
+          }
+        }
       }
     }
-    P = lp;
-    Q = bonus ? lp : lq;
-  } else {
-    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
-      scan(gp[ui], ui, kmp, ip);
-      if (!bonus) scan(gq[ui], ui, kmq, iq);
+    if constexpr (LDSR) {
+      P = lp;
+      Q = bonus ? lp : lq;
+    } else {
+      P = gp;
+      Q = gq;
     }
-    P = gp;
-    Q = gq;
+  }
+  if (!greedy) {   // NaN never enters the float maxima (it marks the row bad)
+    kmp = key_of_value<ET>(mp);
+    kmq = bonus ? 0u : key_of_value<ET>(mq);
   }
   const uint32_t my_kmp = kmp, my_kmq = kmq;
   pb_max3<NTP>(kmp, kmq, bad, s.red_u);   // its barriers also publish the LDS rows
@@ -220,9 +283,11 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
     if (threadIdx.x == 0) *outp = KSEQ_BAD;
     return;
   }
-  const uint32_t argp = pb_min<NTP>(my_kmp == kmp ? ip : NONE, s.red_u);
-  const uint32_t argq = bonus ? 0u : pb_min<NTP>(my_kmq == kmq ? iq : NONE, s.red_u);
-  const bool greedy = Tv == 0.0f;
+  uint32_t argp = 0, argq = 0;
+  if (greedy) {
+    argp = pb_min<NTP>(my_kmp == kmp ? ip : NONE, s.red_u);
+    argq = bonus ? 0u : pb_min<NTP>(my_kmq == kmq ? iq : NONE, s.red_u);
+  }
   Mode m;
   m.g = 1;
   m.mode = MODE_DENSE;
@@ -230,7 +295,25 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   m.T = greedy ? 1.0f : Tv;
   m.tp = tp;
   RowStat sp{}, sq{};
-  if (!greedy) {
+  if (online) {
+    // The threads' sums at the row maxima (a thread that saw no finite
+    // logit holds 0), summed over the block in double.
+    const float zmp = Key<ET>::value(kmp), zmq = bonus ? 0.0f : Key<ET>::value(kmq);
+    const double vp = wave_sum_dpp((double)(smp * __builtin_amdgcn_exp2f((mp - zmp) * cT)));
+    const double vq = bonus ? 0.0 : wave_sum_dpp((double)(smq * __builtin_amdgcn_exp2f((mq - zmq) * cT)));
+    if (lane == 0) {
+      s.part[0][wave] = vp;
+      s.part[1][wave] = vq;
+    }
+    __syncthreads();
+    double Sp = 0.0, Sq = 0.0;
+    for (int w2 = 0; w2 < NTP / 64; ++w2) {
+      Sp += s.part[0][w2];
+      Sq += s.part[1][w2];
+    }
+    sp = RowStat{-INFINITY, zmp, cT, (float)(1.0 / Sp)};
+    sq = bonus ? sp : RowStat{-INFINITY, zmq, cT, (float)(1.0 / Sq)};
+  } else if (!greedy) {
     sp = row_stats<ET, NTP, VECTOR, LDSR>(P, NU, Key<ET>::value(kmp), a, m, kk, s, ps);
     if (!bonus) sq = row_stats<ET, NTP, VECTOR, LDSR>(Q, NU, Key<ET>::value(kmq), a, m, kk, s, ps);
   }
@@ -251,29 +334,83 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   // beta(rho) = sum_x min(q(x), p(x) / rho) and g(rho) = rho beta(rho) -
   // (1 - (1 - beta(rho))^k) at the KSEQ_NPT values rr[] in one pass over the
   // rows (per-thread float sums, block sums in double); results in gg[], bb[].
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  auto g_multi = [&]() {
+  // With gather set, the pass also splits the elements by their ratio
+  // r = p / q against the current bracket [glo, ghi]: r >= ghi contributes q
+  // for every rho in the bracket (summed into gout[0]), r <= glo contributes
+  // p / rho (p summed into gout[1]), and the elements in between are listed
+  // in LDS (up to KSEQ_NG; gcount counts them all).
+  auto g_multi = [&](bool gather, float glo, float ghi) {
     float inv[KSEQ_NPT], acc[KSEQ_NPT];
 #pragma unroll
     for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
       inv[m2] = (float)(1.0 / rr[m2]);
       acc[m2] = 0.0f;
     }
+    float ao = 0.0f, bo = 0.0f;
+    bool glive = gather;   // wavefront-uniform: cleared once the list has overflowed
     for (int ui = threadIdx.x; ui < NU; ui += NTP) {
       const U up = P[ui], uq = Q[ui];
       uint32_t rq[E];
       T::each(uq, [&](int e, uint32_t raw) { rq[e] = raw; });
+      uint32_t inm = 0;   // bit e: element e of the unit lies inside the bracket
       T::each(up, [&](int e, uint32_t raw) {
         const uint32_t idx = (uint32_t)(ui * E + e);
         const float pv = prob_p(idx, raw), qv = prob_q(idx, rq[e]);
 #pragma unroll
         for (int m2 = 0; m2 < KSEQ_NPT; ++m2) acc[m2] += fminf(qv, pv * inv[m2]);
+        if (gather) {
+          const bool above = pv >= qv * ghi, below = !above && pv <= qv * glo;
+          ao += above ? qv : 0.0f;
+          bo += below ? pv : 0.0f;
+          inm |= (!above && !below) ? (1u << e) : 0u;
+        }
       });
+      if (glive) {
+        // One LDS atomic per unit and wavefront: the lanes' counts (<= E <= 8)
+        // are prefix-summed bit by bit over ballots.
+        const uint32_t cnt = (uint32_t)__popc(inm);
+        const unsigned long long below_lane = (1ull << lane) - 1ull;
+        uint32_t pre = 0, tot = 0;
+#pragma unroll
+        for (int bit = 0; bit < 4; ++bit) {
+          const unsigned long long bl = __ballot((cnt >> bit) & 1u);
+          pre += (uint32_t)__popcll(bl & below_lane) << bit;
+          tot += (uint32_t)__popcll(bl) << bit;
+        }
+        if (tot) {
+          const int leader = __ffsll((long long)__ballot(true)) - 1;
+          uint32_t base = 0;
+          if (lane == leader) base = atomicAdd(&gcount, tot);
+          base = (uint32_t)__shfl((int)base, leader, 64);
+          uint32_t slot = base + pre;
+          while (inm) {   // the listed elements again (few once the bracket is narrow)
+            const int e = __builtin_ctz(inm);
+            inm &= inm - 1u;
+            if (slot < (uint32_t)KSEQ_NG) {
+              uint32_t rp = 0, rqe = 0;
+              T::each(up, [&](int e2, uint32_t raw) { rp = e2 == e ? raw : rp; });
+              T::each(uq, [&](int e2, uint32_t raw) { rqe = e2 == e ? raw : rqe; });
+              const uint32_t idx = (uint32_t)(ui * E + e);
+              glp[slot] = prob_p(idx, rp);
+              glq[slot] = prob_q(idx, rqe);
+            }
+            ++slot;
+          }
+          if (base + tot > (uint32_t)KSEQ_NG) glive = false;
+        }
+      }
     }
 #pragma unroll
     for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
       const double w = wave_sum_dpp((double)acc[m2]);
       if (lane == 0) gred[wave][m2] = w;
+    }
+    if (gather) {
+      const double wa = wave_sum_dpp((double)ao), wb = wave_sum_dpp((double)bo);
+      if (lane == 0) {
+        s.part[0][wave] = wa;
+        s.part[1][wave] = wb;
+      }
     }
     __syncthreads();
     if (threadIdx.x < KSEQ_NPT) {
@@ -281,17 +418,61 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
       double bsum = 0.0;
       for (int w2 = 0; w2 < NTP / 64; ++w2) bsum += gred[w2][m2];
       bb[m2] = bsum;
-      gg[m2] = rr[m2] * bsum - (1.0 - pow(1.0 - bsum, (double)k));
+      gg[m2] = rr[m2] * bsum - (1.0 - ipow(1.0 - bsum, k));
+    }
+    if (gather && threadIdx.x == 64) {
+      double sa = 0.0, sb = 0.0;
+      for (int w2 = 0; w2 < NTP / 64; ++w2) {
+        sa += s.part[0][w2];
+        sb += s.part[1][w2];
+      }
+      gout[0] = sa;
+      gout[1] = sb;
     }
     __syncthreads();
   };
-  // rho*: the smallest root of the non-decreasing g on [1, k].  The first
-  // pass tries rho = 1 and spreads the other points up to k; later passes
-  // split the bracket (lo: g < 0, hi: g >= 0) into KSEQ_NPT + 1 parts.
-  if (threadIdx.x < KSEQ_NPT) rr[threadIdx.x] = 1.0 + ((double)k - 1.0) * threadIdx.x / (KSEQ_NPT - 1);
-  __syncthreads();
-  g_multi();
-  double rho = 1.0, beta = bb[0];
+  // One step on the listed elements: 64 points spread over the bracket, one
+  // per lane; wavefront w sums the lane's terms over list entries w, w + 16,
+  // ...; wavefront 0 adds the constant parts, evaluates g and narrows the
+  // bracket to the first sub-interval where g turns non-negative.
+  auto g_list = [&]() {
+    const double lo = brk[0], hi = brk[1];
+    const double rm = lo + (hi - lo) * (double)(lane + 1) / 65.0;
+    const float invm = (float)(1.0 / rm);
+    const uint32_t n = min(gcount, (uint32_t)KSEQ_NG);
+    float acc = 0.0f;
+    for (uint32_t jl = (uint32_t)wave; jl < n; jl += NTP / 64) acc += fminf(glq[jl], glp[jl] * invm);
+    s.part[lane][wave] = (double)acc;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      double bsum = gout[0] + gout[1] / rm;
+      for (int w2 = 0; w2 < NTP / 64; ++w2) bsum += s.part[lane][w2];
+      const double g = rm * bsum - (1.0 - ipow(1.0 - bsum, k));
+      const unsigned long long up = __ballot(g >= 0.0);
+      const int f = up ? __ffsll((long long)up) - 1 : 64;
+      if (lane == f) {
+        brk[1] = rm;
+        brk[2] = bsum;
+      }
+      if (f > 0 && lane == f - 1) brk[0] = rm;
+    }
+    __syncthreads();
+  };
+  // rho*: the smallest root of the non-decreasing g on [1, k].  With one
+  // candidate g(1) = beta - (1 - (1 - beta)) = 0, so rho* = 1, the acceptance
+  // is min(1, p / q) and the residual max(0, p - q): beta is never needed
+  // (P_A / beta = 1 stands for it).  Otherwise the first pass tries rho = 1
+  // and spreads the other points up to k; later passes over the rows split
+  // the bracket (lo: g < 0, hi: g >= 0) into KSEQ_NPT + 1 parts and list the
+  // elements whose ratio lies inside it; once the list holds all of them,
+  // the remaining steps run on the list alone.
+  double rho = 1.0, beta = 1.0;
+  if (k > 1) {
+    if (threadIdx.x < KSEQ_NPT) rr[threadIdx.x] = 1.0 + ((double)k - 1.0) * threadIdx.x / (KSEQ_NPT - 1);
+    __syncthreads();
+    g_multi(false, 0.0f, 0.0f);
+    beta = bb[0];
+  }
   if (k > 1 && gg[0] < 0.0) {
     if (threadIdx.x == 0) {
       double lo = 1.0, hi = (double)k, bhi = bb[KSEQ_NPT - 1];
@@ -308,13 +489,20 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
       brk[2] = bhi;
     }
     __syncthreads();
+    bool listed = false;
     for (int pass = 0; pass < KSEQ_PASSES; ++pass) {
       const double lo = brk[0], hi = brk[1];
       if (!(hi - lo > 1e-15 * hi)) break;          // uniform: every thread reads the same brk
+      if (listed) {
+        g_list();
+        continue;
+      }
       __syncthreads();
       if (threadIdx.x < KSEQ_NPT) rr[threadIdx.x] = lo + (hi - lo) * (threadIdx.x + 1) / (KSEQ_NPT + 1);
+      if (threadIdx.x == 0) gcount = 0;
       __syncthreads();
-      g_multi();
+      g_multi(true, (float)lo, (float)hi);
+      listed = gcount <= (uint32_t)KSEQ_NG;
       if (threadIdx.x == 0) {
         double nlo = lo;
         for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
@@ -332,7 +520,7 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
     rho = brk[1];
     beta = brk[2];
   }
-  const double pacc = 1.0 - pow(1.0 - beta, (double)k);
+  const double pacc = 1.0 - ipow(1.0 - beta, k);
 
   // The candidates in order.
   if (threadIdx.x == 0) {

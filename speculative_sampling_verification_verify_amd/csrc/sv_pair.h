@@ -43,6 +43,7 @@ namespace sv {
 constexpr int PAIR_STREAM_WAVES_PER_EU = 8;
 
 constexpr int PAIR_LDS_ROW_MAX = 65536;   // bytes of one row held in LDS
+constexpr int PAIR_LDS_UR = 4;            // units per row whose loads a thread issues together (rows in LDS)
 constexpr int PAIR_MAXTILE = 64;          // residual tiles (NTP units each) per row
 constexpr int PAIR_NBIN = 2048;           // value bins of the streamed nucleus histogram
 constexpr int PAIR_NCAP = 2048;           // keys of the crossing bin gathered in LDS
@@ -513,36 +514,60 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   const U* gq = resid ? reinterpret_cast<const U*>(row_ptr<ET>(a, b, false, i)) : gp;
 
   // Pass 1: maxima and validity (NaN or +inf makes the pair invalid); the
-  // LDS variant copies the rows on chip as it goes.
+  // LDS variant copies the rows on chip as it goes.  Unfiltered rows also get
+  // their normaliser in this pass: each thread keeps a running maximum m and
+  // the sum of 2^((z - m) c) over its elements, rescaled when m grows (one
+  // exponential per element: 2^(-|z - m| c) is the new term or the rescale
+  // factor); the block combines the sums at the row maximum.
   const U* P;
   const U* Q;
-  float zmp = -INFINITY, zmq = -INFINITY;
+  const bool online = !(k > 0 && k < V) && !(m.tp < 1.0f);
+  const float cT = LOG2E_F / m.T;
+  float zmp = -INFINITY, zmq = -INFINITY, smp = 0.0f, smq = 0.0f;
   uint32_t bad = 0;
-  auto scan_unit = [&](const U& u, float& zm) {
+  auto scan_unit = [&](const U& u, float& zm, float& sm) {
     T::each(u, [&](int, uint32_t raw) {
       const float z = T::val(raw);
-      zm = fmaxf(zm, z);
       bad |= z < INFINITY ? 0u : 1u;
+      if (online) {
+        const float d = (z - zm) * cT;
+        const float ex = z > -INFINITY ? __builtin_amdgcn_exp2f(-fabsf(d)) : 0.0f;
+        sm = d > 0.0f ? fmaf(sm, ex, 1.0f) : sm + ex;
+      }
+      zm = fmaxf(zm, z);
     });
   };
   if constexpr (LDSR) {
+    // Every thread issues the loads of up to PAIR_LDS_UR units of each row
+    // before it examines any: unconditional loads (an index past the row
+    // reads its last unit, which is then skipped) stay in flight together.
     const int nup = (NU * (int)sizeof(U) + 15) / 16 * 16 / (int)sizeof(U);
     U* lp = reinterpret_cast<U*>(pair_rows);
     U* lq = lp + nup;
-    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
-      U up, uq;
-      if constexpr (VECTOR) {
-        up = load_nt(gp + ui);
-        if (resid) uq = load_nt(gq + ui);
-      } else {
-        up = gp[ui];
-        if (resid) uq = gq[ui];
+    for (int u0 = 0; u0 < NU; u0 += PAIR_LDS_UR * NTP) {
+      U pu[PAIR_LDS_UR], qu[PAIR_LDS_UR];
+#pragma unroll
+      for (int r = 0; r < PAIR_LDS_UR; ++r) {
+        const int ui = min(u0 + r * NTP + (int)threadIdx.x, NU - 1);
+        if constexpr (VECTOR) {
+          pu[r] = load_nt(gp + ui);
+          qu[r] = load_nt(gq + ui);
+        } else {
+          pu[r] = gp[ui];
+          qu[r] = gq[ui];
+        }
       }
-      lp[ui] = up;
-      scan_unit(up, zmp);
-      if (resid) {
-        lq[ui] = uq;
-        scan_unit(uq, zmq);
+#pragma unroll
+      for (int r = 0; r < PAIR_LDS_UR; ++r) {
+        const int ui = u0 + r * NTP + (int)threadIdx.x;
+        if (ui < NU) {
+          lp[ui] = pu[r];
+          scan_unit(pu[r], zmp, smp);
+          if (resid) {
+            lq[ui] = qu[r];
+            scan_unit(qu[r], zmq, smq);
+          }
+        }
       }
     }
     P = lp;
@@ -559,13 +584,13 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
       }
 #pragma unroll
       for (int r = 0; r < U1; ++r) {
-        scan_unit(pu[r], zmp);
-        if (resid) scan_unit(qu[r], zmq);
+        scan_unit(pu[r], zmp, smp);
+        if (resid) scan_unit(qu[r], zmq, smq);
       }
     }
     for (; ui < NU; ui += NTP) {
-      scan_unit(gp[ui], zmp);
-      if (resid) scan_unit(gq[ui], zmq);
+      scan_unit(gp[ui], zmp, smp);
+      if (resid) scan_unit(gq[ui], zmq, smq);
     }
     P = gp;
     Q = gq;
@@ -585,9 +610,31 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
     }
     return;
   }
-  const RowStat sp = row_stats<ET, NTP, VECTOR, LDSR>(P, NU, Key<ET>::value(kmp), a, m, k, s, ps);
-  RowStat sq = sp;
-  if (resid) sq = row_stats<ET, NTP, VECTOR, LDSR>(Q, NU, Key<ET>::value(kmq), a, m, k, s, ps);
+  RowStat sp, sq;
+  if (online) {
+    // The threads' sums at the row maxima (a thread that saw no finite
+    // logit holds 0), summed over the block in double.
+    const float zp = Key<ET>::value(kmp), zq = resid ? Key<ET>::value(kmq) : 0.0f;
+    const double vp = wave_sum_dpp((double)(smp * __builtin_amdgcn_exp2f((zmp - zp) * cT)));
+    const double vq = resid ? wave_sum_dpp((double)(smq * __builtin_amdgcn_exp2f((zmq - zq) * cT))) : 0.0;
+    if (lane == 0) {
+      s.part[0][wave] = vp;
+      s.part[1][wave] = vq;
+    }
+    __syncthreads();
+    double Sp = 0.0, Sq = 0.0;
+    for (int w2 = 0; w2 < NW; ++w2) {
+      Sp += s.part[0][w2];
+      Sq += s.part[1][w2];
+    }
+    __syncthreads();   // the weights pass reuses s.part
+    sp = RowStat{-INFINITY, zp, cT, (float)(1.0 / Sp)};
+    sq = resid ? RowStat{-INFINITY, zq, cT, (float)(1.0 / Sq)} : sp;
+  } else {
+    sp = row_stats<ET, NTP, VECTOR, LDSR>(P, NU, Key<ET>::value(kmp), a, m, k, s, ps);
+    sq = sp;
+    if (resid) sq = row_stats<ET, NTP, VECTOR, LDSR>(Q, NU, Key<ET>::value(kmq), a, m, k, s, ps);
+  }
 
   // Overlap and per-(tile, wavefront) sums of the draw weights: the residual
   // max(0, p - q), or p at the bonus position and when the residual is zero.

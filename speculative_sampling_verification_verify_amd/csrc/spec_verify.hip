@@ -525,7 +525,7 @@ static hipError_t launch_spectr(const Args& a, bool ldsr, size_t lds, hipStream_
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = stage_mark(SV_KERNEL_KSEQ, false, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(spectr_walk_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(spectr_walk_kernel, dim3((unsigned)a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

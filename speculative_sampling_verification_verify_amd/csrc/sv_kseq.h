@@ -563,34 +563,46 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   if (threadIdx.x == 0) *outp = tok;
 }
 
-// One thread per sequence: the walk through the nodes.
-__global__ __launch_bounds__(256) void spectr_walk_kernel(Args a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
+// One wavefront per sequence: the walk through the nodes.  The lanes first
+// check the candidates and uniforms and stage the candidates and node
+// outputs in LDS with coalesced loads; the walk then takes one ballot per
+// depth (lane c tests candidate c against the node's output).
+__global__ __launch_bounds__(64) void spectr_walk_kernel(Args a) {
+  __shared__ int32_t cs[SV_MAX_CANDIDATES * SV_MAX_GAMMA];
+  __shared__ int32_t ns[SV_MAX_CANDIDATES * (SV_MAX_GAMMA + 1)];
+  __shared__ int32_t ys[SV_MAX_GAMMA + 1];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
   const int K = a.K, L = a.L, L1 = L + 1, V = a.V;
   const float Tv = a.temp[b];
   const float tp = a.topp ? a.topp[b] : 1.0f;
-  bool ok = Tv >= 0.0f && tp == tp;
   const int32_t* cb = a.cand + (size_t)b * K * L;
-  for (int i = 0; i < K * L && ok; ++i) ok = cb[i] >= 0 && cb[i] < V;
   const float* ub = a.u + (size_t)b * L1 * (K + 1);
-  for (int i = 0; i < L1 * (K + 1) && ok; ++i) ok = ub[i] >= 0.0f && ub[i] < 1.0f;
   const int32_t* nt = a.node_tok + (size_t)b * K * L1;
-  int32_t* ot = a.out_tokens + (size_t)b * L1;
+  bool lane_ok = true;
+  for (int i = lane; i < K * L; i += 64) {
+    const int32_t v = cb[i];
+    cs[i] = v;
+    lane_ok = lane_ok && v >= 0 && v < V;
+  }
+  for (int i = lane; i < K * L1; i += 64) ns[i] = nt[i];
+  for (int i = lane; i < L1 * (K + 1); i += 64) {
+    const float u = ub[i];
+    lane_ok = lane_ok && u >= 0.0f && u < 1.0f;
+  }
+  bool ok = Tv >= 0.0f && tp == tp && __ballot(!lane_ok) == 0ull;
+  __syncthreads();
   unsigned long long alive = K >= 64 ? ~0ull : ((1ull << K) - 1ull);
   int n = L;
-  for (int j = 0; j < L1; ++j) ot[j] = -1;
   for (int j = 0; j < L && ok; ++j) {
     const int rep = __ffsll((long long)alive) - 1;
-    const int y = nt[rep * L1 + j];
+    const int y = ns[rep * L1 + j];
     if (y < 0) {
       ok = false;
       break;
     }
-    ot[j] = y;
-    unsigned long long next = 0ull;
-    for (int c = 0; c < K; ++c)
-      if (((alive >> c) & 1ull) && cb[c * L + j] == y) next |= 1ull << c;
+    if (lane == 0) ys[j] = y;
+    const unsigned long long next = __ballot(lane < K && ((alive >> lane) & 1ull) && cs[lane * L + j] == y);
     if (!next) {
       n = j;
       break;
@@ -598,16 +610,14 @@ __global__ __launch_bounds__(256) void spectr_walk_kernel(Args a) {
     alive = next;
   }
   if (ok && n == L) {
-    const int rep = __ffsll((long long)alive) - 1;
-    const int y = nt[rep * L1 + L];
+    const int y = ns[(__ffsll((long long)alive) - 1) * L1 + L];
     if (y < 0) ok = false;
-    else ot[L] = y;
+    else if (lane == 0) ys[L] = y;
   }
-  if (!ok) {
-    for (int j = 0; j < L1; ++j) ot[j] = -1;
-    n = -1;
-  }
-  a.out_n[b] = n;
+  __syncthreads();
+  int32_t* ot = a.out_tokens + (size_t)b * L1;
+  for (int j = lane; j < L1; j += 64) ot[j] = ok && j <= n ? ys[j] : -1;
+  if (lane == 0) a.out_n[b] = ok ? n : -1;
 }
 
 }  // namespace sv

@@ -681,8 +681,70 @@ __device__ __forceinline__ int dense_draw(const Args& a, FinSmem& s, int b, cons
 // ===========================================================================
 // The finisher kernel: one workgroup per sequence.
 // ===========================================================================
+// A dense sequence whose positions the pair kernel has already resolved:
+// one wavefront reads the records (lane i holds position i), runs the
+// acceptance tests, finds the first rejection by ballot and writes the
+// outputs; the other wavefronts of the workgroup leave at once.
+__device__ __forceinline__ void finish_from_pairs_wave(const Args& a, int b, const Mode& m) {
+  const int lane = threadIdx.x;
+  const int G = a.G, g = m.g;
+  const float* ub = a.u + (size_t)b * (G + 1);
+  const int32_t* xb = a.draft + (size_t)b * G;
+  const PosRec* rec = a.pos + (size_t)b * (G + 1);
+  PosRec r{0.0, 0.0, 0.0, -1, 0u};
+  int32_t xv = 0;
+  float uv = 0.5f;
+  if (lane < g) {
+    r = rec[lane];
+    xv = xb[lane];
+    uv = ub[lane];
+  }
+  const PosRec rb = rec[g];
+  const float ures = ub[G];
+  const uint32_t fl = a.seq_flags[b];
+  const int gl = a.gamma_len ? a.gamma_len[b] : G;
+  const float lv = a.lenience ? a.lenience[b] : 1.0f;
+  bool ok = !(fl & F_BAD) && (a.sampler || (gl >= 1 && gl <= G)) && !(m.tp != m.tp) && lv >= 0.0f && lv <= 1.0f;
+  ok = ok && ures >= 0.0f && ures < 1.0f && !rb.bad;
+  const bool badl = lane < g && (xv < 0 || xv >= a.V || !(uv >= 0.0f && uv < 1.0f) || r.bad);
+  ok = ok && __ballot(badl) == 0ull;
+  const bool rej = lane < g && !((double)uv * (double)lv * r.qx < r.px);
+  const unsigned long long mask = __ballot(rej);
+  const int n = mask ? __ffsll((long long)mask) - 1 : g;
+  const int tn = __shfl(r.tok, n < 64 ? n : 0, 64);
+  const int tok = n < g ? tn : rb.tok;
+  int32_t* ot = a.out_tokens + (size_t)b * (G + 1);
+  float* oa = a.out_alpha + (size_t)b * G;
+  const float qnan = __int_as_float(0x7FC00000);
+  for (int i = lane; i <= G; i += 64) ot[i] = ok ? (i < n ? xv : (i == n ? tok : -1)) : -1;
+  if (lane < G) {
+    oa[lane] = ok ? (lane < g ? (float)r.alpha : 0.0f) : qnan;
+    if (a.out_pq) {
+      float* op = a.out_pq + ((size_t)b * G + lane) * 2;
+      op[0] = ok ? (lane < g ? (float)r.px : 0.0f) : qnan;
+      op[1] = ok ? (lane < g ? (float)r.qx : 0.0f) : qnan;
+    }
+  }
+  if (lane == 0) {
+    if (a.out_n) a.out_n[b] = ok ? n : -1;
+    a.seq_flags[b] = 0;
+    if (b == 0) {   // the pair kernel has finished with the list
+      a.dense_count[0] = 0;
+      a.dense_count[1] = 0;
+      a.dense_count[2] = 0;
+    }
+  }
+}
+
 template <typename ET, bool VECTOR>
 __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
+  {
+    const Mode m = seq_mode(a, b);
+    if (a.pair && m.mode == MODE_DENSE) {   // block-uniform; no block barrier follows
+      if (threadIdx.x < 64) finish_from_pairs_wave(a, b, m);
+      return;
+    }
+  }
   const int RS = a.RS;
   const int G = a.G;
   const float* ub = a.u + (size_t)b * (G + 1);

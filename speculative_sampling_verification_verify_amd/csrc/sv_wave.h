@@ -47,6 +47,19 @@ struct WaveSmem {
   } h;
 };
 
+// Wavefront priority from the work left (left of total steps, both
+// wavefront-uniform): the issue arbiter favours older wavefronts, so without
+// this the first-launched ones finish their parts long before the
+// last-launched ones and the memory system idles in the tail.  A wavefront
+// with more of its part left ranks higher (the four priority levels).
+__device__ __forceinline__ void progress_prio(int left, int total) {
+  const int q = (left * 4) / total;
+  if (q >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (q == 2) __builtin_amdgcn_s_setprio(2);
+  else if (q == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -428,6 +441,7 @@ __device__ __forceinline__ void unit_select(WaveSmem& w, const ET* rp, int e0, i
   __builtin_amdgcn_sched_barrier(0);   // keep A's loads ahead of B's
   B.load(rp, v0 + SPAN, lim, e1);
   for (int s = 0; s < nsteps; s += 2) {
+    progress_prio(nsteps - s, nsteps);
     examine(A, s == 0);
     A.load(rp, v0 + (s + 2) * SPAN, lim, e1);
     examine(B, false);
@@ -585,6 +599,7 @@ __device__ __forceinline__ void unit_select_packed(WaveSmem& w, const uint16_t* 
   // examination into a no-op.  An early exit or a load under a branch would
   // make the compiler wait for both buffers before examining either.
   for (int s = 1; s < nsteps; s += 2) {
+    progress_prio(nsteps - s, nsteps);
     examine(B);
     B.load(rsrc, v0 + (s + 2) * SPAN, lim);
     examine(A);

@@ -57,18 +57,29 @@ struct Plan {
   int PL;     // part length in elements
 };
 
-// Parts per row: enough units to give every SIMD of the chip about four
-// wavefronts (256 CUs x 4 SIMDs x 4), with at least two steps per part.
+// Parts per row: about SV_UNIT_TARGET (row, part) units, with at least
+// SV_MIN_STEPS steps per part.  A part costs a fixed start (certifying the
+// first bound) and end (exact select, list write) besides its stream, and
+// every part's kept set goes to the finisher's pool, so parts stay long:
+// measured at B = 64, V = 128256, gamma = 4, top-k 50, 3 parts per row
+// (1728 units) beat 6 and 7 (55 against 59-60 us per call); the shared-noise
+// verify at the same shapes (320 rows) was fastest at 6 parts (1920 units).
 // RS: logit rows per sequence in the list layout (2G+1 for the verify, G+1
 // for the shared-noise verify, whose draft rows are not inputs).
+#ifndef SV_UNIT_TARGET
+#define SV_UNIT_TARGET 2048
+#endif
+#ifndef SV_MIN_STEPS
+#define SV_MIN_STEPS 2
+#endif
 static Plan plan(int B, int RS, int V, int dtype) {
   const int vec = dtype == SV_BF16 ? 8 : 4;
   const int step = 64 * WVPL * vec;
   const long long R = (long long)B * RS;
-  long long np = R > 0 ? 4096 / R : 1;
+  long long np = R > 0 ? SV_UNIT_TARGET / R : 1;
   np = np < 1 ? 1 : np;
   np = np > MAXNP ? MAXNP : np;
-  const long long by_len = V / (2 * step);
+  const long long by_len = V / ((long long)SV_MIN_STEPS * step);
   if (np > by_len) np = by_len < 1 ? 1 : by_len;
   Plan p;
   int pl = (int)((V + np - 1) / np);

@@ -73,3 +73,12 @@ def test_spectr_duplicates_and_invalid():
     tok, n, ref = check_spectr(sb2, "duplicates-invalid")
     assert (n[1:5] == -1).all() and (tok[1:5] == -1).all()
     assert n[0] >= 0 and n[5] >= 0
+
+
+def test_spectr_bench_shape_sampled():
+    """The benchmark's shape and launch (B = 32, K = 8, L = 8, V = 32000, bf16,
+    T = 0.8), every sequence checked against the oracle (the candidates of a
+    close drafter share prefixes, so the rho* search with its LDS list runs at
+    the shallow nodes)."""
+    sb = synth.make_spectr_batch(32, 8, 8, 32000, dtype="bf16", temperature=0.8)
+    check_spectr(sb, "bench-shape")

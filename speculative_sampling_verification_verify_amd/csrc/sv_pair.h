@@ -379,20 +379,15 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
     for (int i = threadIdx.x; i < PAIR_NBIN; i += NTP) ps.vh[i] = 0ull;
     if (threadIdx.x == 0) ps.ncol = 0;
     __syncthreads();
-    unsigned long long sl = 0;
     each([&](uint32_t raw) {
       const float z = T::val(raw);
       if (z >= zthr) {
         const float e = ew(z, zmax, c);
         const unsigned long long f = fixq(e, two_fb, two_fb32);
-        if (f) {
-          sl += f;
-          atomicAdd(&ps.vh[vbin(e)], f);
-        }
+        if (f) atomicAdd(&ps.vh[vbin(e)], f);
       }
     });
-    S = pb_sum_u64<NTP>(sl, s.red_u64);   // its barriers also publish vh
-    const double tau = (double)m.tp * (double)S;
+    __syncthreads();   // publishes vh
     if (threadIdx.x < 64) {
       constexpr int PER = PAIR_NBIN / 64;
       const int lane = threadIdx.x;
@@ -406,6 +401,13 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
         const uint32_t uhi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), o, 64);
         if (lane >= o) incl += ((unsigned long long)uhi << 32) | ulo;
       }
+      // Every nonzero mass (e >= 2^-fb >= 2^-62) lands in a bin (bin <= 1984),
+      // so the bins' total, lane 63's prefix, is the exact normaliser S.
+      const unsigned long long Sw =
+          ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(incl >> 32), 63) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
+      if (lane == 0) s.red_u64[0] = Sw;
+      const double tau = (double)m.tp * (double)Sw;
       const unsigned long long any = __ballot((double)incl >= tau);
       const int first = any ? __ffsll((long long)any) - 1 : 63;
       if (lane == first) {
@@ -439,6 +441,8 @@ __device__ __forceinline__ RowStat row_stats(const typename PT<ET, VECTOR>::U* s
       }
     }
     __syncthreads();
+    S = s.red_u64[0];
+    const double tau = (double)m.tp * (double)S;
     const uint32_t klo = s.bc[5], khi = s.bc[6];
     const unsigned long long above = (unsigned long long)__double_as_longlong(s.bd[0]);
     const unsigned long long hbin = (unsigned long long)__double_as_longlong(s.bd[1]);

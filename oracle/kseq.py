@@ -27,6 +27,13 @@ Readings where the page leaves a step open:
   non-positive at rho = 1 and non-negative at rho = k, so the roots form an
   interval; the page's "rho >= rho* is valid, and rho* maximises the direct
   acceptance" picks its left end.  Found by bisection (80 halvings).
+* The root is located on the same function written without cancellation:
+  as p sums to 1, 1 - rho beta(rho) = sum max(0, p - rho q) =: D(rho), so
+  rho beta - (1 - (1 - beta)^k) = (1 - beta)^k - D(rho).  For large k the
+  term (1 - beta)^k falls below 1e-16 while rho beta - 1 can only be formed
+  to about 1e-16; D is a sum of non-negative terms, exactly 0 once every
+  element is saturated (rho q >= p), so the sign is never decided by
+  rounding.
 * The acceptance test is strict, u_i < a(X_i) (as for the single-candidate
   test); the residual draw is the same inverse CDF over ascending id at the
   residual uniform u_{k+1}, with Z the sum of the clamped residual weights.
@@ -54,11 +61,17 @@ def beta_of(p: np.ndarray, q: np.ndarray, rho: float) -> float:
     return float(np.minimum(q, p / rho).sum())
 
 
+def deficit_of(p: np.ndarray, q: np.ndarray, rho: float) -> float:
+    """D(rho) = sum max(0, p - rho q) = 1 - rho beta(rho) for normalised p."""
+    return float(np.maximum(p - rho * q, 0.0).sum())
+
+
 def rho_star(p: np.ndarray, q: np.ndarray, k: int) -> float:
-    """Smallest rho in [1, k] with rho beta(rho) >= 1 - (1 - beta(rho))^k."""
+    """Smallest rho in [1, k] with rho beta(rho) >= 1 - (1 - beta(rho))^k,
+    i.e. (1 - beta(rho))^k >= D(rho)."""
     def g(rho):
         b = beta_of(p, q, rho)
-        return rho * b - (1.0 - (1.0 - b) ** k)
+        return (1.0 - b) ** k - deficit_of(p, q, rho)
     if k <= 1 or g(1.0) >= 0.0:
         return 1.0
     lo, hi = 1.0, float(k)

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   __shared__ double brk[3];   // lo, hi, beta(hi)
   __shared__ float glp[KSEQ_NG], glq[KSEQ_NG];   // listed (p, q) of the bracket's elements
   __shared__ uint32_t gcount;
-  __shared__ double gout[2];  // q mass above the listing bracket, p mass below it
+  __shared__ double gout[2];  // p and q mass of the elements above the listing bracket
   const int K = a.K, L = a.L, L1 = L + 1;
   // Grid order (depth, candidate, sequence): the shallow nodes, where
   // candidates still share prefixes and the rho* search runs, start first
@@ -331,19 +331,24 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
     return;
   }
 
-  // beta(rho) = sum_x min(q(x), p(x) / rho) and g(rho) = rho beta(rho) -
-  // (1 - (1 - beta(rho))^k) at the KSEQ_NPT values rr[] in one pass over the
-  // rows (per-thread float sums, block sums in double); results in gg[], bb[].
+  // The root condition rho beta(rho) >= 1 - (1 - beta(rho))^k is evaluated
+  // without cancellation: with D(rho) = sum_x max(0, p(x) - rho q(x)) =
+  // 1 - rho beta(rho), it reads (1 - beta)^k >= D, and beta = (1 - D) / rho.
+  // For large k, (1 - beta)^k drops below the rounding of rho beta - 1 near
+  // the root, whereas D is a sum of non-negative terms that is exactly 0 once
+  // every element is saturated (rho q >= p).  g(rho) = (1 - beta)^k - D at
+  // the KSEQ_NPT values rr[] in one pass over the rows (per-thread float
+  // sums, block sums in double); results in gg[], bb[] (beta).
   // With gather set, the pass also splits the elements by their ratio
-  // r = p / q against the current bracket [glo, ghi]: r >= ghi contributes q
-  // for every rho in the bracket (summed into gout[0]), r <= glo contributes
-  // p / rho (p summed into gout[1]), and the elements in between are listed
+  // r = p / q against the current bracket [glo, ghi]: r >= ghi contributes
+  // p - rho q for every rho in the bracket (p summed into gout[0], q into
+  // gout[1]), r <= glo contributes 0, and the elements in between are listed
   // in LDS (up to KSEQ_NG; gcount counts them all).
   auto g_multi = [&](bool gather, float glo, float ghi) {
-    float inv[KSEQ_NPT], acc[KSEQ_NPT];
+    float rf[KSEQ_NPT], acc[KSEQ_NPT];
 #pragma unroll
     for (int m2 = 0; m2 < KSEQ_NPT; ++m2) {
-      inv[m2] = (float)(1.0 / rr[m2]);
+      rf[m2] = (float)rr[m2];
       acc[m2] = 0.0f;
     }
     float ao = 0.0f, bo = 0.0f;
@@ -357,11 +362,11 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
         const uint32_t idx = (uint32_t)(ui * E + e);
         const float pv = prob_p(idx, raw), qv = prob_q(idx, rq[e]);
 #pragma unroll
-        for (int m2 = 0; m2 < KSEQ_NPT; ++m2) acc[m2] += fminf(qv, pv * inv[m2]);
+        for (int m2 = 0; m2 < KSEQ_NPT; ++m2) acc[m2] += fmaxf(fmaf(-rf[m2], qv, pv), 0.0f);
         if (gather) {
           const bool above = pv >= qv * ghi, below = !above && pv <= qv * glo;
-          ao += above ? qv : 0.0f;
-          bo += below ? pv : 0.0f;
+          ao += above ? pv : 0.0f;
+          bo += above ? qv : 0.0f;
           inm |= (!above && !below) ? (1u << e) : 0u;
         }
       });
@@ -415,10 +420,11 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
     __syncthreads();
     if (threadIdx.x < KSEQ_NPT) {
       const int m2 = threadIdx.x;
-      double bsum = 0.0;
-      for (int w2 = 0; w2 < NTP / 64; ++w2) bsum += gred[w2][m2];
+      double dsum = 0.0;
+      for (int w2 = 0; w2 < NTP / 64; ++w2) dsum += gred[w2][m2];
+      const double bsum = (1.0 - dsum) / rr[m2];
       bb[m2] = bsum;
-      gg[m2] = rr[m2] * bsum - (1.0 - ipow(1.0 - bsum, k));
+      gg[m2] = ipow(1.0 - bsum, k) - dsum;
     }
     if (gather && threadIdx.x == 64) {
       double sa = 0.0, sb = 0.0;
@@ -438,16 +444,17 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   auto g_list = [&]() {
     const double lo = brk[0], hi = brk[1];
     const double rm = lo + (hi - lo) * (double)(lane + 1) / 65.0;
-    const float invm = (float)(1.0 / rm);
+    const float rmf = (float)rm;
     const uint32_t n = min(gcount, (uint32_t)KSEQ_NG);
     float acc = 0.0f;
-    for (uint32_t jl = (uint32_t)wave; jl < n; jl += NTP / 64) acc += fminf(glq[jl], glp[jl] * invm);
+    for (uint32_t jl = (uint32_t)wave; jl < n; jl += NTP / 64) acc += fmaxf(fmaf(-rmf, glq[jl], glp[jl]), 0.0f);
     s.part[lane][wave] = (double)acc;
     __syncthreads();
     if (threadIdx.x < 64) {
-      double bsum = gout[0] + gout[1] / rm;
-      for (int w2 = 0; w2 < NTP / 64; ++w2) bsum += s.part[lane][w2];
-      const double g = rm * bsum - (1.0 - ipow(1.0 - bsum, k));
+      double dsum = fmax(gout[0] - rm * gout[1], 0.0);
+      for (int w2 = 0; w2 < NTP / 64; ++w2) dsum += s.part[lane][w2];
+      const double bsum = (1.0 - dsum) / rm;
+      const double g = ipow(1.0 - bsum, k) - dsum;
       const unsigned long long up = __ballot(g >= 0.0);
       const int f = up ? __ffsll((long long)up) - 1 : 64;
       if (lane == f) {

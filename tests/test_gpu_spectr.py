@@ -82,3 +82,12 @@ def test_spectr_bench_shape_sampled():
     the shallow nodes)."""
     sb = synth.make_spectr_batch(32, 8, 8, 32000, dtype="bf16", temperature=0.8)
     check_spectr(sb, "bench-shape")
+
+
+@pytest.mark.parametrize("B,K,L,V,dtype", [
+    (3, 64, 2, 500, "bf16"),    # K at its limit: the walk's 64-bit class masks, 64 lanes of candidates
+    (2, 2, 64, 300, "fp32"),    # L at its limit: 65 depths staged in the walk's LDS
+])
+def test_spectr_size_limits(B, K, L, V, dtype):
+    sb = synth.make_spectr_batch(B, K, L, V, dtype=dtype, seed=300 + K + L, sigma=0.2, temperature=0.9)
+    check_spectr(sb, f"limits-B{B}-K{K}-L{L}-V{V}-{dtype}")

@@ -206,3 +206,28 @@ def test_spectr_first_token_follows_the_target():
         counts[r.tokens[0]] += 1
     pv = stats.chisquare(counts, p1 * N).pvalue
     assert pv > 1e-4, pv
+
+
+def test_rho_star_at_large_k_is_the_saturation_point():
+    """For large k, (1 - beta)^k is below any rounding of rho beta - 1, so
+    the root sits where every element saturates: for rho < r_max =
+    max p/q, D(rho) = sum max(0, p - rho q) >= (r_max - rho) q(x_max) > 0,
+    which exceeds (1 - beta)^k once r_max - rho > (1 - beta)^k / q(x_max).
+    So rho* = r_max to far better than 1e-9 (it is never above r_max: there
+    D = 0 and (1 - beta)^k > 0)."""
+    rng = np.random.default_rng(7)
+    checked = 0
+    for trial in range(20):
+        V = int(rng.integers(50, 600))
+        q = rng.dirichlet(np.ones(V))
+        p = q * np.exp(0.3 * rng.standard_normal(V))
+        p /= p.sum()
+        r_max = float((p / q).max())
+        beta_rmax = kseq.beta_of(p, q, r_max)
+        for k in (48, 64):
+            if (1.0 - beta_rmax) ** k > 1e-15:
+                continue
+            rho = kseq.rho_star(p, q, k)
+            assert abs(rho - r_max) <= 1e-9 * r_max, (trial, k, rho, r_max)
+            checked += 1
+    assert checked >= 10

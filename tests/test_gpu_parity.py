@@ -257,3 +257,23 @@ def test_gpu_tokens_per_round_law():
     sem = (g.n + 1.0).std() / np.sqrt(N)
     log(f"[stat] tokens per round {mean:.4f} vs {expect:.4f} (sem {sem:.4f})")
     assert abs(mean - expect) < 4 * sem
+
+
+def test_largest_vocabulary():
+    """V = 2^20, the largest the ABI takes, one sequence of each kind: argmax,
+    top-k 64 (streaming select, 256-element steps over a 2 MiB row), unfiltered
+    and top-p (rows past the pair kernel's tile table: the finisher's
+    multi-pass path), bf16 and gamma 2."""
+    bt = synth.make_batch(4, B=4, V=1 << 20)
+    w = dataclasses.replace(bt.workload, gamma_max=2)
+    rng = np.random.default_rng(17)
+    B, G, V = 4, 2, 1 << 20
+    zp = (3 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rng.permutation(V))).astype(np.float32)
+    zq = zp[:, :G] + rng.normal(size=(B, G, V)).astype(np.float32) * 0.5
+    draft = np.argmax(zq, axis=2).astype(np.int32)
+    gl = np.array([2, 2, 1, 2], np.int32)
+    T = np.array([0.0, 0.8, 1.0, 1.2], np.float32)
+    k = np.array([0, 64, 0, 0], np.int32)
+    tp = np.array([1.0, 1.0, 1.0, 0.9], np.float32)
+    bt2 = synth.Batch(w, _bf(zp), _bf(zq), draft, synth.uniforms(17, B, G), gl, T, k, tp, 17)
+    check(bt2, "V2^20")

@@ -277,3 +277,25 @@ def test_largest_vocabulary():
     tp = np.array([1.0, 1.0, 1.0, 0.9], np.float32)
     bt2 = synth.Batch(w, _bf(zp), _bf(zq), draft, synth.uniforms(17, B, G), gl, T, k, tp, 17)
     check(bt2, "V2^20")
+
+
+@pytest.mark.parametrize("V", [3000, 30000, 70000])
+def test_extreme_temperatures(V):
+    """Temperatures far from 1 on every path: near-zero T (weights below the
+    float32 range but the maximum, and below the fixed-point resolution), very
+    large T (near-uniform rows, fixed-point masses near their 2^62 bound), with
+    top-k, top-p and unfiltered rows (V = 3000: rows in LDS; 30000: larger LDS
+    rows; 70000: streamed rows)."""
+    rng = np.random.default_rng(V)
+    B, G = 8, 3
+    zp = (3 * rng.normal(size=(B, G + 1, V))).astype(np.float32)
+    zq = zp[:, :G] + rng.normal(size=(B, G, V)).astype(np.float32) * 0.5
+    draft = np.argmax(zq, axis=2).astype(np.int32)
+    draft[1::2, 0] = rng.integers(0, V, size=B // 2)
+    T = np.array([1e-4, 1e-2, 50.0, 1e3, 1e-4, 50.0, 1e-3, 2e3], np.float32)
+    k = np.array([0, 0, 0, 0, 64, 64, 0, 700], np.int32)
+    tp = np.array([1.0, 0.9, 0.9, 1.0, 1.0, 0.5, 0.95, 0.99], np.float32)
+    bt = synth.make_batch(3, B=B, V=V)
+    bt2 = synth.Batch(bt.workload, _bf(zp), _bf(zq), draft, synth.uniforms(V, B, G), np.full(B, G, np.int32),
+                      T, k, tp, V)
+    check(bt2, f"extreme-T-V{V}")

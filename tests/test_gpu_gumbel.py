@@ -169,3 +169,14 @@ def test_gumbel_gpu_samples_follow_target_chi_square():
     pv = stats.chisquare(obs, p * N).pvalue
     log(f"[gumbel] chi-square p-value of the target's samples: {pv:.3g}")
     assert pv > 1e-4
+
+
+def test_gumbel_extreme_temperatures():
+    """T far from 1 in the score fl(z + fl(T g)): near zero (the noise only
+    breaks ties of the maximum) and very large (the noise decides), with and
+    without filters, on the list and dense paths."""
+    gb = synth.make_gumbel_batch(4, B=8, V=20000)
+    T = np.array([1e-4, 1e3, 1e-4, 1e3, 0.02, 200.0, 1e-4, 1e3], np.float32)
+    k = np.array([0, 0, 64, 64, 0, 0, 0, 0], np.int32)
+    tp = np.array([1.0, 1.0, 1.0, 1.0, 0.9, 0.9, 1.0, 1.0], np.float32)
+    check_gumbel(_replace(gb, temperature=T, top_k=k, top_p=tp), "extreme-T")

@@ -91,3 +91,12 @@ def test_spectr_bench_shape_sampled():
 def test_spectr_size_limits(B, K, L, V, dtype):
     sb = synth.make_spectr_batch(B, K, L, V, dtype=dtype, seed=300 + K + L, sigma=0.2, temperature=0.9)
     check_spectr(sb, f"limits-B{B}-K{K}-L{L}-V{V}-{dtype}")
+
+
+def test_spectr_extreme_temperatures():
+    """Near-one-hot (T = 1e-3) and near-uniform (T = 30) processed rows, with
+    and without top-p, in the K-SEQ nodes."""
+    T = np.array([1e-3, 30.0, 1e-3, 30.0, 0.05, 8.0], np.float32)
+    tp = np.array([1.0, 1.0, 0.9, 0.9, 1.0, 0.95], np.float32)
+    sb = synth.make_spectr_batch(6, 6, 3, 4000, dtype="bf16", seed=77, sigma=0.3, temperature=T, top_p=tp)
+    check_spectr(sb, "extreme-T")

@@ -299,3 +299,22 @@ def test_extreme_temperatures(V):
     bt2 = synth.Batch(bt.workload, _bf(zp), _bf(zq), draft, synth.uniforms(V, B, G), np.full(B, G, np.int32),
                       T, k, tp, V)
     check(bt2, f"extreme-T-V{V}")
+
+
+def test_many_sequences():
+    """B = 8192 sequences of one draft over a 257-token vocabulary, every mode
+    (argmax, top-k, top-p, unfiltered): large grids for every kernel and a
+    long dense-pair list."""
+    rng = np.random.default_rng(8192)
+    B, G, V = 8192, 1, 257
+    zp = (2 * rng.normal(size=(B, G + 1, V))).astype(np.float32)
+    zq = zp[:, :G] + rng.normal(size=(B, G, V)).astype(np.float32)
+    draft = np.argmax(zq, axis=2).astype(np.int32)
+    draft[::3, 0] = rng.integers(0, V, size=len(range(0, B, 3)))
+    T = np.tile(np.array([0.0, 0.8, 1.0, 1.3], np.float32), B // 4)
+    k = np.tile(np.array([0, 20, 0, 0], np.int32), B // 4)
+    tp = np.tile(np.array([1.0, 1.0, 0.9, 1.0], np.float32), B // 4)
+    bt = synth.make_batch(0, B=4, V=V)
+    w = dataclasses.replace(bt.workload, gamma_max=G)
+    bt2 = synth.Batch(w, _bf(zp), _bf(zq), draft, synth.uniforms(8192, B, G), np.full(B, G, np.int32), T, k, tp, 8192)
+    check(bt2, "B8192")

@@ -117,3 +117,15 @@ def test_rows_beyond_the_tile_table_use_multipass():
     bt = dense_batch(V, "bf16", B=3, G=2, seed=3, T=np.array([1.0, 0.7, 1.2]),
                      tp=np.array([1.0, 0.9, 0.8], np.float32))
     compare(bt, run_gpu(bt), run_oracle(bt), "multipass-V70001")
+
+
+def test_streamed_pairs_beyond_one_round():
+    """More streamed pairs (200 sequences x 4 positions = 800) than the pair
+    kernel's resident workgroups (512): the leftovers are taken from the shared
+    counter, bonus positions last, by whichever workgroups finish first."""
+    B = 200
+    rng = np.random.default_rng(5)
+    T = rng.choice(np.array([0.6, 1.0, 1.3], np.float32), size=B)
+    tp = rng.choice(np.array([1.0, 0.9], np.float32), size=B)
+    bt = dense_batch(40000, "bf16", B=B, G=3, seed=11, T=T, tp=tp)
+    compare(bt, run_gpu(bt), run_oracle(bt), "streamed-800-pairs")

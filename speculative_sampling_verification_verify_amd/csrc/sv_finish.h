@@ -51,6 +51,7 @@ struct FinSmem {
   double red_d[NWAVE];
   unsigned long long red_u64[NWAVE];
   uint32_t red_u[NWAVE];
+  uint32_t red_or[NWAVE];
   uint32_t bc[8];
   uint32_t flag;
 };
@@ -162,7 +163,7 @@ __device__ __forceinline__ void pool_row_stats(FinSmem& s, int r, const Mode& m,
   }
   const float invT = 1.0f / m.T;
   const float zmax = Key<ET>::value(kmax);
-  n = wave_keep(s, o, n, kth);
+  if (kth > 1u) n = wave_keep(s, o, n, kth);   // kth == 1: every listed (finite) key is kept
   double S = 0.0;
   for (int i = lane; i < n; i += 64) {
     const float e = expf((Key<ET>::value(s.pool[o + i].x) - zmax) * invT);
@@ -788,9 +789,31 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     const int si = used_slot(G, m.g, r) * a.NP + p;
     c = nslot <= MAXSEG ? s.cslot[si] : (uint32_t)max(a.counts[(size_t)b * RS * a.NP + si], 0);
   }
-  uint32_t total = 0;
-  const uint32_t excl = block_excl_scan(c, s.red_u, &total);
-  ok = ok && block_or_u32(badin, s.red_u) == 0;
+  // The list sizes' exclusive scan and the input checks' OR in one LDS round
+  // trip (the barrier after cslot already separates earlier LDS use, and the
+  // one after soff below separates later use).
+  uint32_t total = 0, excl = 0;
+  {
+    const uint32_t incl = wave_incl_scan(c);
+    uint32_t orw = badin;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) orw |= (uint32_t)__shfl_xor((int)orw, o, 64);
+    if (lane == 63) {
+      s.red_u[wave] = incl;
+      s.red_or[wave] = orw;
+    }
+    __syncthreads();
+    uint32_t base = 0, anybad = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVE; ++i) {
+      const uint32_t v = s.red_u[i];
+      base += i < wave ? v : 0u;
+      total += v;
+      anybad |= s.red_or[i];
+    }
+    excl = base + incl - c;
+    ok = ok && anybad == 0;
+  }
   if (ok && !dense) {
     if ((int)threadIdx.x < NS) s.soff[threadIdx.x] = excl;
     if (threadIdx.x == 0) s.soff[NS] = total;
@@ -812,9 +835,12 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       s.pool[e] = a.lists[list_index(a, rowid, p) + (e - s.soff[lo])];
     }
     __syncthreads();
-    uint32_t empty = 0;
-    if ((int)threadIdx.x < R) empty = s.off[threadIdx.x + 1] == s.off[threadIdx.x] ? 1u : 0u;
-    ok = block_or_u32(empty, s.red_u) == 0;   // a row without a finite logit
+    // A row without a finite logit: every wavefront checks all rows itself
+    // (R <= 129 offsets, published by the barrier above), so no block
+    // reduction is needed.
+    bool empty = false;
+    for (int r = lane; r < R; r += 64) empty = empty || s.off[r + 1] == s.off[r];
+    ok = __ballot(empty) == 0ull;
     if (ok) {
       for (int r = wave; r < R; r += NWAVE) pool_row_stats<ET>(s, r, m, a.NP);
       __syncthreads();

@@ -22,10 +22,11 @@
 // search on block reductions of beta(rho) (g(rho) is non-decreasing in rho);
 // once the elements whose ratio p / q lies inside the bracket fit a list in
 // LDS, the search continues on that list alone.
-// spectr_walk_kernel: one thread per sequence follows the output through the
-// nodes: at depth j the node of the current class gives Y; the class shrinks
-// to the candidates whose j-th token is Y; the round ends at the first depth
-// whose output is no candidate, or with the bonus node after depth L.
+// spectr_walk_kernel: one wavefront per sequence (candidates and node outputs
+// staged in LDS) follows the output through the nodes: at depth j the node of
+// the current class gives Y; the class shrinks, by a ballot over the
+// candidates, to those whose j-th token is Y; the round ends at the first
+// depth whose output is no candidate, or with the bonus node after depth L.
 #pragma once
 
 #include "sv_pair.h"

@@ -412,9 +412,10 @@ def main():
                                       t(bt.gamma_len))
     # The sampling settings are known on the host: when no sequence is dense
     # (every one argmax or top-k <= 512) the call says so and the empty
-    # dense-pair launch is skipped.
+    # dense-pair launch is skipped; when every sequence is dense it says that,
+    # and the select launch (which would only list the pairs) is skipped.
     sel_bytes, pair_bytes = kernel_bytes(bt)
-    hints = binding.SV_HINT_NO_DENSE if pair_bytes == 0 else 0
+    hints = binding.SV_HINT_NO_DENSE if pair_bytes == 0 else (binding.SV_HINT_ALL_DENSE if sel_bytes == 0 else 0)
     ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt_code, device=dev, hints=hints)
     # Copies of the logits, rotated step by step, so that a workload smaller
     # than the 256 MB last-level cache is still read from HBM.
@@ -462,7 +463,8 @@ def main():
     other_us = {}
     for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, "pair_kernel"),
                        (binding.SV_KERNEL_FINISH, "finish_kernel")):
-        if kern == binding.SV_KERNEL_PAIR and hints & binding.SV_HINT_NO_DENSE:
+        if (kern == binding.SV_KERNEL_PAIR and hints & binding.SV_HINT_NO_DENSE) or \
+                (kern == binding.SV_KERNEL_SELECT and hints & binding.SV_HINT_ALL_DENSE):
             other_us[name] = None      # not launched
         elif kern != kernel:
             _, ms = timed(kern, min(K, 20))

@@ -123,10 +123,18 @@ int spec_verify(const void* p_logits, const void* q_logits, int dtype,
 
 /* Hints for spec_verify_ex (bit flags). */
 enum {
-  SV_HINT_NO_DENSE = 1   /* the caller knows that every sequence has T == 0 or 0 < top_k <= 512:
+  SV_HINT_NO_DENSE = 1,  /* the caller knows that every sequence has T == 0 or 0 < top_k <= 512:
                             the per-(sequence, position) kernel for dense sequences is not
                             launched.  A dense sequence in such a call still gets its exact
                             result, from a slower one-workgroup-per-sequence path.            */
+  SV_HINT_ALL_DENSE = 2  /* the caller knows that every sequence is dense (T > 0 and top_k <= 0,
+                            top_k >= V or top_k > 512): the top-k selection kernel, whose only
+                            work would be listing the (sequence, position) pairs, is not
+                            launched, and the pair kernel takes them in a fixed order.  A
+                            sequence that is not dense still gets its exact result, from the
+                            same slower path.  Ignored where the pair kernel does not apply
+                            (rows beyond its size limits).  Combined with SV_HINT_NO_DENSE:
+                            SV_ERR_ARG.                                                        */
 };
 
 /*
@@ -139,7 +147,7 @@ enum {
  *
  *  lenience     [B] float in [0, 1], or NULL (all 1).  A value outside [0, 1] or NaN
  *               makes that sequence invalid.
- *  hints        0 or SV_HINT_* flags (unknown bits: SV_ERR_ARG).
+ *  hints        0 or SV_HINT_* flags (unknown bits, or both flags: SV_ERR_ARG).
  * Every other argument, the workspace and the error behaviour are those of
  * spec_verify.
  */
@@ -331,7 +339,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 7. */
+/* ABI version: 8. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

@@ -21,6 +21,7 @@ SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2,
 SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL, SV_KERNEL_KSEQ = 0, 1, 2, 3, 4
 SV_MAX_CANDIDATES = 64
 SV_HINT_NO_DENSE = 1
+SV_HINT_ALL_DENSE = 2
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 

@@ -166,9 +166,11 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     attr_dev[dev] = dev + 1;
   }
   if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.all_dense) {
+    hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   if (a.pair) {
     size_t plds = 0;
@@ -245,7 +247,8 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
                       const int32_t* top_k, const float* top_p, const float* lenience, int hints, int B,
                       int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha,
                       float* out_pq, void* workspace, size_t workspace_bytes, void* stream, int sampler) {
-  if (hints & ~SV_HINT_NO_DENSE) return SV_ERR_ARG;
+  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
+  if ((hints & SV_HINT_NO_DENSE) && (hints & SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
   if (!p_logits || !uniforms || !temperature || !out_tokens) return SV_ERR_ARG;
   if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
@@ -301,6 +304,9 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
   // dense sequence under that hint still gets its exact result from the
   // finisher's multi-pass path.
   if (hints & SV_HINT_NO_DENSE) a.pair = 0;
+  // The promise that every sequence is dense saves the select launch (whose
+  // only work would be the listing); it needs the pair kernel for this V.
+  if ((hints & SV_HINT_ALL_DENSE) && a.pair && !sampler) a.all_dense = 1;
   // Without the pair kernel the dense sequences go to the finisher whole and
   // nothing is listed.
   a.sel_blocks = a.pair ? sel_grid : grid;
@@ -605,7 +611,7 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 7; }
+extern "C" int spec_verify_version(void) { return 8; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;

@@ -50,6 +50,8 @@ struct Args {
   int32_t* dense_list;    // [B * (G+1)] pair ids b * (G+1) + i of the dense sequences
   long long sel_blocks;   // workgroups of the select kernel that stream rows; the rest list dense pairs
   int pair;               // 1 when the pair-resident kernel runs for the dense sequences
+  int all_dense;          // 1: no select launch; the pair kernel takes every (sequence, position) in
+                          // order and the finisher runs non-dense sequences by its multi-pass path
   const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test
   int sampler;            // 1: G == 0 and each "sequence" is one row to sample (no drafts)
   int K, L;               // multi-candidate verify: candidate sequences and their length

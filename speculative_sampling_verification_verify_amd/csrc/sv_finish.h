@@ -773,7 +773,10 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   ok = ok && !(m.tp != m.tp);
   const float lv = a.lenience ? a.lenience[b] : 1.0f;
   ok = ok && lv >= 0.0f && lv <= 1.0f;
-  bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG;
+  // Without the select launch (every sequence promised dense) there are no
+  // survivor lists: a sequence that is not dense after all takes the
+  // multi-pass path.
+  bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG || a.all_dense;
   const bool from_pairs = a.pair && m.mode == MODE_DENSE;
   uint32_t badin = 0;
   if ((int)threadIdx.x < m.g)

@@ -777,7 +777,9 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
 // cheaper bonus positions last).  Pairs held in LDS are short and many, and a
 // counter taken after each would serialise thousands of atomics on one
 // address: those workgroups step through the list by the grid size.  When no
-// sequence is dense every workgroup reads the counts once and leaves.
+// sequence is dense every workgroup reads the counts once and leaves.  When
+// the caller has promised that every sequence is dense there is no list (and
+// no select launch): the pairs are taken in a fixed order instead.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
 __global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(LDSR ? 1 : PAIR_STREAM_WAVES_PER_EU)))
 void pair_kernel(Args a) {
@@ -787,12 +789,24 @@ void pair_kernel(Args a) {
   __shared__ uint32_t next_pair;
   const int G1 = a.G + 1;
   const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
-  const uint32_t nf = min(a.dense_count[0], npairs);
-  const uint32_t nd = min(nf + a.dense_count[1], npairs);
+  const bool direct = a.all_dense != 0;
+  const uint32_t nf = direct ? npairs : min(a.dense_count[0], npairs);
+  const uint32_t nd = direct ? npairs : min(nf + a.dense_count[1], npairs);
+  const uint32_t nlead = (uint32_t)a.B * (uint32_t)a.G;
   uint32_t t = blockIdx.x;
   while (t < nd) {
-    const uint32_t idx = t < nf ? t : npairs - 1u - (t - nf);
-    const int pid = a.dense_list[idx];
+    int pid;
+    if (direct) {
+      // No list: positions 0..G-1 of every sequence in order, then position G
+      // of every sequence (the bonus position of a full-length draft), so the
+      // cheaper pairs still come last; pair_one skips padding positions and
+      // sequences that are not dense.
+      pid = t < nlead ? (int)((t / (uint32_t)a.G) * (uint32_t)G1 + t % (uint32_t)a.G)
+                      : (int)((t - nlead) * (uint32_t)G1 + (uint32_t)a.G);
+    } else {
+      const uint32_t idx = t < nf ? t : npairs - 1u - (t - nf);
+      pid = a.dense_list[idx];
+    }
     if (pid >= 0 && (uint32_t)pid < npairs) {   // else never written by this call's listing
       const int b = pid / G1;
       pair_one<ET, NTP, VECTOR, LDSR>(a, b, pid - b * G1, s, ps, pair_rows);

@@ -129,3 +129,27 @@ def test_streamed_pairs_beyond_one_round():
     tp = rng.choice(np.array([1.0, 0.9], np.float32), size=B)
     bt = dense_batch(40000, "bf16", B=B, G=3, seed=11, T=T, tp=tp)
     compare(bt, run_gpu(bt), run_oracle(bt), "streamed-800-pairs")
+
+
+# ---- the all-dense hint: no select launch, pairs taken in a fixed order --------
+
+@pytest.mark.parametrize("cid,B,V,label", [
+    (1, 8, None, "rows in LDS, 1024 threads (unfiltered bf16, V 32000)"),
+    (0, 64, None, "rows in LDS, 64 threads (fp32, V 1000)"),
+    (1, 4, 70000, "streamed rows (bf16, V 70000)"),
+    (4, 16, 20000, "ragged drafts with argmax sequences: the promise broken"),
+    (2, 4, 20000, "top-k 50 sequences only: the promise broken everywhere"),
+])
+def test_all_dense_hint_matches_oracle(cid, B, V, label):
+    # The hint skips the select launch; the pair kernel then walks every
+    # (sequence, position) itself, and sequences that are not dense after all
+    # go to the finisher's multi-pass path.  Two calls in a row check that
+    # the pair queue counter is left cleared.
+    from speculative_sampling_verification_verify_amd import binding
+    bt = synth.make_batch(cid, B=B, V=V)
+    log(f"all-dense hint: {label}: B={bt.B} V={bt.V} G={bt.gamma_max}")
+    dt = binding.SV_BF16 if bt.p_logits.dtype == np.uint16 else binding.SV_FP32
+    ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt, device="cuda:0", hints=binding.SV_HINT_ALL_DENSE)
+    ref = run_oracle(bt)
+    for call in range(2):
+        compare(bt, run_gpu(bt, verifier=ver), ref, f"all-dense-{label}-call{call}")

@@ -172,8 +172,11 @@ def main_gumbel(args):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     N = t(gb.noise)
     draft, temp, topk, topp, gl = t(gb.draft), t(gb.temperature), t(gb.top_k), t(gb.top_p), t(gb.gamma_len)
+    # With no argmax or small-top-k sequence the call says so (host-side
+    # facts) and the select and list launches are skipped.
+    ghints = binding.SV_HINT_ALL_DENSE if sel_bytes == 0 else 0
     ver = binding.GumbelVerifier(gb.B, gb.gamma_max, gb.V,
-                                 binding.SV_BF16 if dtype_name == "bf16" else binding.SV_FP32, device=dev)
+                                 binding.SV_BF16 if dtype_name == "bf16" else binding.SV_FP32, device=dev, hints=ghints)
     nsets = int(min(32, max(1, -(-ROTATE_BYTES // max(kbytes, 1)))))
     sets = [(P, N)] + [(P.clone(), N.clone()) for _ in range(nsets - 1)]
     torch.cuda.synchronize()

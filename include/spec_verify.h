@@ -245,6 +245,24 @@ int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, cons
                        int32_t* out_n_accepted, int32_t* out_target, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * spec_verify_gumbel with call hints (same section of the same page).
+ *
+ *  hints        0 or SV_HINT_ALL_DENSE: the caller knows that every sequence has T > 0
+ *               and no top-k of at most 512.  The select and list launches, whose
+ *               only work is on argmax and small-top-k sequences, are skipped, and the
+ *               per-(sequence, position) kernel takes every sequence: one that breaks
+ *               the promise still gets its exact result there.  Any other bit
+ *               (SV_HINT_NO_DENSE included): SV_ERR_ARG.
+ * Every other argument, the workspace and the error behaviour are those of
+ * spec_verify_gumbel.
+ */
+int spec_verify_gumbel_ex(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
+                          const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
+                          const float* top_p, int hints, int B, int gamma_max, int V, int32_t* out_tokens,
+                          int32_t* out_n_accepted, int32_t* out_target, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Workspace of spec_verify_gumbel (and, with gamma_max = 0 and B = R rows, of
  * spec_sample_gumbel): its size (0 for invalid sizes) and its one-time
  * preparation on `stream`.  Returns SV_OK or a negative code. */

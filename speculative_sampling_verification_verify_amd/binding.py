@@ -30,7 +30,7 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_v
             "spec_sample_workspace_bytes", "spec_sample_workspace_init", "spec_sample", "spec_sample_gumbel",
             "spec_verify_expected_tokens", "spec_verify_speedup", "spec_verify_operations",
             "spec_verify_optimal_gamma", "spec_verify_acceptance_length", "spec_verify_spectr",
-            "spec_verify_gumbel_workspace_bytes", "spec_verify_gumbel_workspace_init")
+            "spec_verify_gumbel_workspace_bytes", "spec_verify_gumbel_workspace_init", "spec_verify_gumbel_ex")
 
 _lib = None
 
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_gumbel_workspace_init.argtypes = [vp, sz, i, i, i, i, vp]
         L.spec_verify_gumbel_workspace_init.restype = i
         L.spec_verify_gumbel.restype = i
+        L.spec_verify_gumbel_ex.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.spec_verify_gumbel_ex.restype = i
         L.spec_verify_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_ex.restype = i
         L.spec_sample_workspace_bytes.argtypes = [i, i, i]
@@ -240,8 +242,9 @@ def gumbel_workspace(B: int, gamma_max: int, V: int, dtype: int, device) -> torc
 def spec_verify_gumbel(p_logits: torch.Tensor, noise: torch.Tensor, draft_tokens: torch.Tensor,
                        gamma_len: Optional[torch.Tensor], temperature: torch.Tensor, top_k: Optional[torch.Tensor],
                        top_p: Optional[torch.Tensor], out_tokens: torch.Tensor, out_n_accepted: torch.Tensor,
-                       out_target: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
-    """Enqueue one shared-noise verify call (see include/spec_verify.h)."""
+                       out_target: torch.Tensor, workspace: torch.Tensor, stream=None, hints: int = 0) -> None:
+    """Enqueue one shared-noise verify call (see include/spec_verify.h); with
+    `hints` (SV_HINT_ALL_DENSE) the call goes through spec_verify_gumbel_ex."""
     if p_logits.dim() != 3:
         raise ValueError("p_logits must be [B, gamma_max+1, V]")
     B, G1, V = p_logits.shape
@@ -260,19 +263,24 @@ def spec_verify_gumbel(p_logits: torch.Tensor, noise: torch.Tensor, draft_tokens
     _check(out_tokens, "out_tokens", torch.int32, (B, G + 1), dev)
     _check(out_n_accepted, "out_n_accepted", torch.int32, (B,), dev)
     _check(out_target, "out_target", torch.int32, (B, G + 1), dev)
-    rc = lib().spec_verify_gumbel(_ptr(p_logits), dt, _ptr(noise), _ptr(draft_tokens), _ptr(gamma_len),
-                                  _ptr(temperature), _ptr(top_k), _ptr(top_p), B, G, V, _ptr(out_tokens),
-                                  _ptr(out_n_accepted), _ptr(out_target), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    head = (_ptr(p_logits), dt, _ptr(noise), _ptr(draft_tokens), _ptr(gamma_len), _ptr(temperature), _ptr(top_k),
+            _ptr(top_p))
+    tail = (B, G, V, _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_target), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if hints:
+        rc, name = lib().spec_verify_gumbel_ex(*head, int(hints), *tail), "spec_verify_gumbel_ex"
+    else:
+        rc, name = lib().spec_verify_gumbel(*head, *tail), "spec_verify_gumbel"
     if rc != SV_OK:
-        raise SpecVerifyError(rc, "spec_verify_gumbel")
+        raise SpecVerifyError(rc, name)
 
 
 class GumbelVerifier:
     """Workspace and output buffers for shared-noise verify calls of one shape."""
 
-    def __init__(self, B: int, gamma_max: int, V: int, dtype: int = SV_BF16, device="cuda"):
+    def __init__(self, B: int, gamma_max: int, V: int, dtype: int = SV_BF16, device="cuda", hints: int = 0):
         dev = torch.device(device)
+        self.hints = hints
         self.workspace = gumbel_workspace(B, gamma_max, V, dtype, dev)
         self.tokens = torch.empty((B, gamma_max + 1), dtype=torch.int32, device=dev)
         self.n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -281,7 +289,7 @@ class GumbelVerifier:
     def __call__(self, p_logits, noise, draft_tokens, temperature, top_k=None, top_p=None, gamma_len=None,
                  stream=None):
         spec_verify_gumbel(p_logits, noise, draft_tokens, gamma_len, temperature, top_k, top_p, self.tokens,
-                           self.n_accepted, self.target, self.workspace, stream)
+                           self.n_accepted, self.target, self.workspace, stream, self.hints)
         return self.tokens, self.n_accepted, self.target
 
 

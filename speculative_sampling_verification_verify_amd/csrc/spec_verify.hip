@@ -410,12 +410,16 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
   }
   // 1. Streaming select over the target rows of argmax / top-k sequences.
   if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)sel_grid), dim3(K1_NT), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.all_dense) {
+    hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)sel_grid), dim3(K1_NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   // 2. Their per-position argmax from the survivor lists.
-  hipLaunchKernelGGL((gumbel_list_kernel<ET>), dim3((unsigned)a.B), dim3(NT), sizeof(FinSmem), st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.all_dense) {
+    hipLaunchKernelGGL((gumbel_list_kernel<ET>), dim3((unsigned)a.B), dim3(NT), sizeof(FinSmem), st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // 3. Dense and demoted sequences, one workgroup per (sequence, position).
   if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((gumbel_kernel<ET, GUMBEL_NT, VECTOR>), dim3((unsigned)((long long)a.B * (a.G + 1))),
@@ -434,7 +438,8 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
 static int run_gumbel(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
                       const int32_t* gamma_len, const float* temperature, const int32_t* top_k, const float* top_p,
                       int B, int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_target,
-                      void* workspace, size_t workspace_bytes, void* stream, int sampler) {
+                      void* workspace, size_t workspace_bytes, void* stream, int sampler, int hints) {
+  if (hints & ~SV_HINT_ALL_DENSE) return SV_ERR_ARG;
   if (!p_logits || !noise || !temperature || !out_tokens || !out_target) return SV_ERR_ARG;
   if (!sampler && (!draft_tokens || !out_n_accepted)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
@@ -477,6 +482,9 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   a.counts = reinterpret_cast<int32_t*>(ws + Lw.counts_off);
   a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);
   a.sel_blocks = sel_grid;   // no dense-pair listing here
+  // The promise that every sequence is dense saves the select and list
+  // launches; the per-(sequence, position) kernel then takes every sequence.
+  a.all_dense = (hints & SV_HINT_ALL_DENSE) && !sampler ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dtype == SV_BF16)
@@ -504,7 +512,21 @@ extern "C" int spec_verify_gumbel(const void* p_logits, int dtype, const float* 
   if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
   if (B == 0) return SV_OK;
   return run_gumbel(p_logits, dtype, noise, draft_tokens, gamma_len, temperature, top_k, top_p, B, gamma_max, V,
-                    out_tokens, out_n_accepted, out_target, workspace, workspace_bytes, stream, 0);
+                    out_tokens, out_n_accepted, out_target, workspace, workspace_bytes, stream, 0, 0);
+}
+
+extern "C" int spec_verify_gumbel_ex(const void* p_logits, int dtype, const float* noise, const int32_t* draft_tokens,
+                                     const int32_t* gamma_len, const float* temperature, const int32_t* top_k,
+                                     const float* top_p, int hints, int B, int gamma_max, int V, int32_t* out_tokens,
+                                     int32_t* out_n_accepted, int32_t* out_target, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (hints & ~SV_HINT_ALL_DENSE) return SV_ERR_ARG;
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  return run_gumbel(p_logits, dtype, noise, draft_tokens, gamma_len, temperature, top_k, top_p, B, gamma_max, V,
+                    out_tokens, out_n_accepted, out_target, workspace, workspace_bytes, stream, 0, hints);
 }
 
 extern "C" int spec_sample_gumbel(const void* logits, int dtype, const float* noise, const float* temperature,
@@ -515,7 +537,7 @@ extern "C" int spec_sample_gumbel(const void* logits, int dtype, const float* no
   if (R < 0 || V < 1) return SV_ERR_ARG;
   if (R == 0) return SV_OK;
   return run_gumbel(logits, dtype, noise, nullptr, nullptr, temperature, top_k, top_p, R, 0, V, out_tokens, nullptr,
-                    out_tokens, workspace, workspace_bytes, stream, 1);
+                    out_tokens, workspace, workspace_bytes, stream, 1, 0);
 }
 
 namespace sv {

@@ -50,9 +50,10 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
   if (j > g) return;                          // padding: the finisher writes it
   {
     // Argmax and top-k sequences belong to the list path unless their lists
-    // were demoted (overflow) by the select or the list kernel.
+    // were demoted (overflow) by the select or the list kernel, or there is
+    // no list path in this call (every sequence promised dense).
     const Mode sm = seq_mode(a, b);
-    if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE)) return;
+    if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE) && !a.all_dense) return;
   }
   int32_t* outp = a.out_target + (size_t)b * G1 + j;
   const float Tv = a.temp[b];

@@ -113,6 +113,15 @@ def test_gumbel_host_argument_errors():
     assert call(p=ctypes.c_void_p(0x100001)) == binding.SV_ERR_ARG          # misaligned bf16
     assert call(B=0) == binding.SV_OK
 
+    def call_ex(hints, B=B):
+        return L.spec_verify_gumbel_ex(fake, binding.SV_BF16, fake, fake, nul, fake, nul, nul, hints, B, G, V, fake,
+                                       fake, fake, fake, need, nul)
+
+    assert call_ex(binding.SV_HINT_NO_DENSE) == binding.SV_ERR_ARG
+    assert call_ex(4) == binding.SV_ERR_ARG
+    assert call_ex(binding.SV_HINT_ALL_DENSE, B=0) == binding.SV_OK
+    assert call_ex(binding.SV_HINT_ALL_DENSE, B=-1) == binding.SV_ERR_ARG
+
 
 def test_sample_and_lenient_host_argument_errors():
     L = _ensure_built()

@@ -15,13 +15,16 @@ from gpu_util import TOL, log, logits_to_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu_gumbel(gb, dev="cuda:0", pass_gamma=True, with_params=True):
+def run_gpu_gumbel(gb, dev="cuda:0", pass_gamma=True, with_params=True, hints=0, calls=1):
     import torch
     from speculative_sampling_verification_verify_amd import binding
     P, _ = logits_to_dev(gb.p_logits, dev)
     N = to_dev(np.ascontiguousarray(gb.noise, dtype=np.float32), dev)
     ver = binding.GumbelVerifier(gb.B, gb.gamma_max, gb.V, binding.SV_BF16 if gb.p_logits.dtype == np.uint16
-                                 else binding.SV_FP32, device=dev)
+                                 else binding.SV_FP32, device=dev, hints=hints)
+    for _ in range(calls - 1):
+        ver(P, N, to_dev(gb.draft, dev), to_dev(gb.temperature, dev), to_dev(gb.top_k, dev), to_dev(gb.top_p, dev),
+            to_dev(gb.gamma_len, dev))
     tok, n, tgt = ver(P, N, to_dev(gb.draft, dev), to_dev(gb.temperature, dev),
                       to_dev(gb.top_k, dev) if with_params else None, to_dev(gb.top_p, dev) if with_params else None,
                       to_dev(gb.gamma_len, dev) if pass_gamma else None)
@@ -29,9 +32,9 @@ def run_gpu_gumbel(gb, dev="cuda:0", pass_gamma=True, with_params=True):
     return tok.cpu().numpy(), n.cpu().numpy(), tgt.cpu().numpy()
 
 
-def check_gumbel(gb, label, rows=None):
-    log(f"[gumbel] {label}: B={gb.B} V={gb.V} gamma_max={gb.gamma_max} dtype={gb.p_logits.dtype}")
-    tok, n, tgt = run_gpu_gumbel(gb)
+def check_gumbel(gb, label, rows=None, hints=0, calls=1):
+    log(f"[gumbel] {label}: B={gb.B} V={gb.V} gamma_max={gb.gamma_max} dtype={gb.p_logits.dtype} hints={hints}")
+    tok, n, tgt = run_gpu_gumbel(gb, hints=hints, calls=calls)
     rows = list(range(gb.B)) if rows is None else list(rows)
     ref = oracle.gumbel_verify_batch(gb.p_logits, gb.noise, gb.draft, gb.temperature, gb.top_k, gb.top_p,
                                      gb.gamma_len, rows=rows)
@@ -180,3 +183,15 @@ def test_gumbel_extreme_temperatures():
     k = np.array([0, 0, 64, 64, 0, 0, 0, 0], np.int32)
     tp = np.array([1.0, 1.0, 1.0, 1.0, 0.9, 0.9, 1.0, 1.0], np.float32)
     check_gumbel(_replace(gb, temperature=T, top_k=k, top_p=tp), "extreme-T")
+
+
+@pytest.mark.parametrize("cid,B,V", [(0, 200, None), (1, 8, None), (2, 8, 40000), (4, 24, 20000), (3, 5, 50001),
+                                     (0, 16, 1001)])
+def test_gumbel_all_dense_hint(cid, B, V):
+    # Without the select and list launches every sequence goes to the
+    # per-(sequence, position) kernel; argmax and top-k sequences (which break
+    # the promise) must still come out exact.  The second of two calls is
+    # checked.
+    from speculative_sampling_verification_verify_amd import binding
+    gb = synth.make_gumbel_batch(cid, B=B, V=V)
+    check_gumbel(gb, f"all-dense-hint-w{cid}-B{B}-V{gb.V}", hints=binding.SV_HINT_ALL_DENSE, calls=2)

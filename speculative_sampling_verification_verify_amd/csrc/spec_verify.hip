@@ -18,6 +18,9 @@
 //      dense sequences it takes the pair kernel's per-position results (or,
 //      for rows beyond the pair kernel's limits, runs a multi-pass procedure
 //      over the logits).  See sv_finish.h.
+// A caller that promises that every sequence is dense skips launch 1 (the
+// pair kernel then takes the pairs in a fixed order), and launch 3 becomes
+// finish_dense_kernel, one workgroup per 16 sequences.
 //
 // Definitions followed (page titles and sections): the acceptance rule and
 // the residual, "Fast Inference from Transformers via Speculative Decoding"
@@ -163,6 +166,9 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_kernel<ET, VECTOR>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
     if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_dense_kernel<ET, VECTOR>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
+    if (e != hipSuccess) return e;
     attr_dev[dev] = dev + 1;
   }
   if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
@@ -207,7 +213,11 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     if ((e = stage_mark(SV_KERNEL_PAIR, false, st)) != hipSuccess) return e;
   }
   if ((e = stage_mark(SV_KERNEL_FINISH, true, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((finish_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), fin_lds, st, a);
+  if (a.all_dense)
+    hipLaunchKernelGGL((finish_dense_kernel<ET, VECTOR>), dim3((unsigned)(((long long)a.B + NWAVE - 1) / NWAVE)),
+                       dim3(NT), fin_lds, st, a);
+  else
+    hipLaunchKernelGGL((finish_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), fin_lds, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return stage_mark(SV_KERNEL_FINISH, false, st);

@@ -687,7 +687,7 @@ __device__ __forceinline__ int dense_draw(const Args& a, FinSmem& s, int b, cons
 // acceptance tests, finds the first rejection by ballot and writes the
 // outputs; the other wavefronts of the workgroup leave at once.
 __device__ __forceinline__ void finish_from_pairs_wave(const Args& a, int b, const Mode& m) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int G = a.G, g = m.g;
   const float* ub = a.u + (size_t)b * (G + 1);
   const int32_t* xb = a.draft + (size_t)b * G;
@@ -925,11 +925,45 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   (void)lane;
 }
 
+// One workgroup per sequence; when every sequence was promised dense, one
+// workgroup per NWAVE sequences: each wavefront finishes one pair-resolved
+// sequence, and a sequence that is not dense after all is then finished by
+// the whole workgroup.
 template <typename ET, bool VECTOR>
 __global__ __launch_bounds__(NT) void finish_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char fin_smem_raw[];
   FinSmem& s = *reinterpret_cast<FinSmem*>(fin_smem_raw);
   finish_sequence<ET, VECTOR>(a, s, blockIdx.x);
+}
+
+// The finisher when every sequence was promised dense: a workgroup per NWAVE
+// sequences, each wavefront finishing one pair-resolved sequence; a sequence
+// that is not dense after all is then finished by the whole workgroup.  (A
+// kernel of its own: the loop around the whole-sequence procedure costs
+// registers that the one-sequence finisher should not pay.)
+template <typename ET, bool VECTOR>
+__global__ __launch_bounds__(NT) void finish_dense_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char fin_smem_raw[];
+  FinSmem& s = *reinterpret_cast<FinSmem*>(fin_smem_raw);
+  const int wave = threadIdx.x >> 6;
+  const int b0 = blockIdx.x * NWAVE;
+  uint32_t other = 0;
+  if (b0 + wave < a.B) {
+    const Mode m = seq_mode(a, b0 + wave);
+    if (m.mode == MODE_DENSE) finish_from_pairs_wave(a, b0 + wave, m);
+    else other = 1;
+  }
+  if ((threadIdx.x & 63) == 0) s.red_u[wave] = other;
+  __syncthreads();
+  uint32_t mask = 0;
+  for (int w = 0; w < NWAVE; ++w) mask |= s.red_u[w] << w;
+  __syncthreads();   // finish_sequence reuses the LDS
+  while (mask) {     // workgroup-uniform
+    const int w = __builtin_ctz(mask);
+    mask &= mask - 1u;
+    finish_sequence<ET, VECTOR>(a, s, b0 + w);
+    if (mask) __syncthreads();
+  }
 }
 
 }  // namespace sv

@@ -77,6 +77,13 @@ def test_gumbel_workload_full_size_sampled(cid):
     rng = np.random.default_rng(cid)
     rows = sorted(rng.choice(gb.B, size=min(gb.B, 24), replace=False).tolist())
     check_gumbel(gb, f"workload{cid}-full", rows=rows)
+    # bench.py's launch configuration: with no argmax or small-top-k sequence
+    # it passes the all-dense hint.
+    T, k = gb.temperature, gb.top_k
+    listed = (T == 0) | ((T > 0) & (k > 0) & (k < gb.V) & (k <= 512))
+    if not listed.any():
+        from speculative_sampling_verification_verify_amd import binding
+        check_gumbel(gb, f"workload{cid}-full-all-dense-hint", rows=rows, hints=binding.SV_HINT_ALL_DENSE)
 
 
 def _replace(gb, **kw):

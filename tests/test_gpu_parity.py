@@ -51,10 +51,29 @@ def test_workload_small(cid, B, V):
     check(bt, f"workload{cid}-B{B}-V{bt.V}")
 
 
+def bench_hints(bt):
+    """The call hints bench.py passes for this batch (host-side facts): no
+    dense sequence, or only dense ones."""
+    from speculative_sampling_verification_verify_amd import binding
+    T, k = bt.temperature, bt.top_k
+    listed = (T == 0) | ((T > 0) & (k > 0) & (k < bt.V) & (k <= 512))
+    if listed.all():
+        return binding.SV_HINT_NO_DENSE
+    return binding.SV_HINT_ALL_DENSE if not listed.any() else 0
+
+
 @pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
 def test_workload_full_size(cid):
+    # Without hints, and in the launch configuration bench.py times.
+    from speculative_sampling_verification_verify_amd import binding
     bt = synth.make_batch(cid)
     _, ref, rep = check(bt, f"workload{cid}-full")
+    hints = bench_hints(bt)
+    if hints:
+        dt = binding.SV_BF16 if bt.p_logits.dtype == np.uint16 else binding.SV_FP32
+        ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt, device="cuda:0", hints=hints)
+        compare(bt, run_gpu(bt, verifier=ver), ref, f"workload{cid}-full-hints{hints}")
+        log(f"[parity] workload{cid}-full with hints {hints}: ok")
     log(f"[parity] workload{cid}-full: mean alpha {np.nanmean(ref.alpha[ref.alpha > 0]):.3f}, "
         f"mean tokens/round {np.mean(ref.n[ref.n >= 0] + 1):.3f}, near-margin rows {rep.near}, "
         f"of which differ {rep.near_differ}")

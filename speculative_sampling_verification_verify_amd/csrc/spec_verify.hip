@@ -75,12 +75,20 @@ struct Plan {
 #ifndef SV_MIN_STEPS
 #define SV_MIN_STEPS 2
 #endif
+// Calls of up to this many units at two parts per row still get two: the
+// plan counts every row of the call, but where some sequences are dense (run
+// by the pair kernel) only the others' rows are streamed here, and with one
+// part each those few rows would take one wavefront apiece from end to end.
+#ifndef SV_SPLIT_MAX_UNITS
+#define SV_SPLIT_MAX_UNITS 4608
+#endif
 static Plan plan(int B, int RS, int V, int dtype) {
   const int vec = dtype == SV_BF16 ? 8 : 4;
   const int step = 64 * WVPL * vec;
   const long long R = (long long)B * RS;
   long long np = R > 0 ? SV_UNIT_TARGET / R : 1;
   np = np < 1 ? 1 : np;
+  if (np == 1 && 2 * R <= SV_SPLIT_MAX_UNITS) np = 2;
   np = np > MAXNP ? MAXNP : np;
   const long long by_len = V / ((long long)SV_MIN_STEPS * step);
   if (np > by_len) np = by_len < 1 ? 1 : by_len;

@@ -58,6 +58,7 @@ static bool sizes_ok(int B, int G, int V) {
 struct Plan {
   int NP;     // parts per logit row
   int PL;     // part length in elements
+  int split;  // 1 when NP comes from the small-call rule below
 };
 
 // Parts per row: about SV_UNIT_TARGET (row, part) units, with at least
@@ -75,12 +76,15 @@ struct Plan {
 #ifndef SV_MIN_STEPS
 #define SV_MIN_STEPS 2
 #endif
-// Calls of up to this many units at two parts per row still get two: the
+// Calls of up to this many units at SV_SPLIT_PARTS parts per row get that many: the
 // plan counts every row of the call, but where some sequences are dense (run
 // by the pair kernel) only the others' rows are streamed here, and with one
 // part each those few rows would take one wavefront apiece from end to end.
 #ifndef SV_SPLIT_MAX_UNITS
 #define SV_SPLIT_MAX_UNITS 4608
+#endif
+#ifndef SV_SPLIT_PARTS
+#define SV_SPLIT_PARTS 2
 #endif
 static Plan plan(int B, int RS, int V, int dtype) {
   const int vec = dtype == SV_BF16 ? 8 : 4;
@@ -88,7 +92,11 @@ static Plan plan(int B, int RS, int V, int dtype) {
   const long long R = (long long)B * RS;
   long long np = R > 0 ? SV_UNIT_TARGET / R : 1;
   np = np < 1 ? 1 : np;
-  if (np == 1 && 2 * R <= SV_SPLIT_MAX_UNITS) np = 2;
+  int split = 0;
+  if (np == 1 && SV_SPLIT_PARTS * R <= SV_SPLIT_MAX_UNITS) {
+    np = SV_SPLIT_PARTS;
+    split = 1;
+  }
   np = np > MAXNP ? MAXNP : np;
   const long long by_len = V / ((long long)SV_MIN_STEPS * step);
   if (np > by_len) np = by_len < 1 ? 1 : by_len;
@@ -97,6 +105,7 @@ static Plan plan(int B, int RS, int V, int dtype) {
   pl = (pl + vec - 1) / vec * vec;
   p.PL = pl;
   p.NP = (V + pl - 1) / pl;
+  p.split = split && p.NP > 1;
   return p;
 }
 
@@ -305,6 +314,7 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
   a.G = gamma_max;
   a.V = V;
   a.NP = pl.NP;
+  a.split = pl.split;
   a.PL = pl.PL;
   a.fixbits = 62 - vb;
   a.out_tokens = out_tokens;
@@ -490,6 +500,7 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   a.G = gamma_max;
   a.V = V;
   a.NP = pl.NP;
+  a.split = pl.split;
   a.PL = pl.PL;
   a.fixbits = 62 - vb;
   a.out_tokens = out_tokens;

@@ -11,6 +11,7 @@ enum { MODE_INVALID = 0, MODE_GREEDY = 1, MODE_SPARSE = 2, MODE_DENSE = 3 };
 
 constexpr int SEG = 1024;          // survivor slots per (logit row, row part) in the workspace
 constexpr int MAXNP = 16;          // parts per logit row
+constexpr int POOL = 4096;         // survivor entries of one sequence held in the finisher's LDS
 
 // Sequence flags (workspace, one word per sequence).
 constexpr uint32_t F_BAD = 1u;     // NaN or +inf among the logits
@@ -50,6 +51,8 @@ struct Args {
   int32_t* dense_list;    // [B * (G+1)] pair ids b * (G+1) + i of the dense sequences
   long long sel_blocks;   // workgroups of the select kernel that stream rows; the rest list dense pairs
   int pair;               // 1 when the pair-resident kernel runs for the dense sequences
+  int split;              // 1 when NP > 1 only because the call is small: a top-k sequence whose
+                          // part lists might overflow the finisher's pool streams rows whole
   int all_dense;          // 1: no select launch; the pair kernel takes every (sequence, position) in
                           // order and the finisher runs non-dense sequences by its multi-pass path
   const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test

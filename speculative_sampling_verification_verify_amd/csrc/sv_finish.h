@@ -21,7 +21,6 @@
 
 namespace sv {
 
-constexpr int POOL = 4096;                      // survivor entries of one sequence held in LDS
 constexpr int MAXROWS = 2 * SV_MAX_GAMMA + 1;
 constexpr int MAXSEG = 512;                     // (row, part) lists of one sequence on the list path
 

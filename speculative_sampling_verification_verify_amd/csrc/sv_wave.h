@@ -678,8 +678,14 @@ __global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) v
   const bool isP = slot <= a.G;
   const int pos = isP ? slot : slot - a.G - 1;
   if (isP ? pos > m.g : pos >= m.g) return;   // padding rows are never read
-  const int e0 = part * a.PL;
-  const int e1 = min(a.V, e0 + a.PL);
+  int e0 = part * a.PL;
+  int e1 = min(a.V, e0 + a.PL);
+  // Under the small-call split, a top-k sequence whose part lists might not
+  // fit the finisher's pool together streams each row as one part.
+  if (a.split && m.mode == MODE_SPARSE && (long long)m.k * a.RS * a.NP > POOL) {
+    e0 = part == 0 ? 0 : a.V;
+    e1 = a.V;
+  }
   int32_t* cnt = a.counts + (size_t)rowid * a.NP + part;
   if (e0 < e1) {
     if constexpr (VECTOR && sizeof(ET) == 2)

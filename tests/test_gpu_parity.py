@@ -337,3 +337,15 @@ def test_many_sequences():
     w = dataclasses.replace(bt.workload, gamma_max=G)
     bt2 = synth.Batch(w, _bf(zp), _bf(zq), draft, synth.uniforms(8192, B, G), np.full(B, G, np.int32), T, k, tp, 8192)
     check(bt2, "B8192")
+
+
+@pytest.mark.parametrize("k", [100, 200])
+def test_small_call_split_and_pool_fallback(k):
+    # 128 sequences of up to 8 drafts is a call small enough for two parts per
+    # row.  With top-k 100 the parts' lists fit the finisher's pool; with
+    # top-k 200 they might not, so those sequences stream each row whole.
+    bt = synth.make_batch(4, B=128, V=20000)
+    B = bt.B
+    bt = batch_from(bt, temperature=np.full(B, 1.0, np.float32), top_k=np.full(B, k, np.int32),
+                    top_p=np.ones(B, np.float32))
+    check(bt, f"split-topk{k}")

@@ -224,7 +224,7 @@ def main_gumbel(args):
         "data": "synthetic",
         "config": {"workload": w.name, "B": gb.B, "V": gb.V, "gamma": gb.gamma_max,
                    "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "hints": "all-dense" if ghints else "none"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(kname, w.name),
                      "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,
@@ -492,7 +492,7 @@ def main():
         "config": {"workload": w.name, "B": bt.B, "V": bt.V, "gamma": bt.gamma_max,
                    "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
                    "logit_bytes_per_call": logit_bytes, "parallelism": "single-gpu",
-                   "hints": "no-dense" if hints else "none"},
+                   "hints": {binding.SV_HINT_NO_DENSE: "no-dense", binding.SV_HINT_ALL_DENSE: "all-dense"}.get(hints, "none")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,

@@ -42,6 +42,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace sv {
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
@@ -171,23 +173,62 @@ static hipError_t stage_mark(int kernel, bool begin, hipStream_t st) {
   return ev ? hipEventRecord(ev, st) : hipSuccess;
 }
 
+// Dynamic-LDS limits of every kernel that takes dynamic LDS, raised once per
+// device to the largest size any call can launch with, so that the limit in
+// force never depends on the order of calls or on the calling thread.  The
+// set-up runs under a mutex with the device current; a failed set-up is
+// retried by the next call.
+constexpr int SV_MAX_DEVICES = 64;
+static std::mutex g_setup_mu;
+static bool g_setup_done[SV_MAX_DEVICES];
+
 template <typename ET, bool VECTOR>
-static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
-  // The finisher's LDS exceeds the default dynamic limit; raise it once per
-  // device.
-  static int attr_dev[64];   // 1 + device ordinal once set
+static hipError_t set_lds_limits() {
+  const int fin = (int)sizeof(FinSmem);
+  const int pair_max = 2 * PAIR_LDS_ROW_MAX;   // both rows of a pair, or a K-SEQ node's two rows
+  struct {
+    const void* fn;
+    int bytes;
+  } const lim[] = {
+      {reinterpret_cast<const void*>(&finish_kernel<ET, VECTOR>), fin},
+      {reinterpret_cast<const void*>(&finish_dense_kernel<ET, VECTOR>), fin},
+      {reinterpret_cast<const void*>(&pair_kernel<ET, 64, VECTOR, true>), 2 * 4096},
+      {reinterpret_cast<const void*>(&pair_kernel<ET, 256, VECTOR, true>), 2 * 16384},
+      {reinterpret_cast<const void*>(&pair_kernel<ET, 1024, VECTOR, true>), pair_max},
+      {reinterpret_cast<const void*>(&kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>), pair_max},
+  };
+  for (const auto& l : lim) {
+    const hipError_t e = hipFuncSetAttribute(l.fn, hipFuncAttributeMaxDynamicSharedMemorySize, l.bytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static hipError_t device_setup() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && attr_dev[dev] != dev + 1) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_kernel<ET, VECTOR>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finish_dense_kernel<ET, VECTOR>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds);
-    if (e != hipSuccess) return e;
-    attr_dev[dev] = dev + 1;
-  }
+  if (dev < 0 || dev >= SV_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_setup_mu);
+  if (g_setup_done[dev]) return hipSuccess;
+  if ((e = set_lds_limits<uint16_t, true>()) != hipSuccess) return e;
+  if ((e = set_lds_limits<uint16_t, false>()) != hipSuccess) return e;
+  if ((e = set_lds_limits<float, true>()) != hipSuccess) return e;
+  if ((e = set_lds_limits<float, false>()) != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<float>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
+  if (e != hipSuccess) return e;
+  g_setup_done[dev] = true;
+  return hipSuccess;
+}
+
+template <typename ET, bool VECTOR>
+static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
+  hipError_t e = device_setup();
+  if (e != hipSuccess) return e;
   if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
   if (!a.all_dense) {
     hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
@@ -198,24 +239,7 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
   if (a.pair) {
     size_t plds = 0;
     const int pv = pair_variant(a.V, sizeof(ET) == 2 ? SV_BF16 : SV_FP32, VECTOR, &plds);
-    const void* kfn = nullptr;
-    switch (pv) {
-      case 64: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 64, VECTOR, true>); break;
-      case 256: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 256, VECTOR, true>); break;
-      case 1024: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 1024, VECTOR, true>); break;
-      case -1024: kfn = reinterpret_cast<const void*>(&pair_kernel<ET, 1024, VECTOR, false>); break;
-      default: return hipErrorInvalidValue;
-    }
-    if (plds) {
-      // Raised once per (device, kernel, size); sizes only grow with V.
-      static int pair_lds_set[64][4];
-      const int slot = pv == 64 ? 0 : pv == 256 ? 1 : 2;
-      if (dev < 0 || dev >= 64 || pair_lds_set[dev][slot] < (int)plds) {
-        e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
-        if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) pair_lds_set[dev][slot] = (int)plds;
-      }
-    }
+    if (pv != 64 && pv != 256 && pv != 1024 && pv != -1024) return hipErrorInvalidValue;
     const long long npairs = (long long)a.B * (a.G + 1);
     const dim3 grid((unsigned)(npairs < pair_grid_cap(pv) ? npairs : pair_grid_cap(pv)));
     if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
@@ -266,6 +290,20 @@ static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V,
   return SV_OK;
 }
 
+// Pointer, alignment and hint checks of the verify entry points (sizes are
+// checked by the callers).
+static int check_verify_args(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
+                             const float* uniforms, const float* temperature, int hints, const int32_t* out_tokens,
+                             const int32_t* out_n_accepted, const float* out_alpha, int sampler) {
+  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
+  if ((hints & SV_HINT_NO_DENSE) && (hints & SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
+  if (!p_logits || !uniforms || !temperature || !out_tokens) return SV_ERR_ARG;
+  if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
+  const size_t es = dtype == SV_BF16 ? 2 : 4;
+  if (((uintptr_t)p_logits % es) || (q_logits && ((uintptr_t)q_logits % es))) return SV_ERR_ARG;
+  return SV_OK;
+}
+
 // The verify launch sequence.  sampler == 1: G == 0, every "sequence" is one
 // row drawn from its processed distribution at u[b] (the bonus draw), with no
 // drafts, no draft logits and no n output.
@@ -274,12 +312,9 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
                       const int32_t* top_k, const float* top_p, const float* lenience, int hints, int B,
                       int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha,
                       float* out_pq, void* workspace, size_t workspace_bytes, void* stream, int sampler) {
-  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
-  if ((hints & SV_HINT_NO_DENSE) && (hints & SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
-  if (!p_logits || !uniforms || !temperature || !out_tokens) return SV_ERR_ARG;
-  if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
-  const size_t es = dtype == SV_BF16 ? 2 : 4;
-  if (((uintptr_t)p_logits % es) || (q_logits && ((uintptr_t)q_logits % es))) return SV_ERR_ARG;
+  const int rc = check_verify_args(p_logits, q_logits, dtype, draft_tokens, uniforms, temperature, hints,
+                                   out_tokens, out_n_accepted, out_alpha, sampler);
+  if (rc != SV_OK) return rc;
   const int RS = 2 * gamma_max + 1;
   const size_t need = ws_bytes(B, gamma_max, V, dtype, RS);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256)) return SV_ERR_WORKSPACE;
@@ -426,16 +461,8 @@ namespace sv {
 
 template <typename ET, bool VECTOR>
 static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t st) {
-  hipError_t e;
-  static int attr_dev[64];   // 1 + device ordinal once the list kernel's LDS limit is raised
-  int dev = 0;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && attr_dev[dev] != dev + 1) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<ET>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
-    if (e != hipSuccess) return e;
-    attr_dev[dev] = dev + 1;
-  }
+  hipError_t e = device_setup();
+  if (e != hipSuccess) return e;
   // 1. Streaming select over the target rows of argmax / top-k sequences.
   if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
   if (!a.all_dense) {
@@ -573,19 +600,11 @@ namespace sv {
 
 template <typename ET, bool VECTOR>
 static hipError_t launch_spectr(const Args& a, bool ldsr, size_t lds, hipStream_t st) {
-  hipError_t e;
+  hipError_t e = device_setup();
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((long long)a.B * a.K * (a.L + 1)));
   if ((e = stage_mark(SV_KERNEL_KSEQ, true, st)) != hipSuccess) return e;
   if (ldsr) {
-    static int lds_set[64];
-    int dev = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || lds_set[dev] < (int)lds) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      if (dev >= 0 && dev < 64) lds_set[dev] = (int)lds;
-    }
     hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>), grid, dim3(KSEQ_NT), lds, st, a);
   } else {
     hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, false>), grid, dim3(KSEQ_NT), 0, st, a);

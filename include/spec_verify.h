@@ -62,7 +62,8 @@ enum {
   SV_ERR_ARG = -1,          /* null pointer, bad size, misaligned base      */
   SV_ERR_UNSUPPORTED = -2,  /* unknown dtype, V or gamma_max beyond limits  */
   SV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required  */
-  SV_ERR_HIP = -4           /* a HIP call failed (see spec_verify_strerror) */
+  SV_ERR_HIP = -4,          /* a HIP call failed (see spec_verify_strerror) */
+  SV_ERR_SCRATCH = -5       /* spec_verify_noalloc: the call's workspace exceeds its fixed buffer */
 };
 
 /* Limits (checked synchronously). */
@@ -157,6 +158,36 @@ int spec_verify_ex(const void* p_logits, const void* q_logits, int dtype,
                    int hints, int B, int gamma_max, int V,
                    int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace.  Its workspace is a fixed device array of
+ * SV_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held from the
+ * first call on that GPU until the process ends; the call itself allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *
+ *  Arguments, outputs and data-error behaviour: those of spec_verify_ex, minus
+ *  `workspace` and `workspace_bytes`.  The inputs and outputs are still the
+ *  caller's device buffers.
+ *  SV_ERR_SCRATCH (nothing enqueued) when spec_verify_workspace_bytes(B,
+ *  gamma_max, V, dtype) exceeds SV_NOALLOC_SCRATCH_BYTES; the other codes as
+ *  for spec_verify_ex.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (different streams or host threads without ordering between them) race
+ * and give undefined results.  Calls ordered on one stream are safe.  Each
+ * call clears the counters it needs with a small fill kernel on `stream`, so
+ * no preparation call exists or is needed.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB per GPU */
+
+int spec_verify_noalloc(const void* p_logits, const void* q_logits, int dtype,
+                        const int32_t* draft_tokens, const int32_t* gamma_len, const float* uniforms,
+                        const float* temperature, const int32_t* top_k, const float* top_p, const float* lenience,
+                        int hints, int B, int gamma_max, int V,
+                        int32_t* out_tokens, int32_t* out_n_accepted, float* out_alpha, float* out_pq,
+                        void* stream);
 
 /*
  * Sampling one token per row from its processed distribution (the drafter's
@@ -357,7 +388,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 8. */
+/* ABI version: 9. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

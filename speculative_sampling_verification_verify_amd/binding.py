@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_BF16, SV_FP32 = 0, 1
-SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = 0, -1, -2, -3, -4
+SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+SV_NOALLOC_SCRATCH_BYTES = 64 << 20
 SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL, SV_KERNEL_KSEQ = 0, 1, 2, 3, 4
 SV_MAX_CANDIDATES = 64
 SV_HINT_NO_DENSE = 1
@@ -30,7 +31,8 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_v
             "spec_sample_workspace_bytes", "spec_sample_workspace_init", "spec_sample", "spec_sample_gumbel",
             "spec_verify_expected_tokens", "spec_verify_speedup", "spec_verify_operations",
             "spec_verify_optimal_gamma", "spec_verify_acceptance_length", "spec_verify_spectr",
-            "spec_verify_gumbel_workspace_bytes", "spec_verify_gumbel_workspace_init", "spec_verify_gumbel_ex")
+            "spec_verify_gumbel_workspace_bytes", "spec_verify_gumbel_workspace_init", "spec_verify_gumbel_ex",
+            "spec_verify_noalloc")
 
 _lib = None
 
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_gumbel_ex.restype = i
         L.spec_verify_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.spec_verify_ex.restype = i
+        L.spec_verify_noalloc.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp]
+        L.spec_verify_noalloc.restype = i
         L.spec_sample_workspace_bytes.argtypes = [i, i, i]
         L.spec_sample_workspace_bytes.restype = sz
         L.spec_sample_workspace_init.argtypes = [vp, sz, i, i, i, vp]
@@ -201,6 +205,43 @@ def spec_verify(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: to
                                   _ptr(workspace), wsb, _stream_handle(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify")
+
+
+def spec_verify_noalloc(p_logits: torch.Tensor, q_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                        gamma_len: Optional[torch.Tensor], uniforms: torch.Tensor, temperature: torch.Tensor,
+                        top_k: Optional[torch.Tensor], top_p: Optional[torch.Tensor],
+                        out_tokens: torch.Tensor, out_n_accepted: torch.Tensor, out_alpha: torch.Tensor,
+                        out_pq: Optional[torch.Tensor], stream=None, lenience: Optional[torch.Tensor] = None,
+                        hints: int = 0) -> None:
+    """Enqueue one verify call on the library's fixed per-GPU buffer
+    (spec_verify_noalloc: no workspace argument, nothing allocated)."""
+    if p_logits.dim() != 3 or q_logits.dim() != 3:
+        raise ValueError("p_logits must be [B, gamma_max+1, V] and q_logits [B, gamma_max, V]")
+    B, G1, V = p_logits.shape
+    G = G1 - 1
+    dev = p_logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must live in GPU memory")
+    dt = _dtype_code(p_logits)
+    _check(q_logits, "q_logits", p_logits.dtype, (B, G, V), dev)
+    _check(p_logits, "p_logits", p_logits.dtype, (B, G + 1, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, G), dev)
+    _check(gamma_len, "gamma_len", torch.int32, (B,), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, G + 1), dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    _check(top_k, "top_k", torch.int32, (B,), dev)
+    _check(top_p, "top_p", torch.float32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, G + 1), dev)
+    _check(out_n_accepted, "out_n_accepted", torch.int32, (B,), dev)
+    _check(out_alpha, "out_alpha", torch.float32, (B, G), dev)
+    _check(out_pq, "out_pq", torch.float32, (B, G, 2), dev)
+    _check(lenience, "lenience", torch.float32, (B,), dev)
+    rc = lib().spec_verify_noalloc(_ptr(p_logits), _ptr(q_logits), dt, _ptr(draft_tokens), _ptr(gamma_len),
+                                   _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(lenience),
+                                   int(hints), B, G, V, _ptr(out_tokens), _ptr(out_n_accepted), _ptr(out_alpha),
+                                   _ptr(out_pq), _stream_handle(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_noalloc")
 
 
 class Verifier:

@@ -428,6 +428,73 @@ extern "C" int spec_verify(const void* p_logits, const void* q_logits, int dtype
                         workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// spec_verify_ex without a workspace argument, for callers that cannot
+// allocate device memory.  Its workspace is the file-scope array below: one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol);
+// it uses the device address that hipGetSymbolAddress returned for the
+// current device.
+// ---------------------------------------------------------------------------
+namespace sv {
+
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[SV_MAX_DEVICES];
+
+// The current device's copy of `scratch` (looked up once per device, with
+// that device current).
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SV_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace sv
+
+extern "C" int spec_verify_noalloc(const void* p_logits, const void* q_logits, int dtype,
+                                   const int32_t* draft_tokens, const int32_t* gamma_len, const float* uniforms,
+                                   const float* temperature, const int32_t* top_k, const float* top_p,
+                                   const float* lenience, int hints, int B, int gamma_max, int V, int32_t* out_tokens,
+                                   int32_t* out_n_accepted, float* out_alpha, float* out_pq, void* stream) {
+  if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
+  if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
+  if (B == 0) return SV_OK;
+  int rc = check_verify_args(p_logits, q_logits, dtype, draft_tokens, uniforms, temperature, hints, out_tokens,
+                             out_n_accepted, out_alpha, 0);
+  if (rc != SV_OK) return rc;
+  const int RS = 2 * gamma_max + 1;
+  const size_t need = ws_bytes(B, gamma_max, V, dtype, RS);
+  if (need == 0 || need > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) {
+    snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(e));
+    return SV_ERR_HIP;
+  }
+  // The array keeps whatever the last call on this GPU left in it, and the
+  // counters' offsets depend on the sizes: clear them on every call (a fill
+  // kernel on the stream, as the workspace preparation does).
+  rc = ws_init(ws, SV_NOALLOC_SCRATCH_BYTES, B, gamma_max, V, dtype, RS, stream);
+  if (rc != SV_OK) return rc;
+  return run_verify(p_logits, q_logits, dtype, draft_tokens, gamma_len, uniforms, temperature, top_k, top_p, lenience,
+                    hints, B, gamma_max, V, out_tokens, out_n_accepted, out_alpha, out_pq, ws,
+                    SV_NOALLOC_SCRATCH_BYTES, stream, 0);
+}
+
 extern "C" size_t spec_sample_workspace_bytes(int R, int V, int dtype) { return ws_bytes(R, 0, V, dtype, 1); }
 
 extern "C" int spec_sample_workspace_init(void* workspace, size_t workspace_bytes, int R, int V, int dtype,
@@ -676,12 +743,15 @@ extern "C" const char* spec_verify_strerror(int code) {
     case SV_ERR_ARG: return "invalid argument (null pointer, size out of range or misaligned pointer)";
     case SV_ERR_UNSUPPORTED: return "unsupported dtype or size";
     case SV_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case SV_ERR_SCRATCH:
+      return "the call needs more workspace than the allocation-free entry point's fixed buffer "
+             "(SV_NOALLOC_SCRATCH_BYTES) holds; use spec_verify_ex with a caller workspace";
     case SV_ERR_HIP: return g_errbuf[0] ? g_errbuf : "HIP error";
     default: return "unknown error code";
   }
 }
 
-extern "C" int spec_verify_version(void) { return 8; }
+extern "C" int spec_verify_version(void) { return 9; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 8
+    assert binding.spec_verify_version() == 9
 
 
 def test_workspace_bytes():
@@ -215,3 +215,35 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+def test_noalloc_host_errors():
+    """The allocation-free entry point checks its arguments, and that the call
+    fits its fixed buffer, before any HIP call (no GPU is touched here)."""
+    L = _ensure_built()
+    fake = ctypes.c_void_p(0x100000)
+    nul = None
+    bf = binding.SV_BF16
+
+    def call(p=fake, q=fake, dt=bf, draft=fake, u=fake, temp=fake, hints=0, B=2, G=3, V=64, out=fake):
+        return L.spec_verify_noalloc(p, q, dt, draft, nul, u, temp, nul, nul, nul, hints, B, G, V, out, out, out,
+                                     nul, nul)
+
+    assert call(dt=5) == binding.SV_ERR_UNSUPPORTED
+    assert call(G=65) == binding.SV_ERR_UNSUPPORTED
+    assert call(V=0) == binding.SV_ERR_ARG
+    assert call(p=nul) == binding.SV_ERR_ARG
+    assert call(out=nul) == binding.SV_ERR_ARG
+    assert call(p=ctypes.c_void_p(0x100001)) == binding.SV_ERR_ARG
+    assert call(hints=3) == binding.SV_ERR_ARG
+    assert call(B=0) == binding.SV_OK
+    # Sizes whose workspace exceeds the fixed buffer: a clear error, nothing enqueued.
+    big = (512, 8, 152064)
+    assert binding.spec_verify_workspace_bytes(*big, bf) > binding.SV_NOALLOC_SCRATCH_BYTES
+    rc = call(B=big[0], G=big[1], V=big[2])
+    assert rc == binding.SV_ERR_SCRATCH
+    assert "fixed buffer" in binding.spec_verify_strerror(rc)
+    # The benchmark's workloads fit.
+    for B, G, V, dt in ((1, 4, 1000, binding.SV_FP32), (32, 5, 32000, bf), (64, 4, 128256, bf),
+                        (256, 7, 152064, bf), (128, 8, 128256, bf)):
+        assert binding.spec_verify_workspace_bytes(B, G, V, dt) <= binding.SV_NOALLOC_SCRATCH_BYTES

@@ -153,17 +153,19 @@ class SeqResult:
     pq: np.ndarray            # float64 [gamma_max, 2] = p_i(x_i), q_i(x_i)
     margin_acc: float
     margin_cdf: float
-    margin_topp: float
+    margin_topp: float        # top-p margin of the rows that decided n and the drawn token
     zero_residual: bool       # Z == 0 fallback taken
+    topp_pos: np.ndarray      # float64 [gamma_max]: top-p margin of position i's two rows (alpha_i, pq_i)
 
     @property
     def margin(self):
+        """Decision margin of n and the tokens."""
         return min(self.margin_acc, self.margin_cdf, self.margin_topp)
 
 
 def invalid_result(gamma_max: int) -> SeqResult:
     return SeqResult(np.full(gamma_max + 1, -1, np.int32), -1, np.full(gamma_max, np.nan),
-                     np.full((gamma_max, 2), np.nan), INF, INF, INF, False)
+                     np.full((gamma_max, 2), np.nan), INF, INF, INF, False, np.full(gamma_max, INF))
 
 
 def _inputs_valid(zp, zq, draft, u, T, top_p, gamma_b, V, gamma_max, lenience=1.0) -> bool:
@@ -244,42 +246,21 @@ def verify_sequence(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, u: np.nda
     if T == 0.0:
         margin_cdf = INF
 
-    # Any top-p boundary in the sequence moves alpha, so every used row counts.
-    margin_topp = min([pr.topp_margin for pr in P] + [qr.topp_margin for qr in Q])
+    # A nucleus boundary moves what is computed from its row: alpha_i and
+    # (p_i(x_i), q_i(x_i)) depend on position i's two rows only; n and the
+    # tokens on the rows of the tests that were made (positions 0..n, the
+    # last of them the rejection) and of the draw (position n, or the bonus
+    # row).  Rows after the first rejection decide nothing.
+    topp_pos = np.full(gamma_max, INF)
+    for i in range(gamma_b):
+        topp_pos[i] = min(P[i].topp_margin, Q[i].topp_margin)
+    deciding = [P[j].topp_margin for j in range(n + 1)] + [Q[i].topp_margin for i in range(min(n + 1, gamma_b))]
+    margin_topp = min(deciding)
 
     tokens = np.full(gamma_max + 1, -1, np.int32)
     tokens[:n] = draft[:n]
     tokens[n] = t
-    return SeqResult(tokens, n, alpha, pq, margin_acc, margin_cdf, margin_topp, zero_residual)
-
-
-def verify_sequence_vectorised(zp, zq, draft, u, T, top_k, top_p, gamma_b):
-    """Second formulation of the same step, used to cross-check the first.
-
-    Follows the JAX `verify` listing's structure on "the art of guessing
-    well", section "Speculative sampling": every acceptance flag is computed,
-    n is the index of the first False in (accepted || False), and the draft
-    distribution after the last draft is taken as all-zero so that the
-    residual there is the target's own distribution.  Returns (n, token)."""
-    gamma_max = zq.shape[0]
-    V = zp.shape[1]
-    if not _inputs_valid(zp, zq, draft, u, float(T), float(top_p), gamma_b, V, gamma_max):
-        return -1, -1
-    P = np.stack([process(zp[j], float(T), top_k, float(top_p)).prob for j in range(gamma_b + 1)])
-    Qz = np.zeros((gamma_b + 1, V))
-    for i in range(gamma_b):
-        Qz[i] = process(zq[i], float(T), top_k, float(top_p)).prob
-    idx = np.arange(gamma_b)
-    x = draft[:gamma_b]
-    accepted = u[:gamma_b].astype(np.float64) * Qz[idx, x] < P[idx, x]
-    n = int(np.argmin(np.append(accepted, False)))
-    residual = np.maximum(P[n] - Qz[n], 0.0)
-    if not (residual.sum() > 0.0):
-        residual = P[n]
-    c = np.cumsum(residual)
-    hit = np.nonzero(c > float(u[gamma_max]) * c[-1])[0]
-    tok = int(hit[0]) if hit.size else int(np.nonzero(residual > 0)[0][-1])
-    return n, tok
+    return SeqResult(tokens, n, alpha, pq, margin_acc, margin_cdf, margin_topp, zero_residual, topp_pos)
 
 
 # ----------------------------------------------------------------------------
@@ -291,11 +272,12 @@ class BatchResult:
     n: np.ndarray             # int32 [B]
     alpha: np.ndarray         # float64 [B, gamma_max]
     pq: np.ndarray            # float64 [B, gamma_max, 2]
-    margin: np.ndarray        # float64 [B] = min of the three margins
+    margin: np.ndarray        # float64 [B] = min of the three margins (decides n and the tokens)
     margin_acc: np.ndarray
     margin_cdf: np.ndarray
     margin_topp: np.ndarray
     zero_residual: np.ndarray
+    topp_pos: np.ndarray      # float64 [B, gamma_max]: per-position top-p margin (alpha_i, pq_i)
 
 
 _SHARED = {}
@@ -332,7 +314,7 @@ def verify_batch(p_logits, q_logits, draft, u, temperature, top_k, top_p, gamma_
     R = len(rows)
     out = BatchResult(np.full((R, gamma_max + 1), -1, np.int32), np.zeros(R, np.int32),
                       np.zeros((R, gamma_max)), np.zeros((R, gamma_max, 2)), np.zeros(R),
-                      np.zeros(R), np.zeros(R), np.zeros(R), np.zeros(R, bool))
+                      np.zeros(R), np.zeros(R), np.zeros(R), np.zeros(R, bool), np.full((R, gamma_max), INF))
     for k, r in enumerate(res):
         out.tokens[k] = r.tokens
         out.n[k] = r.n
@@ -343,6 +325,7 @@ def verify_batch(p_logits, q_logits, draft, u, temperature, top_k, top_p, gamma_
         out.margin_cdf[k] = r.margin_cdf
         out.margin_topp[k] = r.margin_topp
         out.zero_residual[k] = r.zero_residual
+        out.topp_pos[k] = r.topp_pos
     _SHARED.clear()
     return out
 
@@ -360,30 +343,40 @@ def verify_batch(p_logits, q_logits, draft, u, temperature, top_k, top_p, gamma_
 # Gumbel noise follows the softmax) is the same section's first part.
 #
 # log p_k(i) = z_i / T - log S over the processed support, so the argmax only
-# needs the support and z_i / T + g_i (log S is common to every i), or, after
-# multiplying by T > 0, which keeps the argmax, z_i + T g_i.
-# Readings: the score is formed in float32 as fl(z + fl(T * g)) with no fused
-# multiply-add, the precision of the kernel, so that both sides take the
-# argmax decision on the same numbers; ties go to the lowest id; T = 0 is
-# exact argmax matching (the noise is unused, as in "Draft and verify").
+# needs the support and the score z_i / T + g_i (log S is common to every i).
+# The scores are formed in float64.  Ties go to the lowest id; T = 0 is exact
+# argmax matching (the noise is unused, as in "Draft and verify").
+# Decision margin of one position: the gap between the best and the
+# second-best score over the support, divided by the magnitude of the terms
+# that form them, max(1, |z/T| + |g|) of either: a score computed in any
+# precision with relative rounding e is off by about e times that, so the
+# argmax can only differ from this one where the gap is that small.
 
 def gumbel_scores(z: np.ndarray, g: np.ndarray, T: float) -> np.ndarray:
-    """float32 scores fl(z + fl(T * g)) of one row (z decoded logits, g the
-    row's noise, T > 0)."""
-    z32 = np.asarray(z, dtype=np.float32)
-    tg = (np.float32(T) * np.asarray(g, dtype=np.float32)).astype(np.float32)
-    return (z32 + tg).astype(np.float32)
+    """float64 scores z / T + g of one row (z decoded logits, g the row's
+    noise, T > 0): log p + g up to the row's common -log S."""
+    return np.asarray(z, dtype=np.float64) / T + np.asarray(g, dtype=np.float64)
 
 
-def gumbel_target_token(z: np.ndarray, g: np.ndarray, T: float, top_k: int, top_p: float):
+def gumbel_target_token(z: np.ndarray, g: np.ndarray, T: float, top_k: int, top_p: float, parts: bool = False):
     """The target's sample at one position: the lowest id maximising the
-    score over the processed support.  Returns (token, top-p margin)."""
-    pr = process(z, T, top_k, top_p)
+    score over the processed support.  Returns (token, margin), the margin
+    being the smaller of the score-gap margin and the top-p margin; with
+    parts, (token, margin, top-p margin)."""
     if T == 0.0:
-        return int(np.argmax(z)), INF
-    sc = gumbel_scores(z, g, T)
-    sc = np.where(pr.kept, sc, np.float32(-np.inf))
-    return int(np.argmax(sc)), pr.topp_margin
+        return (int(np.argmax(z)), INF, INF) if parts else (int(np.argmax(z)), INF)
+    pr = process(z, T, top_k, top_p)
+    sc = np.where(pr.kept, gumbel_scores(z, g, T), -np.inf)
+    t = int(np.argmax(sc))
+    margin = pr.topp_margin
+    if pr.kept.sum() > 1:
+        rest = sc.copy()
+        rest[t] = -np.inf
+        t2 = int(np.argmax(rest))
+        size = lambda i: abs(float(z[i]) / T) + abs(float(g[i]))
+        gap = (sc[t] - sc[t2]) / max(1.0, size(t), size(t2))
+        margin = min(margin, float(gap))
+    return (t, margin, pr.topp_margin) if parts else (t, margin)
 
 
 @dataclasses.dataclass
@@ -391,19 +384,22 @@ class GumbelResult:
     tokens: np.ndarray        # int32 [gamma_max+1]: x_1..x_n, then target[n], -1 padded
     n: int                    # drafts kept, -1 for an invalid sequence
     target: np.ndarray        # int32 [gamma_max+1]: the target's sample at each used position
-    margin_topp: float
+    margin: float             # decision margin of n and the tokens (positions 0..n)
+    margin_pos: np.ndarray    # float64 [gamma_max+1]: decision margin of each position's sample
+    topp_pos: np.ndarray      # float64 [gamma_max+1]: its top-p part alone
 
 
 def gumbel_verify_sequence(zp: np.ndarray, g: np.ndarray, draft: np.ndarray, T: float, top_k: int,
                            top_p: float, gamma_b: int) -> GumbelResult:
     """One sequence.  zp: [gamma_max+1, V] target logits (float64), g:
-    [gamma_max+1, V] noise (float32), draft: [gamma_max] proposed tokens.
-    Rows beyond gamma_b are padding and are never read."""
+    [gamma_max+1, V] noise, draft: [gamma_max] proposed tokens.  Rows beyond
+    gamma_b are padding and are never read."""
     gamma_max = zp.shape[0] - 1
     V = zp.shape[1]
     T = float(T)
     top_p = float(top_p)
-    bad = GumbelResult(np.full(gamma_max + 1, -1, np.int32), -1, np.full(gamma_max + 1, -1, np.int32), INF)
+    bad = GumbelResult(np.full(gamma_max + 1, -1, np.int32), -1, np.full(gamma_max + 1, -1, np.int32), INF,
+                       np.full(gamma_max + 1, INF), np.full(gamma_max + 1, INF))
     if not (1 <= gamma_b <= gamma_max) or not (T >= 0.0) or math.isnan(top_p):
         return bad
     x = np.asarray(draft[:gamma_b])
@@ -413,17 +409,16 @@ def gumbel_verify_sequence(zp: np.ndarray, g: np.ndarray, draft: np.ndarray, T: 
         if not row_is_valid(zp[j]):
             return bad
     target = np.full(gamma_max + 1, -1, np.int32)
-    margin = INF
+    margin_pos = np.full(gamma_max + 1, INF)
+    topp_pos = np.full(gamma_max + 1, INF)
     for j in range(gamma_b + 1):
         # Noise off the processed support never takes part in the argmax;
         # a NaN or infinite value on it makes the sequence invalid.
         if T > 0.0:
             kept = process(zp[j], T, top_k, top_p).kept
-            if not np.isfinite(np.asarray(g[j], dtype=np.float32)[kept]).all():
+            if not np.isfinite(np.asarray(g[j], dtype=np.float64)[kept]).all():
                 return bad
-        t, m = gumbel_target_token(zp[j], g[j], T, top_k, top_p)
-        target[j] = t
-        margin = min(margin, m)
+        target[j], margin_pos[j], topp_pos[j] = gumbel_target_token(zp[j], g[j], T, top_k, top_p, parts=True)
     n = gamma_b
     for k in range(gamma_b):
         if int(x[k]) != int(target[k]):
@@ -432,28 +427,7 @@ def gumbel_verify_sequence(zp: np.ndarray, g: np.ndarray, draft: np.ndarray, T: 
     tokens = np.full(gamma_max + 1, -1, np.int32)
     tokens[:n] = x[:n]
     tokens[n] = target[n]
-    return GumbelResult(tokens, n, target, margin)
-
-
-def gumbel_verify_listing_form(zp, zq, g, T, gamma_b):
-    """Second formulation, following the structure of the JAX
-    `gumbel_verify` listing on the same page (unfiltered rows): the draft is
-    the drafter's argmax of log q + g on the first gamma_b noise rows, the
-    target's samples are the argmax of log p + g on all gamma_b + 1 rows, and
-    n is the first False of (draft == target[:-1]) || False.  log-softmax
-    values are formed in float64 here (a different rounding path from the
-    main formulation).  Returns (draft, n, token)."""
-    def logsoftmax(z):
-        s = np.asarray(z, dtype=np.float64) / T
-        m = s.max()
-        return s - (m + np.log(np.exp(s - m).sum()))
-    gb = np.asarray(g, dtype=np.float64)
-    lq = np.stack([logsoftmax(zq[i]) for i in range(gamma_b)])
-    lp = np.stack([logsoftmax(zp[j]) for j in range(gamma_b + 1)])
-    draft = np.argmax(lq + gb[:gamma_b], axis=-1)
-    target = np.argmax(lp + gb[:gamma_b + 1], axis=-1)
-    n = int(np.argmin(np.append(draft == target[:-1], False)))
-    return draft.astype(np.int32), n, int(target[n])
+    return GumbelResult(tokens, n, target, float(margin_pos[: n + 1].min()), margin_pos, topp_pos)
 
 
 @dataclasses.dataclass
@@ -461,25 +435,46 @@ class GumbelBatchResult:
     tokens: np.ndarray        # int32 [B, gamma_max+1]
     n: np.ndarray             # int32 [B]
     target: np.ndarray        # int32 [B, gamma_max+1]
-    margin_topp: np.ndarray   # float64 [B]
+    margin: np.ndarray        # float64 [B]: decision margin of n and the tokens
+    margin_pos: np.ndarray    # float64 [B, gamma_max+1]: decision margin of each target sample
+    topp_pos: np.ndarray      # float64 [B, gamma_max+1]: its top-p part alone
+
+
+_GSHARED = {}
+
+
+def _gumbel_one(b: int) -> GumbelResult:
+    a = _GSHARED
+    return gumbel_verify_sequence(decode_row(a["p"][b]), a["noise"][b], np.asarray(a["draft"][b]), float(a["T"][b]),
+                                  int(a["k"][b]), float(a["top_p"][b]), int(a["g"][b]))
 
 
 def gumbel_verify_batch(p_logits, noise, draft, temperature, top_k, top_p, gamma_len,
-                        rows: Optional[Sequence[int]] = None) -> GumbelBatchResult:
-    """The Gumbel-coupling verify over the sequences in ``rows`` (serial)."""
+                        rows: Optional[Sequence[int]] = None, processes: int = 1) -> GumbelBatchResult:
+    """The Gumbel-coupling verify over the sequences in ``rows`` (default:
+    all), on `processes` worker processes (fork; 1 = serial)."""
     B = p_logits.shape[0]
     G1 = p_logits.shape[1]
     rows = list(range(B)) if rows is None else list(rows)
     R = len(rows)
+    _GSHARED.update(p=p_logits, noise=noise, draft=draft, T=np.asarray(temperature), k=np.asarray(top_k),
+                    top_p=np.asarray(top_p), g=np.asarray(gamma_len))
+    nproc = max(1, min(processes, R))
+    if nproc == 1:
+        res = [_gumbel_one(b) for b in rows]
+    else:
+        with mp.get_context("fork").Pool(nproc) as pool:
+            res = pool.map(_gumbel_one, rows, chunksize=max(1, R // (4 * nproc)))
+    _GSHARED.clear()
     out = GumbelBatchResult(np.full((R, G1), -1, np.int32), np.zeros(R, np.int32), np.full((R, G1), -1, np.int32),
-                            np.zeros(R))
-    for k, b in enumerate(rows):
-        r = gumbel_verify_sequence(decode_row(p_logits[b]), noise[b], np.asarray(draft[b]), float(temperature[b]),
-                                   int(top_k[b]), float(top_p[b]), int(gamma_len[b]))
+                            np.zeros(R), np.full((R, G1), INF), np.full((R, G1), INF))
+    for k, r in enumerate(res):
         out.tokens[k] = r.tokens
         out.n[k] = r.n
         out.target[k] = r.target
-        out.margin_topp[k] = r.margin_topp
+        out.margin[k] = r.margin
+        out.margin_pos[k] = r.margin_pos
+        out.topp_pos[k] = r.topp_pos
     return out
 
 

@@ -57,15 +57,29 @@ def run_oracle(bt, processes=1):
 @dataclasses.dataclass
 class Report:
     rows: int
-    near: int            # rows with a decision margin below TOL
-    near_differ: int     # of those, rows whose n or tokens differ
+    near: int            # sequences whose n / tokens decision margin is below TOL
+    near_differ: int     # of those, sequences whose n or tokens differ
     max_alpha_err: float
     max_pq_err: float
     invalid: int
+    positions: int       # used draft positions of the valid sequences
+    compared: int        # of those, positions whose alpha and p(x), q(x) were compared
+
+    @property
+    def compared_share(self):
+        return self.compared / self.positions if self.positions else 1.0
 
 
-def compare(bt, g: GpuOut, ref, label=""):
-    """Assert the parity rules; return counts for reporting."""
+def compare(bt, g: GpuOut, ref, label="", min_compared_share=None):
+    """Assert the parity rules; return counts for reporting.
+
+    n and the tokens must match wherever the oracle's decision margin (the
+    acceptance tests made, the draw, and the nucleus boundaries of the rows
+    that decided them) is at least TOL.  alpha_i and (p_i(x_i), q_i(x_i))
+    must be within TOL at every position whose two rows have no nucleus
+    boundary within TOL; padded positions must hold 0.  With
+    min_compared_share, at least that share of the valid sequences' used
+    positions must have been compared."""
     near = ref.margin < TOL
     same = (g.n == ref.n) & (g.tokens == ref.tokens).all(axis=1)
     bad = ~same & ~near
@@ -79,15 +93,23 @@ def compare(bt, g: GpuOut, ref, label=""):
     invalid = ref.n < 0
     assert (g.n[invalid] == -1).all() and (g.tokens[invalid] == -1).all(), f"{label}: sentinel rows"
     assert np.isnan(g.alpha[invalid]).all(), f"{label}: sentinel alpha"
-    # Overlap and probabilities: every valid row whose top-p boundaries are
-    # not within the margin.
-    cmp_rows = ~invalid & (ref.margin_topp >= TOL)
-    ea = np.abs(g.alpha[cmp_rows] - ref.alpha[cmp_rows])
-    ep = np.abs(g.pq[cmp_rows] - ref.pq[cmp_rows])
+    # Overlap and probabilities, position by position.
+    G = ref.alpha.shape[1]
+    used = np.arange(G)[None, :] < np.asarray(bt.gamma_len)[:, None]
+    cmp_pos = ~invalid[:, None] & (ref.topp_pos >= TOL)
+    ea = np.where(cmp_pos, np.abs(g.alpha - ref.alpha), 0.0)
+    ep = np.where(cmp_pos[:, :, None], np.abs(g.pq - ref.pq), 0.0)
     max_a = float(ea.max()) if ea.size else 0.0
     max_p = float(ep.max()) if ep.size else 0.0
-    if max_a > TOL or max_p > TOL:
-        ia = np.unravel_index(int(np.argmax(np.abs(g.alpha - ref.alpha) * cmp_rows[:, None])), g.alpha.shape)
+    if max_a > TOL or max_p > TOL or np.isnan(max_a) or np.isnan(max_p):
+        ia = np.unravel_index(int(np.nanargmax(ea)), g.alpha.shape)
         raise AssertionError(f"{label}: alpha err {max_a:.3g}, pq err {max_p:.3g}; worst alpha at {ia}: "
                              f"gpu {g.alpha[ia]} oracle {ref.alpha[ia]}")
-    return Report(int(len(g.n)), int(near.sum()), int((near & ~same).sum()), max_a, max_p, int(invalid.sum()))
+    positions = int((used & ~invalid[:, None]).sum())
+    compared = int((used & cmp_pos).sum())
+    rep = Report(int(len(g.n)), int(near.sum()), int((near & ~same).sum()), max_a, max_p, int(invalid.sum()),
+                 positions, compared)
+    if min_compared_share is not None:
+        assert rep.compared_share >= min_compared_share, \
+            f"{label}: alpha / pq compared on {compared} of {positions} positions ({rep.compared_share:.3f})"
+    return rep

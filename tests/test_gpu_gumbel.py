@@ -1,8 +1,12 @@
 """Shared-noise (Gumbel coupling) verify on the GPU, through the C ABI,
-against the CPU oracle on the same seeded inputs.  The target's samples, n
-and every output token must be identical, except in sequences whose top-p
-boundary masses lie within 1e-5 of top_p (where the kept set itself is
-decided by rounding); those are counted."""
+against the CPU oracle on the same seeded inputs.  The oracle takes each
+target sample as the float64 argmax of log p + g over the processed support;
+the kernel forms the same argmax in float32.  n and every output token must
+be identical except in sequences whose decision margin (the relative gap
+between the best two scores, or a nucleus boundary, at a position that
+decided them) is below 1e-5; each position's target sample must be identical
+except where that position's own margin is below 1e-5.  Near cases are
+counted."""
 import dataclasses
 
 import numpy as np
@@ -32,24 +36,39 @@ def run_gpu_gumbel(gb, dev="cuda:0", pass_gamma=True, with_params=True, hints=0,
     return tok.cpu().numpy(), n.cpu().numpy(), tgt.cpu().numpy()
 
 
-def check_gumbel(gb, label, rows=None, hints=0, calls=1):
+def check_gumbel(gb, label, hints=0, calls=1, exact_scores=False, min_compared_share=None):
+    """Compare every sequence.  exact_scores: the inputs are chosen so that
+    every score is exact in float32 and float64 (small integers and halves),
+    so ties are true ties on both sides and only the top-p part of the margin
+    excludes anything."""
     log(f"[gumbel] {label}: B={gb.B} V={gb.V} gamma_max={gb.gamma_max} dtype={gb.p_logits.dtype} hints={hints}")
     tok, n, tgt = run_gpu_gumbel(gb, hints=hints, calls=calls)
-    rows = list(range(gb.B)) if rows is None else list(rows)
     ref = oracle.gumbel_verify_batch(gb.p_logits, gb.noise, gb.draft, gb.temperature, gb.top_k, gb.top_p,
-                                     gb.gamma_len, rows=rows)
-    near = ref.margin_topp < TOL
-    same = (n[rows] == ref.n) & (tok[rows] == ref.tokens).all(1) & (tgt[rows] == ref.target).all(1)
+                                     gb.gamma_len, processes=8)
+    mpos = ref.topp_pos if exact_scores else ref.margin_pos
+    G1 = gb.gamma_max + 1
+    used = (np.arange(G1)[None, :] <= np.asarray(gb.gamma_len)[:, None]) & (ref.n >= 0)[:, None]
+    # n and the tokens: decided by positions 0..n.
+    decide = np.arange(G1)[None, :] <= np.maximum(ref.n, 0)[:, None]
+    near = np.where(decide, mpos, np.inf).min(axis=1) < TOL
+    same = (n == ref.n) & (tok == ref.tokens).all(1)
     bad = ~same & ~near
-    if bad.any():
-        i = int(np.nonzero(bad)[0][0])
-        b = rows[i]
-        raise AssertionError(f"{label}: {int(bad.sum())} sequences differ; first b={b}: gpu n={n[b]} "
-                             f"tokens={tok[b].tolist()} target={tgt[b].tolist()} | oracle n={ref.n[i]} "
-                             f"tokens={ref.tokens[i].tolist()} target={ref.target[i].tolist()} "
-                             f"T={gb.temperature[b]} k={gb.top_k[b]} top_p={gb.top_p[b]} gamma={gb.gamma_len[b]}")
-    log(f"[gumbel] {label}: ok, {len(rows)} sequences, near-margin {int(near.sum())} "
-        f"(differ {int((near & ~same).sum())}), mean tokens/round {np.mean(ref.n[ref.n >= 0] + 1):.3f}")
+    # Each position's target sample (and -1 beyond gamma_b and for invalid sequences).
+    cmp_pos = mpos >= TOL
+    tbad = (tgt != ref.target) & cmp_pos
+    if bad.any() or tbad.any():
+        b = int(np.nonzero(bad | tbad.any(1))[0][0])
+        raise AssertionError(f"{label}: {int(bad.sum())} sequences and {int(tbad.sum())} target samples differ; "
+                             f"first b={b}: gpu n={n[b]} tokens={tok[b].tolist()} target={tgt[b].tolist()} | "
+                             f"oracle n={ref.n[b]} tokens={ref.tokens[b].tolist()} target={ref.target[b].tolist()} "
+                             f"margins={np.round(mpos[b], 8).tolist()} T={gb.temperature[b]} k={gb.top_k[b]} "
+                             f"top_p={gb.top_p[b]} gamma={gb.gamma_len[b]}")
+    positions, compared = int(used.sum()), int((used & cmp_pos).sum())
+    log(f"[gumbel] {label}: ok, {gb.B} sequences, near-margin {int(near.sum())} (differ {int((near & ~same).sum())}), "
+        f"target samples compared at {compared} of {positions} positions, "
+        f"mean tokens/round {np.mean(ref.n[ref.n >= 0] + 1) if (ref.n >= 0).any() else 0:.3f}")
+    if min_compared_share is not None and positions:
+        assert compared / positions >= min_compared_share, (label, compared, positions)
     return tok, n, tgt, ref
 
 
@@ -70,20 +89,19 @@ def test_gumbel_workload_small(cid, B, V):
     check_gumbel(gb, f"workload{cid}-B{B}-V{gb.V}")
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
-def test_gumbel_workload_full_size_sampled(cid):
-    # The full shapes on the GPU; the oracle checks a sample of sequences.
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
+def test_gumbel_workload_full_size(cid):
+    # The full shapes, every sequence against the oracle.
     gb = synth.make_gumbel_batch(cid)
-    rng = np.random.default_rng(cid)
-    rows = sorted(rng.choice(gb.B, size=min(gb.B, 24), replace=False).tolist())
-    check_gumbel(gb, f"workload{cid}-full", rows=rows)
+    check_gumbel(gb, f"workload{cid}-full", min_compared_share=0.95)
     # bench.py's launch configuration: with no argmax or small-top-k sequence
     # it passes the all-dense hint.
     T, k = gb.temperature, gb.top_k
     listed = (T == 0) | ((T > 0) & (k > 0) & (k < gb.V) & (k <= 512))
     if not listed.any():
         from speculative_sampling_verification_verify_amd import binding
-        check_gumbel(gb, f"workload{cid}-full-all-dense-hint", rows=rows, hints=binding.SV_HINT_ALL_DENSE)
+        check_gumbel(gb, f"workload{cid}-full-all-dense-hint", hints=binding.SV_HINT_ALL_DENSE,
+                     min_compared_share=0.95)
 
 
 def _replace(gb, **kw):
@@ -137,7 +155,7 @@ def test_gumbel_ties_go_to_lowest_id():
     ref = oracle.gumbel_verify_batch(gb.p_logits, gb.noise, gb.draft, gb.temperature, gb.top_k, gb.top_p,
                                      gb.gamma_len)
     gb.draft[:, :] = np.where(np.arange(G)[None, :] % 2 == 0, ref.target[:, :G], gb.draft)   # some matches
-    check_gumbel(gb, "ties")
+    check_gumbel(gb, "ties", exact_scores=True)
 
 
 def test_gumbel_large_gamma_tiny_vocab_null_params():
@@ -159,7 +177,9 @@ def test_gumbel_large_gamma_tiny_vocab_null_params():
     tok, n, tgt = run_gpu_gumbel(gb2, pass_gamma=False, with_params=False)
     ref = oracle.gumbel_verify_batch(gb2.p_logits, gb2.noise, gb2.draft, gb2.temperature, np.zeros(4, np.int32),
                                      np.ones(4, np.float32), np.full(4, gb2.gamma_max, np.int32))
-    assert (n == ref.n).all() and (tok == ref.tokens).all() and (tgt == ref.target).all()
+    ok = ref.margin >= TOL
+    assert (n == ref.n)[ok].all() and (tok == ref.tokens)[ok].all()
+    assert ((tgt == ref.target) | (ref.margin_pos < TOL)).all()
 
 
 def test_gumbel_gpu_samples_follow_target_chi_square():

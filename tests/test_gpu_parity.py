@@ -20,11 +20,11 @@ def batch_from(bt, **over):
     return synth.Batch(**d)
 
 
-def check(bt, label):
+def check(bt, label, min_compared_share=None):
     log(f"[parity] {label}: B={bt.B} V={bt.V} gamma_max={bt.gamma_max} dtype={bt.p_logits.dtype}")
     g = run_gpu(bt)
     ref = run_oracle(bt)
-    rep = compare(bt, g, ref, label)
+    rep = compare(bt, g, ref, label, min_compared_share)
     log(f"[parity] {label}: ok {rep}")
     return g, ref, rep
 
@@ -67,7 +67,9 @@ def test_workload_full_size(cid):
     # Without hints, and in the launch configuration bench.py times.
     from speculative_sampling_verification_verify_amd import binding
     bt = synth.make_batch(cid)
-    _, ref, rep = check(bt, f"workload{cid}-full")
+    # alpha and p(x), q(x) are compared at all but the few positions whose
+    # rows have a nucleus boundary within the margin.
+    _, ref, rep = check(bt, f"workload{cid}-full", min_compared_share=0.95)
     hints = bench_hints(bt)
     if hints:
         dt = binding.SV_BF16 if bt.p_logits.dtype == np.uint16 else binding.SV_FP32
@@ -76,7 +78,7 @@ def test_workload_full_size(cid):
         log(f"[parity] workload{cid}-full with hints {hints}: ok")
     log(f"[parity] workload{cid}-full: mean alpha {np.nanmean(ref.alpha[ref.alpha > 0]):.3f}, "
         f"mean tokens/round {np.mean(ref.n[ref.n >= 0] + 1):.3f}, near-margin rows {rep.near}, "
-        f"of which differ {rep.near_differ}")
+        f"of which differ {rep.near_differ}; alpha/pq compared at {rep.compared} of {rep.positions} positions")
 
 
 # --------------------------------------------------------------------------

@@ -6,18 +6,23 @@ softmax; with the noise shared, the drafter's and the target's samples agree
 with probability sum_j 1 / sum_i max(p(i)/p(j), q(i)/q(j)), at least
 (1 - TV) / (1 + TV); with independent noise they agree with probability
 sum_i p(i) q(i); the output is the target's own sample under that noise,
-whatever the drafter; greedy decoding is the T = 0 case.  The JAX listing on
-the same page gives a second formulation of the step.  None of these tests
-re-types the oracle's own code path."""
+whatever the drafter; greedy decoding is the T = 0 case.  The decision
+margin (the best two scores' gap relative to the size of their terms) is
+pinned by float32 scoring computed here: outside the margin it picks the
+oracle's token at every temperature, and a planted mistake in the margin
+fails that pin.  None of these tests re-types the oracle's own code path."""
+import inspect
 import json
 import math
 import os
+import textwrap
 
 import numpy as np
 from scipy import stats
 
 import oracle
-from oracle.verify import gumbel_target_token, gumbel_verify_sequence, gumbel_verify_listing_form, verify_sequence
+from oracle import verify as verify_mod
+from oracle.verify import gumbel_target_token, gumbel_verify_sequence, verify_sequence
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -182,26 +187,65 @@ def test_greedy_is_exact_matching():
         assert a.n == b.n and (a.tokens == b.tokens).all(), trial
 
 
-def test_listing_formulation_agrees():
-    # The page's JAX listing (drafter and target argmaxes on the same noise,
-    # first mismatch by argmin) computed in float64 log-softmax form, against
-    # the main formulation fed with the listing's drafts.  The two round
-    # differently, so rows whose best two scores are within 1e-5 may differ.
-    rng = np.random.default_rng(9)
-    G, V = 4, 200
-    differ = 0
-    for trial in range(200):
-        zp = rng.normal(size=(G + 1, V)) * 3
-        zq = zp[:G] + rng.normal(size=(G, V)) * 0.5
-        g = gumbel(rng, (G + 1, V))
-        T = float(rng.choice([0.6, 1.0, 1.4]))
-        draft, n, tok = gumbel_verify_listing_form(zp, zq, g, T, G)
-        r = gumbel_verify_sequence(zp, g, draft, T, 0, 1.0, G)
-        if (r.n, int(r.tokens[r.n])) != (n, tok):
-            sc = np.sort(zp / T + g, axis=1)
-            assert (sc[:, -1] - sc[:, -2]).min() < 1e-5, trial
-            differ += 1
-    assert differ <= 2
+def float32_sample(z, g, T, kept):
+    """The argmax, lowest id on ties, of the score T (z / T + g) formed in
+    float32 as fl(z + fl(T g)): the same decision at another precision."""
+    sc = (np.float32(z) + (np.float32(T) * np.asarray(g, np.float32)).astype(np.float32)).astype(np.float32)
+    return int(np.argmax(np.where(kept, sc, np.float32(-np.inf))))
+
+
+def margin_pin_disagreements(token_fn, seed=21, rows=1200):
+    """Rows where float32 scoring picks another token although the margin
+    says the decision is not near (margin >= 1e-5), and the near count.
+    Half the rows have a tied maximum: at tiny T the noise then decides
+    between values that float32 can hardly tell apart."""
+    rng = np.random.default_rng(seed)
+    bad = near = 0
+    for r in range(rows):
+        V = int(rng.integers(50, 2000))
+        z = np.round(rng.normal(size=V) * 3 * 128) / 128            # bf16-like values: many ties
+        if r % 2:
+            z[int(rng.integers(V))] = z.max()
+        g = gumbel(rng, V)
+        T = float(rng.choice([1e-7, 1e-6, 1e-5, 1e-3, 0.6, 1.0, 1.4, 50.0]))
+        k = int(rng.choice([0, 0, 40]))
+        tp = float(rng.choice([1.0, 1.0, 0.9]))
+        t, m = token_fn(z, g, T, k, tp)
+        kept = oracle.process(z, T, k, tp).kept
+        if m < 1e-5:
+            near += 1
+        elif float32_sample(z, g, T, kept) != t:
+            bad += 1
+    return bad, near
+
+
+def test_margin_covers_float32_scoring():
+    bad, near = margin_pin_disagreements(gumbel_target_token)
+    assert bad == 0
+    assert near < 300          # mostly rows at T <= 1e-5 with a tied maximum, and top-p boundaries
+
+
+def test_margin_pin_rejects_an_unscaled_gap():
+    src = textwrap.dedent(inspect.getsource(verify_mod.gumbel_target_token))
+    old = "gap = (sc[t] - sc[t2]) / max(1.0, size(t), size(t2))"
+    assert old in src
+    ns = dict(vars(verify_mod))
+    exec(compile(src.replace(old, "gap = sc[t] - sc[t2]"), "<planted mistake>", "exec"), ns)
+    bad, _ = margin_pin_disagreements(ns["gumbel_target_token"])
+    assert bad > 0
+
+
+def test_margin_of_a_tie_and_of_a_single_survivor():
+    z = np.array([1.0, 3.0, 3.0, -2.0])
+    g = np.zeros(4, np.float32)
+    t, m = gumbel_target_token(z, g, 1.0, 0, 1.0)
+    assert t == 1 and m == 0.0                 # an exact tie: lowest id, no margin
+    t, m = gumbel_target_token(z, g, 1.0, 1, 1.0)
+    assert t == 1 and m == 0.0                 # top-1 keeps both tied values
+    t, m = gumbel_target_token(np.array([1.0, 3.0, 2.0]), g[:3], 1.0, 1, 1.0)
+    assert t == 1 and m == math.inf            # one survivor: nothing to decide
+    t, m = gumbel_target_token(z, g, 0.0, 0, 1.0)
+    assert t == 1 and m == math.inf            # greedy: exact on the logits
 
 
 def test_ties_go_to_the_lowest_id_and_bad_inputs_are_flagged():

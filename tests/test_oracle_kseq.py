@@ -11,9 +11,22 @@ K-SEQ does not; the page's two-token example bounds the hit rate between the
 single-candidate 0.7 and the optimal-transport 0.94; with one candidate the
 method is the single-candidate test, and a SpecTr round with K = 1 is the
 ordinary verify.  Exact integration runs over the oracle's own decisions
-(thresholds found by bisection), not over re-typed formulas."""
+(thresholds found by bisection), not over re-typed formulas.
+
+The SpecTr walk (section "SpecTr": candidates filtered by the output prefix,
+the walk ends when the output misses the candidates) is pinned on its own
+output: over candidate sets drawn from a prefix-dependent drafter, the
+round's tokens, completed by fresh target draws where the round ended early,
+must follow the target's chain p0(y1) p1(y2 | y1) p2(y3 | y1, y2), and every
+round must obey the stop rule.  Planted mistakes in a copy of the walk (a
+filter on the wrong depth, rows taken from the wrong candidate, no stop) must
+fail the pin."""
+import inspect
 import itertools
 import math
+import multiprocessing as mp
+import os
+import textwrap
 
 import numpy as np
 import pytest
@@ -231,3 +244,93 @@ def test_rho_star_at_large_k_is_the_saturation_point():
             assert abs(rho - r_max) <= 1e-9 * r_max, (trial, k, rho, r_max)
             checked += 1
     assert checked >= 10
+
+
+# --------------------------------------------------------------------------
+# The SpecTr walk beyond the first depth, K > 1.
+# --------------------------------------------------------------------------
+WV, WL = 3, 2
+W_P0 = np.array([0.5, 0.3, 0.2])                                     # target at depth 0
+W_P1 = np.array([[0.1, 0.2, 0.7], [0.6, 0.1, 0.3], [0.3, 0.6, 0.1]])  # target after y1
+W_P2 = np.array([[np.roll([0.7, 0.2, 0.1], (a + 2 * b) % 3) for b in range(3)] for a in range(3)])  # after (y1, y2)
+W_Q0 = np.array([0.2, 0.5, 0.3])                                     # drafter at depth 0
+W_Q1 = np.array([np.roll([0.5, 0.3, 0.2], a) for a in range(3)])      # drafter after y1
+
+# Planted mistakes: (text in the walk, replacement).
+WALK_MUTATIONS = {
+    "filter on the first depth": ("if int(cand[c, j]) == r.token", "if int(cand[c, 0]) == r.token"),
+    "rows of candidate 0": ("c0 = alive[0]", "c0 = 0"),
+    "no stop when the output misses": ("        if not alive:\n            return SpecTrResult(out, j, margin)",
+                                       "        if not alive:\n            alive = list(range(K))"),
+}
+
+
+def _walk(mutation):
+    if mutation is None:
+        return kseq.spectr_sequence
+    src = textwrap.dedent(inspect.getsource(kseq.spectr_sequence))
+    old, new = WALK_MUTATIONS[mutation]
+    assert old in src, mutation
+    ns = dict(vars(kseq))
+    exec(compile(src.replace(old, new, 1), "<planted mistake>", "exec"), ns)
+    return ns["spectr_sequence"]
+
+
+def _walk_rounds(args):
+    """Counts of the completed (y1, y2, y3) and the number of rounds that
+    break the stop rule, over n rounds."""
+    mutation, K, seed, n = args
+    walk = _walk(mutation)
+    rng = np.random.default_rng(seed)
+    counts = np.zeros((WV, WV, WV))
+    broken = 0
+    for _ in range(n):
+        first = rng.choice(WV, size=K, p=W_Q0)
+        cand = np.stack([first, [rng.choice(WV, p=W_Q1[a]) for a in first]], axis=1).astype(np.int32)
+        # Row j of candidate c: the model after c's first j tokens.
+        zp = np.stack([np.stack([logit(W_P0), logit(W_P1[a]), logit(W_P2[a, b])]) for a, b in cand])
+        zq = np.stack([np.stack([logit(W_Q0), logit(W_Q1[a])]) for a, b in cand])
+        r = walk(zp, zq, cand, rng.random((WL + 1, K + 1)), 1.0, 0, 1.0)
+        y = [int(t) for t in r.tokens[: r.n + 1]]
+        # Stop rule: every output before the last continues a candidate
+        # prefix; a round that ended before depth L ended on an output that
+        # is not one.
+        prefixes = {tuple(int(t) for t in cand[c, :j]) for c in range(K) for j in range(1, WL + 1)}
+        ok = len(y) == r.n + 1 and all(tuple(y[: j + 1]) in prefixes for j in range(r.n))
+        if r.n < WL:
+            ok = ok and tuple(y) not in prefixes
+        broken += not ok
+        # The next rounds would continue from the target: complete with it.
+        if len(y) < 2:
+            y.append(int(rng.choice(WV, p=W_P1[y[0]])))
+        if len(y) < 3:
+            y.append(int(rng.choice(WV, p=W_P2[y[0], y[1]])))
+        counts[tuple(y)] += 1
+    return counts, broken
+
+
+def walk_law(mutation, K, rounds, seed):
+    """(chi-square p-value of the completed outputs against the target's
+    chain, rounds breaking the stop rule)."""
+    chunks = 8
+    args = [(mutation, K, seed * 100 + c, rounds // chunks) for c in range(chunks)]
+    with mp.get_context("fork").Pool(min(chunks, os.cpu_count() or 1)) as pool:
+        parts = pool.map(_walk_rounds, args)
+    counts = sum(c for c, _ in parts)
+    broken = sum(b for _, b in parts)
+    expected = W_P0[:, None, None] * W_P1[:, :, None] * W_P2 * counts.sum()
+    return stats.chisquare(counts.ravel(), expected.ravel()).pvalue, broken
+
+
+@pytest.mark.parametrize("K", [2, 3])
+def test_spectr_walk_follows_the_target_chain(K):
+    pv, broken = walk_law(None, K, 24000, seed=K)
+    assert broken == 0
+    assert pv > 1e-4, pv
+
+
+@pytest.mark.parametrize("mutation", sorted(WALK_MUTATIONS))
+def test_spectr_walk_pin_rejects_planted_mistakes(mutation):
+    for K in (2, 3):
+        pv, broken = walk_law(mutation, K, 8000, seed=10 + K)
+        assert broken > 0 or pv < 1e-8, (mutation, K, pv, broken)

@@ -12,7 +12,7 @@ import pytest
 from scipy import stats
 
 import oracle
-from oracle.verify import process, inverse_cdf, verify_sequence, verify_sequence_vectorised, verify_batch, decode_row
+from oracle.verify import process, inverse_cdf, verify_sequence, verify_batch, decode_row
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -403,26 +403,37 @@ def test_argmax_lowest_index():
 
 
 # ----------------------------------------------------------------------------
-# P11: two control-flow formulations agree.
+# Control flow: the first rejection ends the round (Algorithm 1, step 3; the
+# tests are made left to right and the extra token is drawn at the rejected
+# position).  Rows and uniforms after it decide nothing: cutting the round at
+# the rejection, or spoiling what follows it, changes no output.
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("seed", range(60))
-def test_two_formulations_agree(seed):
+@pytest.mark.parametrize("seed", range(40))
+def test_the_first_rejection_ends_the_round(seed):
     rng = np.random.default_rng(600 + seed)
     V = int(rng.integers(3, 40))
-    G = int(rng.integers(1, 6))
-    gb = int(rng.integers(1, G + 1))
+    G = int(rng.integers(2, 7))
     zp = rng.normal(size=(G + 1, V)) * 2
-    zq = zp[:G] + rng.normal(size=(G, V)) * rng.choice([0.1, 1.0, 3.0])
-    if seed % 5 == 0:
-        zq[:, : V // 3] = -np.inf
+    zq = zp[:G] + rng.normal(size=(G, V)) * rng.choice([0.3, 1.0, 3.0])
     T = float(rng.choice([0.0, 0.5, 1.0, 1.3]))
     k = int(rng.choice([0, 1, 3, V]))
     tp = float(rng.choice([1.0, 0.9, 0.5]))
     draft = rng.integers(0, V, size=G).astype(np.int32)
     u = rng.random(G + 1)
-    a = verify_sequence(zp, zq, draft, u, T, k, tp, gb)
-    n, tok = verify_sequence_vectorised(zp, zq, draft, u, T, k, tp, gb)
-    assert a.n == n and a.tokens[a.n] == tok
+    a = verify_sequence(zp, zq, draft, u, T, k, tp, G)
+    if a.n >= G - 1:
+        return
+    n = a.n
+    cut = verify_sequence(zp, zq, draft, u, T, k, tp, n + 1)                # the round ends at the rejection
+    assert cut.n == n and list(cut.tokens[: n + 1]) == list(a.tokens[: n + 1])
+    zp2, zq2, d2, u2 = zp.copy(), zq.copy(), draft.copy(), u.copy()
+    zp2[n + 1:] = rng.normal(size=(G - n, V)) * 5                           # spoil everything after it
+    zq2[n + 1:] = rng.normal(size=(G - n - 1, V)) * 5
+    d2[n + 1:] = rng.integers(0, V, size=G - n - 1)
+    u2[n + 1:G] = rng.random(G - n - 1)
+    b = verify_sequence(zp2, zq2, d2, u2, T, k, tp, G)
+    assert b.n == n and list(b.tokens) == list(a.tokens)
+    assert np.array_equal(b.alpha[: n + 1], a.alpha[: n + 1]) and np.array_equal(b.pq[: n + 1], a.pq[: n + 1])
 
 
 # ----------------------------------------------------------------------------
@@ -513,3 +524,194 @@ def test_topp_mass_exactly_at_threshold(cut):
     pr = process(z, 1.0, 0, float(cum[cut]))
     assert pr.kept.sum() == cut + 1
     assert set(np.nonzero(pr.kept)[0]) == set(order[: cut + 1].tolist())
+
+
+# ----------------------------------------------------------------------------
+# Decision margins against the oracle's own decisions.  A margin says how far
+# a uniform (or top_p) is from the point where the output would change; the
+# change points are found by bisection on the outputs, with nothing re-typed.
+# The pins must also reject planted mistakes (margins in unnormalised units,
+# a missing side) in copies of the oracle's functions.
+# ----------------------------------------------------------------------------
+import inspect
+import textwrap
+
+from oracle import verify as verify_mod
+
+
+def oracle_with(replacements):
+    """verify_sequence and process of a copy of the oracle module in which
+    each (function name, old text, new text) replacement has been made."""
+    ns = dict(vars(verify_mod))
+    for fname in ("process", "inverse_cdf", "verify_sequence"):
+        src = textwrap.dedent(inspect.getsource(getattr(verify_mod, fname)))
+        for name, old, new in replacements:
+            if name == fname:
+                assert old in src, (fname, old)
+                src = src.replace(old, new)
+        exec(compile(src, f"<oracle copy: {fname}>", "exec"), ns)
+    return ns["verify_sequence"], ns["process"]
+
+
+def bisect_edge(pred, good, bad, steps=90):
+    """The point between `good` (pred True) and `bad` (pred False) where pred
+    changes, for pred True on an interval around `good`."""
+    for _ in range(steps):
+        mid = 0.5 * (good + bad)
+        if pred(mid):
+            good = mid
+        else:
+            bad = mid
+    return 0.5 * (good + bad)
+
+
+def margin_cases(n_cases, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(n_cases):
+        V = int(rng.integers(5, 16))
+        G = int(rng.integers(1, 5))
+        T = float(rng.choice([0.7, 1.0, 1.4]))
+        zp = rng.normal(size=(G + 1, V)) * 1.5
+        zq = zp[:G] + rng.normal(size=(G, V)) * 0.8
+        Q = [process(zq[i], T, 0, 1.0).prob for i in range(G)]
+        draft = np.array([int(rng.choice(V, p=Q[i])) for i in range(G)], np.int32)   # on the draft's support
+        yield zp, zq, draft, rng.random(G + 1), T, G
+
+
+def acc_margin_by_bisection(vfn, zp, zq, draft, u, T, G, i):
+    """(change point of the test at position i in u_i, or None when the test
+    accepts on all of [0, 1))."""
+    def accepted(x):
+        uu = u.copy()
+        uu[i] = x
+        return vfn(zp, zq, draft, uu, T, 0, 1.0, G).n > i
+    if not accepted(0.0):
+        return 0.0
+    if accepted(np.nextafter(1.0, 0.0)):
+        return None
+    return bisect_edge(accepted, 0.0, 1.0)
+
+
+def check_margin_acc(vfn, cases):
+    for zp, zq, draft, u, T, G in cases:
+        r = vfn(zp, zq, draft, u, T, 0, 1.0, G)
+        flip, edge = np.inf, np.inf
+        for i in range(min(r.n + 1, G)):            # the tests that were made
+            a = acc_margin_by_bisection(vfn, zp, zq, draft, u, T, G, i)
+            if a is None:
+                edge = min(edge, 1.0 - u[i])        # ratio >= 1: |u - ratio| >= 1 - u
+            else:
+                flip = min(flip, abs(u[i] - a))
+        assert r.margin_acc <= flip + 1e-12, (r.margin_acc, flip)
+        assert r.margin_acc >= min(flip, edge) - 1e-12, (r.margin_acc, flip, edge)
+
+
+def check_margin_cdf(vfn, cases):
+    for zp, zq, draft, u, T, G in cases:
+        r = vfn(zp, zq, draft, u, T, 0, 1.0, G)
+        ur = float(u[G])
+
+        def token(x):
+            uu = u.copy()
+            uu[G] = x
+            return int(vfn(zp, zq, draft, uu, T, 0, 1.0, G).tokens[r.n])
+        t = token(ur)
+        same = lambda x: token(x) == t
+        lo = 0.0 if same(0.0) else bisect_edge(same, ur, 0.0)
+        hi = 1.0 if same(np.nextafter(1.0, 0.0)) else bisect_edge(same, ur, 1.0)
+        assert abs(r.margin_cdf - min(ur - lo, hi - ur)) < 1e-12, (r.margin_cdf, ur, lo, hi)
+
+
+def check_margin_topp(pfn, n_cases, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(n_cases):
+        V = int(rng.integers(4, 14))
+        z = rng.normal(size=V) * 1.5
+        if rng.random() < 0.3:
+            z = np.round(z)                          # ties at the cut
+        T = float(rng.choice([0.6, 1.0, 1.5]))
+        k = int(rng.choice([0, V - 2, V // 2]))
+        tp = float(rng.uniform(0.2, 0.98))
+        kept = pfn(z, T, k, tp).kept
+        same = lambda x: np.array_equal(pfn(z, T, k, x).kept, kept)
+        # The kept set grows with top_p; at top_p = 0 it is the maximum with
+        # its ties, and top_p = 1 turns the filter off.
+        lo_dist = np.inf if same(0.0) else tp - bisect_edge(same, tp, 0.0)
+        hi_dist = 1.0 - tp if same(1.0) else bisect_edge(same, tp, 1.0) - tp
+        assert abs(pfn(z, T, k, tp).topp_margin - min(lo_dist, hi_dist)) < 1e-12, (z, T, k, tp)
+
+
+def test_margin_acc_is_the_distance_to_the_acceptance_change():
+    check_margin_acc(verify_sequence, margin_cases(40, 901))
+
+
+def test_margin_cdf_is_the_distance_to_the_token_change():
+    check_margin_cdf(verify_sequence, margin_cases(40, 902))
+
+
+def test_topp_margin_is_the_distance_to_the_nucleus_change():
+    check_margin_topp(process, 60, 903)
+
+
+def _change_distance(sig, tp):
+    """Distance from tp to the nearest top_p in [0, 1] where sig(top_p)
+    changes (sig constant on an interval around tp; top_p = 1 turns the
+    filter off, so the upper side ends there)."""
+    s0 = sig(tp)
+    same = lambda x: sig(x) == s0
+    lo = np.inf if same(0.0) else tp - bisect_edge(same, tp, 0.0)
+    hi = 1.0 - tp if same(1.0) else bisect_edge(same, tp, 1.0) - tp
+    return min(lo, hi)
+
+
+def test_topp_margins_of_positions_and_decisions():
+    """topp_pos[i] is the distance of top_p to the nearest change of the
+    nucleus of position i's rows, so no change of alpha_i or
+    (p_i(x_i), q_i(x_i)) is nearer; the token margin's top-p part is the
+    same for the rows of the tests made and of the draw, so no change of n
+    or the tokens is nearer."""
+    rng = np.random.default_rng(904)
+    for _ in range(30):
+        V, G = int(rng.integers(5, 12)), int(rng.integers(1, 4))
+        zp = np.round(rng.normal(size=(G + 1, V)) * 3) / 2
+        zq = zp[:G] + np.round(rng.normal(size=(G, V)) * 2) / 2
+        draft = rng.integers(0, V, size=G).astype(np.int32)
+        u, T, tp = rng.random(G + 1), 1.0, float(rng.uniform(0.3, 0.95))
+        run = lambda x: verify_sequence(zp, zq, draft, u, T, 0, x, G)
+        kept = lambda row, x: tuple(np.nonzero(process(row, T, 0, x).kept)[0])
+        r = run(tp)
+        for i in range(G):
+            d_kept = _change_distance(lambda x: (kept(zp[i], x), kept(zq[i], x)), tp)
+            d_out = _change_distance(lambda x: (run(x).alpha[i], tuple(run(x).pq[i])), tp)
+            assert abs(r.topp_pos[i] - d_kept) < 1e-12, (i, r.topp_pos[i], d_kept)
+            assert r.topp_pos[i] <= d_out + 1e-12
+        rows = [zp[j] for j in range(r.n + 1)] + [zq[i] for i in range(min(r.n + 1, G))]
+        d_kept = _change_distance(lambda x: tuple(kept(row, x) for row in rows), tp)
+        d_out = _change_distance(lambda x: (run(x).n, tuple(run(x).tokens)), tp)
+        assert abs(r.margin_topp - d_kept) < 1e-12, (r.margin_topp, d_kept)
+        assert r.margin_topp <= d_out + 1e-12
+
+
+MARGIN_MISTAKES = {
+    "acceptance margin in unnormalised units": (
+        "acc", [("verify_sequence", "abs(ui - px / (lenience * qx))", "abs(ui * lenience * qx - px)")]),
+    "CDF margin in unnormalised units": (
+        "cdf", [("inverse_cdf", "margin = min(u - lo / Z, c[t] / Z - u)", "margin = min(u * Z - lo, c[t] - u * Z)")]),
+    "CDF margin on one side only": (
+        "cdf", [("inverse_cdf", "margin = min(u - lo / Z, c[t] / Z - u)", "margin = c[t] / Z - u")]),
+    "top-p margin without the lower side": (
+        "topp", [("process", "margin = min(margin, top_p - prob[above].sum())", "pass")]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MARGIN_MISTAKES))
+def test_margin_pins_reject_planted_mistakes(name):
+    kind, repl = MARGIN_MISTAKES[name]
+    vfn, pfn = oracle_with(repl)
+    with pytest.raises(AssertionError):
+        if kind == "acc":
+            check_margin_acc(vfn, margin_cases(40, 901))
+        elif kind == "cdf":
+            check_margin_cdf(vfn, margin_cases(40, 902))
+        else:
+            check_margin_topp(pfn, 60, 903)

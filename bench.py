@@ -79,6 +79,96 @@ def traffic_from_profile(kernel: str, workload: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    try:
+        return min(16, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return min(16, os.cpu_count() or 1)
+
+
+def oracle_reference(bt, cores: int):
+    """The oracle's outputs for every sequence of the batch, computed before
+    the GPU is touched (worker processes are forked), to check the timed
+    calls' outputs afterwards."""
+    import oracle
+    return oracle.verify_batch(bt.p_logits, bt.q_logits, bt.draft, bt.u, bt.temperature, bt.top_k, bt.top_p,
+                               bt.gamma_len, processes=cores)
+
+
+def output_check(bt, ref, tokens, n, alpha, pq, tol=1e-5):
+    """The parity rules on one call's outputs: n and the tokens identical
+    wherever the oracle's decision margin is at least tol; alpha and
+    (p(x), q(x)) within tol at every position whose rows have no nucleus
+    boundary within tol.  Returns the counts for the JSON line."""
+    near = ref.margin < tol
+    same = (n == ref.n) & (tokens == ref.tokens).all(axis=1)
+    G = bt.gamma_max
+    used = (np.arange(G)[None, :] < bt.gamma_len[:, None]) & (ref.n >= 0)[:, None]
+    cmp = used & (ref.topp_pos >= tol)
+    ea = np.abs(alpha - ref.alpha)[cmp]
+    ep = np.abs(pq - ref.pq)[cmp]
+    max_a = float(ea.max()) if ea.size else 0.0
+    max_p = float(ep.max()) if ep.size else 0.0
+    ok = bool((same | near).all() and max_a <= tol and max_p <= tol)
+    return {"sequences_checked": int(len(n)), "near": int(near.sum()), "near_differ": int((near & ~same).sum()),
+            "differ_outside_margin": int((~same & ~near).sum()), "positions": int(used.sum()),
+            "positions_compared": int(cmp.sum()), "max_alpha_err": max_a, "max_pq_err": max_p, "ok": ok}
+
+
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "libsvprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing; build it with __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    vp, sz, i, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32
+    L.sv_read_probe.argtypes = [vp, sz, vp, sz, vp, i, i, u32, vp]
+    L.sv_read_probe.restype = i
+    return L
+
+
+def read_ceiling(A, B, launches: int = 10):
+    """Streaming-read ceiling on the call's own logit buffers: a plain
+    read of A and B (each once per launch) in a few launch shapes, timed with
+    events on the current stream; the best shape's GB/s."""
+    import torch
+    L = _probe_lib()
+    nbytes = A.numel() * A.element_size() + B.numel() * B.element_size()
+    out = torch.zeros(16384, dtype=torch.int32, device=A.device)
+    stream = torch.cuda.current_stream().cuda_stream or None
+    best = None
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        for unroll in (8, 16):
+            def launch():
+                rc = L.sv_read_probe(A.data_ptr(), A.numel() * A.element_size(), B.data_ptr(),
+                                     B.numel() * B.element_size(), out.data_ptr(), grid, unroll, 0x9E3779B9, stream)
+                if rc != 0:
+                    raise RuntimeError(f"sv_read_probe failed with {rc}")
+            launch()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+            for a, b in evs:
+                a.record()
+                launch()
+                b.record()
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+            gbs = nbytes / (us * 1e-6) / 1e9
+            if best is None or gbs > best["achieved"]:
+                best = {"achieved": gbs, "unit": "GB/s", "frac_of_peak": gbs / HBM_PEAK_GBS, "bytes": nbytes,
+                        "avg_us": us, "grid": grid, "unroll": unroll}
+    return best
+
+
 def kernel_bytes(bt):
     """Logit bytes read by the streaming select (argmax and top-k <= 512
     sequences) and by the pair kernel (every other sequence with T > 0)."""
@@ -107,7 +197,7 @@ def cpu_baseline(bt, seconds_target: float, cores: int):
     oracle.verify_batch(bt.p_logits, bt.q_logits, bt.draft, bt.u, bt.temperature, bt.top_k, bt.top_p,
                         bt.gamma_len, rows=rows, processes=cores)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+    return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n} sequences cycling through the workload's {bt.B} (float64 numpy oracle, {cores} worker processes, "
                       f"{dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
 
@@ -134,7 +224,7 @@ def cpu_baseline_gumbel(gb, seconds_target: float, cores: int):
     with mp.get_context("fork").Pool(len(chunks)) as pool:
         pool.map(_gumbel_rows, [(data, c) for c in chunks])
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
+    return {"value": n / dt, "unit": "rows/s", "cores": len(chunks), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n} sequences cycling through the workload's {gb.B} (shared-noise oracle, {len(chunks)} worker processes, "
                       f"{dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
 
@@ -276,7 +366,7 @@ def main_spectr(args):
         with mp.get_context("fork").Pool(len(chunks)) as pool:
             pool.map(_spectr_rows, [(data, c) for c in chunks])
         dt = time.perf_counter() - t0
-        cpu = {"value": n / dt, "unit": "rows/s", "cores": len(chunks), "kind": "oracle",
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": len(chunks), "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{n} sequences cycling through the workload's {sb.B} (K-SEQ / SpecTr oracle, {len(chunks)} worker "
                          f"processes, {dt:.2f} s wall, about {per_seq * n:.1f} s of CPU work)"}
     import torch
@@ -358,6 +448,10 @@ def main():
                     help="the multi-candidate (K-SEQ / SpecTr) verify at K = 8, L = 8 instead")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle check of the last timed call's outputs")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling on the call's logit buffers")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the verify step on one GPU; runs on more than one GPU are not supported "
@@ -389,13 +483,14 @@ def main():
     alg_bytes = synth.algorithmic_bytes(bt)
     logit_bytes = int((2 * bt.gamma_len.astype(np.int64) + 1).sum()) * bt.V * bt.p_logits.itemsize
 
-    # CPU baseline first: worker processes are forked before the GPU is touched.
+    # CPU work first: worker processes are forked before the GPU is touched.
+    # The oracle's outputs for every sequence, to check the timed calls' outputs.
+    cores = host_cores()
+    t_ref = time.perf_counter()
+    ref = None if args.no_check else oracle_reference(bt, cores)
+    t_ref = time.perf_counter() - t_ref
     cpu = None
     if not args.no_cpu:
-        try:
-            cores = min(16, len(os.sched_getaffinity(0)))
-        except AttributeError:
-            cores = min(16, os.cpu_count() or 1)
         cpu = cpu_baseline(bt, args.cpu_seconds, cores)
 
     import torch
@@ -462,6 +557,10 @@ def main():
     ms_per_step = wall * 1e3 / K
     n_acc = ver.n_accepted.cpu().numpy()
     alpha = ver.alpha.cpu().numpy()
+    # Outside the timed region: the last timed call's outputs against the oracle.
+    check = None
+    if ref is not None:
+        check = output_check(bt, ref, ver.tokens.cpu().numpy(), n_acc, alpha, ver.pq.cpu().numpy())
     # Outside the timed region: the other kernels' durations, for the record.
     other_us = {}
     for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, "pair_kernel"),
@@ -476,6 +575,9 @@ def main():
     achieved = kbytes / (k_avg * 1e-3) / 1e9
     traffic = traffic_from_profile(kname, bt.workload.name)
     w = bt.workload
+    ceiling = None if args.no_ceiling else read_ceiling(P, Q)
+    single = single_round_latency(bt, P, Q, draft, u, temp, topk, topp, gl, dt_code, hints, ver) \
+        if args.workload == 0 else None
     out = {
         "metric": METRIC,
         "value": bt.B / (ms_per_step * 1e-3),
@@ -499,7 +601,13 @@ def main():
                      "kernel_p10_us": float(np.percentile(k_ms, 10) * 1e3),
                      "kernel_p90_us": float(np.percentile(k_ms, 90) * 1e3)},
         "cpu_baseline": cpu,
+        "cpu_model": cpu_model(),
+        "near_margin": check,
+        "read_ceiling": ceiling,
         "extra": {"call_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+                  "kernel_frac_of_read_ceiling": achieved / ceiling["achieved"] if ceiling else None,
+                  "single_round_B1": single,
+                  "oracle_reference_s": t_ref,
                   "logit_rows_per_s": int((2 * bt.gamma_len.astype(np.int64) + 1).sum()) / (ms_per_step * 1e-3),
                   "mean_alpha": float(alpha[alpha > 0].mean()) if (alpha > 0).any() else None,
                   "mean_tokens_per_round": float((n_acc[n_acc >= 0] + 1).mean()),
@@ -508,6 +616,49 @@ def main():
                   "input_generation_s": t_gen},
     }
     print(json.dumps(out))
+    if check is not None and not check["ok"]:
+        print("bench.py: the timed call's outputs break the parity rules against the oracle", file=sys.stderr)
+        sys.exit(3)
+
+
+def single_round_latency(bt, P, Q, draft, u, temp, topk, topp, gl, dt_code, hints, batched, rounds=1000):
+    """The tiny workload as it is stated: one sequence per call, `rounds`
+    calls in a row (round r takes sequence r of the batch), each call timed
+    with events on the stream; the outputs must equal the batched call's."""
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+    rounds = min(rounds, bt.B)
+    one = binding.Verifier(1, bt.gamma_max, bt.V, dt_code, device=P.device, hints=hints)
+    toks = torch.empty((rounds, bt.gamma_max + 1), dtype=torch.int32, device=P.device)
+    ns = torch.empty((rounds,), dtype=torch.int32, device=P.device)
+    sl = lambda t, r: t[r:r + 1]
+
+    def call(r):
+        return one(sl(P, r), sl(Q, r), sl(draft, r), sl(u, r), sl(temp, r), sl(topk, r), sl(topp, r), sl(gl, r))
+
+    # An untimed pass keeps every round's outputs for the comparison.
+    for r in range(rounds):
+        tok, n, _, _ = call(r)
+        toks[r:r + 1].copy_(tok)
+        ns[r:r + 1].copy_(n)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r, (a, b) in enumerate(evs):
+        a.record()
+        call(r)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    same = bool(torch.equal(toks, batched.tokens[:rounds]) and torch.equal(ns, batched.n_accepted[:rounds]))
+    return {"calls": rounds, "B": 1, "us_per_call_events_mean": float(us.mean()),
+            "us_per_call_events_p50": float(np.median(us)), "us_per_call_events_p90": float(np.percentile(us, 90)),
+            "us_per_call_wall": wall * 1e6 / rounds, "outputs_equal_batched_call": same}
 
 
 if __name__ == "__main__":

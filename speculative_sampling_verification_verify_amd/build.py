@@ -1,4 +1,6 @@
-"""Build libspecverify.so for gfx950 with hipcc (in-tree, next to this file)."""
+"""Build libspecverify.so (the verify library) and libsvprobe.so (the
+streaming-read ceiling probe that bench.py times beside it) for gfx950 with
+hipcc, in-tree, next to this file."""
 from __future__ import annotations
 
 import os
@@ -9,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "spec_verify.hip")
 OUT = os.path.join(HERE, "libspecverify.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "read_probe.hip")
+PROBE_OUT = os.path.join(HERE, "libsvprobe.so")
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
@@ -18,18 +22,24 @@ HIPCC_FLAGS = [
 ]
 
 
-def build_library(verbose: bool = False) -> str:
+def _hipcc(src: str, out: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, SRC]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, src]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}) on {os.path.basename(src)}:\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile both libraries (always); returns the verify library's path."""
+    _hipcc(PROBE_SRC, PROBE_OUT, verbose)
+    return _hipcc(SRC, OUT, verbose)
 
 
 if __name__ == "__main__":

@@ -33,6 +33,7 @@
 
 #include "sv_wave.h"
 #include "sv_pair.h"
+#include "sv_phist.h"
 #include "sv_finish.h"
 #include "sv_gumbel.h"
 #include "sv_kseq.h"
@@ -215,6 +216,9 @@ static hipError_t device_setup() {
   if ((e = set_lds_limits<uint16_t, false>()) != hipSuccess) return e;
   if ((e = set_lds_limits<float, true>()) != hipSuccess) return e;
   if ((e = set_lds_limits<float, false>()) != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pair_hist_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)sizeof(PhSmem));
+  if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
   if (e != hipSuccess) return e;
@@ -238,12 +242,18 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
   if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   if (a.pair) {
     size_t plds = 0;
-    const int pv = pair_variant(a.V, sizeof(ET) == 2 ? SV_BF16 : SV_FP32, VECTOR, &plds);
+    int pv = pair_variant(a.V, sizeof(ET) == 2 ? SV_BF16 : SV_FP32, VECTOR, &plds);
     if (pv != 64 && pv != 256 && pv != 1024 && pv != -1024) return hipErrorInvalidValue;
     const long long npairs = (long long)a.B * (a.G + 1);
-    const dim3 grid((unsigned)(npairs < pair_grid_cap(pv) ? npairs : pair_grid_cap(pv)));
+    // bf16 rows streamed from memory, up to PH_MAX_UNITS 16-byte units: the
+    // histogram variant, one workgroup per CU.
+    const bool hist = pv == -1024 && sizeof(ET) == 2 && VECTOR && (long long)a.V / 8 <= PH_MAX_UNITS;
+    const long long cap = hist ? 256 : pair_grid_cap(pv);
+    const dim3 grid((unsigned)(npairs < cap ? npairs : cap));
     if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
+    if (hist) pv = 0;
     switch (pv) {
+      case 0: hipLaunchKernelGGL(pair_hist_kernel, grid, dim3(PH_NT), sizeof(PhSmem), st, a); break;
       case 64: hipLaunchKernelGGL((pair_kernel<ET, 64, VECTOR, true>), grid, dim3(64), plds, st, a); break;
       case 256: hipLaunchKernelGGL((pair_kernel<ET, 256, VECTOR, true>), grid, dim3(256), plds, st, a); break;
       case 1024: hipLaunchKernelGGL((pair_kernel<ET, 1024, VECTOR, true>), grid, dim3(1024), plds, st, a); break;

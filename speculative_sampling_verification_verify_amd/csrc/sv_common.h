@@ -21,8 +21,10 @@ constexpr uint32_t F_DEMOTE = 2u;  // survivor lists unusable: recompute from th
 struct PosRec {
   double px, qx, alpha;   // p_i(x_i), q_i(x_i), overlap (position < gamma_b)
   int32_t tok;            // draw if the first rejection is here (bonus draw at gamma_b)
-  uint32_t bad;           // a row of the pair has NaN / +inf or no finite logit
+  uint32_t bad;           // 1: a row of the pair has NaN / +inf or no finite logit; REC_REDO: not
+                          // computed, the finisher computes the sequence from the logits
 };
+constexpr uint32_t REC_REDO = 2u;
 
 struct Args {
   const void* p;

@@ -736,13 +736,29 @@ __device__ __forceinline__ void finish_from_pairs_wave(const Args& a, int b, con
   }
 }
 
+// Whether the pair kernel left a position of sequence b uncomputed (a row
+// it could not take): then the whole sequence is computed from the logits.
+// Every wavefront reads the records itself, so the answer is uniform without
+// a block barrier.
+__device__ __forceinline__ bool pair_redo(const Args& a, int b, int g) {
+  const int lane = threadIdx.x & 63;
+  const PosRec* rec = a.pos + (size_t)b * (a.G + 1);
+  bool r = false;
+  for (int i = lane; i <= g; i += 64) r = r || rec[i].bad == REC_REDO;
+  return __ballot(r) != 0ull;
+}
+
 template <typename ET, bool VECTOR>
 __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
+  bool redo = false;
   {
     const Mode m = seq_mode(a, b);
     if (a.pair && m.mode == MODE_DENSE) {   // block-uniform; no block barrier follows
-      if (threadIdx.x < 64) finish_from_pairs_wave(a, b, m);
-      return;
+      redo = pair_redo(a, b, m.g);
+      if (!redo) {
+        if (threadIdx.x < 64) finish_from_pairs_wave(a, b, m);
+        return;
+      }
     }
   }
   const int RS = a.RS;
@@ -776,7 +792,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   // survivor lists: a sequence that is not dense after all takes the
   // multi-pass path.
   bool dense = m.mode == MODE_DENSE || (fl & F_DEMOTE) || NS > MAXSEG || a.all_dense;
-  const bool from_pairs = a.pair && m.mode == MODE_DENSE;
+  const bool from_pairs = a.pair && m.mode == MODE_DENSE && !redo;
   uint32_t badin = 0;
   if ((int)threadIdx.x < m.g)
     badin |= (xraw < 0 || xraw >= a.V || !(uraw >= 0.0f && uraw < 1.0f)) ? 1u : 0u;
@@ -949,7 +965,7 @@ __global__ __launch_bounds__(NT) void finish_dense_kernel(Args a) {
   uint32_t other = 0;
   if (b0 + wave < a.B) {
     const Mode m = seq_mode(a, b0 + wave);
-    if (m.mode == MODE_DENSE) finish_from_pairs_wave(a, b0 + wave, m);
+    if (m.mode == MODE_DENSE && !pair_redo(a, b0 + wave, m.g)) finish_from_pairs_wave(a, b0 + wave, m);
     else other = 1;
   }
   if ((threadIdx.x & 63) == 0) s.red_u[wave] = other;

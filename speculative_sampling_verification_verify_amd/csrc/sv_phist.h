@@ -1,0 +1,587 @@
+// Dense (sequence, position) pairs with bf16 rows too long to hold in LDS:
+// statistics from an exact count histogram of the row's bf16 values.
+//
+// A bf16 logit takes one of 65536 bit patterns, so a row's exact count per
+// value (16-bit counts, two per 32-bit LDS word: 128 KB) fits in one CU's
+// LDS.  One streaming pass over a row fills it; a scan of the histogram in
+// descending value order then gives, with no further pass over the row:
+//   * validity (no NaN or +inf) and the maximum logit,
+//   * the top-k threshold (the k-th largest value, ties kept) for large k,
+//   * the normaliser S = sum of the weights e(z) = 2^((z - zmax) log2(e) / T),
+//     and for top-p the nucleus cut t*: the largest value whose mass at or
+//     above reaches top_p * S (ties kept).
+// Masses are count(value) * e(value), summed in double in a fixed order.  The processed distribution is
+// that of "Fast Inference from Transformers via Speculative Decoding"
+// (mtandhj.com summary), "Speculative Sampling: theoretical basis" (the
+// sampling adjustments applied to both models).
+//
+// Per pair: each row is read once for its histogram (rows of up to 131072
+// values: 16 16-byte units per thread); then both rows are read again, but
+// only in the units whose largest target value can reach the target's
+// nucleus, for the overlap
+// alpha = sum min(p, q) ("How to choose gamma" on the same summary) and the
+// per-(tile, wavefront) sums of the draw weights, the residual max(0, p - q)
+// or, at the bonus position, p ("Speculative Decoding: the art of guessing
+// well", "Speculative sampling"): elsewhere p = 0, so neither has a term.
+// The tile holding the inverse-CDF crossing at u * Z ("Sampling with shared
+// noise" on the same page, ascending vocabulary id) is then examined again.
+// Row bytes read per pair: 2x the algorithmic bytes for unfiltered rows,
+// less the smaller the nucleus (about 1x when it holds a few values).
+//
+// A row in which more than 65535 elements share one value would overflow its
+// 16-bit count; the decoded counts then no longer add up to V.  The pair's
+// record then asks the finisher to compute the whole sequence by its
+// multi-pass procedure over the logits.
+#pragma once
+
+#include "sv_pair.h"
+
+namespace sv {
+
+constexpr int PH_NT = 1024;                 // threads per workgroup (one workgroup per CU)
+constexpr int PH_NW = PH_NT / 64;
+constexpr int PH_UPT = 16;                  // 16-byte units of a row per thread
+constexpr int PH_WORDS = 32768;             // histogram words: bf16 key 2j in the low half of word j, 2j+1 high
+constexpr int PH_INFLIGHT = 8;              // units of a row in flight per thread while it streams
+constexpr int PH_MAX_UNITS = PH_NT * PH_UPT;
+constexpr int PH_SEGW = 64;                 // histogram words per segment (one per lane)
+constexpr int PH_NSEG = PH_WORDS / PH_SEGW; // 512 segments
+
+struct PhSmem {
+  uint32_t hist[PH_WORDS];
+  uint8_t umax[PH_MAX_UNITS];               // top byte of each target unit's largest key
+  double seg[PH_NSEG];                      // per-segment sums of a histogram scan
+  double part[PH_UPT][PH_NW];               // draw-weight sum per (tile, wavefront)
+  uint32_t red[5 * PH_NW];
+  uint32_t bc[8];
+  double bd[2];
+  uint32_t next_pair;
+};
+
+// Order-preserving 16-bit keys of two bf16 patterns at once (+0 and -0 share
+// a key; -inf is 0x0080; NaN and +inf fall outside [0x0080, 0xFF7F]).
+typedef unsigned short ph_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t ph_keys2(uint32_t w) {
+  const ph_u16x2 h = __builtin_bit_cast(ph_u16x2, w);
+  const ph_u16x2 sgn = h >> (unsigned short)15;
+  const ph_u16x2 key = (h ^ (ph_u16x2)(sgn * (unsigned short)0x7FFF + (unsigned short)0x8000)) + sgn;
+  return __builtin_bit_cast(uint32_t, key);
+}
+__device__ __forceinline__ void ph_count(uint32_t* hist, uint32_t key) {
+  atomicAdd(&hist[key >> 1], 1u << ((key & 1u) << 4));
+}
+
+// Adds one 16-byte unit (8 bf16) to the histogram and to the running key
+// extremes (packed: both halves at once).
+// The packed key extremes of one 16-byte unit (8 bf16), folded into kmax2 /
+// kmin2 (both halves at once).
+__device__ __forceinline__ void ph_extremes_unit(const uint4& u, uint32_t& kmax2, uint32_t& kmin2) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t k2 = ph_keys2(w[j]);
+    kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
+                                                                   __builtin_bit_cast(ph_u16x2, k2)));
+    kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
+                                                                   __builtin_bit_cast(ph_u16x2, k2)));
+  }
+}
+// Counts the unit's elements whose key is at least kfloor; the others are
+// added to `skipped`.
+__device__ __forceinline__ void ph_add_unit(uint32_t* hist, const uint4& u, uint32_t kfloor, uint32_t& skipped) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t k2 = ph_keys2(w[j]);
+    const uint32_t klo = k2 & 0xFFFFu, khi = k2 >> 16;
+    if (klo >= kfloor) ph_count(hist, klo);
+    else ++skipped;
+    if (khi >= kfloor) ph_count(hist, khi);
+    else ++skipped;
+  }
+}
+// The largest key of a unit (its max over the 8 elements).
+__device__ __forceinline__ uint32_t ph_unit_max(const uint4& u) {
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+  ph_extremes_unit(u, mx, mn);
+  return max(mx & 0xFFFFu, mx >> 16);
+}
+
+struct PhFind {
+  uint32_t key;    // the key where the running sum first reaches tau (NONE: never)
+  double above;    // sum over larger keys
+  double at;       // above + the key's own contribution
+  double total;    // sum over every key
+  uint32_t count;  // decoded counts over every key
+};
+
+// A scan of the histogram with per-key contributions f(key, count) (double):
+// the total, the decoded counts, and (tau > 0) the largest key at which the
+// running sum over descending keys reaches tau.  Segments of 64 words are
+// summed by whole wavefronts, one word per lane (empty segments skipped by a
+// ballot), so the keys that hold elements, however few and however close,
+// are spread over all the lanes; the sums use DPP lane moves only.
+// Wavefront 0 then scans the 512 segment sums in descending order and, within
+// the crossing segment, its 64 words.
+template <class F>
+__device__ __forceinline__ PhFind ph_scan(PhSmem& s, F f, double tau, int sg_lo, int sg_hi) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  uint32_t cnt = 0;
+  // Segments outside [sg_lo, sg_hi] hold no counted key: they are zero.
+  for (int sg = w; sg < PH_NSEG; sg += PH_NW)
+    if ((sg < sg_lo || sg > sg_hi) && l == 0) s.seg[sg] = 0.0;
+  // Eight segments' words are read before any is examined.
+  constexpr int B = 8;
+  for (int sg0 = sg_lo + w; sg0 <= sg_hi; sg0 += B * PH_NW) {
+    uint32_t word[B];
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+      const int sg = sg0 + r * PH_NW;
+      word[r] = sg <= sg_hi ? s.hist[sg * PH_SEGW + l] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+      const int sg = sg0 + r * PH_NW;
+      if (sg > sg_hi) break;
+      const int wd = sg * PH_SEGW + l;
+      double v = 0.0;
+      if (__ballot(word[r] != 0u)) {
+        const uint32_t chi = word[r] >> 16, clo = word[r] & 0xFFFFu;
+        cnt += chi + clo;
+        if (chi) v += f(2u * (uint32_t)wd + 1u, chi);
+        if (clo) v += f(2u * (uint32_t)wd, clo);
+        v = wave_sum_dpp(v);
+      }
+      if (l == 0) s.seg[sg] = v;
+    }
+  }
+  cnt = wave_reduce_dpp_u32(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+  if (l == 0) s.red[3 * PH_NW + w] = cnt;
+  __syncthreads();
+  PhFind r;
+  r.count = 0;
+  for (int x = 0; x < PH_NW; ++x) r.count += s.red[3 * PH_NW + x];
+  if (w == 0) {
+    // Lane l: segments 511 - 8 l .. 504 - 8 l (descending keys).
+    double sv[8], ls = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sv[i] = s.seg[PH_NSEG - 1 - 8 * l - i];
+      ls += sv[i];
+    }
+    const double inc = wave_incl_scan_f64(ls);
+    const double tot = readlane_f64(inc, 63);
+    uint32_t key = NONE;
+    double above = 0.0, at = 0.0;
+    if (tau > 0.0 && tot >= tau) {
+      const unsigned long long hit = __ballot(inc >= tau);
+      const int cl = __ffsll((long long)hit) - 1;
+      // The crossing segment within lane cl's eight.
+      double run = readlane_f64(inc - ls, cl);
+      int csg = PH_NSEG - 1 - 8 * cl;
+      for (int i = 0; i < 8; ++i) {
+        const double svi = readlane_f64(sv[i], cl);
+        csg = PH_NSEG - 1 - 8 * cl - i;
+        if (run + svi >= tau) break;
+        run += svi;
+      }
+      // Its words, lane l taking word 63 - l (descending keys).
+      const int wd = csg * PH_SEGW + (PH_SEGW - 1 - l);
+      const uint32_t word = s.hist[wd];
+      const uint32_t chi = word >> 16, clo = word & 0xFFFFu;
+      const double fh = chi ? f(2u * (uint32_t)wd + 1u, chi) : 0.0;
+      const double fl = clo ? f(2u * (uint32_t)wd, clo) : 0.0;
+      const double winc = wave_incl_scan_f64(fh + fl);
+      const unsigned long long whit = __ballot(run + winc >= tau);
+      const int wl = whit ? __ffsll((long long)whit) - 1 : 63;
+      const double b0 = run + readlane_f64(winc - fh - fl, wl);
+      const double fhw = readlane_f64(fh, wl), flw = readlane_f64(fl, wl);
+      const int wdw = __builtin_amdgcn_readlane(wd, wl);
+      const bool high = fhw > 0.0 && b0 + fhw >= tau;
+      key = high ? 2u * (uint32_t)wdw + 1u : 2u * (uint32_t)wdw;
+      above = high ? b0 : b0 + fhw;
+      at = high ? b0 + fhw : b0 + fhw + flw;
+    }
+    if (l == 0) {
+      s.bc[0] = key;
+      s.bd[0] = above;
+      s.bd[1] = at;
+      s.seg[0] = tot;
+    }
+  }
+  __syncthreads();
+  r.key = s.bc[0];
+  r.above = s.bd[0];
+  r.at = s.bd[1];
+  r.total = s.seg[0];
+  __syncthreads();   // seg / bc / bd / red are reused by the next scan
+  return r;
+}
+
+enum { PH_OK = 0, PH_BAD = 1, PH_OVERFLOW = 2 };
+
+// The row statistics from its histogram.  kmax / kmin: the row's largest and
+// smallest keys, kcount_min: the lowest floor any wavefront counted from,
+// skipped: elements left out of the histogram (block-uniform).
+// Returns PH_BAD for NaN / +inf or a row of only -inf, PH_OVERFLOW when some
+// count overflowed.
+__device__ __forceinline__ int ph_stats(PhSmem& s, uint32_t kmax, uint32_t kmin, uint32_t kcount_min,
+                                        uint32_t skipped, int V, const Mode& m, int k, RowStat& st) {
+  using K = Key<uint16_t>;
+  if (kmax >= K::POS_INF || kmin < K::NEG_INF || kmax <= K::NEG_INF) return PH_BAD;
+  // Counted keys lie in [max(kmin, kcount_min), kmax]: only their segments are scanned.
+  const int sg_lo = (int)(max(kmin, kcount_min) >> 1) / PH_SEGW, sg_hi = (int)(kmax >> 1) / PH_SEGW;
+  st.zmax = K::value(kmax);
+  st.c = LOG2E_F / m.T;
+  st.zthr = -INFINITY;
+  const float zmax = st.zmax, c = st.c;
+  uint32_t kthr = K::NEG_INF + 1u;   // smallest key that can carry mass
+  bool counted = false;
+  if (k > 0 && k < V) {
+    // Top-k: the k-th largest key (ties kept) from the counts.
+    const PhFind f = ph_scan(s, [](uint32_t, uint32_t cn) { return (double)cn; }, (double)k, sg_lo, sg_hi);
+    if (f.count + skipped != (uint32_t)V) return PH_OVERFLOW;
+    counted = true;
+    if (f.key != NONE && f.key > kthr) kthr = f.key;
+  }
+  // A key's mass: its count times its weight e = 2^((z - zmax) c).
+  auto mass = [&](uint32_t key, uint32_t cn) -> double {
+    if (key < kthr) return 0.0;
+    return (double)cn * (double)ew(K::value(key), zmax, c);
+  };
+  if (kthr > K::NEG_INF + 1u) st.zthr = K::value(kthr);
+  const PhFind t = ph_scan(s, mass, -1.0, sg_lo, sg_hi);
+  if (!counted && t.count + skipped != (uint32_t)V) return PH_OVERFLOW;
+  double S = t.total;
+  if (m.tp < 1.0f) {
+    if (m.tp <= 0.0f) {
+      // Only the largest value (with its ties) survives.
+      st.zthr = zmax;
+      const uint32_t word = s.hist[kmax >> 1];
+      S = (double)((kmax & 1u) ? word >> 16 : word & 0xFFFFu);
+    } else {
+      // The nucleus: the largest value whose mass at or above reaches top_p S.
+      const PhFind f = ph_scan(s, mass, (double)m.tp * S, sg_lo, sg_hi);
+      if (f.key != NONE && f.at > 0.0) {
+        st.zthr = fmaxf(st.zthr, K::value(f.key));
+        S = f.at;
+      }
+    }
+  }
+  st.sp = (float)(1.0 / S);
+  return PH_OK;
+}
+
+// Unit j of the calling thread (16-byte unit threadIdx.x + j * PH_NT of the
+// row) through the row's buffer descriptor: one 32-bit offset per thread,
+// the unit's position in the scalar offset, units past the row read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ph_rsrc(const uint4* row, int NU) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(row), (short)0, NU * 16, BUF_WORD3);
+}
+template <int AUX>
+__device__ __forceinline__ uint4 ph_load(__amdgpu_buffer_rsrc_t r, int j) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)threadIdx.x * 16, j * PH_NT * 16, AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void ph_clear(PhSmem& s) {
+  uint4* h = reinterpret_cast<uint4*>(&s.hist[0]);
+  for (int i = threadIdx.x; i < PH_WORDS / 4; i += PH_NT) h[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Block max / min of the packed key extremes (both halves), in one round trip.
+__device__ __forceinline__ void ph_extremes(PhSmem& s, uint32_t kmax2, uint32_t kmin2, uint32_t& kmax, uint32_t& kmin) {
+  uint32_t mx = max(kmax2 & 0xFFFFu, kmax2 >> 16), mn = min(kmin2 & 0xFFFFu, kmin2 >> 16);
+  mx = wave_max_dpp(mx);
+  mn = wave_min_dpp(mn);
+  if ((threadIdx.x & 63) == 0) {
+    s.red[threadIdx.x >> 6] = mx;
+    s.red[PH_NW + (threadIdx.x >> 6)] = mn;
+  }
+  __syncthreads();
+  kmax = 0;
+  kmin = 0xFFFFu;
+  for (int x = 0; x < PH_NW; ++x) {
+    kmax = max(kmax, s.red[x]);
+    kmin = min(kmin, s.red[PH_NW + x]);
+  }
+  __syncthreads();
+}
+
+// One (sequence b, position i) pair by the whole workgroup.  Thread t's
+// units of a row are t + j * PH_NT, j < PH_UPT (tile j).
+__device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSmem& s) {
+  using T = PT<uint16_t, true>;
+  const int G1 = a.G + 1;
+  const Mode m = seq_mode(a, b);
+  if (m.mode != MODE_DENSE || i > m.g) return;
+  const bool resid = i < m.g;
+  const int V = a.V;
+  const int NU = V / 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = a.topk ? a.topk[b] : 0;
+  const uint4* gp = reinterpret_cast<const uint4*>(row_ptr<uint16_t>(a, b, true, i));
+  const uint4* gq = resid ? reinterpret_cast<const uint4*>(row_ptr<uint16_t>(a, b, false, i)) : gp;
+  const __amdgpu_buffer_rsrc_t rp = ph_rsrc(gp, NU), rq = ph_rsrc(gq, NU);
+  PosRec* rec = a.pos + (size_t)b * G1 + i;
+  const int fb = a.fixbits;
+  const float cT = LOG2E_F / m.T;
+  const bool filter_k = k > 0 && k < V;
+  int bad = 0;
+
+  // Row 0, the draft row, then row 1, the target row: one streaming pass
+  // each, counting the elements at or above a floor into the histogram.
+  // The floor: elements whose weight is below 2^-(fb+2) of the maximum's
+  // (fb = 62 - bits(V + 1), at least 44 for the rows taken here) together hold
+  // less than V 2^-46 <= 2^-29 of the mass, so they are left out of S and can
+  // never be in a nucleus (a float top_p below 1 is at most 1 - 2^-24).  Top-k
+  // rows count every element: the k-th may lie anywhere.  Each wavefront takes
+  // its floor from its own running maximum, never above the row's.  The target
+  // pass also notes the top byte of each unit's largest key.
+  RowStat sq{INFINITY, 0.0f, 0.0f, 0.0f}, sp{};
+  for (int row = resid ? 0 : 1; row < 2; ++row) {
+    const __amdgpu_buffer_rsrc_t rr = row == 0 ? rq : rp;
+    ph_clear(s);
+    __syncthreads();
+    uint32_t kmax2 = 0u, kmin2 = 0xFFFFFFFFu, skipped = 0, kf_first = 0xFFFFFFFFu;
+    for (int j0 = 0; j0 < PH_UPT; j0 += PH_INFLIGHT) {
+      uint4 u[PH_INFLIGHT];
+#pragma unroll
+      for (int r = 0; r < PH_INFLIGHT; ++r) u[r] = ph_load<0>(rr, j0 + r);
+#pragma unroll
+      for (int r = 0; r < PH_INFLIGHT; ++r) {
+        const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
+        if (ui < NU) {
+          uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+          ph_extremes_unit(u[r], mx, mn);
+          kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
+                                                                         __builtin_bit_cast(ph_u16x2, mx)));
+          kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
+                                                                         __builtin_bit_cast(ph_u16x2, mn)));
+          if (row == 1) s.umax[ui] = (uint8_t)(max(mx & 0xFFFFu, mx >> 16) >> 8);
+        }
+      }
+      uint32_t kfloor = 0u;
+      if (!filter_k) {
+        const uint32_t wmax = wave_max_dpp(max(kmax2 & 0xFFFFu, kmax2 >> 16));
+        if (wmax > Key<uint16_t>::NEG_INF && wmax < Key<uint16_t>::POS_INF) {
+          // Smallest bf16 key whose value is at least wmax's - (fb + 2) / c.
+          const float zf = Key<uint16_t>::value(wmax) - (float)(fb + 2) / cT;
+          const uint32_t bits = __float_as_uint(zf);
+          const uint32_t b16 = zf >= 0.0f ? (bits + 0xFFFFu) >> 16 : bits >> 16;
+          kfloor = zf > -INFINITY ? Key<uint16_t>::of_bits(b16) : 0u;
+        }
+      }
+      kf_first = min(kf_first, kfloor);
+#pragma unroll
+      for (int r = 0; r < PH_INFLIGHT; ++r)
+        if ((j0 + r) * PH_NT + (int)threadIdx.x < NU) ph_add_unit(s.hist, u[r], kfloor, skipped);
+    }
+    skipped = wave_reduce_dpp_u32(skipped, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+    if (lane == 0) {
+      s.red[2 * PH_NW + wave] = skipped;
+      s.red[4 * PH_NW + wave] = kf_first;
+    }
+    uint32_t kmax, kmin;
+    ph_extremes(s, kmax2, kmin2, kmax, kmin);   // its barriers also close the counting
+    skipped = 0;
+    uint32_t kcount_min = 0xFFFFFFFFu;
+    for (int x = 0; x < PH_NW; ++x) {
+      skipped += s.red[2 * PH_NW + x];
+      kcount_min = min(kcount_min, s.red[4 * PH_NW + x]);
+    }
+    RowStat st{};
+    bad |= ph_stats(s, kmax, kmin, kcount_min, skipped, V, m, k, st);
+    if (row == 0) sq = st;
+    else sp = st;
+    __syncthreads();   // the statistics' last histogram reads before the next row clears it
+    if (bad) break;
+  }
+  if (bad) {
+    // Invalid data, or a count that overflowed: the finisher then takes the
+    // sequence through its multi-pass procedure (REC_REDO) or reports it
+    // invalid.
+    if (threadIdx.x == 0) {
+      rec->bad = (bad & PH_BAD) ? 1u : REC_REDO;
+      rec->tok = -1;
+    }
+    return;
+  }
+
+  // Overlap and per-(tile, wavefront) draw-weight sums: the residual
+  // max(0, p - q), or p at the bonus position and when the residual is zero
+  // (there the draft's threshold is +inf, so q = 0 everywhere and the same
+  // code sums p).  Only units whose largest target key can reach the target's
+  // nucleus threshold are read again (p = 0 elsewhere: neither sum has a term).
+  const int ntile = (NU + PH_NT - 1) / PH_NT;
+  double al = 0.0;
+  RowStat sqw = sq;   // the draft's statistics as the draw uses them (q = 0 once the residual is empty)
+  const uint32_t kpthr8 = (sp.zthr > -INFINITY ? key_of_value<uint16_t>(sp.zthr) : 0u) >> 8;
+  auto weights_pass = [&](bool use_q) {
+    for (int j0 = 0; j0 < ntile; j0 += PH_INFLIGHT) {
+      uint4 up[PH_INFLIGHT], uq[PH_INFLIGHT];
+      bool nd[PH_INFLIGHT];
+#pragma unroll
+      for (int r = 0; r < PH_INFLIGHT; ++r) {
+        const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
+        nd[r] = ui < NU && (uint32_t)s.umax[ui] >= kpthr8;
+        up[r] = make_uint4(0u, 0u, 0u, 0u);
+        uq[r] = up[r];
+        if (nd[r]) {
+          up[r] = ph_load<BUF_NT>(rp, j0 + r);
+          if (use_q) uq[r] = ph_load<BUF_NT>(rq, j0 + r);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < PH_INFLIGHT; ++r) {
+        if (j0 + r >= ntile) break;
+        float rs = 0.0f, av = 0.0f;
+        if (nd[r]) {
+          const uint32_t pw[4] = {up[r].x, up[r].y, up[r].z, up[r].w}, qw[4] = {uq[r].x, uq[r].y, uq[r].z, uq[r].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t pr = e & 1 ? pw[e >> 1] >> 16 : pw[e >> 1] & 0xFFFFu;
+            const uint32_t qr = e & 1 ? qw[e >> 1] >> 16 : qw[e >> 1] & 0xFFFFu;
+            const float pv = pprob(sp, T::val(pr)), qv = pprob(sqw, T::val(qr));
+            av += fminf(pv, qv);
+            rs += fmaxf(pv - qv, 0.0f);
+          }
+        }
+        al += (double)av;
+        const double wsum = wave_sum_dpp((double)rs);
+        if (lane == 0) s.part[j0 + r][wave] = wsum;
+      }
+    }
+  };
+  weights_pass(resid);
+  __syncthreads();
+  const double u = (double)a.u[(size_t)b * G1 + a.G];
+  auto locate = [&]() {
+    if (threadIdx.x < 64) {
+      double tt = 0.0;
+      if (lane < ntile) {
+#pragma unroll
+        for (int w = 0; w < PH_NW; ++w) tt += s.part[lane][w];
+      }
+      const double incl = wave_incl_scan_f64(tt);
+      const double Z = readlane_f64(incl, 63);
+      const double target = u * Z;
+      const unsigned long long hit = __ballot(lane < ntile && incl > target);
+      const int j = hit ? __ffsll((long long)hit) - 1 : ntile - 1;
+      if (lane == j) {
+        s.bc[0] = (uint32_t)j;
+        s.bd[0] = incl - tt;
+      }
+      if (lane == 0) s.bd[1] = Z > 0.0 ? target : -1.0;
+    }
+    __syncthreads();
+  };
+  locate();
+  bool use_q = resid;
+  if (resid && !(s.bd[1] >= 0.0)) {
+    // Zero residual mass (p == q after processing): draw from p itself.  The
+    // overlap already summed stays (q = 0 adds nothing to it).
+    __syncthreads();
+    sqw.zthr = INFINITY;
+    const double al0 = al;
+    weights_pass(false);
+    al = al0;
+    __syncthreads();
+    locate();
+    use_q = false;
+  }
+  const int tj = (int)s.bc[0];
+  const double base = s.bd[0], target = s.bd[1];
+  // Examine the crossing tile again, in ascending id.
+  uint32_t hitpos = 0xFFFFFFFFu, lastpos = 0;
+  {
+    const int ui = tj * PH_NT + (int)threadIdx.x;
+    const uint4 up = ph_load<0>(rp, tj);
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = 0.0f;
+    float r = 0.0f;
+    const uint4 uq = use_q ? ph_load<0>(rq, tj) : up;
+    if (ui < NU) {
+      T::each(up, [&](int e, uint32_t raw) { w[e] = pprob(sp, T::val(raw)); });
+      T::each(uq, [&](int e, uint32_t raw) {
+        w[e] = fmaxf(w[e] - pprob(sqw, T::val(raw)), 0.0f);
+        r += w[e];
+      });
+    }
+    const double rd = (double)r;
+    const double incl = wave_incl_scan_f64(rd);
+    double cum = base;
+    for (int w2 = 0; w2 < wave; ++w2) cum += s.part[tj][w2];
+    cum += incl - rd;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      cum += (double)w[e];
+      const uint32_t idx = (uint32_t)(ui * 8 + e);
+      if (hitpos == 0xFFFFFFFFu && w[e] > 0.0f && cum > target) hitpos = idx;
+      if (w[e] > 0.0f) lastpos = idx + 1u;
+    }
+  }
+  hitpos = pb_min<PH_NT>(hitpos, s.red);
+  int tok = (int)hitpos;
+  if (hitpos == 0xFFFFFFFFu) tok = (int)pb_max<PH_NT>(lastpos, s.red) - 1;   // rounding left no crossing
+  if (resid) {
+    al = wave_sum_dpp(al);
+    __syncthreads();
+    if (lane == 0) s.part[0][wave] = al;
+    __syncthreads();
+    double tot = 0.0;
+    for (int w2 = 0; w2 < PH_NW; ++w2) tot += s.part[0][w2];
+    al = tot;
+  }
+  if (threadIdx.x == 0) {
+    const int x = resid ? a.draft[(size_t)b * a.G + i] : -1;
+    double pxv = 0.0, qxv = 0.0;
+    if (x >= 0 && x < V) {
+      const uint16_t* pr = reinterpret_cast<const uint16_t*>(gp);
+      const uint16_t* qr = reinterpret_cast<const uint16_t*>(gq);
+      pxv = (double)pprob(sp, T::val(pr[x]));
+      qxv = (double)pprob(sq, T::val(qr[x]));
+    }
+    rec->px = pxv;
+    rec->qx = qxv;
+    rec->alpha = al;
+    rec->tok = tok;
+    rec->bad = 0u;
+  }
+}
+
+// The dense pairs, one workgroup per CU, in the order and with the shared
+// work counter of the streamed pair variant: workgroup w starts with pair w,
+// and a workgroup that has finished takes the next unstarted pair.
+__global__ __launch_bounds__(PH_NT) void pair_hist_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char ph_raw[];
+  PhSmem& s = *reinterpret_cast<PhSmem*>(ph_raw);
+  const int G1 = a.G + 1;
+  const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
+  const bool direct = a.all_dense != 0;
+  const uint32_t nf = direct ? npairs : min(a.dense_count[0], npairs);
+  const uint32_t nd = direct ? npairs : min(nf + a.dense_count[1], npairs);
+  const uint32_t nlead = (uint32_t)a.B * (uint32_t)a.G;
+  uint32_t t = blockIdx.x;
+  while (t < nd) {
+    int pid;
+    if (direct) {
+      pid = t < nlead ? (int)((t / (uint32_t)a.G) * (uint32_t)G1 + t % (uint32_t)a.G)
+                      : (int)((t - nlead) * (uint32_t)G1 + (uint32_t)a.G);
+    } else {
+      const uint32_t idx = t < nf ? t : npairs - 1u - (t - nf);
+      pid = a.dense_list[idx];
+    }
+    if (pid >= 0 && (uint32_t)pid < npairs) {
+      const int b = pid / G1;
+      pair_hist_one(a, b, pid - b * G1, s);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s.next_pair = gridDim.x + atomicAdd(&a.dense_count[2], 1u);
+    __syncthreads();
+    t = s.next_pair;
+  }
+}
+
+}  // namespace sv

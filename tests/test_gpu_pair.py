@@ -153,3 +153,69 @@ def test_all_dense_hint_matches_oracle(cid, B, V, label):
     ref = run_oracle(bt)
     for call in range(2):
         compare(bt, run_gpu(bt, verifier=ver), ref, f"all-dense-{label}-call{call}")
+
+
+# ---- bf16 rows counted in an LDS histogram of their values -------------------
+
+@pytest.mark.parametrize("V", [32776, 65544, 131072])
+def test_histogram_rows_sizes_and_filters(V):
+    """Streamed bf16 rows from just above the LDS-held size to the largest
+    the histogram variant takes (V = 131072, 32 units per thread, partial
+    last tile at 32776 and 65544), with unfiltered, top-p (including 0),
+    large top-k, top-k plus top-p, -inf entries and extreme temperatures."""
+    B, G = 10, 3
+    T = np.array([1.0, 0.6, 1.3, 0.8, 1.0, 0.7, 1e-3, 50.0, 1.1, 0.9], np.float32)
+    k = np.array([0, 0, 0, 600, 5000, 0, 0, 0, 700, 0], np.int32)
+    tp = np.array([1.0, 0.9, 0.0, 1.0, 0.85, 0.3, 0.95, 0.9, 1.0, 0.99], np.float32)
+    rng = np.random.default_rng(V % 1009)
+    rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
+    zp = (3.0 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
+    zq = (zp[:, :G] + 0.7 * rng.normal(size=(B, G, V))).astype(np.float32)
+    zp[9, :, ::7] = -np.inf                    # -inf entries carry no mass
+    zq[9, :, 3::11] = -np.inf
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=V % 89, T=T, k=k, tp=tp, zp=zp, zq=zq)
+    log(f"[pair-hist] V={V}")
+    rep = compare(bt, run_gpu(bt), run_oracle(bt), f"pair-hist-V{V}")
+    log(f"[pair-hist] V={V}: ok {rep}")
+
+
+def test_histogram_count_overflow_takes_the_multipass_path():
+    """More than 65535 equal values in one row overflow its 16-bit count: the
+    pair is marked for the finisher, which computes the sequence from the
+    logits.  Rows of sequence 0 overflow in both, sequence 1 only in the
+    draft rows, sequence 2 only in the target rows; sequence 3 is ordinary."""
+    B, G, V = 4, 2, 131072
+    rng = np.random.default_rng(44)
+    zp = (2.0 * rng.normal(size=(B, G + 1, V))).astype(np.float32)
+    zq = (zp[:, :G] + 0.5 * rng.normal(size=(B, G, V))).astype(np.float32)
+    zp[0, :, :70000] = 0.25
+    zq[0, :, :70000] = 0.25
+    zq[1, :, 1000:67000] = -1.0
+    zp[2, :, 500:66500] = 0.5
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=12, zp=zp, zq=zq, T=np.array([1.0, 0.8, 1.2, 1.0]),
+                     tp=np.array([1.0, 0.9, 0.8, 0.9], np.float32))
+    rep = compare(bt, run_gpu(bt), run_oracle(bt), "hist-overflow")
+    log(f"[pair-hist] overflow: ok {rep}")
+
+
+def test_histogram_row_with_nan_is_invalid_and_others_exact():
+    B, G, V = 4, 2, 50000
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=13, T=np.array([1.0, 0.8, 1.2, 1.0]),
+                     tp=np.array([1.0, 0.9, 0.8, 0.9], np.float32))
+    P, Q = bt.p_logits.copy(), bt.q_logits.copy()
+    Q[1, 1, 777] = 0x7FC1                     # NaN in a draft row
+    P[2, 2, 5] = 0x7F80                       # +inf in the bonus row
+    bt = synth.Batch(bt.workload, P, Q, bt.draft, bt.u, bt.gamma_len, bt.temperature, bt.top_k, bt.top_p, bt.seed)
+    g = run_gpu(bt)
+    ref = run_oracle(bt)
+    assert ref.n[1] == -1 and ref.n[2] == -1
+    compare(bt, g, ref, "hist-invalid")
+
+
+def test_streamed_rows_beyond_the_histogram_variant():
+    # 17500 units per row: more than the histogram variant holds, so the
+    # value-binned streamed variant takes these rows.
+    V = 140000
+    bt = dense_batch(V, "bf16", B=3, G=2, seed=14, T=np.array([1.0, 0.7, 1.2]),
+                     tp=np.array([1.0, 0.9, 0.8], np.float32))
+    compare(bt, run_gpu(bt), run_oracle(bt), "streamed-V140000")

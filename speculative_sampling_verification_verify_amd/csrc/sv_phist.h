@@ -43,14 +43,18 @@ constexpr int PH_NW = PH_NT / 64;
 constexpr int PH_UPT = 16;                  // 16-byte units of a row per thread
 constexpr int PH_WORDS = 32768;             // histogram words: bf16 key 2j in the low half of word j, 2j+1 high
 constexpr int PH_INFLIGHT = 8;              // units of a row in flight per thread while it streams
+constexpr int PH_WINFLIGHT = 8;             // list entries in flight per thread in the weights pass
 constexpr int PH_MAX_UNITS = PH_NT * PH_UPT;
-constexpr int PH_SEGW = 64;                 // histogram words per segment (one per lane)
-constexpr int PH_NSEG = PH_WORDS / PH_SEGW; // 512 segments
+constexpr int PH_BLKW = 256;                // histogram words per block (four per lane of a wavefront)
+constexpr int PH_NBLK = PH_WORDS / PH_BLKW; // 128 blocks
+constexpr int PH_BPW = PH_NBLK / PH_NW;     // blocks per wavefront
 
 struct PhSmem {
   uint32_t hist[PH_WORDS];
-  uint8_t umax[PH_MAX_UNITS];               // top byte of each target unit's largest key
-  double seg[PH_NSEG];                      // per-segment sums of a histogram scan
+  uint8_t umax[PH_MAX_UNITS];               // bucket (ph_bucket) of each target unit's largest value
+  float uref[PH_UPT / PH_INFLIGHT][PH_NW];  // the floor those buckets start from, per (batch, wavefront)
+  double blk[PH_NBLK];                      // per-block sums of f(key, count) from the last ph_sums
+  double wpart[PH_NW];                      // per-wavefront totals of the same
   double part[PH_UPT][PH_NW];               // draw-weight sum per (tile, wavefront)
   uint32_t red[5 * PH_NW];
   uint32_t bc[8];
@@ -106,115 +110,149 @@ __device__ __forceinline__ uint32_t ph_unit_max(const uint4& u) {
   ph_extremes_unit(u, mx, mn);
   return max(mx & 0xFFFFu, mx >> 16);
 }
+// Bucket of a value z above a floor zf in steps of 1 / inv: 0 below the
+// floor (or for NaN), 1 + floor((z - zf) inv) up to 255.  Non-decreasing in
+// z for fixed zf and inv, so a unit whose largest value reaches a threshold
+// has a bucket at least the threshold's: comparing buckets never skips a unit
+// that holds a value at or above it.  A floor of -inf puts every value in 255.
+__device__ __forceinline__ uint32_t ph_bucket(float z, float zf, float inv) {
+  if (!(z >= zf)) return 0u;
+  const float t = (z - zf) * inv;
+  return t >= 254.0f ? 255u : 1u + (uint32_t)t;
+}
 
 struct PhFind {
   uint32_t key;    // the key where the running sum first reaches tau (NONE: never)
   double above;    // sum over larger keys
   double at;       // above + the key's own contribution
-  double total;    // sum over every key
-  uint32_t count;  // decoded counts over every key
 };
 
-// A scan of the histogram with per-key contributions f(key, count) (double):
-// the total, the decoded counts, and (tau > 0) the largest key at which the
-// running sum over descending keys reaches tau.  Segments of 64 words are
-// summed by whole wavefronts, one word per lane (empty segments skipped by a
-// ballot), so the keys that hold elements, however few and however close,
-// are spread over all the lanes; the sums use DPP lane moves only.
-// Wavefront 0 then scans the 512 segment sums in descending order and, within
-// the crossing segment, its 64 words.
+// Sums of per-key contributions f(key, count) (double) over the histogram:
+// each block of 256 words (512 keys) is summed by one wavefront, four words
+// per lane read at once, blocks that hold no count skipped by a ballot, and
+// its sum is kept in s.blk for ph_find.  Blocks outside [b_lo, b_hi] hold no
+// counted key and are not read.  Returns the total (the per-wavefront sums
+// added in wavefront order) and the decoded counts (block-uniform).
 template <class F>
-__device__ __forceinline__ PhFind ph_scan(PhSmem& s, F f, double tau, int sg_lo, int sg_hi) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+__device__ __forceinline__ double ph_sums(PhSmem& s, F f, int b_lo, int b_hi, uint32_t& count) {
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), l = threadIdx.x & 63;
+  const uint4* h4 = reinterpret_cast<const uint4*>(s.hist);
   uint32_t cnt = 0;
-  // Segments outside [sg_lo, sg_hi] hold no counted key: they are zero.
-  for (int sg = w; sg < PH_NSEG; sg += PH_NW)
-    if ((sg < sg_lo || sg > sg_hi) && l == 0) s.seg[sg] = 0.0;
-  // Eight segments' words are read before any is examined.
-  constexpr int B = 8;
-  for (int sg0 = sg_lo + w; sg0 <= sg_hi; sg0 += B * PH_NW) {
-    uint32_t word[B];
+  double wsum = 0.0;
+  constexpr int HALF = PH_BPW / 2;
+#pragma unroll 1
+  for (int r0 = 0; r0 < PH_BPW; r0 += HALF) {
+    uint4 q[HALF];
 #pragma unroll
-    for (int r = 0; r < B; ++r) {
-      const int sg = sg0 + r * PH_NW;
-      word[r] = sg <= sg_hi ? s.hist[sg * PH_SEGW + l] : 0u;
+    for (int r = 0; r < HALF; ++r) {
+      const int bk = w + (r0 + r) * PH_NW;
+      q[r] = bk >= b_lo && bk <= b_hi ? h4[bk * (PH_BLKW / 4) + l] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int r = 0; r < B; ++r) {
-      const int sg = sg0 + r * PH_NW;
-      if (sg > sg_hi) break;
-      const int wd = sg * PH_SEGW + l;
+    for (int r = 0; r < HALF; ++r) {
+      const int bk = w + (r0 + r) * PH_NW;
       double v = 0.0;
-      if (__ballot(word[r] != 0u)) {
-        const uint32_t chi = word[r] >> 16, clo = word[r] & 0xFFFFu;
-        cnt += chi + clo;
-        if (chi) v += f(2u * (uint32_t)wd + 1u, chi);
-        if (clo) v += f(2u * (uint32_t)wd, clo);
+      if (__ballot((q[r].x | q[r].y | q[r].z | q[r].w) != 0u)) {
+        const uint32_t wd0 = (uint32_t)(bk * PH_BLKW + 4 * l);
+        const uint32_t ww[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          const uint32_t chi = ww[j] >> 16, clo = ww[j] & 0xFFFFu;
+          cnt += chi + clo;
+          if (chi) v += f(2u * (wd0 + (uint32_t)j) + 1u, chi);
+          if (clo) v += f(2u * (wd0 + (uint32_t)j), clo);
+        }
         v = wave_sum_dpp(v);
+        wsum += v;
       }
-      if (l == 0) s.seg[sg] = v;
+      if (l == 0) s.blk[bk] = v;
     }
   }
   cnt = wave_reduce_dpp_u32(cnt, 0u, [](uint32_t x, uint32_t y) { return x + y; });
-  if (l == 0) s.red[3 * PH_NW + w] = cnt;
+  if (l == 0) {
+    s.red[3 * PH_NW + w] = cnt;
+    s.wpart[w] = wsum;
+  }
   __syncthreads();
-  PhFind r;
-  r.count = 0;
-  for (int x = 0; x < PH_NW; ++x) r.count += s.red[3 * PH_NW + x];
-  if (w == 0) {
-    // Lane l: segments 511 - 8 l .. 504 - 8 l (descending keys).
-    double sv[8], ls = 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sv[i] = s.seg[PH_NSEG - 1 - 8 * l - i];
-      ls += sv[i];
-    }
-    const double inc = wave_incl_scan_f64(ls);
-    const double tot = readlane_f64(inc, 63);
+  count = 0;
+  double tot = 0.0;
+  for (int x = 0; x < PH_NW; ++x) {
+    count += s.red[3 * PH_NW + x];
+    tot += s.wpart[x];
+  }
+  __syncthreads();   // red / wpart are written again by the next call
+  return tot;
+}
+
+// The largest key at which the running sum of f over descending keys reaches
+// tau (> 0), from the block sums of the last ph_sums with the same f.
+// Wavefront 0 scans the 128 block sums (two per lane), then, within the
+// crossing block, the per-lane sums of its 512 keys (eight per lane), then
+// the eight keys of the crossing lane.  Where rounding leaves a level's
+// running sum short of tau, its smallest entry is taken.
+template <class F>
+__device__ __forceinline__ PhFind ph_find(PhSmem& s, F f, double tau) {
+  const int l = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == 0) {
+    // Lane l: blocks 127 - 2 l and 126 - 2 l (descending keys).
+    const double b1 = s.blk[PH_NBLK - 1 - 2 * l], b0 = s.blk[PH_NBLK - 2 - 2 * l];
+    const double inc = wave_incl_scan_f64(b1 + b0);
     uint32_t key = NONE;
     double above = 0.0, at = 0.0;
-    if (tau > 0.0 && tot >= tau) {
+    if (readlane_f64(inc, 63) >= tau) {
       const unsigned long long hit = __ballot(inc >= tau);
       const int cl = __ffsll((long long)hit) - 1;
-      // The crossing segment within lane cl's eight.
-      double run = readlane_f64(inc - ls, cl);
-      int csg = PH_NSEG - 1 - 8 * cl;
-      for (int i = 0; i < 8; ++i) {
-        const double svi = readlane_f64(sv[i], cl);
-        csg = PH_NSEG - 1 - 8 * cl - i;
-        if (run + svi >= tau) break;
-        run += svi;
+      double run = readlane_f64(inc - b1 - b0, cl);
+      const double c1 = readlane_f64(b1, cl);
+      const bool upper = run + c1 >= tau;
+      const int cb = upper ? PH_NBLK - 1 - 2 * cl : PH_NBLK - 2 - 2 * cl;
+      if (!upper) run += c1;
+      // Lane l: words 4 (63 - l) + 3 .. 4 (63 - l) of the block, descending.
+      const uint32_t wd0 = (uint32_t)(cb * PH_BLKW + 4 * (63 - l));
+      const uint4 q = reinterpret_cast<const uint4*>(s.hist)[cb * (PH_BLKW / 4) + (63 - l)];
+      const uint32_t ww[4] = {q.x, q.y, q.z, q.w};
+      double ls = 0.0;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const uint32_t chi = ww[j] >> 16, clo = ww[j] & 0xFFFFu;
+        if (chi) ls += f(2u * (wd0 + (uint32_t)j) + 1u, chi);
+        if (clo) ls += f(2u * (wd0 + (uint32_t)j), clo);
       }
-      // Its words, lane l taking word 63 - l (descending keys).
-      const int wd = csg * PH_SEGW + (PH_SEGW - 1 - l);
-      const uint32_t word = s.hist[wd];
-      const uint32_t chi = word >> 16, clo = word & 0xFFFFu;
-      const double fh = chi ? f(2u * (uint32_t)wd + 1u, chi) : 0.0;
-      const double fl = clo ? f(2u * (uint32_t)wd, clo) : 0.0;
-      const double winc = wave_incl_scan_f64(fh + fl);
+      const double winc = wave_incl_scan_f64(ls);
       const unsigned long long whit = __ballot(run + winc >= tau);
-      const int wl = whit ? __ffsll((long long)whit) - 1 : 63;
-      const double b0 = run + readlane_f64(winc - fh - fl, wl);
-      const double fhw = readlane_f64(fh, wl), flw = readlane_f64(fl, wl);
-      const int wdw = __builtin_amdgcn_readlane(wd, wl);
-      const bool high = fhw > 0.0 && b0 + fhw >= tau;
-      key = high ? 2u * (uint32_t)wdw + 1u : 2u * (uint32_t)wdw;
-      above = high ? b0 : b0 + fhw;
-      at = high ? b0 + fhw : b0 + fhw + flw;
+      const unsigned long long nz = __ballot(ls > 0.0);
+      const int wl = whit ? __ffsll((long long)whit) - 1 : (nz ? 63 - __clzll((long long)nz) : 63);
+      const double base = run + readlane_f64(winc - ls, wl);
+      // Lanes 0..7: the crossing lane's keys in descending order.
+      const uint32_t lw0 = (uint32_t)__builtin_amdgcn_readlane((int)wd0, wl);
+      double mk = 0.0;
+      uint32_t kk = 0u;
+      if (l < 8) {
+        kk = 2u * (lw0 + 3u - (uint32_t)(l >> 1)) + 1u - (uint32_t)(l & 1);
+        const uint32_t word = s.hist[kk >> 1];
+        const uint32_t cn = (kk & 1u) ? word >> 16 : word & 0xFFFFu;
+        if (cn) mk = f(kk, cn);
+      }
+      const double kinc = wave_incl_scan_f64(mk);
+      const unsigned long long khit = __ballot(l < 8 && base + kinc >= tau);
+      const unsigned long long knz = __ballot(mk > 0.0);
+      const int kl = khit ? __ffsll((long long)khit) - 1 : (knz ? 63 - __clzll((long long)knz) : 7);
+      key = (uint32_t)__builtin_amdgcn_readlane((int)kk, kl);
+      at = base + readlane_f64(kinc, kl);
+      above = at - readlane_f64(mk, kl);
     }
     if (l == 0) {
       s.bc[0] = key;
       s.bd[0] = above;
       s.bd[1] = at;
-      s.seg[0] = tot;
     }
   }
   __syncthreads();
+  PhFind r;
   r.key = s.bc[0];
   r.above = s.bd[0];
   r.at = s.bd[1];
-  r.total = s.seg[0];
-  __syncthreads();   // seg / bc / bd / red are reused by the next scan
+  __syncthreads();   // bc / bd are written again by the next call
   return r;
 }
 
@@ -230,7 +268,7 @@ __device__ __forceinline__ int ph_stats(PhSmem& s, uint32_t kmax, uint32_t kmin,
   using K = Key<uint16_t>;
   if (kmax >= K::POS_INF || kmin < K::NEG_INF || kmax <= K::NEG_INF) return PH_BAD;
   // Counted keys lie in [max(kmin, kcount_min), kmax]: only their segments are scanned.
-  const int sg_lo = (int)(max(kmin, kcount_min) >> 1) / PH_SEGW, sg_hi = (int)(kmax >> 1) / PH_SEGW;
+  const int b_lo = (int)(max(kmin, kcount_min) >> 1) / PH_BLKW, b_hi = (int)(kmax >> 1) / PH_BLKW;
   st.zmax = K::value(kmax);
   st.c = LOG2E_F / m.T;
   st.zthr = -INFINITY;
@@ -239,9 +277,12 @@ __device__ __forceinline__ int ph_stats(PhSmem& s, uint32_t kmax, uint32_t kmin,
   bool counted = false;
   if (k > 0 && k < V) {
     // Top-k: the k-th largest key (ties kept) from the counts.
-    const PhFind f = ph_scan(s, [](uint32_t, uint32_t cn) { return (double)cn; }, (double)k, sg_lo, sg_hi);
-    if (f.count + skipped != (uint32_t)V) return PH_OVERFLOW;
+    auto count_of = [](uint32_t, uint32_t cn) { return (double)cn; };
+    uint32_t n = 0;
+    ph_sums(s, count_of, b_lo, b_hi, n);
+    if (n + skipped != (uint32_t)V) return PH_OVERFLOW;
     counted = true;
+    const PhFind f = ph_find(s, count_of, (double)k);
     if (f.key != NONE && f.key > kthr) kthr = f.key;
   }
   // A key's mass: its count times its weight e = 2^((z - zmax) c).
@@ -250,9 +291,9 @@ __device__ __forceinline__ int ph_stats(PhSmem& s, uint32_t kmax, uint32_t kmin,
     return (double)cn * (double)ew(K::value(key), zmax, c);
   };
   if (kthr > K::NEG_INF + 1u) st.zthr = K::value(kthr);
-  const PhFind t = ph_scan(s, mass, -1.0, sg_lo, sg_hi);
-  if (!counted && t.count + skipped != (uint32_t)V) return PH_OVERFLOW;
-  double S = t.total;
+  uint32_t n = 0;
+  double S = ph_sums(s, mass, b_lo, b_hi, n);
+  if (!counted && n + skipped != (uint32_t)V) return PH_OVERFLOW;
   if (m.tp < 1.0f) {
     if (m.tp <= 0.0f) {
       // Only the largest value (with its ties) survives.
@@ -261,7 +302,7 @@ __device__ __forceinline__ int ph_stats(PhSmem& s, uint32_t kmax, uint32_t kmin,
       S = (double)((kmax & 1u) ? word >> 16 : word & 0xFFFFu);
     } else {
       // The nucleus: the largest value whose mass at or above reaches top_p S.
-      const PhFind f = ph_scan(s, mass, (double)m.tp * S, sg_lo, sg_hi);
+      const PhFind f = ph_find(s, mass, (double)m.tp * S);
       if (f.key != NONE && f.at > 0.0) {
         st.zthr = fmaxf(st.zthr, K::value(f.key));
         S = f.at;
@@ -281,6 +322,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ph_rsrc(const uint4* row, int 
 template <int AUX>
 __device__ __forceinline__ uint4 ph_load(__amdgpu_buffer_rsrc_t r, int j) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)threadIdx.x * 16, j * PH_NT * 16, AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Unit ui of a row (any thread, any unit) through the row's descriptor.
+template <int AUX>
+__device__ __forceinline__ uint4 ph_load_unit(__amdgpu_buffer_rsrc_t r, int ui) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, ui * 16, 0, AUX);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -326,6 +374,7 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
   PosRec* rec = a.pos + (size_t)b * G1 + i;
   const int fb = a.fixbits;
   const float cT = LOG2E_F / m.T;
+  const float binv = 254.0f * cT / (float)(fb + 2);   // buckets per unit of value
   const bool filter_k = k > 0 && k < V;
   int bad = 0;
 
@@ -348,31 +397,48 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
       uint4 u[PH_INFLIGHT];
 #pragma unroll
       for (int r = 0; r < PH_INFLIGHT; ++r) u[r] = ph_load<0>(rr, j0 + r);
+      uint32_t umx[PH_INFLIGHT / 2];   // the units' largest keys, two per word
+      uint32_t bmin2 = 0xFFFFFFFFu;    // the batch's smallest keys
 #pragma unroll
       for (int r = 0; r < PH_INFLIGHT; ++r) {
         const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
+        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
         if (ui < NU) {
-          uint32_t mx = 0u, mn = 0xFFFFFFFFu;
           ph_extremes_unit(u[r], mx, mn);
           kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
                                                                          __builtin_bit_cast(ph_u16x2, mx)));
-          kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
+          bmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, bmin2),
                                                                          __builtin_bit_cast(ph_u16x2, mn)));
-          if (row == 1) s.umax[ui] = (uint8_t)(max(mx & 0xFFFFu, mx >> 16) >> 8);
         }
+        const uint32_t m1 = max(mx & 0xFFFFu, mx >> 16);
+        umx[r >> 1] = (r & 1) ? umx[r >> 1] | (m1 << 16) : m1;
       }
+      // The floor: the value (fb + 2) / c below the wavefront's running
+      // maximum, also the origin of the target units' buckets (in steps of
+      // 1/254 of that distance).
+      const uint32_t wmax = wave_max_dpp(max(kmax2 & 0xFFFFu, kmax2 >> 16));
+      float zf = -INFINITY;
+      if (wmax > Key<uint16_t>::NEG_INF && wmax < Key<uint16_t>::POS_INF)
+        zf = Key<uint16_t>::value(wmax) - (float)(fb + 2) / cT;
       uint32_t kfloor = 0u;
-      if (!filter_k) {
-        const uint32_t wmax = wave_max_dpp(max(kmax2 & 0xFFFFu, kmax2 >> 16));
-        if (wmax > Key<uint16_t>::NEG_INF && wmax < Key<uint16_t>::POS_INF) {
-          // Smallest bf16 key whose value is at least wmax's - (fb + 2) / c.
-          const float zf = Key<uint16_t>::value(wmax) - (float)(fb + 2) / cT;
-          const uint32_t bits = __float_as_uint(zf);
-          const uint32_t b16 = zf >= 0.0f ? (bits + 0xFFFFu) >> 16 : bits >> 16;
-          kfloor = zf > -INFINITY ? Key<uint16_t>::of_bits(b16) : 0u;
+      if (!filter_k && zf > -INFINITY) {
+        // Smallest bf16 key whose value is at least zf.
+        const uint32_t bits = __float_as_uint(zf);
+        const uint32_t b16 = zf >= 0.0f ? (bits + 0xFFFFu) >> 16 : bits >> 16;
+        kfloor = Key<uint16_t>::of_bits(b16);
+      }
+      if (row == 1) {
+        if (lane == 0) s.uref[j0 / PH_INFLIGHT][wave] = zf;
+#pragma unroll
+        for (int r = 0; r < PH_INFLIGHT; ++r) {
+          const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
+          const uint32_t m1 = (r & 1) ? umx[r >> 1] >> 16 : umx[r >> 1] & 0xFFFFu;
+          if (ui < NU) s.umax[ui] = (uint8_t)ph_bucket(Key<uint16_t>::value(m1), zf, binv);
         }
       }
       kf_first = min(kf_first, kfloor);
+      kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
+                                                                     __builtin_bit_cast(ph_u16x2, bmin2)));
 #pragma unroll
       for (int r = 0; r < PH_INFLIGHT; ++r)
         if ((j0 + r) * PH_NT + (int)threadIdx.x < NU) ph_add_unit(s.hist, u[r], kfloor, skipped);
@@ -408,33 +474,78 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
     return;
   }
 
-  // Overlap and per-(tile, wavefront) draw-weight sums: the residual
-  // max(0, p - q), or p at the bonus position and when the residual is zero
-  // (there the draft's threshold is +inf, so q = 0 everywhere and the same
-  // code sums p).  Only units whose largest target key can reach the target's
-  // nucleus threshold are read again (p = 0 elsewhere: neither sum has a term).
-  const int ntile = (NU + PH_NT - 1) / PH_NT;
+  // The units read again: those whose largest target value can reach the
+  // target's nucleus threshold (elsewhere p = 0, so neither the overlap nor a
+  // draw weight has a term), listed in ascending unit order in the
+  // histogram's memory, free once both rows' statistics are known.  Every
+  // list entry is then one thread's work, so a wavefront computes only units
+  // that are needed, however few and however scattered.
+  uint16_t* list = reinterpret_cast<uint16_t*>(s.hist);
+  uint32_t* lcnt = s.hist + PH_WORDS / 2;   // per-(tile, wavefront) counts, then their offsets
+  uint32_t nd_bits = 0;
+#pragma unroll 1
+  for (int j = 0; j < PH_UPT; ++j) {
+    const int ui = j * PH_NT + (int)threadIdx.x;
+    const bool nd = ui < NU && (uint32_t)s.umax[ui] >= ph_bucket(sp.zthr, s.uref[j / PH_INFLIGHT][wave], binv);
+    const unsigned long long bal = __ballot(nd);
+    nd_bits |= nd ? 1u << j : 0u;
+    if (lane == 0) lcnt[j * PH_NW + wave] = (uint32_t)__popcll(bal);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // Exclusive prefix of the (tile, wavefront) counts in that order, four per lane.
+    uint32_t c4[4], sum4 = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      c4[x] = lcnt[4 * lane + x];
+      sum4 += c4[x];
+    }
+    const uint32_t inc = wave_incl_scan_dpp(sum4);
+    uint32_t run = inc - sum4;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      lcnt[4 * lane + x] = run;
+      run += c4[x];
+    }
+    if (lane == 63) s.bc[1] = inc;
+  }
+  __syncthreads();
+  const int nlist = (int)s.bc[1];
+#pragma unroll 1
+  for (int j = 0; j < PH_UPT; ++j) {
+    const bool nd = (nd_bits >> j) & 1u;
+    const unsigned long long bal = __ballot(nd);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (nd) list[lcnt[j * PH_NW + wave] + below] = (uint16_t)(j * PH_NT + (int)threadIdx.x);
+  }
+  __syncthreads();
+
+  // Overlap and per-(chunk, wavefront) draw-weight sums over the list, a
+  // chunk being PH_NT consecutive entries: the residual max(0, p - q), or p
+  // at the bonus position and when the residual is zero (there the draft's
+  // threshold is +inf, so q = 0 everywhere and the same code sums p).
+  const int nch = max(1, (nlist + PH_NT - 1) / PH_NT);
   double al = 0.0;
   RowStat sqw = sq;   // the draft's statistics as the draw uses them (q = 0 once the residual is empty)
-  const uint32_t kpthr8 = (sp.zthr > -INFINITY ? key_of_value<uint16_t>(sp.zthr) : 0u) >> 8;
   auto weights_pass = [&](bool use_q) {
-    for (int j0 = 0; j0 < ntile; j0 += PH_INFLIGHT) {
-      uint4 up[PH_INFLIGHT], uq[PH_INFLIGHT];
-      bool nd[PH_INFLIGHT];
+    for (int c0 = 0; c0 < nch; c0 += PH_WINFLIGHT) {
+      uint4 up[PH_WINFLIGHT], uq[PH_WINFLIGHT];
+      bool nd[PH_WINFLIGHT];
 #pragma unroll
-      for (int r = 0; r < PH_INFLIGHT; ++r) {
-        const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
-        nd[r] = ui < NU && (uint32_t)s.umax[ui] >= kpthr8;
+      for (int r = 0; r < PH_WINFLIGHT; ++r) {
+        const int le = (c0 + r) * PH_NT + (int)threadIdx.x;
+        nd[r] = le < nlist;
         up[r] = make_uint4(0u, 0u, 0u, 0u);
         uq[r] = up[r];
         if (nd[r]) {
-          up[r] = ph_load<BUF_NT>(rp, j0 + r);
-          if (use_q) uq[r] = ph_load<BUF_NT>(rq, j0 + r);
+          const int ui = list[le];
+          up[r] = ph_load_unit<BUF_NT>(rp, ui);
+          if (use_q) uq[r] = ph_load_unit<BUF_NT>(rq, ui);
         }
       }
 #pragma unroll
-      for (int r = 0; r < PH_INFLIGHT; ++r) {
-        if (j0 + r >= ntile) break;
+      for (int r = 0; r < PH_WINFLIGHT; ++r) {
+        if (c0 + r >= nch) break;
         float rs = 0.0f, av = 0.0f;
         if (nd[r]) {
           const uint32_t pw[4] = {up[r].x, up[r].y, up[r].z, up[r].w}, qw[4] = {uq[r].x, uq[r].y, uq[r].z, uq[r].w};
@@ -449,7 +560,7 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
         }
         al += (double)av;
         const double wsum = wave_sum_dpp((double)rs);
-        if (lane == 0) s.part[j0 + r][wave] = wsum;
+        if (lane == 0) s.part[c0 + r][wave] = wsum;
       }
     }
   };
@@ -459,15 +570,15 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
   auto locate = [&]() {
     if (threadIdx.x < 64) {
       double tt = 0.0;
-      if (lane < ntile) {
+      if (lane < nch) {
 #pragma unroll
         for (int w = 0; w < PH_NW; ++w) tt += s.part[lane][w];
       }
       const double incl = wave_incl_scan_f64(tt);
       const double Z = readlane_f64(incl, 63);
       const double target = u * Z;
-      const unsigned long long hit = __ballot(lane < ntile && incl > target);
-      const int j = hit ? __ffsll((long long)hit) - 1 : ntile - 1;
+      const unsigned long long hit = __ballot(lane < nch && incl > target);
+      const int j = hit ? __ffsll((long long)hit) - 1 : nch - 1;
       if (lane == j) {
         s.bc[0] = (uint32_t)j;
         s.bd[0] = incl - tt;
@@ -492,17 +603,19 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
   }
   const int tj = (int)s.bc[0];
   const double base = s.bd[0], target = s.bd[1];
-  // Examine the crossing tile again, in ascending id.
+  // Examine the crossing chunk's units again, in ascending id.
   uint32_t hitpos = 0xFFFFFFFFu, lastpos = 0;
   {
-    const int ui = tj * PH_NT + (int)threadIdx.x;
-    const uint4 up = ph_load<0>(rp, tj);
+    const int le = tj * PH_NT + (int)threadIdx.x;
+    const bool has = le < nlist;
+    const int ui = has ? (int)list[le] : 0;
+    const uint4 up = ph_load_unit<0>(rp, ui);
     float w[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = 0.0f;
     float r = 0.0f;
-    const uint4 uq = use_q ? ph_load<0>(rq, tj) : up;
-    if (ui < NU) {
+    const uint4 uq = use_q ? ph_load_unit<0>(rq, ui) : up;
+    if (has) {
       T::each(up, [&](int e, uint32_t raw) { w[e] = pprob(sp, T::val(raw)); });
       T::each(uq, [&](int e, uint32_t raw) {
         w[e] = fmaxf(w[e] - pprob(sqw, T::val(raw)), 0.0f);

@@ -160,7 +160,7 @@ def test_all_dense_hint_matches_oracle(cid, B, V, label):
 @pytest.mark.parametrize("V", [32776, 65544, 131072])
 def test_histogram_rows_sizes_and_filters(V):
     """Streamed bf16 rows from just above the LDS-held size to the largest
-    the histogram variant takes (V = 131072, 32 units per thread, partial
+    the histogram variant takes (V = 131072, 16 units per thread, partial
     last tile at 32776 and 65544), with unfiltered, top-p (including 0),
     large top-k, top-k plus top-p, -inf entries and extreme temperatures."""
     B, G = 10, 3
@@ -177,6 +177,30 @@ def test_histogram_rows_sizes_and_filters(V):
     log(f"[pair-hist] V={V}")
     rep = compare(bt, run_gpu(bt), run_oracle(bt), f"pair-hist-V{V}")
     log(f"[pair-hist] V={V}: ok {rep}")
+
+
+def test_histogram_reread_lists():
+    """The units read again after the histograms are those whose largest
+    target value reaches the target's nucleus: draft rows equal to the target
+    rows (zero residual everywhere, so the draw sums p), a nucleus held only
+    by the last, partial tile, a nucleus of most units (more list entries
+    than one batch of the weights pass holds), and a large top-k whose cut
+    lies below the floor of the unfiltered rows."""
+    B, G, V = 4, 2, 65544
+    rng = np.random.default_rng(45)
+    rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
+    zp = (3.0 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
+    zq = (zp[:, :G] + 0.7 * rng.normal(size=(B, G, V))).astype(np.float32)
+    zq[0] = zp[0, :G]
+    zp[1, :, V - 12:] = 40.0 + rng.normal(size=(G + 1, 12))
+    zq[1, :, V - 12:] = 40.0 + rng.normal(size=(G, 12))
+    zp[2] = (0.3 * rng.normal(size=(G + 1, V))).astype(np.float32)
+    zq[2] = (zp[2, :G] + 0.1 * rng.normal(size=(G, V))).astype(np.float32)
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=15, zp=zp, zq=zq,
+                     T=np.array([1.0, 0.8, 1.3, 1.0]), k=np.array([0, 0, 0, 40000]),
+                     tp=np.array([0.9, 0.95, 0.97, 1.0], np.float32))
+    rep = compare(bt, run_gpu(bt), run_oracle(bt), "hist-lists")
+    log(f"[pair-hist] reread lists: ok {rep}")
 
 
 def test_histogram_count_overflow_takes_the_multipass_path():

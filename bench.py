@@ -33,7 +33,7 @@ METRIC = "spec-verify rows/sec + achieved HBM GB/s vs peak at B=256,V=152064,γ=
 # rocprofv3 HBM-counter summaries, by (kernel, workload name).
 PMC_SUMMARIES = {
     ("select_kernel", "B256-V152064-g7-T0.7-topk64"): "select_kernel_B256_V152064_g7_pmc.txt",
-    ("pair_kernel", "B128-V128256-mixed-g1..8-topp0.9"): "pair_kernel_B128_V128256_mixed_topp_pmc.txt",
+    ("pair_hist_kernel", "B128-V128256-mixed-g1..8-topp0.9"): "pair_hist_kernel_B128_V128256_mixed_topp_pmc.txt",
 }
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
 ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
@@ -46,6 +46,7 @@ CPU_REPEAT = 16              # the CPU baseline's sample may pass over a batch t
 KERNEL_SOURCES = {
     "select_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_wave.h"),
     "pair_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h"),
+    "pair_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h"),
 }
 
 
@@ -178,6 +179,17 @@ def kernel_bytes(bt):
     sel = (T == 0) | ((T > 0) & (k > 0) & (k < bt.V) & (k <= 512))
     dense = (T > 0) & ~sel
     return int(rows[sel].sum()), int(rows[dense].sum())
+
+
+def pair_kernel_name(bt) -> str:
+    """The kernel of the pair stage for this batch's rows: bf16 rows longer
+    than the 64 KB held in LDS, of whole 16-byte units and at most 16384 of
+    them, are counted into a histogram (pair_hist_kernel); other dense rows
+    take pair_kernel (the library makes the same choice)."""
+    V = bt.V
+    if bt.p_logits.dtype == np.uint16 and V * 2 > 65536 and V % 8 == 0 and V // 8 <= 16384:
+        return "pair_hist_kernel"
+    return "pair_kernel"
 
 
 def cpu_baseline(bt, seconds_target: float, cores: int):
@@ -528,7 +540,7 @@ def main():
     # The kernel that reads most of the logit bytes: the streaming select for
     # top-k / argmax sequences, the pair kernel for dense ones.
     kernel = binding.SV_KERNEL_PAIR if pair_bytes > sel_bytes else binding.SV_KERNEL_SELECT
-    kname = {binding.SV_KERNEL_SELECT: "select_kernel", binding.SV_KERNEL_PAIR: "pair_kernel"}[kernel]
+    kname = "select_kernel" if kernel == binding.SV_KERNEL_SELECT else pair_kernel_name(bt)
     kbytes = max(sel_bytes, pair_bytes)
 
     for j in range(args.warmup):
@@ -563,7 +575,7 @@ def main():
         check = output_check(bt, ref, ver.tokens.cpu().numpy(), n_acc, alpha, ver.pq.cpu().numpy())
     # Outside the timed region: the other kernels' durations, for the record.
     other_us = {}
-    for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, "pair_kernel"),
+    for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, pair_kernel_name(bt)),
                        (binding.SV_KERNEL_FINISH, "finish_kernel")):
         if (kern == binding.SV_KERNEL_PAIR and hints & binding.SV_HINT_NO_DENSE) or \
                 (kern == binding.SV_KERNEL_SELECT and hints & binding.SV_HINT_ALL_DENSE):

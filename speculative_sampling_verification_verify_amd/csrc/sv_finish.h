@@ -43,6 +43,7 @@ struct FinSmem {
   double pos_q[SV_MAX_GAMMA];
   double pos_alpha[SV_MAX_GAMMA];
   int32_t cand_tok[SV_MAX_GAMMA + 1];           // drawn token if the first rejection is at i (i = g: bonus)
+  int32_t xs[SV_MAX_GAMMA];                     // the drafts, staged once
   union {
     uint32_t h32[256];
     unsigned long long h64[256];
@@ -769,6 +770,8 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   // survivor counts of all slots and the drafts and uniforms of all
   // positions (padding included, masked below), with the parameters.
   const int nslot = RS * a.NP;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   int32_t craw = 0, xraw = 0;
   float uraw = 0.5f;
   if (nslot <= MAXSEG && (int)threadIdx.x < nslot) craw = a.counts[(size_t)b * nslot + threadIdx.x];
@@ -776,12 +779,26 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     xraw = xb[threadIdx.x];
     uraw = ub[threadIdx.x];
   }
+  const float ubon = ub[G];          // the bonus / residual draw's uniform
+  // The first SPEC entries of the first 2 NWAVE (slot, part) lists are
+  // fetched in the same round trip as the counts (wavefront w: lists w and
+  // w + NWAVE, one entry per lane), before the counts say how many are
+  // valid: a top-k list of k <= 64 without ties is no longer, so the pool is
+  // then filled from registers.  Every list has SEG slots, so these reads
+  // stay in its storage.
+  constexpr int SPEC = 64;
+  const bool spec = !a.all_dense && nslot <= MAXSEG;
+  uint2 sp[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int li = wave + h * NWAVE;
+    const uint2* lp = a.lists + ((size_t)b * nslot + li) * SEG;
+    sp[h] = spec && li < nslot ? lp[lane] : make_uint2(0u, 0u);
+  }
   const Mode m = seq_mode(a, b);
   const uint32_t fl = a.seq_flags[b];
   const int R = 2 * m.g + 1;
   const int NS = R * a.NP;          // (row, part) lists of the sequence
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
   bool ok = m.mode != MODE_INVALID && !(fl & F_BAD);
   const int gl = a.gamma_len ? a.gamma_len[b] : G;
   ok = ok && (a.sampler || (gl >= 1 && gl <= G));
@@ -796,41 +813,44 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   uint32_t badin = 0;
   if ((int)threadIdx.x < m.g)
     badin |= (xraw < 0 || xraw >= a.V || !(uraw >= 0.0f && uraw < 1.0f)) ? 1u : 0u;
-  if (threadIdx.x == 0) badin |= !(ub[G] >= 0.0f && ub[G] < 1.0f) ? 1u : 0u;
+  if (threadIdx.x == 0) badin |= !(ubon >= 0.0f && ubon < 1.0f) ? 1u : 0u;
+  if ((int)threadIdx.x < G) s.xs[threadIdx.x] = xraw;
   if (nslot <= MAXSEG && (int)threadIdx.x < nslot) s.cslot[threadIdx.x] = (uint32_t)max(craw, 0);
   __syncthreads();
   // List sizes: (row r, part p) -> soff[r * NP + p + 1]; the block scan
   // runs for every sequence so that control flow stays block-uniform.
-  uint32_t c = 0;
+  // A list not fetched whole with the counts (past the first 2 NWAVE, or
+  // longer than SPEC) needs the second round trip below.
+  uint32_t c = 0, rest = 0;
   if (ok && !dense && (int)threadIdx.x < NS) {
     const int r = threadIdx.x / a.NP, p = threadIdx.x - r * a.NP;
     const int si = used_slot(G, m.g, r) * a.NP + p;
     c = nslot <= MAXSEG ? s.cslot[si] : (uint32_t)max(a.counts[(size_t)b * RS * a.NP + si], 0);
+    rest = !spec || si >= 2 * NWAVE || c > (uint32_t)SPEC;
   }
-  // The list sizes' exclusive scan and the input checks' OR in one LDS round
-  // trip (the barrier after cslot already separates earlier LDS use, and the
-  // one after soff below separates later use).
-  uint32_t total = 0, excl = 0;
+  // The list sizes' exclusive scan and the OR of the input checks and of the
+  // lists' needs in one LDS round trip (the barrier after cslot already
+  // separates earlier LDS use, and the one after soff below separates later
+  // use).
+  uint32_t total = 0, excl = 0, flags = 0;
   {
-    const uint32_t incl = wave_incl_scan(c);
-    uint32_t orw = badin;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) orw |= (uint32_t)__shfl_xor((int)orw, o, 64);
+    const uint32_t incl = wave_incl_scan_dpp(c);
+    const uint32_t orw = (__ballot(badin != 0u) ? 1u : 0u) | (__ballot(rest != 0u) ? 2u : 0u);
     if (lane == 63) {
       s.red_u[wave] = incl;
       s.red_or[wave] = orw;
     }
     __syncthreads();
-    uint32_t base = 0, anybad = 0;
+    uint32_t base = 0;
 #pragma unroll
     for (int i = 0; i < NWAVE; ++i) {
       const uint32_t v = s.red_u[i];
       base += i < wave ? v : 0u;
       total += v;
-      anybad |= s.red_or[i];
+      flags |= s.red_or[i];
     }
     excl = base + incl - c;
-    ok = ok && anybad == 0;
+    ok = ok && (flags & 1u) == 0;
   }
   if (ok && !dense) {
     if ((int)threadIdx.x < NS) s.soff[threadIdx.x] = excl;
@@ -840,8 +860,24 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   __syncthreads();
   if (ok && !dense) {
     for (int r = threadIdx.x; r <= R; r += NT) s.off[r] = s.soff[r * a.NP];
-    // All survivor lists in one round trip.
-    for (uint32_t e = threadIdx.x; e < total; e += NT) {
+    // The entries fetched with the counts go from registers to their pool
+    // slots: slot-list li = slot * NP + part is used row r's part (P rows
+    // r = slot <= g, Q rows r = slot - G + g for G < slot <= G + g).
+    if (spec) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int li = wave + h * NWAVE;
+        const int slot = li / a.NP, p = li - slot * a.NP;
+        const int r = slot <= m.g ? slot : (slot > G && slot <= G + m.g ? slot - G + m.g : -1);
+        if (li < nslot && r >= 0) {
+          const uint32_t o = s.soff[r * a.NP + p], n = s.soff[r * a.NP + p + 1] - o;
+          if ((uint32_t)lane < n) s.pool[o + lane] = sp[h];
+        }
+      }
+    }
+    // The rest (lists past the first 2 NWAVE, entries past the first SPEC)
+    // in one round trip.
+    for (uint32_t e = (flags & 2u) ? threadIdx.x : total; e < total; e += NT) {
       int lo = 0, hi = NS;   // list with soff[lo] <= e < soff[lo+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -849,8 +885,10 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
         else hi = mid;
       }
       const int r = lo / a.NP, p = lo - r * a.NP;
-      const int rowid = b * RS + used_slot(G, m.g, r);
-      s.pool[e] = a.lists[list_index(a, rowid, p) + (e - s.soff[lo])];
+      const int si = used_slot(G, m.g, r) * a.NP + p;
+      const uint32_t j = e - s.soff[lo];
+      if (spec && si < 2 * NWAVE && j < (uint32_t)SPEC) continue;
+      s.pool[e] = a.lists[list_index(a, b * RS + used_slot(G, m.g, r), p) + j];
     }
     __syncthreads();
     // A row without a finite logit: every wavefront checks all rows itself
@@ -868,10 +906,10 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       for (int i = wave; i <= m.g; i += NWAVE) {
         int tk;
         if (m.mode != MODE_GREEDY && s.st_sorted[i] && (i == m.g || s.st_sorted[m.g + 1 + i])) {
-          tk = wave_position_draw_sorted(s, i, i < m.g ? xb[i] : -1, m, ub[G]);
+          tk = wave_position_draw_sorted(s, i, i < m.g ? s.xs[i] : -1, m, ubon);
         } else {
-          if (i < m.g) wave_position(s, i, xb[i], m);
-          tk = pool_draw(s, m, i, ub[G]);
+          if (i < m.g) wave_position(s, i, s.xs[i], m);
+          tk = pool_draw(s, m, i, ubon);
         }
         if (lane == 0) s.cand_tok[i] = tk;
       }
@@ -902,7 +940,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     if (threadIdx.x < 64) {
       const int i = threadIdx.x;
       bool rej = false;
-      if (i < m.g) rej = !((double)ub[i] * (double)lv * s.pos_q[i] < s.pos_p[i]);
+      if (i < m.g) rej = !((double)uraw * (double)lv * s.pos_q[i] < s.pos_p[i]);   // uraw = ub[i]
       const unsigned long long mask = __ballot(rej);
       const int nn = mask ? __ffsll((long long)mask) - 1 : m.g;
       if (i == 0) {
@@ -914,11 +952,15 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     n = (int)s.bc[7];
     tok = (int)s.bc[6];
     __syncthreads();
-    if (dense && !from_pairs) tok = dense_draw<ET, VECTOR>(a, s, b, m, n, ub[G]);
+    if (dense && !from_pairs) tok = dense_draw<ET, VECTOR>(a, s, b, m, n, ubon);
   }
   int32_t* ot = a.out_tokens + (size_t)b * (G + 1);
   float* oa = a.out_alpha + (size_t)b * G;
-  for (int i = threadIdx.x; i <= G; i += NT) ot[i] = ok ? (i < n ? xb[i] : (i == n ? tok : -1)) : -1;
+  // Thread i < G holds draft i in xraw (G < NT).
+  if ((int)threadIdx.x <= G) {
+    const int i = threadIdx.x;
+    ot[i] = ok ? (i < n ? xraw : (i == n ? tok : -1)) : -1;
+  }
   const float qnan = __int_as_float(0x7FC00000);
   for (int i = threadIdx.x; i < G; i += NT) {
     oa[i] = ok ? (i < m.g ? (float)s.pos_alpha[i] : 0.0f) : qnan;

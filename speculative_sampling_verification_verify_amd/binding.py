@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# The in-tree build; SV_LIBRARY names another build of the same source (the
+# host-sanitized one the ABI tests also run against).
+LIB_PATH = os.environ.get("SV_LIBRARY") or os.path.join(_HERE, "libspecverify.so")
 
 SV_BF16, SV_FP32 = 0, 1
 SV_OK, SV_ERR_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_SCRATCH = 0, -1, -2, -3, -4, -5

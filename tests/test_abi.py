@@ -50,6 +50,23 @@ def test_workspace_bytes():
         assert ws(*bad) == 0, bad
 
 
+def test_workspace_bytes_sweep():
+    """The plan of parts per row and the workspace layout over a spread of
+    shapes: every valid shape gets a size that holds at least one survivor
+    list (1024 entries of 8 bytes) per logit row, for the verify (2G+1 rows
+    per sequence) and the shared-noise verify (G+1).  (Small batches get more
+    parts per row, so the size need not grow with B.)"""
+    L = _ensure_built()
+    ws = binding.spec_verify_workspace_bytes
+    gws = L.spec_verify_gumbel_workspace_bytes
+    for dt in (binding.SV_BF16, binding.SV_FP32):
+        for V in (1, 7, 8, 1000, 2048, 32000, 32769, 65544, 131072, 152064, 1 << 20):
+            for G in (1, 2, 7, 8, 31, 64):
+                for B in (0, 1, 2, 7, 64, 256, 1000, 4096):
+                    assert ws(B, G, V, dt) >= max(1, B * (2 * G + 1) * 8192), (B, G, V, dt)
+                    assert gws(B, G, V, dt) >= max(1, B * (G + 1) * 8192), (B, G, V, dt)
+
+
 def test_host_argument_errors():
     L = _ensure_built()
     fake = ctypes.c_void_p(0x100000)   # never dereferenced: every case below fails on the host

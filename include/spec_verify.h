@@ -330,7 +330,10 @@ int spec_verify_gumbel_workspace_init(void* workspace, size_t workspace_bytes, i
  *  out_n        [B] int32: depths whose output was a candidate (0..L); -1 invalid.
  *  out_node_tokens [B][K][L+1] int32: the output at the node of candidate c's
  *               prefix of length j, for each class's lowest-numbered candidate (-1
- *               elsewhere).  Also the call's scratch: no workspace.
+ *               elsewhere); a node whose class is a single candidate is computed
+ *               only if the walk reaches it (-3 otherwise).  Also the call's
+ *               scratch: no workspace (out_n holds each sequence's pending
+ *               single-candidate chain between the call's launches).
  * 1 <= K <= SV_MAX_CANDIDATES, 1 <= L <= SV_MAX_GAMMA.  Rows above 64 KB are read
  * from global memory on each pass and may hold at most 65536 16-byte units.
  * Invalid data (NaN / +inf or no finite logit on a visited node, a candidate

@@ -679,16 +679,26 @@ template <typename ET, bool VECTOR>
 static hipError_t launch_spectr(const Args& a, bool ldsr, size_t lds, hipStream_t st) {
   hipError_t e = device_setup();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((long long)a.B * a.K * (a.L + 1)));
+  // 1. The nodes of classes of two or more candidates (the rho* searches);
+  //    single-candidate nodes are deferred.  2. A walk that stops at the
+  //    first deferred node it reaches and records that candidate's chain.
+  //    3. The recorded chains' nodes, from that depth to L: the only
+  //    single-candidate nodes the round can use.  4. The walk.
+  auto nodes = [&](const Args& an, long long n) {
+    const dim3 grid((unsigned)n);
+    if (ldsr) hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>), grid, dim3(KSEQ_NT), lds, st, an);
+    else hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, false>), grid, dim3(KSEQ_NT), 0, st, an);
+    return hipGetLastError();
+  };
+  Args a1 = a, a2 = a;
+  a1.kphase = 1;
+  a2.kphase = 2;
   if ((e = stage_mark(SV_KERNEL_KSEQ, true, st)) != hipSuccess) return e;
-  if (ldsr) {
-    hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, true>), grid, dim3(KSEQ_NT), lds, st, a);
-  } else {
-    hipLaunchKernelGGL((kseq_node_kernel<ET, KSEQ_NT, VECTOR, false>), grid, dim3(KSEQ_NT), 0, st, a);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = nodes(a1, (long long)a.B * a.K * (a.L + 1))) != hipSuccess) return e;
   if ((e = stage_mark(SV_KERNEL_KSEQ, false, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(spectr_walk_kernel, dim3((unsigned)a.B), dim3(64), 0, st, a1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = nodes(a2, (long long)a.B * (a.L + 1))) != hipSuccess) return e;
   hipLaunchKernelGGL(spectr_walk_kernel, dim3((unsigned)a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }

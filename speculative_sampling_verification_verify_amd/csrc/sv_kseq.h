@@ -18,10 +18,18 @@
 // computes it.  Its rows are P[b][c][j] (target after that prefix) and
 // Q[b][c][j] (draft); depth L is the bonus node, a draw from P[b][c][L] at
 // u[L][0].  Rows of up to 64 KB are held in LDS, longer rows are read from
-// global memory on each pass.  rho* is found by a multi-point bracket
-// search on block reductions of beta(rho) (g(rho) is non-decreasing in rho);
-// once the elements whose ratio p / q lies inside the bracket fit a list in
-// LDS, the search continues on that list alone.
+// global memory on each pass.  rho* comes from one pass that bins the ratios
+// p / q with their masses (g is exact at every bin boundary), then one pass
+// that lists the elements of the bracket bin, then bracket steps on that
+// list alone (g(rho) is non-decreasing in rho); a bracket too full for the
+// list takes further listing passes.
+// A call runs the node kernel twice.  The first launch (kphase 1) computes
+// the nodes of classes of two or more candidates and defers the others: a
+// single-candidate node is needed only if the walk reaches it, and from
+// there on the walk follows that one candidate.  A first walk finds, per
+// sequence, the first deferred node it reaches; the second launch (kphase 2)
+// computes that candidate's nodes from that depth to L, at most L + 1 per
+// sequence instead of every single-candidate node of the tree.
 // spectr_walk_kernel: one wavefront per sequence (candidates and node outputs
 // staged in LDS) follows the output through the nodes: at depth j the node of
 // the current class gives Y; the class shrinks, by a ballot over the
@@ -38,8 +46,10 @@ constexpr int KSEQ_MAXK = 64;
 constexpr int KSEQ_NPT = 8;       // points of the rho* bracket evaluated per pass
 constexpr int KSEQ_PASSES = 24;   // bracket steps (over the rows: (KSEQ_NPT + 1)-fold, on the list: 65-fold)
 constexpr int KSEQ_NG = 1536;     // listed elements of the bracket (LDS)
+constexpr int KSEQ_NB = 768;      // ratio bins of the first pass (share the list's LDS)
 constexpr int KSEQ_UR = 4;        // units per row whose loads a thread issues together on the first pass
 constexpr int32_t KSEQ_BAD = -2;
+constexpr int32_t KSEQ_DEFER = -3;   // a single-candidate node left for the pending-chain launch
 
 // x^n for 0 <= n <= 64 by repeated squaring (a few dependent multiplies
 // instead of a general power's logarithm and exponential).
@@ -152,7 +162,15 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   __shared__ double gred[NTP / 64][KSEQ_NPT];
   __shared__ double rr[KSEQ_NPT], gg[KSEQ_NPT], bb[KSEQ_NPT];
   __shared__ double brk[3];   // lo, hi, beta(hi)
-  __shared__ float glp[KSEQ_NG], glq[KSEQ_NG];   // listed (p, q) of the bracket's elements
+  __shared__ union {
+    struct {
+      float p[KSEQ_NG], q[KSEQ_NG];   // listed (p, q) of the bracket's elements
+    } l;
+    struct {
+      double p[KSEQ_NB], q[KSEQ_NB];  // the first pass's p and q mass per ratio bin
+    } h;
+  } gx;
+  __shared__ int32_t bins_root;       // the first bin boundary with g >= 0 (KSEQ_NB: none below k)
   __shared__ uint32_t gcount;
   __shared__ double gout[2];  // p and q mass of the elements above the listing bracket
   const int K = a.K, L = a.L, L1 = L + 1;
@@ -163,9 +181,23 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   // partitions mix sequences rather than candidate numbers (the lowest
   // candidate of a class is its representative, so a candidate-major deal
   // would pile the work on one partition).
-  const int j = blockIdx.x / (a.B * K);
-  const int rem = blockIdx.x - j * a.B * K;
-  const int c = rem / a.B, b = rem - (rem / a.B) * a.B;
+  int j, c, b;
+  if (a.kphase == 2) {
+    // One workgroup per (depth, sequence): the node of depth j on the chain
+    // of the candidate at whose single-candidate node the first walk stopped
+    // (out_n[b] = c (L + 1) + j0 between the launches), for every j >= j0.
+    j = blockIdx.x / a.B;
+    b = blockIdx.x - j * a.B;
+    const int32_t pend = a.out_n[b];
+    if (pend < 0) return;
+    c = pend / L1;
+    if (j < pend - c * L1) return;
+  } else {
+    j = blockIdx.x / (a.B * K);
+    const int rem = blockIdx.x - j * a.B * K;
+    c = rem / a.B;
+    b = rem - (rem / a.B) * a.B;
+  }
   int32_t* outp = a.node_tok + ((size_t)b * K + c) * L1 + j;
   const int32_t* cb = a.cand + (size_t)b * K * L;
   // The node's class: candidates whose first j tokens equal candidate c's.
@@ -185,6 +217,10 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   const int k = (int)kcount;
   if (k == 0) {   // another member of the class computes this node
     if (threadIdx.x == 0) *outp = -1;
+    return;
+  }
+  if (k == 1 && a.kphase == 1) {   // computed later if the walk reaches it
+    if (threadIdx.x == 0) *outp = KSEQ_DEFER;
     return;
   }
   const float Tv = a.temp[b];
@@ -397,8 +433,8 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
               T::each(up, [&](int e2, uint32_t raw) { rp = e2 == e ? raw : rp; });
               T::each(uq, [&](int e2, uint32_t raw) { rqe = e2 == e ? raw : rqe; });
               const uint32_t idx = (uint32_t)(ui * E + e);
-              glp[slot] = prob_p(idx, rp);
-              glq[slot] = prob_q(idx, rqe);
+              gx.l.p[slot] = prob_p(idx, rp);
+              gx.l.q[slot] = prob_q(idx, rqe);
             }
             ++slot;
           }
@@ -448,7 +484,7 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
     const float rmf = (float)rm;
     const uint32_t n = min(gcount, (uint32_t)KSEQ_NG);
     float acc = 0.0f;
-    for (uint32_t jl = (uint32_t)wave; jl < n; jl += NTP / 64) acc += fmaxf(fmaf(-rmf, glq[jl], glp[jl]), 0.0f);
+    for (uint32_t jl = (uint32_t)wave; jl < n; jl += NTP / 64) acc += fmaxf(fmaf(-rmf, gx.l.q[jl], gx.l.p[jl]), 0.0f);
     s.part[lane][wave] = (double)acc;
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -474,29 +510,100 @@ __global__ __launch_bounds__(NTP) void kseq_node_kernel(Args a) {
   // the bracket (lo: g < 0, hi: g >= 0) into KSEQ_NPT + 1 parts and list the
   // elements whose ratio lies inside it; once the list holds all of them,
   // the remaining steps run on the list alone.
-  double rho = 1.0, beta = 1.0;
-  if (k > 1) {
-    if (threadIdx.x < KSEQ_NPT) rr[threadIdx.x] = 1.0 + ((double)k - 1.0) * threadIdx.x / (KSEQ_NPT - 1);
-    __syncthreads();
-    g_multi(false, 0.0f, 0.0f);
-    beta = bb[0];
-  }
-  if (k > 1 && gg[0] < 0.0) {
-    if (threadIdx.x == 0) {
-      double lo = 1.0, hi = (double)k, bhi = bb[KSEQ_NPT - 1];
-      for (int m2 = 1; m2 < KSEQ_NPT; ++m2) {
-        if (gg[m2] >= 0.0) {
-          hi = rr[m2];
-          bhi = bb[m2];
-          break;
-        }
-        lo = rr[m2];
-      }
-      brk[0] = lo;
-      brk[1] = hi;
-      brk[2] = bhi;
+  // The bracket in one pass: the elements with 1 < r = p / q < k go to
+  // KSEQ_NB bins of log_k r (bin i: r in [rho_i, rho_{i+1}), rho_i =
+  // k^(i / KSEQ_NB)), their p and q summed per bin (double LDS atomics); the
+  // elements with r >= k (q = 0 included) are summed per thread.  Elements
+  // with r <= 1 add nothing to D for rho >= 1.  Then D(rho_i) = sum over the
+  // bins at or above i and the r >= k part of (p - rho_i q), exact at every
+  // boundary up to the rounding of the bin assignment (an element within a
+  // rounding of rho_i adds about 0 either way), and wavefront 0 evaluates g
+  // at all KSEQ_NB boundaries.  The root lies at or below the first boundary
+  // i* with g >= 0; the bracket [rho_{i*-2}, rho_{i*}] keeps one bin below in
+  // case rounding put g(rho_{i*-1}) on the wrong side.  Sets brk and
+  // bins_root (0: g(1) >= 0, so rho* = 1, with beta(1) in brk[2]).
+  auto g_bins = [&]() {
+    for (int i = threadIdx.x; i < KSEQ_NB; i += NTP) {
+      gx.h.p[i] = 0.0;
+      gx.h.q[i] = 0.0;
     }
     __syncthreads();
+    const float fk = (float)k;
+    const float sc = (float)KSEQ_NB / __log2f(fk);
+    float ao = 0.0f, bo = 0.0f;
+    for (int ui = threadIdx.x; ui < NU; ui += NTP) {
+      const U up = P[ui], uq = Q[ui];
+      uint32_t rq[E];
+      T::each(uq, [&](int e, uint32_t raw) { rq[e] = raw; });
+      T::each(up, [&](int e, uint32_t raw) {
+        const uint32_t idx = (uint32_t)(ui * E + e);
+        const float pv = prob_p(idx, raw), qv = prob_q(idx, rq[e]);
+        if (pv > qv) {
+          if (qv * fk <= pv) {
+            ao += pv;
+            bo += qv;
+          } else {
+            const int bi = min(KSEQ_NB - 1, max(0, (int)(__log2f(pv / qv) * sc)));
+            atomicAdd(&gx.h.p[bi], (double)pv);
+            atomicAdd(&gx.h.q[bi], (double)qv);
+          }
+        }
+      });
+    }
+    const double wa = wave_sum_dpp((double)ao), wb = wave_sum_dpp((double)bo);
+    if (lane == 0) {
+      s.part[0][wave] = wa;
+      s.part[1][wave] = wb;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      double A = 0.0, Bq = 0.0;
+      for (int w2 = 0; w2 < NTP / 64; ++w2) {
+        A += s.part[0][w2];
+        Bq += s.part[1][w2];
+      }
+      constexpr int BPL = KSEQ_NB / 64;   // lane l: bins BPL l .. BPL l + BPL - 1
+      double lp = 0.0, lq = 0.0;
+      for (int t = 0; t < BPL; ++t) {
+        lp += gx.h.p[BPL * lane + t];
+        lq += gx.h.q[BPL * lane + t];
+      }
+      const double ip = wave_incl_scan_f64(lp), iq = wave_incl_scan_f64(lq);
+      double SP = A + (readlane_f64(ip, 63) - ip), SQ = Bq + (readlane_f64(iq, 63) - iq);
+      const double lk = log2((double)k);
+      int first = BPL;
+      double bfirst = 0.0;
+      for (int t = BPL - 1; t >= 0; --t) {   // boundaries from the lane's top down, while g >= 0
+        const int i = BPL * lane + t;
+        SP += gx.h.p[i];
+        SQ += gx.h.q[i];
+        const double rho_i = exp2(lk * (double)i / KSEQ_NB);
+        const double D = fmax(SP - rho_i * SQ, 0.0);
+        const double be = (1.0 - D) / rho_i;
+        if (!(ipow(1.0 - be, k) - D >= 0.0)) break;
+        first = t;
+        bfirst = be;
+      }
+      const unsigned long long has = __ballot(first < BPL);
+      const int hl = has ? __ffsll((long long)has) - 1 : 0;
+      const int rf = __builtin_amdgcn_readlane(first, hl);
+      const double rb = readlane_f64(bfirst, hl);
+      if (lane == 0) {
+        const int root = has ? BPL * hl + rf : KSEQ_NB;
+        bins_root = root;
+        brk[0] = exp2(lk * (double)max(root - 2, 0) / KSEQ_NB);
+        brk[1] = root >= KSEQ_NB ? (double)k : exp2(lk * (double)root / KSEQ_NB);
+        brk[2] = has ? rb : (1.0 - fmax(A - (double)k * Bq, 0.0)) / (double)k;   // beta(k) when none below k
+      }
+    }
+    __syncthreads();
+  };
+  double rho = 1.0, beta = 1.0;
+  if (k > 1) {
+    g_bins();
+    beta = brk[2];
+  }
+  if (k > 1 && bins_root > 0) {
     bool listed = false;
     for (int pass = 0; pass < KSEQ_PASSES; ++pass) {
       const double lo = brk[0], hi = brk[1];
@@ -602,9 +709,18 @@ __global__ __launch_bounds__(64) void spectr_walk_kernel(Args a) {
   __syncthreads();
   unsigned long long alive = K >= 64 ? ~0ull : ((1ull << K) - 1ull);
   int n = L;
+  // After the first node launch (kphase 1): stop at the first deferred node
+  // the walk reaches and leave its chain, c (L + 1) + j, in out_n[b] for the
+  // second node launch (-1: none).
+  const bool first = a.kphase == 1;
+  int32_t pend = -1;
   for (int j = 0; j < L && ok; ++j) {
     const int rep = __ffsll((long long)alive) - 1;
     const int y = ns[rep * L1 + j];
+    if (first && y == KSEQ_DEFER) {
+      pend = rep * L1 + j;
+      break;
+    }
     if (y < 0) {
       ok = false;
       break;
@@ -617,10 +733,16 @@ __global__ __launch_bounds__(64) void spectr_walk_kernel(Args a) {
     }
     alive = next;
   }
-  if (ok && n == L) {
-    const int y = ns[(__ffsll((long long)alive) - 1) * L1 + L];
-    if (y < 0) ok = false;
+  if (ok && n == L && pend < 0) {
+    const int rep = __ffsll((long long)alive) - 1;
+    const int y = ns[rep * L1 + L];
+    if (first && y == KSEQ_DEFER) pend = rep * L1 + L;
+    else if (y < 0) ok = false;
     else if (lane == 0) ys[L] = y;
+  }
+  if (first) {
+    if (lane == 0) a.out_n[b] = ok ? pend : -1;
+    return;
   }
   __syncthreads();
   int32_t* ot = a.out_tokens + (size_t)b * L1;

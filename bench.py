@@ -34,6 +34,9 @@ METRIC = "spec-verify rows/sec + achieved HBM GB/s vs peak at B=256,V=152064,γ=
 PMC_SUMMARIES = {
     ("select_kernel", "B256-V152064-g7-T0.7-topk64"): "select_kernel_B256_V152064_g7_pmc.txt",
     ("pair_hist_kernel", "B128-V128256-mixed-g1..8-topp0.9"): "pair_hist_kernel_B128_V128256_mixed_topp_pmc.txt",
+    ("select_kernel", "B64-V128256-g4-topk50"): "select_kernel_B64_V128256_g4_topk50_pmc.txt",
+    ("pair_kernel", "B32-V32000-g5-T0.8"): "pair_kernel_B32_V32000_g5_pmc.txt",
+    ("pair_kernel", "tiny-fp32-V1000-g4"): "pair_kernel_B1000_V1000_g4_fp32_pmc.txt",
 }
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
 ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
@@ -182,6 +185,32 @@ def kernel_bytes(bt):
     return int(rows[sel].sum()), int(rows[dense].sum())
 
 
+def timed_calls(step, kern: int, n: int, every: int = EVENT_EVERY):
+    """n calls step(0..n-1) between two device synchronisations, with HIP
+    events around kernel `kern` (SV_KERNEL_*, on the call's stream) on every
+    `every`-th call.  An event recorded between two kernels of a call delays
+    the second by about 5 us, so sampling keeps the call rate a measure of
+    the calls.  Returns (wall seconds, per-launch ms of the sampled calls)."""
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(0, n, every)]
+    for a, b in evs:     # materialise the underlying hipEvent_t handles
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(n):
+        if j % every == 0:
+            a, b = evs[j // every]
+            binding.spec_verify_set_stage_events(a, b, kern)
+        step(j)
+        if j % every == 0:
+            binding.spec_verify_set_stage_events(None, None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, np.array([a.elapsed_time(b) for a, b in evs])
+
+
 def pair_kernel_name(bt) -> str:
     """The kernel of the pair stage for this batch's rows: bf16 rows longer
     than the 64 KB held in LDS, of whole 16-byte units and at most 16384 of
@@ -292,21 +321,9 @@ def main_gumbel(args):
         step(j)
     torch.cuda.synchronize()
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for a, b in evs:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     kern = binding.SV_KERNEL_SELECT if sel_bytes >= dense_bytes else binding.SV_KERNEL_GUMBEL
     kname = "select_kernel" if kern == binding.SV_KERNEL_SELECT else "gumbel_kernel"
-    for j, (a, b) in enumerate(evs):
-        binding.spec_verify_set_stage_events(a, b, kern)
-        step(j)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    binding.spec_verify_set_stage_events(None, None)
-    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    wall, k_ms = timed_calls(step, kern, K)
     ms_per_step = wall * 1e3 / K
     n_acc = ver.n_accepted.cpu().numpy()
     k_avg = float(k_ms.mean())
@@ -411,24 +428,7 @@ def main_spectr(args):
         step(j)
     torch.cuda.synchronize()
     K = args.steps
-    # The first node launch's HIP events on one call in EVENT_EVERY (see timed()).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(0, K, EVENT_EVERY)]
-    for a, b in evs:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j in range(K):
-        if j % EVENT_EVERY == 0:
-            a, b = evs[j // EVENT_EVERY]
-            binding.spec_verify_set_stage_events(a, b, binding.SV_KERNEL_KSEQ)
-        step(j)
-        if j % EVENT_EVERY == 0:
-            binding.spec_verify_set_stage_events(None, None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    wall, k_ms = timed_calls(step, binding.SV_KERNEL_KSEQ, K)
     ms_per_step = wall * 1e3 / K
     n_out = ver.n.cpu().numpy()
     k_avg = float(k_ms.mean())
@@ -563,31 +563,7 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
 
-    def timed(kern, n, every=1):
-        """n calls, with events around kernel `kern` (same stream) on every
-        `every`-th call; returns (wall seconds, per-launch ms of the calls
-        with events).  An event between two kernels of a call delays the
-        second by about 5 us, so the timed loop samples the kernel on one
-        call in EVENT_EVERY rather than perturbing every call."""
-        sel = list(range(0, n, every))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sel]
-        for a, b in evs:     # materialise the underlying hipEvent_t handles
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for j in range(n):
-            if j % every == 0:
-                a, b = evs[j // every]
-                binding.spec_verify_set_stage_events(a, b, kern)
-            step(j)
-            if j % every == 0:
-                binding.spec_verify_set_stage_events(None, None)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, np.array([a.elapsed_time(b) for a, b in evs])
-
-    wall, k_ms = timed(kernel, K, EVENT_EVERY)
+    wall, k_ms = timed_calls(step, kernel, K)
     ms_per_step = wall * 1e3 / K
     n_acc = ver.n_accepted.cpu().numpy()
     alpha = ver.alpha.cpu().numpy()
@@ -603,7 +579,7 @@ def main():
                 (kern == binding.SV_KERNEL_SELECT and hints & binding.SV_HINT_ALL_DENSE):
             other_us[name] = None      # not launched
         elif kern != kernel:
-            _, ms = timed(kern, min(K, 20))
+            _, ms = timed_calls(step, kern, min(K, 20), every=1)
             other_us[name] = float(ms.mean() * 1e3) if (ms > 0).all() else None
     k_avg = float(k_ms.mean())
     achieved = kbytes / (k_avg * 1e-3) / 1e9

@@ -128,7 +128,7 @@ enum {
                             the per-(sequence, position) kernel for dense sequences is not
                             launched.  A dense sequence in such a call still gets its exact
                             result, from a slower one-workgroup-per-sequence path.            */
-  SV_HINT_ALL_DENSE = 2  /* the caller knows that every sequence is dense (T > 0 and top_k <= 0,
+  SV_HINT_ALL_DENSE = 2, /* the caller knows that every sequence is dense (T > 0 and top_k <= 0,
                             top_k >= V or top_k > 512): the top-k selection kernel, whose only
                             work would be listing the (sequence, position) pairs, is not
                             launched, and the pair kernel takes them in a fixed order.  A
@@ -136,6 +136,15 @@ enum {
                             same slower path.  Ignored where the pair kernel does not apply
                             (rows beyond its size limits).  Combined with SV_HINT_NO_DENSE:
                             SV_ERR_ARG.                                                        */
+  SV_HINT_UNFILTERED = 4 /* the caller knows that no sequence has top-k or top-p (top_k <= 0 or
+                            >= V, top_p >= 1, or NULL): when rows are longer than 64 KB, 16-byte
+                            aligned, and the call has at most 512 (sequence, position) pairs,
+                            each dense pair's rows are split into chunks over several
+                            workgroups (three launches that exchange per-chunk maxima,
+                            normalisers and weight sums through the workspace) instead of one
+                            workgroup per pair: the latency of small batches with large
+                            vocabularies.  A sequence that does have top-k or top-p still gets
+                            its exact result, from the slower one-workgroup-per-sequence path. */
 };
 
 /*
@@ -148,7 +157,8 @@ enum {
  *
  *  lenience     [B] float in [0, 1], or NULL (all 1).  A value outside [0, 1] or NaN
  *               makes that sequence invalid.
- *  hints        0 or SV_HINT_* flags (unknown bits, or both flags: SV_ERR_ARG).
+ *  hints        0 or SV_HINT_* flags (unknown bits, or SV_HINT_NO_DENSE with
+ *               SV_HINT_ALL_DENSE: SV_ERR_ARG).
  * Every other argument, the workspace and the error behaviour are those of
  * spec_verify.
  */
@@ -391,7 +401,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 9. */
+/* ABI version: 10. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

@@ -25,6 +25,7 @@ SV_KERNEL_SELECT, SV_KERNEL_PAIR, SV_KERNEL_FINISH, SV_KERNEL_GUMBEL, SV_KERNEL_
 SV_MAX_CANDIDATES = 64
 SV_HINT_NO_DENSE = 1
 SV_HINT_ALL_DENSE = 2
+SV_HINT_UNFILTERED = 4
 SV_MAX_GAMMA = 64
 SV_MAX_VOCAB = 1 << 20
 

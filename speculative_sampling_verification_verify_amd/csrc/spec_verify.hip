@@ -34,6 +34,7 @@
 #include "sv_wave.h"
 #include "sv_pair.h"
 #include "sv_phist.h"
+#include "sv_split.h"
 #include "sv_finish.h"
 #include "sv_gumbel.h"
 #include "sv_kseq.h"
@@ -144,11 +145,44 @@ static int pair_grid_cap(int variant) {
   }
 }
 
+// Chunks per dense pair for the split kernels (1: no split).  Three launches
+// cost about 30 us however small, so the split is for rows longer than the
+// 64 KB that one workgroup holds in LDS (a pair then takes one CU 60-70 us)
+// and calls of at most SV_SPLIT_MAX_PAIRS pairs (at most two rounds of one
+// workgroup per CU): B = 1..8, gamma 4, V = 128256 went from 72-73 to
+// 32-38 us per call, while B = 32, gamma 5, V = 32000 (rows in LDS) went from
+// 27.4 to 33.9 us.  Enough pairs times chunks to give every CU about four
+// workgroups, at most SPL_MAXS, each chunk at least SPL_MIN_UNITS 16-byte
+// units of a row and at most the SPL_MAXTILE tiles of SPL_NT units that the
+// draw kernel holds in registers.
+#ifndef SV_SPLIT_TARGET_WGS
+#define SV_SPLIT_TARGET_WGS 1024
+#endif
+#ifndef SV_SPLIT_MAX_PAIRS
+#define SV_SPLIT_MAX_PAIRS 512
+#endif
+static int split_chunks(int B, int G, int V, int dtype) {
+  const long long npairs = (long long)B * (G + 1);
+  if (npairs <= 0 || npairs > SV_SPLIT_MAX_PAIRS) return 1;
+  const long long row = (long long)V * (dtype == SV_BF16 ? 2 : 4);
+  if (row <= PAIR_LDS_ROW_MAX) return 1;
+  const long long units = row / 16;
+  long long s = (SV_SPLIT_TARGET_WGS + npairs - 1) / npairs;
+  if (s > SPL_MAXS) s = SPL_MAXS;
+  if (s > units / SPL_MIN_UNITS) s = units / SPL_MIN_UNITS;
+  if (s < 2) return 1;
+  while (s < SPL_MAXS && (units + s - 1) / s > (long long)SPL_MAXTILE * SPL_NT) ++s;
+  if ((units + s - 1) / s > (long long)SPL_MAXTILE * SPL_NT || (units + s - 1) / s < SPL_MIN_UNITS) return 1;
+  return (int)s;
+}
+
 struct Layout {
-  size_t seq_flags_off, dense_count_off, counters_bytes, pos_off, dense_list_off, counts_off, lists_off, total;
+  size_t seq_flags_off, dense_count_off, counters_bytes, pos_off, dense_list_off, counts_off, lists_off, chunks_off,
+      total;
 };
 
-static Layout layout(int B, int G, int RS, const Plan& p) {
+// S: chunks per dense pair (split_chunks), for the verify's layout; 0 elsewhere.
+static Layout layout(int B, int G, int RS, const Plan& p, int S = 0) {
   Layout L;
   const size_t R = (size_t)B * RS;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -159,7 +193,8 @@ static Layout layout(int B, int G, int RS, const Plan& p) {
   L.dense_list_off = up(L.pos_off + (size_t)B * (G + 1) * sizeof(PosRec));
   L.counts_off = up(L.dense_list_off + (size_t)B * (G + 1) * 4);
   L.lists_off = up(L.counts_off + R * p.NP * 4);
-  L.total = L.lists_off + R * p.NP * SEG * sizeof(uint2);
+  L.chunks_off = up(L.lists_off + R * p.NP * SEG * sizeof(uint2));
+  L.total = L.chunks_off + (S > 1 ? (size_t)B * (G + 1) * S * sizeof(ChunkRec) : 0);
   return L;
 }
 
@@ -240,7 +275,18 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     if (e != hipSuccess) return e;
   }
   if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
-  if (a.pair) {
+  if (a.pair && a.split_s > 1) {
+    const long long npairs = (long long)a.B * (a.G + 1);
+    const dim3 g1((unsigned)(npairs * a.split_s));
+    if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((split_stats_kernel<ET, VECTOR>), g1, dim3(SPL_NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((split_weights_kernel<ET, VECTOR>), g1, dim3(SPL_NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((split_draw_kernel<ET, VECTOR>), dim3((unsigned)npairs), dim3(SPL_NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = stage_mark(SV_KERNEL_PAIR, false, st)) != hipSuccess) return e;
+  } else if (a.pair) {
     size_t plds = 0;
     int pv = pair_variant(a.V, sizeof(ET) == 2 ? SV_BF16 : SV_FP32, VECTOR, &plds);
     if (pv != 64 && pv != 256 && pv != 1024 && pv != -1024) return hipErrorInvalidValue;
@@ -276,11 +322,16 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
 
 // Workspace size and preparation for B sequences of G drafts (G == 0: rows
 // to sample).
+// The verify's layout (RS = 2G + 1) holds the split kernels' chunk records.
+static int layout_chunks(int B, int G, int V, int dtype, int RS) {
+  return RS == 2 * G + 1 ? split_chunks(B, G, V, dtype) : 0;
+}
+
 static size_t ws_bytes(int B, int G, int V, int dtype, int RS) {
   if (B < 0 || G < 0 || G > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
   if (dtype != SV_BF16 && dtype != SV_FP32) return 0;
   if (B == 0) return 256;
-  return layout(B, G, RS, plan(B, RS, V, dtype)).total;
+  return layout(B, G, RS, plan(B, RS, V, dtype), layout_chunks(B, G, V, dtype, RS)).total;
 }
 
 static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V, int dtype, int RS, void* stream) {
@@ -288,7 +339,7 @@ static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V,
   if (need == 0) return SV_ERR_ARG;
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE;
   if (B == 0) return SV_OK;
-  const Layout L = layout(B, G, RS, plan(B, RS, V, dtype));
+  const Layout L = layout(B, G, RS, plan(B, RS, V, dtype), layout_chunks(B, G, V, dtype, RS));
   const size_t n = L.counters_bytes / 4;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256), 0,
                      (hipStream_t)stream, (uint32_t*)workspace, n);
@@ -305,7 +356,7 @@ static int ws_init(void* workspace, size_t workspace_bytes, int B, int G, int V,
 static int check_verify_args(const void* p_logits, const void* q_logits, int dtype, const int32_t* draft_tokens,
                              const float* uniforms, const float* temperature, int hints, const int32_t* out_tokens,
                              const int32_t* out_n_accepted, const float* out_alpha, int sampler) {
-  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
+  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE | SV_HINT_UNFILTERED)) return SV_ERR_ARG;
   if ((hints & SV_HINT_NO_DENSE) && (hints & SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
   if (!p_logits || !uniforms || !temperature || !out_tokens) return SV_ERR_ARG;
   if (!sampler && (!q_logits || !draft_tokens || !out_n_accepted || !out_alpha)) return SV_ERR_ARG;
@@ -340,7 +391,7 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
                          (!q_logits || (uintptr_t)q_logits % 16 == 0);
   int vb = 0;
   while ((1LL << vb) < (long long)V + 1) ++vb;
-  const Layout Lw = layout(B, gamma_max, RS, pl);
+  const Layout Lw = layout(B, gamma_max, RS, pl, layout_chunks(B, gamma_max, V, dtype, RS));
   char* ws = (char*)workspace;
   Args a;
   memset(&a, 0, sizeof a);
@@ -382,6 +433,11 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
   if ((hints & SV_HINT_ALL_DENSE) && a.pair && !sampler) a.all_dense = 1;
   // Without the pair kernel the dense sequences go to the finisher whole and
   // nothing is listed.
+  // Few pairs of unfiltered rows (the caller's promise): each pair is split
+  // over several workgroups.
+  const int S = layout_chunks(B, gamma_max, V, dtype, RS);
+  a.split_s = (hints & SV_HINT_UNFILTERED) && a.pair && !sampler && vector_ok && S > 1 ? S : 0;
+  a.chunks = reinterpret_cast<ChunkRec*>(ws + Lw.chunks_off);
   a.sel_blocks = a.pair ? sel_grid : grid;
   a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);
   hipStream_t st = (hipStream_t)stream;
@@ -588,7 +644,7 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   const bool vector_ok = (V % vec == 0) && ((uintptr_t)p_logits % 16 == 0) && ((uintptr_t)noise % 16 == 0);
   int vb = 0;
   while ((1LL << vb) < (long long)V + 1) ++vb;
-  const Layout Lw = layout(B, gamma_max, RS, pl);
+  const Layout Lw = layout(B, gamma_max, RS, pl, layout_chunks(B, gamma_max, V, dtype, RS));
   char* ws = (char*)workspace;
   Args a;
   memset(&a, 0, sizeof a);
@@ -771,7 +827,7 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 9; }
+extern "C" int spec_verify_version(void) { return 10; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;

@@ -26,6 +26,8 @@ struct PosRec {
 };
 constexpr uint32_t REC_REDO = 2u;
 
+struct ChunkRec;   // per-(pair, chunk) record of the split dense-pair kernels (sv_split.h)
+
 struct Args {
   const void* p;
   const void* q;
@@ -55,6 +57,8 @@ struct Args {
   int pair;               // 1 when the pair-resident kernel runs for the dense sequences
   int split;              // 1 when NP > 1 only because the call is small: a top-k sequence whose
                           // part lists might overflow the finisher's pool streams rows whole
+  int split_s;            // chunks per dense pair when the split kernels run (0: pair_kernel)
+  ChunkRec* chunks;       // [B * (G+1)][split_s] per-chunk records of the split kernels
   int all_dense;          // 1: no select launch; the pair kernel takes every (sequence, position) in
                           // order and the finisher runs non-dense sequences by its multi-pass path
   const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test

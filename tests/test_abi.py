@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 9
+    assert binding.spec_verify_version() == 10
 
 
 def test_workspace_bytes():
@@ -183,7 +183,8 @@ def test_sample_and_lenient_host_argument_errors():
     assert ex(q=nul) == binding.SV_ERR_ARG
     assert ex(draft=nul) == binding.SV_ERR_ARG
     assert ex(G=0) == binding.SV_ERR_ARG
-    assert ex(hints=6) == binding.SV_ERR_ARG
+    assert ex(hints=8) == binding.SV_ERR_ARG
+    assert ex(hints=binding.SV_HINT_ALL_DENSE | binding.SV_HINT_UNFILTERED | 16) == binding.SV_ERR_ARG
     assert ex(hints=binding.SV_HINT_NO_DENSE | binding.SV_HINT_ALL_DENSE) == binding.SV_ERR_ARG
 
 

@@ -243,3 +243,68 @@ def test_streamed_rows_beyond_the_histogram_variant():
     bt = dense_batch(V, "bf16", B=3, G=2, seed=14, T=np.array([1.0, 0.7, 1.2]),
                      tp=np.array([1.0, 0.9, 0.8], np.float32))
     compare(bt, run_gpu(bt), run_oracle(bt), "streamed-V140000")
+
+
+# ---- dense pairs of unfiltered rows split over several workgroups -------------
+
+def _split_verifier(bt, hints):
+    from speculative_sampling_verification_verify_amd import binding
+    dt = binding.SV_BF16 if bt.p_logits.dtype == np.uint16 else binding.SV_FP32
+    return binding.Verifier(bt.B, bt.gamma_max, bt.V, dt, device="cuda:0", hints=hints)
+
+
+@pytest.mark.parametrize("dtype,V,B,G", [
+    ("bf16", 128256, 2, 3),     # 8 pairs: 31 chunks of 518 units
+    ("bf16", 152064, 1, 7),     # 8 pairs: 32 chunks of 594 units
+    ("bf16", 65544, 4, 3),      # 16 chunks, a ragged last chunk
+    ("bf16", 40000, 3, 2),      # 9 chunks of 556 units
+    ("fp32", 20000, 8, 3),      # fp32 rows of 80 KB, 9 chunks
+    ("bf16", 32000, 32, 5),     # rows held in LDS: no split, the hint changes nothing
+])
+def test_split_pairs_match_oracle(dtype, V, B, G):
+    """Unfiltered dense rows under the unfiltered hint (with and without the
+    all-dense hint): per-chunk maxima and normalisers, per-chunk weights, and
+    the draw from the crossing chunk, against the oracle; two calls in a row
+    reuse the chunk records."""
+    from speculative_sampling_verification_verify_amd import binding
+    T = np.resize(np.array([1.0, 0.6, 1.3, 0.8, 2.0, 1e-3, 50.0, 0.9], np.float32), B)
+    bt = dense_batch(V, dtype, B=B, G=G, seed=V % 97, T=T)
+    ref = run_oracle(bt)
+    for hints in (binding.SV_HINT_UNFILTERED, binding.SV_HINT_ALL_DENSE | binding.SV_HINT_UNFILTERED):
+        ver = _split_verifier(bt, hints)
+        for call in range(2):
+            log(f"[split] {dtype} V={V} B={B} G={G} hints={hints} call {call}")
+            rep = compare(bt, run_gpu(bt, verifier=ver), ref, f"split-{dtype}-V{V}-h{hints}-c{call}")
+        log(f"[split] ok {rep}")
+
+
+def test_split_pairs_edge_cases():
+    """Under the unfiltered hint: equal draft and target rows (zero residual:
+    the draw falls back to p), -inf entries, a NaN row (invalid), short
+    drafts (padding positions), and sequences that break the promise (top-p,
+    top-k above 512, top-k 20, argmax), which take the finisher's paths."""
+    from speculative_sampling_verification_verify_amd import binding
+    B, G, V = 8, 3, 40000
+    rng = np.random.default_rng(46)
+    rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
+    zp = (3.0 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
+    zq = (zp[:, :G] + 0.7 * rng.normal(size=(B, G, V))).astype(np.float32)
+    zq[0] = zp[0, :G]                          # zero residual
+    zp[1, :, ::5] = -np.inf                    # -inf entries
+    zq[1, :, 2::7] = -np.inf
+    T = np.array([1.0, 0.9, 1.1, 0.8, 1.0, 0.7, 1.2, 0.0], np.float32)
+    k = np.array([0, 0, 0, 0, 600, 20, 0, 0], np.int32)
+    tp = np.array([1.0, 1.0, 1.0, 0.9, 1.0, 1.0, 1.0, 1.0], np.float32)
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=47, T=T, k=k, tp=tp, zp=zp, zq=zq)
+    gl = np.array([3, 3, 1, 3, 2, 3, 3, 3], np.int32)
+    P = bt.p_logits.copy()
+    P[2, 1, 99] = 0x7FC1                       # NaN in a target row of sequence 2 (position 1 is used)
+    bt = synth.Batch(bt.workload, P, bt.q_logits, bt.draft, bt.u, gl, bt.temperature, bt.top_k, bt.top_p,
+                     bt.seed)
+    ref = run_oracle(bt)
+    assert ref.n[2] == -1
+    for hints in (binding.SV_HINT_UNFILTERED, binding.SV_HINT_ALL_DENSE | binding.SV_HINT_UNFILTERED):
+        ver = _split_verifier(bt, hints)
+        for call in range(2):
+            log(f"[split] edge cases hints={hints} call {call}")
+            compare(bt, run_gpu(bt, verifier=ver), ref, f"split-edges-h{hints}-c{call}")

@@ -461,6 +461,51 @@ def main_spectr(args):
     print(json.dumps(out))
 
 
+def main_small_batch(args):
+    """Per-call latency of small batches (B = 1, 4, 8; gamma 4, V = 128256;
+    B = 1, gamma 7, V = 152064) of unfiltered bf16 rows at T = 1, all dense:
+    one workgroup per (sequence, position) pair against the pairs split over
+    several workgroups (SV_HINT_UNFILTERED).  Synthetic logits: target
+    N(0, 3^2), draft = target + N(0, 0.7^2), seeded; random drafts and
+    uniforms.  The two forms' tokens must agree."""
+    import torch
+    from speculative_sampling_verification_verify_amd import binding
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    rows = []
+    for B, G, V in ((1, 4, 128256), (4, 4, 128256), (8, 4, 128256), (1, 7, 152064)):
+        rng = np.random.default_rng(1000 * B + G)
+        zp = (3.0 * rng.normal(size=(B, G + 1, V))).astype(np.float32)
+        zq = (zp[:, :G] + 0.7 * rng.normal(size=(B, G, V))).astype(np.float32)
+        P = torch.from_numpy(synth.f32_to_bf16_bits(zp).view(np.int16)).to(dev).view(torch.bfloat16)
+        Q = torch.from_numpy(synth.f32_to_bf16_bits(zq).view(np.int16)).to(dev).view(torch.bfloat16)
+        call = (t(rng.integers(0, V, size=(B, G)).astype(np.int32)), t(rng.random((B, G + 1)).astype(np.float32)),
+                t(np.ones(B, np.float32)), t(np.zeros(B, np.int32)), t(np.ones(B, np.float32)),
+                t(np.full(B, G, np.int32)))
+        # Rotated copies keep the rows out of the last-level cache between calls.
+        nsets = int(min(32, max(1, -(-ROTATE_BYTES // (zp.nbytes // 2 + zq.nbytes // 2)))))
+        sets = [(P, Q)] + [(P.clone(), Q.clone()) for _ in range(nsets - 1)]
+        out = {"B": B, "gamma": G, "V": V}
+        toks = {}
+        for name, hints in (("one_workgroup_per_pair_us", binding.SV_HINT_ALL_DENSE),
+                            ("split_us", binding.SV_HINT_ALL_DENSE | binding.SV_HINT_UNFILTERED)):
+            ver = binding.Verifier(B, G, V, binding.SV_BF16, device=dev, hints=hints)
+            for j in range(args.warmup):
+                ver(*sets[j % nsets], *call)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for j in range(args.steps):
+                ver(*sets[j % nsets], *call)
+            torch.cuda.synchronize()
+            out[name] = (time.perf_counter() - t0) / args.steps * 1e6
+            ver(P, Q, *call)
+            toks[name] = ver.tokens.cpu().numpy().copy()
+        out["same_tokens"] = bool((toks["split_us"] == toks["one_workgroup_per_pair_us"]).all())
+        rows.append(out)
+    print(json.dumps({"metric": "verify call latency, small batches of unfiltered bf16 rows", "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "rows": rows}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -479,6 +524,8 @@ def main():
                     help="skip the oracle check of the last timed call's outputs")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read ceiling on the call's logit buffers")
+    ap.add_argument("--small-batch", action="store_true",
+                    help="call latency of small batches of long unfiltered rows, with and without the split pairs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the verify step on one GPU; runs on more than one GPU are not supported "
@@ -502,6 +549,9 @@ def main():
         return
     if args.spectr:
         main_spectr(args)
+        return
+    if args.small_batch:
+        main_small_batch(args)
         return
 
     t_gen = time.perf_counter()
@@ -541,6 +591,9 @@ def main():
     # and the select launch (which would only list the pairs) is skipped.
     sel_bytes, pair_bytes = kernel_bytes(bt)
     hints = binding.SV_HINT_NO_DENSE if pair_bytes == 0 else (binding.SV_HINT_ALL_DENSE if sel_bytes == 0 else 0)
+    # No top-k and no top-p anywhere: the unfiltered hint (a host-side fact as well).
+    if pair_bytes > 0 and not ((bt.top_k > 0) & (bt.top_k < bt.V)).any() and not (bt.top_p < 1.0).any():
+        hints |= binding.SV_HINT_UNFILTERED
     ver = binding.Verifier(bt.B, bt.gamma_max, bt.V, dt_code, device=dev, hints=hints)
     # Copies of the logits, rotated step by step, so that a workload smaller
     # than the 256 MB last-level cache is still read from HBM.
@@ -604,7 +657,9 @@ def main():
         "config": {"workload": w.name, "B": bt.B, "V": bt.V, "gamma": bt.gamma_max,
                    "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
                    "logit_bytes_per_call": logit_bytes, "parallelism": "single-gpu",
-                   "hints": {binding.SV_HINT_NO_DENSE: "no-dense", binding.SV_HINT_ALL_DENSE: "all-dense"}.get(hints, "none")},
+                   "hints": "+".join(n for f, n in ((binding.SV_HINT_NO_DENSE, "no-dense"),
+                                                     (binding.SV_HINT_ALL_DENSE, "all-dense"),
+                                                     (binding.SV_HINT_UNFILTERED, "unfiltered")) if hints & f) or "none"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,

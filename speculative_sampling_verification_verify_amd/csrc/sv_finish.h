@@ -52,6 +52,8 @@ struct FinSmem {
   unsigned long long red_u64[NWAVE];
   uint32_t red_u[NWAVE];
   uint32_t red_or[NWAVE];
+  uint32_t fflag[NWAVE];                        // register path: per-wavefront input / list checks
+  uint32_t fempty[NWAVE];                       // register path: position i has a row without survivors
   uint32_t bc[8];
   uint32_t flag;
 };
@@ -382,6 +384,263 @@ __device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float
   best = wave_min_dpp(best);
   if (best != 0xFFFFFFFFu) return (int)best;
   return (int)wave_max_dpp(lastpos) - 1;   // rounding left no crossing
+}
+
+// ===========================================================================
+// Register path: one wavefront per position, survivor lists in registers.
+// ===========================================================================
+
+// Chunks of 64 list entries a position wavefront holds per row: a row of NP
+// parts keeps FAST_CH / NP chunks of each part, so a part list of at most
+// 64 * FAST_CH / NP entries fits.
+constexpr int FAST_CH = 4;
+
+// Position i of a top-k (top-p off) or argmax sequence by one wavefront,
+// from the survivor lists of its target row (h = 0) and draft row (h = 1,
+// used when i < g) in registers, for rows of NP parts.  Chunk c of a row is
+// part c / FC, entries (c % FC) * 64 + lane, FC = FAST_CH / NP; f0[h][p]
+// holds part p's first chunk (loaded by the caller), the others are loaded
+// here when the part's size (cnt, lane h * NP + p) reaches them; lp[h] is
+// row h's part-0 list (parts SEG apart).  The same quantities as the LDS
+// list path: the row's kept set (the k-th largest key of the union of its
+// parts and everything above), p = exp((z - zmax)/T)/S, p_i(x_i),
+// q_i(x_i), the overlap, and the draw at i (residual weights
+// max(0, p_i - q_i), or p_g at the bonus) by an inverse CDF in ascending id.
+// Results go to pos_p / pos_q / pos_alpha / cand_tok[i]; fempty[i] = 1 when
+// a row has no survivor, 2 when a list does not fit the registers or is not
+// in ascending id (the sequence then takes the LDS list path).  i is
+// wavefront-uniform.
+template <typename ET, int NP>
+__device__ __forceinline__ void fast_position(FinSmem& s, const Mode& m, int i, const uint2 (&f0)[2][FAST_CH],
+                                              uint32_t cnt, const uint2* lp0, const uint2* lp1, int x, float ures) {
+  constexpr int FC = FAST_CH / NP;
+  const int lane = threadIdx.x & 63;
+  const bool resid = i < m.g;
+  // Entries per chunk (wave-uniform) and the rows' list totals.
+  int ccnt[2][FAST_CH];
+  uint32_t total[2] = {0u, 0u};
+  bool fits = true;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t pc = (h == 0 || resid) ? (uint32_t)__builtin_amdgcn_readlane((int)cnt, h * NP + p) : 0u;
+      total[h] += pc;
+      fits = fits && pc <= (uint32_t)(64 * FC);
+#pragma unroll
+      for (int sub = 0; sub < FC; ++sub) ccnt[h][p * FC + sub] = (int)min(pc - min(pc, (uint32_t)(sub * 64)), 64u);
+    }
+#pragma unroll
+    for (int c = NP * FC; c < FAST_CH; ++c) ccnt[h][c] = 0;
+  }
+  if (!fits) {
+    if (lane == 0) s.fempty[i] = 2u;
+    return;
+  }
+  // The parts' later chunks, then the order check over every chunk.
+  uint2 e[2][FAST_CH];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint2* lp = h ? lp1 : lp0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      e[h][p * FC] = f0[h][p];
+#pragma unroll
+      for (int sub = 1; sub < FC; ++sub)
+        e[h][p * FC + sub] = ccnt[h][p * FC + sub] > 0 ? lp[(size_t)p * SEG + sub * 64 + lane] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int c = NP * FC; c < FAST_CH; ++c) e[h][c] = make_uint2(0u, 0u);
+  }
+  bool unsorted = false;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int c = 0; c < NP * FC; ++c) {
+      const uint32_t id = e[h][c].y;
+      uint32_t prev = (uint32_t)__shfl_up((int)id, 1, 64);
+      if (c % FC > 0) {
+        const uint32_t last = (uint32_t)__builtin_amdgcn_readlane((int)e[h][c > 0 ? c - 1 : 0].y, 63);
+        prev = lane == 0 ? last : prev;
+      }
+      unsorted |= lane < ccnt[h][c] && (lane > 0 || c % FC > 0) && id <= prev;
+    }
+  }
+  if (__ballot(unsorted) != 0ull) {
+    if (lane == 0) s.fempty[i] = 2u;
+    return;
+  }
+  if (total[0] == 0u || (resid && total[1] == 0u)) {
+    if (lane == 0) s.fempty[i] = 1u;
+    return;
+  }
+  // Kept set: for several parts, every key >= the k-th largest of their union.
+  uint32_t kth[2] = {0u, 0u};
+  if (NP > 1 && m.mode != MODE_GREEDY) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((h == 0 || resid) && total[h] > m.k) {
+        kth[h] = wave_kth<Key<ET>::LEVELS>(
+            [&](auto fn) {
+#pragma unroll
+              for (int c = 0; c < NP * FC; ++c)
+                if (lane < ccnt[h][c]) fn(e[h][c].x);
+            },
+            m.k, s.whist[i]);
+      }
+    }
+  }
+  bool kp[2][FAST_CH];
+  uint32_t km[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int c = 0; c < FAST_CH; ++c) {
+      kp[h][c] = lane < ccnt[h][c] && e[h][c].x >= kth[h];
+      km[h] = max(km[h], kp[h][c] ? e[h][c].x : 0u);
+    }
+  }
+  const uint32_t kmax0 = wave_max_dpp(km[0]), kmax1 = wave_max_dpp(km[1]);
+  if (m.mode == MODE_GREEDY) {
+    // p and q are point masses at the lowest id of each row's largest key.
+    uint32_t best0 = NONE, best1 = NONE;
+#pragma unroll
+    for (int c = 0; c < FAST_CH; ++c) {
+      if (kp[0][c] && e[0][c].x == kmax0) best0 = min(best0, e[0][c].y);
+      if (kp[1][c] && e[1][c].x == kmax1) best1 = min(best1, e[1][c].y);
+    }
+    const uint32_t arg0 = wave_min_dpp(best0), arg1 = wave_min_dpp(best1);
+    if (lane == 0) {
+      if (resid) {
+        s.pos_p[i] = (uint32_t)x == arg0 ? 1.0 : 0.0;
+        s.pos_q[i] = (uint32_t)x == arg1 ? 1.0 : 0.0;
+        s.pos_alpha[i] = arg0 == arg1 ? 1.0 : 0.0;
+      }
+      s.cand_tok[i] = (int)arg0;
+      s.fempty[i] = 0u;
+    }
+    return;
+  }
+  // exp((z - zmax) / T) of every kept entry and the rows' normalisers.
+  const float invT = 1.0f / m.T;
+  float ev[2][FAST_CH];
+  double S0 = 0.0, S1 = 0.0;
+  {
+    const float zmax0 = Key<ET>::value(kmax0), zmax1 = Key<ET>::value(kmax1);
+#pragma unroll
+    for (int c = 0; c < FAST_CH; ++c) {
+      ev[0][c] = 0.0f;
+      ev[1][c] = 0.0f;
+      if (ccnt[0][c] > 0) ev[0][c] = kp[0][c] ? expf((Key<ET>::value(e[0][c].x) - zmax0) * invT) : 0.0f;
+      if (ccnt[1][c] > 0) ev[1][c] = kp[1][c] ? expf((Key<ET>::value(e[1][c].x) - zmax1) * invT) : 0.0f;
+      S0 += (double)ev[0][c];
+      S1 += (double)ev[1][c];
+    }
+  }
+  S0 = wave_sum_dpp(S0);
+  S1 = wave_sum_dpp(S1);
+  const double ip = 1.0 / S0, iq = resid ? 1.0 / S1 : 0.0;
+  // q at each target entry's id: the draft row's entries go to the
+  // wavefront's own LDS range (part p at p * FC * 64, in ascending id), and
+  // each target entry searches its part's range (every chunk's search
+  // advances one step per round, so their LDS reads overlap).
+  float qe[FAST_CH];
+#pragma unroll
+  for (int c = 0; c < FAST_CH; ++c) qe[c] = 0.0f;
+  if (resid) {
+    uint2* qs = s.pool + i * (64 * FAST_CH);
+#pragma unroll
+    for (int c = 0; c < FAST_CH; ++c)
+      if (lane < ccnt[1][c]) qs[c * 64 + lane] = make_uint2(e[1][c].y, __float_as_uint(ev[1][c]));
+    wave_lds_sync();
+    int lo[FAST_CH], hi[FAST_CH], end[FAST_CH];
+    int steps = 0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      int nq = 0;
+#pragma unroll
+      for (int sub = 0; sub < FC; ++sub) nq += ccnt[1][p * FC + sub];
+#pragma unroll
+      for (int sub = 0; sub < FC; ++sub) {
+        const int c = p * FC + sub;
+        lo[c] = p * FC * 64;
+        end[c] = hi[c] = lo[c] + nq;
+        if (ccnt[0][c] > 0) steps = max(steps, 32 - __clz(nq));   // bit length: enough halvings for nq + 1 outcomes
+      }
+    }
+    for (int st = 0; st < steps; ++st) {
+      uint32_t v[NP * FC];
+      int mid[NP * FC];
+#pragma unroll
+      for (int c = 0; c < NP * FC; ++c) {
+        mid[c] = (lo[c] + hi[c]) >> 1;
+        v[c] = qs[min(mid[c], 64 * FAST_CH - 1)].x;
+      }
+#pragma unroll
+      for (int c = 0; c < NP * FC; ++c) {
+        const bool go = lo[c] < hi[c];
+        const bool right = v[c] < e[0][c].y;
+        lo[c] = go && right ? mid[c] + 1 : lo[c];
+        hi[c] = go && !right ? mid[c] : hi[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NP * FC; ++c) {
+      const uint2 q = qs[min(lo[c], 64 * FAST_CH - 1)];
+      if (lo[c] < end[c] && q.x == e[0][c].y) qe[c] = __uint_as_float(q.y);
+    }
+  }
+  double al = 0.0, px = 0.0, qx = 0.0, zl = 0.0, zp = 0.0;
+#pragma unroll
+  for (int c = 0; c < FAST_CH; ++c) {
+    const double p = (double)ev[0][c] * ip;
+    const double q = (double)qe[c] * iq;
+    if (kp[0][c]) {
+      al += fmin(p, q);
+      if (e[0][c].y == (uint32_t)x) px = p;
+      zl += resid ? fmax(p - q, 0.0) : p;
+      zp += p;
+    }
+    if (resid && kp[1][c] && e[1][c].y == (uint32_t)x) qx = (double)ev[1][c] * iq;
+  }
+  double Z = wave_sum_dpp(zl);
+  al = wave_sum_dpp(al);
+  px = wave_sum_dpp(px);
+  qx = wave_sum_dpp(qx);
+  zp = wave_sum_dpp(zp);
+  const bool fallback = !(Z > 0.0);   // zero residual mass: draw from the target itself
+  if (fallback) Z = zp;
+  // Inverse CDF in ascending id: chunk by chunk, a prefix scan and a ballot.
+  const double target = (double)ures * Z;
+  double base = 0.0;
+  int tok = -1, lastw = -1, lastk = -1;
+#pragma unroll
+  for (int c = 0; c < NP * FC; ++c) {
+    if (tok < 0 && ccnt[0][c] > 0) {
+      const double p = (double)ev[0][c] * ip;
+      const double w = !kp[0][c] ? 0.0 : (fallback || !resid) ? p : fmax(p - (double)qe[c] * iq, 0.0);
+      const double cv = base + wave_incl_scan_f64(w);
+      const unsigned long long hit = __ballot(kp[0][c] && cv > target);
+      if (hit) {
+        tok = __builtin_amdgcn_readlane((int)e[0][c].y, __ffsll((long long)hit) - 1);
+      } else {
+        const unsigned long long pw = __ballot(w > 0.0), pk = __ballot(kp[0][c]);
+        if (pw) lastw = __builtin_amdgcn_readlane((int)e[0][c].y, 63 - __clzll((long long)pw));
+        if (pk) lastk = __builtin_amdgcn_readlane((int)e[0][c].y, 63 - __clzll((long long)pk));
+        base = readlane_f64(cv, 63);
+      }
+    }
+  }
+  if (tok < 0) tok = lastw >= 0 ? lastw : lastk;   // rounding left no crossing
+  if (lane == 0) {
+    if (resid) {
+      s.pos_p[i] = px;
+      s.pos_q[i] = qx;
+      s.pos_alpha[i] = al;
+    }
+    s.cand_tok[i] = tok;
+    s.fempty[i] = 0u;
+  }
 }
 
 // ===========================================================================
@@ -749,7 +1008,9 @@ __device__ __forceinline__ bool pair_redo(const Args& a, int b, int g) {
   return __ballot(r) != 0ull;
 }
 
-template <typename ET, bool VECTOR>
+// FAST: the register path is compiled in (not for the all-dense finisher,
+// whose calls have no survivor lists).
+template <typename ET, bool VECTOR, bool FAST = true>
 __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b) {
   bool redo = false;
   {
@@ -770,7 +1031,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   // survivor counts of all slots and the drafts and uniforms of all
   // positions (padding included, masked below), with the parameters.
   const int nslot = RS * a.NP;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wavefront-uniform
   const int lane = threadIdx.x & 63;
   int32_t craw = 0, xraw = 0;
   float uraw = 0.5f;
@@ -787,7 +1048,15 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   // then filled from registers.  Every list has SEG slots, so these reads
   // stay in its storage.
   constexpr int SPEC = 64;
-  const bool spec = !a.all_dense && nslot <= MAXSEG;
+  // When the register path can apply (at most FAST_CH parts per row, G <
+  // NWAVE), the first 64 entries of every list are fetched position-wise
+  // instead: wavefront w holds those of its target row (slot w) and draft
+  // row (slot G+1+w, w < G), part p in chunk p * fc, and lane h * NP + p
+  // the part list's size.  Both the register path and the LDS list path use
+  // them.  Every list has SEG >= 64 * FAST_CH slots, so these reads stay in
+  // its storage.
+  const bool fastc = FAST && !a.all_dense && nslot <= MAXSEG && a.NP <= FAST_CH && G < NWAVE;
+  const bool spec = !a.all_dense && nslot <= MAXSEG && !fastc;
   uint2 sp[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -795,6 +1064,28 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     const uint2* lp = a.lists + ((size_t)b * nslot + li) * SEG;
     sp[h] = spec && li < nslot ? lp[lane] : make_uint2(0u, 0u);
   }
+  // f0[h][p]: the first 64 entries of part p of the position's target (h =
+  // 0) and draft (h = 1) row; the conditions are wavefront-uniform.
+  const uint2* lpw[2];
+  uint2 f0[2][FAST_CH];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool row = fastc && wave <= G && (h == 0 || wave < G);
+    lpw[h] = a.lists + list_index(a, b * RS + (row ? (h ? G + 1 + wave : wave) : 0), 0);
+#pragma unroll
+    for (int p = 0; p < FAST_CH; ++p) f0[h][p] = make_uint2(0u, 0u);
+    if (row) {
+#pragma unroll
+      for (int p = 0; p < FAST_CH; ++p)
+        if (p < a.NP) f0[h][p] = lpw[h][(size_t)p * SEG + lane];
+    }
+  }
+  uint32_t fcnt = 0;
+  if (fastc && wave <= G && lane < 2 * a.NP) {
+    const int h = lane / a.NP, p = lane - h * a.NP;
+    if (h == 0 || wave < G) fcnt = (uint32_t)a.counts[(size_t)b * nslot + (h ? G + 1 + wave : wave) * a.NP + p];
+  }
+  const int xw = fastc && wave < G ? xb[wave] : -1;   // draft of the wavefront's position
   const Mode m = seq_mode(a, b);
   const uint32_t fl = a.seq_flags[b];
   const int R = 2 * m.g + 1;
@@ -814,13 +1105,70 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
   if ((int)threadIdx.x < m.g)
     badin |= (xraw < 0 || xraw >= a.V || !(uraw >= 0.0f && uraw < 1.0f)) ? 1u : 0u;
   if (threadIdx.x == 0) badin |= !(ubon >= 0.0f && ubon < 1.0f) ? 1u : 0u;
+  // The register path: top-k sequences without top-p and argmax sequences,
+  // when their lists fit the registers in ascending id (checked in
+  // fast_position; otherwise the LDS list path below takes the sequence).
+  const bool fastm = fastc && ok && !dense && (m.mode == MODE_GREEDY || (m.mode == MODE_SPARSE && !(m.tp < 1.0f)));
+  if constexpr (FAST) {
+    const uint32_t fw = __ballot(badin != 0u) ? 1u : 0u;
+    if (lane == 0) s.fflag[wave] = fw;
+    if (fastm && wave <= m.g) {
+      const int x = wave < m.g ? xw : -1;
+      switch (a.NP) {
+        case 1: fast_position<ET, 1>(s, m, wave, f0, fcnt, lpw[0], lpw[1], x, ubon); break;
+        case 2: fast_position<ET, 2>(s, m, wave, f0, fcnt, lpw[0], lpw[1], x, ubon); break;
+        case 3: fast_position<ET, 3>(s, m, wave, f0, fcnt, lpw[0], lpw[1], x, ubon); break;
+        default: fast_position<ET, 4>(s, m, wave, f0, fcnt, lpw[0], lpw[1], x, ubon); break;
+      }
+    }
+  }
   if ((int)threadIdx.x < G) s.xs[threadIdx.x] = xraw;
   if (nslot <= MAXSEG && (int)threadIdx.x < nslot) s.cslot[threadIdx.x] = (uint32_t)max(craw, 0);
   __syncthreads();
-  // List sizes: (row r, part p) -> soff[r * NP + p + 1]; the block scan
-  // runs for every sequence so that control flow stays block-uniform.
-  // A list not fetched whole with the counts (past the first 2 NWAVE, or
-  // longer than SPEC) needs the second round trip below.
+  bool fast_done = false;
+  if constexpr (FAST) {
+    if (fastm) {
+      uint32_t fflags = 0, fpos = 0;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) {
+        fflags |= s.fflag[w];
+        fpos |= w <= m.g ? s.fempty[w] : 0u;
+      }
+      fast_done = fflags == 0u && (fpos & 2u) == 0u;   // inputs valid, every list held (block-uniform)
+    }
+  }
+  if (fast_done) {
+    if (wave != 0) return;
+    // Wavefront 0: the acceptance test, the first rejection, the outputs
+    // (thread i < 64 holds draft i and its uniform; G < 64).
+    const uint32_t emp = lane <= m.g ? s.fempty[min(lane, NWAVE - 1)] : 0u;
+    const bool fok = __ballot(emp != 0u) == 0ull;
+    const bool rej = lane < m.g && !((double)uraw * (double)lv * s.pos_q[lane] < s.pos_p[lane]);
+    const unsigned long long mask = __ballot(rej);
+    const int nn = mask ? __ffsll((long long)mask) - 1 : m.g;
+    const int tk = s.cand_tok[nn];
+    if (lane <= G) a.out_tokens[(size_t)b * (G + 1) + lane] = fok ? (lane < nn ? xraw : (lane == nn ? tk : -1)) : -1;
+    if (lane < G) {
+      const float qnan = __int_as_float(0x7FC00000);
+      const bool used = lane < m.g;
+      a.out_alpha[(size_t)b * G + lane] = fok ? (used ? (float)s.pos_alpha[lane] : 0.0f) : qnan;
+      if (a.out_pq) {
+        float* op = a.out_pq + ((size_t)b * G + lane) * 2;
+        op[0] = fok ? (used ? (float)s.pos_p[lane] : 0.0f) : qnan;
+        op[1] = fok ? (used ? (float)s.pos_q[lane] : 0.0f) : qnan;
+      }
+    }
+    if (lane == 0) {
+      if (a.out_n) a.out_n[b] = fok ? nn : -1;
+      a.seq_flags[b] = 0;
+      if (b == 0) {   // the pair kernel has finished with the list
+        a.dense_count[0] = 0;
+        a.dense_count[1] = 0;
+        a.dense_count[2] = 0;
+      }
+    }
+    return;
+  }
   uint32_t c = 0, rest = 0;
   if (ok && !dense && (int)threadIdx.x < NS) {
     const int r = threadIdx.x / a.NP, p = threadIdx.x - r * a.NP;
@@ -1018,7 +1366,7 @@ __global__ __launch_bounds__(NT) void finish_dense_kernel(Args a) {
   while (mask) {     // workgroup-uniform
     const int w = __builtin_ctz(mask);
     mask &= mask - 1u;
-    finish_sequence<ET, VECTOR>(a, s, b0 + w);
+    finish_sequence<ET, VECTOR, false>(a, s, b0 + w);
     if (mask) __syncthreads();
   }
 }

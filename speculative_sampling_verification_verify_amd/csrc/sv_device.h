@@ -266,7 +266,7 @@ __device__ __forceinline__ uint32_t block_kth_largest(Feed feed, uint32_t k, uin
       const int top = 255 - 4 * lane;
       uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
       uint32_t s = c0 + c1 + c2 + c3;
-      uint32_t incl = wave_incl_scan(s);
+      uint32_t incl = wave_incl_scan_dpp(s);
       uint32_t excl = incl - s;
       bool hit = excl < krem && incl >= krem;
       unsigned long long any = __ballot(hit);
@@ -324,7 +324,7 @@ __device__ __forceinline__ uint32_t wave_kth(Feed feed, uint32_t k, uint32_t* hi
     const int top = 255 - 4 * lane;
     const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
     const uint32_t sum = c0 + c1 + c2 + c3;
-    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t incl = wave_incl_scan_dpp(sum);
     const uint32_t excl = incl - sum;
     const bool hit = excl < krem && incl >= krem;
     const unsigned long long any = __ballot(hit);

@@ -395,6 +395,82 @@ __device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float
 // 64 * FAST_CH / NP entries fits.
 constexpr int FAST_CH = 4;
 
+// The k-th largest keys of two key sets by one wavefront, one radix level
+// of both per round so that the two selects' LDS round trips overlap (as
+// wave_kth, each on its own 256-word histogram).  feed(h, fn) calls fn(key)
+// for every key of set h this lane holds; set h is skipped (result 0) when
+// !on[h]; a set with fewer than k keys gives 0.
+template <int LEVELS, class Feed>
+__device__ __forceinline__ void wave_kth_pair(Feed feed, uint32_t k, uint32_t* hist0, uint32_t* hist1, const bool (&on)[2],
+                                              uint32_t (&out)[2]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix[2] = {0u, 0u}, pmask = 0u, krem[2] = {k, k};
+  bool live[2] = {on[0], on[1]};
+  for (int lvl = 0; lvl < LEVELS; ++lvl) {
+    const int shift = 8 * (LEVELS - 1 - lvl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hist0[lane + 64 * i] = 0u;
+      hist1[lane + 64 * i] = 0u;
+    }
+    wave_sync_lds();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (live[h]) {
+        uint32_t* hist = h ? hist1 : hist0;
+        const uint32_t pf = prefix[h];
+        feed(h, [&](uint32_t key) {
+          if (key != 0 && (key & pmask) == pf) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        });
+      }
+    }
+    wave_sync_lds();
+    const int top = 255 - 4 * lane;
+    uint32_t c[2][4], incl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t* hist = h ? hist1 : hist0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[h][j] = hist[top - j];
+      incl[h] = wave_incl_scan_dpp(c[h][0] + c[h][1] + c[h][2] + c[h][3]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sum = c[h][0] + c[h][1] + c[h][2] + c[h][3];
+      const uint32_t excl = incl[h] - sum;
+      const bool hit = excl < krem[h] && incl[h] >= krem[h];
+      const unsigned long long any = __ballot(hit);
+      uint32_t d = 0, r = 0;
+      if (hit) {
+        r = krem[h] - excl;
+        if (c[h][0] >= r) {
+          d = top;
+        } else if (c[h][0] + c[h][1] >= r) {
+          d = top - 1; r -= c[h][0];
+        } else if (c[h][0] + c[h][1] + c[h][2] >= r) {
+          d = top - 2; r -= c[h][0] + c[h][1];
+        } else {
+          d = top - 3; r -= c[h][0] + c[h][1] + c[h][2];
+        }
+      }
+      if (any == 0ull) {
+        live[h] = false;
+        prefix[h] = 0u;
+      } else {
+        const int src = __ffsll((long long)any) - 1;
+        d = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
+        r = (uint32_t)__builtin_amdgcn_readlane((int)r, src);
+        prefix[h] |= live[h] ? d << shift : 0u;
+        krem[h] = r;
+      }
+    }
+    pmask |= 255u << shift;
+    wave_sync_lds();
+  }
+  out[0] = on[0] && live[0] ? prefix[0] : 0u;
+  out[1] = on[1] && live[1] ? prefix[1] : 0u;
+}
+
 // Position i of a top-k (top-p off) or argmax sequence by one wavefront,
 // from the survivor lists of its target row (h = 0) and draft row (h = 1,
 // used when i < g) in registers, for rows of NP parts.  Chunk c of a row is
@@ -477,17 +553,17 @@ __device__ __forceinline__ void fast_position(FinSmem& s, const Mode& m, int i, 
   // Kept set: for several parts, every key >= the k-th largest of their union.
   uint32_t kth[2] = {0u, 0u};
   if (NP > 1 && m.mode != MODE_GREEDY) {
+    const bool on[2] = {total[0] > m.k, resid && total[1] > m.k};
+    if (on[0] || on[1]) {
+      // The draft row's histogram in the wavefront's pool range (free until
+      // the q lookup below).
+      wave_kth_pair<Key<ET>::LEVELS>(
+          [&](int h, auto fn) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if ((h == 0 || resid) && total[h] > m.k) {
-        kth[h] = wave_kth<Key<ET>::LEVELS>(
-            [&](auto fn) {
-#pragma unroll
-              for (int c = 0; c < NP * FC; ++c)
-                if (lane < ccnt[h][c]) fn(e[h][c].x);
-            },
-            m.k, s.whist[i]);
-      }
+            for (int c = 0; c < NP * FC; ++c)
+              if (lane < ccnt[h][c]) fn(e[h][c].x);
+          },
+          m.k, s.whist[i], reinterpret_cast<uint32_t*>(s.pool + i * (64 * FAST_CH)), on, kth);
     }
   }
   bool kp[2][FAST_CH];

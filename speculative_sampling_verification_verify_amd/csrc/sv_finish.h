@@ -394,6 +394,7 @@ __device__ __forceinline__ int pool_draw(FinSmem& s, const Mode& m, int n, float
 // parts keeps FAST_CH / NP chunks of each part, so a part list of at most
 // 64 * FAST_CH / NP entries fits.
 constexpr int FAST_CH = 4;
+static_assert(64 * FAST_CH <= SEG, "a row part's register chunks stay inside its list segment");
 
 // The k-th largest keys of two key sets by one wavefront, one radix level
 // of both per round so that the two selects' LDS round trips overlap (as

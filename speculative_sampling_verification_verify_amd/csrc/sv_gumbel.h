@@ -154,26 +154,140 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
     *outp = (bad || kmax <= Key<ET>::NEG_INF || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
 }
 
+// Chunks of 64 list entries the list kernel's register path holds per row
+// (a row of NP <= GUMBEL_CH parts keeps GUMBEL_CH / NP chunks of each part).
+constexpr int GUMBEL_CH = 8;
+static_assert(64 * GUMBEL_CH <= SEG, "a row part's register chunks stay inside its list segment");
+
+// Register path of the list kernel: row r of a top-k (top-p off) or argmax
+// sequence by one wavefront, from its survivor lists in registers (rows of
+// NP parts; chunk c is part c / FC, entries (c % FC) * 64 + lane, FC =
+// GUMBEL_CH / NP; f0[p] holds part p's first chunk, loaded by the caller, the
+// others are loaded here when the part's size (cnt, lane p) reaches them; lp
+// is the row's part-0 list).  The kept set is the k-th largest key of the
+// union of the parts and everything above (all listed keys for one part),
+// and the result is the lowest-id argmax of fl(z + fl(T * g)) over it, as on
+// the LDS path.  Sets *fits = false (and returns nothing) when a part list
+// does not fit the registers.
+template <typename ET, int NP>
+__device__ __forceinline__ int32_t gumbel_row_fast(const Args& a, FinSmem& s, const Mode& m, int b, int r,
+                                                   const uint2 (&f0)[GUMBEL_CH], uint32_t cnt, const uint2* lp,
+                                                   bool* fits) {
+  constexpr int CH = GUMBEL_CH;
+  constexpr int FC = CH / NP;
+  const int lane = threadIdx.x & 63;
+  int ccnt[CH];
+  uint32_t total = 0;
+  bool ok = true;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint32_t pc = (uint32_t)__builtin_amdgcn_readlane((int)cnt, p);
+    total += pc;
+    ok = ok && pc <= (uint32_t)(64 * FC);
+#pragma unroll
+    for (int sub = 0; sub < FC; ++sub) ccnt[p * FC + sub] = (int)min(pc - min(pc, (uint32_t)(sub * 64)), 64u);
+  }
+#pragma unroll
+  for (int c = NP * FC; c < CH; ++c) ccnt[c] = 0;
+  *fits = ok;
+  if (!ok) return GUMBEL_BAD_ROW;
+  if (total == 0u) return GUMBEL_BAD_ROW;   // no finite logit
+  uint2 e[CH];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    e[p * FC] = f0[p];
+#pragma unroll
+    for (int sub = 1; sub < FC; ++sub)
+      e[p * FC + sub] = ccnt[p * FC + sub] > 0 ? lp[(size_t)p * SEG + sub * 64 + lane] : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int c = NP * FC; c < CH; ++c) e[c] = make_uint2(0u, 0u);
+  if (m.mode == MODE_GREEDY) {
+    uint32_t km = 0u;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) km = max(km, lane < ccnt[c] ? e[c].x : 0u);
+    const uint32_t kmax = wave_max_dpp(km);
+    uint32_t best = NONE;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (lane < ccnt[c] && e[c].x == kmax) best = min(best, e[c].y);
+    return (int32_t)wave_min_dpp(best);
+  }
+  uint32_t kth = 0u;
+  if (NP > 1 && total > m.k) {
+    kth = wave_kth<Key<ET>::LEVELS>(
+        [&](auto fn) {
+#pragma unroll
+          for (int c = 0; c < NP * FC; ++c)
+            if (lane < ccnt[c]) fn(e[c].x);
+        },
+        m.k, s.whist[threadIdx.x >> 6]);
+  }
+  // The noise at the kept ids, then the lowest-id argmax of the score.
+  const float* gn = a.noise + ((size_t)b * (a.G + 1) + r) * (size_t)a.V;
+  float nz[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) nz[c] = lane < ccnt[c] && e[c].x >= kth ? gn[e[c].y] : 0.0f;
+  uint32_t bkey = 0u, bid = NONE, bad = 0u;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+#pragma clang fp contract(off)
+    if (lane < ccnt[c] && e[c].x >= kth) {
+      bad |= fabsf(nz[c]) < INFINITY ? 0u : 1u;
+      const float tg = m.T * nz[c];
+      const float sc = Key<ET>::value(e[c].x) + tg;
+      const uint32_t sk = score_key(sc);
+      if (sc == sc && (sk > bkey || (sk == bkey && e[c].y < bid))) {
+        bkey = sk;
+        bid = e[c].y;
+      }
+    }
+  }
+  const uint32_t best = wave_max_dpp(bkey);
+  const uint32_t id = wave_min_dpp(bkey == best && best != 0u ? bid : NONE);
+  return (__ballot(bad != 0u) != 0ull || id == NONE) ? GUMBEL_BAD_ROW : (int32_t)id;
+}
+
 // Argmax and top-k (<= KMAX_SPARSE) sequences from the streaming select's
 // survivor lists: one workgroup per sequence.  Every row's kept set (the
 // union of its part lists cut to the k-th largest, then to the nucleus when
 // top_p < 1) is built in LDS as by the verify's finisher; one wavefront per
 // row then takes the lowest-id argmax of fl(z + fl(T * g)) over it, reading
 // the noise only at the kept ids.  Sequences whose lists do not fit are
-// marked demoted and left to gumbel_kernel, which runs next.
+// marked demoted and left to gumbel_kernel, which runs next.  Top-k
+// sequences without top-p and argmax sequences whose part lists fit in
+// registers take the register path first: wavefront r takes row r
+// (gumbel_row_fast), with no block barrier unless some row does not fit,
+// which sends the whole sequence to the LDS path.
 template <typename ET>
 __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char gl_smem[];
   FinSmem& s = *reinterpret_cast<FinSmem*>(gl_smem);
   const int b = blockIdx.x;
+  const int G = a.G, RS = a.RS, V = a.V;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wavefront-uniform
+  const int lane = threadIdx.x & 63;
+  // The register path's lists, fetched with the parameters: wavefront w <= G
+  // takes row w's first 64 entries of each part (parts <= GUMBEL_CH), and
+  // lane p the part's list size.  Every list has SEG >= 64 * GUMBEL_CH slots.
+  const bool fastc = a.NP <= GUMBEL_CH && G < NWAVE && wave <= G;
+  uint2 f0[GUMBEL_CH];
+  uint32_t fcnt = 0;
+  const uint2* lpw = a.lists + list_index(a, b * RS + (fastc ? wave : 0), 0);
+#pragma unroll
+  for (int p = 0; p < GUMBEL_CH; ++p) f0[p] = make_uint2(0u, 0u);
+  if (fastc) {
+#pragma unroll
+    for (int p = 0; p < GUMBEL_CH; ++p)
+      if (p < a.NP) f0[p] = lpw[(size_t)p * SEG + lane];
+    if (lane < a.NP) fcnt = (uint32_t)a.counts[((size_t)b * RS + wave) * a.NP + lane];
+  }
   const Mode m = seq_mode(a, b);
   if (m.mode != MODE_GREEDY && m.mode != MODE_SPARSE) return;
   const uint32_t fl = a.seq_flags[b];
   if (fl & F_DEMOTE) return;
-  const int G = a.G, RS = a.RS, V = a.V;
   const int R = m.g + 1;
   const int NS = R * a.NP;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int32_t* tgt = a.out_target + (size_t)b * (G + 1);
   if (fl & F_BAD) {
     for (int j = threadIdx.x; j < R; j += NT) tgt[j] = GUMBEL_BAD_ROW;
@@ -182,6 +296,30 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   if (NS > MAXSEG) {
     if (threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
     return;
+  }
+  if (a.NP <= GUMBEL_CH && G < NWAVE && (m.mode == MODE_GREEDY || !(m.tp < 1.0f))) {   // block-uniform
+    bool fits = true;
+    if (wave < R) {
+      int32_t tok;
+      switch (a.NP) {
+        case 1: tok = gumbel_row_fast<ET, 1>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        case 2: tok = gumbel_row_fast<ET, 2>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        case 3: tok = gumbel_row_fast<ET, 3>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        case 4: tok = gumbel_row_fast<ET, 4>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        case 5: tok = gumbel_row_fast<ET, 5>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        case 6: tok = gumbel_row_fast<ET, 6>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        case 7: tok = gumbel_row_fast<ET, 7>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+        default: tok = gumbel_row_fast<ET, 8>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
+      }
+      if (fits && lane == 0) tgt[wave] = tok;
+    }
+    if (lane == 0) s.fflag[wave] = fits ? 0u : 1u;
+    __syncthreads();
+    uint32_t any = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) any |= s.fflag[w];
+    if (any == 0u) return;   // block-uniform
+    __syncthreads();         // the LDS path below reuses the memory
   }
   uint32_t c = 0;
   if ((int)threadIdx.x < NS) c = (uint32_t)max(a.counts[(size_t)b * RS * a.NP + threadIdx.x], 0);

@@ -304,9 +304,10 @@ def main_gumbel(args):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     N = t(gb.noise)
     draft, temp, topk, topp, gl = t(gb.draft), t(gb.temperature), t(gb.top_k), t(gb.top_p), t(gb.gamma_len)
-    # With no argmax or small-top-k sequence the call says so (host-side
-    # facts) and the select and list launches are skipped.
-    ghints = binding.SV_HINT_ALL_DENSE if sel_bytes == 0 else 0
+    # The call says what it knows of its sequences (host-side facts): with no
+    # argmax or small-top-k sequence the select and list launches are skipped;
+    # with only such sequences the list kernel finishes the call.
+    ghints = binding.SV_HINT_ALL_DENSE if sel_bytes == 0 else (binding.SV_HINT_NO_DENSE if dense_bytes == 0 else 0)
     ver = binding.GumbelVerifier(gb.B, gb.gamma_max, gb.V,
                                  binding.SV_BF16 if dtype_name == "bf16" else binding.SV_FP32, device=dev, hints=ghints)
     nsets = int(min(32, max(1, -(-ROTATE_BYTES // max(kbytes, 1)))))
@@ -344,7 +345,8 @@ def main_gumbel(args):
         "data": "synthetic",
         "config": {"workload": w.name, "B": gb.B, "V": gb.V, "gamma": gb.gamma_max,
                    "temperature": float(w.temperature), "top_k": int(w.top_k), "top_p": float(w.top_p),
-                   "parallelism": "single-gpu", "hints": "all-dense" if ghints else "none"},
+                   "parallelism": "single-gpu", "hints": {binding.SV_HINT_ALL_DENSE: "all-dense",
+                                                             binding.SV_HINT_NO_DENSE: "no-dense"}.get(ghints, "none")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profile(kname, w.name),
                      "kernel": kname, "kernel_bytes_per_launch": kbytes, "kernel_avg_us": k_avg * 1e3,

@@ -289,12 +289,18 @@ int spec_verify_gumbel(const void* p_logits, int dtype, const float* noise, cons
 /*
  * spec_verify_gumbel with call hints (same section of the same page).
  *
- *  hints        0 or SV_HINT_ALL_DENSE: the caller knows that every sequence has T > 0
- *               and no top-k of at most 512.  The select and list launches, whose
- *               only work is on argmax and small-top-k sequences, are skipped, and the
+ *  hints        0, SV_HINT_ALL_DENSE or SV_HINT_NO_DENSE.
+ *               SV_HINT_ALL_DENSE: the caller knows that every sequence has T > 0 and
+ *               no top-k of at most 512.  The select and list launches, whose only
+ *               work is on argmax and small-top-k sequences, are skipped, and the
  *               per-(sequence, position) kernel takes every sequence: one that breaks
- *               the promise still gets its exact result there.  Any other bit
- *               (SV_HINT_NO_DENSE included): SV_ERR_ARG.
+ *               the promise still gets its exact result there.
+ *               SV_HINT_NO_DENSE: the caller knows that every sequence has T == 0 or
+ *               0 < top_k <= 512.  The call is two launches: the list kernel also
+ *               finishes every sequence, and takes a sequence that breaks the promise
+ *               (or whose lists overflowed) row by row with one workgroup, with the
+ *               same exact result.
+ *               Both bits, or any other bit: SV_ERR_ARG.
  * Every other argument, the workspace and the error behaviour are those of
  * spec_verify_gumbel.
  */
@@ -401,7 +407,7 @@ double spec_verify_acceptance_length(const double* alpha, int gamma);
 /* Static description of a return code (for SV_ERR_HIP, the last HIP error of this thread). */
 const char* spec_verify_strerror(int code);
 
-/* ABI version: 10. */
+/* ABI version: 11. */
 int spec_verify_version(void);
 
 #ifdef __cplusplus

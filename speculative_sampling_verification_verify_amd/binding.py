@@ -288,7 +288,8 @@ def spec_verify_gumbel(p_logits: torch.Tensor, noise: torch.Tensor, draft_tokens
                        top_p: Optional[torch.Tensor], out_tokens: torch.Tensor, out_n_accepted: torch.Tensor,
                        out_target: torch.Tensor, workspace: torch.Tensor, stream=None, hints: int = 0) -> None:
     """Enqueue one shared-noise verify call (see include/spec_verify.h); with
-    `hints` (SV_HINT_ALL_DENSE) the call goes through spec_verify_gumbel_ex."""
+    `hints` (SV_HINT_ALL_DENSE or SV_HINT_NO_DENSE) the call goes through
+    spec_verify_gumbel_ex."""
     if p_logits.dim() != 3:
         raise ValueError("p_logits must be [B, gamma_max+1, V]")
     B, G1, V = p_logits.shape

@@ -254,12 +254,16 @@ static hipError_t device_setup() {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pair_hist_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)sizeof(PhSmem));
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_list_kernel<float>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinSmem));
-  if (e != hipSuccess) return e;
+  {
+    const void* gk[4] = {reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t, true>),
+                         reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t, false>),
+                         reinterpret_cast<const void*>(&gumbel_list_kernel<float, true>),
+                         reinterpret_cast<const void*>(&gumbel_list_kernel<float, false>)};
+    for (const void* f : gk) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)gumbel_list_smem_bytes());
+      if (e != hipSuccess) return e;
+    }
+  }
   g_setup_done[dev] = true;
   return hipSuccess;
 }
@@ -603,10 +607,13 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
-  // 2. Their per-position argmax from the survivor lists.
+  // 2. Their per-position argmax from the survivor lists (with a.gfuse,
+  //    every sequence's rows and its outputs: the call ends here).
   if (!a.all_dense) {
-    hipLaunchKernelGGL((gumbel_list_kernel<ET>), dim3((unsigned)a.B), dim3(NT), sizeof(FinSmem), st, a);
+    hipLaunchKernelGGL((gumbel_list_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), gumbel_list_smem_bytes(), st,
+                       a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.gfuse) return hipSuccess;
   }
   // 3. Dense and demoted sequences, one workgroup per (sequence, position).
   if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
@@ -627,7 +634,8 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
                       const int32_t* gamma_len, const float* temperature, const int32_t* top_k, const float* top_p,
                       int B, int gamma_max, int V, int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_target,
                       void* workspace, size_t workspace_bytes, void* stream, int sampler, int hints) {
-  if (hints & ~SV_HINT_ALL_DENSE) return SV_ERR_ARG;
+  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
+  if ((hints & SV_HINT_NO_DENSE) && (hints & SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
   if (!p_logits || !noise || !temperature || !out_tokens || !out_target) return SV_ERR_ARG;
   if (!sampler && (!draft_tokens || !out_n_accepted)) return SV_ERR_ARG;
   const size_t es = dtype == SV_BF16 ? 2 : 4;
@@ -674,6 +682,9 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   // The promise that every sequence is dense saves the select and list
   // launches; the per-(sequence, position) kernel then takes every sequence.
   a.all_dense = (hints & SV_HINT_ALL_DENSE) && !sampler ? 1 : 0;
+  // The promise that no sequence is dense lets the list kernel finish the
+  // call: it takes the rare dense, invalid or demoted sequence itself.
+  a.gfuse = (hints & SV_HINT_NO_DENSE) && !sampler ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dtype == SV_BF16)
@@ -709,7 +720,8 @@ extern "C" int spec_verify_gumbel_ex(const void* p_logits, int dtype, const floa
                                      const float* top_p, int hints, int B, int gamma_max, int V, int32_t* out_tokens,
                                      int32_t* out_n_accepted, int32_t* out_target, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  if (hints & ~SV_HINT_ALL_DENSE) return SV_ERR_ARG;
+  if (hints & ~(SV_HINT_NO_DENSE | SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
+  if ((hints & SV_HINT_NO_DENSE) && (hints & SV_HINT_ALL_DENSE)) return SV_ERR_ARG;
   if (dtype != SV_BF16 && dtype != SV_FP32) return SV_ERR_UNSUPPORTED;
   if (gamma_max > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (!sizes_ok(B, gamma_max, V)) return SV_ERR_ARG;
@@ -827,7 +839,7 @@ extern "C" const char* spec_verify_strerror(int code) {
   }
 }
 
-extern "C" int spec_verify_version(void) { return 10; }
+extern "C" int spec_verify_version(void) { return 11; }
 
 extern "C" int spec_verify_set_stage_events(int kernel, void* begin, void* end) {
   if (kernel < SV_KERNEL_SELECT || kernel > SV_KERNEL_KSEQ) return SV_ERR_ARG;

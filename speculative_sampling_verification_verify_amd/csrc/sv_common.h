@@ -64,6 +64,8 @@ struct Args {
   const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test
   int sampler;            // 1: G == 0 and each "sequence" is one row to sample (no drafts)
   int K, L;               // multi-candidate verify: candidate sequences and their length
+  int gfuse;              // shared-noise verify: the list kernel takes every sequence and finishes it
+                          // (no per-(sequence, position) or finish launch follows)
   int kphase;             // multi-candidate verify: 0 every node; 1 nodes of classes of two or more
                           // (single-candidate nodes deferred); 2 the pending chains' nodes
   const int32_t* cand;    // multi-candidate verify: [B][K][L] candidate tokens

@@ -35,34 +35,24 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Position j of sequence b by the whole workgroup (NTP threads): the
+// target's sample, the lowest-id argmax of the score over the processed
+// support, or GUMBEL_BAD_ROW (invalid parameters, NaN / +inf among the
+// logits or the support's noise, no finite logit).  The result is
+// workgroup-uniform.
 template <typename ET, int NTP, bool VECTOR>
-__global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
+__device__ __forceinline__ int32_t gumbel_row_block(const Args& a, PairSmem<NTP>& s, PairStream& ps, int b, int j) {
   using T = PT<ET, VECTOR>;
   using U = typename T::U;
   constexpr int E = T::E;
   constexpr int LEVELS = Key<ET>::LEVELS;
-  __shared__ PairSmem<NTP> s;
-  __shared__ PairStream ps;
   const int G1 = a.G + 1;
-  const int b = blockIdx.x / G1, j = blockIdx.x - (blockIdx.x / G1) * G1;
   const int gl = a.gamma_len ? a.gamma_len[b] : a.G;
   const int g = min(max(gl, 1), a.G);
-  if (j > g) return;                          // padding: the finisher writes it
-  {
-    // Argmax and top-k sequences belong to the list path unless their lists
-    // were demoted (overflow) by the select or the list kernel, or there is
-    // no list path in this call (every sequence promised dense).
-    const Mode sm = seq_mode(a, b);
-    if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE) && !a.all_dense) return;
-  }
-  int32_t* outp = a.out_target + (size_t)b * G1 + j;
   const float Tv = a.temp[b];
   const int k = a.topk ? a.topk[b] : 0;
   const float tp = a.topp ? a.topp[b] : 1.0f;
-  if (!(Tv >= 0.0f) || tp != tp) {            // the finisher rejects the sequence
-    if (threadIdx.x == 0) *outp = GUMBEL_BAD_ROW;
-    return;
-  }
+  if (!(Tv >= 0.0f) || tp != tp) return GUMBEL_BAD_ROW;   // the finisher rejects the sequence
   const int V = a.V;
   const int NU = VECTOR ? V / E : V;
   const U* gp = reinterpret_cast<const U*>(row_ptr<ET>(a, b, true, j));
@@ -83,10 +73,7 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
     });
     uint32_t dummy = 0;
     pb_max3<NTP>(km, bad, dummy, s.red_u);
-    if (bad || km <= Key<ET>::NEG_INF) {
-      if (threadIdx.x == 0) *outp = GUMBEL_BAD_ROW;
-      return;
-    }
+    if (bad || km <= Key<ET>::NEG_INF) return GUMBEL_BAD_ROW;
     if (tp < 1.0f) {
       Mode m;
       m.g = g;
@@ -150,8 +137,27 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
   const uint32_t mykey = bkey;
   pb_max3<NTP>(bkey, bad, kmax, s.red_u);     // block-wide maxima
   const uint32_t win = pb_min<NTP>(bkey != 0u && mykey == bkey ? bidx : NONE, s.red_u);
-  if (threadIdx.x == 0)
-    *outp = (bad || kmax <= Key<ET>::NEG_INF || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
+  return (bad || kmax <= Key<ET>::NEG_INF || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
+}
+
+template <typename ET, int NTP, bool VECTOR>
+__global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
+  __shared__ PairSmem<NTP> s;
+  __shared__ PairStream ps;
+  const int G1 = a.G + 1;
+  const int b = blockIdx.x / G1, j = blockIdx.x - (blockIdx.x / G1) * G1;
+  const int gl = a.gamma_len ? a.gamma_len[b] : a.G;
+  const int g = min(max(gl, 1), a.G);
+  if (j > g) return;                          // padding: the finisher writes it
+  {
+    // Argmax and top-k sequences belong to the list path unless their lists
+    // were demoted (overflow) by the select or the list kernel, or there is
+    // no list path in this call (every sequence promised dense).
+    const Mode sm = seq_mode(a, b);
+    if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE) && !a.all_dense) return;
+  }
+  const int32_t tok = gumbel_row_block<ET, NTP, VECTOR>(a, s, ps, b, j);
+  if (threadIdx.x == 0) a.out_target[(size_t)b * G1 + j] = tok;
 }
 
 // Chunks of 64 list entries the list kernel's register path holds per row
@@ -248,6 +254,56 @@ __device__ __forceinline__ int32_t gumbel_row_fast(const Args& a, FinSmem& s, co
   return (__ballot(bad != 0u) != 0ull || id == NONE) ? GUMBEL_BAD_ROW : (int32_t)id;
 }
 
+// The first disagreement and the outputs of sequence b, by one wavefront:
+// validity (parameters, drafts, every row's sample), the first position
+// whose draft differs from the target's sample (one ballot, find-first-set),
+// then the tokens, n and the per-position samples (-1 past gamma_b or for an
+// invalid sequence).  target(j) is row j's sample for j <= gamma_b.
+template <class TG>
+__device__ __forceinline__ void gumbel_finish_wave(const Args& a, int b, TG target) {
+  const int lane = threadIdx.x & 63;
+  const int G = a.G, G1 = G + 1;
+  const int gl = a.gamma_len ? a.gamma_len[b] : G;
+  const float Tv = a.temp[b];
+  const float tp = a.topp ? a.topp[b] : 1.0f;
+  const int g = min(max(gl, 1), G);
+  int32_t* tgt = a.out_target + (size_t)b * G1;
+  const int32_t* xb = a.draft + (size_t)b * G;
+  uint32_t badl = ((a.sampler || (gl >= 1 && gl <= G)) && Tv >= 0.0f && tp == tp) ? 0u : 1u;
+  for (int jj = lane; jj <= g; jj += 64) badl |= target(jj) < 0 ? 1u : 0u;
+  bool mism = false;
+  if (lane < g) {
+    const int x = xb[lane];
+    badl |= (x < 0 || x >= a.V) ? 1u : 0u;
+    mism = x != target(lane);
+  }
+  const bool ok = __ballot(badl != 0u) == 0ull;
+  const unsigned long long mask = __ballot(mism);
+  const int n = mask ? __ffsll((long long)mask) - 1 : g;
+  const int32_t tok = ok ? target(n) : -1;
+  int32_t* ot = a.out_tokens + (size_t)b * G1;
+  for (int jj = lane; jj <= G; jj += 64) {
+    ot[jj] = ok ? (jj < n ? xb[jj] : (jj == n ? tok : -1)) : -1;
+    if (!ok || jj > g) tgt[jj] = -1;
+  }
+  if (lane == 0) {
+    if (a.out_n) a.out_n[b] = ok ? n : -1;
+    a.seq_flags[b] = 0;
+  }
+}
+
+// The list kernel's LDS: the LDS list path's, or (calls it finishes) the
+// whole-workgroup row path's.
+template <int NTP>
+constexpr size_t gumbel_pair_stream_offset() {
+  return (sizeof(PairSmem<NTP>) + 15) / 16 * 16;
+}
+constexpr size_t gumbel_list_smem_bytes() {
+  return sizeof(FinSmem) > gumbel_pair_stream_offset<NT>() + sizeof(PairStream)
+             ? sizeof(FinSmem)
+             : gumbel_pair_stream_offset<NT>() + sizeof(PairStream);
+}
+
 // Argmax and top-k (<= KMAX_SPARSE) sequences from the streaming select's
 // survivor lists: one workgroup per sequence.  Every row's kept set (the
 // union of its part lists cut to the k-th largest, then to the nucleus when
@@ -259,10 +315,16 @@ __device__ __forceinline__ int32_t gumbel_row_fast(const Args& a, FinSmem& s, co
 // registers take the register path first: wavefront r takes row r
 // (gumbel_row_fast), with no block barrier unless some row does not fit,
 // which sends the whole sequence to the LDS path.
-template <typename ET>
+//
+// With a.gfuse (calls promised to hold no dense sequence) this launch is
+// the last of the call: dense, invalid and demoted sequences get their rows
+// from the whole workgroup here (gumbel_row_block, one row after another),
+// and every sequence is finished here (gumbel_finish_wave).
+template <typename ET, bool VECTOR>
 __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char gl_smem[];
   FinSmem& s = *reinterpret_cast<FinSmem*>(gl_smem);
+  __shared__ int32_t ftok[SV_MAX_GAMMA + 1];   // a.gfuse: every row's sample
   const int b = blockIdx.x;
   const int G = a.G, RS = a.RS, V = a.V;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wavefront-uniform
@@ -283,21 +345,30 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
     if (lane < a.NP) fcnt = (uint32_t)a.counts[((size_t)b * RS + wave) * a.NP + lane];
   }
   const Mode m = seq_mode(a, b);
-  if (m.mode != MODE_GREEDY && m.mode != MODE_SPARSE) return;
   const uint32_t fl = a.seq_flags[b];
-  if (fl & F_DEMOTE) return;
+  const bool fuse = a.gfuse != 0;
   const int R = m.g + 1;
   const int NS = R * a.NP;
   int32_t* tgt = a.out_target + (size_t)b * (G + 1);
-  if (fl & F_BAD) {
-    for (int j = threadIdx.x; j < R; j += NT) tgt[j] = GUMBEL_BAD_ROW;
-    return;
+  // Where the sequence's rows come from (block-uniform).
+  enum { ROWS_LIST, ROWS_BLOCK, ROWS_BAD };
+  int src = ROWS_LIST;
+  if (m.mode != MODE_GREEDY && m.mode != MODE_SPARSE) src = ROWS_BLOCK;
+  else if (fl & F_DEMOTE) src = ROWS_BLOCK;
+  else if (fl & F_BAD) src = ROWS_BAD;
+  else if (NS > MAXSEG) {
+    if (!fuse && threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
+    src = ROWS_BLOCK;
   }
-  if (NS > MAXSEG) {
-    if (threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
-    return;
+  if (src == ROWS_BLOCK && !fuse) return;   // gumbel_kernel takes it
+  if (src == ROWS_BAD) {
+    for (int j = threadIdx.x; j < R; j += NT) {
+      tgt[j] = GUMBEL_BAD_ROW;
+      ftok[j] = GUMBEL_BAD_ROW;
+    }
   }
-  if (a.NP <= GUMBEL_CH && G < NWAVE && (m.mode == MODE_GREEDY || !(m.tp < 1.0f))) {   // block-uniform
+  bool listed = false;   // every row's sample found from the lists (block-uniform)
+  if (src == ROWS_LIST && a.NP <= GUMBEL_CH && G < NWAVE && (m.mode == MODE_GREEDY || !(m.tp < 1.0f))) {
     bool fits = true;
     if (wave < R) {
       int32_t tok;
@@ -311,109 +382,112 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
         case 7: tok = gumbel_row_fast<ET, 7>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
         default: tok = gumbel_row_fast<ET, 8>(a, s, m, b, wave, f0, fcnt, lpw, &fits); break;
       }
-      if (fits && lane == 0) tgt[wave] = tok;
+      if (fits && lane == 0) {
+        tgt[wave] = tok;
+        ftok[wave] = tok;
+      }
     }
     if (lane == 0) s.fflag[wave] = fits ? 0u : 1u;
     __syncthreads();
     uint32_t any = 0;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) any |= s.fflag[w];
-    if (any == 0u) return;   // block-uniform
-    __syncthreads();         // the LDS path below reuses the memory
+    listed = any == 0u;
+    __syncthreads();   // the LDS path below reuses the memory
   }
-  uint32_t c = 0;
-  if ((int)threadIdx.x < NS) c = (uint32_t)max(a.counts[(size_t)b * RS * a.NP + threadIdx.x], 0);
-  uint32_t total = 0;
-  const uint32_t excl = block_excl_scan(c, s.red_u, &total);
-  if (total > (uint32_t)POOL) {
-    if (threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
-    return;
-  }
-  if ((int)threadIdx.x < NS) s.soff[threadIdx.x] = excl;
-  if (threadIdx.x == 0) s.soff[NS] = total;
-  __syncthreads();
-  for (int r = threadIdx.x; r <= R; r += NT) s.off[r] = s.soff[r * a.NP];
-  for (uint32_t e = threadIdx.x; e < total; e += NT) {
-    int lo = 0, hi = NS;   // list with soff[lo] <= e < soff[lo+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s.soff[mid] <= e) lo = mid;
-      else hi = mid;
-    }
-    const int r = lo / a.NP, p = lo - r * a.NP;
-    s.pool[e] = a.lists[list_index(a, b * RS + r, p) + (e - s.soff[lo])];
-  }
-  __syncthreads();
-  for (int r = wave; r < R; r += NWAVE) {
-    if (s.off[r + 1] > s.off[r]) pool_row_stats<ET>(s, r, m, a.NP);
-  }
-  __syncthreads();
-  for (int r = wave; r < R; r += NWAVE) {
-    int32_t tok;
-    if (s.off[r + 1] == s.off[r]) {
-      tok = GUMBEL_BAD_ROW;   // no finite logit
-    } else if (m.mode == MODE_GREEDY) {
-      tok = (int32_t)s.st_arg[r];
+  if (src == ROWS_LIST && !listed) {
+    uint32_t c = 0;
+    if ((int)threadIdx.x < NS) c = (uint32_t)max(a.counts[(size_t)b * RS * a.NP + threadIdx.x], 0);
+    uint32_t total = 0;
+    const uint32_t excl = block_excl_scan(c, s.red_u, &total);
+    if (total > (uint32_t)POOL) {   // does not fit in LDS
+      if (!fuse) {
+        if (threadIdx.x == 0) a.seq_flags[b] = fl | F_DEMOTE;
+        return;
+      }
+      src = ROWS_BLOCK;
     } else {
-      const int o = (int)s.off[r], n = (int)s.st_cnt[r];
-      const float* gn = a.noise + ((size_t)b * (G + 1) + r) * (size_t)V;
-      uint32_t bkey = 0, bid = NONE, bad = 0;
-      for (int j = lane; j < n; j += 64) {
+      if ((int)threadIdx.x < NS) s.soff[threadIdx.x] = excl;
+      if (threadIdx.x == 0) s.soff[NS] = total;
+      __syncthreads();
+      for (int r = threadIdx.x; r <= R; r += NT) s.off[r] = s.soff[r * a.NP];
+      for (uint32_t e = threadIdx.x; e < total; e += NT) {
+        int lo = 0, hi = NS;   // list with soff[lo] <= e < soff[lo+1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s.soff[mid] <= e) lo = mid;
+          else hi = mid;
+        }
+        const int r = lo / a.NP, p = lo - r * a.NP;
+        s.pool[e] = a.lists[list_index(a, b * RS + r, p) + (e - s.soff[lo])];
+      }
+      __syncthreads();
+      for (int r = wave; r < R; r += NWAVE) {
+        if (s.off[r + 1] > s.off[r]) pool_row_stats<ET>(s, r, m, a.NP);
+      }
+      __syncthreads();
+      for (int r = wave; r < R; r += NWAVE) {
+        int32_t tok;
+        if (s.off[r + 1] == s.off[r]) {
+          tok = GUMBEL_BAD_ROW;   // no finite logit
+        } else if (m.mode == MODE_GREEDY) {
+          tok = (int32_t)s.st_arg[r];
+        } else {
+          const int o = (int)s.off[r], n = (int)s.st_cnt[r];
+          const float* gn = a.noise + ((size_t)b * (G + 1) + r) * (size_t)V;
+          uint32_t bkey = 0, bid = NONE, bad = 0;
+          for (int j = lane; j < n; j += 64) {
 #pragma clang fp contract(off)
-        const uint2 e = s.pool[o + j];
-        const float nz = gn[e.y];
-        bad |= fabsf(nz) < INFINITY ? 0u : 1u;
-        const float tg = m.T * nz;
-        const float sc = Key<ET>::value(e.x) + tg;
-        const uint32_t sk = score_key(sc);
-        if (sc == sc && (sk > bkey || (sk == bkey && e.y < bid))) {
-          bkey = sk;
-          bid = e.y;
+            const uint2 e = s.pool[o + j];
+            const float nz = gn[e.y];
+            bad |= fabsf(nz) < INFINITY ? 0u : 1u;
+            const float tg = m.T * nz;
+            const float sc = Key<ET>::value(e.x) + tg;
+            const uint32_t sk = score_key(sc);
+            if (sc == sc && (sk > bkey || (sk == bkey && e.y < bid))) {
+              bkey = sk;
+              bid = e.y;
+            }
+          }
+          const uint32_t best = wave_max_dpp(bkey);
+          const uint32_t id = wave_min_dpp(bkey == best && best != 0u ? bid : NONE);
+          bad = __ballot(bad != 0u) ? 1u : 0u;
+          tok = (bad || id == NONE) ? GUMBEL_BAD_ROW : (int32_t)id;
+        }
+        if (lane == 0) {
+          tgt[r] = tok;
+          ftok[r] = tok;
         }
       }
-      const uint32_t best = wave_max_dpp(bkey);
-      const uint32_t id = wave_min_dpp(bkey == best && best != 0u ? bid : NONE);
-      bad = __ballot(bad != 0u) ? 1u : 0u;
-      tok = (bad || id == NONE) ? GUMBEL_BAD_ROW : (int32_t)id;
     }
-    if (lane == 0) tgt[r] = tok;
   }
+  if (!fuse) return;
+  if (src == ROWS_BLOCK) {
+    // The workgroup takes the rows one after another.
+    __syncthreads();   // the LDS above is free
+    PairSmem<NT>& ps_s = *reinterpret_cast<PairSmem<NT>*>(gl_smem);
+    PairStream& ps_x = *reinterpret_cast<PairStream*>(gl_smem + gumbel_pair_stream_offset<NT>());
+    for (int j = 0; j < R; ++j) {
+      const int32_t tok = gumbel_row_block<ET, NT, VECTOR>(a, ps_s, ps_x, b, j);
+      if (threadIdx.x == 0) {
+        tgt[j] = tok;
+        ftok[j] = tok;
+      }
+      __syncthreads();   // the next row reuses the LDS
+    }
+  }
+  __syncthreads();   // publishes ftok
+  if (wave == 0) gumbel_finish_wave(a, b, [&](int j) { return ftok[j]; });
 }
 
 // One wavefront per sequence: validity, the first disagreement between the
 // drafts and the target's samples (one ballot, find-first-set), outputs.
 __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x * 4 + wave;
   if (b >= a.B) return;
-  const int G = a.G, G1 = G + 1;
-  const int gl = a.gamma_len ? a.gamma_len[b] : G;
-  const float Tv = a.temp[b];
-  const float tp = a.topp ? a.topp[b] : 1.0f;
-  const int g = min(max(gl, 1), G);
-  int32_t* tgt = a.out_target + (size_t)b * G1;
-  const int32_t* xb = a.draft + (size_t)b * G;
-  uint32_t badl = ((a.sampler || (gl >= 1 && gl <= G)) && Tv >= 0.0f && tp == tp) ? 0u : 1u;
-  for (int jj = lane; jj <= g; jj += 64) badl |= tgt[jj] < 0 ? 1u : 0u;
-  bool mism = false;
-  if (lane < g) {
-    const int x = xb[lane];
-    badl |= (x < 0 || x >= a.V) ? 1u : 0u;
-    mism = x != tgt[lane];
-  }
-  const bool ok = __ballot(badl != 0u) == 0ull;
-  const unsigned long long mask = __ballot(mism);
-  const int n = mask ? __ffsll((long long)mask) - 1 : g;
-  const int32_t tok = ok ? tgt[n] : -1;
-  int32_t* ot = a.out_tokens + (size_t)b * G1;
-  for (int jj = lane; jj <= G; jj += 64) {
-    ot[jj] = ok ? (jj < n ? xb[jj] : (jj == n ? tok : -1)) : -1;
-    if (!ok || jj > g) tgt[jj] = -1;
-  }
-  if (lane == 0) {
-    if (a.out_n) a.out_n[b] = ok ? n : -1;
-    a.seq_flags[b] = 0;
-  }
+  const int32_t* tgt = a.out_target + (size_t)b * (a.G + 1);
+  gumbel_finish_wave(a, b, [&](int j) { return tgt[j]; });
 }
 
 }  // namespace sv

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     L = _ensure_built()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert binding.spec_verify_version() == 10
+    assert binding.spec_verify_version() == 11
 
 
 def test_workspace_bytes():
@@ -134,7 +134,8 @@ def test_gumbel_host_argument_errors():
         return L.spec_verify_gumbel_ex(fake, binding.SV_BF16, fake, fake, nul, fake, nul, nul, hints, B, G, V, fake,
                                        fake, fake, fake, need, nul)
 
-    assert call_ex(binding.SV_HINT_NO_DENSE) == binding.SV_ERR_ARG
+    assert call_ex(binding.SV_HINT_NO_DENSE | binding.SV_HINT_ALL_DENSE) == binding.SV_ERR_ARG
+    assert call_ex(binding.SV_HINT_NO_DENSE, B=0) == binding.SV_OK
     assert call_ex(4) == binding.SV_ERR_ARG
     assert call_ex(binding.SV_HINT_ALL_DENSE, B=0) == binding.SV_OK
     assert call_ex(binding.SV_HINT_ALL_DENSE, B=-1) == binding.SV_ERR_ARG

@@ -98,9 +98,12 @@ def test_gumbel_workload_full_size(cid):
     # it passes the all-dense hint.
     T, k = gb.temperature, gb.top_k
     listed = (T == 0) | ((T > 0) & (k > 0) & (k < gb.V) & (k <= 512))
+    from speculative_sampling_verification_verify_amd import binding
     if not listed.any():
-        from speculative_sampling_verification_verify_amd import binding
         check_gumbel(gb, f"workload{cid}-full-all-dense-hint", hints=binding.SV_HINT_ALL_DENSE,
+                     min_compared_share=0.95)
+    if listed.all():   # and with only such sequences, the no-dense hint (two launches)
+        check_gumbel(gb, f"workload{cid}-full-no-dense-hint", hints=binding.SV_HINT_NO_DENSE,
                      min_compared_share=0.95)
 
 
@@ -110,7 +113,10 @@ def _replace(gb, **kw):
     return synth.GumbelBatch(**d)
 
 
-def test_gumbel_invalid_rows_and_padding():
+@pytest.mark.parametrize("hints", [0, 1])
+def test_gumbel_invalid_rows_and_padding(hints):
+    # hints = 1 (SV_HINT_NO_DENSE): the list kernel finishes the call and takes
+    # the dense, invalid and padded sequences itself.
     gb = synth.make_gumbel_batch(4, B=14, V=6000)
     P, N = gb.p_logits.copy(), gb.noise.copy()
     d, T, gl, tp = gb.draft.copy(), gb.temperature.copy(), gb.gamma_len.copy(), gb.top_p.copy()
@@ -133,7 +139,7 @@ def test_gumbel_invalid_rows_and_padding():
         N[b, g + 1:] = np.nan
         d[b, g:] = -7
     gb2 = _replace(gb, p_logits=P, noise=N, draft=d, temperature=T, gamma_len=gl, top_p=tp)
-    tok, n, tgt, ref = check_gumbel(gb2, "invalid-and-padding")
+    tok, n, tgt, ref = check_gumbel(gb2, f"invalid-and-padding-h{hints}", hints=hints, calls=2)
     assert (n[:8] == -1).all() and (ref.n[:8] == -1).all()
     assert (tok[:8] == -1).all() and (tgt[:8] == -1).all()
     assert n[8] >= 0 and (n[9:] >= 0).all()
@@ -222,3 +228,28 @@ def test_gumbel_all_dense_hint(cid, B, V):
     from speculative_sampling_verification_verify_amd import binding
     gb = synth.make_gumbel_batch(cid, B=B, V=V)
     check_gumbel(gb, f"all-dense-hint-w{cid}-B{B}-V{gb.V}", hints=binding.SV_HINT_ALL_DENSE, calls=2)
+
+
+@pytest.mark.parametrize("cid,B,V", [(3, 6, 50001), (2, 8, 40000), (3, 9, 152064), (0, 64, None), (4, 24, 20000),
+                                     (1, 8, None), (2, 3, 131072)])
+def test_gumbel_no_dense_hint(cid, B, V):
+    # The no-dense hint: the list kernel is the last launch.  Workloads 0, 1
+    # and 4 hold dense sequences, which break the promise and must still come
+    # out exact (the list kernel takes them row by row); V = 131072 over few
+    # sequences gives many parts per row.  The second of two calls is
+    # checked.
+    from speculative_sampling_verification_verify_amd import binding
+    gb = synth.make_gumbel_batch(cid, B=B, V=V)
+    check_gumbel(gb, f"no-dense-hint-w{cid}-B{B}-V{gb.V}", hints=binding.SV_HINT_NO_DENSE, calls=2)
+
+
+def test_gumbel_no_dense_hint_demoted_lists():
+    # Top-k lists that overflow the select's buffer (a run of equal logits at
+    # the k-th value) are demoted; under the no-dense hint the list kernel
+    # computes those rows itself.
+    gb = synth.make_gumbel_batch(3, B=6, V=30000)
+    P = gb.p_logits.copy()
+    P[1, :, :20000] = synth.f32_to_bf16_bits(np.float32(3.0))   # 20000 ties at the top
+    P[4, 2, ::2] = synth.f32_to_bf16_bits(np.float32(5.0))
+    from speculative_sampling_verification_verify_amd import binding
+    check_gumbel(_replace(gb, p_logits=P), "no-dense-hint-demoted", hints=binding.SV_HINT_NO_DENSE, calls=2)

@@ -1251,7 +1251,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
     const int r = threadIdx.x / a.NP, p = threadIdx.x - r * a.NP;
     const int si = used_slot(G, m.g, r) * a.NP + p;
     c = nslot <= MAXSEG ? s.cslot[si] : (uint32_t)max(a.counts[(size_t)b * RS * a.NP + si], 0);
-    rest = !spec || si >= 2 * NWAVE || c > (uint32_t)SPEC;
+    rest = fastc ? c > 64u : (!spec || si >= 2 * NWAVE || c > (uint32_t)SPEC);
   }
   // The list sizes' exclusive scan and the OR of the input checks and of the
   // lists' needs in one LDS round trip (the barrier after cslot already
@@ -1299,9 +1299,26 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
           if ((uint32_t)lane < n) s.pool[o + lane] = sp[h];
         }
       }
+    } else if (fastc) {
+      // The register path's first chunks: wavefront w holds those of used
+      // rows w (target) and g + 1 + w (draft).
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = h == 0 ? (wave <= m.g ? wave : -1) : (wave < m.g ? m.g + 1 + wave : -1);
+        if (r >= 0) {
+#pragma unroll
+          for (int p = 0; p < FAST_CH; ++p) {
+            if (p < a.NP) {
+              const uint32_t o = s.soff[r * a.NP + p], n = s.soff[r * a.NP + p + 1] - o;
+              if ((uint32_t)lane < n) s.pool[o + lane] = f0[h][p];
+            }
+          }
+        }
+      }
     }
-    // The rest (lists past the first 2 NWAVE, entries past the first SPEC)
-    // in one round trip.
+    // The rest (lists past the first 2 NWAVE, entries past the first SPEC;
+    // with the register path's chunks, entries past the first 64) in one
+    // round trip.
     for (uint32_t e = (flags & 2u) ? threadIdx.x : total; e < total; e += NT) {
       int lo = 0, hi = NS;   // list with soff[lo] <= e < soff[lo+1]
       while (hi - lo > 1) {
@@ -1312,7 +1329,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       const int r = lo / a.NP, p = lo - r * a.NP;
       const int si = used_slot(G, m.g, r) * a.NP + p;
       const uint32_t j = e - s.soff[lo];
-      if (spec && si < 2 * NWAVE && j < (uint32_t)SPEC) continue;
+      if (fastc ? j < 64u : (spec && si < 2 * NWAVE && j < (uint32_t)SPEC)) continue;
       s.pool[e] = a.lists[list_index(a, b * RS + used_slot(G, m.g, r), p) + j];
     }
     __syncthreads();

@@ -298,7 +298,11 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     // bf16 rows streamed from memory, up to PH_MAX_UNITS 16-byte units: the
     // histogram variant, one workgroup per CU.
     const bool hist = pv == -1024 && sizeof(ET) == 2 && VECTOR && (long long)a.V / 8 <= PH_MAX_UNITS;
-    const long long cap = hist ? 256 : pair_grid_cap(pv);
+    long long cap = hist ? 256 : pair_grid_cap(pv);
+    if (pv == 64 && a.pair_regs) {   // rows in registers: no row LDS, more workgroups per CU
+      plds = 0;
+      cap = 256LL * (sizeof(ET) == 4 ? PAIR_REGS_WGS_F32 : PAIR_REGS_WGS_BF16);
+    }
     const dim3 grid((unsigned)(npairs < cap ? npairs : cap));
     if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
     if (hist) pv = 0;
@@ -440,7 +444,13 @@ static int run_verify(const void* p_logits, const void* q_logits, int dtype, con
   // Few pairs of unfiltered rows (the caller's promise): each pair is split
   // over several workgroups.
   const int S = layout_chunks(B, gamma_max, V, dtype, RS);
+  size_t pair_lds_unused = 0;
   a.split_s = (hints & SV_HINT_UNFILTERED) && a.pair && !sampler && vector_ok && S > 1 ? S : 0;
+  // Short unfiltered rows (the same promise) need no LDS copy: the 64-thread
+  // pair kernel then holds them in registers, and more of its workgroups fit
+  // on a CU.
+  a.pair_regs = (hints & SV_HINT_UNFILTERED) && a.pair && !sampler && vector_ok && a.split_s <= 1 &&
+                pair_variant(V, dtype, true, &pair_lds_unused) == 64 ? 1 : 0;
   a.chunks = reinterpret_cast<ChunkRec*>(ws + Lw.chunks_off);
   a.sel_blocks = a.pair ? sel_grid : grid;
   a.lists = reinterpret_cast<uint2*>(ws + Lw.lists_off);

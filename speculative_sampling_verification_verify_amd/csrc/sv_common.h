@@ -58,6 +58,8 @@ struct Args {
   int split;              // 1 when NP > 1 only because the call is small: a top-k sequence whose
                           // part lists might overflow the finisher's pool streams rows whole
   int split_s;            // chunks per dense pair when the split kernels run (0: pair_kernel)
+  int pair_regs;          // 1: the 64-thread pair kernel holds no rows in LDS (the caller promised
+                          // unfiltered rows); a pair that is not unfiltered gets REC_REDO
   ChunkRec* chunks;       // [B * (G+1)][split_s] per-chunk records of the split kernels
   int all_dense;          // 1: no select launch; the pair kernel takes every (sequence, position) in
                           // order and the finisher runs non-dense sequences by its multi-pass path

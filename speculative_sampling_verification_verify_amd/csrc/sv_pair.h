@@ -498,6 +498,168 @@ __device__ __forceinline__ float pprob(const RowStat& st, float z) {
   return z >= st.zthr ? ew(z, st.zmax, st.c) * st.sp : 0.0f;
 }
 
+// A pair of short unfiltered rows (no top-k below V, no top-p; at most
+// PAIR_SMALL_CH 16-byte units per lane, one wavefront) with the rows in
+// registers: the same record as pair_one, with no LDS and no barrier.  Unit
+// u of a row is chunk u / 64 of lane u % 64, so ascending id is (chunk,
+// lane, element) order.  Every load is issued at once (an index past the
+// row re-reads its last unit, which is then masked).
+constexpr int PAIR_SMALL_CH = 4;
+// Workgroups per CU of the 64-thread variant when no pair holds rows in LDS
+// (its wavefronts per SIMD: five for fp32, four for bf16 rows).
+constexpr int PAIR_REGS_WGS_F32 = 20;
+constexpr int PAIR_REGS_WGS_BF16 = 16;
+template <typename ET>
+__device__ __forceinline__ void pair_small(const Args& a, int b, int i, const Mode& m, bool resid) {
+  using T = PT<ET, true>;
+  using U = typename T::U;
+  constexpr int E = T::E;
+  constexpr int NR = PAIR_SMALL_CH;
+  const int lane = threadIdx.x & 63;
+  const int G1 = a.G + 1;
+  const int NU = a.V / E;
+  const U* gp = reinterpret_cast<const U*>(row_ptr<ET>(a, b, true, i));
+  const U* gq = resid ? reinterpret_cast<const U*>(row_ptr<ET>(a, b, false, i)) : gp;
+  U up[NR], uq[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int ui = min(r * 64 + lane, NU - 1);
+    up[r] = load_nt(gp + ui);
+    uq[r] = load_nt(gq + ui);
+  }
+  const int x = resid ? a.draft[(size_t)b * a.G + i] : -1;
+  const double u = (double)a.u[(size_t)b * G1 + a.G];
+  PosRec* rec = a.pos + (size_t)b * G1 + i;
+  // Validity and the rows' maxima.
+  uint32_t bad = 0;
+  float zmp = -INFINITY, zmq = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (r * 64 + lane < NU) {
+      T::each(up[r], [&](int, uint32_t raw) {
+        const float z = T::val(raw);
+        bad |= z < INFINITY ? 0u : 1u;
+        zmp = fmaxf(zmp, z);
+      });
+      if (resid) {
+        T::each(uq[r], [&](int, uint32_t raw) {
+          const float z = T::val(raw);
+          bad |= z < INFINITY ? 0u : 1u;
+          zmq = fmaxf(zmq, z);
+        });
+      }
+    }
+  }
+  const uint32_t kmp = wave_max_dpp(key_of_value<ET>(zmp));
+  const uint32_t kmq = wave_max_dpp(key_of_value<ET>(zmq));
+  if (__ballot(bad != 0u) != 0ull || kmp <= Key<ET>::NEG_INF || (resid && kmq <= Key<ET>::NEG_INF)) {
+    if (lane == 0) {
+      rec->bad = 1u;
+      rec->tok = -1;
+    }
+    return;
+  }
+  const float c = LOG2E_F / m.T;
+  const float zp = Key<ET>::value(kmp), zq = resid ? Key<ET>::value(kmq) : 0.0f;
+  // Normalisers.
+  double lsp = 0.0, lsq = 0.0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (r * 64 + lane < NU) {
+      float fp = 0.0f, fq = 0.0f;
+      T::each(up[r], [&](int, uint32_t raw) { fp += ew(T::val(raw), zp, c); });
+      if (resid) T::each(uq[r], [&](int, uint32_t raw) { fq += ew(T::val(raw), zq, c); });
+      lsp += (double)fp;
+      lsq += (double)fq;
+    }
+  }
+  const double Sp = wave_sum_dpp(lsp), Sq = wave_sum_dpp(lsq);
+  const RowStat sp{-INFINITY, zp, c, (float)(1.0 / Sp)};
+  const RowStat sq = resid ? RowStat{-INFINITY, zq, c, (float)(1.0 / Sq)} : sp;
+  // Element j of a unit (its bit pattern).
+  auto elem = [](const U& v, int j) -> uint32_t {
+    const uint32_t w = j < E / 4 * 1 ? v.x : (j < 2 * (E / 4) ? v.y : (j < 3 * (E / 4) ? v.z : v.w));
+    if constexpr (sizeof(ET) == 2) return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+    else return w;
+  };
+  // Overlap, p(x), q(x) and the weight totals.
+  double al = 0.0, zl = 0.0, zt = 0.0, px = 0.0, qx = 0.0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int ui = r * 64 + lane;
+    if (ui < NU) {
+      float av = 0.0f, wr = 0.0f, pr = 0.0f;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const float pj = pprob(sp, T::val(elem(up[r], j)));
+        const float qj = resid ? pprob(sq, T::val(elem(uq[r], j))) : 0.0f;
+        av += fminf(pj, qj);
+        wr += resid ? fmaxf(pj - qj, 0.0f) : pj;
+        pr += pj;
+        if (ui * E + j == x) {
+          px = (double)pj;
+          qx = (double)qj;
+        }
+      }
+      al += (double)av;
+      zl += (double)wr;
+      zt += (double)pr;
+    }
+  }
+  al = wave_sum_dpp(al);
+  double Z = wave_sum_dpp(zl);
+  zt = wave_sum_dpp(zt);
+  px = wave_sum_dpp(px);
+  qx = wave_sum_dpp(qx);
+  const bool use_q = resid && Z > 0.0;   // zero residual mass: draw from p itself
+  if (resid && !use_q) Z = zt;
+  // The inverse CDF in ascending id: chunk by chunk, a prefix scan of the
+  // lanes' weight sums, then each lane's own elements in order (weights
+  // formed again rather than kept).
+  auto weight = [&](const U& vp, const U& vq, int j) -> float {
+    const float pj = pprob(sp, T::val(elem(vp, j)));
+    return use_q ? fmaxf(pj - pprob(sq, T::val(elem(vq, j))), 0.0f) : pj;
+  };
+  const double target = u * Z;
+  double base = 0.0;
+  uint32_t hit = NONE, lastpos = 0u;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (hit == NONE && r * 64 < NU) {
+      const int ui = r * 64 + lane;
+      const bool in = ui < NU;
+      double lw = 0.0;
+      if (in) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) lw += (double)weight(up[r], uq[r], j);
+      }
+      const double incl = wave_incl_scan_f64(lw);
+      double cum = base + (incl - lw);
+      uint32_t h = NONE;
+      if (in) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const float wj = weight(up[r], uq[r], j);
+          cum += (double)wj;
+          const uint32_t idx = (uint32_t)(ui * E + j);
+          if (h == NONE && wj > 0.0f && cum > target) h = idx;
+          if (wj > 0.0f) lastpos = idx + 1u;
+        }
+      }
+      hit = wave_min_dpp(h);
+      base += readlane_f64(incl, 63);
+    }
+  }
+  const int tok = hit != NONE ? (int)hit : (int)wave_max_dpp(lastpos) - 1;   // rounding left no crossing
+  if (lane == 0) {
+    rec->px = px;
+    rec->qx = qx;
+    rec->alpha = resid ? al : 0.0;
+    rec->tok = tok;
+    rec->bad = 0u;
+  }
+}
+
 // One (sequence b, position i) pair by the whole workgroup.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
 __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<NTP>& s, PairExtra<LDSR>& ps,
@@ -526,6 +688,16 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   const U* P;
   const U* Q;
   const bool online = !(k > 0 && k < V) && !(m.tp < 1.0f);
+  if constexpr (NTP == 64 && VECTOR && LDSR) {
+    if (online && NU <= PAIR_SMALL_CH * 64) {   // short unfiltered rows: registers only
+      pair_small<ET>(a, b, i, m, resid);
+      return;
+    }
+    if (a.pair_regs) {   // no row LDS in this launch: the finisher computes the sequence
+      if (threadIdx.x == 0) a.pos[(size_t)b * G1 + i].bad = REC_REDO;
+      return;
+    }
+  }
   const float cT = LOG2E_F / m.T;
   float zmp = -INFINITY, zmq = -INFINITY, smp = 0.0f, smq = 0.0f;
   uint32_t bad = 0;
@@ -779,9 +951,12 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
 // address: those workgroups step through the list by the grid size.  When no
 // sequence is dense every workgroup reads the counts once and leaves.  When
 // the caller has promised that every sequence is dense there is no list (and
-// no select launch): the pairs are taken in a fixed order instead.
+// no select launch): the pairs are taken in a fixed order instead.  The
+// 64-thread variant keeps PAIR_REGS_WGS_* / 4 wavefronts per SIMD, which
+// bounds the registers of its register-only path.
 template <typename ET, int NTP, bool VECTOR, bool LDSR>
-__global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(LDSR ? 1 : PAIR_STREAM_WAVES_PER_EU)))
+__global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(
+    LDSR ? (NTP == 64 ? (sizeof(ET) == 4 ? PAIR_REGS_WGS_F32 : PAIR_REGS_WGS_BF16) / 4 : 1) : PAIR_STREAM_WAVES_PER_EU)))
 void pair_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char pair_rows[];
   __shared__ PairSmem<NTP> s;

@@ -278,13 +278,17 @@ def test_split_pairs_match_oracle(dtype, V, B, G):
         log(f"[split] ok {rep}")
 
 
-def test_split_pairs_edge_cases():
+@pytest.mark.parametrize("V,dtype", [(40000, "bf16"), (1000, "fp32"), (2000, "bf16"), (520, "fp32")])
+def test_split_pairs_edge_cases(V, dtype):
     """Under the unfiltered hint: equal draft and target rows (zero residual:
     the draw falls back to p), -inf entries, a NaN row (invalid), short
     drafts (padding positions), and sequences that break the promise (top-p,
-    top-k above 512, top-k 20, argmax), which take the finisher's paths."""
+    top-k above 512, top-k 20, argmax), which take the finisher's paths.
+    V = 40000 runs the split kernels; the short rows run the 64-thread pair
+    kernel with its rows in registers and no row LDS (top-k 600 is a filter
+    only where V > 600)."""
     from speculative_sampling_verification_verify_amd import binding
-    B, G, V = 8, 3, 40000
+    B, G = 8, 3
     rng = np.random.default_rng(46)
     rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
     zp = (3.0 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
@@ -295,10 +299,10 @@ def test_split_pairs_edge_cases():
     T = np.array([1.0, 0.9, 1.1, 0.8, 1.0, 0.7, 1.2, 0.0], np.float32)
     k = np.array([0, 0, 0, 0, 600, 20, 0, 0], np.int32)
     tp = np.array([1.0, 1.0, 1.0, 0.9, 1.0, 1.0, 1.0, 1.0], np.float32)
-    bt = dense_batch(V, "bf16", B=B, G=G, seed=47, T=T, k=k, tp=tp, zp=zp, zq=zq)
+    bt = dense_batch(V, dtype, B=B, G=G, seed=47, T=T, k=k, tp=tp, zp=zp, zq=zq)
     gl = np.array([3, 3, 1, 3, 2, 3, 3, 3], np.int32)
     P = bt.p_logits.copy()
-    P[2, 1, 99] = 0x7FC1                       # NaN in a target row of sequence 2 (position 1 is used)
+    P[2, 1, 99] = 0x7FC1 if dtype == "bf16" else np.nan   # NaN in a target row of sequence 2 (position 1 is used)
     bt = synth.Batch(bt.workload, P, bt.q_logits, bt.draft, bt.u, gl, bt.temperature, bt.top_k, bt.top_p,
                      bt.seed)
     ref = run_oracle(bt)
@@ -306,5 +310,5 @@ def test_split_pairs_edge_cases():
     for hints in (binding.SV_HINT_UNFILTERED, binding.SV_HINT_ALL_DENSE | binding.SV_HINT_UNFILTERED):
         ver = _split_verifier(bt, hints)
         for call in range(2):
-            log(f"[split] edge cases hints={hints} call {call}")
-            compare(bt, run_gpu(bt, verifier=ver), ref, f"split-edges-h{hints}-c{call}")
+            log(f"[split] edge cases V={V} {dtype} hints={hints} call {call}")
+            compare(bt, run_gpu(bt, verifier=ver), ref, f"split-edges-V{V}-h{hints}-c{call}")

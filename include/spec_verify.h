@@ -143,7 +143,9 @@ enum {
                             workgroups (three launches that exchange per-chunk maxima,
                             normalisers and weight sums through the workspace) instead of one
                             workgroup per pair: the latency of small batches with large
-                            vocabularies.  A sequence that does have top-k or top-p still gets
+                            vocabularies.  When rows are at most 4 KB and 16-byte aligned, the
+                            dense pairs' rows stay in registers with no LDS copy, so more pairs
+                            run at once.  A sequence that does have top-k or top-p still gets
                             its exact result, from the slower one-workgroup-per-sequence path. */
 };
 

@@ -2,13 +2,18 @@
 // bonus draw.  One workgroup (NT threads) per sequence.
 //
 // Top-k and argmax sequences work from the survivor lists left by the
-// streaming select: every (row, part) list of the sequence is brought into
-// LDS in one round trip; then each wavefront takes whole rows (the row's
-// exact kept set from the union of its part lists, normaliser, top-p cut)
-// and whole positions (p(x), q(x), overlap), and one wavefront takes the
-// acceptance test and the draw.  Entries are broadcast to the wavefront
-// through registers (readlane), so the all-pairs loops over a row's
-// survivors do not wait on LDS once per entry.
+// streaming select.  Without top-p, and when every part list fits, the
+// register path takes them: one wavefront per position holds its two rows'
+// lists in registers and computes everything for that position with no
+// block barrier; one barrier then gives wavefront 0 every position for the
+// acceptance test (fast_position).  Otherwise the LDS list path: every
+// (row, part) list of the sequence is brought into LDS in one round trip;
+// each wavefront takes whole rows (the row's exact kept set from the union
+// of its part lists, normaliser, top-p cut) and whole positions (p(x),
+// q(x), overlap), and one wavefront takes the acceptance test and the draw.
+// Entries are broadcast to the wavefront through registers (readlane), so
+// the all-pairs loops over a row's survivors do not wait on LDS once per
+// entry.
 //
 // Sequences without top-k (or whose lists overflowed) run a multi-pass
 // procedure over the logits in one workgroup: maximum, count-based radix

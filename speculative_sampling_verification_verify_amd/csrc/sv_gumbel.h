@@ -11,11 +11,17 @@
 // score is formed in float32 as fl(z + fl(T * g)) with no fused multiply-add,
 // and ties go to the lowest id.  T = 0 is argmax of z (noise unused).
 //
-// gumbel_kernel: one workgroup per (sequence, position).  Unfiltered rows
-// take one pass over the logits and the noise (validity, and the argmax of
-// the score); top-k rows first find the k-th largest key (block radix
-// select), top-p rows the nucleus threshold (the pair kernel's row
-// statistics), then the argmax pass runs over the support.
+// gumbel_list_kernel: argmax and top-k sequences from the streaming
+// select's survivor lists, one workgroup per sequence (a wavefront per row
+// in registers, or the rows' kept sets in LDS); with the no-dense promise it
+// is the call's last launch and also takes the other sequences and the
+// outputs.
+// gumbel_kernel: one workgroup per (sequence, position) of the dense and
+// demoted sequences.  Unfiltered rows take one pass over the logits and the
+// noise (validity, and the argmax of the score); top-k rows first find the
+// k-th largest key (block radix select), top-p rows the nucleus threshold
+// (the pair kernel's row statistics), then the argmax pass runs over the
+// support.
 // gumbel_finish_kernel: one wavefront per sequence: the first disagreement
 // by one ballot and find-first-set, and the outputs.
 #pragma once

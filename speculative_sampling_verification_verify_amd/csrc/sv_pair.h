@@ -4,8 +4,10 @@
 // One workgroup per (sequence, position i <= gamma_b) owns the target row p_i
 // and, for i < gamma_b, the draft row q_i; every row belongs to exactly one
 // workgroup.  Rows of up to 64 KB are read from HBM once into LDS and every
-// later pass runs on chip; longer rows are streamed from global memory on
-// each pass (the re-reads of one workgroup's rows hit L2 / MALL).  Per row:
+// later pass runs on chip (short unfiltered rows stay in the wavefront's
+// registers instead: pair_small); longer rows are streamed from global
+// memory on each pass (the re-reads of one workgroup's rows hit L2 / MALL).
+// Per row:
 //   * validity and the maximum logit;
 //   * the top-k threshold key (radix select) when KMAX_SPARSE < k < V;
 //   * the normaliser and, for top-p, the nucleus cut by a mass-weighted radix

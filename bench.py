@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -54,12 +55,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_text(text: str) -> str:
+    """The source with comments removed and whitespace runs collapsed, so that
+    an edit of comments or layout does not mark a profile stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel: str | None = None) -> str:
+    """Hash of the code (not the comments) of the sources a kernel is built
+    from; profiles/ records it beside the counters taken on that code."""
     names = KERNEL_SOURCES.get(kernel) or sorted(os.listdir(CSRC))
     h = hashlib.sha256()
     for name in sorted(names):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -334,7 +334,11 @@ def main_gumbel(args):
     torch.cuda.synchronize()
     K = args.steps
     kern = binding.SV_KERNEL_SELECT if sel_bytes >= dense_bytes else binding.SV_KERNEL_GUMBEL
-    kname = "select_kernel" if kern == binding.SV_KERNEL_SELECT else "gumbel_kernel"
+    # The dense stage is the histogram kernel for filtered bf16 rows of 32K-131K
+    # values (16-byte aligned), else the per-(sequence, position) kernel.
+    hist_rows = dtype_name == "bf16" and 32768 < gb.V <= 131072 and gb.V % 8 == 0
+    kname = ("select_kernel" if kern == binding.SV_KERNEL_SELECT
+             else ("gumbel_hist_kernel" if hist_rows else "gumbel_kernel"))
     wall, k_ms = timed_calls(step, kern, K)
     ms_per_step = wall * 1e3 / K
     n_acc = ver.n_accepted.cpu().numpy()

@@ -264,6 +264,9 @@ static hipError_t device_setup() {
       if (e != hipSuccess) return e;
     }
   }
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_hist_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)sizeof(PhSmem));
+  if (e != hipSuccess) return e;
   g_setup_done[dev] = true;
   return hipSuccess;
 }
@@ -625,8 +628,16 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.gfuse) return hipSuccess;
   }
-  // 3. Dense and demoted sequences, one workgroup per (sequence, position).
+  // 3. Dense and demoted sequences: filtered bf16 rows of 32K-131K values by
+  //    the histogram kernel (one workgroup per CU), the rest one workgroup
+  //    per (sequence, position).
   if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
+  if (a.ghist) {
+    const long long nrows = (long long)a.B * (a.G + 1);
+    hipLaunchKernelGGL(gumbel_hist_kernel, dim3((unsigned)(nrows < 256 ? nrows : 256)), dim3(PH_NT), sizeof(PhSmem),
+                       st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((gumbel_kernel<ET, GUMBEL_NT, VECTOR>), dim3((unsigned)((long long)a.B * (a.G + 1))),
                      dim3(GUMBEL_NT), 0, st, a);
   e = hipGetLastError();
@@ -695,6 +706,10 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   // The promise that no sequence is dense lets the list kernel finish the
   // call: it takes the rare dense, invalid or demoted sequence itself.
   a.gfuse = (hints & SV_HINT_NO_DENSE) && !sampler ? 1 : 0;
+  // Filtered bf16 rows too long for one pass over the row to give their
+  // support cheaply: the exact histogram kernel.
+  a.ghist = !a.gfuse && dtype == SV_BF16 && vector_ok && V > 32768 && V / 8 <= PH_MAX_UNITS ? 1 : 0;
+  a.dense_count = reinterpret_cast<uint32_t*>(ws + Lw.dense_count_off);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dtype == SV_BF16)

@@ -66,6 +66,7 @@ struct Args {
   const float* lenience;  // [B] or null (1): q(x) is multiplied by it in the acceptance test
   int sampler;            // 1: G == 0 and each "sequence" is one row to sample (no drafts)
   int K, L;               // multi-candidate verify: candidate sequences and their length
+  int ghist;              // shared-noise verify: gumbel_hist_kernel runs (filtered bf16 rows of 32K-131K values)
   int gfuse;              // shared-noise verify: the list kernel takes every sequence and finishes it
                           // (no per-(sequence, position) or finish launch follows)
   int kphase;             // multi-candidate verify: 0 every node; 1 nodes of classes of two or more

@@ -27,12 +27,14 @@
 #pragma once
 
 #include "sv_pair.h"
+#include "sv_phist.h"
 #include "sv_finish.h"
 
 namespace sv {
 
 constexpr int GUMBEL_NT = 512;
 constexpr int32_t GUMBEL_BAD_ROW = -2;
+constexpr int32_t GUMBEL_REDO = -3;   // gumbel_hist_kernel left the row to gumbel_kernel
 
 // Order-preserving 32-bit key of a float score (larger float -> larger key;
 // every non-NaN float maps above 0, so 0 means "no candidate").
@@ -146,6 +148,140 @@ __device__ __forceinline__ int32_t gumbel_row_block(const Args& a, PairSmem<NTP>
   return (bad || kmax <= Key<ET>::NEG_INF || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
 }
 
+// Rows that gumbel_hist_kernel takes (when the call launches it, a.ghist):
+// position j <= gamma_b of a sequence outside the list path with T > 0 and a
+// filter (top-k below V, or top-p), whose support the exact histogram gives.
+__device__ __forceinline__ bool gumbel_hist_takes(const Args& a, int b, int j) {
+  if (!a.ghist) return false;
+  const Mode sm = seq_mode(a, b);
+  if (j > sm.g) return false;
+  if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE) && !a.all_dense) return false;
+  const int k = a.topk ? a.topk[b] : 0;
+  return sm.T > 0.0f && sm.tp == sm.tp && ((k > 0 && k < a.V) || sm.tp < 1.0f);
+}
+
+// Position j of sequence b, a filtered bf16 row of at most PH_MAX_UNITS
+// 16-byte units, by the whole workgroup: the row's support from its exact
+// value histogram (one pass over the logits: the k-th largest value for
+// top-k, then the nucleus cut for top-p, as the verify's histogram kernel
+// finds them), then the lowest-id argmax of fl(z + fl(T g)) over the
+// support, reading logits and noise only in the units whose largest value
+// reaches the support's threshold.  Returns the sample, GUMBEL_BAD_ROW, or
+// GUMBEL_REDO when a 16-bit count overflowed (gumbel_kernel then takes the
+// row).  Workgroup-uniform.
+__device__ __forceinline__ int32_t gumbel_hist_row(const Args& a, PhSmem& s, int b, int j) {
+  using T = PT<uint16_t, true>;
+  const int G1 = a.G + 1;
+  const int V = a.V, NU = V / 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const Mode sm = seq_mode(a, b);
+  Mode m = sm;
+  m.mode = MODE_DENSE;
+  const int k = a.topk ? a.topk[b] : 0;
+  const uint4* gp = reinterpret_cast<const uint4*>(row_ptr<uint16_t>(a, b, true, j));
+  const __amdgpu_buffer_rsrc_t rp = ph_rsrc(gp, NU);
+  const float cT = LOG2E_F / m.T;
+  const float binv = 254.0f * cT / (float)(a.fixbits + 2);
+  RowStat st{};
+  const int bad = ph_row_pass(s, rp, NU, a.fixbits, cT, binv, k > 0 && k < V, true, V, m, k, st);
+  if (bad) return (bad & PH_BAD) ? GUMBEL_BAD_ROW : GUMBEL_REDO;
+  // The units that can hold an element of the support, in ascending order,
+  // in the histogram's memory (as the verify's histogram kernel lists them).
+  uint16_t* list = reinterpret_cast<uint16_t*>(s.hist);
+  uint32_t* lcnt = s.hist + PH_WORDS / 2;
+  uint32_t nd_bits = 0;
+#pragma unroll 1
+  for (int jj = 0; jj < PH_UPT; ++jj) {
+    const int ui = jj * PH_NT + (int)threadIdx.x;
+    const bool nd = ui < NU && (uint32_t)s.umax[ui] >= ph_bucket(st.zthr, s.uref[jj / PH_INFLIGHT][wave], binv);
+    const unsigned long long bal = __ballot(nd);
+    nd_bits |= nd ? 1u << jj : 0u;
+    if (lane == 0) lcnt[jj * PH_NW + wave] = (uint32_t)__popcll(bal);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t c4[4], sum4 = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      c4[x] = lcnt[4 * lane + x];
+      sum4 += c4[x];
+    }
+    const uint32_t inc = wave_incl_scan_dpp(sum4);
+    uint32_t run = inc - sum4;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      lcnt[4 * lane + x] = run;
+      run += c4[x];
+    }
+    if (lane == 63) s.bc[1] = inc;
+  }
+  __syncthreads();
+  const int nlist = (int)s.bc[1];
+#pragma unroll 1
+  for (int jj = 0; jj < PH_UPT; ++jj) {
+    const bool nd = (nd_bits >> jj) & 1u;
+    const unsigned long long bal = __ballot(nd);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (nd) list[lcnt[jj * PH_NW + wave] + below] = (uint16_t)(jj * PH_NT + (int)threadIdx.x);
+  }
+  __syncthreads();
+  // The argmax over the listed units: strictly greater keeps the first of
+  // equal scores in this thread's (ascending) order; the block takes the
+  // lowest id among the maxima.
+  const float* gn = a.noise + ((size_t)b * G1 + j) * (size_t)V;
+  const float Tv = m.T, zthr = st.zthr;
+  uint32_t bkey = 0, bidx = NONE, badn = 0;
+  for (int le = threadIdx.x; le < nlist; le += PH_NT) {
+    const int ui = list[le];
+    const uint4 u = ph_load_unit<BUF_NT>(rp, ui);
+    const float4* np4 = reinterpret_cast<const float4*>(gn + (size_t)ui * 8);
+    const float4 n0 = np4[0], n1 = np4[1];
+    const float nv[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+    T::each(u, [&](int e, uint32_t raw) {
+#pragma clang fp contract(off)
+      const float z = T::val(raw);
+      if (z >= zthr) {
+        badn |= fabsf(nv[e]) < INFINITY ? 0u : 1u;   // noise on the support only
+        const float tg = Tv * nv[e];
+        const float sc = z + tg;
+        const uint32_t sk = score_key(sc);
+        if (sc == sc && sk > bkey) {
+          bkey = sk;
+          bidx = (uint32_t)(ui * 8 + e);
+        }
+      }
+    });
+  }
+  const uint32_t mykey = bkey;
+  uint32_t dummy = 0;
+  pb_max3<PH_NT>(bkey, badn, dummy, s.red);
+  const uint32_t win = pb_min<PH_NT>(bkey != 0u && mykey == bkey ? bidx : NONE, s.red);
+  return (badn || win == NONE) ? GUMBEL_BAD_ROW : (int32_t)win;
+}
+
+// The rows gumbel_hist_takes, one workgroup per CU: workgroup w starts with
+// row w (sequence-major order) and then takes the next unstarted row from a
+// workspace counter (cleared by gumbel_finish_kernel); other rows are
+// skipped.
+__global__ __launch_bounds__(PH_NT) void gumbel_hist_kernel(Args a) {
+  extern __shared__ __align__(16) unsigned char gh_raw[];
+  PhSmem& s = *reinterpret_cast<PhSmem*>(gh_raw);
+  const int G1 = a.G + 1;
+  const uint32_t nrows = (uint32_t)a.B * (uint32_t)G1;
+  uint32_t t = blockIdx.x;
+  while (t < nrows) {
+    const int b = (int)(t / (uint32_t)G1), j = (int)(t - (uint32_t)b * (uint32_t)G1);
+    if (gumbel_hist_takes(a, b, j)) {   // workgroup-uniform
+      const int32_t tok = gumbel_hist_row(a, s, b, j);
+      if (threadIdx.x == 0) a.out_target[(size_t)b * G1 + j] = tok;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s.next_pair = gridDim.x + atomicAdd(&a.dense_count[2], 1u);
+    __syncthreads();
+    t = s.next_pair;
+  }
+}
+
 template <typename ET, int NTP, bool VECTOR>
 __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
   __shared__ PairSmem<NTP> s;
@@ -162,6 +298,8 @@ __global__ __launch_bounds__(NTP) void gumbel_kernel(Args a) {
     const Mode sm = seq_mode(a, b);
     if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE) && !a.all_dense) return;
   }
+  // Rows the histogram kernel took (unless a count overflowed there).
+  if (gumbel_hist_takes(a, b, j) && a.out_target[(size_t)b * G1 + j] != GUMBEL_REDO) return;
   const int32_t tok = gumbel_row_block<ET, NTP, VECTOR>(a, s, ps, b, j);
   if (threadIdx.x == 0) a.out_target[(size_t)b * G1 + j] = tok;
 }
@@ -492,6 +630,7 @@ __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x * 4 + wave;
   if (b >= a.B) return;
+  if (b == 0 && threadIdx.x == 0 && a.ghist) a.dense_count[2] = 0;   // gumbel_hist_kernel's row counter
   const int32_t* tgt = a.out_target + (size_t)b * (a.G + 1);
   gumbel_finish_wave(a, b, [&](int j) { return tgt[j]; });
 }

@@ -356,6 +356,88 @@ __device__ __forceinline__ void ph_extremes(PhSmem& s, uint32_t kmax2, uint32_t 
   __syncthreads();
 }
 
+// One streaming pass over a row (resource rr, NU units) into the histogram,
+// then the row's statistics (ph_stats): the count pass of pair_hist_one.
+// With record, each unit's bucket (ph_bucket) of its largest value and the
+// floors they start from are kept in s.umax / s.uref for a list of the units
+// that can reach the nucleus.  Returns ph_stats' result; ends with a block
+// barrier, after which the histogram may be reused.
+__device__ __forceinline__ int ph_row_pass(PhSmem& s, __amdgpu_buffer_rsrc_t rr, int NU, int fb, float cT, float binv,
+                                           bool filter_k, bool record, int V, const Mode& m, int k, RowStat& st) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  ph_clear(s);
+  __syncthreads();
+  uint32_t kmax2 = 0u, kmin2 = 0xFFFFFFFFu, skipped = 0, kf_first = 0xFFFFFFFFu;
+  for (int j0 = 0; j0 < PH_UPT; j0 += PH_INFLIGHT) {
+    uint4 u[PH_INFLIGHT];
+#pragma unroll
+    for (int r = 0; r < PH_INFLIGHT; ++r) u[r] = ph_load<0>(rr, j0 + r);
+    uint32_t umx[PH_INFLIGHT / 2];   // the units' largest keys, two per word
+    uint32_t bmin2 = 0xFFFFFFFFu;    // the batch's smallest keys
+#pragma unroll
+    for (int r = 0; r < PH_INFLIGHT; ++r) {
+      const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
+      uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+      if (ui < NU) {
+        ph_extremes_unit(u[r], mx, mn);
+        kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
+                                                                       __builtin_bit_cast(ph_u16x2, mx)));
+        bmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, bmin2),
+                                                                       __builtin_bit_cast(ph_u16x2, mn)));
+      }
+      const uint32_t m1 = max(mx & 0xFFFFu, mx >> 16);
+      umx[r >> 1] = (r & 1) ? umx[r >> 1] | (m1 << 16) : m1;
+    }
+    // The floor: the value (fb + 2) / c below the wavefront's running
+    // maximum, also the origin of the target units' buckets (in steps of
+    // 1/254 of that distance).
+    const uint32_t wmax = wave_max_dpp(max(kmax2 & 0xFFFFu, kmax2 >> 16));
+    float zf = -INFINITY;
+    if (wmax > Key<uint16_t>::NEG_INF && wmax < Key<uint16_t>::POS_INF)
+      zf = Key<uint16_t>::value(wmax) - (float)(fb + 2) / cT;
+    uint32_t kfloor = 0u;
+    if (!filter_k && zf > -INFINITY) {
+      // Smallest bf16 key whose value is at least zf.
+      const uint32_t bits = __float_as_uint(zf);
+      const uint32_t b16 = zf >= 0.0f ? (bits + 0xFFFFu) >> 16 : bits >> 16;
+      kfloor = Key<uint16_t>::of_bits(b16);
+    }
+    if (record) {
+      if (lane == 0) s.uref[j0 / PH_INFLIGHT][wave] = zf;
+#pragma unroll
+      for (int r = 0; r < PH_INFLIGHT; ++r) {
+        const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
+        const uint32_t m1 = (r & 1) ? umx[r >> 1] >> 16 : umx[r >> 1] & 0xFFFFu;
+        if (ui < NU) s.umax[ui] = (uint8_t)ph_bucket(Key<uint16_t>::value(m1), zf, binv);
+      }
+    }
+    kf_first = min(kf_first, kfloor);
+    kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
+                                                                   __builtin_bit_cast(ph_u16x2, bmin2)));
+#pragma unroll
+    for (int r = 0; r < PH_INFLIGHT; ++r)
+      if ((j0 + r) * PH_NT + (int)threadIdx.x < NU) ph_add_unit(s.hist, u[r], kfloor, skipped);
+  }
+  skipped = wave_reduce_dpp_u32(skipped, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+  if (lane == 0) {
+    s.red[2 * PH_NW + wave] = skipped;
+    s.red[4 * PH_NW + wave] = kf_first;
+  }
+  uint32_t kmax, kmin;
+  ph_extremes(s, kmax2, kmin2, kmax, kmin);   // its barriers also close the counting
+  skipped = 0;
+  uint32_t kcount_min = 0xFFFFFFFFu;
+  for (int x = 0; x < PH_NW; ++x) {
+    skipped += s.red[2 * PH_NW + x];
+    kcount_min = min(kcount_min, s.red[4 * PH_NW + x]);
+  }
+  RowStat r{};
+  const int bad = ph_stats(s, kmax, kmin, kcount_min, skipped, V, m, k, r);
+  st = r;
+  __syncthreads();   // the statistics' last histogram reads before the histogram is reused
+  return bad;
+}
+
 // One (sequence b, position i) pair by the whole workgroup.  Thread t's
 // units of a row are t + j * PH_NT, j < PH_UPT (tile j).
 __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSmem& s) {
@@ -389,78 +471,10 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
   // pass also notes the top byte of each unit's largest key.
   RowStat sq{INFINITY, 0.0f, 0.0f, 0.0f}, sp{};
   for (int row = resid ? 0 : 1; row < 2; ++row) {
-    const __amdgpu_buffer_rsrc_t rr = row == 0 ? rq : rp;
-    ph_clear(s);
-    __syncthreads();
-    uint32_t kmax2 = 0u, kmin2 = 0xFFFFFFFFu, skipped = 0, kf_first = 0xFFFFFFFFu;
-    for (int j0 = 0; j0 < PH_UPT; j0 += PH_INFLIGHT) {
-      uint4 u[PH_INFLIGHT];
-#pragma unroll
-      for (int r = 0; r < PH_INFLIGHT; ++r) u[r] = ph_load<0>(rr, j0 + r);
-      uint32_t umx[PH_INFLIGHT / 2];   // the units' largest keys, two per word
-      uint32_t bmin2 = 0xFFFFFFFFu;    // the batch's smallest keys
-#pragma unroll
-      for (int r = 0; r < PH_INFLIGHT; ++r) {
-        const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
-        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
-        if (ui < NU) {
-          ph_extremes_unit(u[r], mx, mn);
-          kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
-                                                                         __builtin_bit_cast(ph_u16x2, mx)));
-          bmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, bmin2),
-                                                                         __builtin_bit_cast(ph_u16x2, mn)));
-        }
-        const uint32_t m1 = max(mx & 0xFFFFu, mx >> 16);
-        umx[r >> 1] = (r & 1) ? umx[r >> 1] | (m1 << 16) : m1;
-      }
-      // The floor: the value (fb + 2) / c below the wavefront's running
-      // maximum, also the origin of the target units' buckets (in steps of
-      // 1/254 of that distance).
-      const uint32_t wmax = wave_max_dpp(max(kmax2 & 0xFFFFu, kmax2 >> 16));
-      float zf = -INFINITY;
-      if (wmax > Key<uint16_t>::NEG_INF && wmax < Key<uint16_t>::POS_INF)
-        zf = Key<uint16_t>::value(wmax) - (float)(fb + 2) / cT;
-      uint32_t kfloor = 0u;
-      if (!filter_k && zf > -INFINITY) {
-        // Smallest bf16 key whose value is at least zf.
-        const uint32_t bits = __float_as_uint(zf);
-        const uint32_t b16 = zf >= 0.0f ? (bits + 0xFFFFu) >> 16 : bits >> 16;
-        kfloor = Key<uint16_t>::of_bits(b16);
-      }
-      if (row == 1) {
-        if (lane == 0) s.uref[j0 / PH_INFLIGHT][wave] = zf;
-#pragma unroll
-        for (int r = 0; r < PH_INFLIGHT; ++r) {
-          const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
-          const uint32_t m1 = (r & 1) ? umx[r >> 1] >> 16 : umx[r >> 1] & 0xFFFFu;
-          if (ui < NU) s.umax[ui] = (uint8_t)ph_bucket(Key<uint16_t>::value(m1), zf, binv);
-        }
-      }
-      kf_first = min(kf_first, kfloor);
-      kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
-                                                                     __builtin_bit_cast(ph_u16x2, bmin2)));
-#pragma unroll
-      for (int r = 0; r < PH_INFLIGHT; ++r)
-        if ((j0 + r) * PH_NT + (int)threadIdx.x < NU) ph_add_unit(s.hist, u[r], kfloor, skipped);
-    }
-    skipped = wave_reduce_dpp_u32(skipped, 0u, [](uint32_t x, uint32_t y) { return x + y; });
-    if (lane == 0) {
-      s.red[2 * PH_NW + wave] = skipped;
-      s.red[4 * PH_NW + wave] = kf_first;
-    }
-    uint32_t kmax, kmin;
-    ph_extremes(s, kmax2, kmin2, kmax, kmin);   // its barriers also close the counting
-    skipped = 0;
-    uint32_t kcount_min = 0xFFFFFFFFu;
-    for (int x = 0; x < PH_NW; ++x) {
-      skipped += s.red[2 * PH_NW + x];
-      kcount_min = min(kcount_min, s.red[4 * PH_NW + x]);
-    }
     RowStat st{};
-    bad |= ph_stats(s, kmax, kmin, kcount_min, skipped, V, m, k, st);
+    bad |= ph_row_pass(s, row == 0 ? rq : rp, NU, fb, cT, binv, filter_k, row == 1, V, m, k, st);
     if (row == 0) sq = st;
     else sp = st;
-    __syncthreads();   // the statistics' last histogram reads before the next row clears it
     if (bad) break;
   }
   if (bad) {

@@ -253,3 +253,89 @@ def test_gumbel_no_dense_hint_demoted_lists():
     P[4, 2, ::2] = synth.f32_to_bf16_bits(np.float32(5.0))
     from speculative_sampling_verification_verify_amd import binding
     check_gumbel(_replace(gb, p_logits=P), "no-dense-hint-demoted", hints=binding.SV_HINT_NO_DENSE, calls=2)
+
+
+def _hist_batch(V, B, seed, T, k, tp, G=3):
+    """Zipf-shaped bf16 rows (the histogram kernel's range is 32K < V <= 131072)
+    with the given per-sequence temperature and filters."""
+    rng = np.random.default_rng(seed)
+    rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
+    zp = (2.5 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
+    noise = -np.log(-np.log(rng.random(size=(B, G + 1, V)))).astype(np.float32)
+    base = synth.make_gumbel_batch(3, B=2, V=64)
+    draft = np.argmax(zp[:, :G] + noise[:, :G], axis=2).astype(np.int32)
+    draft[::3, 1] = rng.integers(0, V, size=draft[::3, 1].shape)   # some disagreements
+    return synth.GumbelBatch(base.workload, synth.f32_to_bf16_bits(zp), noise, draft, np.full(B, G, np.int32),
+                             np.asarray(T, np.float32), np.asarray(k, np.int32), np.asarray(tp, np.float32), seed)
+
+
+@pytest.mark.parametrize("V", [32776, 65544, 131072])
+def test_gumbel_histogram_rows(V):
+    # Filtered dense rows above 32K values take the exact-histogram kernel:
+    # top-p at several temperatures, top-k above 512, both filters, top_p at
+    # 0 (the maximum's ties only), and one argmax and one top-k-64 sequence
+    # (the list path) beside them.
+    T = [0.3, 1.0, 3.0, 1.0, 0.7, 1.0, 1.3, 0.0, 1.0]
+    k = [0, 0, 0, 1000, 2000, 0, 700, 0, 64]
+    tp = [0.9, 0.5, 0.99, 1.0, 0.8, 0.0, 0.95, 1.0, 1.0]
+    gb = _hist_batch(V, len(T), 300 + V % 97, T, k, tp)
+    check_gumbel(gb, f"hist-rows-V{V}", calls=2)
+
+
+def test_gumbel_histogram_rows_invalid_and_overflow():
+    # NaN logits and NaN noise inside the support make the sequence invalid;
+    # NaN noise outside the support does not; a row with more than 65535 equal
+    # values overflows its 16-bit count and is left to the per-position
+    # kernel; padding rows beyond gamma_b are never read.
+    V, G = 131072, 3
+    T = [1.0] * 6
+    k = [0] * 6
+    tp = [0.9] * 6
+    gb = _hist_batch(V, 6, 911, T, k, tp, G=G)
+    P, N, gl = gb.p_logits.copy(), gb.noise.copy(), gb.gamma_len.copy()
+    P[0, 1, 77] = 0x7FC0                                   # NaN logit
+    top = int(np.argmax(oracle.decode_row(P[1, 2])))
+    N[1, 2, top] = np.nan                                  # NaN noise at the row's largest logit (in the support)
+    low = int(np.argmin(oracle.decode_row(P[2, 0])))
+    N[2, 0, low] = np.nan                                  # NaN noise at the smallest logit (outside the support)
+    P[3, 0, :70000] = synth.f32_to_bf16_bits(np.float32(-3.0))   # 70000 equal values: count overflow
+    gl[4] = 1
+    P[4, 2:] = 0x7FC0                                      # padding rows (positions 2, 3) never read
+    N[4, 2:] = np.nan
+    gb2 = _replace(gb, p_logits=P, noise=N, gamma_len=gl)
+    tok, n, tgt, ref = check_gumbel(gb2, "hist-invalid-overflow", calls=2)
+    assert n[0] == -1 and n[1] == -1 and ref.n[0] == -1 and ref.n[1] == -1
+    assert n[2] >= 0 and n[3] >= 0 and n[4] >= 0
+
+
+def test_gumbel_histogram_rows_all_dense_hint():
+    # The all-dense hint skips the select and list launches: top-k sequences of
+    # at most 512 (which break the promise) also go through the histogram
+    # kernel.
+    from speculative_sampling_verification_verify_amd import binding
+    T = [1.0, 0.8, 1.2, 1.0, 0.0]
+    k = [50, 0, 512, 0, 0]
+    tp = [1.0, 0.9, 0.7, 1.0, 1.0]
+    gb = _hist_batch(50000, len(T), 77, T, k, tp)
+    check_gumbel(gb, "hist-all-dense-hint", hints=binding.SV_HINT_ALL_DENSE, calls=2)
+
+
+def test_gumbel_histogram_rows_ties():
+    # Integer logits and integer noise above 32K values: many equal scores
+    # inside the support, split over the workgroup's threads; the lowest id
+    # must win.
+    rng = np.random.default_rng(21)
+    B, G, V = 6, 3, 40000
+    zp = rng.integers(-3, 4, size=(B, G + 1, V)).astype(np.float32)
+    noise = rng.integers(-1, 2, size=(B, G + 1, V)).astype(np.float32)
+    T = np.array([1.0, 2.0, 1.0, 0.5, 1.0, 3.0], np.float32)
+    k = np.array([0, 0, 1000, 0, 600, 0], np.int32)
+    tp = np.array([0.9, 0.6, 1.0, 0.95, 0.9, 0.3], np.float32)
+    draft = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    base = synth.make_gumbel_batch(3, B=2, V=64)
+    gb = synth.GumbelBatch(base.workload, synth.f32_to_bf16_bits(zp), noise, draft, np.full(B, G, np.int32),
+                           T, k, tp, 0)
+    ref = oracle.gumbel_verify_batch(gb.p_logits, gb.noise, gb.draft, gb.temperature, gb.top_k, gb.top_p,
+                                     gb.gamma_len)
+    gb.draft[:, :] = np.where(np.arange(G)[None, :] % 2 == 0, ref.target[:, :G], gb.draft)   # some matches
+    check_gumbel(gb, "hist-ties", exact_scores=True, calls=2)

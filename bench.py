@@ -38,6 +38,7 @@ PMC_SUMMARIES = {
     ("select_kernel", "B64-V128256-g4-topk50"): "select_kernel_B64_V128256_g4_topk50_pmc.txt",
     ("pair_kernel", "B32-V32000-g5-T0.8"): "pair_kernel_B32_V32000_g5_pmc.txt",
     ("pair_kernel", "tiny-fp32-V1000-g4"): "pair_kernel_B1000_V1000_g4_fp32_pmc.txt",
+    ("gumbel_hist_kernel", "B128-V128256-mixed-g1..8-topp0.9-gumbel"): "gumbel_hist_kernel_B128_V128256_mixed_topp_pmc.txt",
 }
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
 ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
@@ -52,6 +53,8 @@ KERNEL_SOURCES = {
     "select_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_wave.h"),
     "pair_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h"),
     "pair_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h"),
+    "gumbel_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h", "sv_finish.h",
+                           "sv_gumbel.h"),
 }
 
 

@@ -60,6 +60,7 @@ struct PhSmem {
   uint32_t bc[8];
   double bd[2];
   uint32_t next_pair;
+  uint32_t spare[64];                       // per-lane targets of the count pass's below-floor atomics
 };
 
 // Order-preserving 16-bit keys of two bf16 patterns at once (+0 and -0 share
@@ -75,8 +76,6 @@ __device__ __forceinline__ void ph_count(uint32_t* hist, uint32_t key) {
   atomicAdd(&hist[key >> 1], 1u << ((key & 1u) << 4));
 }
 
-// Adds one 16-byte unit (8 bf16) to the histogram and to the running key
-// extremes (packed: both halves at once).
 // The packed key extremes of one 16-byte unit (8 bf16), folded into kmax2 /
 // kmin2 (both halves at once).
 __device__ __forceinline__ void ph_extremes_unit(const uint4& u, uint32_t& kmax2, uint32_t& kmin2) {
@@ -90,18 +89,35 @@ __device__ __forceinline__ void ph_extremes_unit(const uint4& u, uint32_t& kmax2
                                                                    __builtin_bit_cast(ph_u16x2, k2)));
   }
 }
-// Counts the unit's elements whose key is at least kfloor; the others are
-// added to `skipped`.
-__device__ __forceinline__ void ph_add_unit(uint32_t* hist, const uint4& u, uint32_t kfloor, uint32_t& skipped) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// The same, replacing the unit's patterns by their keys (two per word), so
+// the count that follows need not form them again.
+__device__ __forceinline__ void ph_keys_extremes_unit(uint4& u, uint32_t& kmax2, uint32_t& kmin2) {
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t k2 = ph_keys2(w[j]);
-    const uint32_t klo = k2 & 0xFFFFu, khi = k2 >> 16;
-    if (klo >= kfloor) ph_count(hist, klo);
-    else ++skipped;
-    if (khi >= kfloor) ph_count(hist, khi);
-    else ++skipped;
+    w[j] = ph_keys2(w[j]);
+    kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
+                                                                   __builtin_bit_cast(ph_u16x2, w[j])));
+    kmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, kmin2),
+                                                                   __builtin_bit_cast(ph_u16x2, w[j])));
+  }
+  u = make_uint4(w[0], w[1], w[2], w[3]);
+}
+// Counts the keys of a unit (ph_keys_extremes_unit's output) that are at
+// least kfloor, with no branch: a key below the floor adds to the lane's own
+// spare word instead (no two lanes share one, so those atomics never meet),
+// and the wavefront's number of such keys is added to skipped
+// (wavefront-uniform).
+__device__ __forceinline__ void ph_add_keys(uint32_t* hist, uint32_t* spare, const uint4& kk, uint32_t kfloor,
+                                            uint32_t& skipped) {
+  const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t klo = w[j] & 0xFFFFu, khi = w[j] >> 16;
+    const bool glo = klo >= kfloor, ghi = khi >= kfloor;
+    skipped += (uint32_t)__popcll(__ballot(!glo)) + (uint32_t)__popcll(__ballot(!ghi));
+    atomicAdd(glo ? &hist[klo >> 1] : spare, 1u << ((klo & 1u) << 4));
+    atomicAdd(ghi ? &hist[khi >> 1] : spare, 1u << ((khi & 1u) << 4));
   }
 }
 // The largest key of a unit (its max over the 8 elements).
@@ -379,7 +395,7 @@ __device__ __forceinline__ int ph_row_pass(PhSmem& s, __amdgpu_buffer_rsrc_t rr,
       const int ui = (j0 + r) * PH_NT + (int)threadIdx.x;
       uint32_t mx = 0u, mn = 0xFFFFFFFFu;
       if (ui < NU) {
-        ph_extremes_unit(u[r], mx, mn);
+        ph_keys_extremes_unit(u[r], mx, mn);
         kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ph_u16x2, kmax2),
                                                                        __builtin_bit_cast(ph_u16x2, mx)));
         bmin2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ph_u16x2, bmin2),
@@ -416,9 +432,9 @@ __device__ __forceinline__ int ph_row_pass(PhSmem& s, __amdgpu_buffer_rsrc_t rr,
                                                                    __builtin_bit_cast(ph_u16x2, bmin2)));
 #pragma unroll
     for (int r = 0; r < PH_INFLIGHT; ++r)
-      if ((j0 + r) * PH_NT + (int)threadIdx.x < NU) ph_add_unit(s.hist, u[r], kfloor, skipped);
+      if ((j0 + r) * PH_NT + (int)threadIdx.x < NU) ph_add_keys(s.hist, &s.spare[lane], u[r], kfloor, skipped);
   }
-  skipped = wave_reduce_dpp_u32(skipped, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+  skipped = (uint32_t)__builtin_amdgcn_readfirstlane((int)skipped);
   if (lane == 0) {
     s.red[2 * PH_NW + wave] = skipped;
     s.red[4 * PH_NW + wave] = kf_first;

@@ -251,9 +251,6 @@ static hipError_t device_setup() {
   if ((e = set_lds_limits<uint16_t, false>()) != hipSuccess) return e;
   if ((e = set_lds_limits<float, true>()) != hipSuccess) return e;
   if ((e = set_lds_limits<float, false>()) != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pair_hist_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)sizeof(PhSmem));
-  if (e != hipSuccess) return e;
   {
     const void* gk[4] = {reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t, true>),
                          reinterpret_cast<const void*>(&gumbel_list_kernel<uint16_t, false>),
@@ -264,9 +261,6 @@ static hipError_t device_setup() {
       if (e != hipSuccess) return e;
     }
   }
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gumbel_hist_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)sizeof(PhSmem));
-  if (e != hipSuccess) return e;
   g_setup_done[dev] = true;
   return hipSuccess;
 }
@@ -310,7 +304,7 @@ static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hip
     if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
     if (hist) pv = 0;
     switch (pv) {
-      case 0: hipLaunchKernelGGL(pair_hist_kernel, grid, dim3(PH_NT), sizeof(PhSmem), st, a); break;
+      case 0: hipLaunchKernelGGL(pair_hist_kernel, grid, dim3(PH_NT), 0, st, a); break;
       case 64: hipLaunchKernelGGL((pair_kernel<ET, 64, VECTOR, true>), grid, dim3(64), plds, st, a); break;
       case 256: hipLaunchKernelGGL((pair_kernel<ET, 256, VECTOR, true>), grid, dim3(256), plds, st, a); break;
       case 1024: hipLaunchKernelGGL((pair_kernel<ET, 1024, VECTOR, true>), grid, dim3(1024), plds, st, a); break;
@@ -634,8 +628,7 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
   if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
   if (a.ghist) {
     const long long nrows = (long long)a.B * (a.G + 1);
-    hipLaunchKernelGGL(gumbel_hist_kernel, dim3((unsigned)(nrows < 256 ? nrows : 256)), dim3(PH_NT), sizeof(PhSmem),
-                       st, a);
+    hipLaunchKernelGGL(gumbel_hist_kernel, dim3((unsigned)(nrows < 256 ? nrows : 256)), dim3(PH_NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((gumbel_kernel<ET, GUMBEL_NT, VECTOR>), dim3((unsigned)((long long)a.B * (a.G + 1))),

@@ -264,8 +264,7 @@ __device__ __forceinline__ int32_t gumbel_hist_row(const Args& a, PhSmem& s, int
 // workspace counter (cleared by gumbel_finish_kernel); other rows are
 // skipped.
 __global__ __launch_bounds__(PH_NT) void gumbel_hist_kernel(Args a) {
-  extern __shared__ __align__(16) unsigned char gh_raw[];
-  PhSmem& s = *reinterpret_cast<PhSmem*>(gh_raw);
+  __shared__ __align__(16) PhSmem s;   // static, as in pair_hist_kernel
   const int G1 = a.G + 1;
   const uint32_t nrows = (uint32_t)a.B * (uint32_t)G1;
   uint32_t t = blockIdx.x;

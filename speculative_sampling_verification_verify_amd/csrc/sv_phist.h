@@ -116,8 +116,11 @@ __device__ __forceinline__ void ph_add_keys(uint32_t* hist, uint32_t* spare, con
     const uint32_t klo = w[j] & 0xFFFFu, khi = w[j] >> 16;
     const bool glo = klo >= kfloor, ghi = khi >= kfloor;
     skipped += (uint32_t)__popcll(__ballot(!glo)) + (uint32_t)__popcll(__ballot(!ghi));
-    atomicAdd(glo ? &hist[klo >> 1] : spare, 1u << ((klo & 1u) << 4));
-    atomicAdd(ghi ? &hist[khi >> 1] : spare, 1u << ((khi & 1u) << 4));
+    // Word key >> 1 of each key (bit-field extracts), and the count's half
+    // (key & 1) as a shift of 16, formed for both keys at once.
+    const uint32_t sh = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ph_u16x2, w[j]) << (unsigned short)4);
+    atomicAdd(glo ? &hist[__builtin_amdgcn_ubfe(w[j], 1u, 15u)] : spare, 1u << (sh & 16u));
+    atomicAdd(ghi ? &hist[__builtin_amdgcn_ubfe(w[j], 17u, 15u)] : spare, 1u << ((sh >> 16) & 16u));
   }
 }
 // The largest key of a unit (its max over the 8 elements).
@@ -698,8 +701,9 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
 // work counter of the streamed pair variant: workgroup w starts with pair w,
 // and a workgroup that has finished takes the next unstarted pair.
 __global__ __launch_bounds__(PH_NT) void pair_hist_kernel(Args a) {
-  extern __shared__ __align__(16) unsigned char ph_raw[];
-  PhSmem& s = *reinterpret_cast<PhSmem*>(ph_raw);
+  // Static, so the histogram's LDS addresses are constants the count pass
+  // need not add.
+  __shared__ __align__(16) PhSmem s;
   const int G1 = a.G + 1;
   const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
   const bool direct = a.all_dense != 0;

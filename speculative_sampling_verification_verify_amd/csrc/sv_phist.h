@@ -61,6 +61,7 @@ struct PhSmem {
   double bd[2];
   uint32_t next_pair;
   uint32_t spare[64];                       // per-lane targets of the count pass's below-floor atomics
+  uint32_t rx[2];                           // thread 0's draft token and its two logits' patterns
 };
 
 // Order-preserving 16-bit keys of two bf16 patterns at once (+0 and -0 share
@@ -478,6 +479,20 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
   const float binv = 254.0f * cT / (float)(fb + 2);   // buckets per unit of value
   const bool filter_k = k > 0 && k < V;
   int bad = 0;
+  // The draft token and the patterns of its two logits, for the record
+  // written at the end: fetched now, so their two dependent round trips
+  // overlap the other wavefronts' row passes instead of ending the pair.
+  if (threadIdx.x == 0) {
+    const int x = resid ? a.draft[(size_t)b * a.G + i] : -1;
+    uint32_t raw = 0u;
+    if (x >= 0 && x < V) {
+      const uint16_t* pr = reinterpret_cast<const uint16_t*>(gp);
+      const uint16_t* qr = reinterpret_cast<const uint16_t*>(gq);
+      raw = (uint32_t)pr[x] | ((uint32_t)qr[x] << 16);
+    }
+    s.rx[0] = (uint32_t)x;
+    s.rx[1] = raw;
+  }
 
   // Row 0, the draft row, then row 1, the target row: one streaming pass
   // each, counting the elements at or above a floor into the histogram.
@@ -681,13 +696,11 @@ __device__ __forceinline__ void pair_hist_one(const Args& a, int b, int i, PhSme
     al = tot;
   }
   if (threadIdx.x == 0) {
-    const int x = resid ? a.draft[(size_t)b * a.G + i] : -1;
+    const int x = (int)s.rx[0];
     double pxv = 0.0, qxv = 0.0;
     if (x >= 0 && x < V) {
-      const uint16_t* pr = reinterpret_cast<const uint16_t*>(gp);
-      const uint16_t* qr = reinterpret_cast<const uint16_t*>(gq);
-      pxv = (double)pprob(sp, T::val(pr[x]));
-      qxv = (double)pprob(sq, T::val(qr[x]));
+      pxv = (double)pprob(sp, T::val(s.rx[1] & 0xFFFFu));
+      qxv = (double)pprob(sq, T::val(s.rx[1] >> 16));
     }
     rec->px = pxv;
     rec->qx = qxv;

@@ -67,10 +67,14 @@ struct PhSmem {
 // Order-preserving 16-bit keys of two bf16 patterns at once (+0 and -0 share
 // a key; -inf is 0x0080; NaN and +inf fall outside [0x0080, 0xFF7F]).
 typedef unsigned short ph_u16x2 __attribute__((ext_vector_type(2)));
+typedef short ph_i16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t ph_keys2(uint32_t w) {
   const ph_u16x2 h = __builtin_bit_cast(ph_u16x2, w);
-  const ph_u16x2 sgn = h >> (unsigned short)15;
-  const ph_u16x2 key = (h ^ (ph_u16x2)(sgn * (unsigned short)0x7FFF + (unsigned short)0x8000)) + sgn;
+  // m = 0xFFFF for a negative pattern, else 0: a negative pattern's key is
+  // its complement plus one (so -0 meets +0), a positive one's its pattern
+  // with the top bit set.
+  const ph_u16x2 m = __builtin_bit_cast(ph_u16x2, __builtin_bit_cast(ph_i16x2, w) >> (short)15);
+  const ph_u16x2 key = (h ^ (m | (unsigned short)0x8000)) - m;
   return __builtin_bit_cast(uint32_t, key);
 }
 __device__ __forceinline__ void ph_count(uint32_t* hist, uint32_t key) {

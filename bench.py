@@ -34,7 +34,7 @@ METRIC = "spec-verify rows/sec + achieved HBM GB/s vs peak at B=256,V=152064,γ=
 # rocprofv3 HBM-counter summaries, by (kernel, workload name).
 PMC_SUMMARIES = {
     ("select_kernel", "B256-V152064-g7-T0.7-topk64"): "select_kernel_B256_V152064_g7_pmc.txt",
-    ("pair_hist_kernel", "B128-V128256-mixed-g1..8-topp0.9"): "pair_hist_kernel_B128_V128256_mixed_topp_pmc.txt",
+    ("mixed_hist_kernel", "B128-V128256-mixed-g1..8-topp0.9"): "mixed_hist_kernel_B128_V128256_mixed_topp_pmc.txt",
     ("select_kernel", "B64-V128256-g4-topk50"): "select_kernel_B64_V128256_g4_topk50_pmc.txt",
     ("pair_kernel", "B32-V32000-g5-T0.8"): "pair_kernel_B32_V32000_g5_pmc.txt",
     ("pair_kernel", "tiny-fp32-V1000-g4"): "pair_kernel_B1000_V1000_g4_fp32_pmc.txt",
@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "select_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_wave.h"),
     "pair_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h"),
     "pair_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h"),
+    "mixed_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h", "sv_wave.h"),
     "gumbel_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h", "sv_finish.h",
                            "sv_gumbel.h"),
 }
@@ -225,14 +226,16 @@ def timed_calls(step, kern: int, n: int, every: int = EVENT_EVERY):
     return wall, np.array([a.elapsed_time(b) for a, b in evs])
 
 
-def pair_kernel_name(bt) -> str:
+def pair_kernel_name(bt, mixed: bool = False) -> str:
     """The kernel of the pair stage for this batch's rows: bf16 rows longer
     than the 64 KB held in LDS, of whole 16-byte units and at most 16384 of
-    them, are counted into a histogram (pair_hist_kernel); other dense rows
-    take pair_kernel (the library makes the same choice)."""
+    them, are counted into a histogram (pair_hist_kernel; mixed_hist_kernel,
+    which also streams the select's rows, when the call has both kinds of
+    sequence); other dense rows take pair_kernel (the library makes the same
+    choice)."""
     V = bt.V
     if bt.p_logits.dtype == np.uint16 and V * 2 > 65536 and V % 8 == 0 and V // 8 <= 16384:
-        return "pair_hist_kernel"
+        return "mixed_hist_kernel" if mixed else "pair_hist_kernel"
     return "pair_kernel"
 
 
@@ -626,10 +629,13 @@ def main():
         ver(Pj, Qj, draft, u, temp, topk, topp, gl)
 
     # The kernel that reads most of the logit bytes: the streaming select for
-    # top-k / argmax sequences, the pair kernel for dense ones.
-    kernel = binding.SV_KERNEL_PAIR if pair_bytes > sel_bytes else binding.SV_KERNEL_SELECT
-    kname = "select_kernel" if kernel == binding.SV_KERNEL_SELECT else pair_kernel_name(bt)
-    kbytes = max(sel_bytes, pair_bytes)
+    # top-k / argmax sequences, the pair kernel for dense ones; with both kinds
+    # on the histogram variant, the pair-stage kernel that reads them all (the
+    # select launch then only lists the dense pairs).
+    mixed = sel_bytes > 0 and pair_bytes > 0 and pair_kernel_name(bt) == "pair_hist_kernel"
+    kernel = binding.SV_KERNEL_PAIR if pair_bytes > sel_bytes or mixed else binding.SV_KERNEL_SELECT
+    kname = "select_kernel" if kernel == binding.SV_KERNEL_SELECT else pair_kernel_name(bt, mixed)
+    kbytes = sel_bytes + pair_bytes if mixed else max(sel_bytes, pair_bytes)
 
     for j in range(args.warmup):
         step(j)
@@ -646,8 +652,8 @@ def main():
         check = output_check(bt, ref, ver.tokens.cpu().numpy(), n_acc, alpha, ver.pq.cpu().numpy())
     # Outside the timed region: the other kernels' durations, for the record.
     other_us = {}
-    for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel"), (binding.SV_KERNEL_PAIR, pair_kernel_name(bt)),
-                       (binding.SV_KERNEL_FINISH, "finish_kernel")):
+    for kern, name in ((binding.SV_KERNEL_SELECT, "select_kernel (dense-pair listing only)" if mixed else "select_kernel"),
+                       (binding.SV_KERNEL_PAIR, pair_kernel_name(bt, mixed)), (binding.SV_KERNEL_FINISH, "finish_kernel")):
         if (kern == binding.SV_KERNEL_PAIR and hints & binding.SV_HINT_NO_DENSE) or \
                 (kern == binding.SV_KERNEL_SELECT and hints & binding.SV_HINT_ALL_DENSE):
             other_us[name] = None      # not launched

@@ -188,7 +188,7 @@ static Layout layout(int B, int G, int RS, const Plan& p, int S = 0) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L.seq_flags_off = 0;
   L.dense_count_off = (size_t)B * 4;
-  L.counters_bytes = up(L.dense_count_off + 3 * 4);
+  L.counters_bytes = up(L.dense_count_off + 4 * 4);
   L.pos_off = L.counters_bytes;
   L.dense_list_off = up(L.pos_off + (size_t)B * (G + 1) * sizeof(PosRec));
   L.counts_off = up(L.dense_list_off + (size_t)B * (G + 1) * 4);
@@ -265,18 +265,42 @@ static hipError_t device_setup() {
   return hipSuccess;
 }
 
+#ifndef SV_MIXED
+#define SV_MIXED 1
+#endif
 template <typename ET, bool VECTOR>
 static hipError_t launch_pair(const Args& a, long long grid, size_t fin_lds, hipStream_t st) {
   hipError_t e = device_setup();
   if (e != hipSuccess) return e;
+  // Dense pairs on the histogram variant beside streamed rows: the select
+  // units run inside the pair launch (mixed_hist_kernel), and the select
+  // launch only lists the dense pairs.
+  bool mixed = false;
+  if constexpr (VECTOR && sizeof(ET) == 2) {
+    if (SV_MIXED && a.pair && a.split_s <= 1 && !a.all_dense) {
+      size_t plds = 0;
+      mixed = pair_variant(a.V, SV_BF16, true, &plds) == -1024 && (long long)a.V / 8 <= PH_MAX_UNITS;
+    }
+  }
   if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
   if (!a.all_dense) {
-    hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
+    if (mixed) {
+      Args al = a;
+      al.sel_blocks = 0;
+      hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)(grid - a.sel_blocks)), dim3(K1_NT), 0, st, al);
+    } else {
+      hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)grid), dim3(K1_NT), 0, st, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
-  if (a.pair && a.split_s > 1) {
+  if (mixed) {
+    if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(mixed_hist_kernel, dim3(256), dim3(PH_NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = stage_mark(SV_KERNEL_PAIR, false, st)) != hipSuccess) return e;
+  } else if (a.pair && a.split_s > 1) {
     const long long npairs = (long long)a.B * (a.G + 1);
     const dim3 g1((unsigned)(npairs * a.split_s));
     if ((e = stage_mark(SV_KERNEL_PAIR, true, st)) != hipSuccess) return e;

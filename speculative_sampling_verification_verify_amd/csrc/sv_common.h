@@ -50,8 +50,9 @@ struct Args {
   int32_t* counts;        // [R][NP] survivors per (row, part)
   uint2* lists;           // [R][NP][SEG] (key, vocabulary id)
   PosRec* pos;            // [B][G+1] pair-resident results
-  uint32_t* dense_count;  // [3]: draft pairs listed from the front of dense_list, bonus positions listed
-                          // from its back, the pair kernel's work queue; cleared by the finisher
+  uint32_t* dense_count;  // [4]: draft pairs listed from the front of dense_list, bonus positions listed
+                          // from its back, the pair kernel's work queue, the mixed kernel's select
+                          // groups; cleared by the finisher
   int32_t* dense_list;    // [B * (G+1)] pair ids b * (G+1) + i of the dense sequences
   long long sel_blocks;   // workgroups of the select kernel that stream rows; the rest list dense pairs
   int pair;               // 1 when the pair-resident kernel runs for the dense sequences

@@ -1074,6 +1074,7 @@ __device__ __forceinline__ void finish_from_pairs_wave(const Args& a, int b, con
       a.dense_count[0] = 0;
       a.dense_count[1] = 0;
       a.dense_count[2] = 0;
+      a.dense_count[3] = 0;
     }
   }
 }
@@ -1247,6 +1248,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
         a.dense_count[0] = 0;
         a.dense_count[1] = 0;
         a.dense_count[2] = 0;
+        a.dense_count[3] = 0;
       }
     }
     return;
@@ -1424,6 +1426,7 @@ __device__ __forceinline__ void finish_sequence(const Args& a, FinSmem& s, int b
       a.dense_count[0] = 0;
       a.dense_count[1] = 0;
       a.dense_count[2] = 0;
+      a.dense_count[3] = 0;
     }
   }
   (void)lane;

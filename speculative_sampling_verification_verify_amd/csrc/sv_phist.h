@@ -35,6 +35,7 @@
 #pragma once
 
 #include "sv_pair.h"
+#include "sv_wave.h"
 
 namespace sv {
 
@@ -745,6 +746,55 @@ __global__ __launch_bounds__(PH_NT) void pair_hist_kernel(Args a) {
     if (threadIdx.x == 0) s.next_pair = gridDim.x + atomicAdd(&a.dense_count[2], 1u);
     __syncthreads();
     t = s.next_pair;
+  }
+}
+
+// Calls with both dense and streamed (top-k, argmax) sequences on this
+// variant: the select units and the dense pairs in one launch, after a
+// launch that only lists the dense pairs.  One workgroup per CU first takes
+// groups of PH_NW consecutive select units (a wavefront each) from a
+// workspace counter, then dense pairs from the pair counter, every one
+// claimed.  So the CUs whose groups hold streamed rows (a few, since a
+// group covers consecutive rows of one or two sequences) stream them while
+// the others start on the pairs, and the pairs' tail no longer waits for a
+// separate select launch.  Both counters are cleared by the finisher.
+__global__ __launch_bounds__(PH_NT) void mixed_hist_kernel(Args a) {
+  __shared__ __align__(16) union {
+    PhSmem ph;
+    WaveSmem w[PH_NW];
+  } sm;
+  __shared__ uint32_t claim;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const long long units = (long long)a.B * a.RS * a.NP;
+  const long long ngroups = (units + PH_NW - 1) / PH_NW;
+  for (;;) {
+    __syncthreads();   // every wavefront has read the last claim
+    if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[3], 1u);
+    __syncthreads();
+    const uint32_t g = claim;
+    if ((long long)g >= ngroups) break;
+    select_unit<uint16_t, true>(a, (long long)g * PH_NW + wave, sm.w[wave]);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  const int G1 = a.G + 1;
+  const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
+  const uint32_t nf = min(a.dense_count[0], npairs);
+  const uint32_t nd = min(nf + a.dense_count[1], npairs);
+  __syncthreads();   // the select units' LDS, and the last claim, are done with
+  if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[2], 1u);
+  __syncthreads();
+  uint32_t t = claim;
+  while (t < nd) {
+    const uint32_t idx = t < nf ? t : npairs - 1u - (t - nf);
+    const int pid = a.dense_list[idx];
+    if (pid >= 0 && (uint32_t)pid < npairs) {
+      const int b = pid / G1;
+      pair_hist_one(a, b, pid - b * G1, sm.ph);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[2], 1u);
+    __syncthreads();
+    t = claim;
   }
 }
 

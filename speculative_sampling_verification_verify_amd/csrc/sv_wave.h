@@ -655,18 +655,13 @@ __device__ __forceinline__ void list_dense_pairs(const Args& a, long long blk) {
   if (cb) a.dense_list[npairs - 1u - (baseb + inb - 1u)] = b * G1 + g;
 }
 
+// One streaming unit (logit row, row part) by the calling wavefront, with
+// its LDS w; units of sequences that are neither top-k nor argmax, and
+// padding rows, return at once.
 template <typename ET, bool VECTOR>
-__global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void select_kernel(Args a) {
-  __shared__ WaveSmem smem[K1_WAVES];
-  if ((long long)blockIdx.x >= a.sel_blocks) {
-    list_dense_pairs(a, (long long)blockIdx.x - a.sel_blocks);
-    return;
-  }
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+__device__ __forceinline__ void select_unit(const Args& a, long long unit, WaveSmem& w) {
   const int lane = threadIdx.x & 63;
-  WaveSmem& w = smem[wave];
   const int RS = a.RS;
-  const long long unit = (long long)blockIdx.x * K1_WAVES + wave;
   const long long rowid_ll = unit / a.NP;
   if (rowid_ll >= (long long)a.B * RS) return;
   const int rowid = (int)rowid_ll;
@@ -697,6 +692,17 @@ __global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) v
   } else if (lane == 0) {
     *cnt = 0;
   }
+}
+
+template <typename ET, bool VECTOR>
+__global__ __launch_bounds__(K1_NT) __attribute__((amdgpu_waves_per_eu(4, 8))) void select_kernel(Args a) {
+  __shared__ WaveSmem smem[K1_WAVES];
+  if ((long long)blockIdx.x >= a.sel_blocks) {
+    list_dense_pairs(a, (long long)blockIdx.x - a.sel_blocks);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  select_unit<ET, VECTOR>(a, (long long)blockIdx.x * K1_WAVES + wave, smem[wave]);
 }
 
 }  // namespace sv

@@ -38,7 +38,7 @@ PMC_SUMMARIES = {
     ("select_kernel", "B64-V128256-g4-topk50"): "select_kernel_B64_V128256_g4_topk50_pmc.txt",
     ("pair_kernel", "B32-V32000-g5-T0.8"): "pair_kernel_B32_V32000_g5_pmc.txt",
     ("pair_kernel", "tiny-fp32-V1000-g4"): "pair_kernel_B1000_V1000_g4_fp32_pmc.txt",
-    ("gumbel_hist_kernel", "B128-V128256-mixed-g1..8-topp0.9-gumbel"): "gumbel_hist_kernel_B128_V128256_mixed_topp_pmc.txt",
+    ("gumbel_mixed_kernel", "B128-V128256-mixed-g1..8-topp0.9-gumbel"): "gumbel_mixed_kernel_B128_V128256_mixed_topp_pmc.txt",
 }
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_verify_amd", "csrc")
 ROTATE_BYTES = 768 << 20     # rotate input copies until this many bytes are in flight
@@ -56,6 +56,8 @@ KERNEL_SOURCES = {
     "mixed_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h", "sv_wave.h"),
     "gumbel_hist_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h", "sv_finish.h",
                            "sv_gumbel.h"),
+    "gumbel_mixed_kernel": ("spec_verify.hip", "sv_common.h", "sv_device.h", "sv_pair.h", "sv_phist.h", "sv_finish.h",
+                            "sv_gumbel.h", "sv_wave.h"),
 }
 
 
@@ -339,12 +341,18 @@ def main_gumbel(args):
         step(j)
     torch.cuda.synchronize()
     K = args.steps
-    kern = binding.SV_KERNEL_SELECT if sel_bytes >= dense_bytes else binding.SV_KERNEL_GUMBEL
     # The dense stage is the histogram kernel for filtered bf16 rows of 32K-131K
-    # values (16-byte aligned), else the per-(sequence, position) kernel.
+    # values (16-byte aligned), else the per-(sequence, position) kernel.  With
+    # both kinds of sequence on the histogram rows (no hint), one launch,
+    # gumbel_mixed_kernel, streams the select's rows and takes the histogram
+    # rows: it reads both kinds of bytes.
     hist_rows = dtype_name == "bf16" and 32768 < gb.V <= 131072 and gb.V % 8 == 0
+    gmixed = hist_rows and ghints == 0
+    kern = binding.SV_KERNEL_SELECT if sel_bytes >= dense_bytes and not gmixed else binding.SV_KERNEL_GUMBEL
     kname = ("select_kernel" if kern == binding.SV_KERNEL_SELECT
-             else ("gumbel_hist_kernel" if hist_rows else "gumbel_kernel"))
+             else ("gumbel_mixed_kernel" if gmixed else ("gumbel_hist_kernel" if hist_rows else "gumbel_kernel")))
+    if gmixed:
+        kbytes = sel_bytes + dense_bytes
     wall, k_ms = timed_calls(step, kern, K)
     ms_per_step = wall * 1e3 / K
     n_acc = ver.n_accepted.cpu().numpy()

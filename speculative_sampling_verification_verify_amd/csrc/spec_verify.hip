@@ -631,13 +631,21 @@ template <typename ET, bool VECTOR>
 static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t st) {
   hipError_t e = device_setup();
   if (e != hipSuccess) return e;
-  // 1. Streaming select over the target rows of argmax / top-k sequences.
-  if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
-  if (!a.all_dense) {
-    hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)sel_grid), dim3(K1_NT), 0, st, a);
+  // 1. Streaming select over the target rows of argmax / top-k sequences
+  //    (with a.gmix, in one launch with the histogram rows).
+  if (a.gmix) {
+    if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(gumbel_mixed_kernel, dim3(256), dim3(PH_NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = stage_mark(SV_KERNEL_GUMBEL, false, st)) != hipSuccess) return e;
+  } else {
+    if ((e = stage_mark(SV_KERNEL_SELECT, true, st)) != hipSuccess) return e;
+    if (!a.all_dense) {
+      hipLaunchKernelGGL((select_kernel<ET, VECTOR>), dim3((unsigned)sel_grid), dim3(K1_NT), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   }
-  if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   // 2. Their per-position argmax from the survivor lists (with a.gfuse,
   //    every sequence's rows and its outputs: the call ends here).
   if (!a.all_dense) {
@@ -649,8 +657,8 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
   // 3. Dense and demoted sequences: filtered bf16 rows of 32K-131K values by
   //    the histogram kernel (one workgroup per CU), the rest one workgroup
   //    per (sequence, position).
-  if ((e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
-  if (a.ghist) {
+  if (!a.gmix && (e = stage_mark(SV_KERNEL_GUMBEL, true, st)) != hipSuccess) return e;
+  if (a.ghist && !a.gmix) {
     const long long nrows = (long long)a.B * (a.G + 1);
     hipLaunchKernelGGL(gumbel_hist_kernel, dim3((unsigned)(nrows < 256 ? nrows : 256)), dim3(PH_NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -659,7 +667,7 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
                      dim3(GUMBEL_NT), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = stage_mark(SV_KERNEL_GUMBEL, false, st)) != hipSuccess) return e;
+  if (!a.gmix && (e = stage_mark(SV_KERNEL_GUMBEL, false, st)) != hipSuccess) return e;
   // 4. The first disagreement and the outputs.
   hipLaunchKernelGGL(gumbel_finish_kernel, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
@@ -726,6 +734,9 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   // Filtered bf16 rows too long for one pass over the row to give their
   // support cheaply: the exact histogram kernel.
   a.ghist = !a.gfuse && dtype == SV_BF16 && vector_ok && V > 32768 && V / 8 <= PH_MAX_UNITS ? 1 : 0;
+  // With a list path beside it, the select units run in the histogram rows'
+  // launch.
+  a.gmix = SV_MIXED && a.ghist && !a.all_dense ? 1 : 0;
   a.dense_count = reinterpret_cast<uint32_t*>(ws + Lw.dense_count_off);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;

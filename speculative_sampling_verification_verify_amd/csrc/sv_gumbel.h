@@ -155,7 +155,10 @@ __device__ __forceinline__ bool gumbel_hist_takes(const Args& a, int b, int j) {
   if (!a.ghist) return false;
   const Mode sm = seq_mode(a, b);
   if (j > sm.g) return false;
-  if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && !(a.seq_flags[b] & F_DEMOTE) && !a.all_dense) return false;
+  // Under a.gmix the rows are taken while the select still runs, before any
+  // demotion is known: a demoted top-k sequence then goes to gumbel_kernel.
+  if ((sm.mode == MODE_GREEDY || sm.mode == MODE_SPARSE) && (a.gmix || !(a.seq_flags[b] & F_DEMOTE)) && !a.all_dense)
+    return false;
   const int k = a.topk ? a.topk[b] : 0;
   return sm.T > 0.0f && sm.tp == sm.tp && ((k > 0 && k < a.V) || sm.tp < 1.0f);
 }
@@ -278,6 +281,65 @@ __global__ __launch_bounds__(PH_NT) void gumbel_hist_kernel(Args a) {
     if (threadIdx.x == 0) s.next_pair = gridDim.x + atomicAdd(&a.dense_count[2], 1u);
     __syncthreads();
     t = s.next_pair;
+  }
+}
+
+// The select units and the histogram rows of a shared-noise call in one
+// launch (a.gmix), in the manner of mixed_hist_kernel: one workgroup per CU
+// first takes groups of PH_NW consecutive select units (a wavefront each),
+// then the rows gumbel_hist_takes, every one claimed from the row counter.
+// A call in which no sequence is dense (found by each workgroup from the
+// sampling settings) has its units taken one per wavefront instead, spread
+// over all CUs.  Both counters are cleared by gumbel_finish_kernel.
+__global__ __launch_bounds__(PH_NT) void gumbel_mixed_kernel(Args a) {
+  __shared__ __align__(16) union {
+    PhSmem ph;
+    WaveSmem w[PH_NW];
+  } sm;
+  __shared__ uint32_t claim;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const long long units = (long long)a.B * a.RS * a.NP;
+  const long long ngroups = (units + PH_NW - 1) / PH_NW;
+  int dense = 0;
+  for (int b = threadIdx.x; b < a.B; b += PH_NT) {
+    const int md = seq_mode(a, b).mode;
+    dense |= md != MODE_GREEDY && md != MODE_SPARSE ? 1 : 0;
+  }
+  if (!__syncthreads_or(dense)) {
+    for (;;) {
+      uint32_t u = 0;
+      if ((threadIdx.x & 63) == 0) u = atomicAdd(&a.dense_count[3], 1u);
+      u = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
+      if ((long long)u >= units) return;
+      select_unit<uint16_t, true>(a, (long long)u, sm.w[wave]);
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+  for (;;) {
+    __syncthreads();   // every wavefront has read the last claim
+    if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[3], 1u);
+    __syncthreads();
+    const uint32_t g = claim;
+    if ((long long)g >= ngroups) break;
+    select_unit<uint16_t, true>(a, (long long)g * PH_NW + wave, sm.w[wave]);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  const int G1 = a.G + 1;
+  const uint32_t nrows = (uint32_t)a.B * (uint32_t)G1;
+  __syncthreads();   // the select units' LDS, and the last claim, are done with
+  if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[2], 1u);
+  __syncthreads();
+  uint32_t t = claim;
+  while (t < nrows) {
+    const int b = (int)(t / (uint32_t)G1), j = (int)(t - (uint32_t)b * (uint32_t)G1);
+    if (gumbel_hist_takes(a, b, j)) {   // workgroup-uniform
+      const int32_t tok = gumbel_hist_row(a, sm.ph, b, j);
+      if (threadIdx.x == 0) a.out_target[(size_t)b * G1 + j] = tok;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[2], 1u);
+    __syncthreads();
+    t = claim;
   }
 }
 
@@ -629,7 +691,10 @@ __global__ __launch_bounds__(256) void gumbel_finish_kernel(Args a) {
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x * 4 + wave;
   if (b >= a.B) return;
-  if (b == 0 && threadIdx.x == 0 && a.ghist) a.dense_count[2] = 0;   // gumbel_hist_kernel's row counter
+  if (b == 0 && threadIdx.x == 0 && a.ghist) {   // the histogram rows' counter, the select groups' counter
+    a.dense_count[2] = 0;
+    a.dense_count[3] = 0;
+  }
   const int32_t* tgt = a.out_target + (size_t)b * (a.G + 1);
   gumbel_finish_wave(a, b, [&](int j) { return tgt[j]; });
 }

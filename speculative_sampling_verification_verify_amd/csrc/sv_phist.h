@@ -749,15 +749,18 @@ __global__ __launch_bounds__(PH_NT) void pair_hist_kernel(Args a) {
   }
 }
 
-// Calls with both dense and streamed (top-k, argmax) sequences on this
-// variant: the select units and the dense pairs in one launch, after a
+// Calls that may hold both dense and streamed (top-k, argmax) sequences on
+// this variant: the select units and the dense pairs in one launch, after a
 // launch that only lists the dense pairs.  One workgroup per CU first takes
 // groups of PH_NW consecutive select units (a wavefront each) from a
 // workspace counter, then dense pairs from the pair counter, every one
 // claimed.  So the CUs whose groups hold streamed rows (a few, since a
 // group covers consecutive rows of one or two sequences) stream them while
 // the others start on the pairs, and the pairs' tail no longer waits for a
-// separate select launch.  Both counters are cleared by the finisher.
+// separate select launch.  When the listing found no dense pair, every
+// wavefront instead takes single units from the counter, so the streamed
+// rows spread over all CUs as in the select kernel.  Both counters are
+// cleared by the finisher.
 __global__ __launch_bounds__(PH_NT) void mixed_hist_kernel(Args a) {
   __shared__ __align__(16) union {
     PhSmem ph;
@@ -767,6 +770,20 @@ __global__ __launch_bounds__(PH_NT) void mixed_hist_kernel(Args a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const long long units = (long long)a.B * a.RS * a.NP;
   const long long ngroups = (units + PH_NW - 1) / PH_NW;
+  const int G1 = a.G + 1;
+  const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
+  const uint32_t nf = min(a.dense_count[0], npairs);
+  const uint32_t nd = min(nf + a.dense_count[1], npairs);
+  if (nd == 0) {
+    for (;;) {
+      uint32_t u = 0;
+      if ((threadIdx.x & 63) == 0) u = atomicAdd(&a.dense_count[3], 1u);
+      u = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
+      if ((long long)u >= units) return;
+      select_unit<uint16_t, true>(a, (long long)u, sm.w[wave]);
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
   for (;;) {
     __syncthreads();   // every wavefront has read the last claim
     if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[3], 1u);
@@ -776,10 +793,6 @@ __global__ __launch_bounds__(PH_NT) void mixed_hist_kernel(Args a) {
     select_unit<uint16_t, true>(a, (long long)g * PH_NW + wave, sm.w[wave]);
     __builtin_amdgcn_s_setprio(0);
   }
-  const int G1 = a.G + 1;
-  const uint32_t npairs = (uint32_t)a.B * (uint32_t)G1;
-  const uint32_t nf = min(a.dense_count[0], npairs);
-  const uint32_t nd = min(nf + a.dense_count[1], npairs);
   __syncthreads();   // the select units' LDS, and the last claim, are done with
   if (threadIdx.x == 0) claim = atomicAdd(&a.dense_count[2], 1u);
   __syncthreads();

@@ -320,6 +320,29 @@ def test_gumbel_histogram_rows_all_dense_hint():
     check_gumbel(gb, "hist-all-dense-hint", hints=binding.SV_HINT_ALL_DENSE, calls=2)
 
 
+def test_gumbel_histogram_rows_beside_a_demoted_list():
+    # No hint at a histogram V: the select units run in the histogram rows'
+    # launch, before any list is demoted, so a top-k sequence demoted there
+    # (20000 ties at its k-th value) is computed by the per-position kernel.
+    T = [1.0, 0.0, 0.8, 1.0, 1.0]
+    k = [0, 0, 0, 64, 50]
+    tp = [0.9, 1.0, 0.95, 1.0, 1.0]
+    gb = _hist_batch(65544, len(T), 808, T, k, tp)
+    P = gb.p_logits.copy()
+    P[4, :, :20000] = synth.f32_to_bf16_bits(np.float32(3.0))
+    check_gumbel(_replace(gb, p_logits=P), "hist-mixed-demoted", calls=2)
+
+
+def test_gumbel_histogram_vocab_without_dense_sequences():
+    # Only argmax and top-k sequences at a histogram V, no hint: the units are
+    # taken one per wavefront over every CU.
+    B = 24
+    T = np.where(np.arange(B) % 2 == 0, 0.0, 0.7)
+    k = np.where(np.arange(B) % 4 == 1, 64, np.where(np.arange(B) % 4 == 3, 300, 0))
+    gb = _hist_batch(65544, B, 809, T, k, np.ones(B))
+    check_gumbel(gb, "hist-vocab-no-dense", calls=2)
+
+
 def test_gumbel_histogram_rows_ties():
     # Integer logits and integer noise above 32K values: many equal scores
     # inside the support, split over the workgroup's threads; the lowest id

@@ -236,6 +236,54 @@ def test_histogram_row_with_nan_is_invalid_and_others_exact():
     compare(bt, g, ref, "hist-invalid")
 
 
+# ---- calls with dense and streamed sequences on the histogram variant --------
+
+def _mixed_logits(B, G, V, seed):
+    rng = np.random.default_rng(seed)
+    rank = np.stack([rng.permutation(V) for _ in range(B)])[:, None, :]
+    zp = (3.0 * rng.normal(size=(B, G + 1, V)) - 1.1 * np.log1p(rank)).astype(np.float32)
+    zq = (zp[:, :G] + 0.7 * rng.normal(size=(B, G, V))).astype(np.float32)
+    return zp, zq
+
+
+def test_mixed_call_select_units_beside_histogram_pairs():
+    """Dense top-p sequences beside argmax and top-k sequences at V = 65544,
+    no hint: the select units run in the histogram pairs' launch.  The last
+    top-k sequence has more ties at its k-th value than the select's buffer
+    holds (demoted to the finisher's multi-pass path).  Two calls in a row on
+    one verifier check the counters the finisher clears."""
+    from speculative_sampling_verification_verify_amd import binding
+    B, G, V = 8, 3, 65544
+    zp, zq = _mixed_logits(B, G, V, 61)
+    zp[7, :, :20000] = 3.0
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=61, zp=zp, zq=zq,
+                     T=np.array([1.0, 0.0, 0.8, 1.0, 0.6, 1.3, 0.0, 1.0]),
+                     k=np.array([0, 0, 0, 64, 0, 0, 0, 50]),
+                     tp=np.array([0.9, 1.0, 0.95, 1.0, 0.8, 0.9, 1.0, 1.0], np.float32))
+    ver = binding.Verifier(B, G, V, binding.SV_BF16, device="cuda:0")
+    ref = run_oracle(bt)
+    for call in range(2):
+        rep = compare(bt, run_gpu(bt, verifier=ver), ref, f"mixed-call{call}")
+    log(f"[pair-hist] mixed call: ok {rep}")
+
+
+def test_mixed_kernel_without_dense_sequences():
+    """Only argmax and top-k sequences at a histogram-variant V, no hint: the
+    listing finds no dense pair, and the select units are taken one per
+    wavefront, spread over the CUs, instead of in groups of 16."""
+    from speculative_sampling_verification_verify_amd import binding
+    B, G, V = 40, 4, 65544
+    zp, zq = _mixed_logits(B, G, V, 62)
+    T = np.where(np.arange(B) % 2 == 0, 0.0, 0.8).astype(np.float32)
+    k = np.where(np.arange(B) % 4 == 1, 64, np.where(np.arange(B) % 4 == 3, 200, 0)).astype(np.int32)
+    bt = dense_batch(V, "bf16", B=B, G=G, seed=62, zp=zp, zq=zq, T=T, k=k)
+    ver = binding.Verifier(B, G, V, binding.SV_BF16, device="cuda:0")
+    ref = run_oracle(bt)
+    for call in range(2):
+        rep = compare(bt, run_gpu(bt, verifier=ver), ref, f"mixed-no-dense-call{call}")
+    log(f"[pair-hist] mixed kernel, no dense sequence: ok {rep}")
+
+
 def test_streamed_rows_beyond_the_histogram_variant():
     # 17500 units per row: more than the histogram variant holds, so the
     # value-binned streamed variant takes these rows.

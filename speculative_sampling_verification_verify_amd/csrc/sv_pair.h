@@ -684,9 +684,10 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   // Pass 1: maxima and validity (NaN or +inf makes the pair invalid); the
   // LDS variant copies the rows on chip as it goes.  Unfiltered rows also get
   // their normaliser in this pass: each thread keeps a running maximum m and
-  // the sum of 2^((z - m) c) over its elements, rescaled when m grows (one
-  // exponential per element: 2^(-|z - m| c) is the new term or the rescale
-  // factor); the block combines the sums at the row maximum.
+  // the sum of 2^((z - m) c) over its elements, taken a unit at a time (the
+  // unit's maximum first, the sum rescaled once if m grows, then one
+  // exponential per element); the block combines the sums at the row
+  // maximum.
   const U* P;
   const U* Q;
   const bool online = !(k > 0 && k < V) && !(m.tp < 1.0f);
@@ -704,16 +705,22 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   float zmp = -INFINITY, zmq = -INFINITY, smp = 0.0f, smq = 0.0f;
   uint32_t bad = 0;
   auto scan_unit = [&](const U& u, float& zm, float& sm) {
+    float um = -INFINITY;
     T::each(u, [&](int, uint32_t raw) {
       const float z = T::val(raw);
       bad |= z < INFINITY ? 0u : 1u;
-      if (online) {
-        const float d = (z - zm) * cT;
-        const float ex = z > -INFINITY ? __builtin_amdgcn_exp2f(-fabsf(d)) : 0.0f;
-        sm = d > 0.0f ? fmaf(sm, ex, 1.0f) : sm + ex;
-      }
-      zm = fmaxf(zm, z);
+      um = fmaxf(um, z);
     });
+    if (online) {
+      // Terms relative to the new running maximum (0 while every element
+      // seen is -inf, whose terms are then 0).
+      const float mn = fmaxf(zm, um);
+      const float base = mn > -INFINITY ? mn : 0.0f;
+      float acc = sm * __builtin_amdgcn_exp2f((zm - base) * cT);
+      T::each(u, [&](int, uint32_t raw) { acc += __builtin_amdgcn_exp2f((T::val(raw) - base) * cT); });
+      sm = acc;
+    }
+    zm = fmaxf(zm, um);
   };
   if constexpr (LDSR) {
     // Every thread issues the loads of up to PAIR_LDS_UR units of each row
@@ -819,7 +826,13 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   // Streamed rows load the next tile while the current one is summed.
   const int ntile = (NU + NTP - 1) / NTP;
   double al = 0.0;
-  auto weights_pass = [&](bool use_q) {
+  // unf: unfiltered rows (every element in the support), whose probability
+  // needs no threshold test.
+  auto weights_pass = [&](bool use_q, auto unf) {
+    const auto prob = [&](const RowStat& st, float z) {
+      if constexpr (decltype(unf)::value) return ew(z, st.zmax, st.c) * st.sp;
+      else return pprob(st, z);
+    };
     int ui = threadIdx.x;
     U np{}, nq{};
     if (ui < NU) {
@@ -836,14 +849,14 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
       if (ui < NU) {
         if (use_q) {
           float pv[E];
-          T::each(up, [&](int j, uint32_t raw) { pv[j] = pprob(sp, T::val(raw)); });
+          T::each(up, [&](int j, uint32_t raw) { pv[j] = prob(sp, T::val(raw)); });
           T::each(uq, [&](int j, uint32_t raw) {
-            const float qv = pprob(sq, T::val(raw));
+            const float qv = prob(sq, T::val(raw));
             av += fminf(pv[j], qv);
             r += fmaxf(pv[j] - qv, 0.0f);
           });
         } else {
-          T::each(up, [&](int, uint32_t raw) { r += pprob(sp, T::val(raw)); });
+          T::each(up, [&](int, uint32_t raw) { r += prob(sp, T::val(raw)); });
         }
       }
       al += (double)av;
@@ -851,7 +864,10 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
       if (lane == 0) s.part[t][wave] = w;
     }
   };
-  weights_pass(resid);
+  if (online)
+    weights_pass(resid, std::true_type{});
+  else
+    weights_pass(resid, std::false_type{});
   __syncthreads();
   // The crossing tile: lane t of wavefront 0 holds tile t's total.
   const double u = (double)a.u[(size_t)b * G1 + a.G];
@@ -880,7 +896,10 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   if (resid && !(s.bd[1] >= 0.0)) {
     // Zero residual mass (p == q after processing): draw from p itself.
     __syncthreads();
-    weights_pass(false);
+    if (online)
+      weights_pass(false, std::true_type{});
+    else
+      weights_pass(false, std::false_type{});
     __syncthreads();
     locate();
     use_q = false;

@@ -63,6 +63,7 @@ struct PairSmem {
   uint32_t red_u[3 * (NTP / 64)];
   uint32_t bc[8];
   double bd[2];
+  int xd;   // thread 0's draft token of the pair, fetched at its start
 };
 struct PairStream {   // extra LDS of the streamed variant
   unsigned long long vh[PAIR_NBIN];
@@ -701,6 +702,9 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
       return;
     }
   }
+  // The draft token, for the record written at the end: fetched now, so its
+  // round trip overlaps the passes.
+  if (threadIdx.x == 0) s.xd = resid ? a.draft[(size_t)b * a.G + i] : -1;
   const float cT = LOG2E_F / m.T;
   float zmp = -INFINITY, zmq = -INFINITY, smp = 0.0f, smq = 0.0f;
   uint32_t bad = 0;
@@ -948,7 +952,7 @@ __device__ __forceinline__ void pair_one(const Args& a, int b, int i, PairSmem<N
   if (hitpos == 0xFFFFFFFFu) tok = (int)pb_max<NTP>(lastpos, s.red_u) - 1;   // rounding left no crossing
   if (resid) al = pb_sum_f64<NTP>(al, s.red_d);
   if (threadIdx.x == 0) {
-    const int x = resid ? a.draft[(size_t)b * a.G + i] : -1;
+    const int x = s.xd;
     double px = 0.0, qx = 0.0;
     if (x >= 0 && x < V) {
       px = (double)pprob(sp, T::val(T::raw_at(P, x)));

@@ -579,6 +579,9 @@ __device__ __forceinline__ void pair_small(const Args& a, int b, int i, const Mo
   const double Sp = wave_sum_dpp(lsp), Sq = wave_sum_dpp(lsq);
   const RowStat sp{-INFINITY, zp, c, (float)(1.0 / Sp)};
   const RowStat sq = resid ? RowStat{-INFINITY, zq, c, (float)(1.0 / Sq)} : sp;
+  // Unfiltered rows: every element is in the support, so a probability needs
+  // no threshold test.
+  const auto uprob = [](const RowStat& st, float z) { return ew(z, st.zmax, st.c) * st.sp; };
   // Element j of a unit (its bit pattern).
   auto elem = [](const U& v, int j) -> uint32_t {
     const uint32_t w = j < E / 4 * 1 ? v.x : (j < 2 * (E / 4) ? v.y : (j < 3 * (E / 4) ? v.z : v.w));
@@ -594,8 +597,8 @@ __device__ __forceinline__ void pair_small(const Args& a, int b, int i, const Mo
       float av = 0.0f, wr = 0.0f, pr = 0.0f;
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        const float pj = pprob(sp, T::val(elem(up[r], j)));
-        const float qj = resid ? pprob(sq, T::val(elem(uq[r], j))) : 0.0f;
+        const float pj = uprob(sp, T::val(elem(up[r], j)));
+        const float qj = resid ? uprob(sq, T::val(elem(uq[r], j))) : 0.0f;
         av += fminf(pj, qj);
         wr += resid ? fmaxf(pj - qj, 0.0f) : pj;
         pr += pj;
@@ -620,8 +623,8 @@ __device__ __forceinline__ void pair_small(const Args& a, int b, int i, const Mo
   // lanes' weight sums, then each lane's own elements in order (weights
   // formed again rather than kept).
   auto weight = [&](const U& vp, const U& vq, int j) -> float {
-    const float pj = pprob(sp, T::val(elem(vp, j)));
-    return use_q ? fmaxf(pj - pprob(sq, T::val(elem(vq, j))), 0.0f) : pj;
+    const float pj = uprob(sp, T::val(elem(vp, j)));
+    return use_q ? fmaxf(pj - uprob(sq, T::val(elem(vq, j))), 0.0f) : pj;
   };
   const double target = u * Z;
   double base = 0.0;

@@ -367,10 +367,17 @@ int spec_verify_spectr(const void* p_logits, const void* q_logits, int dtype, co
 /* Kernels of one call, for spec_verify_set_stage_events. */
 enum {
   SV_KERNEL_SELECT = 0,  /* streaming top-k / argmax select over the logit rows      */
+                         /* (in a call that runs the mixed kernel: only the listing */
+                         /* of the dense pairs)                                     */
   SV_KERNEL_PAIR = 1,    /* per-(sequence, position) pass over dense (unfiltered,   */
-                         /* large top-k, top-p) sequences; launched when V allows   */
+                         /* large top-k, top-p) sequences; launched when V allows.  */
+                         /* For bf16 rows of 32K-131K values with both kinds of     */
+                         /* sequence and no hint, the mixed kernel that also        */
+                         /* streams the select's rows                               */
   SV_KERNEL_FINISH = 2,  /* per-sequence acceptance, first rejection and draw       */
-  SV_KERNEL_GUMBEL = 3,  /* per-(sequence, position) pass of spec_verify_gumbel      */
+  SV_KERNEL_GUMBEL = 3,  /* spec_verify_gumbel: the histogram rows' kernel (with    */
+                         /* the select units when a list path runs beside it), or   */
+                         /* the per-(sequence, position) kernel                     */
   SV_KERNEL_KSEQ = 4     /* per-(sequence, prefix node) K-SEQ of spec_verify_spectr */
 };
 

@@ -20,7 +20,10 @@
 //      over the logits).  See sv_finish.h.
 // A caller that promises that every sequence is dense skips launch 1 (the
 // pair kernel then takes the pairs in a fixed order), and launch 3 becomes
-// finish_dense_kernel, one workgroup per 16 sequences.
+// finish_dense_kernel, one workgroup per 16 sequences.  When the dense pairs
+// take the histogram variant (bf16 rows of 32K-131K values) and no hint is
+// given, launch 1 only lists the pairs and launch 2 is mixed_hist_kernel,
+// which streams the select units as well (see sv_phist.h).
 //
 // Definitions followed (page titles and sections): the acceptance rule and
 // the residual, "Fast Inference from Transformers via Speculative Decoding"

@@ -32,6 +32,10 @@
 // 16-bit count; the decoded counts then no longer add up to V.  The pair's
 // record then asks the finisher to compute the whole sequence by its
 // multi-pass procedure over the logits.
+//
+// Two kernels run these pairs: pair_hist_kernel, and mixed_hist_kernel for
+// calls that also hold top-k / argmax sequences, which streams their select
+// units in the same launch (at the end of this file).
 #pragma once
 
 #include "sv_pair.h"

@@ -43,7 +43,7 @@ def _same(label, a, b):
 # (workload, first (B, V), second (B, V), hints): each pair of calls shrinks.
 CASES = [
     (3, (48, 40000), (12, 9000), binding.SV_HINT_NO_DENSE),     # top-k sequences: select + finisher
-    (4, (24, 60000), (8, 20000), 0),                            # mixed: argmax, dense top-p (streamed rows)
+    (4, (24, 60000), (8, 20000), 0),                            # mixed: argmax and dense top-p rows in one launch
     (1, (16, 32000), (6, 3000), binding.SV_HINT_ALL_DENSE),     # unfiltered: pair kernel, rows in LDS
     (0, (64, 1000), (5, 700), 0),                               # fp32 rows
 ]

@@ -649,13 +649,13 @@ static hipError_t launch_gumbel(const Args& a, long long sel_grid, hipStream_t s
     }
     if ((e = stage_mark(SV_KERNEL_SELECT, false, st)) != hipSuccess) return e;
   }
-  // 2. Their per-position argmax from the survivor lists (with a.gfuse,
-  //    every sequence's rows and its outputs: the call ends here).
+  // 2. Their per-position argmax from the survivor lists (with a.gfuse or
+  //    a.gmix, every sequence's rows and its outputs: the call ends here).
   if (!a.all_dense) {
     hipLaunchKernelGGL((gumbel_list_kernel<ET, VECTOR>), dim3((unsigned)a.B), dim3(NT), gumbel_list_smem_bytes(), st,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.gfuse) return hipSuccess;
+    if (a.gfuse || a.gmix) return hipSuccess;
   }
   // 3. Dense and demoted sequences: filtered bf16 rows of 32K-131K values by
   //    the histogram kernel (one workgroup per CU), the rest one workgroup
@@ -738,8 +738,8 @@ static int run_gumbel(const void* p_logits, int dtype, const float* noise, const
   // support cheaply: the exact histogram kernel.
   a.ghist = !a.gfuse && dtype == SV_BF16 && vector_ok && V > 32768 && V / 8 <= PH_MAX_UNITS ? 1 : 0;
   // With a list path beside it, the select units run in the histogram rows'
-  // launch.
-  a.gmix = SV_MIXED && a.ghist && !a.all_dense ? 1 : 0;
+  // launch, and the list kernel then finishes the call.
+  a.gmix = SV_MIXED && a.ghist && !a.all_dense && !sampler ? 1 : 0;
   a.dense_count = reinterpret_cast<uint32_t*>(ws + Lw.dense_count_off);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;

@@ -71,7 +71,8 @@ struct Args {
   int gfuse;              // shared-noise verify: the list kernel takes every sequence and finishes it
                           // (no per-(sequence, position) or finish launch follows)
   int gmix;               // shared-noise verify with ghist: gumbel_mixed_kernel streams the select
-                          // units and takes the histogram rows (never a top-k or argmax sequence's)
+                          // units and takes the histogram rows (never a top-k or argmax sequence's);
+                          // the list kernel then finishes the call
   int kphase;             // multi-candidate verify: 0 every node; 1 nodes of classes of two or more
                           // (single-candidate nodes deferred); 2 the pending chains' nodes
   const int32_t* cand;    // multi-candidate verify: [B][K][L] candidate tokens

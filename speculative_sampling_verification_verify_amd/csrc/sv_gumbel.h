@@ -524,7 +524,9 @@ constexpr size_t gumbel_list_smem_bytes() {
 // With a.gfuse (calls promised to hold no dense sequence) this launch is
 // the last of the call: dense, invalid and demoted sequences get their rows
 // from the whole workgroup here (gumbel_row_block, one row after another),
-// and every sequence is finished here (gumbel_finish_wave).
+// and every sequence is finished here (gumbel_finish_wave).  So it is with
+// a.gmix, where gumbel_mixed_kernel has already sampled the histogram rows:
+// those samples are taken as they are, unless a count overflowed there.
 template <typename ET, bool VECTOR>
 __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   extern __shared__ __align__(16) unsigned char gl_smem[];
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   }
   const Mode m = seq_mode(a, b);
   const uint32_t fl = a.seq_flags[b];
-  const bool fuse = a.gfuse != 0;
+  const bool fuse = a.gfuse != 0 || a.gmix != 0;
   const int R = m.g + 1;
   const int NS = R * a.NP;
   int32_t* tgt = a.out_target + (size_t)b * (G + 1);
@@ -673,7 +675,11 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
     PairSmem<NT>& ps_s = *reinterpret_cast<PairSmem<NT>*>(gl_smem);
     PairStream& ps_x = *reinterpret_cast<PairStream*>(gl_smem + gumbel_pair_stream_offset<NT>());
     for (int j = 0; j < R; ++j) {
-      const int32_t tok = gumbel_row_block<ET, NT, VECTOR>(a, ps_s, ps_x, b, j);
+      int32_t tok;
+      if (a.gmix && gumbel_hist_takes(a, b, j) && tgt[j] != GUMBEL_REDO)   // block-uniform
+        tok = tgt[j];
+      else
+        tok = gumbel_row_block<ET, NT, VECTOR>(a, ps_s, ps_x, b, j);
       if (threadIdx.x == 0) {
         tgt[j] = tok;
         ftok[j] = tok;
@@ -683,6 +689,10 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   }
   __syncthreads();   // publishes ftok
   if (wave == 0) gumbel_finish_wave(a, b, [&](int j) { return ftok[j]; });
+  if (b == 0 && threadIdx.x == 0 && a.gmix) {   // gumbel_mixed_kernel's counters
+    a.dense_count[2] = 0;
+    a.dense_count[3] = 0;
+  }
 }
 
 // One wavefront per sequence: validity, the first disagreement between the

@@ -670,21 +670,23 @@ __global__ __launch_bounds__(NT) void gumbel_list_kernel(Args a) {
   }
   if (!fuse) return;
   if (src == ROWS_BLOCK) {
-    // The workgroup takes the rows one after another.
+    // The workgroup takes the rows one after another; under a.gmix the rows
+    // gumbel_mixed_kernel sampled are first taken as they are, all at once.
+    constexpr int32_t NEED = INT32_MIN;
     __syncthreads();   // the LDS above is free
+    for (int j = threadIdx.x; j < R; j += NT)
+      ftok[j] = a.gmix && gumbel_hist_takes(a, b, j) && tgt[j] != GUMBEL_REDO ? tgt[j] : NEED;
+    __syncthreads();
     PairSmem<NT>& ps_s = *reinterpret_cast<PairSmem<NT>*>(gl_smem);
     PairStream& ps_x = *reinterpret_cast<PairStream*>(gl_smem + gumbel_pair_stream_offset<NT>());
     for (int j = 0; j < R; ++j) {
-      int32_t tok;
-      if (a.gmix && gumbel_hist_takes(a, b, j) && tgt[j] != GUMBEL_REDO)   // block-uniform
-        tok = tgt[j];
-      else
-        tok = gumbel_row_block<ET, NT, VECTOR>(a, ps_s, ps_x, b, j);
+      if (ftok[j] != NEED) continue;   // block-uniform
+      const int32_t tok = gumbel_row_block<ET, NT, VECTOR>(a, ps_s, ps_x, b, j);
       if (threadIdx.x == 0) {
         tgt[j] = tok;
         ftok[j] = tok;
       }
-      __syncthreads();   // the next row reuses the LDS
+      __syncthreads();   // the next row reuses the LDS, and ftok[j] is published
     }
   }
   __syncthreads();   // publishes ftok

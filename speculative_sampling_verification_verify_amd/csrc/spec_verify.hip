@@ -268,6 +268,9 @@ static hipError_t device_setup() {
   return hipSuccess;
 }
 
+// The mixed launches (select units inside the histogram kernels' launch, for
+// calls that hold both kinds of sequence) are on unless built with
+// -DSV_MIXED=0, which restores the separate select launch for comparison.
 #ifndef SV_MIXED
 #define SV_MIXED 1
 #endif

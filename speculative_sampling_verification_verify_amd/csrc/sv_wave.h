@@ -51,11 +51,13 @@ struct WaveSmem {
 // wavefront-uniform): the issue arbiter favours older wavefronts, so without
 // this the first-launched ones finish their parts long before the
 // last-launched ones and the memory system idles in the tail.  A wavefront
-// with more of its part left ranks higher (the four priority levels).
+// with more of its part left ranks higher (the four priority levels, at
+// half, a quarter and an eighth of the part left, so the levels are finest
+// where the parts end).
 __device__ __forceinline__ void progress_prio(int left, int total) {
-  const int q = (left * 4) / total;
-  if (q >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (q == 2) __builtin_amdgcn_s_setprio(2);
+  const int q = (left * 8) / total;
+  if (q >= 4) __builtin_amdgcn_s_setprio(3);
+  else if (q >= 2) __builtin_amdgcn_s_setprio(2);
   else if (q == 1) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
